@@ -1,0 +1,483 @@
+"""DFlash gamma-block drafter -- plain, slow CPU oracle.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg import this module. The HIP library and its Python binding never
+call it, and the two share no code: no kernels, headers, helpers or tables.
+
+Sources (page title -- section). Every function below names the one it follows.
+  [memra]   memra_engine/dflash.rs (docs.rs source page) -- the drafter written as a
+            readable forward: DflashDraft::ctx_features, ::forward_block, ::ingest_ctx,
+            ::forward_round, ::rope_rows, DflashDraft::load (YaRN table),
+            HybridModel::generate_spec_dflash (block construction, lm_head rows, argmax).
+  [atlas-fw]  spark_model/layers/dflash_head/from_weights.rs -- from_weights: vanilla
+            RMSNorm choice, paged KV pool sizing, inv_freq table (plain and YaRN), fused
+            K/V weight layout.
+  [atlas-head] spark_model/layers/dflash_head.rs -- DflashBatch (bands of gamma rows per
+            sequence) and DraftProposer::propose_batch (drop row 0 of each band).
+
+Arithmetic: numpy float64 by default (float32 on request, for timing only). Inputs
+arrive as bf16 bit patterns (uint16) and are widened exactly; no intermediate value is
+rounded. Where the pages leave a step open, the reading taken is marked READING and
+listed in the design doc.
+
+Parity unpinned (no worked example on the pages fixes them): the sliding-window rule
+inside a non-causal block (READING c1 below) and the placement of the YaRN mscale when
+a trained checkpoint is used (READING c2). Both are pinned only by invariants.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+# ----------------------------------------------------------------------------------
+# bf16 inputs
+# ----------------------------------------------------------------------------------
+
+
+def widen(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """Exact bf16 -> float widening of uint16 bit patterns (a bf16 is the top half of
+    an IEEE binary32)."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(dtype)
+
+
+# ----------------------------------------------------------------------------------
+# elementary steps
+# ----------------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis in the vanilla (HF) form out = x * w / RMS(x).
+
+    [atlas-fw] from_weights, kernel table: the drafter uses the vanilla form, not the
+    offset form x*(1+w). READING c6: RMS(x) = sqrt(mean(x^2) + eps).
+    """
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def inv_freq_plain(theta: float, head_dim: int) -> np.ndarray:
+    """inv_freq[j] = theta^(-2j/d), j < d/2, rotary dim = head_dim.
+    [atlas-fw] from_weights, inv_freq table (default arm)."""
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * j / head_dim)
+
+
+def yarn_bounds(head_dim: int, theta: float, factor: float, orig: float,
+                beta_fast: float, beta_slow: float):
+    """The YaRN correction range (low, high) in pair-index units.
+
+    [memra] DflashDraft::load, YaRN arm; [atlas-fw] from_weights, YaRN arm:
+    corr(r) = d * ln(orig / (2 pi r)) / (2 ln base); low = max(floor(corr(beta_fast)), 0);
+    high = min(ceil(corr(beta_slow)), d - 1).
+    """
+    d = float(head_dim)
+
+    def corr(r):
+        return d * math.log(orig / (r * 2.0 * math.pi)) / (2.0 * math.log(theta))
+
+    low = max(math.floor(corr(beta_fast)), 0.0)
+    high = min(math.ceil(corr(beta_slow)), d - 1.0)
+    return float(low), float(high)
+
+
+def inv_freq_yarn(head_dim: int, theta: float, factor: float, orig: float,
+                  beta_fast: float, beta_slow: float) -> np.ndarray:
+    """YaRN-blended inverse frequencies.
+
+    [memra] DflashDraft::load and [atlas-fw] from_weights (YaRN arm): a linear ramp over
+    pair index j from `low` to `high` moves each frequency from the plain value
+    (extrapolation, ramp 0) to the plain value divided by `factor` (interpolation,
+    ramp 1). READING c3: when high == low the ramp denominator gets +0.001 (the Atlas
+    page's guard; the memra page has none -- never hit by the shapes used here).
+    """
+    low, high = yarn_bounds(head_dim, theta, factor, orig, beta_fast, beta_slow)
+    base = inv_freq_plain(theta, head_dim)
+    denom = (high - low) if abs(high - low) >= 1e-6 else (high - low + 0.001)
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    ramp = np.clip((j - low) / denom, 0.0, 1.0)
+    return (base / factor) * ramp + base * (1.0 - ramp)
+
+
+def yarn_mscale(factor: float) -> float:
+    """[memra] DflashDraft::load: attention scaling 0.1 * ln(factor) + 1."""
+    return 0.1 * math.log(factor) + 1.0
+
+
+def rope_neox(x: np.ndarray, pos: np.ndarray, inv_freq: np.ndarray) -> np.ndarray:
+    """NeoX (rotate-half) rotary embedding over the whole head.
+
+    x: [..., head_dim]; pos: integer positions broadcastable to x.shape[:-1].
+    For j < d/2 with angle a = pos * inv_freq[j]:
+      out[j]       = x[j] cos a - x[j + d/2] sin a
+      out[j + d/2] = x[j + d/2] cos a + x[j] sin a
+    [memra] DflashDraft::rope_rows (rope_neox, rotary dim = head_dim); [atlas-fw]
+    from_weights ("applies rope to full head_dim"). READING c4: pairs (j, j + d/2).
+    """
+    half = x.shape[-1] // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq.astype(np.float64)
+    c = np.cos(ang).astype(x.dtype)
+    s = np.sin(ang).astype(x.dtype)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def gqa_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndarray,
+                  k_pos: np.ndarray, scale: float, window: int) -> np.ndarray:
+    """Non-causal grouped-query softmax attention.
+
+    q: [T, nh, d]; k, v: [Tk, nkv, d]; q_pos [T], k_pos [Tk] integer positions.
+    Query head h reads kv head h // (nh / nkv) (READING c5: contiguous groups).
+    Every query sees every key (non-causal) unless `window` > 0, in which case key j
+    is visible to query i iff q_pos[i] - k_pos[j] < window (READING c1: the usual
+    decoder window that includes the query's own position, no upper bound).
+    [memra] DflashDraft::forward_round (sdpa_naive, causal = false, scale 1/sqrt(d)).
+    """
+    T, nh, d = q.shape
+    nkv = k.shape[1]
+    G = nh // nkv
+    out = np.empty((T, nh, d), dtype=q.dtype)
+    if window > 0:
+        vis = (q_pos[:, None].astype(np.int64) - k_pos[None, :].astype(np.int64)) < window
+    else:
+        vis = np.ones((T, k.shape[0]), dtype=bool)
+    for h in range(nh):
+        kh = h // G
+        s = (q[:, h, :] @ k[:, kh, :].T) * scale          # [T, Tk]
+        s = np.where(vis, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, kh, :]
+    return out
+
+
+def argmax_lowest(x: np.ndarray) -> np.ndarray:
+    """Row-wise argmax; READING c7: the lowest index wins an exact tie."""
+    return np.argmax(x, axis=-1).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------------
+# paged KV pool: the integer model
+# ----------------------------------------------------------------------------------
+
+PAGE = 16  # tokens per page ([atlas-fw] from_weights: block size 16)
+
+
+def pool_pages(max_seq_len: int, gamma_max: int, max_batch: int) -> tuple[int, int]:
+    """(pages per sequence, pages in the pool).
+
+    [atlas-fw] from_weights, pool sizing: per sequence ceil((max_seq_len + gamma + 1) / 16)
+    pages, times max_batch, plus one spare. The spare is page 0 here: a zeroed sentinel
+    that is never handed out (READING: the spare page doubles as the dummy block).
+    """
+    per_seq = -(-(max_seq_len + gamma_max + 1) // PAGE)
+    return per_seq, per_seq * max(1, max_batch) + 1
+
+
+class PoolError(Exception):
+    def __init__(self, code: str, msg: str):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+class PagePool:
+    """Free list + per-sequence block tables.
+
+    The free list starts as `page_order` (a permutation of 1..P-1) or ascending 1..P-1.
+    Allocation pops from the head, in sequence-then-page order; a page is taken the first
+    time a sequence writes a position inside it (context rows and transient block rows
+    alike). Resetting a sequence appends its pages to the tail of the free list in
+    block-table order. slot(p) = block_table[p // 16] * 16 + p % 16 (int64).
+    [atlas-fw] from_weights (lazy per-sequence allocation, pool exhaustion is an error);
+    [atlas-head] slot mapping from the block table.
+    """
+
+    def __init__(self, max_seq_len, gamma_max, max_batch, page_order=None, num_pages=0):
+        self.per_seq, self.num_pages = pool_pages(max_seq_len, gamma_max, max_batch)
+        if num_pages:            # an explicit (smaller) pool, to exercise exhaustion
+            self.num_pages = int(num_pages)
+        if page_order is None:
+            self.free = list(range(1, self.num_pages))
+        else:
+            po = [int(p) for p in page_order]
+            if sorted(po) != list(range(1, self.num_pages)):
+                raise PoolError("EINVAL", "page_order is not a permutation of 1..P-1")
+            self.free = po
+        self.bt = {s: [] for s in range(max(1, max_batch))}
+
+    def pages_needed(self, seq: int, end_pos: int) -> int:
+        """New pages sequence `seq` needs so that logical positions [0, end_pos) are backed."""
+        need = -(-end_pos // PAGE)
+        return max(0, need - len(self.bt[seq]))
+
+    def ensure(self, seq: int, end_pos: int) -> list[int]:
+        n = self.pages_needed(seq, end_pos)
+        if n > len(self.free):
+            raise PoolError("EPOOL", "KV pool exhausted")
+        if len(self.bt[seq]) + n > self.per_seq:
+            raise PoolError("ERANGE", "sequence exceeds its page budget")
+        new, self.free = self.free[:n], self.free[n:]
+        self.bt[seq].extend(new)
+        return new
+
+    def slots(self, seq: int, positions) -> np.ndarray:
+        bt = self.bt[seq]
+        return np.array([bt[p // PAGE] * PAGE + (p % PAGE) for p in positions], dtype=np.int64)
+
+    def reset(self, seq: int):
+        self.free.extend(self.bt[seq])
+        self.bt[seq] = []
+
+
+# ----------------------------------------------------------------------------------
+# the drafter
+# ----------------------------------------------------------------------------------
+
+
+class Drafter:
+    """The drafter's arithmetic on one sequence at a time.
+
+    m: model dict (hidden, heads, taps, rope, window ...); weights: name -> bf16 bits.
+    """
+
+    def __init__(self, m: dict, weights: dict, dtype=np.float64, cache_weights: bool = True):
+        self.m = m
+        self.bits = weights
+        self.dtype = dtype
+        self.cache_weights = cache_weights
+        self._cache = {}
+        hd = m["head_dim"]
+        if m.get("rope_type", "plain") == "yarn":
+            self.inv_freq = inv_freq_yarn(hd, m["rope_theta"], m["yarn_factor"], m["yarn_orig_max_pos"],
+                                          m["yarn_beta_fast"], m["yarn_beta_slow"])
+            self.mscale = yarn_mscale(m["yarn_factor"])
+        else:
+            self.inv_freq = inv_freq_plain(m["rope_theta"], hd)
+            self.mscale = None
+
+    def w(self, name: str) -> np.ndarray:
+        if name in self._cache:
+            return self._cache[name]
+        a = widen(self.bits[name], self.dtype)
+        if self.cache_weights:
+            self._cache[name] = a
+        return a
+
+    def lw(self, l: int, name: str) -> np.ndarray:
+        return self.w(f"layers.{l}.{name}")
+
+    def sliding(self, l: int) -> bool:
+        ls = self.m.get("layer_sliding")
+        return bool(ls[l]) if ls else False
+
+    def rope_rows(self, x: np.ndarray, pos: np.ndarray) -> np.ndarray:
+        """[memra] DflashDraft::rope_rows: NeoX RoPE, then (YaRN only) multiply by mscale.
+        READING c2: mscale multiplies both q and k after the rotation."""
+        y = rope_neox(x, pos, self.inv_freq)
+        if self.mscale is not None:
+            y = y * self.mscale
+        return y
+
+    # -- context append -----------------------------------------------------------
+
+    def ctx_features(self, taps_bits: np.ndarray) -> np.ndarray:
+        """F = hidden_norm(taps @ fc^T). taps: [n, num_taps * target_hidden], taps in
+        target_layer_ids order (READING c13). [memra] DflashDraft::ctx_features."""
+        m = self.m
+        x = widen(taps_bits, self.dtype)
+        f = x @ self.w("fc").T
+        return rms_norm(f, self.w("hidden_norm"), m["rms_eps"])
+
+    def ctx_kv(self, F: np.ndarray, positions: np.ndarray):
+        """Per layer: K = rope(k_norm(F Wk^T per head), pos), V = F Wv^T.
+        Context features are not passed through input_layernorm.
+        [memra] DflashDraft::ingest_ctx; DflashDraft::forward_block (ctx features are
+        norm-free per layer)."""
+        m = self.m
+        n = F.shape[0]
+        nkv, hd = m["num_kv_heads"], m["head_dim"]
+        out = []
+        for l in range(m["num_layers"]):
+            k = (F @ self.lw(l, "k_proj").T).reshape(n, nkv, hd)
+            v = (F @ self.lw(l, "v_proj").T).reshape(n, nkv, hd)
+            k = rms_norm(k, self.lw(l, "k_norm"), m["rms_eps"])
+            k = self.rope_rows(k, np.asarray(positions)[:, None])
+            out.append((k, v))
+        return out
+
+    # -- one gamma block ------------------------------------------------------------
+
+    def block_forward(self, ctx_k, ctx_v, ctx_pos, bonus: int, q_rope_pos: int, gamma: int,
+                      want_hidden: bool = False):
+        """One band: block [bonus, mask x (gamma-1)] through every layer, final norm,
+        lm_head on rows 1..gamma-1, argmax.
+
+        ctx_k[l], ctx_v[l]: [C, nkv, hd] cached context K (normed, roped) and V; ctx_pos [C].
+        Row i of the block sits at position q_rope_pos + i (READING c9).
+        [memra] HybridModel::generate_spec_dflash (block = [last, MASK x b-1]; drafts =
+        argmax(lm_head(rows 1..b))) and DflashDraft::forward_round (per-layer math, block
+        K/V appended after the context keys, never committed).
+        """
+        toks = np.full(gamma, self.m["mask_token_id"], dtype=np.int64)
+        toks[0] = bonus
+        bpos = q_rope_pos + np.arange(gamma, dtype=np.int64)
+        y = self.block_hidden(ctx_k, ctx_v, ctx_pos, toks, bpos)
+        logits = self.lm_head(y[1:])
+        res = dict(logits=logits, tokens=argmax_lowest(logits))
+        if want_hidden:
+            res["hidden"] = y
+        return res
+
+    def block_hidden(self, ctx_k, ctx_v, ctx_pos, toks, bpos):
+        """Final-normed hidden rows [T, h] of a block with explicit token ids `toks` [T]
+        at explicit positions `bpos` [T]; the gamma-block forward calls it with
+        [bonus, mask x (gamma-1)] at q_rope_pos + i. Keys are the context keys followed by
+        the block's own keys; every query sees every key (non-causal).
+        [memra] DflashDraft::forward_round: per layer input_layernorm on block rows,
+        q/k/v projections, per-head q_norm / k_norm, RoPE, attention over context + block,
+        o_proj + residual, post_attention_layernorm, SwiGLU MLP + residual; final norm.
+        """
+        m = self.m
+        h, nh, nkv, hd = m["hidden"], m["num_q_heads"], m["num_kv_heads"], m["head_dim"]
+        eps = m["rms_eps"]
+        gamma = len(toks)
+        bpos = np.asarray(bpos, dtype=np.int64)
+        x = widen(self.bits["embed_tokens"][np.asarray(toks)], self.dtype)       # [T, h]
+        scale = 1.0 / math.sqrt(hd)
+        for l in range(m["num_layers"]):
+            xn = rms_norm(x, self.lw(l, "input_layernorm"), eps)
+            q = (xn @ self.lw(l, "q_proj").T).reshape(gamma, nh, hd)
+            kb = (xn @ self.lw(l, "k_proj").T).reshape(gamma, nkv, hd)
+            vb = (xn @ self.lw(l, "v_proj").T).reshape(gamma, nkv, hd)
+            q = self.rope_rows(rms_norm(q, self.lw(l, "q_norm"), eps), bpos[:, None])
+            kb = self.rope_rows(rms_norm(kb, self.lw(l, "k_norm"), eps), bpos[:, None])
+            k_all = np.concatenate([ctx_k[l], kb], axis=0)
+            v_all = np.concatenate([ctx_v[l], vb], axis=0)
+            k_pos = np.concatenate([np.asarray(ctx_pos, dtype=np.int64), bpos])
+            win = int(m.get("sliding_window", 0) or 0) if self.sliding(l) else 0
+            attn = gqa_attention(q, bpos, k_all, v_all, k_pos, scale, win).reshape(gamma, nh * hd)
+            x1 = x + attn @ self.lw(l, "o_proj").T
+            x1n = rms_norm(x1, self.lw(l, "post_attention_layernorm"), eps)
+            g = x1n @ self.lw(l, "gate_proj").T
+            u = x1n @ self.lw(l, "up_proj").T
+            x = x1 + (silu(g) * u) @ self.lw(l, "down_proj").T
+        return rms_norm(x, self.w("norm"), eps)
+
+    def lm_head(self, y: np.ndarray, chunk: int = 16384) -> np.ndarray:
+        """logits = y @ lm_head^T, the vocabulary taken in chunks (memory only)."""
+        V = self.m["vocab"]
+        out = np.empty((y.shape[0], V), dtype=self.dtype)
+        for s in range(0, V, chunk):
+            e = min(V, s + chunk)
+            out[:, s:e] = y @ widen(self.bits["lm_head"][s:e], self.dtype).T
+        return out
+
+
+# ----------------------------------------------------------------------------------
+# the whole boundary, as the C ABI exposes it
+# ----------------------------------------------------------------------------------
+
+
+class Engine:
+    """Host-side model of the four calls: create / ctx_kv_append / block_forward /
+    seq_reset, with the pool's integer state (block tables, slots) and each sequence's
+    cached context K/V kept contiguous (the memra page's DflashKv layout).
+
+    Every check happens before any state changes; a failing call raises PoolError and
+    leaves the engine as it was ([atlas-head] propose_batch: a sequence that cannot be
+    served aborts the whole batch).
+    """
+
+    def __init__(self, m: dict, weights: dict, max_seq_len: int, max_batch: int,
+                 page_order=None, dtype=np.float64, cache_weights: bool = True, num_pages: int = 0):
+        self.m = m
+        self.d = Drafter(m, weights, dtype, cache_weights)
+        self.max_seq_len = max_seq_len
+        self.max_batch = max_batch
+        self.pool = PagePool(max_seq_len, m["gamma_max"], max_batch, page_order, num_pages)
+        self.seqs = {s: self._empty() for s in range(max_batch)}
+        self.last_slots = np.zeros(0, dtype=np.int64)
+
+    def _empty(self):
+        L = self.m["num_layers"]
+        nkv, hd = self.m["num_kv_heads"], self.m["head_dim"]
+        z = np.zeros((0, nkv, hd), dtype=self.d.dtype)
+        return dict(k=[z] * L, v=[z] * L, pos=np.zeros(0, dtype=np.int64))
+
+    def kv_len(self, seq: int) -> int:
+        return int(self.seqs[seq]["pos"].shape[0])
+
+    def block_table(self, seq: int) -> list[int]:
+        return list(self.pool.bt[seq])
+
+    def seq_reset(self, seq: int):
+        if not (0 <= seq < self.max_batch):
+            raise PoolError("ERANGE", "seq out of range")
+        self.pool.reset(seq)
+        self.seqs[seq] = self._empty()
+
+    def ctx_kv_append(self, seq: int, taps_bits: np.ndarray, positions=None):
+        if not (0 <= seq < self.max_batch):
+            raise PoolError("ERANGE", "seq out of range")
+        n = int(taps_bits.shape[0])
+        if n <= 0:
+            raise PoolError("EINVAL", "n must be positive")
+        s = self.seqs[seq]
+        C = self.kv_len(seq)
+        if C + n > self.max_seq_len:
+            raise PoolError("ERANGE", "kv_len + n exceeds max_seq_len")
+        if positions is None:
+            positions = np.arange(C, C + n, dtype=np.int64)
+        positions = np.asarray(positions, dtype=np.int64)
+        last = s["pos"][-1] if C else -1
+        if positions.shape[0] != n or positions[0] <= last or np.any(np.diff(positions) <= 0) \
+                or positions[-1] > np.iinfo(np.int32).max:
+            raise PoolError("EINVAL", "positions must be strictly increasing")
+        self.pool.ensure(seq, C + n)
+        self.last_slots = self.pool.slots(seq, range(C, C + n))
+        F = self.d.ctx_features(taps_bits)
+        kv = self.d.ctx_kv(F, positions)
+        for l, (k, v) in enumerate(kv):
+            s["k"][l] = np.concatenate([s["k"][l], k], axis=0)
+            s["v"][l] = np.concatenate([s["v"][l], v], axis=0)
+        s["pos"] = np.concatenate([s["pos"], positions])
+
+    def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False):
+        m = self.m
+        gamma = m["gamma_max"] if gamma is None else gamma
+        seqs = [int(x) for x in seqs]
+        if len(seqs) == 0 or len(seqs) > self.max_batch:
+            raise PoolError("EINVAL", "bad number of sequences")
+        if len(set(seqs)) != len(seqs) or any(not (0 <= x < self.max_batch) for x in seqs):
+            raise PoolError("ERANGE", "seq out of range or repeated")
+        if not (2 <= gamma <= m["gamma_max"]):
+            raise PoolError("ERANGE", "gamma out of range")
+        if any(not (0 <= int(b) < m["vocab"]) for b in bonus):
+            raise PoolError("EINVAL", "bonus token out of range")
+        # page budget for every band, checked before anything is taken
+        need = sum(self.pool.pages_needed(x, self.kv_len(x) + gamma) for x in seqs)
+        if need > len(self.pool.free):
+            raise PoolError("EPOOL", "KV pool exhausted")
+        slots = []
+        for x in seqs:
+            C = self.kv_len(x)
+            self.pool.ensure(x, C + gamma)
+            slots.append(self.pool.slots(x, range(C, C + gamma)))
+        self.last_slots = np.concatenate(slots)
+        outs = []
+        for i, x in enumerate(seqs):
+            s = self.seqs[x]
+            C = self.kv_len(x)
+            P = C if q_rope_pos is None else int(q_rope_pos[i])
+            outs.append(self.d.block_forward(s["k"], s["v"], s["pos"], int(bonus[i]), P, gamma,
+                                             want_hidden=want_hidden))
+        res = dict(tokens=np.stack([o["tokens"] for o in outs]),
+                   logits=np.stack([o["logits"] for o in outs]))
+        if want_hidden:
+            res["hidden"] = np.stack([o["hidden"] for o in outs])
+        return res

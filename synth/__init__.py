@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the DFlash gamma-block drafter.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and
+benchmark. It holds workload shapes and seeded random draws only: no step of the
+drafter's arithmetic lives here. Every tensor is returned as bf16 bit patterns
+(numpy uint16) so that both sides start from the same exact values.
+
+Recipe (also stated in the design doc):
+  * generator: numpy PCG64 seeded with SeedSequence([seed, stream, index]);
+    float32 draws rounded to bf16 with round-to-nearest-even;
+  * weight matrices ~ N(0, 0.02); norm weights ~ 1 + N(0, 0.02);
+  * tapped target hidden states ~ N(0, 1);
+  * bonus tokens uniform over the vocabulary; context lengths uniform over the
+    workload's range; the pool's page order is a seeded permutation.
+
+No public dataset or benchmark is involved: these draws stand in for the pages'
+drafters (trained checkpoints) and for hidden states captured from a target model.
+"""
+from __future__ import annotations
+
+import copy
+import numpy as np
+
+# --------------------------------------------------------------------------------------
+# model shapes (the drafter families the pages describe) and workloads
+# --------------------------------------------------------------------------------------
+
+_TINY = dict(
+    num_layers=2, hidden=256, num_q_heads=8, num_kv_heads=2, head_dim=32,
+    intermediate=512, vocab=1024, num_taps=3, target_hidden=256, gamma_max=16,
+    mask_token_id=4, rms_eps=1e-6, rope_theta=1e6, rope_type="plain",
+    sliding_window=0, layer_sliding=None,
+)
+
+_QWEN3_8L_2048 = dict(
+    num_layers=8, hidden=2048, num_q_heads=32, num_kv_heads=4, head_dim=128,
+    intermediate=6144, vocab=151936, num_taps=5, target_hidden=2048, gamma_max=16,
+    mask_token_id=4, rms_eps=1e-6, rope_theta=1e6, rope_type="plain",
+    sliding_window=0, layer_sliding=None,
+)
+
+_WIDE_5L_5376 = dict(
+    num_layers=5, hidden=5376, num_q_heads=64, num_kv_heads=8, head_dim=128,
+    intermediate=10752, vocab=262144, num_taps=6, target_hidden=5376, gamma_max=16,
+    mask_token_id=4, rms_eps=1e-6, rope_theta=1e6, rope_type="yarn",
+    yarn_factor=32.0, yarn_orig_max_pos=8192.0, yarn_beta_fast=32.0,
+    yarn_beta_slow=1.0, sliding_window=2048,
+    layer_sliding=[True, True, True, True, False],
+)
+
+MODELS = {
+    "tiny-L2-h256": _TINY,
+    "qwen3-L8-h2048": _QWEN3_8L_2048,
+    "wide-L5-h5376-yarn-swa2048": _WIDE_5L_5376,
+}
+
+# A workload = a model, how many sequences one forward call carries, how their
+# contexts are filled, and the pool geometry.
+#   ctx: (lo, hi) inclusive range of existing context lengths per sequence
+#   append: rows appended (timed) right before the block forward, 0 = none
+WORKLOADS = {
+    "tiny-L2-h256-ctx64-b1": dict(
+        model="tiny-L2-h256", batch=1, ctx=(64, 64), append=0,
+        max_seq_len=128, max_batch=1, permute_pages=False, seed=1001),
+    "qwen3-L8-h2048-ctx4096-b1": dict(
+        model="qwen3-L8-h2048", batch=1, ctx=(4096, 4096), append=0,
+        max_seq_len=8192, max_batch=1, permute_pages=False, seed=1002),
+    "qwen3-L8-h2048-b16-ctx512to8192": dict(
+        model="qwen3-L8-h2048", batch=16, ctx=(512, 8192), append=0,
+        max_seq_len=8192, max_batch=16, permute_pages=True, seed=1003),
+    "wide-L5-h5376-yarn-swa2048-ctx16384-b1": dict(
+        model="wide-L5-h5376-yarn-swa2048", batch=1, ctx=(16384, 16384), append=0,
+        max_seq_len=20480, max_batch=1, permute_pages=False, seed=1004),
+    "qwen3-L8-h2048-b32-ctx8192to32768-append2048": dict(
+        model="qwen3-L8-h2048", batch=32, ctx=(8192, 32768), append=2048,
+        max_seq_len=34816, max_batch=32, permute_pages=True, seed=1005),
+}
+
+
+def model(name: str) -> dict:
+    return copy.deepcopy(MODELS[name])
+
+
+def workload(name: str) -> dict:
+    w = copy.deepcopy(WORKLOADS[name])
+    w["name"] = name
+    w["model_cfg"] = model(w["model"])
+    return w
+
+
+# --------------------------------------------------------------------------------------
+# draws
+# --------------------------------------------------------------------------------------
+
+# stream ids (second word of every SeedSequence)
+S_WEIGHTS, S_HIDDEN, S_BONUS, S_CTXLEN, S_PAGES, S_POS = 1, 2, 3, 4, 5, 6
+
+
+def rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, index])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round-to-nearest-even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_bf16(g: np.random.Generator, shape, mean: float, std: float) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    chunk = 1 << 24
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = g.standard_normal(e - s, dtype=np.float32)
+        x *= np.float32(std)
+        if mean != 0.0:
+            x += np.float32(mean)
+        out[s:e] = f32_to_bf16_bits(x)
+    return out.reshape(shape)
+
+
+def weight_specs(m: dict):
+    """(name, shape, kind) in the fixed generation order; kind is 'mat' or 'norm'."""
+    h, hd = m["hidden"], m["head_dim"]
+    qd, kvd, ff = m["num_q_heads"] * hd, m["num_kv_heads"] * hd, m["intermediate"]
+    specs = [
+        ("fc", (h, m["num_taps"] * m["target_hidden"]), "mat"),
+        ("hidden_norm", (h,), "norm"),
+        ("norm", (h,), "norm"),
+        ("embed_tokens", (m["vocab"], h), "mat"),
+        ("lm_head", (m["vocab"], h), "mat"),
+    ]
+    for l in range(m["num_layers"]):
+        p = f"layers.{l}."
+        specs += [
+            (p + "q_proj", (qd, h), "mat"),
+            (p + "k_proj", (kvd, h), "mat"),
+            (p + "v_proj", (kvd, h), "mat"),
+            (p + "o_proj", (h, qd), "mat"),
+            (p + "q_norm", (hd,), "norm"),
+            (p + "k_norm", (hd,), "norm"),
+            (p + "input_layernorm", (h,), "norm"),
+            (p + "post_attention_layernorm", (h,), "norm"),
+            (p + "gate_proj", (ff, h), "mat"),
+            (p + "up_proj", (ff, h), "mat"),
+            (p + "down_proj", (h, ff), "mat"),
+        ]
+    return specs
+
+
+def gen_weight(m: dict, seed: int, name: str) -> np.ndarray:
+    for i, (n, shape, kind) in enumerate(weight_specs(m)):
+        if n == name:
+            g = rng(seed, S_WEIGHTS, i)
+            if kind == "mat":
+                return _normal_bf16(g, shape, 0.0, 0.02)
+            return _normal_bf16(g, shape, 1.0, 0.02)
+    raise KeyError(name)
+
+
+def gen_weights(m: dict, seed: int) -> dict:
+    return {n: gen_weight(m, seed, n) for n, _, _ in weight_specs(m)}
+
+
+def gen_hidden(m: dict, seed: int, n_rows: int, index: int = 0) -> np.ndarray:
+    """Tapped target hidden states, [n_rows, num_taps * target_hidden] bf16 bits."""
+    return _normal_bf16(rng(seed, S_HIDDEN, index), (n_rows, m["num_taps"] * m["target_hidden"]), 0.0, 1.0)
+
+
+def gen_bonus(m: dict, seed: int, n: int, index: int = 0) -> np.ndarray:
+    return rng(seed, S_BONUS, index).integers(0, m["vocab"], size=n, dtype=np.int64).astype(np.int32)
+
+
+def gen_ctx_lengths(lo: int, hi: int, n: int, seed: int) -> np.ndarray:
+    return rng(seed, S_CTXLEN).integers(lo, hi + 1, size=n, dtype=np.int64).astype(np.int32)
+
+
+def gen_page_order(n_allocatable: int, seed: int) -> np.ndarray:
+    """A seeded permutation of page ids 1..n_allocatable (page 0 is never handed out)."""
+    return (rng(seed, S_PAGES).permutation(n_allocatable) + 1).astype(np.int32)
+
+
+def gen_positions_gapped(start: int, n: int, seed: int, index: int = 0, max_gap: int = 3) -> np.ndarray:
+    """Strictly increasing stamped positions with random gaps in 1..max_gap."""
+    gaps = rng(seed, S_POS, index).integers(1, max_gap + 1, size=n, dtype=np.int64)
+    return (start + np.cumsum(gaps) - gaps[0]).astype(np.int32)

@@ -1,0 +1,524 @@
+"""Pins for the CPU oracle: closed forms, textbook identities, brute force on tiny
+inputs and invariants of the method. None of these re-runs the oracle's own formula
+through the same code; each would fail on a plausible mistake in it (a dropped term, a
+wrong sign or index, a transposed operand, an offset-form norm, interleaved RoPE pairs,
+a wrong GQA head map, a causal mask, a wrong lm_head row)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import dflash_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- bf16 widening
+
+def test_widen_known_bit_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x4049, 0x7F7F], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0078125, 0.0, -0.0, 3.140625, 3.3895313892515355e38]
+    got = O.widen(bits)
+    assert got.tolist() == want
+
+
+def test_bf16_rounding_of_generator_is_rne():
+    # 1 + 2^-8 lies exactly between two bf16 values; RNE keeps the even one (1.0)
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.5], dtype=np.float32)
+    assert synth.f32_to_bf16_bits(x).tolist() == [0x3F80, 0x3F82, 0xBFC0]
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rms_norm_hand_value_and_vanilla_form():
+    x = np.array([[3.0, 4.0]])
+    w = np.array([2.0, 1.0])
+    y = O.rms_norm(x, w, 0.0)
+    r = math.sqrt((9 + 16) / 2)
+    assert np.allclose(y, [[6 / r, 4 / r]], rtol=0, atol=1e-15)
+
+
+def test_rms_norm_closed_form_unit_weight():
+    g = np.random.default_rng(0)
+    x = g.standard_normal((7, 64)) * 0.01
+    eps = 1e-6
+    y = O.rms_norm(x, np.ones(64), eps)
+    ms = np.mean(x * x, axis=1)
+    assert np.allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-12)
+
+
+def test_rms_norm_is_not_offset_form():
+    # with w ~ 1 + N(0, 0.02) the vanilla form keeps output RMS ~ 1; the offset form
+    # x * (1 + w) would give ~ 2
+    g = np.random.default_rng(1)
+    x = g.standard_normal((4, 512))
+    w = 1 + 0.02 * g.standard_normal(512)
+    y = O.rms_norm(x, w, 1e-6)
+    rms = np.sqrt(np.mean(y * y, axis=1))
+    assert np.all(np.abs(rms - 1.0) < 0.01)
+
+
+# ---------------------------------------------------------------- RoPE / YaRN
+
+def test_inv_freq_plain_closed_form():
+    f = O.inv_freq_plain(1e6, 128)
+    assert f.shape == (64,)
+    assert f[0] == 1.0
+    assert math.isclose(f[1], 10 ** (-6 / 64), rel_tol=1e-14)
+    assert math.isclose(f[63], 1e6 ** (-126 / 128), rel_tol=1e-14)
+
+
+def test_rope_hand_example():
+    # hd = 4, theta = 100 -> inv_freq = [1, 0.1]; pairs (0, 2) and (1, 3)
+    x = np.array([1.0, 0.0, 0.0, 1.0])
+    y = O.rope_neox(x[None], np.array([1]), O.inv_freq_plain(100.0, 4))[0]
+    want = [math.cos(1), -math.sin(0.1), math.sin(1), math.cos(0.1)]
+    assert np.allclose(y, want, atol=1e-15)
+
+
+def test_rope_equals_complex_rotation_of_half_pairs():
+    # textbook: rotate-half RoPE multiplies z_j = x_j + i x_{j+d/2} by exp(i pos w_j)
+    g = np.random.default_rng(2)
+    d = 16
+    x = g.standard_normal((5, d))
+    pos = np.array([0, 1, 7, 1000, 34815])
+    w = O.inv_freq_plain(1e6, d)
+    y = O.rope_neox(x, pos, w)
+    z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * pos[:, None] * w[None, :])
+    assert np.allclose(y[:, : d // 2], z.real, atol=1e-12)
+    assert np.allclose(y[:, d // 2:], z.imag, atol=1e-12)
+
+
+def test_rope_norm_and_relative_angle():
+    g = np.random.default_rng(3)
+    d = 32
+    a, b = g.standard_normal(d), g.standard_normal(d)
+    w = O.inv_freq_plain(1e4, d)
+    ra = O.rope_neox(a[None], np.array([37]), w)[0]
+    rb = O.rope_neox(b[None], np.array([101]), w)[0]
+    assert math.isclose(np.linalg.norm(ra), np.linalg.norm(a), rel_tol=1e-13)
+    # <R(p)a, R(q)b> = <a, R(q - p) b>
+    rb2 = O.rope_neox(b[None], np.array([101 - 37]), w)[0]
+    assert math.isclose(ra @ rb, a @ rb2, rel_tol=1e-11, abs_tol=1e-12)
+
+
+def test_yarn_constants_match_golden():
+    gd = json.load(open(os.path.join(GOLD, "yarn_wide_drafter.json")))
+    low, high = O.yarn_bounds(gd["head_dim"], gd["rope_theta"], gd["factor"], gd["orig"],
+                              gd["beta_fast"], gd["beta_slow"])
+    assert (low, high) == (gd["low"], gd["high"])
+    assert math.isclose(O.yarn_mscale(gd["factor"]), gd["mscale"], rel_tol=1e-15)
+    f = O.inv_freq_yarn(gd["head_dim"], gd["rope_theta"], gd["factor"], gd["orig"],
+                        gd["beta_fast"], gd["beta_slow"])
+    base = np.array([1e6 ** (-j / 64) for j in range(64)])
+    # pairs at or below `low` keep the plain frequency, pairs at or above `high` are
+    # divided by the factor, and the ramp between is linear in j
+    assert np.allclose(f[:18], base[:18], rtol=1e-14)
+    assert np.allclose(f[34:], base[34:] / 32.0, rtol=1e-14)
+    j = 25
+    r = (j - 17) / 17
+    assert math.isclose(f[j], base[j] * (1 - r) + base[j] / 32 * r, rel_tol=1e-14)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_brute(q, qp, k, v, kp, scale, window):
+    T, nh, d = q.shape
+    Tk, nkv, _ = k.shape
+    G = nh // nkv
+    out = np.zeros_like(q)
+    for i in range(T):
+        for h in range(nh):
+            kh = h // G
+            s = []
+            for j in range(Tk):
+                if window > 0 and not (qp[i] - kp[j] < window):
+                    continue
+                s.append((j, sum(q[i, h, t] * k[j, kh, t] for t in range(d)) * scale))
+            mx = max(val for _, val in s)
+            den = sum(math.exp(val - mx) for _, val in s)
+            for j, val in s:
+                out[i, h, :] += math.exp(val - mx) / den * v[j, kh, :]
+    return out
+
+
+@pytest.mark.parametrize("window", [0, 3])
+def test_attention_brute_force(window):
+    g = np.random.default_rng(4)
+    q = g.standard_normal((3, 4, 5))
+    k = g.standard_normal((7, 2, 5))
+    v = g.standard_normal((7, 2, 5))
+    qp = np.array([5, 6, 7])
+    kp = np.array([0, 1, 2, 3, 5, 6, 7])
+    a = O.gqa_attention(q, qp, k, v, kp, 0.4, window)
+    b = _attn_brute(q, qp, k, v, kp, 0.4, window)
+    assert np.allclose(a, b, atol=1e-13)
+
+
+def test_attention_single_key_and_zero_query():
+    g = np.random.default_rng(5)
+    k = g.standard_normal((6, 1, 4))
+    v = g.standard_normal((6, 1, 4))
+    # single visible key (window 1 and only key 5 shares the query's position) -> its V
+    q = g.standard_normal((1, 2, 4))
+    a = O.gqa_attention(q, np.array([9]), k, v, np.array([0, 1, 2, 3, 4, 9]), 1.0, 1)
+    assert np.allclose(a[0, 0], v[5, 0]) and np.allclose(a[0, 1], v[5, 0])
+    # zero query -> uniform weights -> mean of V
+    a = O.gqa_attention(np.zeros((1, 1, 4)), np.array([0]), k, v, np.arange(6), 1.0, 0)
+    assert np.allclose(a[0, 0], v[:, 0].mean(axis=0))
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    g = np.random.default_rng(6)
+    nh, nkv, d = 8, 2, 6
+    q = g.standard_normal((4, nh, d))
+    k = g.standard_normal((9, nkv, d))
+    v = g.standard_normal((9, nkv, d))
+    qp, kp = np.arange(4) + 9, np.arange(9)
+    a = O.gqa_attention(q, qp, k, v, kp, 0.3, 0)
+    kr, vr = np.repeat(k, nh // nkv, axis=1), np.repeat(v, nh // nkv, axis=1)
+    b = O.gqa_attention(q, qp, kr, vr, kp, 0.3, 0)
+    assert np.allclose(a, b, atol=1e-14)
+    # and each head is plain single-head attention against its group's kv head
+    for h in range(nh):
+        c = O.gqa_attention(q[:, h:h + 1], qp, k[:, h // 4:h // 4 + 1], v[:, h // 4:h // 4 + 1], kp, 0.3, 0)
+        assert np.allclose(a[:, h], c[:, 0], atol=1e-14)
+
+
+def test_window_equals_truncation():
+    g = np.random.default_rng(7)
+    q = g.standard_normal((4, 2, 8))
+    k = g.standard_normal((30, 1, 8))
+    v = g.standard_normal((30, 1, 8))
+    kp = np.arange(30)
+    qp = np.array([26, 27, 28, 29])
+    W = 10
+    a = O.gqa_attention(q, qp, k, v, kp, 0.35, W)
+    for i in range(4):
+        keep = kp > qp[i] - W
+        b = O.gqa_attention(q[i:i + 1], qp[i:i + 1], k[keep], v[keep], kp[keep], 0.35, 0)
+        assert np.allclose(a[i], b[0], atol=1e-14)
+
+
+def test_attention_is_non_causal():
+    # a key placed after the query still contributes
+    q = np.ones((1, 1, 2))
+    k = np.array([[[0.0, 0.0]], [[5.0, 5.0]]])
+    v = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    a = O.gqa_attention(q, np.array([0]), k, v, np.array([0, 1]), 1.0, 0)
+    assert a[0, 0, 1] > 0.99
+
+
+# ---------------------------------------------------------------- silu / argmax
+
+def test_silu_and_argmax():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert math.isclose(O.silu(np.array([1.0]))[0], 1 / (1 + math.exp(-1)), rel_tol=1e-15)
+    assert math.isclose(O.silu(np.array([40.0]))[0], 40.0, rel_tol=1e-15)
+    assert O.argmax_lowest(np.array([[1.0, 3.0, 3.0, 2.0]]))[0] == 1
+
+
+# ---------------------------------------------------------------- the page model
+
+def test_pool_sizing_golden():
+    gd = json.load(open(os.path.join(GOLD, "pool_sizing.json")))
+    for c in gd["cases"]:
+        assert O.pool_pages(c["max_seq_len"], c["gamma"], c["max_batch"]) == (c["per_seq"], c["pool"])
+
+
+def test_page_model_brute_force():
+    order = synth.gen_page_order(O.pool_pages(64, 16, 2)[1] - 1, 9)
+    p = O.PagePool(64, 16, 2, order)
+    assert p.num_pages == 13 and sorted(p.free) == list(range(1, 13))
+    p.ensure(0, 20)          # 2 pages
+    p.ensure(1, 5)           # 1 page
+    p.ensure(0, 33)          # 1 more
+    assert p.bt[0] == list(order[:2]) + [order[3]] and p.bt[1] == [order[2]]
+    sl = p.slots(0, [0, 15, 16, 32])
+    bt = p.bt[0]
+    assert sl.tolist() == [bt[0] * 16, bt[0] * 16 + 15, bt[1] * 16, bt[2] * 16]
+    assert sl.dtype == np.int64
+    # slots of distinct positions never collide, and never touch page 0
+    allsl = np.concatenate([p.slots(0, range(48)), p.slots(1, range(16))])
+    assert len(set(allsl.tolist())) == 64 and allsl.min() >= 16
+    freed = list(p.bt[0])
+    p.reset(0)
+    assert p.free[-3:] == freed and p.bt[0] == []
+    with pytest.raises(O.PoolError):
+        p.ensure(1, 16 * 20)
+
+
+# ---------------------------------------------------------------- the drafter
+
+def _micro_model(**kw):
+    m = dict(num_layers=1, hidden=8, num_q_heads=4, num_kv_heads=2, head_dim=4,
+             intermediate=6, vocab=11, num_taps=2, target_hidden=5, gamma_max=3,
+             mask_token_id=4, rms_eps=1e-6, rope_theta=100.0, rope_type="plain",
+             sliding_window=0, layer_sliding=None)
+    m.update(kw)
+    return m
+
+
+def _micro_brute(m, Wf, taps, ctx_pos, bonus, q_pos, gamma):
+    """Scalar-loop re-derivation of the micro drafter from the definitions:
+    y[o] = sum_k W[o][k] x[k] for every [out, in] weight, rotate-half RoPE as a complex
+    rotation, softmax attention over (context keys, block keys)."""
+    h, nh, nkv, d, ff = m["hidden"], m["num_q_heads"], m["num_kv_heads"], m["head_dim"], m["intermediate"]
+    eps = m["rms_eps"]
+    G = nh // nkv
+
+    def lin(W, x):
+        return [sum(W[o][k] * x[k] for k in range(len(x))) for o in range(len(W))]
+
+    def norm(x, w):
+        r = math.sqrt(sum(t * t for t in x) / len(x) + eps)
+        return [x[i] / r * w[i] for i in range(len(x))]
+
+    def rope(x, p):
+        half = d // 2
+        out = list(x)
+        for j in range(half):
+            a = p * m["rope_theta"] ** (-2.0 * j / d)
+            z = complex(x[j], x[j + half]) * complex(math.cos(a), math.sin(a))
+            out[j], out[j + half] = z.real, z.imag
+        return out
+
+    L = Wf
+    # context features and keys
+    ctx = []
+    for r in range(len(taps)):
+        f = norm(lin(L["fc"], list(taps[r])), L["hidden_norm"])
+        ctx.append(f)
+    layers_kv = []
+    for l in range(m["num_layers"]):
+        p = f"layers.{l}."
+        ks, vs = [], []
+        for r, f in enumerate(ctx):
+            kr = lin(L[p + "k_proj"], f)
+            vr = lin(L[p + "v_proj"], f)
+            ks.append([rope(norm(kr[g * d:(g + 1) * d], L[p + "k_norm"]), ctx_pos[r]) for g in range(nkv)])
+            vs.append([vr[g * d:(g + 1) * d] for g in range(nkv)])
+        layers_kv.append((ks, vs))
+    toks = [bonus] + [m["mask_token_id"]] * (gamma - 1)
+    x = [list(L["embed_tokens"][t]) for t in toks]
+    bpos = [q_pos + i for i in range(gamma)]
+    for l in range(m["num_layers"]):
+        p = f"layers.{l}."
+        xn = [norm(r, L[p + "input_layernorm"]) for r in x]
+        qs = [lin(L[p + "q_proj"], r) for r in xn]
+        kb = [lin(L[p + "k_proj"], r) for r in xn]
+        vb = [lin(L[p + "v_proj"], r) for r in xn]
+        qh = [[rope(norm(qs[i][hh * d:(hh + 1) * d], L[p + "q_norm"]), bpos[i]) for hh in range(nh)] for i in range(gamma)]
+        kbh = [[rope(norm(kb[i][g * d:(g + 1) * d], L[p + "k_norm"]), bpos[i]) for g in range(nkv)] for i in range(gamma)]
+        vbh = [[vb[i][g * d:(g + 1) * d] for g in range(nkv)] for i in range(gamma)]
+        ks = layers_kv[l][0] + kbh
+        vs = layers_kv[l][1] + vbh
+        new_x = []
+        for i in range(gamma):
+            att = []
+            for hh in range(nh):
+                g = hh // G
+                sc = [sum(qh[i][hh][t] * ks[j][g][t] for t in range(d)) / math.sqrt(d) for j in range(len(ks))]
+                mx = max(sc)
+                e = [math.exp(s - mx) for s in sc]
+                z = sum(e)
+                att += [sum(e[j] / z * vs[j][g][t] for j in range(len(ks))) for t in range(d)]
+            o = lin(L[p + "o_proj"], att)
+            x1 = [x[i][t] + o[t] for t in range(h)]
+            n1 = norm(x1, L[p + "post_attention_layernorm"])
+            gg = lin(L[p + "gate_proj"], n1)
+            uu = lin(L[p + "up_proj"], n1)
+            a = [gg[t] / (1 + math.exp(-gg[t])) * uu[t] for t in range(ff)]
+            dn = lin(L[p + "down_proj"], a)
+            new_x.append([x1[t] + dn[t] for t in range(h)])
+        x = new_x
+    y = [norm(r, L["norm"]) for r in x]
+    return [lin(L["lm_head"], y[i]) for i in range(1, gamma)]
+
+
+def test_micro_drafter_brute_force():
+    """Non-square micro shapes so that any transposed weight or wrong head slicing fails."""
+    m = _micro_model()
+    W = synth.gen_weights(m, 77)
+    # inflate the weights so that every term matters at fp64 precision
+    Wbig = {}
+    for k, v in W.items():
+        a = O.widen(v)
+        Wbig[k] = synth.f32_to_bf16_bits((a if a.ndim == 1 else a * 25.0).astype(np.float32))
+    taps = synth.gen_hidden(m, 77, 5)
+    ctx_pos = np.array([0, 1, 2, 4, 7])
+    eng = O.Engine(m, Wbig, max_seq_len=16, max_batch=1)
+    eng.ctx_kv_append(0, taps, positions=ctx_pos)
+    res = eng.block_forward([0], [9], q_rope_pos=[8], gamma=3)
+    Wf = {k: O.widen(v).tolist() for k, v in Wbig.items()}
+    want = _micro_brute(m, Wf, O.widen(taps).tolist(), ctx_pos.tolist(), 9, 8, 3)
+    assert np.allclose(res["logits"][0], np.array(want), rtol=1e-10, atol=1e-10)
+    assert res["tokens"][0].tolist() == np.argmax(np.array(want), axis=1).tolist()
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    m = synth.model("tiny-L2-h256")
+    W = synth.gen_weights(m, 1001)
+    return m, W
+
+
+def _engine_with_ctx(m, W, n=64, seed=1001, positions=None, **kw):
+    eng = O.Engine(m, W, max_seq_len=kw.pop("max_seq_len", 128), max_batch=kw.pop("max_batch", 1), **kw)
+    eng.ctx_kv_append(0, synth.gen_hidden(m, seed, n), positions=positions)
+    return eng
+
+
+def test_position_shift_invariance_plain(tiny):
+    m, W = tiny
+    e1 = _engine_with_ctx(m, W)
+    e2 = _engine_with_ctx(m, W, positions=np.arange(64) + 5000)
+    a = e1.block_forward([0], [17], gamma=16)
+    b = e2.block_forward([0], [17], q_rope_pos=[5064], gamma=16)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-9)
+
+
+def test_position_shift_invariance_yarn_and_window(tiny):
+    m, W = tiny
+    m = dict(m, rope_type="yarn", yarn_factor=4.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,
+             yarn_beta_slow=1.0, sliding_window=24, layer_sliding=[True, False])
+    e1 = _engine_with_ctx(m, W)
+    e2 = _engine_with_ctx(m, W, positions=np.arange(64) + 777)
+    a = e1.block_forward([0], [3], gamma=16)
+    b = e2.block_forward([0], [3], q_rope_pos=[777 + 64], gamma=16)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-9)
+    # and a yarn drafter is not the plain one
+    c = _engine_with_ctx(dict(m, rope_type="plain"), W).block_forward([0], [3], gamma=16)
+    assert np.abs(a["logits"] - c["logits"]).max() > 1e-3
+
+
+def test_non_causal_permutation(tiny):
+    """Permuting block rows 1..T-1 together with their positions permutes the outputs."""
+    m, W = tiny
+    e = _engine_with_ctx(m, W)
+    s = e.seqs[0]
+    toks = np.array([17] + [m["mask_token_id"]] * 15)
+    bpos = 64 + np.arange(16)
+    y = e.d.block_hidden(s["k"], s["v"], s["pos"], toks, bpos)
+    perm = np.concatenate([[0], 1 + np.random.default_rng(8).permutation(15)])
+    yp = e.d.block_hidden(s["k"], s["v"], s["pos"], toks[perm], bpos[perm])
+    assert np.allclose(yp, y[perm], atol=1e-11)
+    # all block rows at one position: the 15 mask rows are identical
+    ye = e.d.block_hidden(s["k"], s["v"], s["pos"], toks, np.full(16, 70))
+    assert np.allclose(ye[1:], ye[1], atol=1e-12)
+    assert np.abs(ye[0] - ye[1]).max() > 1e-3
+
+
+def test_window_layer_equals_full_when_window_covers_all(tiny):
+    m, W = tiny
+    mw = dict(m, sliding_window=64 + 16, layer_sliding=[True, True])
+    a = _engine_with_ctx(m, W).block_forward([0], [5], gamma=16)
+    b = _engine_with_ctx(mw, W).block_forward([0], [5], gamma=16)
+    assert np.allclose(a["logits"], b["logits"], atol=1e-12)
+    mw2 = dict(m, sliding_window=20, layer_sliding=[True, True])
+    c = _engine_with_ctx(mw2, W).block_forward([0], [5], gamma=16)
+    assert np.abs(a["logits"] - c["logits"]).max() > 1e-4
+
+
+def test_chunked_append_equals_one_shot(tiny):
+    m, W = tiny
+    H = synth.gen_hidden(m, 1001, 64)
+    e1 = O.Engine(m, W, 128, 1)
+    e1.ctx_kv_append(0, H)
+    e2 = O.Engine(m, W, 128, 1)
+    e2.ctx_kv_append(0, H[:23])
+    e2.ctx_kv_append(0, H[23:])
+    for l in range(m["num_layers"]):
+        assert np.allclose(e1.seqs[0]["k"][l], e2.seqs[0]["k"][l], atol=1e-13)
+        assert np.allclose(e1.seqs[0]["v"][l], e2.seqs[0]["v"][l], atol=1e-13)
+    assert e1.block_table(0) == e2.block_table(0)
+
+
+def test_bands_are_independent(tiny):
+    m, W = tiny
+    e = O.Engine(m, W, 128, 3, page_order=synth.gen_page_order(O.pool_pages(128, 16, 3)[1] - 1, 4))
+    for s, n in [(0, 40), (1, 17), (2, 64)]:
+        e.ctx_kv_append(s, synth.gen_hidden(m, 1001 + s, n))
+    both = e.block_forward([2, 0, 1], [7, 8, 9], gamma=12)
+    for i, (s, b) in enumerate([(2, 7), (0, 8), (1, 9)]):
+        one = e.block_forward([s], [b], gamma=12)
+        assert np.array_equal(one["logits"][0], both["logits"][i])
+
+
+def test_lm_head_planted_argmax(tiny):
+    m, W = tiny
+    e = _engine_with_ctx(m, W)
+    res = e.block_forward([0], [11], gamma=16, want_hidden=True)
+    y = res["hidden"][0]
+    W2 = dict(W)
+    lm = O.widen(W["lm_head"]).copy()
+    planted = {1: 901, 5: 3, 15: 1023}
+    for row, tok in planted.items():
+        lm[tok] = y[row] * 4.0
+    W2["lm_head"] = synth.f32_to_bf16_bits(lm.astype(np.float32))
+    e2 = _engine_with_ctx(m, W2)
+    r2 = e2.block_forward([0], [11], gamma=16)
+    for row, tok in planted.items():
+        assert r2["tokens"][0][row - 1] == tok   # drafts come from rows 1..gamma-1
+
+
+def test_engine_errors_leave_state_unchanged(tiny):
+    m, W = tiny
+    e = O.Engine(m, W, 40, 2)
+    e.ctx_kv_append(0, synth.gen_hidden(m, 1, 30))
+    bt, free = e.block_table(0), list(e.pool.free)
+    with pytest.raises(O.PoolError) as ei:
+        e.ctx_kv_append(0, synth.gen_hidden(m, 1, 11))
+    assert ei.value.code == "ERANGE"
+    with pytest.raises(O.PoolError):
+        e.ctx_kv_append(0, synth.gen_hidden(m, 1, 2), positions=[5, 6])   # not increasing
+    with pytest.raises(O.PoolError):
+        e.block_forward([0, 0], [1, 2])
+    with pytest.raises(O.PoolError):
+        e.block_forward([0], [1], gamma=17)
+    with pytest.raises(O.PoolError):
+        e.block_forward([0], [1], gamma=1)
+    assert e.block_table(0) == bt and e.pool.free == free and e.kv_len(0) == 30
+
+
+def test_pool_exhaustion_is_all_or_nothing(tiny):
+    m, W = tiny
+    # an explicit 6-page pool (5 usable) shared by two sequences
+    e = O.Engine(m, W, 64, 2, num_pages=6)
+    e.ctx_kv_append(0, synth.gen_hidden(m, 1, 32))      # pages 1, 2
+    e.ctx_kv_append(1, synth.gen_hidden(m, 2, 20))      # pages 3, 4
+    assert e.pool.free == [5]
+    before = (e.block_table(0), e.block_table(1), list(e.pool.free))
+    # seq 0 needs 1 page (positions 32..47), seq 1 needs 1 (36 > 32): 2 > 1 free
+    with pytest.raises(O.PoolError) as ei:
+        e.block_forward([0, 1], [1, 2], gamma=16)
+    assert ei.value.code == "EPOOL"
+    assert (e.block_table(0), e.block_table(1), list(e.pool.free)) == before
+    with pytest.raises(O.PoolError) as ei:
+        e.ctx_kv_append(1, synth.gen_hidden(m, 3, 29))  # needs 2 pages
+    assert ei.value.code == "EPOOL" and e.kv_len(1) == 20
+    e.block_forward([0], [1], gamma=16)                # takes page 5
+    assert e.block_table(0) == [1, 2, 5] and e.pool.free == []
+    e.seq_reset(1)
+    assert e.pool.free == [3, 4] and e.kv_len(1) == 0
+    e.block_forward([1], [2], gamma=16)
+    assert e.block_table(1) == [3]
+
+
+def test_yarn_mscale_scales_cached_keys(tiny):
+    """With unit k_norm weights a normed head has norm sqrt(hd * ms / (ms + eps)); RoPE
+    preserves it, and YaRN's mscale multiplies it (memra page, rope_rows)."""
+    m, W = tiny
+    my = dict(m, rope_type="yarn", yarn_factor=8.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,
+              yarn_beta_slow=1.0)
+    W1 = dict(W)
+    for l in range(m["num_layers"]):
+        W1[f"layers.{l}.k_norm"] = np.full(m["head_dim"], 0x3F80, dtype=np.uint16)
+    for mm, scale in [(m, 1.0), (my, 0.1 * math.log(8.0) + 1.0)]:
+        e = _engine_with_ctx(mm, W1, n=9)
+        k = e.seqs[0]["k"][1]                       # [9, nkv, hd]
+        n = np.linalg.norm(k, axis=-1)
+        assert np.allclose(n, scale * math.sqrt(m["head_dim"]), rtol=1e-4)
