@@ -1,0 +1,200 @@
+"""ctypes binding of libdflash.so: the C ABI's structs and calls under the same names, plus
+a small `Drafter` wrapper that turns a config dict and torch tensors into those structs.
+Argument marshalling only: every step of the drafter runs in the HIP library. There is no
+fallback; if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+
+DFLASH_OK, DFLASH_EINVAL, DFLASH_ENOMEM, DFLASH_EPOOL, DFLASH_ERANGE, DFLASH_EHIP = 0, -1, -2, -3, -4, -5
+CODE_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EPOOL", -4: "ERANGE", -5: "EHIP"}
+DFLASH_BUF_POOL, DFLASH_BUF_KPOS, DFLASH_BUF_SLOTS, DFLASH_BUF_BLOCKTAB, DFLASH_BUF_HIDDEN = 0, 1, 2, 3, 4
+
+
+class dflash_config(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32), ("hidden", C.c_int32), ("num_q_heads", C.c_int32),
+        ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+        ("vocab", C.c_int32), ("num_taps", C.c_int32), ("target_hidden", C.c_int32),
+        ("gamma_max", C.c_int32), ("mask_token_id", C.c_int32), ("rms_eps", C.c_float),
+        ("rope_theta", C.c_double), ("rope_type", C.c_int32),
+        ("yarn_factor", C.c_double), ("yarn_orig_max_pos", C.c_double),
+        ("yarn_beta_fast", C.c_double), ("yarn_beta_slow", C.c_double),
+        ("sliding_window", C.c_int32), ("layer_sliding", C.POINTER(C.c_uint8)),
+        ("max_seq_len", C.c_int32), ("max_batch", C.c_int32), ("num_pages", C.c_int32),
+        ("page_order", C.POINTER(C.c_int32)),
+    ]
+
+
+class dflash_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "q_proj", "k_proj", "v_proj", "o_proj", "q_norm", "k_norm", "input_layernorm",
+        "post_attention_layernorm", "gate_proj", "up_proj", "down_proj")]
+
+
+class dflash_weights(C.Structure):
+    _fields_ = [("fc", C.c_void_p), ("hidden_norm", C.c_void_p), ("norm", C.c_void_p),
+                ("embed_tokens", C.c_void_p), ("lm_head", C.c_void_p),
+                ("layers", C.POINTER(dflash_layer_weights))]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m block_diffusion_draft_02_amd.build` (no fallback path exists)")
+        L = C.CDLL(_LIB_PATH)
+        vp, i32, i64p, i32p = C.c_void_p, C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int32)
+        L.dflash_create.argtypes = [C.POINTER(dflash_config), C.POINTER(dflash_weights), vp, C.POINTER(vp)]
+        L.dflash_ctx_kv_append.argtypes = [vp, i32, vp, i32p, i32, vp]
+        L.dflash_block_forward.argtypes = [vp, i32, i32p, i32p, i32p, i32, vp, vp, vp]
+        L.dflash_destroy.argtypes = [vp]
+        L.dflash_destroy.restype = None
+        L.dflash_seq_reset.argtypes = [vp, i32]
+        L.dflash_seq_info.argtypes = [vp, i32, i32p, i32p, i32p, i32]
+        L.dflash_pool_geometry.argtypes = [vp, i64p, i64p, i64p, i64p, i64p]
+        L.dflash_debug_copy.argtypes = [vp, i32, vp, C.c_size_t, C.c_size_t, vp]
+        L.dflash_last_error.argtypes = [vp]
+        L.dflash_last_error.restype = C.c_char_p
+        L.dflash_strerror.argtypes = [C.c_int]
+        L.dflash_strerror.restype = C.c_char_p
+        for f in ("dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_seq_reset",
+                  "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_destroy",
+            "dflash_seq_reset", "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy",
+            "dflash_last_error", "dflash_strerror")
+
+
+class DflashError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{CODE_NAMES.get(code, code)}: {msg}")
+        self.code = code
+        self.name = CODE_NAMES.get(code, str(code))
+
+
+def _i32_array(vals):
+    if vals is None:
+        return None
+    vals = [int(v) for v in vals]
+    return (C.c_int32 * max(1, len(vals)))(*vals)
+
+
+def make_config(m: dict, max_seq_len: int, max_batch: int, num_pages: int = 0, page_order=None):
+    """dflash_config from a model dict (the keys of synth.MODELS). Returns (struct, keepalive)."""
+    ls = m.get("layer_sliding")
+    ls_arr = (C.c_uint8 * m["num_layers"])(*[1 if x else 0 for x in ls]) if ls else None
+    po = _i32_array(page_order)
+    cfg = dflash_config(
+        num_layers=m["num_layers"], hidden=m["hidden"], num_q_heads=m["num_q_heads"],
+        num_kv_heads=m["num_kv_heads"], head_dim=m["head_dim"], intermediate=m["intermediate"],
+        vocab=m["vocab"], num_taps=m["num_taps"], target_hidden=m["target_hidden"],
+        gamma_max=m["gamma_max"], mask_token_id=m["mask_token_id"], rms_eps=m["rms_eps"],
+        rope_theta=m["rope_theta"], rope_type=1 if m.get("rope_type") == "yarn" else 0,
+        yarn_factor=m.get("yarn_factor", 0.0), yarn_orig_max_pos=m.get("yarn_orig_max_pos", 0.0),
+        yarn_beta_fast=m.get("yarn_beta_fast", 0.0), yarn_beta_slow=m.get("yarn_beta_slow", 0.0),
+        sliding_window=int(m.get("sliding_window") or 0),
+        layer_sliding=C.cast(ls_arr, C.POINTER(C.c_uint8)) if ls_arr is not None else None,
+        max_seq_len=max_seq_len, max_batch=max_batch, num_pages=num_pages,
+        page_order=C.cast(po, C.POINTER(C.c_int32)) if po is not None else None)
+    return cfg, (ls_arr, po)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(stream)
+    import torch
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Drafter:
+    """One dflash_ctx. `weights` maps the synth weight names to device bf16 torch tensors,
+    which must outlive the object."""
+
+    def __init__(self, m: dict, weights: dict, max_seq_len: int, max_batch: int,
+                 num_pages: int = 0, page_order=None, stream=None):
+        self.m = m
+        self.L = lib()
+        self.weights = weights
+        cfg, self._keep = make_config(m, max_seq_len, max_batch, num_pages, page_order)
+        nl = m["num_layers"]
+        lay = (dflash_layer_weights * nl)()
+        for l in range(nl):
+            p = f"layers.{l}."
+            for f in dflash_layer_weights._fields_:
+                setattr(lay[l], f[0], weights[p + f[0]].data_ptr())
+        w = dflash_weights(fc=weights["fc"].data_ptr(), hidden_norm=weights["hidden_norm"].data_ptr(),
+                           norm=weights["norm"].data_ptr(), embed_tokens=weights["embed_tokens"].data_ptr(),
+                           lm_head=weights["lm_head"].data_ptr(), layers=lay)
+        ctx = C.c_void_p()
+        rc = self.L.dflash_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(ctx))
+        if rc != DFLASH_OK:
+            raise DflashError(rc, "dflash_create failed")
+        self.ctx = ctx
+
+    def _check(self, rc):
+        if rc != DFLASH_OK:
+            raise DflashError(rc, self.L.dflash_last_error(self.ctx).decode())
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.L.dflash_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- the calls -------------------------------------------------------------------------
+    def dflash_ctx_kv_append(self, seq, target_hidden, positions=None, stream=None):
+        n = int(target_hidden.shape[0])
+        pos = _i32_array(positions)
+        self._check(self.L.dflash_ctx_kv_append(self.ctx, seq, _ptr(target_hidden), pos, n, _stream(stream)))
+
+    def dflash_block_forward(self, seqs, bonus, draft_tokens, logits=None, q_rope_pos=None,
+                             gamma=None, stream=None):
+        gamma = self.m["gamma_max"] if gamma is None else gamma
+        s, b, q = _i32_array(seqs), _i32_array(bonus), _i32_array(q_rope_pos)
+        self._check(self.L.dflash_block_forward(
+            self.ctx, len(seqs), s, b, q, gamma, _ptr(draft_tokens),
+            _ptr(logits) if logits is not None else None, _stream(stream)))
+
+    def dflash_seq_reset(self, seq):
+        self._check(self.L.dflash_seq_reset(self.ctx, seq))
+
+    def dflash_seq_info(self, seq, cap=1 << 16):
+        kv, npg = C.c_int32(), C.c_int32()
+        bt = (C.c_int32 * cap)()
+        self._check(self.L.dflash_seq_info(self.ctx, seq, C.byref(kv), C.byref(npg), bt, cap))
+        return kv.value, list(bt[: npg.value])
+
+    def dflash_pool_geometry(self):
+        vals = [C.c_int64() for _ in range(5)]
+        self._check(self.L.dflash_pool_geometry(self.ctx, *[C.byref(v) for v in vals]))
+        keys = ("num_pages", "pages_per_seq", "page_layer_bytes", "pool_bytes", "fused_kv_weight_bytes")
+        return dict(zip(keys, [v.value for v in vals]))
+
+    def dflash_debug_copy(self, buffer, dst, offset=0, nbytes=None, stream=None):
+        """Copy into a torch tensor (host or device) `dst`; nbytes defaults to dst's size."""
+        nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+        self._check(self.L.dflash_debug_copy(self.ctx, buffer, C.c_void_p(dst.data_ptr()), offset, nbytes,
+                                             _stream(stream)))

@@ -1,0 +1,85 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 storage, 16-byte vector loads,
+// the 16x16x32 bf16 MFMA and wavefront reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+typedef uint16_t bf16;  // storage type: raw IEEE bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  u32x4 u;
+  u[0] = pack2(v[0], v[1]);
+  u[1] = pack2(v[2], v[3]);
+  u[2] = pack2(v[4], v[5]);
+  u[3] = pack2(v[6], v[7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// D(16x16) += A(16x32) * B(32x16). Lane l holds A row (l%16) and B column (l%16), each
+// 8 consecutive k-values of group (l/16); it receives D rows 4*(l/16)+i, column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// block-wide sum for blockDim.x == 256 (4 waves); `red` is 4 floats of shared memory
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// NeoX rotation of the pair (x1, x2) = (x[j], x[j + d/2]) by pos * inv_freq[j]. The angle
+// and its sine/cosine are taken in double precision: positions reach tens of thousands,
+// where a float angle would be off by ~1e-3 rad.
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, int pos, double inv_freq) {
+  double s, c;
+  sincos((double)pos * inv_freq, &s, &c);
+  const float cf = (float)c, sf = (float)s;
+  const float y1 = x1 * cf - x2 * sf;
+  const float y2 = x2 * cf + x1 * sf;
+  x1 = y1;
+  x2 = y2;
+}
+
+}  // namespace dfl

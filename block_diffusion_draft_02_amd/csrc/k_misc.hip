@@ -1,0 +1,296 @@
+// Row-wise kernels of the drafter: the forward prologue (block-table updates, block-row
+// slots, embedding gather + first input RMSNorm), the Q/K/V epilogue (per-head RMSNorm,
+// RoPE, YaRN mscale, K/V writeback into the paged pool), residual add + RMSNorm, SwiGLU,
+// and the context-append kernels (slots, hidden_norm, context K/V writeback).
+//
+// Arithmetic follows memra_engine/dflash.rs (DflashDraft::forward_round, ::ingest_ctx,
+// ::ctx_features, ::rope_rows): vanilla RMSNorm x * w / sqrt(mean(x^2) + eps) (the form
+// spark_model/layers/dflash_head/from_weights.rs picks for the drafter), NeoX RoPE over
+// the whole head, mscale multiplied into q and k after the rotation under YaRN.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dfl {
+
+// ---- forward prologue ------------------------------------------------------------------
+// workgroup 0: block-table updates, slots and stamped positions of the block rows, band
+// table; workgroup 1 + r: embedding row of block row r and its input RMSNorm of layer 0.
+__global__ __launch_bounds__(256) void k_fwd_prologue(FwdArgs a, Band* __restrict__ bands_dev,
+                                                      int* __restrict__ bt,
+                                                      long long* __restrict__ slots,
+                                                      int* __restrict__ kpos,
+                                                      const bf16* __restrict__ embed,
+                                                      const bf16* __restrict__ w_in0, int h,
+                                                      float eps, float* __restrict__ X,
+                                                      bf16* __restrict__ Xn) {
+  __shared__ float red[4];
+  if (blockIdx.x == 0) {
+    for (int j = threadIdx.x; j < a.n_upd; j += 256) bt[a.upd_off[j]] = a.upd_page[j];
+    const int M = a.n_bands * a.gamma;
+    for (int r = threadIdx.x; r < M; r += 256) {
+      const int b = r / a.gamma, i = r % a.gamma;
+      const int C = a.bands[b].kv_len;
+      const int p = C + i;
+      const int lp = (p >> 4) - (C >> 4);
+      const long long slot = (long long)a.bands[b].pg[lp] * PAGE + (p & (PAGE - 1));
+      slots[r] = slot;
+      kpos[slot] = a.bands[b].q_pos + i;
+    }
+    for (int b = threadIdx.x; b < a.n_bands; b += 256) bands_dev[b] = a.bands[b];
+    return;
+  }
+  const int r = blockIdx.x - 1;
+  const int b = r / a.gamma, i = r % a.gamma;
+  const int tok = (i == 0) ? a.bands[b].bonus : a.mask_token;
+  const bf16* e = embed + (size_t)tok * h;
+  float* x = X + (size_t)r * h;
+  float ss = 0.f;
+  for (int j = threadIdx.x; j < h; j += 256) {
+    const float v = bf2f(e[j]);
+    x[j] = v;
+    ss += v * v;
+  }
+  ss = block_sum256(ss, red);
+  const float rs = rsqrtf(ss / (float)h + eps);
+  bf16* xn = Xn + (size_t)r * h;
+  for (int j = threadIdx.x; j < h; j += 256) xn[j] = f2bf(x[j] * rs * bf2f(w_in0[j]));
+}
+
+hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
+                               int* kpos, const bf16* embed, const bf16* w_in0, int h,
+                               float eps, float* X, bf16* Xn, hipStream_t st) {
+  const int M = a.n_bands * a.gamma;
+  k_fwd_prologue<<<1 + M, 256, 0, st>>>(a, bands_dev, bt, slots, kpos, embed, w_in0, h, eps, X, Xn);
+  return hipGetLastError();
+}
+
+// ---- Q/K/V epilogue ---------------------------------------------------------------------
+// one wavefront per (row, head) of the fused [q | k | v] projection; lane l < hd/2 owns the
+// RoPE pair (l, l + hd/2)
+template <int HD>
+__global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, int S,
+                                                 long long ps, int N, int gamma,
+                                                 const Band* __restrict__ bands, int nh, int nkv,
+                                                 const bf16* __restrict__ qn,
+                                                 const bf16* __restrict__ kn, float eps,
+                                                 const double* __restrict__ inv_freq,
+                                                 float mscale, const long long* __restrict__ slots,
+                                                 KvGeom g, int layer, bf16* __restrict__ Q) {
+  constexpr int H2 = HD / 2;
+  const int r = blockIdx.x, hh = blockIdx.y, l = threadIdx.x;
+  const bool act = l < H2;
+  const int col = hh * HD + (act ? l : 0);
+  float x1 = 0.f, x2 = 0.f;
+  if (act) {
+    const float* p = P + (size_t)r * N + col;
+    for (int s = 0; s < S; ++s) {
+      x1 += p[(long long)s * ps];
+      x2 += p[(long long)s * ps + H2];
+    }
+  }
+  const int kind = hh < nh ? 0 : (hh < nh + nkv ? 1 : 2);
+  if (kind != 2) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float rs = rsqrtf(ss / (float)HD + eps);
+    if (act) {
+      const bf16* w = kind == 0 ? qn : kn;
+      x1 *= rs * bf2f(w[l]);
+      x2 *= rs * bf2f(w[l + H2]);
+      const int b = r / gamma, i = r % gamma;
+      rope_pair(x1, x2, bands[b].q_pos + i, inv_freq[l]);
+      x1 *= mscale;
+      x2 *= mscale;
+    }
+  }
+  if (!act) return;
+  if (kind == 0) {
+    bf16* q = Q + ((size_t)r * nh + hh) * HD;
+    q[l] = f2bf(x1);
+    q[l + H2] = f2bf(x2);
+    return;
+  }
+  const long long slot = slots[r];
+  const long long page = slot >> 4;
+  const int off = (int)(slot & (PAGE - 1));
+  bf16* pg = g.pool + ((size_t)layer * g.num_pages + page) * page_layer_elems(g.nkv, HD);
+  if (kind == 1) {
+    bf16* k = pg + ((size_t)(hh - nh) * PAGE + off) * HD;
+    k[l] = f2bf(x1);
+    k[l + H2] = f2bf(x2);
+  } else {
+    bf16* v = pg + (size_t)(g.nkv + hh - nh - nkv) * HD * PAGE + off;
+    v[(size_t)l * PAGE] = f2bf(x1);
+    v[(size_t)(l + H2) * PAGE] = f2bf(x2);
+  }
+}
+
+hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
+                           const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
+                           const bf16* k_norm, float eps, const double* inv_freq, float mscale,
+                           const long long* slots, KvGeom g, int layer, bf16* Q, hipStream_t st) {
+  const int N = (nh + 2 * nkv) * hd;
+  dim3 grid(M, nh + 2 * nkv);
+  switch (hd) {
+    case 32: k_qkv_post<32><<<grid, 64, 0, st>>>(P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q); break;
+    case 64: k_qkv_post<64><<<grid, 64, 0, st>>>(P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q); break;
+    case 128: k_qkv_post<128><<<grid, 64, 0, st>>>(P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---- residual add + RMSNorm ---------------------------------------------------------------
+// X[r] += sum_s P[s][r]; Xn[r] = bf16(RMSNorm_w(X[r]))
+__global__ __launch_bounds__(256) void k_resid_norm(float* __restrict__ X, const float* __restrict__ P,
+                                                    int S, long long ps, int h,
+                                                    const bf16* __restrict__ w, float eps,
+                                                    bf16* __restrict__ Xn) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  float* x = X + (size_t)r * h;
+  const float* p = P + (size_t)r * h;
+  float ss = 0.f;
+  for (int j = threadIdx.x; j < h; j += 256) {
+    float v = x[j];
+    for (int s = 0; s < S; ++s) v += p[(long long)s * ps + j];
+    x[j] = v;
+    ss += v * v;
+  }
+  ss = block_sum256(ss, red);
+  const float rs = rsqrtf(ss / (float)h + eps);
+  bf16* xn = Xn + (size_t)r * h;
+  for (int j = threadIdx.x; j < h; j += 256) xn[j] = f2bf(x[j] * rs * bf2f(w[j]));
+}
+
+hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
+                             int h, const bf16* w, float eps, bf16* Xn, hipStream_t st) {
+  k_resid_norm<<<M, 256, 0, st>>>(X, P, S, part_stride, h, w, eps, Xn);
+  return hipGetLastError();
+}
+
+// ---- SwiGLU -----------------------------------------------------------------------------
+// the fused gate/up projection's columns are [gate (ff) | up (ff)]
+__global__ __launch_bounds__(256) void k_silu_mul(const float* __restrict__ P, int S, long long ps,
+                                                  int M, int ff, bf16* __restrict__ A) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)M * ff) return;
+  const size_t r = idx / ff, j = idx % ff;
+  const float* p = P + r * 2 * ff + j;
+  float gs = 0.f, us = 0.f;
+  for (int s = 0; s < S; ++s) {
+    gs += p[(long long)s * ps];
+    us += p[(long long)s * ps + ff];
+  }
+  A[idx] = f2bf(silu(gs) * us);
+}
+
+hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
+                           bf16* A, hipStream_t st) {
+  const size_t n = (size_t)M * ff;
+  k_silu_mul<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(P, S, part_stride, M, ff, A);
+  return hipGetLastError();
+}
+
+// ---- context append ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_append_setup(AppendArgs a, int* __restrict__ bt,
+                                                      long long* __restrict__ slots,
+                                                      int* __restrict__ rowpos,
+                                                      int* __restrict__ kpos) {
+  for (int j = threadIdx.x; j < a.n_upd; j += 256) bt[a.upd_off[j]] = a.upd_page[j];
+  for (int r = threadIdx.x; r < a.n; r += 256) {
+    const int p = a.kv_len + r;
+    const int lp = (p >> 4) - a.first_lpage;
+    const long long slot = (long long)a.pages[lp] * PAGE + (p & (PAGE - 1));
+    const int pos = a.positions ? a.positions[r] : p;
+    slots[r] = slot;
+    rowpos[r] = pos;
+    kpos[slot] = pos;
+  }
+}
+
+hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
+                               int* kpos, hipStream_t st) {
+  k_append_setup<<<1, 256, 0, st>>>(a, bt, slots, rowpos, kpos);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_rows_rmsnorm(const float* __restrict__ X, int h,
+                                                      const bf16* __restrict__ w, float eps,
+                                                      bf16* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const float* x = X + (size_t)r * h;
+  float ss = 0.f;
+  for (int j = threadIdx.x; j < h; j += 256) ss += x[j] * x[j];
+  ss = block_sum256(ss, red);
+  const float rs = rsqrtf(ss / (float)h + eps);
+  bf16* o = out + (size_t)r * h;
+  for (int j = threadIdx.x; j < h; j += 256) o[j] = f2bf(x[j] * rs * bf2f(w[j]));
+}
+
+hipError_t launch_rows_rmsnorm(const float* X, int M, int h, const bf16* w, float eps, bf16* out,
+                               hipStream_t st) {
+  k_rows_rmsnorm<<<M, 256, 0, st>>>(X, h, w, eps, out);
+  return hipGetLastError();
+}
+
+// one wavefront per (row, layer, K|V, kv head) of the fused [K0 | V0 | K1 | V1 | ...] output
+template <int HD>
+__global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__ KV, int L,
+                                                       const bf16* __restrict__ kn_all, float eps,
+                                                       const double* __restrict__ inv_freq,
+                                                       float mscale,
+                                                       const long long* __restrict__ slots,
+                                                       const int* __restrict__ rowpos, KvGeom g) {
+  constexpr int H2 = HD / 2;
+  const int r = blockIdx.x, idx = blockIdx.y, l = threadIdx.x;
+  const int nkv = g.nkv;
+  const int layer = idx / (2 * nkv), rem = idx % (2 * nkv);
+  const int kv = rem / nkv, kvh = rem % nkv;
+  const bool act = l < H2;
+  const size_t ld = (size_t)L * 2 * nkv * HD;
+  const float* src = KV + (size_t)r * ld + (size_t)idx * HD;
+  float x1 = act ? src[l] : 0.f, x2 = act ? src[l + H2] : 0.f;
+  if (kv == 0) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float rs = rsqrtf(ss / (float)HD + eps);
+    if (act) {
+      const bf16* w = kn_all + (size_t)layer * HD;
+      x1 *= rs * bf2f(w[l]);
+      x2 *= rs * bf2f(w[l + H2]);
+      rope_pair(x1, x2, rowpos[r], inv_freq[l]);
+      x1 *= mscale;
+      x2 *= mscale;
+    }
+  }
+  if (!act) return;
+  const long long slot = slots[r];
+  const long long page = slot >> 4;
+  const int off = (int)(slot & (PAGE - 1));
+  bf16* pg = g.pool + ((size_t)layer * g.num_pages + page) * page_layer_elems(nkv, HD);
+  if (kv == 0) {
+    bf16* k = pg + ((size_t)kvh * PAGE + off) * HD;
+    k[l] = f2bf(x1);
+    k[l + H2] = f2bf(x2);
+  } else {
+    bf16* v = pg + (size_t)(nkv + kvh) * HD * PAGE + off;
+    v[(size_t)l * PAGE] = f2bf(x1);
+    v[(size_t)(l + H2) * PAGE] = f2bf(x2);
+  }
+}
+
+hipError_t launch_kv_append_post(const float* KV, int n, int L, const bf16* k_norm_all,
+                                 float eps, const double* inv_freq, float mscale,
+                                 const long long* slots, const int* rowpos, KvGeom g,
+                                 hipStream_t st) {
+  dim3 grid(n, L * 2 * g.nkv);
+  switch (g.hd) {
+    case 32: k_kv_append_post<32><<<grid, 64, 0, st>>>(KV, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 64: k_kv_append_post<64><<<grid, 64, 0, st>>>(KV, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 128: k_kv_append_post<128><<<grid, 64, 0, st>>>(KV, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfl

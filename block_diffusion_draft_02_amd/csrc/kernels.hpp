@@ -1,0 +1,108 @@
+// Launch interface between the host runtime and the gfx950 kernels. Every launcher
+// enqueues on `st` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+typedef uint16_t bf16;
+
+constexpr int PAGE = 16;          // tokens per KV page
+constexpr int MAX_BANDS = 32;     // sequences in one forward call
+constexpr int MAX_CHUNKS = 32;    // split-KV chunks per (band, kv head) in attention
+constexpr int APPEND_ROWS = 2048; // context rows per append launch sequence
+constexpr int APPEND_PAGES = APPEND_ROWS / PAGE + 1;
+
+// One band (sequence) of a forward call, as the kernels see it.
+struct Band {
+  int seq;       // sequence slot
+  int kv_len;    // context rows already cached (C)
+  int q_pos;     // RoPE position of block row 0 (P)
+  int bonus;     // token of block row 0
+  int pg[2];     // physical pages of logical pages C/16 and C/16 + 1
+  // split-KV work of full-attention and of sliding-window layers: keys from kstart
+  // (page aligned) to C + gamma, `nch` chunks of `ck` keys, partial slots from `base`
+  int kstart[2], ck[2], nch[2], base[2];
+};
+
+struct FwdArgs {
+  int n_bands, gamma, mask_token, per_seq;
+  int n_upd;                   // block-table entries to write: bt[upd_off] = upd_page
+  int upd_off[2 * MAX_BANDS];
+  int upd_page[2 * MAX_BANDS];
+  Band bands[MAX_BANDS];
+};
+
+struct AppendArgs {
+  int seq, kv_len, n, per_seq;
+  int first_lpage, n_lpages;   // logical pages touched by rows kv_len..kv_len+n-1
+  int pages[APPEND_PAGES];     // their physical pages
+  int n_upd;
+  int upd_off[APPEND_PAGES];
+  int upd_page[APPEND_PAGES];
+  const int* positions;        // device int32 [n] or nullptr (kv_len + r)
+};
+
+// Geometry the attention / writeback kernels need.
+struct KvGeom {
+  bf16* pool;        // [L][num_pages][2][nkv] x (K [16][hd] | V [hd][16])
+  int* kpos;         // [num_pages * 16]
+  int* bt;           // [max_batch][per_seq]
+  long long num_pages;
+  int nkv, hd, per_seq;
+};
+
+__host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (size_t)2 * nkv * PAGE * hd; }
+
+// ---- GEMMs (k_gemm.hip) --------------------------------------------------------------
+// Y[M,N] = A[M,K] W[N,K]^T. Skinny form: partials P[s][M][N] over K splits of k_len
+// (k_len, K multiples of 128); M <= 64 per launch.
+hipError_t launch_gemm_skinny(const bf16* A, int lda, int M, const bf16* W, int N, int K,
+                              int k_len, float* P, long long part_stride, hipStream_t st);
+// Tiled form for large M: C[M,N] fp32 (ldc), K multiple of 64.
+hipError_t launch_gemm_tiled(const bf16* A, int lda, int M, const bf16* W, int N, int K,
+                             float* C, int ldc, hipStream_t st);
+// lm_head + argmax partials: for rows r0..r0+M-1 of the forward (M <= 64), best (value,
+// index) per row over each workgroup's vocabulary range; optionally the fp32 logits of
+// drafted rows (row % gamma != 0) into logits[(r/gamma)*(gamma-1) + r%gamma - 1][V].
+int lmhead_groups(int V);
+hipError_t launch_lmhead_argmax(const bf16* Y, int ldy, int M, int r0, const bf16* W, int V,
+                                int K, float* best_v, int* best_i, int n_groups, int gamma,
+                                float* logits, hipStream_t st);
+hipError_t launch_argmax_reduce(const float* best_v, const int* best_i, int n_groups,
+                                int n_bands, int gamma, int* tokens, hipStream_t st);
+
+// ---- forward elementwise (k_misc.hip) ------------------------------------------------
+hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
+                               int* kpos, const bf16* embed, const bf16* w_in0, int h,
+                               float eps, float* X, bf16* Xn, hipStream_t st);
+hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
+                           const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
+                           const bf16* k_norm, float eps, const double* inv_freq, float mscale,
+                           const long long* slots, KvGeom g, int layer, bf16* Q, hipStream_t st);
+hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
+                             int h, const bf16* w, float eps, bf16* Xn, hipStream_t st);
+hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
+                           bf16* A, hipStream_t st);
+
+// ---- attention (k_attn.hip) ----------------------------------------------------------
+// total_chunks = sum over bands of nch[sw]; partial buffers sized [total_chunks*nkv][128][hd]
+hipError_t launch_block_attn(const bf16* Q, const Band* bands_dev, int n_bands, int total_chunks,
+                             int gamma, int nh, KvGeom g, int layer, int sw, int window,
+                             float scale_log2, float* part_o, float* part_ml, hipStream_t st);
+hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,
+                               int n_bands, int gamma, int nh, int nkv, int hd, int sw,
+                               bf16* out, hipStream_t st);
+
+// ---- context append (k_misc.hip) -----------------------------------------------------
+hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
+                               int* kpos, hipStream_t st);
+hipError_t launch_rows_rmsnorm(const float* X, int M, int h, const bf16* w, float eps, bf16* out,
+                               hipStream_t st);
+hipError_t launch_kv_append_post(const float* KV, int n, int L, const bf16* k_norm_all,
+                                 float eps, const double* inv_freq, float mscale,
+                                 const long long* slots, const int* rowpos, KvGeom g,
+                                 hipStream_t st);
+
+}  // namespace dfl

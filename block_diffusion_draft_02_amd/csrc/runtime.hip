@@ -1,0 +1,601 @@
+// Host runtime behind include/dflash.h: configuration checks, the paged KV pool and its
+// free list, block tables, scratch, the fused weight copies, and the launch sequences of
+// the context append and of the gamma-block forward. One stream per call, no host sync
+// inside a call, no environment reads.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.hpp"
+
+using namespace dfl;
+
+namespace {
+
+constexpr int RING = 8;          // staging slots for caller-stamped append positions
+constexpr int ROW_GROUP = 64;    // rows per skinny-GEMM launch
+
+struct LayerDev {
+  const bf16 *o_proj, *down_proj, *q_norm, *k_norm, *in_norm, *post_norm;
+  bf16 *w_qkv, *w_gu;  // owned fused copies [q;k;v], [gate;up]
+};
+
+struct SeqState {
+  std::vector<int> bt;   // physical page of each logical page
+  std::vector<int> pos;  // stamped position of every cached context row
+  int kv_len = 0;
+};
+
+struct GemmPlan { int N, K, klen, S; };
+
+}  // namespace
+
+struct dflash_ctx {
+  // configuration
+  int L, h, nh, nkv, hd, qd, kvd, ff, V, T, Ht, gmax, mask, max_seq, max_batch;
+  float eps;
+  int rope_type, window;
+  std::vector<uint8_t> sliding;
+  double mscale = 1.0;
+  long long num_pages;
+  int per_seq;
+  int m_max;
+  // weights
+  const bf16 *fc, *hidden_norm, *norm, *embed, *lm_head;
+  std::vector<LayerDev> layers;
+  bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;...
+  bf16* knorm_all = nullptr;   // [L, hd]
+  double* inv_freq = nullptr;  // [hd/2]
+  // pool and tables
+  bf16* pool = nullptr;
+  int* kpos = nullptr;
+  int* bt_dev = nullptr;
+  long long* slots = nullptr;
+  int* rowpos = nullptr;
+  Band* bands_dev = nullptr;
+  // forward scratch
+  float* X = nullptr;
+  bf16* Xn = nullptr;
+  bf16* Qb = nullptr;
+  bf16* attn = nullptr;
+  bf16* act = nullptr;
+  float* part = nullptr;
+  size_t part_elems = 0;
+  float* aparts_o = nullptr;
+  float* aparts_ml = nullptr;
+  float* best_v = nullptr;
+  int* best_i = nullptr;
+  int lm_groups = 0;
+  GemmPlan g_qkv, g_o, g_gu, g_down;
+  // append scratch
+  float* F32 = nullptr;
+  bf16* Fb = nullptr;
+  float* KV32 = nullptr;
+  int* ring_host = nullptr;
+  int* ring_dev = nullptr;
+  hipEvent_t ring_ev[RING] = {};
+  int ring_next = 0;
+  // host state
+  std::vector<SeqState> seqs;
+  std::deque<int> free_pages;
+  std::vector<void*> owned;
+  std::string err;
+  bool poisoned = false;
+};
+
+namespace {
+
+int fail(dflash_ctx* c, int code, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+    if (code == DFLASH_EHIP) c->poisoned = true;
+  }
+  return code;
+}
+
+#define HIPCHK(c, expr)                                                                     \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail((c), DFLASH_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));        \
+  } while (0)
+
+template <class T>
+int dalloc(dflash_ctx* c, T** p, size_t elems) {
+  void* q = nullptr;
+  const size_t bytes = std::max<size_t>(elems * sizeof(T), 256);
+  hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, DFLASH_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  c->owned.push_back(q);
+  *p = static_cast<T*>(q);
+  return DFLASH_OK;
+}
+
+GemmPlan plan_gemm(int N, int K) {
+  // ~2048 wavefronts per weight-streaming launch; every split at least 256 deep
+  const int ntiles = (N + 15) / 16;
+  int S = std::max(1, 2048 / ntiles);
+  S = std::max(1, std::min(S, K / 256));
+  const int klen = ((K / S) + 127) / 128 * 128;
+  return GemmPlan{N, K, klen, (K + klen - 1) / klen};
+}
+
+void plan_chunks(int kstart, int kend, int& ck, int& nch) {
+  const int pages = (kend - kstart + PAGE - 1) / PAGE;
+  const int ckp = std::max(2, (pages + MAX_CHUNKS - 1) / MAX_CHUNKS);
+  nch = (pages + ckp - 1) / ckp;
+  ck = ckp * PAGE;
+}
+
+bool sliding_layer(const dflash_ctx* c, int l) { return c->window > 0 && c->sliding[l]; }
+
+KvGeom geom(dflash_ctx* c) {
+  return KvGeom{c->pool, c->kpos, c->bt_dev, c->num_pages, c->nkv, c->hd, c->per_seq};
+}
+
+int check_config(const dflash_config* cfg, const dflash_weights* w, std::string& why) {
+  auto bad = [&](const char* m) { why = m; return DFLASH_EINVAL; };
+  if (!cfg || !w || !w->layers) return bad("NULL config or weights");
+  if (cfg->num_layers <= 0 || cfg->hidden <= 0 || cfg->vocab <= 0 || cfg->num_taps <= 0 ||
+      cfg->target_hidden <= 0 || cfg->intermediate <= 0)
+    return bad("sizes must be positive");
+  if (cfg->head_dim != 32 && cfg->head_dim != 64 && cfg->head_dim != 128)
+    return bad("head_dim must be 32, 64 or 128");
+  if (cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads != 0)
+    return bad("num_q_heads must be a multiple of num_kv_heads");
+  if (cfg->num_q_heads / cfg->num_kv_heads > 8) return bad("at most 8 query heads per kv head");
+  if (cfg->gamma_max < 2 || cfg->gamma_max > 16) return bad("gamma_max must be in [2, 16]");
+  if (cfg->hidden % 128 || cfg->intermediate % 128 || (cfg->num_q_heads * cfg->head_dim) % 128 ||
+      (cfg->num_taps * cfg->target_hidden) % 128)
+    return bad("hidden, intermediate, q_dim and num_taps*target_hidden must be multiples of 128");
+  if (cfg->mask_token_id < 0 || cfg->mask_token_id >= cfg->vocab) return bad("mask_token_id out of range");
+  if (cfg->max_batch < 1 || cfg->max_batch > MAX_BANDS) return bad("max_batch must be in [1, 32]");
+  if (cfg->max_seq_len < 1 || cfg->max_seq_len > (1 << 28)) return bad("max_seq_len out of range");
+  if (!(cfg->rms_eps >= 0.f)) return bad("rms_eps must be >= 0");
+  if (!(cfg->rope_theta > 1.0)) return bad("rope_theta must be > 1");
+  if (cfg->rope_type != 0 && cfg->rope_type != 1) return bad("rope_type must be 0 or 1");
+  if (cfg->rope_type == 1 && !(cfg->yarn_factor > 0 && cfg->yarn_orig_max_pos > 0 &&
+                               cfg->yarn_beta_fast > 0 && cfg->yarn_beta_slow > 0))
+    return bad("YaRN parameters must be positive");
+  if (cfg->sliding_window < 0) return bad("sliding_window must be >= 0");
+  if (cfg->num_pages != 0 && cfg->num_pages < 2) return bad("num_pages must be 0 or >= 2");
+  if (!w->fc || !w->hidden_norm || !w->norm || !w->embed_tokens || !w->lm_head)
+    return bad("NULL head weight");
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    if (!lw.q_proj || !lw.k_proj || !lw.v_proj || !lw.o_proj || !lw.q_norm || !lw.k_norm ||
+        !lw.input_layernorm || !lw.post_attention_layernorm || !lw.gate_proj || !lw.up_proj ||
+        !lw.down_proj)
+      return bad("NULL layer weight");
+  }
+  return DFLASH_OK;
+}
+
+// inverse frequencies, double precision: plain theta^(-2j/d), or the YaRN blend
+// (memra_engine/dflash.rs, DflashDraft::load; spark_model/layers/dflash_head/
+// from_weights.rs, from_weights: ramp from low to high pair index, plain frequency below,
+// frequency / factor above; a zero-width ramp gets +0.001)
+std::vector<double> inv_freq_table(const dflash_config* cfg, double* mscale) {
+  const int hd = cfg->head_dim, half = hd / 2;
+  const double base = cfg->rope_theta, d = hd;
+  std::vector<double> f(half);
+  for (int j = 0; j < half; ++j) f[j] = std::pow(base, -2.0 * j / d);
+  *mscale = 1.0;
+  if (cfg->rope_type == 1) {
+    const double fac = cfg->yarn_factor, orig = cfg->yarn_orig_max_pos;
+    auto corr = [&](double r) { return d * std::log(orig / (r * 2.0 * M_PI)) / (2.0 * std::log(base)); };
+    const double low = std::max(std::floor(corr(cfg->yarn_beta_fast)), 0.0);
+    const double high = std::min(std::ceil(corr(cfg->yarn_beta_slow)), d - 1.0);
+    const double den = std::fabs(high - low) < 1e-6 ? high - low + 0.001 : high - low;
+    for (int j = 0; j < half; ++j) {
+      const double ramp = std::min(1.0, std::max(0.0, (j - low) / den));
+      f[j] = (f[j] / fac) * ramp + f[j] * (1.0 - ramp);
+    }
+    *mscale = 0.1 * std::log(fac) + 1.0;
+  }
+  return f;
+}
+
+void release(dflash_ctx* c) {
+  if (!c) return;
+  for (int i = 0; i < RING; ++i)
+    if (c->ring_ev[i]) (void)hipEventDestroy(c->ring_ev[i]);
+  if (c->ring_host) (void)hipHostFree(c->ring_host);
+  for (void* p : c->owned) (void)hipFree(p);
+  delete c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_strerror(int code) {
+  switch (code) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument";
+    case DFLASH_ENOMEM: return "out of memory";
+    case DFLASH_EPOOL: return "KV pool exhausted";
+    case DFLASH_ERANGE: return "out of range";
+    case DFLASH_EHIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err.c_str() : ""; }
+
+int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* stream, dflash_ctx** out) {
+  if (!out) return DFLASH_EINVAL;
+  *out = nullptr;
+  std::string why;
+  int rc = check_config(cfg, w, why);
+  if (rc != DFLASH_OK) return rc;
+  dflash_ctx* c = new dflash_ctx();
+  hipStream_t st = (hipStream_t)stream;
+  c->L = cfg->num_layers; c->h = cfg->hidden; c->nh = cfg->num_q_heads; c->nkv = cfg->num_kv_heads;
+  c->hd = cfg->head_dim; c->qd = c->nh * c->hd; c->kvd = c->nkv * c->hd; c->ff = cfg->intermediate;
+  c->V = cfg->vocab; c->T = cfg->num_taps; c->Ht = cfg->target_hidden; c->gmax = cfg->gamma_max;
+  c->mask = cfg->mask_token_id; c->max_seq = cfg->max_seq_len; c->max_batch = cfg->max_batch;
+  c->eps = cfg->rms_eps; c->rope_type = cfg->rope_type; c->window = cfg->sliding_window;
+  c->sliding.assign(c->L, 0);
+  if (cfg->layer_sliding)
+    for (int l = 0; l < c->L; ++l) c->sliding[l] = cfg->layer_sliding[l] ? 1 : 0;
+  // pool: ceil((max_seq_len + gamma + 1) / 16) pages per sequence, times max_batch, + 1
+  // (spark_model/layers/dflash_head/from_weights.rs, from_weights); page 0 is the spare,
+  // a zeroed sentinel that is never handed out
+  c->per_seq = (c->max_seq + c->gmax + 1 + PAGE - 1) / PAGE;
+  c->num_pages = cfg->num_pages ? cfg->num_pages : (long long)c->per_seq * c->max_batch + 1;
+  if (cfg->page_order) {
+    std::vector<char> seen(c->num_pages, 0);
+    for (long long i = 0; i + 1 < c->num_pages; ++i) {
+      const int p = cfg->page_order[i];
+      if (p < 1 || p >= c->num_pages || seen[p]) {
+        release(c);
+        return DFLASH_EINVAL;
+      }
+      seen[p] = 1;
+      c->free_pages.push_back(p);
+    }
+  } else {
+    for (long long p = 1; p < c->num_pages; ++p) c->free_pages.push_back((int)p);
+  }
+  c->seqs.resize(c->max_batch);
+  c->m_max = c->max_batch * c->gmax;
+  c->fc = (const bf16*)w->fc; c->hidden_norm = (const bf16*)w->hidden_norm; c->norm = (const bf16*)w->norm;
+  c->embed = (const bf16*)w->embed_tokens; c->lm_head = (const bf16*)w->lm_head;
+
+  auto fin = [&](int r) { if (r != DFLASH_OK) { std::string e = c->err; release(c); (void)e; } return r; };
+  const size_t hsz = (size_t)c->h;
+  const size_t pl = page_layer_elems(c->nkv, c->hd);
+  c->g_qkv = plan_gemm(c->qd + 2 * c->kvd, c->h);
+  c->g_o = plan_gemm(c->h, c->qd);
+  c->g_gu = plan_gemm(2 * c->ff, c->h);
+  c->g_down = plan_gemm(c->h, c->ff);
+  size_t part = 0;
+  for (const GemmPlan* g : {&c->g_qkv, &c->g_o, &c->g_gu, &c->g_down})
+    part = std::max(part, (size_t)g->S * c->m_max * g->N);
+  c->part_elems = part;
+  c->lm_groups = lmhead_groups(c->V);
+  const size_t items = (size_t)c->max_batch * MAX_CHUNKS * c->nkv;
+  if ((rc = dalloc(c, &c->pool, (size_t)c->L * c->num_pages * pl)) ||
+      (rc = dalloc(c, &c->kpos, (size_t)c->num_pages * PAGE)) ||
+      (rc = dalloc(c, &c->bt_dev, (size_t)c->max_batch * c->per_seq)) ||
+      (rc = dalloc(c, &c->slots, (size_t)std::max(c->m_max, APPEND_ROWS))) ||
+      (rc = dalloc(c, &c->rowpos, (size_t)APPEND_ROWS)) ||
+      (rc = dalloc(c, &c->bands_dev, (size_t)MAX_BANDS)) ||
+      (rc = dalloc(c, &c->X, (size_t)c->m_max * hsz)) ||
+      (rc = dalloc(c, &c->Xn, (size_t)c->m_max * hsz)) ||
+      (rc = dalloc(c, &c->Qb, (size_t)c->m_max * c->qd)) ||
+      (rc = dalloc(c, &c->attn, (size_t)c->m_max * c->qd)) ||
+      (rc = dalloc(c, &c->act, (size_t)c->m_max * c->ff)) ||
+      (rc = dalloc(c, &c->part, part)) ||
+      (rc = dalloc(c, &c->aparts_o, items * 128 * c->hd)) ||
+      (rc = dalloc(c, &c->aparts_ml, items * 128 * 2)) ||
+      (rc = dalloc(c, &c->best_v, (size_t)c->m_max * c->lm_groups)) ||
+      (rc = dalloc(c, &c->best_i, (size_t)c->m_max * c->lm_groups)) ||
+      (rc = dalloc(c, &c->F32, (size_t)APPEND_ROWS * hsz)) ||
+      (rc = dalloc(c, &c->Fb, (size_t)APPEND_ROWS * hsz)) ||
+      (rc = dalloc(c, &c->KV32, (size_t)APPEND_ROWS * c->L * 2 * c->kvd)) ||
+      (rc = dalloc(c, &c->ring_dev, (size_t)RING * APPEND_ROWS)) ||
+      (rc = dalloc(c, &c->w_kv, (size_t)c->L * 2 * c->kvd * hsz)) ||
+      (rc = dalloc(c, &c->knorm_all, (size_t)c->L * c->hd)) ||
+      (rc = dalloc(c, &c->inv_freq, (size_t)c->hd / 2)))
+    return fin(rc);
+  c->layers.resize(c->L);
+  for (int l = 0; l < c->L; ++l) {
+    LayerDev& d = c->layers[l];
+    const dflash_layer_weights& lw = w->layers[l];
+    d.o_proj = (const bf16*)lw.o_proj; d.down_proj = (const bf16*)lw.down_proj;
+    d.q_norm = (const bf16*)lw.q_norm; d.k_norm = (const bf16*)lw.k_norm;
+    d.in_norm = (const bf16*)lw.input_layernorm; d.post_norm = (const bf16*)lw.post_attention_layernorm;
+    if ((rc = dalloc(c, &d.w_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
+        (rc = dalloc(c, &d.w_gu, (size_t)2 * c->ff * hsz)))
+      return fin(rc);
+  }
+  if (hipHostMalloc((void**)&c->ring_host, (size_t)RING * APPEND_ROWS * sizeof(int), hipHostMallocDefault) != hipSuccess) {
+    c->ring_host = nullptr;
+    return fin(fail(c, DFLASH_ENOMEM, "hipHostMalloc failed"));
+  }
+  for (int i = 0; i < RING; ++i)
+    if (hipEventCreateWithFlags(&c->ring_ev[i], hipEventDisableTiming) != hipSuccess)
+      return fin(fail(c, DFLASH_EHIP, "hipEventCreate failed"));
+
+  auto cp = [&](void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+  };
+  const size_t qb = (size_t)c->qd * hsz * 2, kb = (size_t)c->kvd * hsz * 2, fb = (size_t)c->ff * hsz * 2;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < c->L && e == hipSuccess; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    LayerDev& d = c->layers[l];
+    char* q = (char*)d.w_qkv;
+    if ((e = cp(q, lw.q_proj, qb)) || (e = cp(q + qb, lw.k_proj, kb)) || (e = cp(q + qb + kb, lw.v_proj, kb)) ||
+        (e = cp(d.w_gu, lw.gate_proj, fb)) || (e = cp((char*)d.w_gu + fb, lw.up_proj, fb)) ||
+        (e = cp((char*)c->w_kv + (size_t)l * 2 * kb, lw.k_proj, kb)) ||
+        (e = cp((char*)c->w_kv + (size_t)l * 2 * kb + kb, lw.v_proj, kb)) ||
+        (e = cp(c->knorm_all + (size_t)l * c->hd, lw.k_norm, (size_t)c->hd * 2)))
+      break;
+  }
+  std::vector<double> f = inv_freq_table(cfg, &c->mscale);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->inv_freq, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, (size_t)c->L * c->num_pages * pl * 2, st);
+  if (e == hipSuccess) e = hipMemsetAsync(c->kpos, 0, (size_t)c->num_pages * PAGE * 4, st);
+  if (e == hipSuccess) e = hipMemsetAsync(c->bt_dev, 0, (size_t)c->max_batch * c->per_seq * 4, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fin(fail(c, DFLASH_EHIP, "create: %s", hipGetErrorString(e)));
+  *out = c;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_ctx* c) {
+  if (!c) return;
+  (void)hipDeviceSynchronize();
+  release(c);
+}
+
+int dflash_seq_reset(dflash_ctx* c, int32_t seq) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  if (seq < 0 || seq >= c->max_batch) return fail(c, DFLASH_ERANGE, "seq %d out of range", seq);
+  SeqState& s = c->seqs[seq];
+  for (int p : s.bt) c->free_pages.push_back(p);
+  // device block-table rows of freed pages go back to the sentinel lazily: every reader
+  // bounds its page lookups by the sequence's length, and new pages overwrite the entries
+  s.bt.clear();
+  s.pos.clear();
+  s.kv_len = 0;
+  return DFLASH_OK;
+}
+
+int dflash_seq_info(const dflash_ctx* c, int32_t seq, int32_t* kv_len, int32_t* n_pages,
+                    int32_t* block_table, int32_t cap) {
+  if (!c || seq < 0 || seq >= c->max_batch) return DFLASH_ERANGE;
+  const SeqState& s = c->seqs[seq];
+  if (kv_len) *kv_len = s.kv_len;
+  if (n_pages) *n_pages = (int32_t)s.bt.size();
+  if (block_table)
+    for (int i = 0; i < cap && i < (int)s.bt.size(); ++i) block_table[i] = s.bt[i];
+  return DFLASH_OK;
+}
+
+int dflash_pool_geometry(const dflash_ctx* c, int64_t* num_pages, int64_t* pages_per_seq,
+                         int64_t* page_layer_bytes, int64_t* pool_bytes, int64_t* fused_kv_weight_bytes) {
+  if (!c) return DFLASH_EINVAL;
+  const int64_t plb = (int64_t)page_layer_elems(c->nkv, c->hd) * 2;
+  if (num_pages) *num_pages = c->num_pages;
+  if (pages_per_seq) *pages_per_seq = c->per_seq;
+  if (page_layer_bytes) *page_layer_bytes = plb;
+  if (pool_bytes) *pool_bytes = plb * c->L * c->num_pages;
+  if (fused_kv_weight_bytes) *fused_kv_weight_bytes = (int64_t)c->L * 2 * c->kvd * c->h * 2;
+  return DFLASH_OK;
+}
+
+int dflash_debug_copy(dflash_ctx* c, int32_t buffer, void* dst, size_t offset, size_t bytes, void* stream) {
+  if (!c || !dst) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  const char* base = nullptr;
+  size_t size = 0;
+  switch (buffer) {
+    case DFLASH_BUF_POOL: base = (const char*)c->pool; size = (size_t)c->L * c->num_pages * page_layer_elems(c->nkv, c->hd) * 2; break;
+    case DFLASH_BUF_KPOS: base = (const char*)c->kpos; size = (size_t)c->num_pages * PAGE * 4; break;
+    case DFLASH_BUF_SLOTS: base = (const char*)c->slots; size = (size_t)std::max(c->m_max, APPEND_ROWS) * 8; break;
+    case DFLASH_BUF_BLOCKTAB: base = (const char*)c->bt_dev; size = (size_t)c->max_batch * c->per_seq * 4; break;
+    case DFLASH_BUF_HIDDEN: base = (const char*)c->Xn; size = (size_t)c->m_max * c->h * 2; break;
+    default: return fail(c, DFLASH_EINVAL, "unknown buffer %d", buffer);
+  }
+  if (offset > size || bytes > size - offset) return fail(c, DFLASH_ERANGE, "copy past the end of buffer %d", buffer);
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(c, hipMemcpyAsync(dst, base + offset, bytes, hipMemcpyDefault, st));
+  HIPCHK(c, hipStreamSynchronize(st));
+  return DFLASH_OK;
+}
+
+int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
+                         const int32_t* positions, int32_t n, void* stream) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  if (seq < 0 || seq >= c->max_batch) return fail(c, DFLASH_ERANGE, "seq %d out of range", seq);
+  if (n <= 0) return fail(c, DFLASH_EINVAL, "n must be positive");
+  if (!target_hidden) return fail(c, DFLASH_EINVAL, "NULL target_hidden");
+  SeqState& s = c->seqs[seq];
+  const int C = s.kv_len;
+  if ((long long)C + n > c->max_seq) return fail(c, DFLASH_ERANGE, "kv_len %d + n %d exceeds max_seq_len %d", C, n, c->max_seq);
+  long long last = s.pos.empty() ? -1 : s.pos.back();
+  for (int i = 0; i < n; ++i) {
+    const long long p = positions ? positions[i] : (long long)C + i;
+    if (p <= last || p >= (1LL << 30))
+      return fail(c, DFLASH_EINVAL, "positions must be strictly increasing, in [0, 2^30)");
+    last = p;
+  }
+  const int need = (C + n + PAGE - 1) / PAGE - (int)s.bt.size();
+  if (need > (int)c->free_pages.size()) return fail(c, DFLASH_EPOOL, "KV pool exhausted (%d pages needed, %zu free)", need, c->free_pages.size());
+  // --- committed from here on
+  const int old_pages = (int)s.bt.size();
+  for (int i = 0; i < need; ++i) {
+    s.bt.push_back(c->free_pages.front());
+    c->free_pages.pop_front();
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const KvGeom g = geom(c);
+  const int ld = c->T * c->Ht;
+  for (int r0 = 0; r0 < n; r0 += APPEND_ROWS) {
+    const int nc = std::min(APPEND_ROWS, n - r0);
+    AppendArgs a{};
+    a.seq = seq; a.kv_len = C + r0; a.n = nc; a.per_seq = c->per_seq;
+    a.first_lpage = (C + r0) / PAGE;
+    a.n_lpages = (C + r0 + nc - 1) / PAGE - a.first_lpage + 1;
+    a.n_upd = 0;
+    for (int i = 0; i < a.n_lpages; ++i) {
+      const int lp = a.first_lpage + i;
+      a.pages[i] = s.bt[lp];
+      if (lp >= old_pages) {
+        a.upd_off[a.n_upd] = seq * c->per_seq + lp;
+        a.upd_page[a.n_upd] = s.bt[lp];
+        ++a.n_upd;
+      }
+    }
+    a.positions = nullptr;
+    int slot = -1;
+    if (positions) {
+      slot = c->ring_next;
+      c->ring_next = (c->ring_next + 1) % RING;
+      HIPCHK(c, hipEventSynchronize(c->ring_ev[slot]));
+      int* hp = c->ring_host + (size_t)slot * APPEND_ROWS;
+      int* dp = c->ring_dev + (size_t)slot * APPEND_ROWS;
+      memcpy(hp, positions + r0, (size_t)nc * sizeof(int));
+      HIPCHK(c, hipMemcpyAsync(dp, hp, (size_t)nc * sizeof(int), hipMemcpyHostToDevice, st));
+      a.positions = dp;
+    }
+    HIPCHK(c, launch_append_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st));
+    if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
+    HIPCHK(c, launch_gemm_tiled((const bf16*)target_hidden + (size_t)r0 * ld, ld, nc, c->fc, c->h, ld, c->F32, c->h, st));
+    HIPCHK(c, launch_rows_rmsnorm(c->F32, nc, c->h, c->hidden_norm, c->eps, c->Fb, st));
+    HIPCHK(c, launch_gemm_tiled(c->Fb, c->h, nc, c->w_kv, c->L * 2 * c->kvd, c->h, c->KV32, c->L * 2 * c->kvd, st));
+    HIPCHK(c, launch_kv_append_post(c->KV32, nc, c->L, c->knorm_all, c->eps, c->inv_freq, (float)c->mscale,
+                                    c->slots, c->rowpos, g, st));
+  }
+  for (int i = 0; i < n; ++i) s.pos.push_back(positions ? positions[i] : C + i);
+  s.kv_len = C + n;
+  return DFLASH_OK;
+}
+
+int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int32_t* bonus,
+                         const int32_t* q_rope_pos, int32_t gamma, int32_t* draft_tokens,
+                         float* logits, void* stream) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  if (n_seqs < 1 || n_seqs > c->max_batch) return fail(c, DFLASH_EINVAL, "n_seqs %d not in [1, %d]", n_seqs, c->max_batch);
+  if (!seqs || !bonus || !draft_tokens) return fail(c, DFLASH_EINVAL, "NULL seqs, bonus_tokens or draft_tokens");
+  if (gamma < 2 || gamma > c->gmax) return fail(c, DFLASH_ERANGE, "gamma %d not in [2, %d]", gamma, c->gmax);
+  std::vector<char> seen(c->max_batch, 0);
+  int need = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    const int q = seqs[b];
+    if (q < 0 || q >= c->max_batch || seen[q]) return fail(c, DFLASH_ERANGE, "seq %d out of range or repeated", q);
+    seen[q] = 1;
+    if (bonus[b] < 0 || bonus[b] >= c->V) return fail(c, DFLASH_EINVAL, "bonus token %d out of range", bonus[b]);
+    if (q_rope_pos && (q_rope_pos[b] < 0 || q_rope_pos[b] >= (1 << 30)))
+      return fail(c, DFLASH_EINVAL, "q_rope_pos must be in [0, 2^30)");
+    const SeqState& s = c->seqs[q];
+    need += std::max(0, (s.kv_len + gamma + PAGE - 1) / PAGE - (int)s.bt.size());
+  }
+  if (need > (int)c->free_pages.size()) return fail(c, DFLASH_EPOOL, "KV pool exhausted (%d pages needed, %zu free)", need, c->free_pages.size());
+  // --- committed from here on
+  FwdArgs a{};
+  a.n_bands = n_seqs; a.gamma = gamma; a.mask_token = c->mask; a.per_seq = c->per_seq; a.n_upd = 0;
+  int base[2] = {0, 0};
+  for (int b = 0; b < n_seqs; ++b) {
+    const int q = seqs[b];
+    SeqState& s = c->seqs[q];
+    const int C = s.kv_len;
+    const int want = (C + gamma + PAGE - 1) / PAGE;
+    while ((int)s.bt.size() < want) {
+      const int p = c->free_pages.front();
+      c->free_pages.pop_front();
+      a.upd_off[a.n_upd] = q * c->per_seq + (int)s.bt.size();
+      a.upd_page[a.n_upd] = p;
+      ++a.n_upd;
+      s.bt.push_back(p);
+    }
+    Band& B = a.bands[b];
+    B.seq = q; B.kv_len = C; B.q_pos = q_rope_pos ? q_rope_pos[b] : C; B.bonus = bonus[b];
+    const int lp0 = C / PAGE;
+    B.pg[0] = s.bt[lp0];
+    B.pg[1] = lp0 + 1 < (int)s.bt.size() ? s.bt[lp0 + 1] : 0;
+    const int kend = C + gamma;
+    // full layers: every key; sliding layers: from the first context row whose stamped
+    // position is within the window of block row 0 (rows further down see a subset)
+    int klo = 0;
+    if (c->window > 0) {
+      const long long lim = (long long)B.q_pos - c->window;  // visible iff pos > lim
+      klo = (int)(std::upper_bound(s.pos.begin(), s.pos.end(), lim) - s.pos.begin());
+    }
+    for (int sw = 0; sw < 2; ++sw) {
+      B.kstart[sw] = sw == 0 ? 0 : (klo / PAGE) * PAGE;
+      plan_chunks(B.kstart[sw], kend, B.ck[sw], B.nch[sw]);
+      B.base[sw] = base[sw];
+      base[sw] += B.nch[sw];
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const KvGeom g = geom(c);
+  const int M = n_seqs * gamma;
+  const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
+  HIPCHK(c, launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed,
+                                c->layers[0].in_norm, c->h, c->eps, c->X, c->Xn, st));
+  auto gemm = [&](const bf16* A, int lda, const bf16* W, const GemmPlan& p) -> hipError_t {
+    const long long ps = (long long)M * p.N;
+    for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
+      const int mg = std::min(ROW_GROUP, M - r0);
+      hipError_t e = launch_gemm_skinny(A + (size_t)r0 * lda, lda, mg, W, p.N, p.K, p.klen,
+                                        c->part + (size_t)r0 * p.N, ps, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  for (int l = 0; l < c->L; ++l) {
+    const LayerDev& d = c->layers[l];
+    const int sw = sliding_layer(c, l) ? 1 : 0;
+    HIPCHK(c, gemm(c->Xn, c->h, d.w_qkv, c->g_qkv));
+    HIPCHK(c, launch_qkv_post(c->part, c->g_qkv.S, (long long)M * c->g_qkv.N, M, gamma, c->bands_dev,
+                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
+                              (float)c->mscale, c->slots, g, l, c->Qb, st));
+    HIPCHK(c, launch_block_attn(c->Qb, c->bands_dev, n_seqs, base[sw], gamma, c->nh, g, l, sw,
+                                sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st));
+    HIPCHK(c, launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
+                                  c->nkv, c->hd, sw, c->attn, st));
+    HIPCHK(c, gemm(c->attn, c->qd, d.o_proj, c->g_o));
+    HIPCHK(c, launch_resid_norm(c->X, c->part, c->g_o.S, (long long)M * c->g_o.N, M, c->h, d.post_norm,
+                                c->eps, c->Xn, st));
+    HIPCHK(c, gemm(c->Xn, c->h, d.w_gu, c->g_gu));
+    HIPCHK(c, launch_silu_mul(c->part, c->g_gu.S, (long long)M * c->g_gu.N, M, c->ff, c->act, st));
+    HIPCHK(c, gemm(c->act, c->ff, d.down_proj, c->g_down));
+    const bf16* wn = l + 1 < c->L ? c->layers[l + 1].in_norm : c->norm;
+    HIPCHK(c, launch_resid_norm(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h, wn,
+                                c->eps, c->Xn, st));
+  }
+  for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
+    const int mg = std::min(ROW_GROUP, M - r0);
+    HIPCHK(c, launch_lmhead_argmax(c->Xn + (size_t)r0 * c->h, c->h, mg, r0, c->lm_head, c->V, c->h,
+                                   c->best_v, c->best_i, c->lm_groups, gamma, logits, st));
+  }
+  HIPCHK(c, launch_argmax_reduce(c->best_v, c->best_i, c->lm_groups, n_seqs, gamma, draft_tokens, st));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+/*
+ * dflash.h -- C ABI of the DFlash block-diffusion drafter's gamma-block forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (page titles and sections of the describing pages):
+ *  - memra_engine/dflash.rs, DflashDraft::ctx_features and ::ingest_ctx: tapped target
+ *    hidden states are concatenated, projected through `fc`, normalised by
+ *    `hidden_norm`, and every layer's context K (k_norm + RoPE) and V are written to the
+ *    drafter's KV cache.
+ *  - memra_engine/dflash.rs, DflashDraft::forward_round and
+ *    HybridModel::generate_spec_dflash: the block [bonus, mask x (gamma-1)] is embedded
+ *    with the shared target embedding and runs through every layer (RMSNorm, Q/K/V,
+ *    per-head q/k RMSNorm, RoPE, block K/V written after the context, non-causal GQA
+ *    attention over context + block, o_proj + residual, SwiGLU MLP + residual); the
+ *    final norm, the shared lm_head and a per-row argmax over rows 1..gamma-1 give
+ *    gamma-1 draft tokens.
+ *  - spark_model/layers/dflash_head/from_weights.rs, from_weights: a paged BF16 KV pool
+ *    of 16-token pages sized ceil((max_seq_len + gamma + 1) / 16) * max_batch + 1.
+ *  - spark_model/layers/dflash_head.rs, DflashBatch and DraftProposer::propose_batch:
+ *    several sequences in one call, sequence i owning rows [i*gamma, (i+1)*gamma).
+ *
+ * Conventions for every entry point:
+ *  - Weights, hidden states and outputs are caller-owned DEVICE memory (bf16 = raw
+ *    IEEE bfloat16 bit patterns, row-major, matrices [out_features, in_features]).
+ *    Weight pointers are borrowed: they must stay valid until dflash_destroy.
+ *  - Everything named "host" is host memory read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on it and
+ *    the call returns; outputs are valid once the stream has reached that point. A
+ *    context is used by one host thread at a time.
+ *  - Every condition the host can check is checked before anything is enqueued, and a
+ *    failing call changes no state (no pages taken, kv_len unchanged). A HIP runtime
+ *    failure returns DFLASH_EHIP and leaves the context unusable (every later call
+ *    returns DFLASH_EHIP). dflash_last_error() gives a message for the last failure.
+ *  - No environment variables are read.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dflash_ctx dflash_ctx;
+
+enum {
+  DFLASH_OK = 0,
+  DFLASH_EINVAL = -1, /* bad argument / unsupported shape */
+  DFLASH_ENOMEM = -2, /* device or host allocation failed */
+  DFLASH_EPOOL = -3,  /* the KV pool cannot supply the pages this call needs */
+  DFLASH_ERANGE = -4, /* seq id, gamma, or kv_len + n beyond max_seq_len */
+  DFLASH_EHIP = -5    /* HIP runtime error; the context is unusable */
+};
+
+/* Model and pool configuration (all host memory, copied by dflash_create).
+ * Supported shapes: head_dim in {32, 64, 128}; num_q_heads % num_kv_heads == 0 with a
+ * group of at most 8 query heads; gamma_max in [2, 16]; hidden, intermediate,
+ * num_q_heads*head_dim and num_taps*target_hidden multiples of 64; max_batch <= 64. */
+typedef struct {
+  int32_t num_layers, hidden, num_q_heads, num_kv_heads, head_dim, intermediate, vocab;
+  int32_t num_taps, target_hidden; /* fc in_features = num_taps * target_hidden */
+  int32_t gamma_max;               /* widest block a forward call may ask for */
+  int32_t mask_token_id;           /* id of the mask rows 1..gamma-1 */
+  float rms_eps;                   /* RMSNorm eps (vanilla form x * w / sqrt(mean(x^2)+eps)) */
+  double rope_theta;
+  int32_t rope_type;               /* 0 = plain NeoX RoPE, 1 = YaRN */
+  double yarn_factor, yarn_orig_max_pos, yarn_beta_fast, yarn_beta_slow;
+  int32_t sliding_window;          /* window W of sliding layers, 0 = none */
+  const uint8_t *layer_sliding;    /* host [num_layers], 1 = sliding layer; NULL = none */
+  int32_t max_seq_len;             /* context rows a sequence may hold */
+  int32_t max_batch;               /* sequence slots 0..max_batch-1 */
+  int32_t num_pages;               /* 0 = the formula above; >= 2 = explicit pool size */
+  const int32_t *page_order;       /* host [num_pages-1]: free-list order, a permutation of
+                                      1..num_pages-1; NULL = ascending. Page 0 is a zeroed
+                                      sentinel and is never handed out. */
+} dflash_config;
+
+/* Per-layer weights, device bf16. q/k/v/o/gate/up/down are [out, in]; norms [hidden]
+ * or [head_dim] (q_norm, k_norm). */
+typedef struct {
+  const void *q_proj, *k_proj, *v_proj, *o_proj, *q_norm, *k_norm;
+  const void *input_layernorm, *post_attention_layernorm;
+  const void *gate_proj, *up_proj, *down_proj;
+} dflash_layer_weights;
+
+/* fc [hidden, num_taps*target_hidden]; hidden_norm, norm [hidden]; embed_tokens and
+ * lm_head [vocab, hidden] are the target's, shared (they may alias). `layers` is a host
+ * array [num_layers]. */
+typedef struct {
+  const void *fc, *hidden_norm, *norm, *embed_tokens, *lm_head;
+  const dflash_layer_weights *layers;
+} dflash_weights;
+
+/* Create a drafter: validates the configuration, allocates the KV pool, block tables and
+ * scratch, builds the inverse-frequency table (plain or YaRN, in double precision) and
+ * copies the weights it fuses ([Wq;Wk;Wv], [Wgate;Wup] per layer and the all-layer
+ * [K0;V0;K1;V1;...] weight of the context append; spark_model/layers/dflash_head/
+ * from_weights.rs, fused K/V weight). The copies are enqueued on `stream`.
+ * On success *out owns everything it allocated; on failure *out is NULL. */
+int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *stream,
+                  dflash_ctx **out);
+
+/* Append n context rows to sequence `seq` (memra_engine/dflash.rs, ctx_features +
+ * ingest_ctx): F = hidden_norm(H fc^T); per layer K = RoPE(k_norm(F Wk^T)), V = F Wv^T,
+ * written at logical positions kv_len..kv_len+n-1; then kv_len += n. Pages are taken from
+ * the pool as positions first touch them (in ascending page order).
+ *   target_hidden: device bf16 [n, num_taps*target_hidden], taps concatenated in the
+ *                  drafter's target_layer_ids order;
+ *   positions:     host int32 [n], the RoPE position stamped on each row, strictly
+ *                  increasing and above the sequence's last stamped position; NULL means
+ *                  kv_len + i.
+ * Errors: ERANGE (seq, kv_len + n > max_seq_len), EINVAL (n <= 0, NULL hidden, positions
+ * not increasing), EPOOL. */
+int dflash_ctx_kv_append(dflash_ctx *ctx, int32_t seq, const void *target_hidden,
+                         const int32_t *positions, int32_t n, void *stream);
+
+/* One gamma-block forward for n_seqs sequences at once (band b = seqs[b] owns rows
+ * [b*gamma, (b+1)*gamma)). Row i of band b is token bonus_tokens[b] (i = 0) or
+ * mask_token_id, at RoPE position q_rope_pos[b] + i (q_rope_pos NULL: the sequence's
+ * kv_len). The block's K/V are written to slots kv_len..kv_len+gamma-1 (pages taken as
+ * needed) but kv_len does NOT advance: the next append overwrites them.
+ *   draft_tokens: device int32 [n_seqs, gamma-1]: argmax of rows 1..gamma-1 (lowest
+ *                 index on an exact tie);
+ *   logits:       device fp32 [n_seqs*(gamma-1), vocab] or NULL.
+ * Errors: EINVAL (n_seqs not in 1..max_batch, NULL pointers, bonus token out of range),
+ * ERANGE (seq out of range or repeated, gamma not in [2, gamma_max]), EPOOL. */
+int dflash_block_forward(dflash_ctx *ctx, int32_t n_seqs, const int32_t *seqs,
+                         const int32_t *bonus_tokens, const int32_t *q_rope_pos,
+                         int32_t gamma, int32_t *draft_tokens, float *logits, void *stream);
+
+/* Release everything the context owns (waits for its outstanding work). NULL is a no-op. */
+void dflash_destroy(dflash_ctx *ctx);
+
+/* ---- sequence management and introspection ------------------------------------- */
+
+/* Return a sequence's pages to the tail of the free list (block-table order) and set its
+ * kv_len to 0 (spark_model/layers/dflash_head.rs, DraftProposer::free_state). */
+int dflash_seq_reset(dflash_ctx *ctx, int32_t seq);
+
+/* Host view of a sequence: kv_len, number of pages and up to `cap` block-table entries. */
+int dflash_seq_info(const dflash_ctx *ctx, int32_t seq, int32_t *kv_len, int32_t *n_pages,
+                    int32_t *block_table, int32_t cap);
+
+/* Pool geometry: pages in the pool, pages per sequence, bytes of one page of one layer
+ * (K and V of every kv head), total pool bytes, and bytes of the fused append weight. */
+int dflash_pool_geometry(const dflash_ctx *ctx, int64_t *num_pages, int64_t *pages_per_seq,
+                         int64_t *page_layer_bytes, int64_t *pool_bytes,
+                         int64_t *fused_kv_weight_bytes);
+
+/* Copy `bytes` bytes at byte `offset` of a device-side buffer into `dst` (host or device)
+ * and wait for it. Buffers:
+ *   DFLASH_BUF_POOL      the KV pool: bf16 [num_layers][num_pages][2][num_kv_heads]x
+ *                        {K: [16][head_dim], V: [head_dim][16]} (V pages are stored
+ *                        transposed);
+ *   DFLASH_BUF_KPOS      int32 [num_pages*16]: the position stamped on every slot;
+ *   DFLASH_BUF_SLOTS     int64 slots written by the last append / forward call;
+ *   DFLASH_BUF_BLOCKTAB  int32 [max_batch][pages_per_seq]: the device block tables;
+ *   DFLASH_BUF_HIDDEN    bf16 [rows][hidden]: the final-normed hidden rows of the last
+ *                        forward (debug seam). */
+enum { DFLASH_BUF_POOL = 0, DFLASH_BUF_KPOS = 1, DFLASH_BUF_SLOTS = 2,
+       DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4 };
+int dflash_debug_copy(dflash_ctx *ctx, int32_t buffer, void *dst, size_t offset, size_t bytes,
+                      void *stream);
+
+/* Message of the last failure on this context ("" if none); valid until the next call. */
+const char *dflash_last_error(const dflash_ctx *ctx);
+/* Static name of an error code. */
+const char *dflash_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

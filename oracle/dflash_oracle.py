@@ -370,6 +370,8 @@ class Drafter:
 
     def lm_head(self, y: np.ndarray, chunk: int = 16384) -> np.ndarray:
         """logits = y @ lm_head^T, the vocabulary taken in chunks (memory only)."""
+        if self.cache_weights:
+            return y @ self.w("lm_head").T
         V = self.m["vocab"]
         out = np.empty((y.shape[0], V), dtype=self.dtype)
         for s in range(0, V, chunk):

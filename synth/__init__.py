@@ -164,8 +164,13 @@ def gen_weight(m: dict, seed: int, name: str) -> np.ndarray:
     raise KeyError(name)
 
 
-def gen_weights(m: dict, seed: int) -> dict:
-    return {n: gen_weight(m, seed, n) for n, _, _ in weight_specs(m)}
+def gen_weights(m: dict, seed: int, threads: int = 8) -> dict:
+    """All weights; tensors are independent streams, so they are drawn in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+    names = [n for n, _, _ in weight_specs(m)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        arrs = list(ex.map(lambda n: gen_weight(m, seed, n), names))
+    return dict(zip(names, arrs))
 
 
 def gen_hidden(m: dict, seed: int, n_rows: int, index: int = 0) -> np.ndarray:

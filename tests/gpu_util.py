@@ -1,0 +1,103 @@
+"""Helpers shared by the GPU parity tests: device copies of the seeded inputs, the
+GPU-side drafter next to the CPU oracle, and the parity criteria.
+
+Parity bar (floating point): max |logit_gpu - logit_oracle| <= 3e-2 * max |logit_oracle|
+over the drafted rows, and >= 99.5 % argmax agreement over positions whose oracle top-2
+gap is at least 1e-2. Integer state (block tables, slots, stamped positions) is compared
+bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+from block_diffusion_draft_02_amd import binding as B
+from oracle import dflash_oracle as O
+
+DEV = torch.device("cuda:0")
+LOGIT_REL_TOL = 3e-2
+NEAR_TIE = 1e-2
+AGREE_MIN = 0.995
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dev_weights(W: dict) -> dict:
+    return {k: dev_bf16(v) for k, v in W.items()}
+
+
+class Pair:
+    """The HIP drafter and the oracle engine on the same seeded weights and pool."""
+
+    def __init__(self, m, W, max_seq_len, max_batch, page_order=None, num_pages=0, oracle_cache=True):
+        self.m, self.W = m, W
+        self.Wd = dev_weights(W)
+        self.gpu = B.Drafter(m, self.Wd, max_seq_len, max_batch, num_pages=num_pages, page_order=page_order)
+        self.ora = O.Engine(m, W, max_seq_len, max_batch, page_order=page_order, num_pages=num_pages,
+                            cache_weights=oracle_cache)
+
+    def append(self, seq, H, positions=None):
+        self.gpu.dflash_ctx_kv_append(seq, dev_bf16(H), positions=positions)
+        self.ora.ctx_kv_append(seq, H, positions=positions)
+
+    def forward(self, seqs, bonus, q_rope_pos=None, gamma=None):
+        gamma = self.m["gamma_max"] if gamma is None else gamma
+        n = len(seqs)
+        toks = torch.full((n, gamma - 1), -1, dtype=torch.int32, device=DEV)
+        logits = torch.empty((n * (gamma - 1), self.m["vocab"]), dtype=torch.float32, device=DEV)
+        self.gpu.dflash_block_forward(seqs, bonus, toks, logits, q_rope_pos=q_rope_pos, gamma=gamma)
+        torch.cuda.synchronize()
+        ref = self.ora.block_forward(seqs, bonus, q_rope_pos=q_rope_pos, gamma=gamma)
+        return (toks.cpu().numpy(), logits.cpu().numpy().astype(np.float64).reshape(n, gamma - 1, -1), ref)
+
+    def close(self):
+        self.gpu.close()
+
+
+class Agreement:
+    """Pools argmax agreement over many blocks."""
+
+    def __init__(self):
+        self.n = 0
+        self.ok = 0
+        self.max_rel = 0.0
+
+    def add(self, toks, logits, ref):
+        rl = ref["logits"]
+        err = np.abs(logits - rl).max()
+        scale = np.abs(rl).max()
+        self.max_rel = max(self.max_rel, err / scale)
+        assert err <= LOGIT_REL_TOL * scale, f"max|dlogit| {err:.4g} > {LOGIT_REL_TOL} * {scale:.4g}"
+        s = np.sort(rl, axis=-1)
+        keep = (s[..., -1] - s[..., -2]) >= NEAR_TIE
+        self.n += int(keep.sum())
+        self.ok += int(((toks == ref["tokens"]) & keep).sum())
+
+    def check(self, min_positions=1):
+        assert self.n >= min_positions, f"only {self.n} positions outside near-ties"
+        rate = self.ok / self.n
+        assert rate >= AGREE_MIN, f"argmax agreement {rate:.4f} over {self.n} positions"
+        return rate
+
+
+def pool_view(gpu: B.Drafter):
+    """The whole KV pool as a host numpy uint16 array [L, P, 2, nkv, 16*hd]."""
+    geo = gpu.dflash_pool_geometry()
+    m = gpu.m
+    buf = torch.empty(geo["pool_bytes"] // 2, dtype=torch.int16)
+    gpu.dflash_debug_copy(B.DFLASH_BUF_POOL, buf)
+    return buf.numpy().view(np.uint16).reshape(m["num_layers"], geo["num_pages"], 2, m["num_kv_heads"], -1)
+
+
+def read_i32(gpu, which, n):
+    buf = torch.empty(n, dtype=torch.int32)
+    gpu.dflash_debug_copy(which, buf)
+    return buf.numpy()
+
+
+def read_i64(gpu, which, n):
+    buf = torch.empty(n, dtype=torch.int64)
+    gpu.dflash_debug_copy(which, buf)
+    return buf.numpy()

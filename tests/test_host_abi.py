@@ -1,0 +1,99 @@
+"""CPU-side checks of the boundary: the library loads, exports every entry point the
+header declares, and rejects bad configurations before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import synth
+from block_diffusion_draft_02_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", f)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(dflash_\w+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_entry_point():
+    L = B.lib()
+    decl = _declared()
+    assert {"dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_destroy"} <= set(decl)
+    for n in decl:
+        assert hasattr(L, n), n
+    assert set(B.EXPORTED) == set(decl)
+
+
+def test_strerror_names():
+    L = B.lib()
+    assert L.dflash_strerror(-3) == b"KV pool exhausted"
+    assert L.dflash_strerror(0) == b"ok"
+
+
+def _null_weights(m):
+    lay = (B.dflash_layer_weights * m["num_layers"])()
+    for l in range(m["num_layers"]):
+        for f, _ in B.dflash_layer_weights._fields_:
+            setattr(lay[l], f, 0x1000)
+    w = B.dflash_weights(fc=0x1000, hidden_norm=0x1000, norm=0x1000, embed_tokens=0x1000,
+                         lm_head=0x1000, layers=lay)
+    return w, lay
+
+
+@pytest.mark.parametrize("change", [
+    dict(head_dim=48), dict(num_kv_heads=3), dict(gamma_max=17), dict(gamma_max=1),
+    dict(hidden=200), dict(intermediate=500), dict(mask_token_id=5000), dict(num_q_heads=32, num_kv_heads=2),
+])
+def test_create_rejects_unsupported_shapes_before_any_gpu_call(change):
+    m = dict(synth.model("tiny-L2-h256"), **change)
+    cfg, keep = B.make_config(m, 128, 1)
+    w, lay = _null_weights(synth.model("tiny-L2-h256"))
+    ctx = C.c_void_p()
+    rc = B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx))
+    assert rc == B.DFLASH_EINVAL and not ctx.value
+
+
+def test_create_rejects_bad_pool_arguments():
+    m = synth.model("tiny-L2-h256")
+    w, lay = _null_weights(m)
+    for kw in [dict(max_batch=0), dict(max_batch=33), dict(num_pages=1)]:
+        cfg, keep = B.make_config(m, 128, kw.get("max_batch", 1), num_pages=kw.get("num_pages", 0))
+        ctx = C.c_void_p()
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    # a page order that is not a permutation of 1..P-1 (P = 11 here)
+    for order in ([1, 2, 3], list(range(0, 10)), [1] * 10):
+        cfg, keep = B.make_config(m, 128, 1, page_order=order)
+        ctx = C.c_void_p()
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+
+
+def test_null_arguments():
+    L = B.lib()
+    m = synth.model("tiny-L2-h256")
+    cfg, keep = B.make_config(m, 128, 1)
+    ctx = C.c_void_p()
+    assert L.dflash_create(C.byref(cfg), None, None, C.byref(ctx)) == B.DFLASH_EINVAL
+    assert L.dflash_create(None, None, None, C.byref(ctx)) == B.DFLASH_EINVAL
+    w, lay = _null_weights(m)
+    lay[1].down_proj = None
+    assert L.dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    assert L.dflash_ctx_kv_append(None, 0, None, None, 1, None) == B.DFLASH_EINVAL
+    assert L.dflash_block_forward(None, 1, None, None, None, 16, None, None, None) == B.DFLASH_EINVAL
+    L.dflash_destroy(None)
+
+
+def test_config_struct_layout_matches_header():
+    # offsets of the C struct on x86-64 (natural alignment)
+    assert B.dflash_config.rope_theta.offset == 48
+    assert B.dflash_config.yarn_factor.offset == 64
+    assert B.dflash_config.layer_sliding.offset == 104
+    assert B.dflash_config.page_order.offset == 128
+    assert C.sizeof(B.dflash_config) == 136
+    assert C.sizeof(B.dflash_layer_weights) == 88 and C.sizeof(B.dflash_weights) == 48
