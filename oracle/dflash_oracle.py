@@ -41,6 +41,16 @@ def widen(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
     return u.view(np.float32).astype(dtype)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (8 significant bits, ties to even), in one step
+    from x's own precision: x = f * 2^e with 0.5 <= |f| < 1, and f * 256 is rounded to an
+    integer half-to-even (exact arithmetic in binary64). Values stay in x's float type.
+    (bf16 subnormals, below 2^-126, do not occur in the drafter's K/V.)"""
+    x = np.asarray(x)
+    f, e = np.frexp(x.astype(np.float64))
+    return np.ldexp(np.round(f * 256.0) / 256.0, e).astype(x.dtype)
+
+
 # ----------------------------------------------------------------------------------
 # elementary steps
 # ----------------------------------------------------------------------------------
@@ -245,10 +255,17 @@ class Drafter:
     m: model dict (hidden, heads, taps, rope, window ...); weights: name -> bf16 bits.
     """
 
-    def __init__(self, m: dict, weights: dict, dtype=np.float64, cache_weights: bool = True):
+    def __init__(self, m: dict, weights: dict, dtype=np.float64, cache_weights: bool = True,
+                 kv_bf16: bool = True):
         self.m = m
         self.bits = weights
         self.dtype = dtype
+        # The drafter's KV cache holds bf16 values (spark_model/layers/dflash_head/
+        # from_weights.rs, from_weights: the paged drafter pool is KvCacheDtype::Bf16;
+        # spark_model/layers/dflash_head.rs: the gamma-block attention reads BF16 K/V from
+        # the layer pool). Every K/V row written to the cache -- context rows and the
+        # block's own rows -- is therefore rounded to bf16; kv_bf16=False keeps them exact.
+        self.kv_bf16 = kv_bf16
         self.cache_weights = cache_weights
         self._cache = {}
         hd = m["head_dim"]
@@ -270,6 +287,9 @@ class Drafter:
 
     def lw(self, l: int, name: str) -> np.ndarray:
         return self.w(f"layers.{l}.{name}")
+
+    def cache_store(self, x: np.ndarray) -> np.ndarray:
+        return round_bf16(x) if self.kv_bf16 else x
 
     def sliding(self, l: int) -> bool:
         ls = self.m.get("layer_sliding")
@@ -294,8 +314,9 @@ class Drafter:
         return rms_norm(f, self.w("hidden_norm"), m["rms_eps"])
 
     def ctx_kv(self, F: np.ndarray, positions: np.ndarray):
-        """Per layer: K = rope(k_norm(F Wk^T per head), pos), V = F Wv^T.
-        Context features are not passed through input_layernorm.
+        """Per layer: K = rope(k_norm(F Wk^T per head), pos), V = F Wv^T, as stored in the
+        cache (bf16 unless kv_bf16 is off). Context features are not passed through
+        input_layernorm.
         [memra] DflashDraft::ingest_ctx; DflashDraft::forward_block (ctx features are
         norm-free per layer)."""
         m = self.m
@@ -307,7 +328,7 @@ class Drafter:
             v = (F @ self.lw(l, "v_proj").T).reshape(n, nkv, hd)
             k = rms_norm(k, self.lw(l, "k_norm"), m["rms_eps"])
             k = self.rope_rows(k, np.asarray(positions)[:, None])
-            out.append((k, v))
+            out.append((self.cache_store(k), self.cache_store(v)))
         return out
 
     # -- one gamma block ------------------------------------------------------------
@@ -356,8 +377,8 @@ class Drafter:
             vb = (xn @ self.lw(l, "v_proj").T).reshape(gamma, nkv, hd)
             q = self.rope_rows(rms_norm(q, self.lw(l, "q_norm"), eps), bpos[:, None])
             kb = self.rope_rows(rms_norm(kb, self.lw(l, "k_norm"), eps), bpos[:, None])
-            k_all = np.concatenate([ctx_k[l], kb], axis=0)
-            v_all = np.concatenate([ctx_v[l], vb], axis=0)
+            k_all = np.concatenate([ctx_k[l], self.cache_store(kb)], axis=0)
+            v_all = np.concatenate([ctx_v[l], self.cache_store(vb)], axis=0)
             k_pos = np.concatenate([np.asarray(ctx_pos, dtype=np.int64), bpos])
             win = int(m.get("sliding_window", 0) or 0) if self.sliding(l) else 0
             attn = gqa_attention(q, bpos, k_all, v_all, k_pos, scale, win).reshape(gamma, nh * hd)
@@ -396,9 +417,10 @@ class Engine:
     """
 
     def __init__(self, m: dict, weights: dict, max_seq_len: int, max_batch: int,
-                 page_order=None, dtype=np.float64, cache_weights: bool = True, num_pages: int = 0):
+                 page_order=None, dtype=np.float64, cache_weights: bool = True, num_pages: int = 0,
+                 kv_bf16: bool = True):
         self.m = m
-        self.d = Drafter(m, weights, dtype, cache_weights)
+        self.d = Drafter(m, weights, dtype, cache_weights, kv_bf16)
         self.max_seq_len = max_seq_len
         self.max_batch = max_batch
         self.pool = PagePool(max_seq_len, m["gamma_max"], max_batch, page_order, num_pages)

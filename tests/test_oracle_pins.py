@@ -350,7 +350,7 @@ def test_micro_drafter_brute_force():
         Wbig[k] = synth.f32_to_bf16_bits((a if a.ndim == 1 else a * 25.0).astype(np.float32))
     taps = synth.gen_hidden(m, 77, 5)
     ctx_pos = np.array([0, 1, 2, 4, 7])
-    eng = O.Engine(m, Wbig, max_seq_len=16, max_batch=1)
+    eng = O.Engine(m, Wbig, max_seq_len=16, max_batch=1, kv_bf16=False)
     eng.ctx_kv_append(0, taps, positions=ctx_pos)
     res = eng.block_forward([0], [9], q_rope_pos=[8], gamma=3)
     Wf = {k: O.widen(v).tolist() for k, v in Wbig.items()}
@@ -374,8 +374,8 @@ def _engine_with_ctx(m, W, n=64, seed=1001, positions=None, **kw):
 
 def test_position_shift_invariance_plain(tiny):
     m, W = tiny
-    e1 = _engine_with_ctx(m, W)
-    e2 = _engine_with_ctx(m, W, positions=np.arange(64) + 5000)
+    e1 = _engine_with_ctx(m, W, kv_bf16=False)
+    e2 = _engine_with_ctx(m, W, positions=np.arange(64) + 5000, kv_bf16=False)
     a = e1.block_forward([0], [17], gamma=16)
     b = e2.block_forward([0], [17], q_rope_pos=[5064], gamma=16)
     assert np.allclose(a["logits"], b["logits"], atol=1e-9)
@@ -385,8 +385,8 @@ def test_position_shift_invariance_yarn_and_window(tiny):
     m, W = tiny
     m = dict(m, rope_type="yarn", yarn_factor=4.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,
              yarn_beta_slow=1.0, sliding_window=24, layer_sliding=[True, False])
-    e1 = _engine_with_ctx(m, W)
-    e2 = _engine_with_ctx(m, W, positions=np.arange(64) + 777)
+    e1 = _engine_with_ctx(m, W, kv_bf16=False)
+    e2 = _engine_with_ctx(m, W, positions=np.arange(64) + 777, kv_bf16=False)
     a = e1.block_forward([0], [3], gamma=16)
     b = e2.block_forward([0], [3], q_rope_pos=[777 + 64], gamma=16)
     assert np.allclose(a["logits"], b["logits"], atol=1e-9)
@@ -518,7 +518,50 @@ def test_yarn_mscale_scales_cached_keys(tiny):
     for l in range(m["num_layers"]):
         W1[f"layers.{l}.k_norm"] = np.full(m["head_dim"], 0x3F80, dtype=np.uint16)
     for mm, scale in [(m, 1.0), (my, 0.1 * math.log(8.0) + 1.0)]:
-        e = _engine_with_ctx(mm, W1, n=9)
+        e = _engine_with_ctx(mm, W1, n=9, kv_bf16=False)
         k = e.seqs[0]["k"][1]                       # [9, nkv, hd]
         n = np.linalg.norm(k, axis=-1)
         assert np.allclose(n, scale * math.sqrt(m["head_dim"]), rtol=1e-4)
+
+
+# ---------------------------------------------------------------- the bf16 cache
+
+def test_round_bf16_hand_values():
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8 + 2 ** -40),
+                  3.140625, 1e-3, -0.0])
+    want = [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -(1 + 2 ** -7), 3.140625, 131 / 128 * 2 ** -10, -0.0]
+    assert O.round_bf16(x).tolist() == want
+
+
+def test_round_bf16_is_nearest_bf16():
+    """Brute force against the two bf16 neighbours of every value."""
+    g = np.random.default_rng(11)
+    x = np.concatenate([g.standard_normal(20000), g.standard_normal(2000) * 1e-3, g.standard_normal(2000) * 300])
+    r = O.round_bf16(x)
+    bits = r.astype(np.float32).view(np.uint32)
+    assert not (bits & 0xFFFF).any()                                    # representable in bf16
+    lo = (x.astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32).astype(np.float64)
+    _, e = np.frexp(lo)                       # |lo| = f 2^e, 0.5 <= f < 1: bf16 spacing 2^(e-8)
+    hi = lo + np.sign(x) * np.ldexp(1.0, e - 8)
+    # r is one of the neighbours, and no farther from x than the other one
+    assert np.all((r == lo) | (r == hi))
+    assert np.all(np.abs(r - x) <= np.minimum(np.abs(lo - x), np.abs(hi - x)))
+
+
+def test_cache_holds_bf16_rounded_kv(tiny):
+    m, W = tiny
+    e1 = _engine_with_ctx(m, W, n=40)
+    e0 = _engine_with_ctx(m, W, n=40, kv_bf16=False)
+    for l in range(m["num_layers"]):
+        for kv in ("k", "v"):
+            a, b = e1.seqs[0][kv][l], e0.seqs[0][kv][l]
+            assert np.array_equal(a, O.round_bf16(b))
+            assert np.abs(a - b).max() <= 2 ** -8 * np.abs(b).max()
+    # the block's own K/V enter attention through the cache as well: with kv_bf16 off the
+    # logits move by a small, nonzero amount
+    a = e1.block_forward([0], [3], gamma=16)["logits"]
+    b = _engine_with_ctx(m, W, n=40, kv_bf16=False)
+    b.seqs[0]["k"] = [O.round_bf16(k) for k in b.seqs[0]["k"]]
+    b.seqs[0]["v"] = [O.round_bf16(v) for v in b.seqs[0]["v"]]
+    bl = b.block_forward([0], [3], gamma=16)["logits"]
+    assert 0 < np.abs(a - bl).max() < 0.05 * np.abs(a).max()
