@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash drafter's hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the context append of the rows
+a propose round commits (fc + hidden_norm, per-layer K/V with k_norm + RoPE, page
+allocation and writeback; `--append-rows`, default 16 = a fully accepted gamma=16 block)
+followed by one gamma=16 block forward (embedding, every layer, final norm, lm_head +
+argmax). Workload: the 8-layer, hidden-2048, GQA 32:4, head_dim-128, ff-6144,
+vocab-151936 drafter with 5 taps of hidden 2048, one sequence whose context is
+prefilled (untimed) with 4096 rows of N(0,1) hidden states; weights N(0,0.02) bf16
+from seed. Inputs are resident in HBM before the timed region.
+
+Prints one JSON line on stdout: blocks/s (value), tokens/s, the roofline of the
+dominant kernel class measured live with HIP events over the timed region, a per-class
+breakdown, a 16-sequence batched line, and the CPU oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "drafted γ=16 blocks/sec at batch 1 and 16; achieved HBM GB/s vs peak"
+WORKLOAD = "qwen3-L8-h2048-ctx4096-b1"
+WORKLOAD_B16 = "qwen3-L8-h2048-b16-ctx512to8192"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_bytes(m, M):
+    """Algorithmic HBM bytes of the forward's weight-streaming GEMMs for M block rows:
+    each weight byte once, the bf16 activation in, the fp32 result out."""
+    h, hd, nh, nkv, ff = m["hidden"], m["head_dim"], m["num_q_heads"], m["num_kv_heads"], m["intermediate"]
+    qd, kvd = nh * hd, nkv * hd
+    shapes = [(qd + 2 * kvd, h), (h, qd), (2 * ff, h), (h, ff)]
+    per_layer = sum(N * K * 2 + M * K * 2 + M * N * 4 for N, K in shapes)
+    return per_layer * m["num_layers"]
+
+
+def lmhead_bytes(m, M):
+    return m["vocab"] * m["hidden"] * 2 + M * m["hidden"] * 2
+
+
+def attn_bytes(m, kv_lens, gamma):
+    """K and V bytes every layer reads: (C + gamma) keys per band, both halves, all kv heads."""
+    kvd = m["num_kv_heads"] * m["head_dim"]
+    return sum((c + gamma) for c in kv_lens) * kvd * 2 * 2 * m["num_layers"]
+
+
+def forward_bytes(m, kv_lens, gamma):
+    """Algorithmic bytes of one forward: every weight once (layers, lm_head, the touched
+    embedding rows) and the K/V of every visible key, per layer."""
+    h, hd, nh, nkv, ff = m["hidden"], m["head_dim"], m["num_q_heads"], m["num_kv_heads"], m["intermediate"]
+    qd, kvd = nh * hd, nkv * hd
+    layer_w = ((qd + 2 * kvd) * h + h * qd + 2 * ff * h + h * ff) * 2 + (2 * h + 2 * hd) * 2
+    return (layer_w * m["num_layers"] + m["vocab"] * h * 2 + h * 2
+            + attn_bytes(m, kv_lens, gamma) + len(kv_lens) * 2 * h * 2)
+
+
+def append_bytes(m, n):
+    h, kvd, L = m["hidden"], m["num_kv_heads"] * m["head_dim"], m["num_layers"]
+    return (h * m["num_taps"] * m["target_hidden"] * 2 + L * 2 * kvd * h * 2
+            + n * m["num_taps"] * m["target_hidden"] * 2 + n * L * 2 * kvd * 2)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"]), info[0].get("internal_api", "blas")
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_baseline(m, W, H_ctx, H_steps, bonus, a, gamma, budget_s):
+    """The oracle as it stands, on this host: untimed prefill + fp64 weight widening, then
+    steps (append a rows + one block forward) until `budget_s` of timed work."""
+    from oracle import dflash_oracle as O
+    eng = O.Engine(m, W, H_ctx.shape[0] + 64 * a + gamma + 16, 1)
+    eng.ctx_kv_append(0, H_ctx)
+    for n, _, _ in __import__("synth").weight_specs(m):
+        eng.d.w(n)
+    t0 = time.perf_counter()
+    n = 0
+    n_max = min(64, H_steps.shape[0] // a, len(bonus))
+    while True:
+        eng.ctx_kv_append(0, H_steps[n * a:(n + 1) * a])
+        eng.block_forward([0], [int(bonus[n])], gamma=gamma)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= n_max:
+            break
+    thr, api = blas_threads()
+    return dict(value=n / el, unit="blocks/s", cores=thr, kind="oracle",
+                sample=f"{n} steps ({a}-row context append + one gamma={gamma} block forward) of the "
+                       f"same workload after an untimed {H_ctx.shape[0]}-row prefill and fp64 weight "
+                       f"widening; numpy float64, BLAS={api}; host CPU: {cpu_model()}",
+                seconds=el)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--append-rows", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="timed budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path would shard data-parallel over sequences, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from block_diffusion_draft_02_amd import binding as B
+
+    dev = torch.device("cuda:0")
+    w = synth.workload(WORKLOAD)
+    m = w["model_cfg"]
+    gamma = m["gamma_max"]
+    a = args.append_rows
+    ctx = w["ctx"][0]
+    total = args.warmup + args.steps + 8
+    t = time.perf_counter()
+    W = synth.gen_weights(m, w["seed"])
+    H_ctx = synth.gen_hidden(m, w["seed"], ctx, 0)
+    H_steps = synth.gen_hidden(m, w["seed"], total * a, 1)
+    bonus = synth.gen_bonus(m, w["seed"], total)
+    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f}s")
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    Wd = {k: to_dev(v) for k, v in W.items()}
+    max_seq = ctx + total * a + gamma + 16
+    d = B.Drafter(m, Wd, max_seq, 1)
+    d.dflash_ctx_kv_append(0, to_dev(H_ctx))
+    Hs = to_dev(H_steps)
+    toks = torch.empty((1, gamma - 1), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    step_i = [0]
+
+    def step():
+        i = step_i[0]
+        d.dflash_ctx_kv_append(0, Hs[i * a:(i + 1) * a])
+        d.dflash_block_forward([0], [int(bonus[i])], toks, gamma=gamma)
+        step_i[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-class breakdown on a few untimed steps (every launch bracketed by events)
+    d.dflash_timing(list(B.K_CLASSES))
+    nb = 4
+    for _ in range(nb):
+        step()
+    torch.cuda.synchronize()
+    br = d.dflash_timing_read()
+    d.dflash_timing([])
+    breakdown = {k: dict(ms_per_step=v[0] / nb, launches_per_step=v[1] / nb) for k, v in br.items() if v[1]}
+    dominant = max(breakdown, key=lambda k: breakdown[k]["ms_per_step"])
+    log("[bench] breakdown (ms/step): " + ", ".join(f"{k}={v['ms_per_step']:.4f}" for k, v in breakdown.items()))
+
+    # the timed region: only the dominant class is bracketed by events
+    kv0 = d.dflash_seq_info(0)[0]
+    d.dflash_timing([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom = d.dflash_timing_read()[dominant]
+    d.dflash_timing([])
+    el = t1 - t0
+    ms_step = el / args.steps * 1e3
+    blocks = args.steps / el
+    M = gamma
+    mean_kv = kv0 + a * (args.steps + 1) / 2
+    dom_bytes_step = {"gemm": gemm_bytes(m, M), "lmhead": lmhead_bytes(m, M),
+                      "attn": attn_bytes(m, [mean_kv], gamma)}.get(dominant)
+    roofline = None
+    if dom_bytes_step is not None and dom[1]:
+        launches_per_step = dom[1] / args.steps
+        avg_ms = dom[0] / dom[1]
+        per_launch = dom_bytes_step / launches_per_step
+        achieved = per_launch / (avg_ms * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel_class=dominant,
+                        avg_launch_us=round(avg_ms * 1e3, 3), launches_per_step=launches_per_step,
+                        algorithmic_bytes_per_launch=int(per_launch))
+    step_bytes = forward_bytes(m, [mean_kv], gamma) + append_bytes(m, a)
+    log(f"[bench] {blocks:.1f} blocks/s, {ms_step:.3f} ms/step, whole-step {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(blocks, 2), "unit": "blocks/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": 1, "ctx": ctx, "gamma": gamma,
+                   "append_rows_per_step": a, "layers": m["num_layers"], "hidden": m["hidden"],
+                   "vocab": m["vocab"]},
+        "tokens_per_s": round(blocks * (gamma - 1), 1),
+        "step_algorithmic_bytes": int(step_bytes),
+        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in breakdown.items()},
+    }
+    d.close()
+
+    if not args.no_batch16:
+        out["batch16"] = bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev)
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        out["cpu_baseline"] = run_cpu_baseline(m, W, H_ctx, H_steps, bonus, a, gamma, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
+    """16 sequences with contexts U[512, 8192] on a shared pool with permuted pages; a step
+    appends `a` rows to every sequence and runs one 16-band forward. Same weights as the
+    batch-1 line (the shapes, not the draws, set the cost)."""
+    w = synth.workload(WORKLOAD_B16)
+    nb = w["batch"]
+    dev = torch.device("cuda:0")
+    lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, w["seed"])
+    steps = max(5, args.steps // 2)
+    total = args.warmup + steps
+    max_seq = int(lens.max()) + total * a + gamma + 16
+    per_seq = -(-(max_seq + gamma + 1) // 16)
+    order = synth.gen_page_order(per_seq * nb, w["seed"])
+    d = B.Drafter(m, Wd, max_seq, nb, page_order=order)
+    for s in range(nb):
+        d.dflash_ctx_kv_append(s, to_dev(synth.gen_hidden(m, w["seed"], int(lens[s]), s)))
+    Hs = to_dev(synth.gen_hidden(m, w["seed"], total * a, 100))
+    bonus = synth.gen_bonus(m, w["seed"], nb * total)
+    toks = torch.empty((nb, gamma - 1), dtype=torch.int32, device=dev)
+    seqs = list(range(nb))
+
+    def step(i):
+        for s in seqs:
+            d.dflash_ctx_kv_append(s, Hs[i * a:(i + 1) * a])
+        d.dflash_block_forward(seqs, bonus[i * nb:(i + 1) * nb], toks, gamma=gamma)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    d.dflash_timing(list(B.K_CLASSES))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    br = d.dflash_timing_read()
+    d.dflash_timing([])
+    d.close()
+    blocks = nb * steps / el
+    log(f"[bench] batch16: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step")
+    return dict(workload=WORKLOAD_B16, value=round(blocks, 2), unit="blocks/s", steps=steps,
+                ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
+                ctx_lengths=[int(x) for x in lens], timing="all launch classes bracketed by events",
+                kernels_ms_per_step={k: round(v[0] / steps, 4) for k, v in br.items() if v[1]})
+
+
+if __name__ == "__main__":
+    main()

@@ -13,6 +13,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.
 DFLASH_OK, DFLASH_EINVAL, DFLASH_ENOMEM, DFLASH_EPOOL, DFLASH_ERANGE, DFLASH_EHIP = 0, -1, -2, -3, -4, -5
 CODE_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EPOOL", -4: "ERANGE", -5: "EHIP"}
 DFLASH_BUF_POOL, DFLASH_BUF_KPOS, DFLASH_BUF_SLOTS, DFLASH_BUF_BLOCKTAB, DFLASH_BUF_HIDDEN = 0, 1, 2, 3, 4
+DFLASH_BUF_HIDDEN_LO = 5
 
 
 class dflash_config(C.Structure):
@@ -65,10 +66,13 @@ def lib():
         L.dflash_debug_copy.argtypes = [vp, i32, vp, C.c_size_t, C.c_size_t, vp]
         L.dflash_last_error.argtypes = [vp]
         L.dflash_last_error.restype = C.c_char_p
+        L.dflash_timing.argtypes = [vp, C.c_uint32]
+        L.dflash_timing_read.argtypes = [vp, C.POINTER(C.c_double), i64p, i32]
         L.dflash_strerror.argtypes = [C.c_int]
         L.dflash_strerror.restype = C.c_char_p
         for f in ("dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_seq_reset",
-                  "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy"):
+                  "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy", "dflash_timing",
+                  "dflash_timing_read"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -76,7 +80,10 @@ def lib():
 
 EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_destroy",
             "dflash_seq_reset", "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy",
-            "dflash_last_error", "dflash_strerror")
+            "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
+
+K_CLASSES = ("prologue", "gemm", "qkv_post", "attn", "attn_combine", "resid_norm", "silu",
+             "lmhead", "argmax", "append_gemm", "append_misc")
 
 
 class DflashError(RuntimeError):
@@ -192,6 +199,20 @@ class Drafter:
         self._check(self.L.dflash_pool_geometry(self.ctx, *[C.byref(v) for v in vals]))
         keys = ("num_pages", "pages_per_seq", "page_layer_bytes", "pool_bytes", "fused_kv_weight_bytes")
         return dict(zip(keys, [v.value for v in vals]))
+
+    def dflash_timing(self, classes):
+        """Time the launches of the named classes (see K_CLASSES); [] turns timing off."""
+        mask = 0
+        for c in classes:
+            mask |= 1 << K_CLASSES.index(c)
+        self._check(self.L.dflash_timing(self.ctx, mask))
+
+    def dflash_timing_read(self):
+        """{class: (milliseconds, launches)} since the last read."""
+        n = len(K_CLASSES)
+        ms, cnt = (C.c_double * n)(), (C.c_int64 * n)()
+        self._check(self.L.dflash_timing_read(self.ctx, ms, cnt, n))
+        return {K_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
 
     def dflash_debug_copy(self, buffer, dst, offset=0, nbytes=None, stream=None):
         """Copy into a torch tensor (host or device) `dst`; nbytes defaults to dst's size."""

@@ -22,6 +22,13 @@ __device__ __forceinline__ bf16 f2bf(float f) {
   return (bf16)(u >> 16);
 }
 
+// v = bf2f(hi) + bf2f(lo) to about 16 significant bits: a float carried through bf16
+// MFMA operands as two terms
+__device__ __forceinline__ void split_bf16(float v, bf16& hi, bf16& lo) {
+  hi = f2bf(v);
+  lo = f2bf(v - bf2f(hi));
+}
+
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }

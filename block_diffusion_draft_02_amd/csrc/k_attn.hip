@@ -2,9 +2,11 @@
 // every block query sees every context key and every block key; scale 1/sqrt(head_dim);
 // sliding layers additionally hide keys with q_pos - k_pos >= window).
 //
-// Work split: one workgroup per (band, kv head, key chunk). Its four wavefronts own the
-// band's gamma * G query rows of that kv head (G = query heads per kv head), 16 or 32 rows
-// each, and walk the chunk 32 keys at a time:
+// Work split: one workgroup per (band, kv head, key chunk of at most 256 keys). The
+// workgroup first stages the chunk's K rows, V pages and key positions in LDS with every
+// load in flight at once; its four wavefronts then own the band's gamma * G query rows of
+// that kv head (G = query heads per kv head), 16 or 32 rows each, and walk the chunk 32 keys
+// at a time:
 //   S^T = K Q^T   two 16x16x32 MFMA tiles per 32 keys; the key order inside the tiles is
 //                 permuted so that every lane ends up holding 8 consecutive keys of one row
 //   online softmax per row (exp2 domain), lane-local partial sums
@@ -18,8 +20,22 @@
 
 namespace dfl {
 
+constexpr int KCMAX = 256;  // keys per chunk (16 pages); the runtime never plans more
+
+// The chunk's keys in LDS: K rows padded to HD + 8 (1 KB + 16 B rows keep the MFMA operand
+// reads of any 8 consecutive lanes on distinct banks), V pages as stored ([d][16] per page),
+// the stamped position of every key, and the chunk's physical pages.
+template <int HD>
+struct AttnLds {
+  bf16 k[KCMAX][HD + 8];
+  bf16 v[KCMAX / PAGE][HD][PAGE];
+  int pos[KCMAX];
+  int page[KCMAX / PAGE];
+};
+
 template <int HD, int RT>
 __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
+                                                    const bf16* __restrict__ Q_lo,
                                                     const Band* __restrict__ bands, int n_bands,
                                                     int gamma, int nh, KvGeom g, int layer, int sw,
                                                     int window, float scale_log2,
@@ -28,6 +44,8 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
   constexpr int NS = HD / 32;
   constexpr int ND = HD / 16;
   constexpr int RPAD = 4 * RT * 16;
+  constexpr int P8 = HD / 8;  // 16-byte pieces per K row
+  __shared__ __attribute__((aligned(16))) AttnLds<HD> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, grp = lane >> 4;
   const int kvh = blockIdx.y;
@@ -39,23 +57,64 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
   const int seq = bands[b].seq, C = bands[b].kv_len, qpos0 = bands[b].q_pos;
   const int ch = cg - bands[b].base[sw];
   const int kend = C + gamma;
-  const int k0 = bands[b].kstart[sw] + ch * bands[b].ck[sw];
+  const int k0 = bands[b].kstart[sw] + ch * bands[b].ck[sw];   // page aligned
   const int k1 = min(k0 + bands[b].ck[sw], kend);
+  const int npg = (k1 - k0 + PAGE - 1) / PAGE;                 // pages holding keys of the chunk
+  const int nst = (k1 - k0 + 31) / 32 * 2;                     // pages staged: whole 32-key tiles
   const int R = gamma * G;
-  const int* btrow = g.bt + (size_t)seq * g.per_seq;
   const size_t pl = page_layer_elems(nkv, HD);
   const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
 
-  bf16x8 qb[RT][NS];
+  // ---- stage the chunk: page ids, then every K row, V page and position at once. A tile's
+  // second page past the chunk's end is the zeroed sentinel page 0, so every value the MFMAs
+  // read is finite (masked keys then contribute exactly zero).
+  if (threadIdx.x < nst)
+    sm.page[threadIdx.x] = threadIdx.x < npg ? g.bt[(size_t)seq * g.per_seq + (k0 >> 4) + threadIdx.x] : 0;
+  __syncthreads();
+  {
+    const int nk = nst * PAGE;           // keys staged (the tail past k1 is masked below)
+    const int pieces = nk * P8;          // K pieces; V has the same count
+    for (int base = 0; base < pieces; base += 256 * 8) {
+      u32x4 kr[8], vr[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pc = base + u * 256 + threadIdx.x;
+        if (pc < pieces) {
+          const int kl = pc / P8, d8 = pc % P8;
+          const bf16* pg = lpool + (size_t)sm.page[kl >> 4] * pl;
+          kr[u] = *reinterpret_cast<const u32x4*>(pg + ((size_t)kvh * PAGE + (kl & 15)) * HD + d8 * 8);
+          // V: piece pc is the pc-th 16 bytes of the chunk's [page][d][16] block
+          const int vp = pc / (HD * 2), vo = pc % (HD * 2);
+          vr[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)sm.page[vp] * pl + (size_t)(nkv + kvh) * HD * PAGE + vo * 8);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pc = base + u * 256 + threadIdx.x;
+        if (pc < pieces) {
+          const int kl = pc / P8, d8 = pc % P8;
+          *reinterpret_cast<u32x4*>(&sm.k[kl][d8 * 8]) = kr[u];
+          *reinterpret_cast<u32x4*>(&sm.v[0][0][0] + (size_t)pc * 8) = vr[u];
+        }
+      }
+    }
+    if (window > 0)
+      for (int kl = threadIdx.x; kl < nk; kl += 256) sm.pos[kl] = g.kpos[(size_t)sm.page[kl >> 4] * PAGE + (kl & 15)];
+  }
+
+  bf16x8 qb[RT][NS], ql[RT][NS];
   int qpos[RT];
 #pragma unroll
   for (int j = 0; j < RT; ++j) {
     const int r = (wave * RT + j) * 16 + c;
     const bool rv = r < R;
     const int i = rv ? r % gamma : 0, hq = rv ? r / gamma : 0;
-    const bf16* qp = Q + ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + grp * 8;
+    const size_t qo = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + grp * 8;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[j][s] = ld8(qp + s * 32);
+    for (int s = 0; s < NS; ++s) {
+      qb[j][s] = ld8(Q + qo + s * 32);
+      ql[j][s] = ld8(Q_lo + qo + s * 32);
+    }
     qpos[j] = qpos0 + i;
   }
   float m_run[RT], l_run[RT];
@@ -67,32 +126,27 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();
 
-  for (int kt = k0; kt < k1; kt += 32) {
+  for (int kt = 0; kt < k1 - k0; kt += 32) {
     f32x4 sacc[RT][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int key = kt + (c >> 2) * 8 + t * 4 + (c & 3);
-      const int page = key < k1 ? btrow[key >> 4] : 0;
-      const bf16* kp = lpool + (size_t)page * pl + ((size_t)kvh * PAGE + (key & 15)) * HD + grp * 8;
+      const int kl = kt + (c >> 2) * 8 + t * 4 + (c & 3);   // < npg * 16: staged
 #pragma unroll
       for (int j = 0; j < RT; ++j) sacc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const bf16x8 a = ld8(kp + s * 32);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.k[kl][s * 32 + grp * 8]));
 #pragma unroll
-        for (int j = 0; j < RT; ++j) sacc[j][t] = mfma16(a, qb[j][s], sacc[j][t]);
+        for (int j = 0; j < RT; ++j) {
+          sacc[j][t] = mfma16(a, qb[j][s], sacc[j][t]);
+          sacc[j][t] = mfma16(a, ql[j][s], sacc[j][t]);
+        }
       }
     }
     // this lane now holds, for query row c of every row tile, keys kbase + 0..7
-    const int kbase = kt + grp * 8;
-    const int pg8 = kbase < k1 ? btrow[kbase >> 4] : 0;
-    int kp8[8];
-    if (window > 0) {
-      const int* kq = g.kpos + (size_t)pg8 * PAGE + (kbase & 15);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kp8[e] = kq[e];
-    }
+    const int kbl = kt + grp * 8;
     bf16x8 pb[RT];
 #pragma unroll
     for (int j = 0; j < RT; ++j) {
@@ -100,9 +154,8 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int key = kbase + e;
-        bool ok = key < k1;
-        if (window > 0) ok = ok && (qpos[j] - kp8[e] < window);
+        bool ok = k0 + kbl + e < k1;
+        if (window > 0) ok = ok && (qpos[j] - sm.pos[kbl + e] < window);
         sv[e] = ok ? sacc[j][e >> 2][e & 3] * scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, sv[e]);
       }
@@ -123,10 +176,10 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
       for (int dt = 0; dt < ND; ++dt) o[j][dt] *= alpha;
       pb[j] = pack8(p);
     }
-    const bf16* vp = lpool + (size_t)pg8 * pl + (size_t)(nkv + kvh) * HD * PAGE + (kbase & 15);
+    const bf16* vp = &sm.v[kbl >> 4][0][kbl & 15];
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
-      const bf16x8 a = ld8(vp + (size_t)(dt * 16 + c) * PAGE);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + (size_t)(dt * 16 + c) * PAGE));
 #pragma unroll
       for (int j = 0; j < RT; ++j) o[j][dt] = mfma16(a, pb[j], o[j][dt]);
     }
@@ -152,7 +205,7 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
 
 static int attn_rt(int gamma, int G) { return gamma * G <= 64 ? 1 : 2; }
 
-hipError_t launch_block_attn(const bf16* Q, const Band* bands_dev, int n_bands, int total_chunks,
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_dev, int n_bands, int total_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st) {
   const int G = nh / g.nkv;
@@ -160,7 +213,7 @@ hipError_t launch_block_attn(const bf16* Q, const Band* bands_dev, int n_bands, 
   dim3 grid(total_chunks, g.nkv);
   const int rt = attn_rt(gamma, G);
 #define DFL_ATTN(HDV, RTV)                                                                   \
-  k_block_attn<HDV, RTV><<<grid, 256, 0, st>>>(Q, bands_dev, n_bands, gamma, nh, g, layer, sw, \
+  (void)launch(k_block_attn<HDV, RTV>, grid, 256, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, \
                                                window, scale_log2, part_o, part_ml)
   if (g.hd == 128) { if (rt == 1) DFL_ATTN(128, 1); else DFL_ATTN(128, 2); }
   else if (g.hd == 64) { if (rt == 1) DFL_ATTN(64, 1); else DFL_ATTN(64, 2); }
@@ -170,15 +223,21 @@ hipError_t launch_block_attn(const bf16* Q, const Band* bands_dev, int n_bands, 
   return hipGetLastError();
 }
 
-// one wavefront per (band, kv head, query row): merge the band's chunks in chunk order
+// merge a band's chunks in chunk order: one workgroup per (band, kv head, 16 query rows);
+// thread (row, 8-float slice of the head)
 template <int HD>
-__global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ part_o,
-                                                     const float* __restrict__ part_ml,
-                                                     const Band* __restrict__ bands, int gamma,
-                                                     int nh, int nkv, int sw, int rpad,
-                                                     bf16* __restrict__ out) {
-  const int b = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z, l = threadIdx.x;
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      const Band* __restrict__ bands, int gamma,
+                                                      int nh, int nkv, int sw, int rpad,
+                                                      bf16* __restrict__ out,
+                                                      bf16* __restrict__ out_lo) {
+  constexpr int DC = HD / 8;
+  const int b = blockIdx.x, kvh = blockIdx.y;
+  const int rl = threadIdx.x / DC, dc = threadIdx.x % DC;
+  const int r = blockIdx.z * 16 + rl;
   const int G = nh / nkv;
+  if (rl >= 16 || r >= gamma * G) return;
   const int i = r % gamma, hq = r / gamma;
   const int nch = bands[b].nch[sw], base = bands[b].base[sw];
   float M = -INFINITY;
@@ -186,42 +245,39 @@ __global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ p
     const size_t item = (size_t)(base + c) * nkv + kvh;
     M = fmaxf(M, part_ml[(item * rpad + r) * 2]);
   }
-  constexpr int E = HD > 64 ? HD / 64 : 1;
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
+#pragma unroll 4
   for (int c = 0; c < nch; ++c) {
     const size_t item = (size_t)(base + c) * nkv + kvh;
     const float mc = part_ml[(item * rpad + r) * 2];
+    const float lc = part_ml[(item * rpad + r) * 2 + 1];
+    const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (item * rpad + r) * HD + dc * 8);
+    const f32x4 o0 = po[0], o1 = po[1];
     const float w = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
-    L += w * part_ml[(item * rpad + r) * 2 + 1];
-    const float* po = part_o + (item * rpad + r) * HD;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int d = l + 64 * e;
-      if (d < HD) acc[e] += w * po[d];
-    }
+    L += w * lc;
+    a0 += w * o0;
+    a1 += w * o1;
   }
   const float inv = 1.f / L;
-  bf16* o = out + ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD;
+  const size_t o = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + dc * 8;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int d = l + 64 * e;
-    if (d < HD) o[d] = f2bf(acc[e] * inv);
+  for (int e = 0; e < 4; ++e) {
+    split_bf16(a0[e] * inv, out[o + e], out_lo[o + e]);
+    split_bf16(a1[e] * inv, out[o + 4 + e], out_lo[o + 4 + e]);
   }
 }
 
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,
                                int n_bands, int gamma, int nh, int nkv, int hd, int sw,
-                               bf16* out, hipStream_t st) {
+                               bf16* out, bf16* out_lo, hipStream_t st) {
   const int G = nh / nkv;
   const int rpad = 4 * attn_rt(gamma, G) * 16;
-  dim3 grid(n_bands, nkv, gamma * G);
+  dim3 grid(n_bands, nkv, (gamma * G + 15) / 16);
   switch (hd) {
-    case 32: k_attn_combine<32><<<grid, 64, 0, st>>>(part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out); break;
-    case 64: k_attn_combine<64><<<grid, 64, 0, st>>>(part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out); break;
-    case 128: k_attn_combine<128><<<grid, 64, 0, st>>>(part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out); break;
+    case 32: (void)launch(k_attn_combine<32>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
+    case 64: (void)launch(k_attn_combine<64>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
+    case 128: (void)launch(k_attn_combine<128>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,6 +1,10 @@
 // BF16 MFMA GEMMs of the drafter: Y = A W^T with W row-major [N, K] (weights stored
 // [out_features, in_features]).
 //
+// Activations enter as two bf16 terms (hi + lo, about 16 significant bits): every k-step
+// issues one MFMA per term against the same exact bf16 weight operand. The weight stream,
+// not the MFMA rate, bounds these GEMMs at the forward's row counts.
+//
 //  * k_gemm_skinny: the weight-streaming form for the block forward (M = bands * gamma
 //    rows, at most 64 per launch). One wavefront owns 16 output columns over one K split
 //    and streams those 16 weight rows exactly once; the activation rows come from L2.
@@ -14,45 +18,121 @@
 
 namespace dfl {
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A, int lda, int M,
+// Depth of one activation chunk staged in LDS and of one weight chunk a wavefront has in
+// flight: 512 k = sixteen 16-byte loads per lane.
+constexpr int KS = 512;
+constexpr int APAD = 8;  // LDS row padding (bf16): rows 1040 B apart keep 8-lane groups conflict-free
+
+// The workgroup's shared activation chunk: the hi (and with SPLIT the lo) term of MT*16
+// rows x KS columns.
+template <int MT, bool SPLIT>
+struct AChunk {
+  bf16 v[SPLIT ? 2 : 1][MT * 16][KS + APAD];
+};
+
+// Stage activation columns [k0, k0 + kn) of rows 0..MT*16-1 (rows >= M repeat row 0; their
+// results are never stored) into LDS. kn is 256 or 512.
+template <int MT, bool SPLIT>
+__device__ __forceinline__ void stage_a(AChunk<MT, SPLIT>& sa, const bf16* __restrict__ A,
+                                        const bf16* __restrict__ A_lo, int lda, int M, int k0,
+                                        int kn) {
+  const int per_row = kn / 8;  // 16-byte pieces per row
+  for (int ch = threadIdx.x; ch < MT * 16 * per_row; ch += 256) {
+    const int r = ch / per_row, cc = (ch % per_row) * 8;
+    const size_t src = (size_t)(r < M ? r : 0) * lda + k0 + cc;
+    *reinterpret_cast<u32x4*>(&sa.v[0][r][cc]) = *reinterpret_cast<const u32x4*>(A + src);
+    if (SPLIT) *reinterpret_cast<u32x4*>(&sa.v[SPLIT ? 1 : 0][r][cc]) = *reinterpret_cast<const u32x4*>(A_lo + src);
+  }
+}
+
+__device__ __forceinline__ void load_w(bf16x8 (&w)[16], const bf16* __restrict__ wp, int k, bool full) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) w[u] = ld8(wp + k + u * 32);
+  if (full) {
+#pragma unroll
+    for (int u = 8; u < 16; ++u) w[u] = ld8(wp + k + u * 32);
+  }
+}
+
+template <int MT, bool SPLIT>
+__device__ __forceinline__ void mfma_chunk(const AChunk<MT, SPLIT>& sa, const bf16x8 (&w)[16], bool full,
+                                           int c, int g, f32x4 (&acc)[MT]) {
+  const int nu = full ? 16 : 8;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    if (u < nu) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sa.v[0][mt * 16 + c][u * 32 + g * 8]));
+        acc[mt] = mfma16(a, w[u], acc[mt]);
+        if (SPLIT) {
+          const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sa.v[SPLIT ? 1 : 0][mt * 16 + c][u * 32 + g * 8]));
+          acc[mt] = mfma16(al, w[u], acc[mt]);
+        }
+      }
+    }
+  }
+}
+
+// The workgroup's weight stream over k in [kb, ke) (ke - kb a multiple of 256): each
+// wavefront owns 16 weight rows (lane l reads row wp's n0 + l%16); the rows arrive in KS-deep
+// chunks, double-buffered in registers so the next chunk is in flight while the current one
+// meets its activation chunk in LDS. Every k-step is one MFMA per activation term, in
+// ascending k, starting from zero.
+template <int MT, bool SPLIT>
+__device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* __restrict__ wp,
+                                            const bf16* __restrict__ A, const bf16* __restrict__ A_lo,
+                                            int lda, int M, int kb, int ke, f32x4 (&acc)[MT]) {
+  const int c = (threadIdx.x & 63) & 15, g = (threadIdx.x & 63) >> 4;
+  bf16x8 w0[16], w1[16];
+  bool f0 = ke - kb >= KS;
+  load_w(w0, wp, kb, f0);
+  for (int k = kb; k < ke;) {
+    // chunk at k sits in w0 (full = f0); prefetch the next one into w1
+    const int k1 = k + (f0 ? KS : 256);
+    const bool has1 = k1 < ke;
+    const bool f1 = ke - k1 >= KS;
+    if (has1) load_w(w1, wp, k1, f1);
+    stage_a<MT, SPLIT>(sa, A, A_lo, lda, M, k, f0 ? KS : 256);
+    __syncthreads();
+    mfma_chunk<MT, SPLIT>(sa, w0, f0, c, g, acc);
+    __syncthreads();
+    if (!has1) break;
+    const int k2 = k1 + (f1 ? KS : 256);
+    const bool has2 = k2 < ke;
+    const bool f2 = ke - k2 >= KS;
+    if (has2) load_w(w0, wp, k2, f2);
+    stage_a<MT, SPLIT>(sa, A, A_lo, lda, M, k1, f1 ? KS : 256);
+    __syncthreads();
+    mfma_chunk<MT, SPLIT>(sa, w1, f1, c, g, acc);
+    __syncthreads();
+    k = k2;
+    f0 = f2;
+  }
+}
+
+template <int MT, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A,
+                                                     const bf16* __restrict__ A_lo, int lda, int M,
                                                      const bf16* __restrict__ W, int N, int K,
                                                      int k_len, float* __restrict__ P,
                                                      long long part_stride) {
+  __shared__ __attribute__((aligned(16))) AChunk<MT, SPLIT> sa;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * 4 + wave) * 16;
-  if (n0 >= N) return;
   const int s = blockIdx.y;
   const int kb = s * k_len;
   const int ke = min(K, kb + k_len);
   const int c = lane & 15, g = lane >> 4;
   const int n = n0 + c;
   const bool nv = n < N;
-  // out-of-range columns / rows read a valid row; their results are never stored
-  const bf16* wp = W + (size_t)(nv ? n : n0) * K + g * 8;
-  const bf16* ap[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + c;
-    ap[mt] = A + (size_t)(m < M ? m : 0) * lda + g * 8;
-  }
+  // out-of-range columns read a valid row (every wave stays for the workgroup's barriers);
+  // their results are never stored
+  const bf16* wp = W + (size_t)(nv ? n : min(n0, N - 1)) * K + g * 8;
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k = kb; k < ke; k += 128) {
-    bf16x8 b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) b[u] = ld8(wp + k + u * 32);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      bf16x8 a[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = ld8(ap[mt] + k + u * 32);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[mt] = mfma16(a[u], b[u], acc[mt]);
-    }
-  }
+  stream_tile<MT, SPLIT>(sa, wp, A, A_lo, lda, M, kb, ke, acc);
   if (!nv) return;
   float* pp = P + (long long)s * part_stride;
 #pragma unroll
@@ -65,18 +145,31 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A,
   }
 }
 
-hipError_t launch_gemm_skinny(const bf16* A, int lda, int M, const bf16* W, int N, int K,
-                              int k_len, float* P, long long part_stride, hipStream_t st) {
+hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
+                              int N, int K, int k_len, float* P, long long part_stride,
+                              hipStream_t st) {
   const int S = (K + k_len - 1) / k_len;
   dim3 grid((N + 63) / 64, S);
   const int mt = (M + 15) / 16;
-  switch (mt) {
-    case 1: k_gemm_skinny<1><<<grid, 256, 0, st>>>(A, lda, M, W, N, K, k_len, P, part_stride); break;
-    case 2: k_gemm_skinny<2><<<grid, 256, 0, st>>>(A, lda, M, W, N, K, k_len, P, part_stride); break;
-    case 3: k_gemm_skinny<3><<<grid, 256, 0, st>>>(A, lda, M, W, N, K, k_len, P, part_stride); break;
-    case 4: k_gemm_skinny<4><<<grid, 256, 0, st>>>(A, lda, M, W, N, K, k_len, P, part_stride); break;
-    default: return hipErrorInvalidValue;
+#define DFL_SKINNY(MTV, SP) (void)launch(k_gemm_skinny<MTV, SP>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, k_len, P, part_stride)
+  if (A_lo) {
+    switch (mt) {
+      case 1: DFL_SKINNY(1, true); break;
+      case 2: DFL_SKINNY(2, true); break;
+      case 3: DFL_SKINNY(3, true); break;
+      case 4: DFL_SKINNY(4, true); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (mt) {
+      case 1: DFL_SKINNY(1, false); break;
+      case 2: DFL_SKINNY(2, false); break;
+      case 3: DFL_SKINNY(3, false); break;
+      case 4: DFL_SKINNY(4, false); break;
+      default: return hipErrorInvalidValue;
+    }
   }
+#undef DFL_SKINNY
   return hipGetLastError();
 }
 
@@ -84,10 +177,13 @@ hipError_t launch_gemm_skinny(const bf16* A, int lda, int M, const bf16* W, int 
 
 constexpr int TB = 128, TK = 64, TPAD = 8;
 
-__global__ __launch_bounds__(256) void k_gemm_tiled(const bf16* __restrict__ A, int lda, int M,
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_tiled(const bf16* __restrict__ A,
+                                                    const bf16* __restrict__ A_lo, int lda, int M,
                                                     const bf16* __restrict__ W, int N, int K,
                                                     float* __restrict__ C, int ldc) {
   __shared__ __attribute__((aligned(16))) bf16 sA[TB][TK + TPAD];
+  __shared__ __attribute__((aligned(16))) bf16 sAl[SPLIT ? TB : 1][TK + TPAD];
   __shared__ __attribute__((aligned(16))) bf16 sW[TB][TK + TPAD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -107,22 +203,30 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const bf16* __restrict__ A, 
       const int gm = min(m0 + r, M - 1), gn = min(n0 + r, N - 1);
       *reinterpret_cast<u32x4*>(&sA[r][cc]) =
           *reinterpret_cast<const u32x4*>(A + (size_t)gm * lda + k0 + cc);
+      if (SPLIT)
+        *reinterpret_cast<u32x4*>(&sAl[r][cc]) =
+            *reinterpret_cast<const u32x4*>(A_lo + (size_t)gm * lda + k0 + cc);
       *reinterpret_cast<u32x4*>(&sW[r][cc]) =
           *reinterpret_cast<const u32x4*>(W + (size_t)gn * K + k0 + cc);
     }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < TK; kk += 32) {
-      bf16x8 a[4], b[4];
+      bf16x8 a[4], al[4], b[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sA[wm * 64 + t * 16 + c][kk + g * 8]));
+        if (SPLIT)
+          al[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sAl[wm * 64 + t * 16 + c][kk + g * 8]));
         b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sW[wn * 64 + t * 16 + c][kk + g * 8]));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+          if (SPLIT) acc[i][j] = mfma16(al[i], b[j], acc[i][j]);
+        }
     }
     __syncthreads();
   }
@@ -141,21 +245,23 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const bf16* __restrict__ A, 
   }
 }
 
-hipError_t launch_gemm_tiled(const bf16* A, int lda, int M, const bf16* W, int N, int K,
-                             float* C, int ldc, hipStream_t st) {
+hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
+                             int N, int K, float* C, int ldc, hipStream_t st) {
   if (M <= 0 || N <= 0 || (K % TK) != 0) return hipErrorInvalidValue;
   dim3 grid((N + TB - 1) / TB, (M + TB - 1) / TB);
-  k_gemm_tiled<<<grid, 256, 0, st>>>(A, lda, M, W, N, K, C, ldc);
+  if (A_lo)
+    (void)launch(k_gemm_tiled<true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, C, ldc);
+  else
+    (void)launch(k_gemm_tiled<false>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, C, ldc);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------
-// lm_head + argmax. Each wave walks LM_TILES consecutive 16-column vocabulary tiles over
-// the full K, keeping per row the best (value, lowest index); the workgroup's four waves
-// then merge into one partial per (row, workgroup).
+// lm_head + argmax. Each wave streams one 16-column vocabulary tile over the full K and
+// keeps per row the best (value, lowest index); the workgroup's four waves then merge into
+// one partial per (row, workgroup).
 
-constexpr int LM_TILES = 2;
-constexpr int LM_COLS = 4 * 16 * LM_TILES;  // vocabulary columns per workgroup
+constexpr int LM_COLS = 4 * 16;  // vocabulary columns per workgroup (one 16-column tile per wave)
 
 int lmhead_groups(int V) { return (V + LM_COLS - 1) / LM_COLS; }
 
@@ -164,21 +270,17 @@ __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
 }
 
 template <int MT>
-__global__ __launch_bounds__(256) void k_lmhead_argmax(const bf16* __restrict__ Y, int ldy, int M,
+__global__ __launch_bounds__(256) void k_lmhead_argmax(const bf16* __restrict__ Y,
+                                                       const bf16* __restrict__ Y_lo, int ldy, int M,
                                                        int r0, const bf16* __restrict__ W, int V,
                                                        int K, float* __restrict__ best_v,
                                                        int* __restrict__ best_i, int n_groups,
                                                        int gamma, float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) AChunk<MT, true> sa;
   __shared__ float sv[4][64];
   __shared__ int si[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const bf16* ap[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + c;
-    ap[mt] = Y + (size_t)(m < M ? m : 0) * ldy + g * 8;
-  }
   float bv[MT][4];
   int bi[MT][4];
 #pragma unroll
@@ -186,28 +288,16 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(const bf16* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 4; ++e) { bv[mt][e] = -INFINITY; bi[mt][e] = 0x7fffffff; }
 
-  for (int t = 0; t < LM_TILES; ++t) {
-    const int n0 = (blockIdx.x * 4 * LM_TILES + wave * LM_TILES + t) * 16;
-    if (n0 >= V) break;
+  const int n0 = (blockIdx.x * 4 + wave) * 16;
+  {
     const int n = n0 + c;
     const bool nv = n < V;
-    const bf16* wp = W + (size_t)(nv ? n : n0) * K + g * 8;
+    // every wave takes part in the workgroup's barriers; columns past V read a valid row
+    const bf16* wp = W + (size_t)(nv ? n : min(n0, V - 1)) * K + g * 8;
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; k += 128) {
-      bf16x8 b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) b[u] = ld8(wp + k + u * 32);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        bf16x8 a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = ld8(ap[mt] + k + u * 32);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[mt] = mfma16(a[u], b[u], acc[mt]);
-      }
-    }
+    stream_tile<MT, true>(sa, wp, Y, Y_lo, ldy, M, 0, K, acc);
     if (nv) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -266,15 +356,15 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(const bf16* __restrict__ 
   }
 }
 
-hipError_t launch_lmhead_argmax(const bf16* Y, int ldy, int M, int r0, const bf16* W, int V,
+hipError_t launch_lmhead_argmax(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W, int V,
                                 int K, float* best_v, int* best_i, int n_groups, int gamma,
                                 float* logits, hipStream_t st) {
   dim3 grid(n_groups);
   switch ((M + 15) / 16) {
-    case 1: k_lmhead_argmax<1><<<grid, 256, 0, st>>>(Y, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
-    case 2: k_lmhead_argmax<2><<<grid, 256, 0, st>>>(Y, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
-    case 3: k_lmhead_argmax<3><<<grid, 256, 0, st>>>(Y, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
-    case 4: k_lmhead_argmax<4><<<grid, 256, 0, st>>>(Y, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
+    case 1: (void)launch(k_lmhead_argmax<1>, grid, 256, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
+    case 2: (void)launch(k_lmhead_argmax<2>, grid, 256, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
+    case 3: (void)launch(k_lmhead_argmax<3>, grid, 256, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
+    case 4: (void)launch(k_lmhead_argmax<4>, grid, 256, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -313,7 +403,7 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const float* __restrict__
 
 hipError_t launch_argmax_reduce(const float* best_v, const int* best_i, int n_groups,
                                 int n_bands, int gamma, int* tokens, hipStream_t st) {
-  k_argmax_reduce<<<n_bands * (gamma - 1), 256, 0, st>>>(best_v, best_i, n_groups, gamma, tokens);
+  (void)launch(k_argmax_reduce, n_bands * (gamma - 1), 256, 0, st, best_v, best_i, n_groups, gamma, tokens);
   return hipGetLastError();
 }
 

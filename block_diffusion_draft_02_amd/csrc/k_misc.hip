@@ -12,6 +12,19 @@
 
 namespace dfl {
 
+// sum of S split-K partials P[s][r][j], s = 0..S-1, in a fixed order (eight running sums
+// over s mod 8, then added pairwise), so the result of a row never depends on the launch
+__device__ __forceinline__ float sum_parts(const float* __restrict__ p, int S, long long ps) {
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += p[(long long)(s + u) * ps];
+  }
+  for (int u = 0; s < S; ++s, ++u) a[u] += p[(long long)s * ps];
+  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
 // ---- forward prologue ------------------------------------------------------------------
 // workgroup 0: block-table updates, slots and stamped positions of the block rows, band
 // table; workgroup 1 + r: embedding row of block row r and its input RMSNorm of layer 0.
@@ -22,7 +35,8 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(FwdArgs a, Band* __restric
                                                       const bf16* __restrict__ embed,
                                                       const bf16* __restrict__ w_in0, int h,
                                                       float eps, float* __restrict__ X,
-                                                      bf16* __restrict__ Xn) {
+                                                      bf16* __restrict__ Xn,
+                                                      bf16* __restrict__ Xn_lo) {
   __shared__ float red[4];
   if (blockIdx.x == 0) {
     for (int j = threadIdx.x; j < a.n_upd; j += 256) bt[a.upd_off[j]] = a.upd_page[j];
@@ -53,14 +67,15 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(FwdArgs a, Band* __restric
   ss = block_sum256(ss, red);
   const float rs = rsqrtf(ss / (float)h + eps);
   bf16* xn = Xn + (size_t)r * h;
-  for (int j = threadIdx.x; j < h; j += 256) xn[j] = f2bf(x[j] * rs * bf2f(w_in0[j]));
+  bf16* xl = Xn_lo + (size_t)r * h;
+  for (int j = threadIdx.x; j < h; j += 256) split_bf16(x[j] * rs * bf2f(w_in0[j]), xn[j], xl[j]);
 }
 
 hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
                                int* kpos, const bf16* embed, const bf16* w_in0, int h,
-                               float eps, float* X, bf16* Xn, hipStream_t st) {
+                               float eps, float* X, bf16* Xn, bf16* Xn_lo, hipStream_t st) {
   const int M = a.n_bands * a.gamma;
-  k_fwd_prologue<<<1 + M, 256, 0, st>>>(a, bands_dev, bt, slots, kpos, embed, w_in0, h, eps, X, Xn);
+  (void)launch(k_fwd_prologue, 1 + M, 256, 0, st, a, bands_dev, bt, slots, kpos, embed, w_in0, h, eps, X, Xn, Xn_lo);
   return hipGetLastError();
 }
 
@@ -75,7 +90,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, in
                                                  const bf16* __restrict__ kn, float eps,
                                                  const double* __restrict__ inv_freq,
                                                  float mscale, const long long* __restrict__ slots,
-                                                 KvGeom g, int layer, bf16* __restrict__ Q) {
+                                                 KvGeom g, int layer, bf16* __restrict__ Q,
+                                                 bf16* __restrict__ Q_lo) {
   constexpr int H2 = HD / 2;
   const int r = blockIdx.x, hh = blockIdx.y, l = threadIdx.x;
   const bool act = l < H2;
@@ -83,10 +99,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, in
   float x1 = 0.f, x2 = 0.f;
   if (act) {
     const float* p = P + (size_t)r * N + col;
-    for (int s = 0; s < S; ++s) {
-      x1 += p[(long long)s * ps];
-      x2 += p[(long long)s * ps + H2];
-    }
+    x1 = sum_parts(p, S, ps);
+    x2 = sum_parts(p + H2, S, ps);
   }
   const int kind = hh < nh ? 0 : (hh < nh + nkv ? 1 : 2);
   if (kind != 2) {
@@ -104,9 +118,9 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, in
   }
   if (!act) return;
   if (kind == 0) {
-    bf16* q = Q + ((size_t)r * nh + hh) * HD;
-    q[l] = f2bf(x1);
-    q[l + H2] = f2bf(x2);
+    const size_t o = ((size_t)r * nh + hh) * HD;
+    split_bf16(x1, Q[o + l], Q_lo[o + l]);
+    split_bf16(x2, Q[o + l + H2], Q_lo[o + l + H2]);
     return;
   }
   const long long slot = slots[r];
@@ -127,67 +141,72 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, in
 hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
                            const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
                            const bf16* k_norm, float eps, const double* inv_freq, float mscale,
-                           const long long* slots, KvGeom g, int layer, bf16* Q, hipStream_t st) {
+                           const long long* slots, KvGeom g, int layer, bf16* Q, bf16* Q_lo,
+                           hipStream_t st) {
   const int N = (nh + 2 * nkv) * hd;
   dim3 grid(M, nh + 2 * nkv);
   switch (hd) {
-    case 32: k_qkv_post<32><<<grid, 64, 0, st>>>(P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q); break;
-    case 64: k_qkv_post<64><<<grid, 64, 0, st>>>(P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q); break;
-    case 128: k_qkv_post<128><<<grid, 64, 0, st>>>(P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q); break;
+    case 32: (void)launch(k_qkv_post<32>, grid, 64, 0, st, P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
+    case 64: (void)launch(k_qkv_post<64>, grid, 64, 0, st, P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
+    case 128: (void)launch(k_qkv_post<128>, grid, 64, 0, st, P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 // ---- residual add + RMSNorm ---------------------------------------------------------------
-// X[r] += sum_s P[s][r]; Xn[r] = bf16(RMSNorm_w(X[r]))
-__global__ __launch_bounds__(256) void k_resid_norm(float* __restrict__ X, const float* __restrict__ P,
-                                                    int S, long long ps, int h,
-                                                    const bf16* __restrict__ w, float eps,
-                                                    bf16* __restrict__ Xn) {
-  __shared__ float red[4];
+// X[r] += sum_s P[s][r]; Xn[r] = RMSNorm_w(X[r]) as hi + lo bf16; 1024 threads per row
+__global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ X, const float* __restrict__ P,
+                                                     int S, long long ps, int h,
+                                                     const bf16* __restrict__ w, float eps,
+                                                     bf16* __restrict__ Xn, bf16* __restrict__ Xn_lo) {
+  __shared__ float red[16];
   const int r = blockIdx.x;
   float* x = X + (size_t)r * h;
   const float* p = P + (size_t)r * h;
   float ss = 0.f;
-  for (int j = threadIdx.x; j < h; j += 256) {
-    float v = x[j];
-    for (int s = 0; s < S; ++s) v += p[(long long)s * ps + j];
+  for (int j = threadIdx.x; j < h; j += 1024) {
+    const float v = x[j] + sum_parts(p + j, S, ps);
     x[j] = v;
     ss += v * v;
   }
-  ss = block_sum256(ss, red);
-  const float rs = rsqrtf(ss / (float)h + eps);
+  ss = wave_sum(ss);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tot += red[i];
+  const float rs = rsqrtf(tot / (float)h + eps);
   bf16* xn = Xn + (size_t)r * h;
-  for (int j = threadIdx.x; j < h; j += 256) xn[j] = f2bf(x[j] * rs * bf2f(w[j]));
+  bf16* xl = Xn_lo + (size_t)r * h;
+  for (int j = threadIdx.x; j < h; j += 1024) split_bf16(x[j] * rs * bf2f(w[j]), xn[j], xl[j]);
 }
 
 hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
-                             int h, const bf16* w, float eps, bf16* Xn, hipStream_t st) {
-  k_resid_norm<<<M, 256, 0, st>>>(X, P, S, part_stride, h, w, eps, Xn);
+                             int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
+                             hipStream_t st) {
+  (void)launch(k_resid_norm, M, 1024, 0, st, X, P, S, part_stride, h, w, eps, Xn, Xn_lo);
   return hipGetLastError();
 }
 
 // ---- SwiGLU -----------------------------------------------------------------------------
 // the fused gate/up projection's columns are [gate (ff) | up (ff)]
 __global__ __launch_bounds__(256) void k_silu_mul(const float* __restrict__ P, int S, long long ps,
-                                                  int M, int ff, bf16* __restrict__ A) {
+                                                  int M, int ff, bf16* __restrict__ A,
+                                                  bf16* __restrict__ A_lo) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)M * ff) return;
   const size_t r = idx / ff, j = idx % ff;
   const float* p = P + r * 2 * ff + j;
-  float gs = 0.f, us = 0.f;
-  for (int s = 0; s < S; ++s) {
-    gs += p[(long long)s * ps];
-    us += p[(long long)s * ps + ff];
-  }
-  A[idx] = f2bf(silu(gs) * us);
+  const float gs = sum_parts(p, S, ps), us = sum_parts(p + ff, S, ps);
+  split_bf16(silu(gs) * us, A[idx], A_lo[idx]);
 }
 
 hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
-                           bf16* A, hipStream_t st) {
+                           bf16* A, bf16* A_lo, hipStream_t st) {
   const size_t n = (size_t)M * ff;
-  k_silu_mul<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(P, S, part_stride, M, ff, A);
+  (void)launch(k_silu_mul, (unsigned)((n + 255) / 256), 256, 0, st, P, S, part_stride, M, ff, A, A_lo);
   return hipGetLastError();
 }
 
@@ -210,33 +229,47 @@ __global__ __launch_bounds__(256) void k_append_setup(AppendArgs a, int* __restr
 
 hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
                                int* kpos, hipStream_t st) {
-  k_append_setup<<<1, 256, 0, st>>>(a, bt, slots, rowpos, kpos);
+  (void)launch(k_append_setup, 1, 256, 0, st, a, bt, slots, rowpos, kpos);
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_rows_rmsnorm(const float* __restrict__ X, int h,
-                                                      const bf16* __restrict__ w, float eps,
-                                                      bf16* __restrict__ out) {
-  __shared__ float red[4];
+// one workgroup per row; the row (the sum of S split-K partials) is staged in LDS
+__global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__ X, int S, long long ps,
+                                                       int h, const bf16* __restrict__ w, float eps,
+                                                       bf16* __restrict__ out,
+                                                       bf16* __restrict__ out_lo) {
+  extern __shared__ float xs[];
+  __shared__ float red[16];
   const int r = blockIdx.x;
   const float* x = X + (size_t)r * h;
   float ss = 0.f;
-  for (int j = threadIdx.x; j < h; j += 256) ss += x[j] * x[j];
-  ss = block_sum256(ss, red);
-  const float rs = rsqrtf(ss / (float)h + eps);
+  for (int j = threadIdx.x; j < h; j += 1024) {
+    const float v = sum_parts(x + j, S, ps);
+    xs[j] = v;
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tot += red[i];
+  const float rs = rsqrtf(tot / (float)h + eps);
   bf16* o = out + (size_t)r * h;
-  for (int j = threadIdx.x; j < h; j += 256) o[j] = f2bf(x[j] * rs * bf2f(w[j]));
+  bf16* ol = out_lo + (size_t)r * h;
+  for (int j = threadIdx.x; j < h; j += 1024) split_bf16(xs[j] * rs * bf2f(w[j]), o[j], ol[j]);
 }
 
-hipError_t launch_rows_rmsnorm(const float* X, int M, int h, const bf16* w, float eps, bf16* out,
-                               hipStream_t st) {
-  k_rows_rmsnorm<<<M, 256, 0, st>>>(X, h, w, eps, out);
+hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int M, int h,
+                               const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st) {
+  (void)launch(k_rows_rmsnorm, M, 1024, (size_t)h * sizeof(float), st, X, S, part_stride, h, w, eps, out, out_lo);
   return hipGetLastError();
 }
 
 // one wavefront per (row, layer, K|V, kv head) of the fused [K0 | V0 | K1 | V1 | ...] output
 template <int HD>
-__global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__ KV, int L,
+__global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__ KV, int S,
+                                                       long long ps, int L,
                                                        const bf16* __restrict__ kn_all, float eps,
                                                        const double* __restrict__ inv_freq,
                                                        float mscale,
@@ -250,7 +283,7 @@ __global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__
   const bool act = l < H2;
   const size_t ld = (size_t)L * 2 * nkv * HD;
   const float* src = KV + (size_t)r * ld + (size_t)idx * HD;
-  float x1 = act ? src[l] : 0.f, x2 = act ? src[l + H2] : 0.f;
+  float x1 = act ? sum_parts(src + l, S, ps) : 0.f, x2 = act ? sum_parts(src + l + H2, S, ps) : 0.f;
   if (kv == 0) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float rs = rsqrtf(ss / (float)HD + eps);
@@ -279,15 +312,16 @@ __global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__
   }
 }
 
-hipError_t launch_kv_append_post(const float* KV, int n, int L, const bf16* k_norm_all,
+hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int n, int L,
+                                 const bf16* k_norm_all,
                                  float eps, const double* inv_freq, float mscale,
                                  const long long* slots, const int* rowpos, KvGeom g,
                                  hipStream_t st) {
   dim3 grid(n, L * 2 * g.nkv);
   switch (g.hd) {
-    case 32: k_kv_append_post<32><<<grid, 64, 0, st>>>(KV, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
-    case 64: k_kv_append_post<64><<<grid, 64, 0, st>>>(KV, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
-    case 128: k_kv_append_post<128><<<grid, 64, 0, st>>>(KV, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 32: (void)launch(k_kv_append_post<32>, grid, 64, 0, st, KV, S, part_stride, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 64: (void)launch(k_kv_append_post<64>, grid, 64, 0, st, KV, S, part_stride, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 128: (void)launch(k_kv_append_post<128>, grid, 64, 0, st, KV, S, part_stride, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

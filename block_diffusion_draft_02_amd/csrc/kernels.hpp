@@ -1,16 +1,31 @@
 // Launch interface between the host runtime and the gfx950 kernels. Every launcher
 // enqueues on `st` and returns hipGetLastError().
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dfl {
 
+// Start/stop events the next launches attach to their own dispatch packets (so they time the
+// kernel alone, as a profiler's kernel trace does); both null when timing is off.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+template <typename... KA, typename... A>
+inline hipError_t launch(void (*k)(KA...), dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                         A... args) {
+  const LaunchEvents& e = launch_events();
+  hipExtLaunchKernelGGL(k, grid, block, (uint32_t)shmem, st, e.start, e.stop, 0u, args...);
+  return hipGetLastError();
+}
+
 typedef uint16_t bf16;
 
 constexpr int PAGE = 16;          // tokens per KV page
 constexpr int MAX_BANDS = 32;     // sequences in one forward call
-constexpr int MAX_CHUNKS = 32;    // split-KV chunks per (band, kv head) in attention
 constexpr int APPEND_ROWS = 2048; // context rows per append launch sequence
 constexpr int APPEND_PAGES = APPEND_ROWS / PAGE + 1;
 
@@ -56,18 +71,20 @@ struct KvGeom {
 __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (size_t)2 * nkv * PAGE * hd; }
 
 // ---- GEMMs (k_gemm.hip) --------------------------------------------------------------
-// Y[M,N] = A[M,K] W[N,K]^T. Skinny form: partials P[s][M][N] over K splits of k_len
-// (k_len, K multiples of 128); M <= 64 per launch.
-hipError_t launch_gemm_skinny(const bf16* A, int lda, int M, const bf16* W, int N, int K,
-                              int k_len, float* P, long long part_stride, hipStream_t st);
-// Tiled form for large M: C[M,N] fp32 (ldc), K multiple of 64.
-hipError_t launch_gemm_tiled(const bf16* A, int lda, int M, const bf16* W, int N, int K,
-                             float* C, int ldc, hipStream_t st);
+// Y[M,N] = A[M,K] W[N,K]^T where the activation A = A_hi + A_lo is carried as two bf16
+// terms (each k-step issues two MFMAs). Skinny form: partials P[s][M][N] over K splits of
+// k_len (k_len, K multiples of 128); M <= 64 per launch.
+hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
+                              int N, int K, int k_len, float* P, long long part_stride,
+                              hipStream_t st);
+// Tiled form for large M: C[M,N] fp32 (ldc), K multiple of 64; A_lo may be null (A exact).
+hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
+                             int N, int K, float* C, int ldc, hipStream_t st);
 // lm_head + argmax partials: for rows r0..r0+M-1 of the forward (M <= 64), best (value,
 // index) per row over each workgroup's vocabulary range; optionally the fp32 logits of
 // drafted rows (row % gamma != 0) into logits[(r/gamma)*(gamma-1) + r%gamma - 1][V].
 int lmhead_groups(int V);
-hipError_t launch_lmhead_argmax(const bf16* Y, int ldy, int M, int r0, const bf16* W, int V,
+hipError_t launch_lmhead_argmax(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W, int V,
                                 int K, float* best_v, int* best_i, int n_groups, int gamma,
                                 float* logits, hipStream_t st);
 hipError_t launch_argmax_reduce(const float* best_v, const int* best_i, int n_groups,
@@ -76,31 +93,35 @@ hipError_t launch_argmax_reduce(const float* best_v, const int* best_i, int n_gr
 // ---- forward elementwise (k_misc.hip) ------------------------------------------------
 hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
                                int* kpos, const bf16* embed, const bf16* w_in0, int h,
-                               float eps, float* X, bf16* Xn, hipStream_t st);
+                               float eps, float* X, bf16* Xn, bf16* Xn_lo, hipStream_t st);
 hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
                            const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
                            const bf16* k_norm, float eps, const double* inv_freq, float mscale,
-                           const long long* slots, KvGeom g, int layer, bf16* Q, hipStream_t st);
+                           const long long* slots, KvGeom g, int layer, bf16* Q, bf16* Q_lo,
+                           hipStream_t st);
 hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
-                             int h, const bf16* w, float eps, bf16* Xn, hipStream_t st);
+                             int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
+                             hipStream_t st);
 hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
-                           bf16* A, hipStream_t st);
+                           bf16* A, bf16* A_lo, hipStream_t st);
 
 // ---- attention (k_attn.hip) ----------------------------------------------------------
 // total_chunks = sum over bands of nch[sw]; partial buffers sized [total_chunks*nkv][128][hd]
-hipError_t launch_block_attn(const bf16* Q, const Band* bands_dev, int n_bands, int total_chunks,
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_dev, int n_bands, int total_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st);
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,
                                int n_bands, int gamma, int nh, int nkv, int hd, int sw,
-                               bf16* out, hipStream_t st);
+                               bf16* out, bf16* out_lo, hipStream_t st);
 
 // ---- context append (k_misc.hip) -----------------------------------------------------
 hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
                                int* kpos, hipStream_t st);
-hipError_t launch_rows_rmsnorm(const float* X, int M, int h, const bf16* w, float eps, bf16* out,
-                               hipStream_t st);
-hipError_t launch_kv_append_post(const float* KV, int n, int L, const bf16* k_norm_all,
+// inputs are split-K partials X[s][M][...] (S = 1, part_stride unused for a plain result)
+hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int M, int h,
+                               const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st);
+hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int n, int L,
+                                 const bf16* k_norm_all,
                                  float eps, const double* inv_freq, float mscale,
                                  const long long* slots, const int* rowpos, KvGeom g,
                                  hipStream_t st);

@@ -22,6 +22,7 @@ namespace {
 
 constexpr int RING = 8;          // staging slots for caller-stamped append positions
 constexpr int ROW_GROUP = 64;    // rows per skinny-GEMM launch
+constexpr int APPEND_SKINNY = 64; // appends of up to this many rows stream their weights once
 
 struct LayerDev {
   const bf16 *o_proj, *down_proj, *q_norm, *k_norm, *in_norm, *post_norm;
@@ -62,11 +63,11 @@ struct dflash_ctx {
   int* rowpos = nullptr;
   Band* bands_dev = nullptr;
   // forward scratch
-  float* X = nullptr;
-  bf16* Xn = nullptr;
-  bf16* Qb = nullptr;
-  bf16* attn = nullptr;
-  bf16* act = nullptr;
+  float* X = nullptr;                      // residual stream, fp32
+  bf16 *Xn = nullptr, *Xn_lo = nullptr;    // activations as hi + lo bf16 terms
+  bf16 *Qb = nullptr, *Qb_lo = nullptr;
+  bf16 *attn = nullptr, *attn_lo = nullptr;
+  bf16 *act = nullptr, *act_lo = nullptr;
   float* part = nullptr;
   size_t part_elems = 0;
   float* aparts_o = nullptr;
@@ -74,15 +75,21 @@ struct dflash_ctx {
   float* best_v = nullptr;
   int* best_i = nullptr;
   int lm_groups = 0;
-  GemmPlan g_qkv, g_o, g_gu, g_down;
+  GemmPlan g_qkv, g_o, g_gu, g_down, g_fc, g_kvapp;
   // append scratch
   float* F32 = nullptr;
-  bf16* Fb = nullptr;
+  bf16 *Fb = nullptr, *Fb_lo = nullptr;
   float* KV32 = nullptr;
   int* ring_host = nullptr;
   int* ring_dev = nullptr;
   hipEvent_t ring_ev[RING] = {};
   int ring_next = 0;
+  // launch timing (opt-in per class)
+  uint32_t tmask = 0;
+  std::vector<hipEvent_t> tev;   // pairs (start, end)
+  std::vector<int> tcls;         // class of each recorded pair
+  double tms[DFLASH_K_NUM_CLASSES] = {};
+  long long tcnt[DFLASH_K_NUM_CLASSES] = {};
   // host state
   std::vector<SeqState> seqs;
   std::deque<int> free_pages;
@@ -128,22 +135,75 @@ int dalloc(dflash_ctx* c, T** p, size_t elems) {
 }
 
 GemmPlan plan_gemm(int N, int K) {
-  // ~2048 wavefronts per weight-streaming launch; every split at least 256 deep
-  const int ntiles = (N + 15) / 16;
-  int S = std::max(1, 2048 / ntiles);
-  S = std::max(1, std::min(S, K / 256));
-  const int klen = ((K / S) + 127) / 128 * 128;
+  // K splits of 512 (the depth a workgroup stages and a wavefront keeps in flight); the last
+  // split may be 256 deep. Depends on (N, K) only, never on the number of rows.
+  const int klen = K >= 512 ? 512 : K;
   return GemmPlan{N, K, klen, (K + klen - 1) / klen};
 }
 
 void plan_chunks(int kstart, int kend, int& ck, int& nch) {
+  // 16 pages (256 keys, the most a workgroup stages in LDS) per chunk: the per-chunk partial
+  // output (every query row of a kv head) then stays at half the K/V bytes the chunk reads
   const int pages = (kend - kstart + PAGE - 1) / PAGE;
-  const int ckp = std::max(2, (pages + MAX_CHUNKS - 1) / MAX_CHUNKS);
+  const int ckp = 16;
   nch = (pages + ckp - 1) / ckp;
   ck = ckp * PAGE;
 }
 
 bool sliding_layer(const dflash_ctx* c, int l) { return c->window > 0 && c->sliding[l]; }
+
+constexpr size_t TIMING_PAIRS = 4096;
+
+}  // namespace
+
+namespace dfl {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace dfl
+
+namespace {
+
+hipError_t timing_harvest(dflash_ctx* c) {
+  const size_t n = c->tcls.size();
+  if (n == 0) return hipSuccess;
+  hipError_t e = hipEventSynchronize(c->tev[2 * n - 1]);
+  if (e != hipSuccess) return e;
+  for (size_t i = 0; i < n; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, c->tev[2 * i], c->tev[2 * i + 1]);
+    if (e != hipSuccess) return e;
+    c->tms[c->tcls[i]] += ms;
+    c->tcnt[c->tcls[i]] += 1;
+  }
+  c->tcls.clear();
+  return hipSuccess;
+}
+
+// run `launch` (one kernel launch on st); time it if its class is timed
+template <class F>
+hipError_t timed(dflash_ctx* c, int cls, hipStream_t st, F&& launch) {
+  if (!((c->tmask >> cls) & 1u)) return launch();
+  if (c->tcls.size() == TIMING_PAIRS) {
+    hipError_t e = timing_harvest(c);
+    if (e != hipSuccess) return e;
+  }
+  const size_t i = c->tcls.size();
+  while (c->tev.size() < 2 * (i + 1)) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+    c->tev.push_back(ev);
+  }
+  // the events ride on the kernel's own dispatch: they time the kernel alone
+  launch_events() = LaunchEvents{c->tev[2 * i], c->tev[2 * i + 1]};
+  hipError_t e = launch();
+  launch_events() = LaunchEvents{};
+  if (e != hipSuccess) return e;
+  c->tcls.push_back(cls);
+  return hipSuccess;
+}
 
 KvGeom geom(dflash_ctx* c) {
   return KvGeom{c->pool, c->kpos, c->bt_dev, c->num_pages, c->nkv, c->hd, c->per_seq};
@@ -161,9 +221,9 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
     return bad("num_q_heads must be a multiple of num_kv_heads");
   if (cfg->num_q_heads / cfg->num_kv_heads > 8) return bad("at most 8 query heads per kv head");
   if (cfg->gamma_max < 2 || cfg->gamma_max > 16) return bad("gamma_max must be in [2, 16]");
-  if (cfg->hidden % 128 || cfg->intermediate % 128 || (cfg->num_q_heads * cfg->head_dim) % 128 ||
-      (cfg->num_taps * cfg->target_hidden) % 128)
-    return bad("hidden, intermediate, q_dim and num_taps*target_hidden must be multiples of 128");
+  if (cfg->hidden % 256 || cfg->intermediate % 256 || (cfg->num_q_heads * cfg->head_dim) % 256 ||
+      (cfg->num_taps * cfg->target_hidden) % 256)
+    return bad("hidden, intermediate, q_dim and num_taps*target_hidden must be multiples of 256");
   if (cfg->mask_token_id < 0 || cfg->mask_token_id >= cfg->vocab) return bad("mask_token_id out of range");
   if (cfg->max_batch < 1 || cfg->max_batch > MAX_BANDS) return bad("max_batch must be in [1, 32]");
   if (cfg->max_seq_len < 1 || cfg->max_seq_len > (1 << 28)) return bad("max_seq_len out of range");
@@ -217,6 +277,7 @@ void release(dflash_ctx* c) {
   for (int i = 0; i < RING; ++i)
     if (c->ring_ev[i]) (void)hipEventDestroy(c->ring_ev[i]);
   if (c->ring_host) (void)hipHostFree(c->ring_host);
+  for (hipEvent_t e : c->tev) (void)hipEventDestroy(e);
   for (void* p : c->owned) (void)hipFree(p);
   delete c;
 }
@@ -286,12 +347,17 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->g_o = plan_gemm(c->h, c->qd);
   c->g_gu = plan_gemm(2 * c->ff, c->h);
   c->g_down = plan_gemm(c->h, c->ff);
+  c->g_fc = plan_gemm(c->h, c->T * c->Ht);
+  c->g_kvapp = plan_gemm(c->L * 2 * c->kvd, c->h);
   size_t part = 0;
   for (const GemmPlan* g : {&c->g_qkv, &c->g_o, &c->g_gu, &c->g_down})
     part = std::max(part, (size_t)g->S * c->m_max * g->N);
+  for (const GemmPlan* g : {&c->g_fc, &c->g_kvapp})
+    part = std::max(part, (size_t)g->S * APPEND_SKINNY * g->N);
   c->part_elems = part;
   c->lm_groups = lmhead_groups(c->V);
-  const size_t items = (size_t)c->max_batch * MAX_CHUNKS * c->nkv;
+  // split-KV partial slots: every band can have ceil(pages per sequence / 16) chunks
+  const size_t items = (size_t)c->max_batch * ((c->per_seq + 15) / 16) * c->nkv;
   if ((rc = dalloc(c, &c->pool, (size_t)c->L * c->num_pages * pl)) ||
       (rc = dalloc(c, &c->kpos, (size_t)c->num_pages * PAGE)) ||
       (rc = dalloc(c, &c->bt_dev, (size_t)c->max_batch * c->per_seq)) ||
@@ -300,9 +366,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->bands_dev, (size_t)MAX_BANDS)) ||
       (rc = dalloc(c, &c->X, (size_t)c->m_max * hsz)) ||
       (rc = dalloc(c, &c->Xn, (size_t)c->m_max * hsz)) ||
+      (rc = dalloc(c, &c->Xn_lo, (size_t)c->m_max * hsz)) ||
       (rc = dalloc(c, &c->Qb, (size_t)c->m_max * c->qd)) ||
+      (rc = dalloc(c, &c->Qb_lo, (size_t)c->m_max * c->qd)) ||
       (rc = dalloc(c, &c->attn, (size_t)c->m_max * c->qd)) ||
+      (rc = dalloc(c, &c->attn_lo, (size_t)c->m_max * c->qd)) ||
       (rc = dalloc(c, &c->act, (size_t)c->m_max * c->ff)) ||
+      (rc = dalloc(c, &c->act_lo, (size_t)c->m_max * c->ff)) ||
       (rc = dalloc(c, &c->part, part)) ||
       (rc = dalloc(c, &c->aparts_o, items * 128 * c->hd)) ||
       (rc = dalloc(c, &c->aparts_ml, items * 128 * 2)) ||
@@ -310,6 +380,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->best_i, (size_t)c->m_max * c->lm_groups)) ||
       (rc = dalloc(c, &c->F32, (size_t)APPEND_ROWS * hsz)) ||
       (rc = dalloc(c, &c->Fb, (size_t)APPEND_ROWS * hsz)) ||
+      (rc = dalloc(c, &c->Fb_lo, (size_t)APPEND_ROWS * hsz)) ||
       (rc = dalloc(c, &c->KV32, (size_t)APPEND_ROWS * c->L * 2 * c->kvd)) ||
       (rc = dalloc(c, &c->ring_dev, (size_t)RING * APPEND_ROWS)) ||
       (rc = dalloc(c, &c->w_kv, (size_t)c->L * 2 * c->kvd * hsz)) ||
@@ -416,6 +487,7 @@ int dflash_debug_copy(dflash_ctx* c, int32_t buffer, void* dst, size_t offset, s
     case DFLASH_BUF_SLOTS: base = (const char*)c->slots; size = (size_t)std::max(c->m_max, APPEND_ROWS) * 8; break;
     case DFLASH_BUF_BLOCKTAB: base = (const char*)c->bt_dev; size = (size_t)c->max_batch * c->per_seq * 4; break;
     case DFLASH_BUF_HIDDEN: base = (const char*)c->Xn; size = (size_t)c->m_max * c->h * 2; break;
+    case DFLASH_BUF_HIDDEN_LO: base = (const char*)c->Xn_lo; size = (size_t)c->m_max * c->h * 2; break;
     default: return fail(c, DFLASH_EINVAL, "unknown buffer %d", buffer);
   }
   if (offset > size || bytes > size - offset) return fail(c, DFLASH_ERANGE, "copy past the end of buffer %d", buffer);
@@ -481,13 +553,43 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
       HIPCHK(c, hipMemcpyAsync(dp, hp, (size_t)nc * sizeof(int), hipMemcpyHostToDevice, st));
       a.positions = dp;
     }
-    HIPCHK(c, launch_append_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st));
+    HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] { return launch_append_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st); }));
     if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
-    HIPCHK(c, launch_gemm_tiled((const bf16*)target_hidden + (size_t)r0 * ld, ld, nc, c->fc, c->h, ld, c->F32, c->h, st));
-    HIPCHK(c, launch_rows_rmsnorm(c->F32, nc, c->h, c->hidden_norm, c->eps, c->Fb, st));
-    HIPCHK(c, launch_gemm_tiled(c->Fb, c->h, nc, c->w_kv, c->L * 2 * c->kvd, c->h, c->KV32, c->L * 2 * c->kvd, st));
-    HIPCHK(c, launch_kv_append_post(c->KV32, nc, c->L, c->knorm_all, c->eps, c->inv_freq, (float)c->mscale,
-                                    c->slots, c->rowpos, g, st));
+    const bf16* Hc = (const bf16*)target_hidden + (size_t)r0 * ld;
+    const int nkv2 = c->L * 2 * c->kvd;
+    if (nc <= APPEND_SKINNY) {
+      // few rows: weight-streaming GEMMs with split-K partials, reduced by the consumers
+      const long long ps_fc = (long long)nc * c->h, ps_kv = (long long)nc * nkv2;
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+        return launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->g_fc.klen, c->part, ps_fc, st);
+      }));
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+        return launch_rows_rmsnorm(c->part, c->g_fc.S, ps_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
+                                   c->Fb_lo, st);
+      }));
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+        return launch_gemm_skinny(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->g_kvapp.klen, c->part,
+                                  ps_kv, st);
+      }));
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+        return launch_kv_append_post(c->part, c->g_kvapp.S, ps_kv, nc, c->L, c->knorm_all, c->eps, c->inv_freq,
+                                     (float)c->mscale, c->slots, c->rowpos, g, st);
+      }));
+    } else {
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+        return launch_gemm_tiled(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->F32, c->h, st);
+      }));
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+        return launch_rows_rmsnorm(c->F32, 1, 0, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st);
+      }));
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+        return launch_gemm_tiled(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->KV32, nkv2, st);
+      }));
+      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+        return launch_kv_append_post(c->KV32, 1, 0, nc, c->L, c->knorm_all, c->eps, c->inv_freq, (float)c->mscale,
+                                     c->slots, c->rowpos, g, st);
+      }));
+    }
   }
   for (int i = 0; i < n; ++i) s.pos.push_back(positions ? positions[i] : C + i);
   s.kv_len = C + n;
@@ -556,14 +658,18 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   const KvGeom g = geom(c);
   const int M = n_seqs * gamma;
   const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
-  HIPCHK(c, launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed,
-                                c->layers[0].in_norm, c->h, c->eps, c->X, c->Xn, st));
-  auto gemm = [&](const bf16* A, int lda, const bf16* W, const GemmPlan& p) -> hipError_t {
+  HIPCHK(c, timed(c, DFLASH_K_PROLOGUE, st, [&] {
+    return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed,
+                               c->layers[0].in_norm, c->h, c->eps, c->X, c->Xn, c->Xn_lo, st);
+  }));
+  auto gemm = [&](const bf16* A, const bf16* A_lo, int lda, const bf16* W, const GemmPlan& p) -> hipError_t {
     const long long ps = (long long)M * p.N;
     for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
       const int mg = std::min(ROW_GROUP, M - r0);
-      hipError_t e = launch_gemm_skinny(A + (size_t)r0 * lda, lda, mg, W, p.N, p.K, p.klen,
-                                        c->part + (size_t)r0 * p.N, ps, st);
+      hipError_t e = timed(c, DFLASH_K_GEMM, st, [&] {
+        return launch_gemm_skinny(A + (size_t)r0 * lda, A_lo + (size_t)r0 * lda, lda, mg, W, p.N, p.K,
+                                  p.klen, c->part + (size_t)r0 * p.N, ps, st);
+      });
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -571,30 +677,66 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   for (int l = 0; l < c->L; ++l) {
     const LayerDev& d = c->layers[l];
     const int sw = sliding_layer(c, l) ? 1 : 0;
-    HIPCHK(c, gemm(c->Xn, c->h, d.w_qkv, c->g_qkv));
-    HIPCHK(c, launch_qkv_post(c->part, c->g_qkv.S, (long long)M * c->g_qkv.N, M, gamma, c->bands_dev,
-                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
-                              (float)c->mscale, c->slots, g, l, c->Qb, st));
-    HIPCHK(c, launch_block_attn(c->Qb, c->bands_dev, n_seqs, base[sw], gamma, c->nh, g, l, sw,
-                                sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st));
-    HIPCHK(c, launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
-                                  c->nkv, c->hd, sw, c->attn, st));
-    HIPCHK(c, gemm(c->attn, c->qd, d.o_proj, c->g_o));
-    HIPCHK(c, launch_resid_norm(c->X, c->part, c->g_o.S, (long long)M * c->g_o.N, M, c->h, d.post_norm,
-                                c->eps, c->Xn, st));
-    HIPCHK(c, gemm(c->Xn, c->h, d.w_gu, c->g_gu));
-    HIPCHK(c, launch_silu_mul(c->part, c->g_gu.S, (long long)M * c->g_gu.N, M, c->ff, c->act, st));
-    HIPCHK(c, gemm(c->act, c->ff, d.down_proj, c->g_down));
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_qkv, c->g_qkv));
+    HIPCHK(c, timed(c, DFLASH_K_QKV_POST, st, [&] {
+      return launch_qkv_post(c->part, c->g_qkv.S, (long long)M * c->g_qkv.N, M, gamma, c->bands_dev,
+                             c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
+                             (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
+      return launch_block_attn(c->Qb, c->Qb_lo, c->bands_dev, n_seqs, base[sw], gamma, c->nh, g, l, sw,
+                               sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_ATTN_COMBINE, st, [&] {
+      return launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
+                                 c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
+    }));
+    HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, d.o_proj, c->g_o));
+    HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+      return launch_resid_norm(c->X, c->part, c->g_o.S, (long long)M * c->g_o.N, M, c->h, d.post_norm,
+                               c->eps, c->Xn, c->Xn_lo, st);
+    }));
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_gu, c->g_gu));
+    HIPCHK(c, timed(c, DFLASH_K_SILU, st, [&] {
+      return launch_silu_mul(c->part, c->g_gu.S, (long long)M * c->g_gu.N, M, c->ff, c->act, c->act_lo, st);
+    }));
+    HIPCHK(c, gemm(c->act, c->act_lo, c->ff, d.down_proj, c->g_down));
     const bf16* wn = l + 1 < c->L ? c->layers[l + 1].in_norm : c->norm;
-    HIPCHK(c, launch_resid_norm(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h, wn,
-                                c->eps, c->Xn, st));
+    HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+      return launch_resid_norm(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h, wn,
+                               c->eps, c->Xn, c->Xn_lo, st);
+    }));
   }
   for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
     const int mg = std::min(ROW_GROUP, M - r0);
-    HIPCHK(c, launch_lmhead_argmax(c->Xn + (size_t)r0 * c->h, c->h, mg, r0, c->lm_head, c->V, c->h,
-                                   c->best_v, c->best_i, c->lm_groups, gamma, logits, st));
+    HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
+      return launch_lmhead_argmax(c->Xn + (size_t)r0 * c->h, c->Xn_lo + (size_t)r0 * c->h, c->h, mg, r0,
+                                  c->lm_head, c->V, c->h,
+                                  c->best_v, c->best_i, c->lm_groups, gamma, logits, st);
+    }));
   }
-  HIPCHK(c, launch_argmax_reduce(c->best_v, c->best_i, c->lm_groups, n_seqs, gamma, draft_tokens, st));
+  HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] {
+    return launch_argmax_reduce(c->best_v, c->best_i, c->lm_groups, n_seqs, gamma, draft_tokens, st);
+  }));
+  return DFLASH_OK;
+}
+
+int dflash_timing(dflash_ctx* c, uint32_t class_mask) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  c->tmask = class_mask & ((1u << DFLASH_K_NUM_CLASSES) - 1u);
+  return DFLASH_OK;
+}
+
+int dflash_timing_read(dflash_ctx* c, double* ms, int64_t* launches, int32_t n_classes) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  HIPCHK(c, timing_harvest(c));
+  for (int i = 0; i < n_classes && i < DFLASH_K_NUM_CLASSES; ++i) {
+    if (ms) ms[i] = c->tms[i];
+    if (launches) launches[i] = c->tcnt[i];
+  }
+  for (int i = 0; i < DFLASH_K_NUM_CLASSES; ++i) { c->tms[i] = 0.0; c->tcnt[i] = 0; }
   return DFLASH_OK;
 }
 

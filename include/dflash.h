@@ -57,7 +57,8 @@ enum {
 /* Model and pool configuration (all host memory, copied by dflash_create).
  * Supported shapes: head_dim in {32, 64, 128}; num_q_heads % num_kv_heads == 0 with a
  * group of at most 8 query heads; gamma_max in [2, 16]; hidden, intermediate,
- * num_q_heads*head_dim and num_taps*target_hidden multiples of 64; max_batch <= 64. */
+ * num_q_heads*head_dim and num_taps*target_hidden multiples of 256; max_batch in [1, 32];
+ * max_seq_len in [1, 2^28]. Positions (stamped and RoPE) lie in [0, 2^30). */
 typedef struct {
   int32_t num_layers, hidden, num_q_heads, num_kv_heads, head_dim, intermediate, vocab;
   int32_t num_taps, target_hidden; /* fc in_features = num_taps * target_hidden */
@@ -158,11 +159,36 @@ int dflash_pool_geometry(const dflash_ctx *ctx, int64_t *num_pages, int64_t *pag
  *   DFLASH_BUF_SLOTS     int64 slots written by the last append / forward call;
  *   DFLASH_BUF_BLOCKTAB  int32 [max_batch][pages_per_seq]: the device block tables;
  *   DFLASH_BUF_HIDDEN    bf16 [rows][hidden]: the final-normed hidden rows of the last
- *                        forward (debug seam). */
+ *                        forward (debug seam), high bf16 term;
+ *   DFLASH_BUF_HIDDEN_LO the same rows' low bf16 term (hidden = high + low). */
 enum { DFLASH_BUF_POOL = 0, DFLASH_BUF_KPOS = 1, DFLASH_BUF_SLOTS = 2,
-       DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4 };
+       DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4, DFLASH_BUF_HIDDEN_LO = 5 };
 int dflash_debug_copy(dflash_ctx *ctx, int32_t buffer, void *dst, size_t offset, size_t bytes,
                       void *stream);
+
+/* ---- kernel timing ------------------------------------------------------------------
+ * Launch classes of the append and forward sequences. With timing on, every launch of a
+ * class whose bit (1 << class) is set in `class_mask` carries a start and a stop HIP event
+ * in its own dispatch (hipExtLaunchKernel), so the pair times that kernel alone;
+ * dflash_timing_read waits for them and returns, per class, the summed milliseconds and
+ * the number of launches since the last read (arrays of n_classes entries), then clears
+ * the tallies. class_mask 0 turns timing off. */
+enum {
+  DFLASH_K_PROLOGUE = 0,      /* block-table updates, block-row slots, embedding + first norm */
+  DFLASH_K_GEMM = 1,          /* weight-streaming Q/K/V, O, gate/up, down GEMMs of the forward */
+  DFLASH_K_QKV_POST = 2,      /* q/k RMSNorm, RoPE, K/V writeback */
+  DFLASH_K_ATTN = 3,          /* split-KV block attention */
+  DFLASH_K_ATTN_COMBINE = 4,  /* merge of the attention chunks */
+  DFLASH_K_RESID_NORM = 5,    /* residual add + RMSNorm */
+  DFLASH_K_SILU = 6,          /* SwiGLU */
+  DFLASH_K_LMHEAD = 7,        /* lm_head + argmax partials */
+  DFLASH_K_ARGMAX = 8,        /* argmax reduction */
+  DFLASH_K_APPEND_GEMM = 9,   /* fc and fused K/V GEMMs of the context append */
+  DFLASH_K_APPEND_MISC = 10,  /* append slots, hidden_norm, K/V epilogue + writeback */
+  DFLASH_K_NUM_CLASSES = 11
+};
+int dflash_timing(dflash_ctx *ctx, uint32_t class_mask);
+int dflash_timing_read(dflash_ctx *ctx, double *ms, int64_t *launches, int32_t n_classes);
 
 /* Message of the last failure on this context ("" if none); valid until the next call. */
 const char *dflash_last_error(const dflash_ctx *ctx);

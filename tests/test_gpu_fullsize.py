@@ -1,0 +1,97 @@
+"""GPU parity at the full drafter shape of the benchmark (8 layers, hidden 2048, GQA 32:4,
+head_dim 128, ff 6144, vocab 151936, 5 taps of hidden 2048), in the launch configuration
+bench.py times: context 4096, batch 1, gamma 16; and the 16-sequence batched forward."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_diffusion_draft_02_amd import binding as B
+from oracle import dflash_oracle as O
+from gpu_util import Agreement, Pair, dev_bf16, pool_view, read_i32, read_i64, DEV
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qwen3():
+    w = synth.workload("qwen3-L8-h2048-ctx4096-b1")
+    m = w["model_cfg"]
+    return m, synth.gen_weights(m, w["seed"]), w["seed"]
+
+
+def test_ctx4096_batch1_parity(qwen3):
+    m, W, seed = qwen3
+    pair = Pair(m, W, 8192, 1)
+    pair.append(0, synth.gen_hidden(m, seed, 4096, 0))
+    # cached K/V of sampled rows, every layer and kv head, against the oracle
+    geo = pair.gpu.dflash_pool_geometry()
+    pool = pool_view(pair.gpu)
+    hd, nkv = m["head_dim"], m["num_kv_heads"]
+    s = pair.ora.seqs[0]
+    rows = np.array([0, 1, 15, 16, 1000, 2047, 2048, 4095])
+    slots = pair.ora.pool.slots(0, rows)
+    pg, off = slots // 16, slots % 16
+    kpos = read_i32(pair.gpu, B.DFLASH_BUF_KPOS, geo["num_pages"] * 16)
+    assert np.array_equal(kpos[slots], rows)
+    for l in range(m["num_layers"]):
+        K = pool[l, pg, 0].reshape(len(rows), nkv, 16, hd)[np.arange(len(rows)), :, off, :]
+        V = pool[l, pg, 1].reshape(len(rows), nkv, hd, 16)[np.arange(len(rows)), :, :, off]
+        for got, want in ((K, s["k"][l][rows]), (V, s["v"][l][rows])):
+            assert np.abs(O.widen(got) - want).max() <= 2e-2 * np.abs(want).max()
+    agree = Agreement()
+    for call in range(12):
+        qpos = None if call % 3 else [4096 + 7 * call]
+        toks, logits, ref = pair.forward([0], synth.gen_bonus(m, seed, 1, index=call), q_rope_pos=qpos)
+        agree.add(toks, logits, ref)
+        assert np.array_equal(read_i64(pair.gpu, B.DFLASH_BUF_SLOTS, 16), pair.ora.last_slots)
+    rate = agree.check(min_positions=150)
+    print(f"ctx4096 parity: {agree.n} positions, agreement {rate:.4f}, max rel dlogit {agree.max_rel:.3e}")
+    pair.close()
+
+
+def test_batch16_forward_parity_short_contexts(qwen3):
+    """The 16-band forward (256 rows: several skinny-GEMM row groups, 16 attention bands) on
+    non-contiguous pages, against the oracle, at contexts it computes in seconds."""
+    m, W, seed = qwen3
+    nb = 16
+    max_seq = 512
+    P = O.pool_pages(max_seq, 16, nb)[1]
+    pair = Pair(m, W, max_seq, nb, page_order=synth.gen_page_order(P - 1, seed))
+    lens = synth.gen_ctx_lengths(1, 300, nb, seed)
+    for s in range(nb):
+        pair.append(s, synth.gen_hidden(m, seed, int(lens[s]), 50 + s))
+    agree = Agreement()
+    toks, logits, ref = pair.forward(list(range(nb))[::-1], synth.gen_bonus(m, seed, nb, index=77))
+    agree.add(toks, logits, ref)
+    rate = agree.check(min_positions=200)
+    print(f"batch16 parity: {agree.n} positions, agreement {rate:.4f}, max rel dlogit {agree.max_rel:.3e}")
+    pair.close()
+
+
+def test_batch16_full_contexts_band_invariance(qwen3):
+    """At the batched workload's own context lengths (512..8192) every band of the 16-band
+    call equals the same band run alone, bit for bit."""
+    m, W, seed = qwen3
+    w = synth.workload("qwen3-L8-h2048-b16-ctx512to8192")
+    nb = w["batch"]
+    lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, w["seed"])
+    max_seq = 8192
+    per_seq = -(-(max_seq + 17) // 16)
+    Wd = {k: dev_bf16(v) for k, v in W.items()}
+    d = B.Drafter(m, Wd, max_seq, nb, page_order=synth.gen_page_order(per_seq * nb, w["seed"]))
+    for s in range(nb):
+        d.dflash_ctx_kv_append(s, dev_bf16(synth.gen_hidden(m, w["seed"], int(lens[s]), s)))
+    bonus = synth.gen_bonus(m, w["seed"], nb)
+    V = m["vocab"]
+    tb = torch.empty((nb, 15), dtype=torch.int32, device=DEV)
+    lb = torch.empty((nb * 15, V), dtype=torch.float32, device=DEV)
+    d.dflash_block_forward(list(range(nb)), bonus, tb, lb)
+    for s in (0, 5, 11, 15):
+        t1 = torch.empty((1, 15), dtype=torch.int32, device=DEV)
+        l1 = torch.empty((15, V), dtype=torch.float32, device=DEV)
+        d.dflash_block_forward([s], [bonus[s]], t1, l1)
+        torch.cuda.synchronize()
+        assert torch.equal(t1[0], tb[s]) and torch.equal(l1, lb[s * 15:(s + 1) * 15])
+    assert int(tb.min()) >= 0 and int(tb.max()) < V
+    d.close()
