@@ -33,18 +33,21 @@ struct AttnLds {
   int page[KCMAX / PAGE];
 };
 
-template <int HD, int RT>
-__global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
-                                                    const bf16* __restrict__ Q_lo,
-                                                    const Band* __restrict__ bands, int n_bands,
-                                                    int gamma, int nh, KvGeom g, int layer, int sw,
-                                                    int window, float scale_log2,
-                                                    float* __restrict__ part_o,
-                                                    float* __restrict__ part_ml) {
+constexpr int AW = 8;       // wavefronts per attention workgroup, 16 query rows each
+constexpr int RPAD = AW * 16;
+
+template <int HD>
+__global__ __launch_bounds__(AW * 64) void k_block_attn(const bf16* __restrict__ Q,
+                                                        const bf16* __restrict__ Q_lo,
+                                                        const Band* __restrict__ bands, int n_bands,
+                                                        int gamma, int nh, KvGeom g, int layer, int sw,
+                                                        int window, float scale_log2,
+                                                        float* __restrict__ part_o,
+                                                        float* __restrict__ part_ml) {
   constexpr int NS = HD / 32;
   constexpr int ND = HD / 16;
-  constexpr int RPAD = 4 * RT * 16;
   constexpr int P8 = HD / 8;  // 16-byte pieces per K row
+  constexpr int NT = AW * 64;
   __shared__ __attribute__((aligned(16))) AttnLds<HD> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, grp = lane >> 4;
@@ -60,37 +63,37 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
   const int k0 = bands[b].kstart[sw] + ch * bands[b].ck[sw];   // page aligned
   const int k1 = min(k0 + bands[b].ck[sw], kend);
   const int npg = (k1 - k0 + PAGE - 1) / PAGE;                 // pages holding keys of the chunk
-  const int nst = (k1 - k0 + 31) / 32 * 2;                     // pages staged: whole 32-key tiles
+  const int nst = (k1 - k0 + 63) / 64 * 4;                     // pages staged: whole 64-key steps
   const int R = gamma * G;
   const size_t pl = page_layer_elems(nkv, HD);
   const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
 
-  // ---- stage the chunk: page ids, then every K row, V page and position at once. A tile's
-  // second page past the chunk's end is the zeroed sentinel page 0, so every value the MFMAs
+  // ---- stage the chunk: page ids, then every K row, V page and position at once. Pages of
+  // a step past the chunk's end are the zeroed sentinel page 0, so every value the MFMAs
   // read is finite (masked keys then contribute exactly zero).
   if (threadIdx.x < nst)
     sm.page[threadIdx.x] = threadIdx.x < npg ? g.bt[(size_t)seq * g.per_seq + (k0 >> 4) + threadIdx.x] : 0;
   __syncthreads();
   {
-    const int nk = nst * PAGE;           // keys staged (the tail past k1 is masked below)
+    const int nk = nst * PAGE;
     const int pieces = nk * P8;          // K pieces; V has the same count
-    for (int base = 0; base < pieces; base += 256 * 8) {
+    for (int base = 0; base < pieces; base += NT * 8) {
       u32x4 kr[8], vr[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int pc = base + u * 256 + threadIdx.x;
+        const int pc = base + u * NT + threadIdx.x;
         if (pc < pieces) {
           const int kl = pc / P8, d8 = pc % P8;
-          const bf16* pg = lpool + (size_t)sm.page[kl >> 4] * pl;
-          kr[u] = *reinterpret_cast<const u32x4*>(pg + ((size_t)kvh * PAGE + (kl & 15)) * HD + d8 * 8);
-          // V: piece pc is the pc-th 16 bytes of the chunk's [page][d][16] block
+          kr[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)sm.page[kl >> 4] * pl +
+                                                  ((size_t)kvh * PAGE + (kl & 15)) * HD + d8 * 8);
           const int vp = pc / (HD * 2), vo = pc % (HD * 2);
-          vr[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)sm.page[vp] * pl + (size_t)(nkv + kvh) * HD * PAGE + vo * 8);
+          vr[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)sm.page[vp] * pl +
+                                                  (size_t)(nkv + kvh) * HD * PAGE + vo * 8);
         }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int pc = base + u * 256 + threadIdx.x;
+        const int pc = base + u * NT + threadIdx.x;
         if (pc < pieces) {
           const int kl = pc / P8, d8 = pc % P8;
           *reinterpret_cast<u32x4*>(&sm.k[kl][d8 * 8]) = kr[u];
@@ -99,127 +102,114 @@ __global__ __launch_bounds__(256) void k_block_attn(const bf16* __restrict__ Q,
       }
     }
     if (window > 0)
-      for (int kl = threadIdx.x; kl < nk; kl += 256) sm.pos[kl] = g.kpos[(size_t)sm.page[kl >> 4] * PAGE + (kl & 15)];
+      for (int kl = threadIdx.x; kl < nk; kl += NT) sm.pos[kl] = g.kpos[(size_t)sm.page[kl >> 4] * PAGE + (kl & 15)];
   }
 
-  bf16x8 qb[RT][NS], ql[RT][NS];
-  int qpos[RT];
-#pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    const int r = (wave * RT + j) * 16 + c;
-    const bool rv = r < R;
+  // this wave's 16 query rows: r = wave * 16 + c (block row r % gamma, head r / gamma)
+  const int r = wave * 16 + c;
+  const bool rv = r < R;
+  const bool wave_active = wave * 16 < R;
+  bf16x8 qb[NS], ql[NS];
+  int qpos;
+  {
     const int i = rv ? r % gamma : 0, hq = rv ? r / gamma : 0;
     const size_t qo = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + grp * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      qb[j][s] = ld8(Q + qo + s * 32);
-      ql[j][s] = ld8(Q_lo + qo + s * 32);
+      qb[s] = ld8(Q + qo + s * 32);
+      ql[s] = ld8(Q_lo + qo + s * 32);
     }
-    qpos[j] = qpos0 + i;
+    qpos = qpos0 + i;
   }
-  float m_run[RT], l_run[RT];
-  f32x4 o[RT][ND];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[ND];
 #pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  for (int kt = 0; kt < k1 - k0; kt += 32) {
-    f32x4 sacc[RT][2];
+  if (wave_active) {
+    for (int kt = 0; kt < k1 - k0; kt += 64) {
+      // S^T for 64 keys: MFMA tile t covers keys (t/2)*32 + (m/4)*8 + (t%2)*4 + m%4 for its
+      // row m, so lane (c, grp) ends up with keys kt + p*32 + grp*8 + 0..7 (p = 0, 1) of row c
+      f32x4 sacc[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int kl = kt + (c >> 2) * 8 + t * 4 + (c & 3);   // < npg * 16: staged
+      for (int t = 0; t < 4; ++t) {
+        const int kl = kt + (t >> 1) * 32 + (c >> 2) * 8 + (t & 1) * 4 + (c & 3);
+        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < RT; ++j) sacc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.k[kl][s * 32 + grp * 8]));
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-          sacc[j][t] = mfma16(a, qb[j][s], sacc[j][t]);
-          sacc[j][t] = mfma16(a, ql[j][s], sacc[j][t]);
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.k[kl][s * 32 + grp * 8]));
+          sacc[t] = mfma16(a, qb[s], sacc[t]);
+          sacc[t] = mfma16(a, ql[s], sacc[t]);
         }
       }
-    }
-    // this lane now holds, for query row c of every row tile, keys kbase + 0..7
-    const int kbl = kt + grp * 8;
-    bf16x8 pb[RT];
-#pragma unroll
-    for (int j = 0; j < RT; ++j) {
-      float sv[8];
+      float sv[16];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bool ok = k0 + kbl + e < k1;
-        if (window > 0) ok = ok && (qpos[j] - sm.pos[kbl + e] < window);
-        sv[e] = ok ? sacc[j][e >> 2][e & 3] * scale_log2 : -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        const int kl = kt + (e >> 3) * 32 + grp * 8 + (e & 7);
+        bool ok = k0 + kl < k1;
+        if (window > 0) ok = ok && (qpos - sm.pos[kl] < window);
+        sv[e] = ok ? sacc[(e >> 3) * 2 + ((e >> 2) & 1)][e & 3] * scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, sv[e]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[j], tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[j] - m_new);
-      float p[8];
-      float ps = 0.f;
+      const float m_new = fmaxf(m_run, tmax);
+      // rescale the running output only when some row's maximum moved
+      if (__any(m_new > m_run)) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - m_new);
-        ps += p[e];
+        for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
       }
-      l_run[j] = l_run[j] * alpha + ps;
-      m_run[j] = m_new;
+      m_run = m_new;
+      float p[16];
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) o[j][dt] *= alpha;
-      pb[j] = pack8(p);
-    }
-    const bf16* vp = &sm.v[kbl >> 4][0][kbl & 15];
+      for (int e = 0; e < 16; ++e) {
+        p[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - m_new);
+        l_run += p[e];
+      }
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + (size_t)(dt * 16 + c) * PAGE));
+      for (int ps = 0; ps < 2; ++ps) {
+        const bf16x8 pb = pack8(p + ps * 8);
+        const int kl = kt + ps * 32 + grp * 8;
+        const bf16* vp = &sm.v[kl >> 4][0][kl & 15];
 #pragma unroll
-      for (int j = 0; j < RT; ++j) o[j][dt] = mfma16(a, pb[j], o[j][dt]);
+        for (int dt = 0; dt < ND; ++dt) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + (size_t)(dt * 16 + c) * PAGE));
+          o[dt] = mfma16(a, pb, o[dt]);
+        }
+      }
     }
   }
 
+  float lt = l_run;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (!rv) return;
   const size_t item = (size_t)cg * nkv + kvh;
+  float* po = part_o + (item * RPAD + r) * HD + 4 * grp;
 #pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    float lt = l_run[j];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const int r = (wave * RT + j) * 16 + c;
-    if (r >= R) continue;
-    float* po = part_o + (item * RPAD + r) * HD + 4 * grp;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[j][dt];
-    if (grp == 0) {
-      part_ml[(item * RPAD + r) * 2 + 0] = m_run[j];
-      part_ml[(item * RPAD + r) * 2 + 1] = lt;
-    }
+  for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+  if (grp == 0) {
+    part_ml[(item * RPAD + r) * 2 + 0] = m_run;
+    part_ml[(item * RPAD + r) * 2 + 1] = lt;
   }
 }
-
-static int attn_rt(int gamma, int G) { return gamma * G <= 64 ? 1 : 2; }
 
 hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_dev, int n_bands, int total_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st) {
   const int G = nh / g.nkv;
-  if (gamma * G > 128) return hipErrorInvalidValue;
+  if (gamma * G > RPAD) return hipErrorInvalidValue;
   dim3 grid(total_chunks, g.nkv);
-  const int rt = attn_rt(gamma, G);
-#define DFL_ATTN(HDV, RTV)                                                                   \
-  (void)launch(k_block_attn<HDV, RTV>, grid, 256, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, \
-                                               window, scale_log2, part_o, part_ml)
-  if (g.hd == 128) { if (rt == 1) DFL_ATTN(128, 1); else DFL_ATTN(128, 2); }
-  else if (g.hd == 64) { if (rt == 1) DFL_ATTN(64, 1); else DFL_ATTN(64, 2); }
-  else if (g.hd == 32) { if (rt == 1) DFL_ATTN(32, 1); else DFL_ATTN(32, 2); }
-  else return hipErrorInvalidValue;
-#undef DFL_ATTN
+  switch (g.hd) {
+    case 128: (void)launch(k_block_attn<128>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml); break;
+    case 64: (void)launch(k_block_attn<64>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml); break;
+    case 32: (void)launch(k_block_attn<32>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -272,7 +262,7 @@ hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const 
                                int n_bands, int gamma, int nh, int nkv, int hd, int sw,
                                bf16* out, bf16* out_lo, hipStream_t st) {
   const int G = nh / nkv;
-  const int rpad = 4 * attn_rt(gamma, G) * 16;
+  const int rpad = RPAD;
   dim3 grid(n_bands, nkv, (gamma * G + 15) / 16);
   switch (hd) {
     case 32: (void)launch(k_attn_combine<32>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
