@@ -2,13 +2,13 @@
 // every block query sees every context key and every block key; scale 1/sqrt(head_dim);
 // sliding layers additionally hide keys with q_pos - k_pos >= window).
 //
-// Work split: one workgroup per (band, kv head, key chunk of at most 256 keys). The
-// workgroup first stages the chunk's K rows, V pages and key positions in LDS with every
-// load in flight at once; its four wavefronts then own the band's gamma * G query rows of
-// that kv head (G = query heads per kv head), 16 or 32 rows each, and walk the chunk 32 keys
-// at a time:
-//   S^T = K Q^T   two 16x16x32 MFMA tiles per 32 keys; the key order inside the tiles is
-//                 permuted so that every lane ends up holding 8 consecutive keys of one row
+// Work split: one workgroup per (band, kv head, key chunk of at most 256 keys). The chunk
+// streams through two 64-key LDS buffers: the next step's K rows and V pages are in flight
+// while the current step is computed. The four wavefronts own the band's gamma * G query
+// rows of that kv head (G = query heads per kv head), two 16-row tiles each, so every K and
+// V fragment read from LDS feeds two MFMAs. Per 64-key step and row tile:
+//   S^T = K Q^T   four 16x16x32 MFMA tiles; the key order inside the tiles is permuted so
+//                 that every lane ends up holding 8 consecutive keys of one row
 //   online softmax per row (exp2 domain), lane-local partial sums
 //   O^T += V^T P^T one MFMA per 16 head dims; P^T comes straight from the lane's own
 //                 registers and V^T is one 16-byte load because V pages are stored [d][16]
@@ -21,22 +21,84 @@
 namespace dfl {
 
 constexpr int KCMAX = 256;  // keys per chunk (16 pages); the runtime never plans more
+constexpr int KSTEP = 64;   // keys per LDS buffer and softmax step
+constexpr int RT = 2;       // 16-row query tiles per wavefront
+constexpr int AW = 4;       // wavefronts per attention workgroup
+constexpr int RPAD = AW * RT * 16;
 
-// The chunk's keys in LDS: K rows padded to HD + 8 (1 KB + 16 B rows keep the MFMA operand
-// reads of any 8 consecutive lanes on distinct banks), V pages as stored ([d][16] per page),
-// the stamped position of every key, and the chunk's physical pages.
+// One 64-key step of the chunk in LDS.
+//  k: K rows padded to HD + 8, stored in MFMA tile order: LDS row t*16 + m holds the key
+//     that tile t's row m covers (kt_key below), so the 16 lanes reading one tile read 16
+//     consecutive LDS rows and any 8 of them hit distinct banks.
+//  v: the step's four V pages as stored ([d][16] per page) with the two 16-byte halves of a
+//     row d swapped when bit 2 of d is set (vswz), so lanes reading rows d..d+7 of one half
+//     hit distinct banks.
+template <int HD>
+struct AttnBuf {
+  bf16 k[KSTEP][HD + 8];
+  bf16 v[KSTEP / PAGE][HD][PAGE];
+};
+
 template <int HD>
 struct AttnLds {
-  bf16 k[KCMAX][HD + 8];
-  bf16 v[KCMAX / PAGE][HD][PAGE];
+  AttnBuf<HD> buf[2];
   int pos[KCMAX];
   int page[KCMAX / PAGE];
 };
 
-constexpr int AW = 8;       // wavefronts per attention workgroup, 16 query rows each
-constexpr int RPAD = AW * 16;
+// key (within a 64-key step) that row m of S^T tile t covers: tiles 2p and 2p+1 cover keys
+// 32p..32p+31 such that lane (c, g) of the MFMA result holds keys 32p + 8g + 0..7 of query
+// row c (4 from each tile)
+__device__ __forceinline__ int kt_key(int t, int m) { return (t >> 1) * 32 + (m >> 2) * 8 + (t & 1) * 4 + (m & 3); }
+// inverse: LDS row of a key
+__device__ __forceinline__ int key_row(int kl) {
+  const int w = kl & 31;
+  return ((kl >> 5) * 2 + ((w >> 2) & 1)) * 16 + (w >> 3) * 4 + (w & 3);
+}
+__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 1; }
+
+// the 16-byte pieces of one step each thread carries from HBM to LDS
+template <int HD>
+struct StepRegs {
+  static constexpr int PIECES = KSTEP * HD / 8;          // per K (and per V)
+  static constexpr int PER_T = (PIECES + AW * 64 - 1) / (AW * 64);
+  u32x4 k[PER_T], v[PER_T];
+};
 
 template <int HD>
+__device__ __forceinline__ void step_load(StepRegs<HD>& rg, const AttnLds<HD>& sm, const bf16* lpool,
+                                          size_t pl, int kvh, int nkv, int step) {
+  constexpr int P8 = HD / 8;
+#pragma unroll
+  for (int u = 0; u < StepRegs<HD>::PER_T; ++u) {
+    const int pc = u * AW * 64 + threadIdx.x;          // piece of this step
+    if (pc < StepRegs<HD>::PIECES) {
+      const int kl = pc / P8, d8 = pc % P8;              // key of the step, 8-element slice
+      const int pg = sm.page[step * (KSTEP / PAGE) + (kl >> 4)];
+      rg.k[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)pg * pl + ((size_t)kvh * PAGE + (kl & 15)) * HD + d8 * 8);
+      const int vp = pc / (HD * 2), vo = pc % (HD * 2);   // V: page of the step, 16-byte slice
+      const int pgv = sm.page[step * (KSTEP / PAGE) + vp];
+      rg.v[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)pgv * pl + (size_t)(nkv + kvh) * HD * PAGE + vo * 8);
+    }
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void step_store(AttnBuf<HD>& b, const StepRegs<HD>& rg) {
+  constexpr int P8 = HD / 8;
+#pragma unroll
+  for (int u = 0; u < StepRegs<HD>::PER_T; ++u) {
+    const int pc = u * AW * 64 + threadIdx.x;
+    if (pc < StepRegs<HD>::PIECES) {
+      const int kl = pc / P8, d8 = pc % P8;
+      *reinterpret_cast<u32x4*>(&b.k[key_row(kl)][d8 * 8]) = rg.k[u];
+      const int vp = pc / (HD * 2), d = (pc % (HD * 2)) >> 1, h = pc & 1;
+      *reinterpret_cast<u32x4*>(&b.v[vp][d][(h ^ vswz(d)) * 8]) = rg.v[u];
+    }
+  }
+}
+
+template <int HD, bool WIN>
 __global__ __launch_bounds__(AW * 64) void k_block_attn(const bf16* __restrict__ Q,
                                                         const bf16* __restrict__ Q_lo,
                                                         const Band* __restrict__ bands, int n_bands,
@@ -46,8 +108,6 @@ __global__ __launch_bounds__(AW * 64) void k_block_attn(const bf16* __restrict__
                                                         float* __restrict__ part_ml) {
   constexpr int NS = HD / 32;
   constexpr int ND = HD / 16;
-  constexpr int P8 = HD / 8;  // 16-byte pieces per K row
-  constexpr int NT = AW * 64;
   __shared__ __attribute__((aligned(16))) AttnLds<HD> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, grp = lane >> 4;
@@ -63,138 +123,145 @@ __global__ __launch_bounds__(AW * 64) void k_block_attn(const bf16* __restrict__
   const int k0 = bands[b].kstart[sw] + ch * bands[b].ck[sw];   // page aligned
   const int k1 = min(k0 + bands[b].ck[sw], kend);
   const int npg = (k1 - k0 + PAGE - 1) / PAGE;                 // pages holding keys of the chunk
-  const int nst = (k1 - k0 + 63) / 64 * 4;                     // pages staged: whole 64-key steps
+  const int nsteps = (k1 - k0 + KSTEP - 1) / KSTEP;
+  const int nst = nsteps * (KSTEP / PAGE);                     // pages staged: whole steps
   const int R = gamma * G;
   const size_t pl = page_layer_elems(nkv, HD);
   const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
 
-  // ---- stage the chunk: page ids, then every K row, V page and position at once. Pages of
-  // a step past the chunk's end are the zeroed sentinel page 0, so every value the MFMAs
-  // read is finite (masked keys then contribute exactly zero).
+  // page ids and stamped positions of the chunk. Pages of a step past the chunk's end are
+  // the zeroed sentinel page 0, so every value the MFMAs read is finite (masked keys then
+  // contribute exactly zero).
   if (threadIdx.x < nst)
     sm.page[threadIdx.x] = threadIdx.x < npg ? g.bt[(size_t)seq * g.per_seq + (k0 >> 4) + threadIdx.x] : 0;
   __syncthreads();
-  {
-    const int nk = nst * PAGE;
-    const int pieces = nk * P8;          // K pieces; V has the same count
-    for (int base = 0; base < pieces; base += NT * 8) {
-      u32x4 kr[8], vr[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int pc = base + u * NT + threadIdx.x;
-        if (pc < pieces) {
-          const int kl = pc / P8, d8 = pc % P8;
-          kr[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)sm.page[kl >> 4] * pl +
-                                                  ((size_t)kvh * PAGE + (kl & 15)) * HD + d8 * 8);
-          const int vp = pc / (HD * 2), vo = pc % (HD * 2);
-          vr[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)sm.page[vp] * pl +
-                                                  (size_t)(nkv + kvh) * HD * PAGE + vo * 8);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int pc = base + u * NT + threadIdx.x;
-        if (pc < pieces) {
-          const int kl = pc / P8, d8 = pc % P8;
-          *reinterpret_cast<u32x4*>(&sm.k[kl][d8 * 8]) = kr[u];
-          *reinterpret_cast<u32x4*>(&sm.v[0][0][0] + (size_t)pc * 8) = vr[u];
-        }
-      }
-    }
-    if (window > 0)
-      for (int kl = threadIdx.x; kl < nk; kl += NT) sm.pos[kl] = g.kpos[(size_t)sm.page[kl >> 4] * PAGE + (kl & 15)];
-  }
+  if (WIN)
+    for (int kl = threadIdx.x; kl < nst * PAGE; kl += AW * 64) sm.pos[kl] = g.kpos[(size_t)sm.page[kl >> 4] * PAGE + (kl & 15)];
 
-  // this wave's 16 query rows: r = wave * 16 + c (block row r % gamma, head r / gamma)
-  const int r = wave * 16 + c;
-  const bool rv = r < R;
-  const bool wave_active = wave * 16 < R;
-  bf16x8 qb[NS], ql[NS];
-  int qpos;
-  {
+  StepRegs<HD> rg;
+  step_load<HD>(rg, sm, lpool, pl, kvh, nkv, 0);
+
+  // this wave's query rows: tile rt holds rows r = (wave * RT + rt) * 16 + c, i.e. block
+  // row r % gamma of query head r / gamma (of this kv head's group)
+  const bool wave_active = wave * RT * 16 < R;
+  bf16x8 qb[RT][NS], ql[RT][NS];
+  int qpos[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = (wave * RT + rt) * 16 + c;
+    const bool rv = r < R;
     const int i = rv ? r % gamma : 0, hq = rv ? r / gamma : 0;
     const size_t qo = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + grp * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      qb[s] = ld8(Q + qo + s * 32);
-      ql[s] = ld8(Q_lo + qo + s * 32);
+      qb[rt][s] = ld8(Q + qo + s * 32);
+      ql[rt][s] = ld8(Q_lo + qo + s * 32);
     }
-    qpos = qpos0 + i;
+    qpos[rt] = qpos0 + i;
   }
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[ND];
+  float m_run[RT], l_run[RT];
+  f32x4 o[RT][ND];
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  step_store<HD>(sm.buf[0], rg);
   __syncthreads();
 
-  if (wave_active) {
-    for (int kt = 0; kt < k1 - k0; kt += 64) {
-      // S^T for 64 keys: MFMA tile t covers keys (t/2)*32 + (m/4)*8 + (t%2)*4 + m%4 for its
-      // row m, so lane (c, grp) ends up with keys kt + p*32 + grp*8 + 0..7 (p = 0, 1) of row c
-      f32x4 sacc[4];
+  for (int st = 0; st < nsteps; ++st) {
+    // the next step's pieces are in flight while this one is computed
+    if (st + 1 < nsteps) step_load<HD>(rg, sm, lpool, pl, kvh, nkv, st + 1);
+    const AttnBuf<HD>& bf = sm.buf[st & 1];
+    const int kt = st * KSTEP;
+    const int lim = k1 - k0 - kt;   // keys of this step that exist
+    if (wave_active) {
+      // S^T = K Q^T: per tile and row tile, the hi and lo query terms accumulate in separate
+      // chains, so consecutive MFMAs are independent
+      f32x4 sh[RT][4], sl[RT][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int kl = kt + (t >> 1) * 32 + (c >> 2) * 8 + (t & 1) * 4 + (c & 3);
-        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sh[rt][t] = sl[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.k[kl][s * 32 + grp * 8]));
-          sacc[t] = mfma16(a, qb[s], sacc[t]);
-          sacc[t] = mfma16(a, ql[s], sacc[t]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&bf.k[t * 16 + c][s * 32 + grp * 8]));
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            sh[rt][t] = mfma16(a, qb[rt][s], sh[rt][t]);
+            sl[rt][t] = mfma16(a, ql[rt][s], sl[rt][t]);
+          }
         }
       }
-      float sv[16];
-      float tmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kl = kt + (e >> 3) * 32 + grp * 8 + (e & 7);
-        bool ok = k0 + kl < k1;
-        if (window > 0) ok = ok && (qpos - sm.pos[kl] < window);
-        sv[e] = ok ? sacc[(e >> 3) * 2 + ((e >> 2) & 1)][e & 3] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[e]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      // rescale the running output only when some row's maximum moved
-      if (__any(m_new > m_run)) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        l_run *= alpha;
+      for (int rt = 0; rt < RT; ++rt) {
+        // lane (c, grp) holds keys p*32 + grp*8 + 0..7 (p = 0, 1) of row c: element e is key
+        // (e/8)*32 + grp*8 + e%8, from tile 2*(e/8) + (e/4)%2, slot e%4
+        float sv[16];
+        float tmax = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
-      }
-      m_run = m_new;
-      float p[16];
+        for (int e = 0; e < 16; ++e) {
+          const int kl = (e >> 3) * 32 + grp * 8 + (e & 7);
+          const int t = (e >> 3) * 2 + ((e >> 2) & 1);
+          const float x = (sh[rt][t][e & 3] + sl[rt][t][e & 3]) * scale_log2;
+          bool ok = kl < lim;
+          if (WIN) ok = ok & (qpos[rt] - sm.pos[kt + kl] < window);
+          sv[e] = ok ? x : -INFINITY;
+          tmax = fmaxf(tmax, sv[e]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run[rt], tmax);
+        // rescale the running output only when some row's maximum moved
+        if (__any(m_new > m_run[rt])) {
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+          l_run[rt] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - m_new);
-        l_run += p[e];
-      }
+          for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
+        }
+        m_run[rt] = m_new;
 #pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        const bf16x8 pb = pack8(p + ps * 8);
-        const int kl = kt + ps * 32 + grp * 8;
-        const bf16* vp = &sm.v[kl >> 4][0][kl & 15];
+        for (int e = 0; e < 16; ++e) {
+          sv[e] = (sv[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
+          l_run[rt] += sv[e];
+        }
+        // O^T += V^T P^T over the two 32-key halves
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + (size_t)(dt * 16 + c) * PAGE));
-          o[dt] = mfma16(a, pb, o[dt]);
+        for (int ps = 0; ps < 2; ++ps) {
+          const bf16x8 pb = pack8(sv + ps * 8);
+          const int kl = ps * 32 + grp * 8;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const int d = dt * 16 + c;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                &bf.v[kl >> 4][d][(((kl & 15) >> 3) ^ vswz(d)) * 8]));
+            o[rt][dt] = mfma16(a, pb, o[rt][dt]);
+          }
         }
       }
     }
+    if (st + 1 < nsteps) step_store<HD>(sm.buf[(st + 1) & 1], rg);
+    __syncthreads();
   }
 
-  float lt = l_run;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (!rv) return;
   const size_t item = (size_t)cg * nkv + kvh;
-  float* po = part_o + (item * RPAD + r) * HD + 4 * grp;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
-  if (grp == 0) {
-    part_ml[(item * RPAD + r) * 2 + 0] = m_run;
-    part_ml[(item * RPAD + r) * 2 + 1] = lt;
+  for (int rt = 0; rt < RT; ++rt) {
+    float lt = l_run[rt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const int r = (wave * RT + rt) * 16 + c;
+    if (r < R) {
+      float* po = part_o + (item * RPAD + r) * HD + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[rt][dt];
+      if (grp == 0) {
+        part_ml[(item * RPAD + r) * 2 + 0] = m_run[rt];
+        part_ml[(item * RPAD + r) * 2 + 1] = lt;
+      }
+    }
   }
 }
 
@@ -204,12 +271,15 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_
   const int G = nh / g.nkv;
   if (gamma * G > RPAD) return hipErrorInvalidValue;
   dim3 grid(total_chunks, g.nkv);
+#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
+  const bool win = window > 0;
   switch (g.hd) {
-    case 128: (void)launch(k_block_attn<128>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml); break;
-    case 64: (void)launch(k_block_attn<64>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml); break;
-    case 32: (void)launch(k_block_attn<32>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml); break;
+    case 128: if (win) DFL_ATTN(128, true); else DFL_ATTN(128, false); break;
+    case 64: if (win) DFL_ATTN(64, true); else DFL_ATTN(64, false); break;
+    case 32: if (win) DFL_ATTN(32, true); else DFL_ATTN(32, false); break;
     default: return hipErrorInvalidValue;
   }
+#undef DFL_ATTN
   return hipGetLastError();
 }
 
