@@ -2,153 +2,83 @@
 // every block query sees every context key and every block key; scale 1/sqrt(head_dim);
 // sliding layers additionally hide keys with q_pos - k_pos >= window).
 //
-// Work split: one workgroup per (band, kv head, key chunk of at most 256 keys). The chunk
-// streams through two 64-key LDS buffers: the next step's K rows and V pages are in flight
-// while the current step is computed. The four wavefronts own the band's gamma * G query
-// rows of that kv head (G = query heads per kv head), two 16-row tiles each, so every K and
-// V fragment read from LDS feeds two MFMAs. Per 64-key step and row tile:
-//   S^T = K Q^T   four 16x16x32 MFMA tiles; the key order inside the tiles is permuted so
-//                 that every lane ends up holding 8 consecutive keys of one row
-//   online softmax per row (exp2 domain), lane-local partial sums
+// Work split: the keys of a band are cut into chunks whose length depends only on the band's
+// own length (a multiple of 128 keys), so a band's result does not depend on which other
+// bands share the call. One workgroup per (chunk, kv head, 32 query rows): each of its four
+// wavefronts takes 32-key slices of the chunk (keys 32w, 32w + 128, ...), loads the K and V^T
+// fragments of a slice straight from the pool into MFMA operands, and keeps an online
+// softmax state for its two 16-row query tiles:
+//   S^T = K Q^T   two 16x16x32 MFMA tiles per slice; the key order inside the tiles is
+//                 permuted so that every lane ends up holding 8 consecutive keys of one row
 //   O^T += V^T P^T one MFMA per 16 head dims; P^T comes straight from the lane's own
 //                 registers and V^T is one 16-byte load because V pages are stored [d][16]
-// Each chunk leaves (max, sum, unnormalised O) per row; k_attn_combine merges the chunks of
-// a band in chunk order. The chunking of a band depends only on its own length, so a band's
-// result does not depend on which other bands share the call.
+// The four states are merged in wave order through LDS into one (max, sum, unnormalised O)
+// partial per row and chunk; k_attn_combine merges the chunks of a band.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dfl {
 
-constexpr int KCMAX = 256;  // keys per chunk (16 pages); the runtime never plans more
-constexpr int KSTEP = 64;   // keys per LDS buffer and softmax step
-constexpr int RT = 2;       // 16-row query tiles per wavefront
-constexpr int AW = 4;       // wavefronts per attention workgroup
-constexpr int RPAD = AW * RT * 16;
+constexpr int KW = 32;           // keys of one wavefront's slice per pass
+constexpr int AW = 4;            // wavefronts per workgroup
+constexpr int KP = AW * KW;      // keys of one workgroup pass
+constexpr int RG = 32;           // query rows per workgroup: two 16-row tiles
+constexpr int RPAD = 128;        // query-row slots of one (chunk, kv head) partial
+constexpr int NCH_MAX = 64;      // chunks of one band that k_attn_combine accepts
 
-// One 64-key step of the chunk in LDS.
-//  k: K rows padded to HD + 8, stored in MFMA tile order: LDS row t*16 + m holds the key
-//     that tile t's row m covers (kt_key below), so the 16 lanes reading one tile read 16
-//     consecutive LDS rows and any 8 of them hit distinct banks.
-//  v: the step's four V pages as stored ([d][16] per page) with the two 16-byte halves of a
-//     row d swapped when bit 2 of d is set (vswz), so lanes reading rows d..d+7 of one half
-//     hit distinct banks.
+// the waves' partial states, merged in wave order at the end of a workgroup
 template <int HD>
-struct AttnBuf {
-  bf16 k[KSTEP][HD + 8];
-  bf16 v[KSTEP / PAGE][HD][PAGE];
+struct MergeLds {
+  float o[AW][RG][HD + 4];   // rows padded by 16 B: the lanes storing one tile hit distinct banks
+  float m[AW][RG];
+  float l[AW][RG];
 };
-
-template <int HD>
-struct AttnLds {
-  AttnBuf<HD> buf[2];
-  int pos[KCMAX];
-  int page[KCMAX / PAGE];
-};
-
-// key (within a 64-key step) that row m of S^T tile t covers: tiles 2p and 2p+1 cover keys
-// 32p..32p+31 such that lane (c, g) of the MFMA result holds keys 32p + 8g + 0..7 of query
-// row c (4 from each tile)
-__device__ __forceinline__ int kt_key(int t, int m) { return (t >> 1) * 32 + (m >> 2) * 8 + (t & 1) * 4 + (m & 3); }
-// inverse: LDS row of a key
-__device__ __forceinline__ int key_row(int kl) {
-  const int w = kl & 31;
-  return ((kl >> 5) * 2 + ((w >> 2) & 1)) * 16 + (w >> 3) * 4 + (w & 3);
-}
-__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 1; }
-
-// the 16-byte pieces of one step each thread carries from HBM to LDS
-template <int HD>
-struct StepRegs {
-  static constexpr int PIECES = KSTEP * HD / 8;          // per K (and per V)
-  static constexpr int PER_T = (PIECES + AW * 64 - 1) / (AW * 64);
-  u32x4 k[PER_T], v[PER_T];
-};
-
-template <int HD>
-__device__ __forceinline__ void step_load(StepRegs<HD>& rg, const AttnLds<HD>& sm, const bf16* lpool,
-                                          size_t pl, int kvh, int nkv, int step) {
-  constexpr int P8 = HD / 8;
-#pragma unroll
-  for (int u = 0; u < StepRegs<HD>::PER_T; ++u) {
-    const int pc = u * AW * 64 + threadIdx.x;          // piece of this step
-    if (pc < StepRegs<HD>::PIECES) {
-      const int kl = pc / P8, d8 = pc % P8;              // key of the step, 8-element slice
-      const int pg = sm.page[step * (KSTEP / PAGE) + (kl >> 4)];
-      rg.k[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)pg * pl + ((size_t)kvh * PAGE + (kl & 15)) * HD + d8 * 8);
-      const int vp = pc / (HD * 2), vo = pc % (HD * 2);   // V: page of the step, 16-byte slice
-      const int pgv = sm.page[step * (KSTEP / PAGE) + vp];
-      rg.v[u] = *reinterpret_cast<const u32x4*>(lpool + (size_t)pgv * pl + (size_t)(nkv + kvh) * HD * PAGE + vo * 8);
-    }
-  }
-}
-
-template <int HD>
-__device__ __forceinline__ void step_store(AttnBuf<HD>& b, const StepRegs<HD>& rg) {
-  constexpr int P8 = HD / 8;
-#pragma unroll
-  for (int u = 0; u < StepRegs<HD>::PER_T; ++u) {
-    const int pc = u * AW * 64 + threadIdx.x;
-    if (pc < StepRegs<HD>::PIECES) {
-      const int kl = pc / P8, d8 = pc % P8;
-      *reinterpret_cast<u32x4*>(&b.k[key_row(kl)][d8 * 8]) = rg.k[u];
-      const int vp = pc / (HD * 2), d = (pc % (HD * 2)) >> 1, h = pc & 1;
-      *reinterpret_cast<u32x4*>(&b.v[vp][d][(h ^ vswz(d)) * 8]) = rg.v[u];
-    }
-  }
-}
 
 template <int HD, bool WIN>
-__global__ __launch_bounds__(AW * 64) void k_block_attn(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn(const bf16* __restrict__ Q,
                                                         const bf16* __restrict__ Q_lo,
                                                         const Band* __restrict__ bands, int n_bands,
-                                                        int gamma, int nh, KvGeom g, int layer, int sw,
-                                                        int window, float scale_log2,
-                                                        float* __restrict__ part_o,
+                                                        int n_items, int nrg, int gamma, int nh,
+                                                        KvGeom g, int layer, int sw, int window,
+                                                        float scale_log2, float* __restrict__ part_o,
                                                         float* __restrict__ part_ml) {
   constexpr int NS = HD / 32;
   constexpr int ND = HD / 16;
-  __shared__ __attribute__((aligned(16))) AttnLds<HD> sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) MergeLds<HD> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, grp = lane >> 4;
-  const int kvh = blockIdx.y;
+  // Workgroups are handed to the eight XCDs round robin, so ids 8 apart share an XCD and its
+  // L2: the row groups of one (chunk, kv head) item get ids 8 apart and read its K/V from
+  // HBM once.
+  const int id = blockIdx.x;
+  const int qd = id >> 3;
+  const int rg = qd % nrg;
+  const int item = (qd / nrg) * 8 + (id & 7);
+  if (item >= n_items) return;
   const int nkv = g.nkv;
+  const int cg = item / nkv, kvh = item - cg * nkv;
   const int G = nh / nkv;
-  const int cg = blockIdx.x;
   int b = 0;
   while (b + 1 < n_bands && cg >= bands[b + 1].base[sw]) ++b;
   const int seq = bands[b].seq, C = bands[b].kv_len, qpos0 = bands[b].q_pos;
   const int ch = cg - bands[b].base[sw];
-  const int kend = C + gamma;
   const int k0 = bands[b].kstart[sw] + ch * bands[b].ck[sw];   // page aligned
-  const int k1 = min(k0 + bands[b].ck[sw], kend);
-  const int npg = (k1 - k0 + PAGE - 1) / PAGE;                 // pages holding keys of the chunk
-  const int nsteps = (k1 - k0 + KSTEP - 1) / KSTEP;
-  const int nst = nsteps * (KSTEP / PAGE);                     // pages staged: whole steps
+  const int k1 = min(k0 + bands[b].ck[sw], C + gamma);
+  const int nkeys = k1 - k0;
+  const int npg = (nkeys + PAGE - 1) / PAGE;
   const int R = gamma * G;
   const size_t pl = page_layer_elems(nkv, HD);
   const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
+  const int* bt = g.bt + (size_t)seq * g.per_seq + (k0 >> 4);
 
-  // page ids and stamped positions of the chunk. Pages of a step past the chunk's end are
-  // the zeroed sentinel page 0, so every value the MFMAs read is finite (masked keys then
-  // contribute exactly zero).
-  if (threadIdx.x < nst)
-    sm.page[threadIdx.x] = threadIdx.x < npg ? g.bt[(size_t)seq * g.per_seq + (k0 >> 4) + threadIdx.x] : 0;
-  __syncthreads();
-  if (WIN)
-    for (int kl = threadIdx.x; kl < nst * PAGE; kl += AW * 64) sm.pos[kl] = g.kpos[(size_t)sm.page[kl >> 4] * PAGE + (kl & 15)];
-
-  StepRegs<HD> rg;
-  step_load<HD>(rg, sm, lpool, pl, kvh, nkv, 0);
-
-  // this wave's query rows: tile rt holds rows r = (wave * RT + rt) * 16 + c, i.e. block
-  // row r % gamma of query head r / gamma (of this kv head's group)
-  const bool wave_active = wave * RT * 16 < R;
-  bf16x8 qb[RT][NS], ql[RT][NS];
-  int qpos[RT];
+  // this workgroup's query rows: tile rt holds rows r = rg*32 + rt*16 + c, i.e. block row
+  // r % gamma of query head r / gamma (of this kv head's group)
+  bf16x8 qb[2][NS], ql[2][NS];
+  int qpos[2];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = (wave * RT + rt) * 16 + c;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = rg * RG + rt * 16 + c;
     const bool rv = r < R;
     const int i = rv ? r % gamma : 0, hq = rv ? r / gamma : 0;
     const size_t qo = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + grp * 8;
@@ -159,109 +89,135 @@ __global__ __launch_bounds__(AW * 64) void k_block_attn(const bf16* __restrict__
     }
     qpos[rt] = qpos0 + i;
   }
-  float m_run[RT], l_run[RT];
-  f32x4 o[RT][ND];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][ND];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  step_store<HD>(sm.buf[0], rg);
-  __syncthreads();
 
-  for (int st = 0; st < nsteps; ++st) {
-    // the next step's pieces are in flight while this one is computed
-    if (st + 1 < nsteps) step_load<HD>(rg, sm, lpool, pl, kvh, nkv, st + 1);
-    const AttnBuf<HD>& bf = sm.buf[st & 1];
-    const int kt = st * KSTEP;
-    const int lim = k1 - k0 - kt;   // keys of this step that exist
-    if (wave_active) {
-      // S^T = K Q^T: per tile and row tile, the hi and lo query terms accumulate in separate
-      // chains, so consecutive MFMAs are independent
-      f32x4 sh[RT][4], sl[RT][4];
+  for (int kt = wave * KW; kt < nkeys; kt += KP) {
+    // the slice's 32 keys lie on chunk pages kt/16 and kt/16 + 1 (the zeroed sentinel page 0
+    // past the chunk, so every operand is finite and masked keys add exactly zero)
+    const int lp = kt >> 4;
+    const int p0 = bt[lp];
+    const int p1 = lp + 1 < npg ? bt[lp + 1] : 0;
+    // K fragments: S^T tile t, row c covers slice key (c/4)*8 + t*4 + c%4, so lane (c, grp)
+    // of the result holds slice keys grp*8 + 0..7 of query row c (e = t*4 + slot)
+    bf16x8 kf[2][NS];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
+      const int kk = (c >> 2) * 8 + t * 4 + (c & 3);
+      const bf16* kp = lpool + (size_t)(kk >> 4 ? p1 : p0) * pl + ((size_t)kvh * PAGE + (kk & 15)) * HD + grp * 8;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sh[rt][t] = sl[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&bf.k[t * 16 + c][s * 32 + grp * 8]));
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            sh[rt][t] = mfma16(a, qb[rt][s], sh[rt][t]);
-            sl[rt][t] = mfma16(a, ql[rt][s], sl[rt][t]);
-          }
-        }
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        // lane (c, grp) holds keys p*32 + grp*8 + 0..7 (p = 0, 1) of row c: element e is key
-        // (e/8)*32 + grp*8 + e%8, from tile 2*(e/8) + (e/4)%2, slot e%4
-        float sv[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kl = (e >> 3) * 32 + grp * 8 + (e & 7);
-          const int t = (e >> 3) * 2 + ((e >> 2) & 1);
-          const float x = (sh[rt][t][e & 3] + sl[rt][t][e & 3]) * scale_log2;
-          bool ok = kl < lim;
-          if (WIN) ok = ok & (qpos[rt] - sm.pos[kt + kl] < window);
-          sv[e] = ok ? x : -INFINITY;
-          tmax = fmaxf(tmax, sv[e]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run[rt], tmax);
-        // rescale the running output only when some row's maximum moved
-        if (__any(m_new > m_run[rt])) {
-          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
-          l_run[rt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
-        }
-        m_run[rt] = m_new;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sv[e] = (sv[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
-          l_run[rt] += sv[e];
-        }
-        // O^T += V^T P^T over the two 32-key halves
-#pragma unroll
-        for (int ps = 0; ps < 2; ++ps) {
-          const bf16x8 pb = pack8(sv + ps * 8);
-          const int kl = ps * 32 + grp * 8;
-#pragma unroll
-          for (int dt = 0; dt < ND; ++dt) {
-            const int d = dt * 16 + c;
-            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                &bf.v[kl >> 4][d][(((kl & 15) >> 3) ^ vswz(d)) * 8]));
-            o[rt][dt] = mfma16(a, pb, o[rt][dt]);
-          }
-        }
-      }
+      for (int s = 0; s < NS; ++s) kf[t][s] = ld8(kp + s * 32);
     }
-    if (st + 1 < nsteps) step_store<HD>(sm.buf[(st + 1) & 1], rg);
-    __syncthreads();
+    // V^T fragments: row d = dt*16 + c, slice keys grp*8 + 0..7 (one 16-byte run of a
+    // [d][16] V page)
+    bf16x8 vf[ND];
+    {
+      const bf16* vp = lpool + (size_t)(grp >> 1 ? p1 : p0) * pl + (size_t)(nkv + kvh) * HD * PAGE + c * PAGE + (grp & 1) * 8;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) vf[dt] = ld8(vp + dt * 16 * PAGE);
+    }
+    int kp8[8];
+    if (WIN) {
+      const int* pp = g.kpos + (size_t)(grp >> 1 ? p1 : p0) * PAGE + (grp & 1) * 8;
+      const i32x4 a = *reinterpret_cast<const i32x4*>(pp), bq = *reinterpret_cast<const i32x4*>(pp + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { kp8[e] = a[e]; kp8[4 + e] = bq[e]; }
+    }
+    // S^T = K Q^T; the hi and lo query terms accumulate in separate chains
+    f32x4 sh[2][2], sl[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sh[rt][t] = sl[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          sh[rt][t] = mfma16(kf[t][s], qb[rt][s], sh[rt][t]);
+          sl[rt][t] = mfma16(kf[t][s], ql[rt][s], sl[rt][t]);
+        }
+    const int lim = nkeys - kt - grp * 8;   // keys e < lim of this lane exist
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (sh[rt][e >> 2][e & 3] + sl[rt][e >> 2][e & 3]) * scale_log2;
+        bool ok = e < lim;
+        if (WIN) ok = ok & (qpos[rt] - kp8[e] < window);
+        sv[e] = ok ? x : -INFINITY;
+        tmax = fmaxf(tmax, sv[e]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run[rt], tmax);
+      // rescale the running output only when some row's maximum moved
+      if (__any(m_new > m_run[rt])) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+        l_run[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
+      }
+      m_run[rt] = m_new;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sv[e] = (sv[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
+        l_run[rt] += sv[e];
+      }
+      // O^T += V^T P^T: P^T comes straight from the lane's own registers
+      const bf16x8 pb = pack8(sv);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[rt][dt] = mfma16(vf[dt], pb, o[rt][dt]);
+    }
   }
 
-  const size_t item = (size_t)cg * nkv + kvh;
+  // merge the four waves' states in wave order
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < 2; ++rt) {
     float lt = l_run[rt];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    const int r = (wave * RT + rt) * 16 + c;
-    if (r < R) {
-      float* po = part_o + (item * RPAD + r) * HD + 4 * grp;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[rt][dt];
-      if (grp == 0) {
-        part_ml[(item * RPAD + r) * 2 + 0] = m_run[rt];
-        part_ml[(item * RPAD + r) * 2 + 1] = lt;
-      }
+    for (int dt = 0; dt < ND; ++dt)
+      *reinterpret_cast<f32x4*>(&sm.o[wave][rt * 16 + c][dt * 16 + 4 * grp]) = o[rt][dt];
+    if (grp == 0) {
+      sm.m[wave][rt * 16 + c] = m_run[rt];
+      sm.l[wave][rt * 16 + c] = lt;
     }
+  }
+  __syncthreads();
+  constexpr int DS = HD / 8;   // dims per thread: 8 threads per row
+  const int row = threadIdx.x >> 3, slc = threadIdx.x & 7;
+  const int r = rg * RG + row;
+  if (r >= R) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) M = fmaxf(M, sm.m[w][row]);
+  float wt[AW], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) {
+    const float mw = sm.m[w][row];
+    wt[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    L += wt[w] * sm.l[w][row];
+  }
+  float* po = part_o + ((size_t)item * RPAD + r) * HD + slc * DS;
+#pragma unroll
+  for (int v = 0; v < DS / 4; ++v) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < AW; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&sm.o[w][row][slc * DS + v * 4]);
+    *reinterpret_cast<f32x4*>(po + v * 4) = acc;
+  }
+  if (slc == 0) {
+    part_ml[((size_t)item * RPAD + r) * 2 + 0] = M;
+    part_ml[((size_t)item * RPAD + r) * 2 + 1] = L;
   }
 }
 
@@ -269,9 +225,12 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st) {
   const int G = nh / g.nkv;
-  if (gamma * G > RPAD) return hipErrorInvalidValue;
-  dim3 grid(total_chunks, g.nkv);
-#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
+  const int R = gamma * G;
+  if (R > RPAD || R < 1 || total_chunks < 1) return hipErrorInvalidValue;
+  const int n_items = total_chunks * g.nkv;
+  const int nrg = (R + RG - 1) / RG;
+  const dim3 grid(((n_items + 7) / 8) * 8 * nrg);
+#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
   const bool win = window > 0;
   switch (g.hd) {
     case 128: if (win) DFL_ATTN(128, true); else DFL_ATTN(128, false); break;
@@ -283,61 +242,92 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_
   return hipGetLastError();
 }
 
-// merge a band's chunks in chunk order: one workgroup per (band, kv head, 16 query rows);
-// thread (row, 8-float slice of the head)
+// Merge a band's chunk partials into the attention output (hi + lo bf16 terms). One
+// workgroup per (band, kv head, 8 query rows); thread (row, 4-float slice, chunk group q)
+// folds chunks q, q + CQ, q + 2CQ, ... with a running maximum, all of its loads issued at
+// once; the CQ groups are then merged in group order. The order depends only on the band's
+// own chunk count.
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml,
-                                                      const Band* __restrict__ bands, int gamma,
-                                                      int nh, int nkv, int sw, int rpad,
-                                                      bf16* __restrict__ out,
-                                                      bf16* __restrict__ out_lo) {
-  constexpr int DC = HD / 8;
+__global__ __launch_bounds__(1024) void k_attn_combine(const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml,
+                                                       const Band* __restrict__ bands, int gamma,
+                                                       int nh, int nkv, int sw,
+                                                       bf16* __restrict__ out,
+                                                       bf16* __restrict__ out_lo) {
+  constexpr int NSL = HD / 4;             // 4-float slices per row
+  constexpr int CQ = 1024 / (8 * NSL);    // chunk groups
+  constexpr int JM = NCH_MAX / CQ;        // chunks per group at most
+  __shared__ f32x4 red_o[CQ][8][NSL];
+  __shared__ float red_m[CQ][8], red_l[CQ][8];
   const int b = blockIdx.x, kvh = blockIdx.y;
-  const int rl = threadIdx.x / DC, dc = threadIdx.x % DC;
-  const int r = blockIdx.z * 16 + rl;
+  const int q = threadIdx.x / (8 * NSL);
+  const int row = (threadIdx.x / NSL) % 8, slc = threadIdx.x % NSL;
+  const int r = blockIdx.z * 8 + row;
   const int G = nh / nkv;
-  if (rl >= 16 || r >= gamma * G) return;
-  const int i = r % gamma, hq = r / gamma;
+  const bool rv = r < gamma * G;
   const int nch = bands[b].nch[sw], base = bands[b].base[sw];
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) {
-    const size_t item = (size_t)(base + c) * nkv + kvh;
-    M = fmaxf(M, part_ml[(item * rpad + r) * 2]);
-  }
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < nch; ++c) {
-    const size_t item = (size_t)(base + c) * nkv + kvh;
-    const float mc = part_ml[(item * rpad + r) * 2];
-    const float lc = part_ml[(item * rpad + r) * 2 + 1];
-    const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (item * rpad + r) * HD + dc * 8);
-    const f32x4 o0 = po[0], o1 = po[1];
-    const float w = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
-    L += w * lc;
-    a0 += w * o0;
-    a1 += w * o1;
-  }
-  const float inv = 1.f / L;
-  const size_t o = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + dc * 8;
+  float mc[JM], lc[JM];
+  f32x4 oc[JM];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    split_bf16(a0[e] * inv, out[o + e], out_lo[o + e]);
-    split_bf16(a1[e] * inv, out[o + 4 + e], out_lo[o + 4 + e]);
+  for (int j = 0; j < JM; ++j) {
+    const int cc = q + j * CQ;
+    if (rv && cc < nch) {
+      const size_t it = ((size_t)(base + cc) * nkv + kvh) * RPAD + r;
+      mc[j] = part_ml[it * 2];
+      lc[j] = part_ml[it * 2 + 1];
+      oc[j] = *reinterpret_cast<const f32x4*>(part_o + it * HD + slc * 4);
+    } else {
+      mc[j] = -INFINITY;
+      lc[j] = 0.f;
+      oc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < JM; ++j) M = fmaxf(M, mc[j]);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll
+  for (int j = 0; j < JM; ++j) {
+    const float w = (mc[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc[j] - M);
+    acc += w * oc[j];
+    L += w * lc[j];
+  }
+  red_o[q][row][slc] = acc;
+  if (slc == 0) {
+    red_m[q][row] = M;
+    red_l[q][row] = L;
+  }
+  __syncthreads();
+  if (q != 0 || !rv) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int g2 = 0; g2 < CQ; ++g2) Mt = fmaxf(Mt, red_m[g2][row]);
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  float Lt = 0.f;
+#pragma unroll
+  for (int g2 = 0; g2 < CQ; ++g2) {
+    const float mg = red_m[g2][row];
+    const float w = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mg - Mt);
+    tot += w * red_o[g2][row][slc];
+    Lt += w * red_l[g2][row];
+  }
+  const float inv = 1.f / Lt;
+  const int i = r % gamma, hq = r / gamma;
+  const size_t o = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + slc * 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_bf16(tot[e] * inv, out[o + e], out_lo[o + e]);
 }
 
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,
                                int n_bands, int gamma, int nh, int nkv, int hd, int sw,
                                bf16* out, bf16* out_lo, hipStream_t st) {
   const int G = nh / nkv;
-  const int rpad = RPAD;
-  dim3 grid(n_bands, nkv, (gamma * G + 15) / 16);
+  dim3 grid(n_bands, nkv, (gamma * G + 7) / 8);
   switch (hd) {
-    case 32: (void)launch(k_attn_combine<32>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
-    case 64: (void)launch(k_attn_combine<64>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
-    case 128: (void)launch(k_attn_combine<128>, grid, 256, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, rpad, out, out_lo); break;
+    case 32: (void)launch(k_attn_combine<32>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
+    case 64: (void)launch(k_attn_combine<64>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
+    case 128: (void)launch(k_attn_combine<128>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -135,19 +135,32 @@ int dalloc(dflash_ctx* c, T** p, size_t elems) {
 }
 
 GemmPlan plan_gemm(int N, int K) {
-  // K splits of 512 (the depth a workgroup stages and a wavefront keeps in flight); the last
-  // split may be 256 deep. Depends on (N, K) only, never on the number of rows.
-  const int klen = K >= 512 ? 512 : K;
+  // K splits of 256: each workgroup streams one 64-column x 256-deep weight tile, so even the
+  // narrow projections launch several hundred workgroups and the whole matrix is in flight at
+  // once. Depends on (N, K) only, never on the number of rows.
+  const int klen = 256;
   return GemmPlan{N, K, klen, (K + klen - 1) / klen};
 }
 
+int chunk_pages(int pages) {
+  // 16 pages (256 keys: two passes of the attention workgroup's four 32-key wave slices) per
+  // chunk, widened in steps of 16 pages so that a band never has more than 32 chunks: a
+  // 4K-key band keeps every workgroup of a layer resident at once, long bands keep the
+  // partial traffic and the merge bounded
+  return 16 * std::max(1, (pages + 511) / 512);
+}
+
 void plan_chunks(int kstart, int kend, int& ck, int& nch) {
-  // 16 pages (256 keys, the most a workgroup stages in LDS) per chunk: the per-chunk partial
-  // output (every query row of a kv head) then stays at half the K/V bytes the chunk reads
   const int pages = (kend - kstart + PAGE - 1) / PAGE;
-  const int ckp = 16;
+  const int ckp = chunk_pages(pages);
   nch = (pages + ckp - 1) / ckp;
   ck = ckp * PAGE;
+}
+
+int max_chunks(int pages_max) {
+  int m = 1;
+  for (int p = 1; p <= pages_max; ++p) m = std::max(m, (p + chunk_pages(p) - 1) / chunk_pages(p));
+  return m;
 }
 
 bool sliding_layer(const dflash_ctx* c, int l) { return c->window > 0 && c->sliding[l]; }
@@ -356,8 +369,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
     part = std::max(part, (size_t)g->S * APPEND_SKINNY * g->N);
   c->part_elems = part;
   c->lm_groups = lmhead_groups(c->V);
-  // split-KV partial slots: every band can have ceil(pages per sequence / 16) chunks
-  const size_t items = (size_t)c->max_batch * ((c->per_seq + 15) / 16) * c->nkv;
+  // split-KV partial slots: chunks per band are bounded by the chunk plan
+  const size_t items = (size_t)c->max_batch * max_chunks(c->per_seq) * c->nkv;
   if ((rc = dalloc(c, &c->pool, (size_t)c->L * c->num_pages * pl)) ||
       (rc = dalloc(c, &c->kpos, (size_t)c->num_pages * PAGE)) ||
       (rc = dalloc(c, &c->bt_dev, (size_t)c->max_batch * c->per_seq)) ||
