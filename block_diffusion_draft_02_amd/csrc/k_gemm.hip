@@ -77,8 +77,10 @@ __device__ __forceinline__ void mfma_chunk(const AChunk<MT, SPLIT>& sa, const bf
 // The workgroup's weight stream over k in [kb, ke) (ke - kb a multiple of 256): each
 // wavefront owns 16 weight rows (lane l reads row wp's n0 + l%16); the rows arrive in KS-deep
 // chunks, double-buffered in registers so the next chunk is in flight while the current one
-// meets its activation chunk in LDS. Every k-step is one MFMA per activation term, in
-// ascending k, starting from zero.
+// meets its activation chunk in LDS. The activation chunk is staged before the next weight
+// chunk is requested: loads complete in issue order, so waiting for the activations then
+// never waits for the prefetch. Every k-step is one MFMA per activation term, in ascending
+// k, starting from zero.
 template <int MT, bool SPLIT>
 __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* __restrict__ wp,
                                             const bf16* __restrict__ A, const bf16* __restrict__ A_lo,
@@ -92,8 +94,8 @@ __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* _
     const int k1 = k + (f0 ? KS : 256);
     const bool has1 = k1 < ke;
     const bool f1 = ke - k1 >= KS;
-    if (has1) load_w(w1, wp, k1, f1);
     stage_a<MT, SPLIT>(sa, A, A_lo, lda, M, k, f0 ? KS : 256);
+    if (has1) load_w(w1, wp, k1, f1);
     __syncthreads();
     mfma_chunk<MT, SPLIT>(sa, w0, f0, c, g, acc);
     __syncthreads();
@@ -101,13 +103,82 @@ __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* _
     const int k2 = k1 + (f1 ? KS : 256);
     const bool has2 = k2 < ke;
     const bool f2 = ke - k2 >= KS;
-    if (has2) load_w(w0, wp, k2, f2);
     stage_a<MT, SPLIT>(sa, A, A_lo, lda, M, k1, f1 ? KS : 256);
+    if (has2) load_w(w0, wp, k2, f2);
     __syncthreads();
     mfma_chunk<MT, SPLIT>(sa, w1, f1, c, g, acc);
     __syncthreads();
     k = k2;
     f0 = f2;
+  }
+}
+
+// One 256-deep split per workgroup (the forward's GEMMs): four wavefronts x 16 weight rows.
+// The activation pieces are requested first (they come from L2), then the eight weight
+// loads per lane; the activations go to LDS while the weights are still in flight. Small
+// LDS and register footprints keep every workgroup of a launch resident at once.
+constexpr int KT = 256;
+
+template <int MT, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
+                                                    const bf16* __restrict__ A_lo, int lda, int M,
+                                                    const bf16* __restrict__ W, int N, int K,
+                                                    float* __restrict__ P, long long part_stride) {
+  __shared__ __attribute__((aligned(16))) bf16 sa[SPLIT ? 2 : 1][MT * 16][KT + APAD];
+  constexpr int PT = MT * 16 * KT / 8 / 256;   // 16-byte activation pieces per thread and term
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * 4 + wave) * 16;
+  const int kb = blockIdx.y * KT;
+  const int c = lane & 15, g = lane >> 4;
+  const int n = n0 + c;
+  const bool nv = n < N;
+  u32x4 ah[PT], al[SPLIT ? PT : 1];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int ch = u * 256 + threadIdx.x;
+    const int r = ch / (KT / 8), cc = (ch % (KT / 8)) * 8;
+    const size_t src = (size_t)(r < M ? r : 0) * lda + kb + cc;   // rows >= M repeat row 0
+    ah[u] = *reinterpret_cast<const u32x4*>(A + src);
+    if (SPLIT) al[SPLIT ? u : 0] = *reinterpret_cast<const u32x4*>(A_lo + src);
+  }
+  // out-of-range columns read a valid row (every wave stays for the barrier); their results
+  // are never stored
+  const bf16* wp = W + (size_t)(nv ? n : min(n0, N - 1)) * K + kb + g * 8;
+  bf16x8 w[KT / 32];
+#pragma unroll
+  for (int u = 0; u < KT / 32; ++u) w[u] = ld8(wp + u * 32);
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int ch = u * 256 + threadIdx.x;
+    const int r = ch / (KT / 8), cc = (ch % (KT / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&sa[0][r][cc]) = ah[u];
+    if (SPLIT) *reinterpret_cast<u32x4*>(&sa[SPLIT ? 1 : 0][r][cc]) = al[SPLIT ? u : 0];
+  }
+  __syncthreads();
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < KT / 32; ++u) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sa[0][mt * 16 + c][u * 32 + g * 8]));
+      acc[mt] = mfma16(a, w[u], acc[mt]);
+      if (SPLIT) {
+        const bf16x8 a2 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sa[SPLIT ? 1 : 0][mt * 16 + c][u * 32 + g * 8]));
+        acc[mt] = mfma16(a2, w[u], acc[mt]);
+      }
+    }
+  }
+  if (!nv) return;
+  float* pp = P + (long long)blockIdx.y * part_stride;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + 4 * g + i;
+      if (m < M) pp[(size_t)m * N + n] = acc[mt][i];
+    }
   }
 }
 
@@ -151,23 +222,26 @@ hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, c
   const int S = (K + k_len - 1) / k_len;
   dim3 grid((N + 63) / 64, S);
   const int mt = (M + 15) / 16;
+  if (mt < 1 || mt > 4) return hipErrorInvalidValue;
+  if (k_len == KT && K % KT == 0) {
+#define DFL_SPLIT(MTV, SP) (void)launch(k_gemm_split<MTV, SP>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride)
+    if (A_lo) {
+      switch (mt) { case 1: DFL_SPLIT(1, true); break; case 2: DFL_SPLIT(2, true); break;
+                    case 3: DFL_SPLIT(3, true); break; default: DFL_SPLIT(4, true); break; }
+    } else {
+      switch (mt) { case 1: DFL_SPLIT(1, false); break; case 2: DFL_SPLIT(2, false); break;
+                    case 3: DFL_SPLIT(3, false); break; default: DFL_SPLIT(4, false); break; }
+    }
+#undef DFL_SPLIT
+    return hipGetLastError();
+  }
 #define DFL_SKINNY(MTV, SP) (void)launch(k_gemm_skinny<MTV, SP>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, k_len, P, part_stride)
   if (A_lo) {
-    switch (mt) {
-      case 1: DFL_SKINNY(1, true); break;
-      case 2: DFL_SKINNY(2, true); break;
-      case 3: DFL_SKINNY(3, true); break;
-      case 4: DFL_SKINNY(4, true); break;
-      default: return hipErrorInvalidValue;
-    }
+    switch (mt) { case 1: DFL_SKINNY(1, true); break; case 2: DFL_SKINNY(2, true); break;
+                  case 3: DFL_SKINNY(3, true); break; default: DFL_SKINNY(4, true); break; }
   } else {
-    switch (mt) {
-      case 1: DFL_SKINNY(1, false); break;
-      case 2: DFL_SKINNY(2, false); break;
-      case 3: DFL_SKINNY(3, false); break;
-      case 4: DFL_SKINNY(4, false); break;
-      default: return hipErrorInvalidValue;
-    }
+    switch (mt) { case 1: DFL_SKINNY(1, false); break; case 2: DFL_SKINNY(2, false); break;
+                  case 3: DFL_SKINNY(3, false); break; default: DFL_SKINNY(4, false); break; }
   }
 #undef DFL_SKINNY
   return hipGetLastError();

@@ -155,37 +155,117 @@ hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, 
 }
 
 // ---- residual add + RMSNorm ---------------------------------------------------------------
-// X[r] += sum_s P[s][r]; Xn[r] = RMSNorm_w(X[r]) as hi + lo bf16; 1024 threads per row
+// The row-wise consumers of split-K partials: 1024 threads per row = RN_G partial groups x
+// RN_T threads; thread t of group q sums splits q, q + RN_G, ... (ascending) for two 4-float
+// slices of the row, with every load of a pass issued before the first add; the groups are
+// then added in group order through LDS. The order depends only on S.
+constexpr int RN_T = 256;
+constexpr int RN_G = 4;
+constexpr int RN_JM = 8;           // splits per group and pass
+constexpr int RN_HMAX = 8192;      // row length the LDS row buffer holds
+
+__device__ __forceinline__ void group_sum2(const float* __restrict__ p, int S, long long ps, int q,
+                                           int j0, int j1, int h, f32x4& a0, f32x4& a1) {
+  a0 = a1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sb = q; sb < S; sb += RN_G * RN_JM) {
+    f32x4 v0[RN_JM], v1[RN_JM];
+#pragma unroll
+    for (int u = 0; u < RN_JM; ++u) {
+      const int sp = sb + u * RN_G;
+      const float* b = p + (long long)sp * ps;
+      v0[u] = (sp < S && j0 < h) ? *reinterpret_cast<const f32x4*>(b + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v1[u] = (sp < S && j1 < h) ? *reinterpret_cast<const f32x4*>(b + j1) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < RN_JM; ++u) {
+      a0 += v0[u];
+      a1 += v1[u];
+    }
+  }
+}
+
+// x (LDS row of h floats, complete) -> out = x * rs * w as hi + lo bf16
+__device__ __forceinline__ void norm_out(const float* xs, int h, float rs, const bf16* __restrict__ w,
+                                         bf16* __restrict__ o, bf16* __restrict__ ol) {
+  for (int j = threadIdx.x * 4; j < h; j += 1024 * 4) {
+    // the norm weight is a caller's pointer with only bf16 alignment guaranteed
+    const float wf[4] = {bf2f(w[j]), bf2f(w[j + 1]), bf2f(w[j + 2]), bf2f(w[j + 3])};
+    bf16 hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(xs[j + e] * rs * wf[e], hi[e], lo[e]);
+    *reinterpret_cast<u32x2*>(o + j) = u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
+    *reinterpret_cast<u32x2*>(ol + j) = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+  }
+}
+
+// Sum of the split partials of row r (plus the residual X when given), kept in the LDS row
+// xs and written back to X; returns the row's sum of squares (valid in every thread).
+__device__ __forceinline__ float rows_gather(float* __restrict__ X, const float* __restrict__ p, int S,
+                                             long long ps, int h, float* xs, f32x4 (*red)[RN_T][2],
+                                             float* red_ss) {
+  const int q = threadIdx.x / RN_T, t = threadIdx.x % RN_T;
+  float ss = 0.f;
+  for (int base = 0; base < h; base += RN_T * 8) {
+    const int j0 = base + t * 4, j1 = base + RN_T * 4 + t * 4;
+    f32x4 x0 = f32x4{0.f, 0.f, 0.f, 0.f}, x1 = x0;
+    if (X != nullptr && q == 0) {
+      if (j0 < h) x0 = *reinterpret_cast<const f32x4*>(X + j0);
+      if (j1 < h) x1 = *reinterpret_cast<const f32x4*>(X + j1);
+    }
+    f32x4 a0, a1;
+    group_sum2(p, S, ps, q, j0, j1, h, a0, a1);
+    red[q][t][0] = a0;
+    red[q][t][1] = a1;
+    __syncthreads();
+    if (q == 0) {
+      f32x4 s0 = red[0][t][0], s1 = red[0][t][1];
+#pragma unroll
+      for (int g2 = 1; g2 < RN_G; ++g2) {
+        s0 += red[g2][t][0];
+        s1 += red[g2][t][1];
+      }
+      s0 += x0;
+      s1 += x1;
+      if (j0 < h) {
+        *reinterpret_cast<f32x4*>(xs + j0) = s0;
+        if (X != nullptr) *reinterpret_cast<f32x4*>(X + j0) = s0;
+        ss += s0[0] * s0[0] + s0[1] * s0[1] + s0[2] * s0[2] + s0[3] * s0[3];
+      }
+      if (j1 < h) {
+        *reinterpret_cast<f32x4*>(xs + j1) = s1;
+        if (X != nullptr) *reinterpret_cast<f32x4*>(X + j1) = s1;
+        ss += s1[0] * s1[0] + s1[1] * s1[1] + s1[2] * s1[2] + s1[3] * s1[3];
+      }
+    }
+    __syncthreads();
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red_ss[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tot += red_ss[i];
+  return tot;
+}
+
+// X[r] += sum_s P[s][r]; Xn[r] = RMSNorm_w(X[r]) as hi + lo bf16; one workgroup per row
 __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ X, const float* __restrict__ P,
                                                      int S, long long ps, int h,
                                                      const bf16* __restrict__ w, float eps,
                                                      bf16* __restrict__ Xn, bf16* __restrict__ Xn_lo) {
-  __shared__ float red[16];
+  __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
+  __shared__ f32x4 red[RN_G][RN_T][2];
+  __shared__ float red_ss[16];
   const int r = blockIdx.x;
-  float* x = X + (size_t)r * h;
-  const float* p = P + (size_t)r * h;
-  float ss = 0.f;
-  for (int j = threadIdx.x; j < h; j += 1024) {
-    const float v = x[j] + sum_parts(p + j, S, ps);
-    x[j] = v;
-    ss += v * v;
-  }
-  ss = wave_sum(ss);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) tot += red[i];
+  const float tot = rows_gather(X + (size_t)r * h, P + (size_t)r * h, S, ps, h, xs, red, red_ss);
   const float rs = rsqrtf(tot / (float)h + eps);
-  bf16* xn = Xn + (size_t)r * h;
-  bf16* xl = Xn_lo + (size_t)r * h;
-  for (int j = threadIdx.x; j < h; j += 1024) split_bf16(x[j] * rs * bf2f(w[j]), xn[j], xl[j]);
+  norm_out(xs, h, rs, w, Xn + (size_t)r * h, Xn_lo + (size_t)r * h);
 }
 
 hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
                              int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
                              hipStream_t st) {
+  if (h > RN_HMAX || h % 4) return hipErrorInvalidValue;
   (void)launch(k_resid_norm, M, 1024, 0, st, X, P, S, part_stride, h, w, eps, Xn, Xn_lo);
   return hipGetLastError();
 }
@@ -233,36 +313,24 @@ hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, i
   return hipGetLastError();
 }
 
-// one workgroup per row; the row (the sum of S split-K partials) is staged in LDS
+// one workgroup per row: the sum of the row's S split-K partials, RMSNorm'd
 __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__ X, int S, long long ps,
                                                        int h, const bf16* __restrict__ w, float eps,
                                                        bf16* __restrict__ out,
                                                        bf16* __restrict__ out_lo) {
-  extern __shared__ float xs[];
-  __shared__ float red[16];
+  __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
+  __shared__ f32x4 red[RN_G][RN_T][2];
+  __shared__ float red_ss[16];
   const int r = blockIdx.x;
-  const float* x = X + (size_t)r * h;
-  float ss = 0.f;
-  for (int j = threadIdx.x; j < h; j += 1024) {
-    const float v = sum_parts(x + j, S, ps);
-    xs[j] = v;
-    ss += v * v;
-  }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) tot += red[i];
+  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, h, xs, red, red_ss);
   const float rs = rsqrtf(tot / (float)h + eps);
-  bf16* o = out + (size_t)r * h;
-  bf16* ol = out_lo + (size_t)r * h;
-  for (int j = threadIdx.x; j < h; j += 1024) split_bf16(xs[j] * rs * bf2f(w[j]), o[j], ol[j]);
+  norm_out(xs, h, rs, w, out + (size_t)r * h, out_lo + (size_t)r * h);
 }
 
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st) {
-  (void)launch(k_rows_rmsnorm, M, 1024, (size_t)h * sizeof(float), st, X, S, part_stride, h, w, eps, out, out_lo);
+  if (h > RN_HMAX || h % 4) return hipErrorInvalidValue;
+  (void)launch(k_rows_rmsnorm, M, 1024, 0, st, X, S, part_stride, h, w, eps, out, out_lo);
   return hipGetLastError();
 }
 

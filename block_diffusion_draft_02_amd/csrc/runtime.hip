@@ -257,6 +257,15 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
         !lw.down_proj)
       return bad("NULL layer weight");
   }
+  // matrices are streamed with 16-byte loads
+  auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!a16(w->fc) || !a16(w->embed_tokens) || !a16(w->lm_head)) return bad("head weight matrices must be 16-byte aligned");
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    if (!a16(lw.q_proj) || !a16(lw.k_proj) || !a16(lw.v_proj) || !a16(lw.o_proj) || !a16(lw.gate_proj) ||
+        !a16(lw.up_proj) || !a16(lw.down_proj))
+      return bad("layer weight matrices must be 16-byte aligned");
+  }
   return DFLASH_OK;
 }
 

@@ -79,7 +79,8 @@ typedef struct {
 } dflash_config;
 
 /* Per-layer weights, device bf16. q/k/v/o/gate/up/down are [out, in]; norms [hidden]
- * or [head_dim] (q_norm, k_norm). */
+ * or [head_dim] (q_norm, k_norm). Matrices (here and fc, embed_tokens, lm_head below)
+ * must be 16-byte aligned: create fails with EINVAL otherwise. */
 typedef struct {
   const void *q_proj, *k_proj, *v_proj, *o_proj, *q_norm, *k_norm;
   const void *input_layernorm, *post_attention_layernorm;

@@ -89,6 +89,21 @@ def test_null_arguments():
     L.dflash_destroy(None)
 
 
+def test_create_rejects_misaligned_matrices():
+    # matrices are streamed with 16-byte loads; the check comes before any GPU call
+    L = B.lib()
+    m = synth.model("tiny-L2-h256")
+    cfg, keep = B.make_config(m, 128, 1)
+    ctx = C.c_void_p()
+    w, lay = _null_weights(m)
+    lay[1].o_proj = 0x1002
+    assert L.dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    w, lay = _null_weights(m)
+    w.lm_head = 0x1008
+    assert L.dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    assert not ctx.value
+
+
 def test_config_struct_layout_matches_header():
     # offsets of the C struct on x86-64 (natural alignment)
     assert B.dflash_config.rope_theta.offset == 48
