@@ -19,6 +19,8 @@ drafters (trained checkpoints) and for hidden states captured from a target mode
 from __future__ import annotations
 
 import copy
+import os
+
 import numpy as np
 
 # --------------------------------------------------------------------------------------
@@ -96,8 +98,9 @@ def workload(name: str) -> dict:
 S_WEIGHTS, S_HIDDEN, S_BONUS, S_CTXLEN, S_PAGES, S_POS = 1, 2, 3, 4, 5, 6
 
 
-def rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, index])))
+def rng(seed: int, stream: int, index: int = 0, block=None) -> np.random.Generator:
+    words = [seed, stream, index] + ([] if block is None else [block])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(words)))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -111,17 +114,38 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _normal_bf16(g: np.random.Generator, shape, mean: float, std: float) -> np.ndarray:
+BLOCK = 1 << 22   # elements per independently seeded block of a normal draw
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
+def _normal_block(out: np.ndarray, seed: int, stream: int, index: int, j: int, mean: float, std: float):
+    s, e = j * BLOCK, min(out.size, (j + 1) * BLOCK)
+    x = rng(seed, stream, index, j).standard_normal(e - s, dtype=np.float32)
+    x *= np.float32(std)
+    if mean != 0.0:
+        x += np.float32(mean)
+    out[s:e] = f32_to_bf16_bits(x)
+
+
+def _normal_bf16(seed: int, stream: int, index: int, shape, mean: float, std: float, wait=True):
+    """N(mean, std) in float32, rounded to bf16 bits; the row-major elements are drawn in
+    blocks of BLOCK, block j from PCG64(SeedSequence([seed, stream, index, j]))."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    chunk = 1 << 24
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        x = g.standard_normal(e - s, dtype=np.float32)
-        x *= np.float32(std)
-        if mean != 0.0:
-            x += np.float32(mean)
-        out[s:e] = f32_to_bf16_bits(x)
+    futs = [_pool().submit(_normal_block, out, seed, stream, index, j, mean, std)
+            for j in range((n + BLOCK - 1) // BLOCK)]
+    if not wait:
+        return out.reshape(shape), futs
+    for f in futs:
+        f.result()
     return out.reshape(shape)
 
 
@@ -154,28 +178,37 @@ def weight_specs(m: dict):
     return specs
 
 
-def gen_weight(m: dict, seed: int, name: str) -> np.ndarray:
+def _weight_args(m: dict, name: str):
     for i, (n, shape, kind) in enumerate(weight_specs(m)):
         if n == name:
-            g = rng(seed, S_WEIGHTS, i)
-            if kind == "mat":
-                return _normal_bf16(g, shape, 0.0, 0.02)
-            return _normal_bf16(g, shape, 1.0, 0.02)
+            return i, shape, (0.0 if kind == "mat" else 1.0)
     raise KeyError(name)
 
 
-def gen_weights(m: dict, seed: int, threads: int = 8) -> dict:
-    """All weights; tensors are independent streams, so they are drawn in parallel."""
-    from concurrent.futures import ThreadPoolExecutor
-    names = [n for n, _, _ in weight_specs(m)]
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        arrs = list(ex.map(lambda n: gen_weight(m, seed, n), names))
-    return dict(zip(names, arrs))
+def gen_weight(m: dict, seed: int, name: str) -> np.ndarray:
+    """Weight `name`: matrices N(0, 0.02), norm weights 1 + N(0, 0.02); tensor i of the
+    fixed order draws from stream S_WEIGHTS, index i."""
+    i, shape, mean = _weight_args(m, name)
+    return _normal_bf16(seed, S_WEIGHTS, i, shape, mean, 0.02)
+
+
+def gen_weights(m: dict, seed: int) -> dict:
+    """All weights, every block of every tensor drawn in parallel."""
+    pending = {}
+    for n, _, _ in weight_specs(m):
+        i, shape, mean = _weight_args(m, n)
+        pending[n] = _normal_bf16(seed, S_WEIGHTS, i, shape, mean, 0.02, wait=False)
+    out = {}
+    for n, (arr, futs) in pending.items():
+        for f in futs:
+            f.result()
+        out[n] = arr
+    return out
 
 
 def gen_hidden(m: dict, seed: int, n_rows: int, index: int = 0) -> np.ndarray:
     """Tapped target hidden states, [n_rows, num_taps * target_hidden] bf16 bits."""
-    return _normal_bf16(rng(seed, S_HIDDEN, index), (n_rows, m["num_taps"] * m["target_hidden"]), 0.0, 1.0)
+    return _normal_bf16(seed, S_HIDDEN, index, (n_rows, m["num_taps"] * m["target_hidden"]), 0.0, 1.0)
 
 
 def gen_bonus(m: dict, seed: int, n: int, index: int = 0) -> np.ndarray:

@@ -101,3 +101,22 @@ def read_i64(gpu, which, n):
     buf = torch.empty(n, dtype=torch.int64)
     gpu.dflash_debug_copy(which, buf)
     return buf.numpy()
+
+
+def read_slot_kv(gpu, layer: int, slots: np.ndarray):
+    """K and V rows stored at the given int64 slots of one layer, each [len(slots), nkv, hd]
+    bf16 bits, read page by page (the pool of a large workload is not copied whole)."""
+    geo = gpu.dflash_pool_geometry()
+    m = gpu.m
+    nkv, hd = m["num_kv_heads"], m["head_dim"]
+    plb = geo["page_layer_bytes"]
+    K = np.empty((len(slots), nkv, hd), dtype=np.uint16)
+    V = np.empty((len(slots), nkv, hd), dtype=np.uint16)
+    buf = torch.empty(plb // 2, dtype=torch.int16)
+    for i, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        page, off = int(s) // 16, int(s) % 16
+        gpu.dflash_debug_copy(B.DFLASH_BUF_POOL, buf, offset=(layer * geo["num_pages"] + page) * plb, nbytes=plb)
+        pg = buf.numpy().view(np.uint16).reshape(2, nkv, -1)
+        K[i] = pg[0].reshape(nkv, 16, hd)[:, off, :]
+        V[i] = pg[1].reshape(nkv, hd, 16)[:, :, off]
+    return K, V
