@@ -31,6 +31,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "drafted γ=16 blocks/sec at batch 1 and 16; achieved HBM GB/s vs peak"
 WORKLOAD = "qwen3-L8-h2048-ctx4096-b1"
 WORKLOAD_B16 = "qwen3-L8-h2048-b16-ctx512to8192"
+WORKLOAD_LONG = "qwen3-L8-h2048-b32-ctx8192to32768-append2048"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def log(*a):
@@ -45,6 +47,39 @@ def gemm_bytes(m, M):
     shapes = [(qd + 2 * kvd, h), (h, qd), (2 * ff, h), (h, ff)]
     per_layer = sum(N * K * 2 + M * K * 2 + M * N * 4 for N, K in shapes)
     return per_layer * m["num_layers"]
+
+
+# HBM bytes per launch of the forward's layer GEMMs (k_gemm_split<1, true>, mean over
+# the QKV, O, gate/up and down shapes), from `rocprofv3 --pmc FETCH_SIZE` and
+# `--pmc WRITE_SIZE` runs of `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-batch16
+# --no-longctx`, scaled by what the same counters read for 20 plain 256 MiB device copies
+# (`bench.py --calibrate-copy 256`: FETCH_SIZE 0.500 of the bytes read, WRITE_SIZE 1.000 of
+# the bytes written). Valid only for the kernel source they were taken on.
+TRAFFIC = {
+    "gemm": dict(source="block_diffusion_draft_02_amd/csrc/k_gemm.hip",
+                 sha256="5d2ec9b5f7efe2b715035a15c9840bbce40a0645e0af9e3c19dcdf6d443d1300",
+                 fetch_bytes=30.18e6, write_bytes=3.545e6),
+}
+
+
+def measured_traffic(kind):
+    import hashlib
+    t = TRAFFIC.get(kind)
+    if t is None:
+        return None
+    try:
+        with open(os.path.join(ROOT, t["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
+                return None
+    except OSError:
+        return None
+    return int(t["fetch_bytes"] + t["write_bytes"])
+
+
+def gemm_weight_elems(m):
+    h, hd, nh, nkv, ff = m["hidden"], m["head_dim"], m["num_q_heads"], m["num_kv_heads"], m["intermediate"]
+    qd, kvd = nh * hd, nkv * hd
+    return ((qd + 2 * kvd) * h + h * qd + 2 * ff * h + h * ff) * m["num_layers"]
 
 
 def lmhead_bytes(m, M):
@@ -129,7 +164,21 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="timed budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch16", action="store_true")
+    ap.add_argument("--no-longctx", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 20 plain device-to-device copies of MIB MiB (the reference for "
+                         "scaling the HBM traffic counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 20}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the path would shard data-parallel over sequences, see DESIGN.md)", file=sys.stderr)
@@ -203,10 +252,11 @@ def main():
     M = gamma
     mean_kv = kv0 + a * (args.steps + 1) / 2
 
-    # the roofline pass: the same number of steps right after, with every launch of the
-    # dominant class bracketed by dispatch-attached HIP events on the launch stream
+    # the roofline pass: the same number of steps right after, every launch bracketed by
+    # dispatch-attached HIP events on the launch stream (bracketing only the dominant class
+    # would slow exactly those launches); the dominant class's average is the roofline's
     kv1 = d.dflash_seq_info(0)[0]
-    d.dflash_timing([dominant])
+    d.dflash_timing(list(B.K_CLASSES))
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for _ in range(args.steps):
@@ -225,7 +275,8 @@ def main():
         per_launch = dom_bytes_step / launches_per_step
         achieved = per_launch / (avg_ms * 1e-3) / 1e9
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel_class=dominant,
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(dominant),
+                        kernel_class=dominant,
                         avg_launch_us=round(avg_ms * 1e3, 3), launches_per_step=launches_per_step,
                         algorithmic_bytes_per_launch=int(per_launch),
                         pass_ms_per_step=round((t3 - t2) / args.steps * 1e3, 4))
@@ -250,6 +301,8 @@ def main():
 
     if not args.no_batch16:
         out["batch16"] = bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev)
+    if not args.no_longctx:
+        out["longctx"] = bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
@@ -297,10 +350,80 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     d.close()
     blocks = nb * steps / el
     log(f"[bench] batch16: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step")
+    gemm_ms = br["gemm"][0] / steps
+    M = nb * gamma
+    gemm_flop = 2 * M * gemm_weight_elems(m)
+    gemm_stats = dict(rows=M, flop_per_step=gemm_flop, ms_per_step=round(gemm_ms, 4),
+                      tflops=round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 1),
+                      mfma_frac=round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                      weight_gbs=round(gemm_weight_elems(m) * 2 / (gemm_ms * 1e-3) / 1e9, 1))
     return dict(workload=WORKLOAD_B16, value=round(blocks, 2), unit="blocks/s", steps=steps,
                 ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
                 ctx_lengths=[int(x) for x in lens], timing="all launch classes bracketed by events",
+                layer_gemms=gemm_stats,
                 kernels_ms_per_step={k: round(v[0] / steps, 4) for k, v in br.items() if v[1]})
+
+
+def bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev):
+    """32 sequences with contexts U{8192..32768} on a pool of permuted pages (prefilled
+    untimed from four reused seeded 2048-row chunks: the shapes, not the draws, set the
+    cost); timed: the 2048-row append of every sequence (MFMA-bound) and the 32-band block
+    forward (attention-bound), with the attention launches bracketed by events."""
+    w = synth.workload(WORKLOAD_LONG)
+    nb, app_rows = w["batch"], w["append"]
+    dev = torch.device("cuda:0")
+    lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, w["seed"])
+    per_seq = -(-(w["max_seq_len"] + gamma + 1) // 16)
+    d = B.Drafter(m, Wd, w["max_seq_len"], nb, page_order=synth.gen_page_order(per_seq * nb, w["seed"]))
+    chunks = [to_dev(synth.gen_hidden(m, w["seed"], 2048, 1000 + i)) for i in range(4)]
+    t = time.perf_counter()
+    for s in range(nb):
+        for c, r0 in enumerate(range(0, int(lens[s]), 2048)):
+            d.dflash_ctx_kv_append(s, chunks[c % 4][:min(2048, int(lens[s]) - r0)])
+    torch.cuda.synchronize()
+    log(f"[bench] longctx: prefilled {int(lens.sum())} rows in {time.perf_counter() - t:.1f}s")
+    tail = to_dev(synth.gen_hidden(m, w["seed"], app_rows, 999))
+    t0 = time.perf_counter()
+    for s in range(nb):
+        d.dflash_ctx_kv_append(s, tail)
+    torch.cuda.synchronize()
+    app_s = time.perf_counter() - t0
+    kvd = m["num_kv_heads"] * m["head_dim"]
+    app_flop = nb * 2 * app_rows * (m["num_taps"] * m["target_hidden"] * m["hidden"]
+                                     + m["hidden"] * m["num_layers"] * 2 * kvd)
+    toks = torch.empty((nb, gamma - 1), dtype=torch.int32, device=dev)
+    bonus = synth.gen_bonus(m, w["seed"], nb)
+    seqs = list(range(nb))
+    d.dflash_block_forward(seqs, bonus, toks, gamma=gamma)
+    torch.cuda.synchronize()
+    reps = 10
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        d.dflash_block_forward(seqs, bonus, toks, gamma=gamma)
+    torch.cuda.synchronize()
+    fwd_s = (time.perf_counter() - t0) / reps
+    d.dflash_timing(["attn"])
+    for _ in range(reps):
+        d.dflash_block_forward(seqs, bonus, toks, gamma=gamma)
+    torch.cuda.synchronize()
+    attn = d.dflash_timing_read()["attn"]
+    d.dflash_timing([])
+    d.close()
+    kv_lens = [int(c) + app_rows for c in lens]
+    kv_bytes = attn_bytes(m, kv_lens, gamma)
+    attn_ms = attn[0] / reps
+    attn_gbs = kv_bytes / (attn_ms * 1e-3) / 1e9
+    log(f"[bench] longctx: append {app_flop / app_s / 1e12:.0f} TFLOP/s, forward {nb / fwd_s:.0f} blocks/s, "
+        f"attention {attn_gbs:.0f} GB/s")
+    return dict(workload=WORKLOAD_LONG, appended_rows_per_seq=app_rows, ctx_lengths=[int(x) for x in lens],
+                append=dict(seconds=round(app_s, 5), flop=app_flop, tflops=round(app_flop / app_s / 1e12, 1),
+                            mfma_frac=round(app_flop / app_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                            timing="wall clock around the 32 appends (one sample: each append advances kv_len)"),
+                forward=dict(ms=round(fwd_s * 1e3, 4), blocks_per_s=round(nb / fwd_s, 2),
+                             tokens_per_s=round(nb * (gamma - 1) / fwd_s, 1)),
+                attention=dict(bound="hbm", kv_bytes_per_forward=int(kv_bytes), ms_per_forward=round(attn_ms, 4),
+                               launches_per_forward=attn[1] / reps, achieved=round(attn_gbs, 1),
+                               peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4)))
 
 
 if __name__ == "__main__":
