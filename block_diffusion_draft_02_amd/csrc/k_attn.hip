@@ -3,13 +3,15 @@
 // sliding layers additionally hide keys with q_pos - k_pos >= window).
 //
 // Work split: the keys of a band are cut into chunks whose length depends only on the band's
-// own length (a multiple of 128 keys), so a band's result does not depend on which other
-// bands share the call. One workgroup per (chunk, kv head, 32 query rows): each of its four
-// wavefronts takes 32-key slices of the chunk (keys 32w, 32w + 128, ...), loads the K and V^T
-// fragments of a slice straight from the pool into MFMA operands, and keeps an online
-// softmax state for its two 16-row query tiles:
-//   S^T = K Q^T   two 16x16x32 MFMA tiles per slice; the key order inside the tiles is
-//                 permuted so that every lane ends up holding 8 consecutive keys of one row
+// own length (a multiple of 256 keys), so a band's result does not depend on which other
+// bands share the call. One workgroup per (chunk, kv head, 32 query rows), with the band
+// table passed by value. The workgroup stages its query rows (hi, lo) and the chunk's page
+// ids in LDS; each of its four wavefronts then takes 32-key slices of the chunk (keys 32w,
+// 32w + 128, ...), loading a slice's K and V^T fragments straight from the pool into MFMA
+// operands, and keeps an online softmax state for its two 16-row query tiles:
+//   S^T = K Q^T   two 16x16x32 MFMA tiles per slice and query tile; the key order inside
+//                 the tiles is permuted so that every lane ends up holding 8 consecutive
+//                 keys of one row
 //   O^T += V^T P^T one MFMA per 16 head dims; P^T comes straight from the lane's own
 //                 registers and V^T is one 16-byte load because V pages are stored [d][16]
 // The four states are merged in wave order through LDS into one (max, sum, unnormalised O)
@@ -25,26 +27,138 @@ constexpr int KP = AW * KW;      // keys of one workgroup pass
 constexpr int RG = 32;           // query rows per workgroup: two 16-row tiles
 constexpr int RPAD = 128;        // query-row slots of one (chunk, kv head) partial
 constexpr int NCH_MAX = 64;      // chunks of one band that k_attn_combine accepts
+constexpr int PG_LDS = 128;      // chunk pages whose ids are staged in LDS (the rest are read from the table)
 
-// the waves' partial states, merged in wave order at the end of a workgroup
+// LDS: the workgroup's query rows (hi, lo) during the key loop, then the four waves'
+// partial states for the merge; plus the chunk's page ids
 template <int HD>
-struct MergeLds {
-  float o[AW][RG][HD + 4];   // rows padded by 16 B: the lanes storing one tile hit distinct banks
-  float m[AW][RG];
-  float l[AW][RG];
+struct AttnLds {
+  union {
+    struct {
+      bf16 h[RG][HD + 8];   // rows padded by 16 B: 8 lanes reading 8 rows hit distinct banks
+      bf16 l[RG][HD + 8];
+    } q;
+    struct {
+      float o[AW][RG][HD + 4];
+      float m[AW][RG];
+      float l[AW][RG];
+    } mg;
+  };
+  int page[PG_LDS];
+};
+
+// one wave's 32-key slice in registers: K fragments of the two S^T tiles, V^T fragments,
+// and (sliding layers) the stamped positions of the lane's 8 keys
+template <int HD, bool WIN>
+struct Slice {
+  bf16x8 kf[2][HD / 32];
+  bf16x8 vf[HD / 16];
+  int kp[WIN ? 8 : 1];
 };
 
 template <int HD, bool WIN>
-__global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn(const bf16* __restrict__ Q,
-                                                        const bf16* __restrict__ Q_lo,
-                                                        const Band* __restrict__ bands, int n_bands,
-                                                        int n_items, int nrg, int gamma, int nh,
-                                                        KvGeom g, int layer, int sw, int window,
-                                                        float scale_log2, float* __restrict__ part_o,
-                                                        float* __restrict__ part_ml) {
-  constexpr int NS = HD / 32;
+__device__ __forceinline__ void load_slice(Slice<HD, WIN>& sl, const AttnLds<HD>& sm, const int* __restrict__ bt,
+                                           const bf16* __restrict__ lpool, const int* __restrict__ kpos,
+                                           size_t pl, int kvh, int nkv, int npg, int kt, int c, int grp) {
+  constexpr int NS = HD / 32, ND = HD / 16;
+  // the slice's 32 keys lie on chunk pages kt/16 and kt/16 + 1 (the zeroed sentinel page 0
+  // past the chunk, so every operand is finite and masked keys add exactly zero)
+  const int lp = kt >> 4;
+  const int p0 = lp < PG_LDS ? sm.page[lp] : bt[lp];
+  const int p1 = lp + 1 < npg ? (lp + 1 < PG_LDS ? sm.page[lp + 1] : bt[lp + 1]) : 0;
+  // K fragments: S^T tile t, row c covers slice key (c/4)*8 + t*4 + c%4, so lane (c, grp)
+  // of the result holds slice keys grp*8 + 0..7 of query row c (e = t*4 + slot)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int kk = (c >> 2) * 8 + t * 4 + (c & 3);
+    const bf16* kp = lpool + (size_t)(kk >> 4 ? p1 : p0) * pl + ((size_t)kvh * PAGE + (kk & 15)) * HD + grp * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sl.kf[t][s] = ld8(kp + s * 32);
+  }
+  // V^T fragments: row d = dt*16 + c, slice keys grp*8 + 0..7 (one 16-byte run of a [d][16]
+  // V page)
+  const int pv = grp >> 1 ? p1 : p0;
+  const bf16* vp = lpool + (size_t)pv * pl + (size_t)(nkv + kvh) * HD * PAGE + c * PAGE + (grp & 1) * 8;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) sl.vf[dt] = ld8(vp + dt * 16 * PAGE);
+  if (WIN) {
+    const int* pp = kpos + (size_t)pv * PAGE + (grp & 1) * 8;
+    const i32x4 a = *reinterpret_cast<const i32x4*>(pp), b = *reinterpret_cast<const i32x4*>(pp + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { sl.kp[e] = a[e]; sl.kp[(4 + e) & (WIN ? 7 : 0)] = b[e]; }
+  }
+}
+
+template <int HD, bool WIN>
+__device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const AttnLds<HD>& sm, int lim,
+                                              const int (&qpos)[2], int window, float scale_log2,
+                                              float (&m_run)[2], float (&l_run)[2], f32x4 (&o)[2][HD / 16],
+                                              int c, int grp) {
+  constexpr int NS = HD / 32, ND = HD / 16;
+  // S^T = K Q^T: four independent accumulator chains (query tile x key tile), each taking
+  // the hi then the lo query term at every k-step
+  f32x4 sh[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sh[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const bf16x8 qh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.q.h[rt * 16 + c][s * 32 + grp * 8]));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(sl.kf[t][s], qh, sh[rt][t]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const bf16x8 ql = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.q.l[rt * 16 + c][s * 32 + grp * 8]));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(sl.kf[t][s], ql, sh[rt][t]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float sv[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = sh[rt][e >> 2][e & 3] * scale_log2;
+      bool ok = e < lim;
+      if (WIN) ok = ok & (qpos[rt] - sl.kp[e & (WIN ? 7 : 0)] < window);
+      sv[e] = ok ? x : -INFINITY;
+      tmax = fmaxf(tmax, sv[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run[rt], tmax);
+    // rescale the running output only when some row's maximum moved
+    if (__any(m_new > m_run[rt])) {
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+      l_run[rt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
+    }
+    m_run[rt] = m_new;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = (sv[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
+      l_run[rt] += sv[e];
+    }
+    // O^T += V^T P^T: P^T comes straight from the lane's own registers
+    const bf16x8 pb = pack8(sv);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[rt][dt] = mfma16(sl.vf[dt], pb, o[rt][dt]);
+  }
+}
+
+template <int HD, bool WIN>
+__global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn(
+    const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo, const AttnBands ab, int n_items, int nrg,
+    int gamma, int nh, KvGeom g, int layer, int sw, int window, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int ND = HD / 16;
-  __shared__ __attribute__((aligned(16))) MergeLds<HD> sm;
+  __shared__ __attribute__((aligned(16))) AttnLds<HD> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, grp = lane >> 4;
@@ -60,11 +174,11 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int cg = item / nkv, kvh = item - cg * nkv;
   const int G = nh / nkv;
   int b = 0;
-  while (b + 1 < n_bands && cg >= bands[b + 1].base[sw]) ++b;
-  const int seq = bands[b].seq, C = bands[b].kv_len, qpos0 = bands[b].q_pos;
-  const int ch = cg - bands[b].base[sw];
-  const int k0 = bands[b].kstart[sw] + ch * bands[b].ck[sw];   // page aligned
-  const int k1 = min(k0 + bands[b].ck[sw], C + gamma);
+  while (b + 1 < ab.n && cg >= ab.b[b + 1].base[sw]) ++b;
+  const int seq = ab.b[b].seq, C = ab.b[b].kv_len, qpos0 = ab.b[b].q_pos;
+  const int ch = cg - ab.b[b].base[sw];
+  const int k0 = ab.b[b].kstart[sw] + ch * ab.b[b].ck[sw];   // page aligned
+  const int k1 = min(k0 + ab.b[b].ck[sw], C + gamma);
   const int nkeys = k1 - k0;
   const int npg = (nkeys + PAGE - 1) / PAGE;
   const int R = gamma * G;
@@ -72,113 +186,43 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
   const int* bt = g.bt + (size_t)seq * g.per_seq + (k0 >> 4);
 
-  // this workgroup's query rows: tile rt holds rows r = rg*32 + rt*16 + c, i.e. block row
-  // r % gamma of query head r / gamma (of this kv head's group)
-  bf16x8 qb[2][NS], ql[2][NS];
+  // the chunk's page ids and this workgroup's query rows (row r = rg*32 + rr is block row
+  // r % gamma of query head r / gamma of this kv head's group; rows past R are zero)
+  for (int i = threadIdx.x; i < min(npg, PG_LDS); i += AW * 64) sm.page[i] = bt[i];
+  for (int pc = threadIdx.x; pc < RG * HD / 8; pc += AW * 64) {
+    const int rr = pc / (HD / 8), d8 = (pc % (HD / 8)) * 8;
+    const int r = rg * RG + rr;
+    u32x4 vh = u32x4{0u, 0u, 0u, 0u}, vl = vh;
+    if (r < R) {
+      const size_t qo = ((size_t)(b * gamma + r % gamma) * nh + kvh * G + r / gamma) * HD + d8;
+      vh = *reinterpret_cast<const u32x4*>(Q + qo);
+      vl = *reinterpret_cast<const u32x4*>(Q_lo + qo);
+    }
+    *reinterpret_cast<u32x4*>(&sm.q.h[rr][d8]) = vh;
+    *reinterpret_cast<u32x4*>(&sm.q.l[rr][d8]) = vl;
+  }
   int qpos[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = rg * RG + rt * 16 + c;
-    const bool rv = r < R;
-    const int i = rv ? r % gamma : 0, hq = rv ? r / gamma : 0;
-    const size_t qo = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + grp * 8;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qb[rt][s] = ld8(Q + qo + s * 32);
-      ql[rt][s] = ld8(Q_lo + qo + s * 32);
-    }
-    qpos[rt] = qpos0 + i;
-  }
+  for (int rt = 0; rt < 2; ++rt) qpos[rt] = qpos0 + ((rg * RG + rt * 16 + c) % gamma);
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   f32x4 o[2][ND];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
 
+  // this wave's slices: keys kt = 32w, 32w + 128, ... (two waves per SIMD, and a second
+  // workgroup per CU, cover the load latency; a register double buffer of the next slice
+  // does not fit next to the 64-register output at head_dim 128)
   for (int kt = wave * KW; kt < nkeys; kt += KP) {
-    // the slice's 32 keys lie on chunk pages kt/16 and kt/16 + 1 (the zeroed sentinel page 0
-    // past the chunk, so every operand is finite and masked keys add exactly zero)
-    const int lp = kt >> 4;
-    const int p0 = bt[lp];
-    const int p1 = lp + 1 < npg ? bt[lp + 1] : 0;
-    // K fragments: S^T tile t, row c covers slice key (c/4)*8 + t*4 + c%4, so lane (c, grp)
-    // of the result holds slice keys grp*8 + 0..7 of query row c (e = t*4 + slot)
-    bf16x8 kf[2][NS];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int kk = (c >> 2) * 8 + t * 4 + (c & 3);
-      const bf16* kp = lpool + (size_t)(kk >> 4 ? p1 : p0) * pl + ((size_t)kvh * PAGE + (kk & 15)) * HD + grp * 8;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) kf[t][s] = ld8(kp + s * 32);
-    }
-    // V^T fragments: row d = dt*16 + c, slice keys grp*8 + 0..7 (one 16-byte run of a
-    // [d][16] V page)
-    bf16x8 vf[ND];
-    {
-      const bf16* vp = lpool + (size_t)(grp >> 1 ? p1 : p0) * pl + (size_t)(nkv + kvh) * HD * PAGE + c * PAGE + (grp & 1) * 8;
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) vf[dt] = ld8(vp + dt * 16 * PAGE);
-    }
-    int kp8[8];
-    if (WIN) {
-      const int* pp = g.kpos + (size_t)(grp >> 1 ? p1 : p0) * PAGE + (grp & 1) * 8;
-      const i32x4 a = *reinterpret_cast<const i32x4*>(pp), bq = *reinterpret_cast<const i32x4*>(pp + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { kp8[e] = a[e]; kp8[4 + e] = bq[e]; }
-    }
-    // S^T = K Q^T; the hi and lo query terms accumulate in separate chains
-    f32x4 sh[2][2], sl[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sh[rt][t] = sl[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          sh[rt][t] = mfma16(kf[t][s], qb[rt][s], sh[rt][t]);
-          sl[rt][t] = mfma16(kf[t][s], ql[rt][s], sl[rt][t]);
-        }
-    const int lim = nkeys - kt - grp * 8;   // keys e < lim of this lane exist
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float sv[8];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (sh[rt][e >> 2][e & 3] + sl[rt][e >> 2][e & 3]) * scale_log2;
-        bool ok = e < lim;
-        if (WIN) ok = ok & (qpos[rt] - kp8[e] < window);
-        sv[e] = ok ? x : -INFINITY;
-        tmax = fmaxf(tmax, sv[e]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[rt], tmax);
-      // rescale the running output only when some row's maximum moved
-      if (__any(m_new > m_run[rt])) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
-        l_run[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
-      }
-      m_run[rt] = m_new;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = (sv[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
-        l_run[rt] += sv[e];
-      }
-      // O^T += V^T P^T: P^T comes straight from the lane's own registers
-      const bf16x8 pb = pack8(sv);
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) o[rt][dt] = mfma16(vf[dt], pb, o[rt][dt]);
-    }
+    Slice<HD, WIN> sl;
+    load_slice<HD, WIN>(sl, sm, bt, lpool, g.kpos, pl, kvh, nkv, npg, kt, c, grp);
+    compute_slice<HD, WIN>(sl, sm, nkeys - kt - grp * 8, qpos, window, scale_log2, m_run, l_run, o, c, grp);
   }
 
-  // merge the four waves' states in wave order
+  // merge the four waves' states in wave order (the LDS now holds the merge area)
+  __syncthreads();
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     float lt = l_run[rt];
@@ -186,10 +230,10 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     lt += __shfl_xor(lt, 32, 64);
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
-      *reinterpret_cast<f32x4*>(&sm.o[wave][rt * 16 + c][dt * 16 + 4 * grp]) = o[rt][dt];
+      *reinterpret_cast<f32x4*>(&sm.mg.o[wave][rt * 16 + c][dt * 16 + 4 * grp]) = o[rt][dt];
     if (grp == 0) {
-      sm.m[wave][rt * 16 + c] = m_run[rt];
-      sm.l[wave][rt * 16 + c] = lt;
+      sm.mg.m[wave][rt * 16 + c] = m_run[rt];
+      sm.mg.l[wave][rt * 16 + c] = lt;
     }
   }
   __syncthreads();
@@ -199,20 +243,20 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (r >= R) return;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < AW; ++w) M = fmaxf(M, sm.m[w][row]);
+  for (int w = 0; w < AW; ++w) M = fmaxf(M, sm.mg.m[w][row]);
   float wt[AW], L = 0.f;
 #pragma unroll
   for (int w = 0; w < AW; ++w) {
-    const float mw = sm.m[w][row];
+    const float mw = sm.mg.m[w][row];
     wt[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    L += wt[w] * sm.l[w][row];
+    L += wt[w] * sm.mg.l[w][row];
   }
   float* po = part_o + ((size_t)item * RPAD + r) * HD + slc * DS;
 #pragma unroll
   for (int v = 0; v < DS / 4; ++v) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < AW; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&sm.o[w][row][slc * DS + v * 4]);
+    for (int w = 0; w < AW; ++w) acc += wt[w] * *reinterpret_cast<const f32x4*>(&sm.mg.o[w][row][slc * DS + v * 4]);
     *reinterpret_cast<f32x4*>(po + v * 4) = acc;
   }
   if (slc == 0) {
@@ -221,16 +265,16 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_dev, int n_bands, int total_chunks,
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int total_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st) {
   const int G = nh / g.nkv;
   const int R = gamma * G;
-  if (R > RPAD || R < 1 || total_chunks < 1) return hipErrorInvalidValue;
+  if (R > RPAD || R < 1 || total_chunks < 1 || bands.n < 1 || bands.n > MAX_BANDS) return hipErrorInvalidValue;
   const int n_items = total_chunks * g.nkv;
   const int nrg = (R + RG - 1) / RG;
   const dim3 grid(((n_items + 7) / 8) * 8 * nrg);
-#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands_dev, n_bands, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
+#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
   const bool win = window > 0;
   switch (g.hd) {
     case 128: if (win) DFL_ATTN(128, true); else DFL_ATTN(128, false); break;

@@ -41,6 +41,12 @@ struct Band {
   int kstart[2], ck[2], nch[2], base[2];
 };
 
+// the band table of one forward, passed by value to the kernels that need it at their start
+struct AttnBands {
+  int n;
+  Band b[MAX_BANDS];
+};
+
 struct FwdArgs {
   int n_bands, gamma, mask_token, per_seq;
   int n_upd;                   // block-table entries to write: bt[upd_off] = upd_page
@@ -107,7 +113,7 @@ hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, 
 
 // ---- attention (k_attn.hip) ----------------------------------------------------------
 // total_chunks = sum over bands of nch[sw]; partial buffers sized [total_chunks*nkv][128][hd]
-hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const Band* bands_dev, int n_bands, int total_chunks,
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int total_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st);
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,

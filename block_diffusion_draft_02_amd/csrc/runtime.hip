@@ -679,6 +679,9 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   hipStream_t st = (hipStream_t)stream;
   const KvGeom g = geom(c);
   const int M = n_seqs * gamma;
+  AttnBands ab{};
+  ab.n = n_seqs;
+  for (int b = 0; b < n_seqs; ++b) ab.b[b] = a.bands[b];
   const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
   HIPCHK(c, timed(c, DFLASH_K_PROLOGUE, st, [&] {
     return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed,
@@ -706,7 +709,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
                              (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
-      return launch_block_attn(c->Qb, c->Qb_lo, c->bands_dev, n_seqs, base[sw], gamma, c->nh, g, l, sw,
+      return launch_block_attn(c->Qb, c->Qb_lo, ab, base[sw], gamma, c->nh, g, l, sw,
                                sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN_COMBINE, st, [&] {
