@@ -45,12 +45,49 @@ __device__ __forceinline__ void stage_a(AChunk<MT, SPLIT>& sa, const bf16* __res
   }
 }
 
+// T16 weight layout (the forward's GEMMs and the lm_head): the rows of a [N, K] weight go
+// in tiles of 16; a tile's K is a run of 256-deep blocks, and a block holds its 16 x 256
+// values as 8 x 64 16-byte pieces in exactly the order the 64 lanes of a wavefront load them
+// (piece (u, lane) = row lane%16, k = u*32 + (lane/16)*8 .. +7). A tile is then 16*K
+// contiguous values, and every load instruction of a wavefront reads 1 KB in one run.
+constexpr int T16_BLOCK = 16 * 256;
+
+__global__ __launch_bounds__(256) void k_tile_weight(const bf16* __restrict__ src, int N, int K,
+                                                     int n_pad, bf16* __restrict__ dst) {
+  const size_t p = (size_t)blockIdx.x * 256 + threadIdx.x;   // destination piece
+  if (p >= (size_t)n_pad * K / 8) return;
+  const int lane = (int)(p & 63);
+  const size_t q = p >> 6;
+  const int u = (int)(q & 7);
+  const size_t blk = q >> 3;
+  const int S = K / 256;
+  const int s = (int)(blk % S);
+  const size_t n = (blk / S) * 16 + (lane & 15);
+  const int k = s * 256 + u * 32 + (lane >> 4) * 8;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};   // rows past N (padding to a whole tile) are zero
+  if (n < (size_t)N) v = *reinterpret_cast<const u32x4*>(src + n * K + k);
+  *reinterpret_cast<u32x4*>(dst + p * 8) = v;
+}
+
+hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStream_t st) {
+  if (N < 1 || K < 256 || K % 256) return hipErrorInvalidValue;
+  const int n_pad = (N + 15) / 16 * 16;
+  const size_t pieces = (size_t)n_pad * K / 8;
+  k_tile_weight<<<(unsigned)((pieces + 255) / 256), 256, 0, st>>>(src, N, K, n_pad, dst);
+  return hipGetLastError();
+}
+
+// One KS-deep (or 256-deep, full = false) weight chunk at depth k for the lane: row-major
+// (wp = row + (lane/16)*8) or T16 (wp = tile + lane*8).
+template <bool TILED>
 __device__ __forceinline__ void load_w(bf16x8 (&w)[16], const bf16* __restrict__ wp, int k, bool full) {
+  const bf16* b = TILED ? wp + (size_t)(k >> 8) * T16_BLOCK : wp + k;
+  constexpr int step = TILED ? 512 : 32;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) w[u] = ld8(wp + k + u * 32);
+  for (int u = 0; u < 8; ++u) w[u] = ld8(b + u * step);
   if (full) {
 #pragma unroll
-    for (int u = 8; u < 16; ++u) w[u] = ld8(wp + k + u * 32);
+    for (int u = 8; u < 16; ++u) w[u] = ld8(b + u * step);
   }
 }
 
@@ -81,21 +118,21 @@ __device__ __forceinline__ void mfma_chunk(const AChunk<MT, SPLIT>& sa, const bf
 // chunk is requested: loads complete in issue order, so waiting for the activations then
 // never waits for the prefetch. Every k-step is one MFMA per activation term, in ascending
 // k, starting from zero.
-template <int MT, bool SPLIT>
+template <int MT, bool SPLIT, bool TILED>
 __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* __restrict__ wp,
                                             const bf16* __restrict__ A, const bf16* __restrict__ A_lo,
                                             int lda, int M, int kb, int ke, f32x4 (&acc)[MT]) {
   const int c = (threadIdx.x & 63) & 15, g = (threadIdx.x & 63) >> 4;
   bf16x8 w0[16], w1[16];
   bool f0 = ke - kb >= KS;
-  load_w(w0, wp, kb, f0);
+  load_w<TILED>(w0, wp, kb, f0);
   for (int k = kb; k < ke;) {
     // chunk at k sits in w0 (full = f0); prefetch the next one into w1
     const int k1 = k + (f0 ? KS : 256);
     const bool has1 = k1 < ke;
     const bool f1 = ke - k1 >= KS;
     stage_a<MT, SPLIT>(sa, A, A_lo, lda, M, k, f0 ? KS : 256);
-    if (has1) load_w(w1, wp, k1, f1);
+    if (has1) load_w<TILED>(w1, wp, k1, f1);
     __syncthreads();
     mfma_chunk<MT, SPLIT>(sa, w0, f0, c, g, acc);
     __syncthreads();
@@ -104,7 +141,7 @@ __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* _
     const bool has2 = k2 < ke;
     const bool f2 = ke - k2 >= KS;
     stage_a<MT, SPLIT>(sa, A, A_lo, lda, M, k1, f1 ? KS : 256);
-    if (has2) load_w(w0, wp, k2, f2);
+    if (has2) load_w<TILED>(w0, wp, k2, f2);
     __syncthreads();
     mfma_chunk<MT, SPLIT>(sa, w1, f1, c, g, acc);
     __syncthreads();
@@ -119,7 +156,7 @@ __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* _
 // LDS and register footprints keep every workgroup of a launch resident at once.
 constexpr int KT = 256;
 
-template <int MT, bool SPLIT>
+template <int MT, bool SPLIT, bool TILED>
 __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
                                                     const bf16* __restrict__ A_lo, int lda, int M,
                                                     const bf16* __restrict__ W, int N, int K,
@@ -143,10 +180,11 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
   }
   // out-of-range columns read a valid row (every wave stays for the barrier); their results
   // are never stored
-  const bf16* wp = W + (size_t)(nv ? n : min(n0, N - 1)) * K + kb + g * 8;
+  const bf16* wp = TILED ? W + ((size_t)min(n0, N - 16) / 16 * (K / KT) + blockIdx.y) * T16_BLOCK + lane * 8
+                         : W + (size_t)(nv ? n : min(n0, N - 1)) * K + kb + g * 8;
   bf16x8 w[KT / 32];
 #pragma unroll
-  for (int u = 0; u < KT / 32; ++u) w[u] = ld8(wp + u * 32);
+  for (int u = 0; u < KT / 32; ++u) w[u] = ld8(wp + u * (TILED ? 512 : 32));
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int ch = u * 256 + threadIdx.x;
@@ -203,7 +241,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A,
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_tile<MT, SPLIT>(sa, wp, A, A_lo, lda, M, kb, ke, acc);
+  stream_tile<MT, SPLIT, false>(sa, wp, A, A_lo, lda, M, kb, ke, acc);
   if (!nv) return;
   float* pp = P + (long long)s * part_stride;
 #pragma unroll
@@ -217,21 +255,23 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A,
 }
 
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
-                              int N, int K, int k_len, float* P, long long part_stride,
+                              int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
                               hipStream_t st) {
   const int S = (K + k_len - 1) / k_len;
   dim3 grid((N + 63) / 64, S);
   const int mt = (M + 15) / 16;
   if (mt < 1 || mt > 4) return hipErrorInvalidValue;
+  if (w_tiled && (k_len != KT || K % KT || N % 16)) return hipErrorInvalidValue;
   if (k_len == KT && K % KT == 0) {
-#define DFL_SPLIT(MTV, SP) (void)launch(k_gemm_split<MTV, SP>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride)
+#define DFL_SPLIT(MTV, SP, TL) (void)launch(k_gemm_split<MTV, SP, TL>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride)
+#define DFL_SPLIT_MT(SP, TL) switch (mt) { case 1: DFL_SPLIT(1, SP, TL); break; case 2: DFL_SPLIT(2, SP, TL); break; \
+                                           case 3: DFL_SPLIT(3, SP, TL); break; default: DFL_SPLIT(4, SP, TL); break; }
     if (A_lo) {
-      switch (mt) { case 1: DFL_SPLIT(1, true); break; case 2: DFL_SPLIT(2, true); break;
-                    case 3: DFL_SPLIT(3, true); break; default: DFL_SPLIT(4, true); break; }
+      if (w_tiled) { DFL_SPLIT_MT(true, true) } else { DFL_SPLIT_MT(true, false) }
     } else {
-      switch (mt) { case 1: DFL_SPLIT(1, false); break; case 2: DFL_SPLIT(2, false); break;
-                    case 3: DFL_SPLIT(3, false); break; default: DFL_SPLIT(4, false); break; }
+      if (w_tiled) { DFL_SPLIT_MT(false, true) } else { DFL_SPLIT_MT(false, false) }
     }
+#undef DFL_SPLIT_MT
 #undef DFL_SPLIT
     return hipGetLastError();
   }
@@ -366,12 +406,14 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(const bf16* __restrict__ 
   {
     const int n = n0 + c;
     const bool nv = n < V;
-    // every wave takes part in the workgroup's barriers; columns past V read a valid row
-    const bf16* wp = W + (size_t)(nv ? n : min(n0, V - 1)) * K + g * 8;
+    // W is in the T16 layout with V padded to whole tiles; every wave takes part in the
+    // workgroup's barriers, waves past the last tile re-read the last tile
+    const int n_tiles = (V + 15) / 16;
+    const bf16* wp = W + (size_t)min(n0 / 16, n_tiles - 1) * 16 * K + lane * 8;
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_tile<MT, true>(sa, wp, Y, Y_lo, ldy, M, 0, K, acc);
+    stream_tile<MT, true, true>(sa, wp, Y, Y_lo, ldy, M, 0, K, acc);
     if (nv) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {

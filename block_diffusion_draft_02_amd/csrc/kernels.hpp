@@ -79,14 +79,18 @@ __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (si
 // ---- GEMMs (k_gemm.hip) --------------------------------------------------------------
 // Y[M,N] = A[M,K] W[N,K]^T where the activation A = A_hi + A_lo is carried as two bf16
 // terms (each k-step issues two MFMAs). Skinny form: partials P[s][M][N] over K splits of
-// k_len (k_len, K multiples of 128); M <= 64 per launch.
+// k_len (k_len, K multiples of 256); M <= 64 per launch. W is row-major, or (w_tiled) in the
+// T16 layout, which needs k_len 256 and N a multiple of 16.
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
-                              int N, int K, int k_len, float* P, long long part_stride,
+                              int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
                               hipStream_t st);
+// Copy a row-major [N, K] bf16 weight into the T16 layout (ceil(N/16)*16 rows, the padding
+// rows zero); K a multiple of 256.
+hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStream_t st);
 // Tiled form for large M: C[M,N] fp32 (ldc), K multiple of 64; A_lo may be null (A exact).
 hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                              int N, int K, float* C, int ldc, hipStream_t st);
-// lm_head + argmax partials: for rows r0..r0+M-1 of the forward (M <= 64), best (value,
+// lm_head (W in the T16 layout) + argmax partials: for rows r0..r0+M-1 of the forward (M <= 64), best (value,
 // index) per row over each workgroup's vocabulary range; optionally the fp32 logits of
 // drafted rows (row % gamma != 0) into logits[(r/gamma)*(gamma-1) + r%gamma - 1][V].
 int lmhead_groups(int V);

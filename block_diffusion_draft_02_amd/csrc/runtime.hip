@@ -25,8 +25,9 @@ constexpr int ROW_GROUP = 64;    // rows per skinny-GEMM launch
 constexpr int APPEND_SKINNY = 64; // appends of up to this many rows stream their weights once
 
 struct LayerDev {
-  const bf16 *o_proj, *down_proj, *q_norm, *k_norm, *in_norm, *post_norm;
-  bf16 *w_qkv, *w_gu;  // owned fused copies [q;k;v], [gate;up]
+  const bf16 *q_norm, *k_norm, *in_norm, *post_norm;
+  // owned T16 copies of the forward's weights: fused [q;k;v], fused [gate;up], o, down
+  bf16 *w_qkv, *w_gu, *o_proj, *down_proj;
 };
 
 struct SeqState {
@@ -50,7 +51,8 @@ struct dflash_ctx {
   int per_seq;
   int m_max;
   // weights
-  const bf16 *fc, *hidden_norm, *norm, *embed, *lm_head;
+  const bf16 *fc, *hidden_norm, *norm, *embed;
+  bf16* lm_head = nullptr;   // owned T16 copy, vocab padded to whole tiles
   std::vector<LayerDev> layers;
   bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;...
   bf16* knorm_all = nullptr;   // [L, hd]
@@ -360,7 +362,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->seqs.resize(c->max_batch);
   c->m_max = c->max_batch * c->gmax;
   c->fc = (const bf16*)w->fc; c->hidden_norm = (const bf16*)w->hidden_norm; c->norm = (const bf16*)w->norm;
-  c->embed = (const bf16*)w->embed_tokens; c->lm_head = (const bf16*)w->lm_head;
+  c->embed = (const bf16*)w->embed_tokens;
 
   auto fin = [&](int r) { if (r != DFLASH_OK) { std::string e = c->err; release(c); (void)e; } return r; };
   const size_t hsz = (size_t)c->h;
@@ -407,17 +409,19 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->ring_dev, (size_t)RING * APPEND_ROWS)) ||
       (rc = dalloc(c, &c->w_kv, (size_t)c->L * 2 * c->kvd * hsz)) ||
       (rc = dalloc(c, &c->knorm_all, (size_t)c->L * c->hd)) ||
-      (rc = dalloc(c, &c->inv_freq, (size_t)c->hd / 2)))
+      (rc = dalloc(c, &c->inv_freq, (size_t)c->hd / 2)) ||
+      (rc = dalloc(c, &c->lm_head, (size_t)(c->V + 15) / 16 * 16 * hsz)))
     return fin(rc);
   c->layers.resize(c->L);
   for (int l = 0; l < c->L; ++l) {
     LayerDev& d = c->layers[l];
     const dflash_layer_weights& lw = w->layers[l];
-    d.o_proj = (const bf16*)lw.o_proj; d.down_proj = (const bf16*)lw.down_proj;
     d.q_norm = (const bf16*)lw.q_norm; d.k_norm = (const bf16*)lw.k_norm;
     d.in_norm = (const bf16*)lw.input_layernorm; d.post_norm = (const bf16*)lw.post_attention_layernorm;
     if ((rc = dalloc(c, &d.w_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
-        (rc = dalloc(c, &d.w_gu, (size_t)2 * c->ff * hsz)))
+        (rc = dalloc(c, &d.w_gu, (size_t)2 * c->ff * hsz)) ||
+        (rc = dalloc(c, &d.o_proj, (size_t)hsz * c->qd)) ||
+        (rc = dalloc(c, &d.down_proj, (size_t)hsz * c->ff)))
       return fin(rc);
   }
   if (hipHostMalloc((void**)&c->ring_host, (size_t)RING * APPEND_ROWS * sizeof(int), hipHostMallocDefault) != hipSuccess) {
@@ -431,19 +435,29 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   auto cp = [&](void* dst, const void* src, size_t bytes) {
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
   };
-  const size_t qb = (size_t)c->qd * hsz * 2, kb = (size_t)c->kvd * hsz * 2, fb = (size_t)c->ff * hsz * 2;
+  const size_t kb = (size_t)c->kvd * hsz * 2;
   hipError_t e = hipSuccess;
+  // the forward's weights in the T16 layout: a tiled [A;B] is tiled A followed by tiled B
+  // when A's rows are a whole number of 16-row tiles (q_dim, kv_dim and ff all are)
+  auto tile = [&](const void* src, int N, int K, bf16* dst) {
+    return launch_tile_weight((const bf16*)src, N, K, dst, st);
+  };
   for (int l = 0; l < c->L && e == hipSuccess; ++l) {
     const dflash_layer_weights& lw = w->layers[l];
     LayerDev& d = c->layers[l];
-    char* q = (char*)d.w_qkv;
-    if ((e = cp(q, lw.q_proj, qb)) || (e = cp(q + qb, lw.k_proj, kb)) || (e = cp(q + qb + kb, lw.v_proj, kb)) ||
-        (e = cp(d.w_gu, lw.gate_proj, fb)) || (e = cp((char*)d.w_gu + fb, lw.up_proj, fb)) ||
+    if ((e = tile(lw.q_proj, c->qd, c->h, d.w_qkv)) ||
+        (e = tile(lw.k_proj, c->kvd, c->h, d.w_qkv + (size_t)c->qd * hsz)) ||
+        (e = tile(lw.v_proj, c->kvd, c->h, d.w_qkv + (size_t)(c->qd + c->kvd) * hsz)) ||
+        (e = tile(lw.gate_proj, c->ff, c->h, d.w_gu)) ||
+        (e = tile(lw.up_proj, c->ff, c->h, d.w_gu + (size_t)c->ff * hsz)) ||
+        (e = tile(lw.o_proj, c->h, c->qd, d.o_proj)) ||
+        (e = tile(lw.down_proj, c->h, c->ff, d.down_proj)) ||
         (e = cp((char*)c->w_kv + (size_t)l * 2 * kb, lw.k_proj, kb)) ||
         (e = cp((char*)c->w_kv + (size_t)l * 2 * kb + kb, lw.v_proj, kb)) ||
         (e = cp(c->knorm_all + (size_t)l * c->hd, lw.k_norm, (size_t)c->hd * 2)))
       break;
   }
+  if (e == hipSuccess) e = tile(w->lm_head, c->V, c->h, c->lm_head);
   std::vector<double> f = inv_freq_table(cfg, &c->mscale);
   if (e == hipSuccess) e = hipMemcpyAsync(c->inv_freq, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, (size_t)c->L * c->num_pages * pl * 2, st);
@@ -583,7 +597,7 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
       // few rows: weight-streaming GEMMs with split-K partials, reduced by the consumers
       const long long ps_fc = (long long)nc * c->h, ps_kv = (long long)nc * nkv2;
       HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->g_fc.klen, c->part, ps_fc, st);
+        return launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->g_fc.klen, c->part, ps_fc, false, st);
       }));
       HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
         return launch_rows_rmsnorm(c->part, c->g_fc.S, ps_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
@@ -591,7 +605,7 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
       }));
       HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
         return launch_gemm_skinny(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->g_kvapp.klen, c->part,
-                                  ps_kv, st);
+                                  ps_kv, false, st);
       }));
       HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
         return launch_kv_append_post(c->part, c->g_kvapp.S, ps_kv, nc, c->L, c->knorm_all, c->eps, c->inv_freq,
@@ -693,7 +707,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       const int mg = std::min(ROW_GROUP, M - r0);
       hipError_t e = timed(c, DFLASH_K_GEMM, st, [&] {
         return launch_gemm_skinny(A + (size_t)r0 * lda, A_lo + (size_t)r0 * lda, lda, mg, W, p.N, p.K,
-                                  p.klen, c->part + (size_t)r0 * p.N, ps, st);
+                                  p.klen, c->part + (size_t)r0 * p.N, ps, true, st);
       });
       if (e != hipSuccess) return e;
     }
