@@ -54,7 +54,9 @@ struct dflash_ctx {
   const bf16 *fc, *hidden_norm, *norm, *embed;
   bf16* lm_head = nullptr;   // owned T16 copy, vocab padded to whole tiles
   std::vector<LayerDev> layers;
-  bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;...
+  bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;... (row-major, for the tiled GEMM)
+  bf16* w_kv_t = nullptr;      // the same in the T16 layout (short appends)
+  bf16* fc_t = nullptr;        // fc in the T16 layout (short appends)
   bf16* knorm_all = nullptr;   // [L, hd]
   double* inv_freq = nullptr;  // [hd/2]
   // pool and tables
@@ -408,6 +410,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->KV32, (size_t)APPEND_ROWS * c->L * 2 * c->kvd)) ||
       (rc = dalloc(c, &c->ring_dev, (size_t)RING * APPEND_ROWS)) ||
       (rc = dalloc(c, &c->w_kv, (size_t)c->L * 2 * c->kvd * hsz)) ||
+      (rc = dalloc(c, &c->w_kv_t, (size_t)c->L * 2 * c->kvd * hsz)) ||
+      (rc = dalloc(c, &c->fc_t, (size_t)hsz * c->T * c->Ht)) ||
       (rc = dalloc(c, &c->knorm_all, (size_t)c->L * c->hd)) ||
       (rc = dalloc(c, &c->inv_freq, (size_t)c->hd / 2)) ||
       (rc = dalloc(c, &c->lm_head, (size_t)(c->V + 15) / 16 * 16 * hsz)))
@@ -458,6 +462,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       break;
   }
   if (e == hipSuccess) e = tile(w->lm_head, c->V, c->h, c->lm_head);
+  if (e == hipSuccess) e = tile(w->fc, c->h, c->T * c->Ht, c->fc_t);
+  if (e == hipSuccess) e = tile(c->w_kv, c->L * 2 * c->kvd, c->h, c->w_kv_t);   // after the copies above, same stream
   std::vector<double> f = inv_freq_table(cfg, &c->mscale);
   if (e == hipSuccess) e = hipMemcpyAsync(c->inv_freq, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, (size_t)c->L * c->num_pages * pl * 2, st);
@@ -597,15 +603,15 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
       // few rows: weight-streaming GEMMs with split-K partials, reduced by the consumers
       const long long ps_fc = (long long)nc * c->h, ps_kv = (long long)nc * nkv2;
       HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->g_fc.klen, c->part, ps_fc, false, st);
+        return launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc_t, c->h, ld, c->g_fc.klen, c->part, ps_fc, true, st);
       }));
       HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
         return launch_rows_rmsnorm(c->part, c->g_fc.S, ps_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
                                    c->Fb_lo, st);
       }));
       HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_skinny(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->g_kvapp.klen, c->part,
-                                  ps_kv, false, st);
+        return launch_gemm_skinny(c->Fb, c->Fb_lo, c->h, nc, c->w_kv_t, nkv2, c->h, c->g_kvapp.klen, c->part,
+                                  ps_kv, true, st);
       }));
       HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
         return launch_kv_append_post(c->part, c->g_kvapp.S, ps_kv, nc, c->L, c->knorm_all, c->eps, c->inv_freq,

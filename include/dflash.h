@@ -98,9 +98,10 @@ typedef struct {
 /* Create a drafter: validates the configuration, allocates the KV pool, block tables and
  * scratch, builds the inverse-frequency table (plain or YaRN, in double precision) and
  * copies the weights: the all-layer [K0;V0;K1;V1;...] weight of the context append
- * (spark_model/layers/dflash_head/from_weights.rs, fused K/V weight), and the forward's
- * matrices ([Wq;Wk;Wv] and [Wgate;Wup] fused per layer, Wo, Wdown, lm_head) in a tiled
- * order the weight-streaming GEMMs read in whole runs. The copies are enqueued on `stream`.
+ * (spark_model/layers/dflash_head/from_weights.rs, fused K/V weight), and, in a tiled order
+ * the weight-streaming GEMMs read in whole runs, that weight, fc and the forward's
+ * matrices ([Wq;Wk;Wv] and [Wgate;Wup] fused per layer, Wo, Wdown, lm_head). The copies
+ * are enqueued on `stream`.
  * On success *out owns everything it allocated; on failure *out is NULL. */
 int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *stream,
                   dflash_ctx **out);
