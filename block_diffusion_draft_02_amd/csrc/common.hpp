@@ -38,6 +38,12 @@ __device__ __forceinline__ bf16x8 ld8(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// eight bf16 bit patterns as one 16-byte word (element 0 lowest)
+__device__ __forceinline__ u32x4 pack_bits8(const bf16 (&b)[8]) {
+  return u32x4{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16),
+               (uint32_t)b[4] | ((uint32_t)b[5] << 16), (uint32_t)b[6] | ((uint32_t)b[7] << 16)};
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
   u32x4 u;
   u[0] = pack2(v[0], v[1]);

@@ -16,6 +16,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace dfl {
 
 // Depth of one activation chunk staged in LDS and of one weight chunk a wavefront has in
@@ -156,12 +158,16 @@ __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* _
 // LDS and register footprints keep every workgroup of a launch resident at once.
 constexpr int KT = 256;
 
-template <int MT, bool SPLIT, bool TILED>
+// NORM: the activation (A, A_lo) is x * w of an RMSNorm (NormIn); the result rows are
+// multiplied by the rows' scales 1/sqrt(mean(x^2) + eps).
+template <int MT, bool SPLIT, bool TILED, bool NORM>
 __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
                                                     const bf16* __restrict__ A_lo, int lda, int M,
                                                     const bf16* __restrict__ W, int N, int K,
-                                                    float* __restrict__ P, long long part_stride) {
+                                                    float* __restrict__ P, long long part_stride,
+                                                    NormIn nrm) {
   __shared__ __attribute__((aligned(16))) bf16 sa[SPLIT ? 2 : 1][MT * 16][KT + APAD];
+  __shared__ float srs[NORM ? MT * 16 : 1];
   constexpr int PT = MT * 16 * KT / 8 / 256;   // 16-byte activation pieces per thread and term
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * 4 + wave) * 16;
@@ -169,6 +175,18 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
   const int c = lane & 15, g = lane >> 4;
   const int n = n0 + c;
   const bool nv = n < N;
+  // RMSNorm scales (requested first: the shuffles that combine them need nothing else):
+  // wave w < MT takes rows 16w..16w+15, four lanes a row; lane q of a row adds slices q,
+  // q + 4, ... (the rows are SSQ_STRIDE long with a zero tail, so every load is unconditional),
+  // then the four lanes combine in a fixed order
+  constexpr int SQ_PER_LANE = SSQ_STRIDE / 4;
+  float sqv[NORM ? SQ_PER_LANE : 1];
+  if (NORM) {
+    const int row = wave * 16 + (lane >> 2);
+    const float* q = nrm.ssq + (size_t)(wave < MT && row < M ? row : 0) * SSQ_STRIDE + (lane & 3);
+#pragma unroll
+    for (int t = 0; t < SQ_PER_LANE; ++t) sqv[NORM ? t : 0] = q[4 * t];
+  }
   u32x4 ah[PT], al[SPLIT ? PT : 1];
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
@@ -185,6 +203,15 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
   bf16x8 w[KT / 32];
 #pragma unroll
   for (int u = 0; u < KT / 32; ++u) w[u] = ld8(wp + u * (TILED ? 512 : 32));
+  if (NORM) {
+    // after the weight loads are issued: waiting on the sums does not wait on the weights
+    float ssum = 0.f;
+#pragma unroll
+    for (int t = 0; t < SQ_PER_LANE; ++t) ssum += sqv[NORM ? t : 0];
+    ssum += __shfl_xor(ssum, 1, 64);
+    ssum += __shfl_xor(ssum, 2, 64);
+    if (wave < MT && (lane & 3) == 0) srs[wave * 16 + (lane >> 2)] = rsqrtf(ssum / (float)nrm.h + nrm.eps);
+  }
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int ch = u * 256 + threadIdx.x;
@@ -215,7 +242,7 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + 4 * g + i;
-      if (m < M) pp[(size_t)m * N + n] = acc[mt][i];
+      if (m < M) pp[(size_t)m * N + n] = NORM ? acc[mt][i] * srs[NORM ? m : 0] : acc[mt][i];
     }
   }
 }
@@ -256,25 +283,30 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A,
 
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                               int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
-                              hipStream_t st) {
+                              hipStream_t st, const NormIn* norm) {
   const int S = (K + k_len - 1) / k_len;
   dim3 grid((N + 63) / 64, S);
   const int mt = (M + 15) / 16;
   if (mt < 1 || mt > 4) return hipErrorInvalidValue;
   if (w_tiled && (k_len != KT || K % KT || N % 16)) return hipErrorInvalidValue;
+  const NormIn nn = norm ? *norm : NormIn{};
+  if (norm && (!w_tiled || !A_lo || nn.h != K || K % SSQ_COLS || K > SSQ_STRIDE * SSQ_COLS)) return hipErrorInvalidValue;
   if (k_len == KT && K % KT == 0) {
-#define DFL_SPLIT(MTV, SP, TL) (void)launch(k_gemm_split<MTV, SP, TL>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride)
-#define DFL_SPLIT_MT(SP, TL) switch (mt) { case 1: DFL_SPLIT(1, SP, TL); break; case 2: DFL_SPLIT(2, SP, TL); break; \
-                                           case 3: DFL_SPLIT(3, SP, TL); break; default: DFL_SPLIT(4, SP, TL); break; }
-    if (A_lo) {
-      if (w_tiled) { DFL_SPLIT_MT(true, true) } else { DFL_SPLIT_MT(true, false) }
+#define DFL_SPLIT(MTV, SP, TL, NM) (void)launch(k_gemm_split<MTV, SP, TL, NM>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride, nn)
+#define DFL_SPLIT_MT(SP, TL, NM) switch (mt) { case 1: DFL_SPLIT(1, SP, TL, NM); break; case 2: DFL_SPLIT(2, SP, TL, NM); break; \
+                                               case 3: DFL_SPLIT(3, SP, TL, NM); break; default: DFL_SPLIT(4, SP, TL, NM); break; }
+    if (norm) {
+      DFL_SPLIT_MT(true, true, true)
+    } else if (A_lo) {
+      if (w_tiled) { DFL_SPLIT_MT(true, true, false) } else { DFL_SPLIT_MT(true, false, false) }
     } else {
-      if (w_tiled) { DFL_SPLIT_MT(false, true) } else { DFL_SPLIT_MT(false, false) }
+      if (w_tiled) { DFL_SPLIT_MT(false, true, false) } else { DFL_SPLIT_MT(false, false, false) }
     }
 #undef DFL_SPLIT_MT
 #undef DFL_SPLIT
     return hipGetLastError();
   }
+  if (norm || w_tiled) return hipErrorInvalidValue;
 #define DFL_SKINNY(MTV, SP) (void)launch(k_gemm_skinny<MTV, SP>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, k_len, P, part_stride)
   if (A_lo) {
     switch (mt) { case 1: DFL_SKINNY(1, true); break; case 2: DFL_SKINNY(2, true); break;
@@ -483,6 +515,128 @@ hipError_t launch_lmhead_argmax(const bf16* Y, const bf16* Y_lo, int ldy, int M,
     case 4: (void)launch(k_lmhead_argmax<4>, grid, 256, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i, n_groups, gamma, logits); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// lm_head + argmax for one group of at most 16 rows whose normed rows fit in LDS whole
+// (K <= LMP_KMAX): persistent workgroups of eight wavefronts, one per CU. The rows (hi, lo)
+// are staged once; every wavefront then streams its T16 vocabulary tiles (tiles w, w + W,
+// ... over all waves W of the grid) as one continuous sequence of 512-deep chunks,
+// double-buffered in registers, with no barrier or restaging in the loop, and keeps a
+// running (max, lowest index) per row. The waves merge in LDS and write one partial per
+// (row, workgroup).
+constexpr int LMP_WAVES = 8;
+constexpr int LMP_KMAX = 2048;
+
+int lmhead_persistent_groups(int V, int K, int M, int n_cu) {
+  if (M > 16 || K > LMP_KMAX || K % KS) return 0;
+  const int tiles = (V + 15) / 16;
+  return std::max(1, std::min(n_cu, (tiles + LMP_WAVES - 1) / LMP_WAVES));
+}
+
+__global__ __launch_bounds__(LMP_WAVES * 64) void k_lmhead_persist(const bf16* __restrict__ Y,
+                                                                 const bf16* __restrict__ Y_lo, int ldy,
+                                                                 int M, int r0, const bf16* __restrict__ W,
+                                                                 int V, int K, float* __restrict__ best_v,
+                                                                 int* __restrict__ best_i, int gamma,
+                                                                 float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) bf16 sy[2][16][LMP_KMAX + APAD];
+  __shared__ float sv[LMP_WAVES][16];
+  __shared__ int si[LMP_WAVES][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  // the rows, hi and lo (rows >= M are zero; their results are never used)
+  for (int pc = threadIdx.x; pc < 16 * K / 8; pc += LMP_WAVES * 64) {
+    const int r = pc / (K / 8), k8 = (pc % (K / 8)) * 8;
+    u32x4 h = u32x4{0u, 0u, 0u, 0u}, l = h;
+    if (r < M) {
+      h = *reinterpret_cast<const u32x4*>(Y + (size_t)r * ldy + k8);
+      l = *reinterpret_cast<const u32x4*>(Y_lo + (size_t)r * ldy + k8);
+    }
+    *reinterpret_cast<u32x4*>(&sy[0][r][k8]) = h;
+    *reinterpret_cast<u32x4*>(&sy[1][r][k8]) = l;
+  }
+  __syncthreads();
+  float bv[4];
+  int bi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { bv[e] = -INFINITY; bi[e] = 0x7fffffff; }
+  const int n_tiles = (V + 15) / 16;
+  const int nch = K / KS;
+  const int stride = gridDim.x * LMP_WAVES;
+  const int t0 = blockIdx.x * LMP_WAVES + wave;
+  const int my_tiles = t0 < n_tiles ? (n_tiles - 1 - t0) / stride + 1 : 0;
+  const int items = my_tiles * nch;   // (tile, chunk) pairs this wave streams, in order
+  auto wptr = [&](int q) { return W + (size_t)(t0 + (q / nch) * stride) * 16 * K + lane * 8; };
+  bf16x8 w0[16], w1[16];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](const bf16x8 (&w)[16], int q) {
+    const int j = q % nch;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = j * KS + u * 32 + g * 8;
+      acc = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sy[0][c][k])), w[u], acc);
+      acc = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sy[1][c][k])), w[u], acc);
+    }
+    if (j == nch - 1) {
+      // tile done: lane (c, g) holds rows 4g..4g+3 of column t*16 + c
+      const int n = (t0 + (q / nch) * stride) * 16 + c;
+      if (n < V) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          better(bv[e], bi[e], acc[e], n);
+          const int m = 4 * g + e;
+          if (logits != nullptr && m < M) {
+            const int r = r0 + m, b = r / gamma, i = r % gamma;
+            if (i != 0) logits[(size_t)(b * (gamma - 1) + i - 1) * V + n] = acc[e];
+          }
+        }
+      }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (items > 0) load_w<true>(w0, wptr(0), 0, true);
+  for (int q = 0; q < items; q += 2) {
+    if (q + 1 < items) load_w<true>(w1, wptr(q + 1), ((q + 1) % nch) * KS, true);
+    consume(w0, q);
+    if (q + 1 >= items) break;
+    if (q + 2 < items) load_w<true>(w0, wptr(q + 2), ((q + 2) % nch) * KS, true);
+    consume(w1, q + 1);
+  }
+  // merge across the 16 lanes of a row group, then across the waves
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = bv[e];
+    int i = bi[e];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float ov = __shfl_xor(v, o, 64);
+      const int oi = __shfl_xor(i, o, 64);
+      better(v, i, ov, oi);
+    }
+    if (c == 0) {
+      sv[wave][4 * g + e] = v;
+      si[wave][4 * g + e] = i;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float v = sv[0][threadIdx.x];
+    int i = si[0][threadIdx.x];
+    for (int w = 1; w < LMP_WAVES; ++w) better(v, i, sv[w][threadIdx.x], si[w][threadIdx.x]);
+    if ((int)threadIdx.x < M) {
+      best_v[(size_t)(r0 + threadIdx.x) * gridDim.x + blockIdx.x] = v;
+      best_i[(size_t)(r0 + threadIdx.x) * gridDim.x + blockIdx.x] = i;
+    }
+  }
+}
+
+hipError_t launch_lmhead_persistent(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W,
+                                    int V, int K, float* best_v, int* best_i, int n_groups, int gamma,
+                                    float* logits, hipStream_t st) {
+  if (M < 1 || M > 16 || K > LMP_KMAX || K % KS || n_groups < 1) return hipErrorInvalidValue;
+  (void)launch(k_lmhead_persist, n_groups, LMP_WAVES * 64, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i,
+               gamma, logits);
   return hipGetLastError();
 }
 

@@ -27,17 +27,17 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ p, int S, l
 
 // ---- forward prologue ------------------------------------------------------------------
 // workgroup 0: block-table updates, slots and stamped positions of the block rows, band
-// table; workgroup 1 + r: embedding row of block row r and its input RMSNorm of layer 0.
+// table; workgroup 1 + r: embedding row of block row r into the residual stream, the sums
+// of squares of its 256-column slices (wave w takes slices w, w + 4, ...) and the row times
+// layer 0's input-norm weight as hi + lo bf16.
 __global__ __launch_bounds__(256) void k_fwd_prologue(FwdArgs a, Band* __restrict__ bands_dev,
                                                       int* __restrict__ bt,
                                                       long long* __restrict__ slots,
                                                       int* __restrict__ kpos,
                                                       const bf16* __restrict__ embed,
                                                       const bf16* __restrict__ w_in0, int h,
-                                                      float eps, float* __restrict__ X,
-                                                      bf16* __restrict__ Xn,
-                                                      bf16* __restrict__ Xn_lo) {
-  __shared__ float red[4];
+                                                      float* __restrict__ X, float* __restrict__ ssq,
+                                                      bf16* __restrict__ Xw, bf16* __restrict__ Xw_lo) {
   if (blockIdx.x == 0) {
     for (int j = threadIdx.x; j < a.n_upd; j += 256) bt[a.upd_off[j]] = a.upd_page[j];
     const int M = a.n_bands * a.gamma;
@@ -58,24 +58,29 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(FwdArgs a, Band* __restric
   const int tok = (i == 0) ? a.bands[b].bonus : a.mask_token;
   const bf16* e = embed + (size_t)tok * h;
   float* x = X + (size_t)r * h;
-  float ss = 0.f;
-  for (int j = threadIdx.x; j < h; j += 256) {
-    const float v = bf2f(e[j]);
-    x[j] = v;
-    ss += v * v;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nsl = h / SSQ_COLS;
+  for (int j = wave; j < nsl; j += 4) {
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < SSQ_COLS / 64; ++q) {
+      const int col = j * SSQ_COLS + q * 64 + lane;
+      const float v = bf2f(e[col]);
+      x[col] = v;
+      ss += v * v;
+      split_bf16(v * bf2f(w_in0[col]), Xw[(size_t)r * h + col], Xw_lo[(size_t)r * h + col]);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) ssq[(size_t)r * SSQ_STRIDE + j] = ss;
   }
-  ss = block_sum256(ss, red);
-  const float rs = rsqrtf(ss / (float)h + eps);
-  bf16* xn = Xn + (size_t)r * h;
-  bf16* xl = Xn_lo + (size_t)r * h;
-  for (int j = threadIdx.x; j < h; j += 256) split_bf16(x[j] * rs * bf2f(w_in0[j]), xn[j], xl[j]);
 }
 
 hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
-                               int* kpos, const bf16* embed, const bf16* w_in0, int h,
-                               float eps, float* X, bf16* Xn, bf16* Xn_lo, hipStream_t st) {
+                               int* kpos, const bf16* embed, const bf16* w_in0, int h, float* X,
+                               float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st) {
+  if (h % SSQ_COLS || h > SSQ_STRIDE * SSQ_COLS) return hipErrorInvalidValue;
   const int M = a.n_bands * a.gamma;
-  (void)launch(k_fwd_prologue, 1 + M, 256, 0, st, a, bands_dev, bt, slots, kpos, embed, w_in0, h, eps, X, Xn, Xn_lo);
+  (void)launch(k_fwd_prologue, 1 + M, 256, 0, st, a, bands_dev, bt, slots, kpos, embed, w_in0, h, X, ssq, Xw, Xw_lo);
   return hipGetLastError();
 }
 
@@ -267,6 +272,50 @@ hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_str
                              hipStream_t st) {
   if (h > RN_HMAX || h % 4) return hipErrorInvalidValue;
   (void)launch(k_resid_norm, M, 1024, 0, st, X, P, S, part_stride, h, w, eps, Xn, Xn_lo);
+  return hipGetLastError();
+}
+
+// ---- residual add, parallel form ----------------------------------------------------------
+// One 64-thread workgroup per (row, 256-column slice): X[r] += sum_s P[s][r] with the splits
+// added in order, every load of a pass issued before the first add; then the slice's sum of
+// squares (the next GEMM turns the row's sums into its RMSNorm scale) and X * w as the next
+// GEMM's hi + lo activation.
+constexpr int RS_BATCH = 16;   // splits per load pass
+
+__global__ __launch_bounds__(64) void k_resid_sum(float* __restrict__ X, const float* __restrict__ P,
+                                                  int S, long long ps, int h, const bf16* __restrict__ w,
+                                                  float* __restrict__ ssq, bf16* __restrict__ Xw,
+                                                  bf16* __restrict__ Xw_lo) {
+  const int r = blockIdx.x, j = blockIdx.y;
+  const int col = j * SSQ_COLS + threadIdx.x * 4;
+  const size_t o = (size_t)r * h + col;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(X + o);
+  const u32x2 wb = *reinterpret_cast<const u32x2*>(w + col);   // the context's aligned copy
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += RS_BATCH) {
+    f32x4 v[RS_BATCH];
+#pragma unroll
+    for (int u = 0; u < RS_BATCH; ++u)
+      v[u] = s0 + u < S ? *reinterpret_cast<const f32x4*>(P + (long long)(s0 + u) * ps + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < RS_BATCH; ++u) acc += v[u];
+  }
+  const f32x4 y = x + acc;
+  *reinterpret_cast<f32x4*>(X + o) = y;
+  const float wf[4] = {bf2f((bf16)(wb.x & 0xffff)), bf2f((bf16)(wb.x >> 16)), bf2f((bf16)(wb.y & 0xffff)), bf2f((bf16)(wb.y >> 16))};
+  bf16 hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_bf16(y[e] * wf[e], hi[e], lo[e]);
+  *reinterpret_cast<u32x2*>(Xw + o) = u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
+  *reinterpret_cast<u32x2*>(Xw_lo + o) = u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
+  const float ss = wave_sum(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
+  if (threadIdx.x == 0) ssq[(size_t)r * SSQ_STRIDE + j] = ss;
+}
+
+hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stride, int M, int h,
+                            const bf16* w, float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st) {
+  if (h % SSQ_COLS || h > SSQ_STRIDE * SSQ_COLS) return hipErrorInvalidValue;
+  (void)launch(k_resid_sum, dim3(M, h / SSQ_COLS), 64, 0, st, X, P, S, part_stride, h, w, ssq, Xw, Xw_lo);
   return hipGetLastError();
 }
 

@@ -41,6 +41,19 @@ struct Band {
   int kstart[2], ck[2], nch[2], base[2];
 };
 
+// A GEMM activation under an RMSNorm whose per-row scale is applied to the result: the
+// activation operand (A, A_lo) holds x * w, and row r of the result is multiplied by
+// rs[r] = 1/sqrt(sum_j ssq[r][j] / h + eps), where ssq[r][j] is the sum of squares of
+// columns [256j, 256j + 256) of the residual row x (written by the producer with x * w).
+// ssq rows are SSQ_STRIDE floats; entries past h/256 stay zero (h <= 8192).
+constexpr int SSQ_COLS = 256;
+constexpr int SSQ_STRIDE = 32;
+struct NormIn {
+  const float* ssq;
+  float eps;
+  int h;
+};
+
 // the band table of one forward, passed by value to the kernels that need it at their start
 struct AttnBands {
   int n;
@@ -83,7 +96,7 @@ __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (si
 // T16 layout, which needs k_len 256 and N a multiple of 16.
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                               int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
-                              hipStream_t st);
+                              hipStream_t st, const NormIn* norm = nullptr);
 // Copy a row-major [N, K] bf16 weight into the T16 layout (ceil(N/16)*16 rows, the padding
 // rows zero); K a multiple of 256.
 hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStream_t st);
@@ -94,6 +107,12 @@ hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, co
 // index) per row over each workgroup's vocabulary range; optionally the fp32 logits of
 // drafted rows (row % gamma != 0) into logits[(r/gamma)*(gamma-1) + r%gamma - 1][V].
 int lmhead_groups(int V);
+// The persistent lm_head (<= 16 rows, K <= 2048, W in the T16 layout): its number of
+// workgroups = argmax partials per row (0 when the shape does not qualify).
+int lmhead_persistent_groups(int V, int K, int M, int n_cu);
+hipError_t launch_lmhead_persistent(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W,
+                                    int V, int K, float* best_v, int* best_i, int n_groups, int gamma,
+                                    float* logits, hipStream_t st);
 hipError_t launch_lmhead_argmax(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W, int V,
                                 int K, float* best_v, int* best_i, int n_groups, int gamma,
                                 float* logits, hipStream_t st);
@@ -101,9 +120,11 @@ hipError_t launch_argmax_reduce(const float* best_v, const int* best_i, int n_gr
                                 int n_bands, int gamma, int* tokens, hipStream_t st);
 
 // ---- forward elementwise (k_misc.hip) ------------------------------------------------
+// block tables, slots, band table; X = the block rows' embeddings, their slice sums of
+// squares ssq [rows][h/256], and X * w_in0 as hi + lo bf16 (Xw, Xw_lo)
 hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
-                               int* kpos, const bf16* embed, const bf16* w_in0, int h,
-                               float eps, float* X, bf16* Xn, bf16* Xn_lo, hipStream_t st);
+                               int* kpos, const bf16* embed, const bf16* w_in0, int h, float* X,
+                               float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st);
 hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
                            const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
                            const bf16* k_norm, float eps, const double* inv_freq, float mscale,
@@ -112,6 +133,10 @@ hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, 
 hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
                              int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
                              hipStream_t st);
+// X[r] += sum_s P[s][r] (splits in order); the slice sums of squares of the new rows and
+// X * w as hi + lo bf16 (w: the norm weight of the GEMM that consumes them)
+hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stride, int M, int h,
+                            const bf16* w, float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st);
 hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
                            bf16* A, bf16* A_lo, hipStream_t st);
 

@@ -25,7 +25,8 @@ constexpr int ROW_GROUP = 64;    // rows per skinny-GEMM launch
 constexpr int APPEND_SKINNY = 64; // appends of up to this many rows stream their weights once
 
 struct LayerDev {
-  const bf16 *q_norm, *k_norm, *in_norm, *post_norm;
+  const bf16 *q_norm, *k_norm;
+  bf16 *in_norm, *post_norm;   // owned copies (16-byte aligned: the GEMM staging reads them whole)
   // owned T16 copies of the forward's weights: fused [q;k;v], fused [gate;up], o, down
   bf16 *w_qkv, *w_gu, *o_proj, *down_proj;
 };
@@ -67,7 +68,8 @@ struct dflash_ctx {
   int* rowpos = nullptr;
   Band* bands_dev = nullptr;
   // forward scratch
-  float* X = nullptr;                      // residual stream, fp32
+  float* X = nullptr;          // residual stream, fp32
+  float* ssq = nullptr;        // [rows][SSQ_STRIDE] slice sums of squares of X (zero tail)
   bf16 *Xn = nullptr, *Xn_lo = nullptr;    // activations as hi + lo bf16 terms
   bf16 *Qb = nullptr, *Qb_lo = nullptr;
   bf16 *attn = nullptr, *attn_lo = nullptr;
@@ -79,6 +81,7 @@ struct dflash_ctx {
   float* best_v = nullptr;
   int* best_i = nullptr;
   int lm_groups = 0;
+  int n_cu = 1;               // compute units of the device the context was created on
   GemmPlan g_qkv, g_o, g_gu, g_down, g_fc, g_kvapp;
   // append scratch
   float* F32 = nullptr;
@@ -238,6 +241,7 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
     return bad("num_q_heads must be a multiple of num_kv_heads");
   if (cfg->num_q_heads / cfg->num_kv_heads > 8) return bad("at most 8 query heads per kv head");
   if (cfg->gamma_max < 2 || cfg->gamma_max > 16) return bad("gamma_max must be in [2, 16]");
+  if (cfg->hidden > 8192) return bad("hidden must be at most 8192");
   if (cfg->hidden % 256 || cfg->intermediate % 256 || (cfg->num_q_heads * cfg->head_dim) % 256 ||
       (cfg->num_taps * cfg->target_hidden) % 256)
     return bad("hidden, intermediate, q_dim and num_taps*target_hidden must be multiples of 256");
@@ -382,6 +386,11 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
     part = std::max(part, (size_t)g->S * APPEND_SKINNY * g->N);
   c->part_elems = part;
   c->lm_groups = lmhead_groups(c->V);
+  {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+      c->n_cu = ncu;
+  }
   // split-KV partial slots: chunks per band are bounded by the chunk plan
   const size_t items = (size_t)c->max_batch * max_chunks(c->per_seq) * c->nkv;
   if ((rc = dalloc(c, &c->pool, (size_t)c->L * c->num_pages * pl)) ||
@@ -391,6 +400,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->rowpos, (size_t)APPEND_ROWS)) ||
       (rc = dalloc(c, &c->bands_dev, (size_t)MAX_BANDS)) ||
       (rc = dalloc(c, &c->X, (size_t)c->m_max * hsz)) ||
+      (rc = dalloc(c, &c->ssq, (size_t)c->m_max * SSQ_STRIDE)) ||
       (rc = dalloc(c, &c->Xn, (size_t)c->m_max * hsz)) ||
       (rc = dalloc(c, &c->Xn_lo, (size_t)c->m_max * hsz)) ||
       (rc = dalloc(c, &c->Qb, (size_t)c->m_max * c->qd)) ||
@@ -421,8 +431,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
     LayerDev& d = c->layers[l];
     const dflash_layer_weights& lw = w->layers[l];
     d.q_norm = (const bf16*)lw.q_norm; d.k_norm = (const bf16*)lw.k_norm;
-    d.in_norm = (const bf16*)lw.input_layernorm; d.post_norm = (const bf16*)lw.post_attention_layernorm;
-    if ((rc = dalloc(c, &d.w_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
+    if ((rc = dalloc(c, &d.in_norm, hsz)) || (rc = dalloc(c, &d.post_norm, hsz)) ||
+        (rc = dalloc(c, &d.w_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
         (rc = dalloc(c, &d.w_gu, (size_t)2 * c->ff * hsz)) ||
         (rc = dalloc(c, &d.o_proj, (size_t)hsz * c->qd)) ||
         (rc = dalloc(c, &d.down_proj, (size_t)hsz * c->ff)))
@@ -456,6 +466,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
         (e = tile(lw.up_proj, c->ff, c->h, d.w_gu + (size_t)c->ff * hsz)) ||
         (e = tile(lw.o_proj, c->h, c->qd, d.o_proj)) ||
         (e = tile(lw.down_proj, c->h, c->ff, d.down_proj)) ||
+        (e = cp(d.in_norm, lw.input_layernorm, hsz * 2)) ||
+        (e = cp(d.post_norm, lw.post_attention_layernorm, hsz * 2)) ||
         (e = cp((char*)c->w_kv + (size_t)l * 2 * kb, lw.k_proj, kb)) ||
         (e = cp((char*)c->w_kv + (size_t)l * 2 * kb + kb, lw.v_proj, kb)) ||
         (e = cp(c->knorm_all + (size_t)l * c->hd, lw.k_norm, (size_t)c->hd * 2)))
@@ -468,6 +480,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   if (e == hipSuccess) e = hipMemcpyAsync(c->inv_freq, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipMemsetAsync(c->pool, 0, (size_t)c->L * c->num_pages * pl * 2, st);
   if (e == hipSuccess) e = hipMemsetAsync(c->kpos, 0, (size_t)c->num_pages * PAGE * 4, st);
+  if (e == hipSuccess) e = hipMemsetAsync(c->ssq, 0, (size_t)c->m_max * SSQ_STRIDE * 4, st);
   if (e == hipSuccess) e = hipMemsetAsync(c->bt_dev, 0, (size_t)c->max_batch * c->per_seq * 4, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fin(fail(c, DFLASH_EHIP, "create: %s", hipGetErrorString(e)));
@@ -704,16 +717,20 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   for (int b = 0; b < n_seqs; ++b) ab.b[b] = a.bands[b];
   const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
   HIPCHK(c, timed(c, DFLASH_K_PROLOGUE, st, [&] {
-    return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed,
-                               c->layers[0].in_norm, c->h, c->eps, c->X, c->Xn, c->Xn_lo, st);
+    return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed, c->layers[0].in_norm, c->h,
+                               c->X, c->ssq, c->Xn, c->Xn_lo, st);
   }));
-  auto gemm = [&](const bf16* A, const bf16* A_lo, int lda, const bf16* W, const GemmPlan& p) -> hipError_t {
+  // normed: (A, A_lo) is the residual stream times a norm weight, and the result rows take
+  // the rows' RMSNorm scales from the slice sums of squares
+  auto gemm = [&](const bf16* A, const bf16* A_lo, int lda, const bf16* W, const GemmPlan& p,
+                  bool normed) -> hipError_t {
     const long long ps = (long long)M * p.N;
     for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
       const int mg = std::min(ROW_GROUP, M - r0);
+      const NormIn nn{c->ssq + (size_t)r0 * SSQ_STRIDE, c->eps, c->h};
       hipError_t e = timed(c, DFLASH_K_GEMM, st, [&] {
-        return launch_gemm_skinny(A + (size_t)r0 * lda, A_lo + (size_t)r0 * lda, lda, mg, W, p.N, p.K,
-                                  p.klen, c->part + (size_t)r0 * p.N, ps, true, st);
+        return launch_gemm_skinny(A + (size_t)r0 * lda, A_lo + (size_t)r0 * lda, lda, mg, W, p.N, p.K, p.klen,
+                                  c->part + (size_t)r0 * p.N, ps, true, st, normed ? &nn : nullptr);
       });
       if (e != hipSuccess) return e;
     }
@@ -722,7 +739,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   for (int l = 0; l < c->L; ++l) {
     const LayerDev& d = c->layers[l];
     const int sw = sliding_layer(c, l) ? 1 : 0;
-    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_qkv, c->g_qkv));
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_qkv, c->g_qkv, true));
     HIPCHK(c, timed(c, DFLASH_K_QKV_POST, st, [&] {
       return launch_qkv_post(c->part, c->g_qkv.S, (long long)M * c->g_qkv.N, M, gamma, c->bands_dev,
                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
@@ -736,32 +753,50 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       return launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
     }));
-    HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, d.o_proj, c->g_o));
+    HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, d.o_proj, c->g_o, false));
     HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-      return launch_resid_norm(c->X, c->part, c->g_o.S, (long long)M * c->g_o.N, M, c->h, d.post_norm,
-                               c->eps, c->Xn, c->Xn_lo, st);
+      return launch_resid_sum(c->X, c->part, c->g_o.S, (long long)M * c->g_o.N, M, c->h, d.post_norm, c->ssq,
+                              c->Xn, c->Xn_lo, st);
     }));
-    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_gu, c->g_gu));
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_gu, c->g_gu, true));
     HIPCHK(c, timed(c, DFLASH_K_SILU, st, [&] {
       return launch_silu_mul(c->part, c->g_gu.S, (long long)M * c->g_gu.N, M, c->ff, c->act, c->act_lo, st);
     }));
-    HIPCHK(c, gemm(c->act, c->act_lo, c->ff, d.down_proj, c->g_down));
-    const bf16* wn = l + 1 < c->L ? c->layers[l + 1].in_norm : c->norm;
-    HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-      return launch_resid_norm(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h, wn,
-                               c->eps, c->Xn, c->Xn_lo, st);
-    }));
+    HIPCHK(c, gemm(c->act, c->act_lo, c->ff, d.down_proj, c->g_down, false));
+    if (l + 1 < c->L) {
+      HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+        return launch_resid_sum(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h,
+                                c->layers[l + 1].in_norm, c->ssq, c->Xn, c->Xn_lo, st);
+      }));
+    } else {
+      // the last residual add also applies the final norm: the lm_head's rows (hi + lo)
+      HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+        return launch_resid_norm(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h, c->norm,
+                                 c->eps, c->Xn, c->Xn_lo, st);
+      }));
+    }
   }
-  for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
-    const int mg = std::min(ROW_GROUP, M - r0);
+  // one row group of at most 16 rows with the rows in LDS whole: the persistent lm_head;
+  // otherwise one launch per row group of up to 64 rows
+  const int ng_p = lmhead_persistent_groups(c->V, c->h, M, c->n_cu);
+  const int ng = ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
+  if (ng_p > 0) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
-      return launch_lmhead_argmax(c->Xn + (size_t)r0 * c->h, c->Xn_lo + (size_t)r0 * c->h, c->h, mg, r0,
-                                  c->lm_head, c->V, c->h,
-                                  c->best_v, c->best_i, c->lm_groups, gamma, logits, st);
+      return launch_lmhead_persistent(c->Xn, c->Xn_lo, c->h, M, 0, c->lm_head, c->V, c->h, c->best_v, c->best_i,
+                                      ng, gamma, logits, st);
     }));
+  } else {
+    for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
+      const int mg = std::min(ROW_GROUP, M - r0);
+      HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
+        return launch_lmhead_argmax(c->Xn + (size_t)r0 * c->h, c->Xn_lo + (size_t)r0 * c->h, c->h, mg, r0,
+                                    c->lm_head, c->V, c->h,
+                                    c->best_v, c->best_i, ng, gamma, logits, st);
+      }));
+    }
   }
   HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] {
-    return launch_argmax_reduce(c->best_v, c->best_i, c->lm_groups, n_seqs, gamma, draft_tokens, st);
+    return launch_argmax_reduce(c->best_v, c->best_i, ng, n_seqs, gamma, draft_tokens, st);
   }));
   return DFLASH_OK;
 }

@@ -57,7 +57,8 @@ enum {
 /* Model and pool configuration (all host memory, copied by dflash_create).
  * Supported shapes: head_dim in {32, 64, 128}; num_q_heads % num_kv_heads == 0 with a
  * group of at most 8 query heads; gamma_max in [2, 16]; hidden, intermediate,
- * num_q_heads*head_dim and num_taps*target_hidden multiples of 256; max_batch in [1, 32];
+ * num_q_heads*head_dim and num_taps*target_hidden multiples of 256; hidden <= 8192;
+ * max_batch in [1, 32];
  * max_seq_len in [1, 2^28]. Positions (stamped and RoPE) lie in [0, 2^30). */
 typedef struct {
   int32_t num_layers, hidden, num_q_heads, num_kv_heads, head_dim, intermediate, vocab;

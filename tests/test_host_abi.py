@@ -50,6 +50,7 @@ def _null_weights(m):
 @pytest.mark.parametrize("change", [
     dict(head_dim=48), dict(num_kv_heads=3), dict(gamma_max=17), dict(gamma_max=1),
     dict(hidden=200), dict(intermediate=640), dict(hidden=384), dict(mask_token_id=5000), dict(num_q_heads=32, num_kv_heads=2),
+    dict(hidden=8448, target_hidden=8448, intermediate=8448),
 ])
 def test_create_rejects_unsupported_shapes_before_any_gpu_call(change):
     m = dict(synth.model("tiny-L2-h256"), **change)
