@@ -49,7 +49,7 @@ def gemm_bytes(m, M):
     return per_layer * m["num_layers"]
 
 
-# HBM bytes per launch of the forward's layer GEMMs (k_gemm_split<1, true>, mean over
+# HBM bytes per launch of the forward's layer GEMMs (k_gemm_split, mean over
 # the QKV, O, gate/up and down shapes), from `rocprofv3 --pmc FETCH_SIZE` and
 # `--pmc WRITE_SIZE` runs of `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-batch16
 # --no-longctx`, scaled by what the same counters read for 20 plain 256 MiB device copies
@@ -57,8 +57,8 @@ def gemm_bytes(m, M):
 # the bytes written). Valid only for the kernel source they were taken on.
 TRAFFIC = {
     "gemm": dict(source="block_diffusion_draft_02_amd/csrc/k_gemm.hip",
-                 sha256="5d2ec9b5f7efe2b715035a15c9840bbce40a0645e0af9e3c19dcdf6d443d1300",
-                 fetch_bytes=30.18e6, write_bytes=3.545e6),
+                 sha256="f1030a888ebbc96325604316880b915fcec7460c99f8c471c76e86903ba7fa5c",
+                 fetch_bytes=30.20e6, write_bytes=3.543e6),
 }
 
 
