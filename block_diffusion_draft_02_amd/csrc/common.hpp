@@ -81,6 +81,38 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// The canonical sum of S split-K partials p[s * ps], s = 0..S-1: consecutive groups of gsz
+// splits are each added in split order starting from zero, then the group sums in group
+// order starting from zero. Every consumer of the forward's GEMM partials adds them this
+// way, so a GEMM that forms the group sums itself (handing over one partial per group, then
+// gsz = 1) gives the same bits. Loads go out B at a time before their adds, unconditionally
+// (a pass past S re-reads the last split and drops it), so none waits for another.
+template <typename T>
+__device__ __forceinline__ T ld_part(const float* p) { return *reinterpret_cast<const T*>(p); }
+
+template <int B, typename T>
+__device__ __forceinline__ T sum_splits(const float* __restrict__ p, int S, long long ps, int gsz) {
+  T t = T{}, grp = T{};
+  int in_grp = 0;
+  for (int s0 = 0; s0 < S; s0 += B) {
+    T v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) v[u] = ld_part<T>(p + (long long)min(s0 + u, S - 1) * ps);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (s0 + u < S) {
+        grp += v[u];
+        if (++in_grp == gsz || s0 + u + 1 == S) {
+          t += grp;
+          grp = T{};
+          in_grp = 0;
+        }
+      }
+    }
+  }
+  return t;
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 // NeoX rotation of the pair (x1, x2) = (x[j], x[j + d/2]) by pos * inv_freq[j]. The angle

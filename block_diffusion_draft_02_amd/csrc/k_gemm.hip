@@ -8,8 +8,12 @@
 //  * k_gemm_skinny: the weight-streaming form for the block forward (M = bands * gamma
 //    rows, at most 64 per launch). One wavefront owns 16 output columns over one K split
 //    and streams those 16 weight rows exactly once; the activation rows come from L2.
-//    Partial sums of every split go to P[s][M][N] and are added in split order by the
-//    consumer, so a row's result never depends on how many other rows share the launch.
+//    Partial sums of every split go to P[s][M][N] and are added by the consumer in the
+//    canonical order (sum_splits), so a row's result never depends on how many other rows
+//    share the launch.
+//  * k_gemm_wide: the batched forward's form (more than 64 rows): 128 x 128 output tiles
+//    with the same per-element MFMA chains, adding each group of splits itself; and the
+//    batched lm_head with the argmax epilogue.
 //  * k_gemm_tiled: an LDS-tiled 128x128x64 form for the context append (thousands of rows).
 //  * k_lmhead_argmax: the skinny form over the vocabulary with a running (max, index) per
 //    row in the epilogue instead of a logits store; k_argmax_reduce finishes the argmax.
@@ -320,6 +324,288 @@ hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, c
 }
 
 // ---------------------------------------------------------------------------------------
+// Wide form for many rows (the batched forward): one workgroup computes WD_M rows x WD_N
+// columns. Activation chunks (hi and lo, WD_KC deep) are staged through LDS, double
+// buffered and shared by the four waves; wave w owns columns [32w, 32w + 32) as two T16
+// tiles and loads their weight operands straight into registers (every load one contiguous
+// 1 KB run), one chunk ahead. Per output element the MFMA sequence is the skinny kernels':
+// 256-deep chains from zero, each 32-deep step one MFMA on the hi term, then one on the lo
+// term.
+//  * partial mode (layer GEMMs): the workgroup takes one group of gsz consecutive 256-deep
+//    splits and adds their chains in split order from zero (each times the row's RMSNorm
+//    scale under NORM). That is the group sum the consumers form from the skinny kernel's
+//    per-split partials (sum_splits), so one partial per group is handed over.
+//  * argmax mode (lm_head): one chain over the full K, then per row the best (value, lowest
+//    index) over the workgroup's columns, and optionally the drafted rows' fp32 logits.
+constexpr int WD_M = 128;   // rows per workgroup (eight 16-row tiles)
+constexpr int WD_N = 128;   // columns per workgroup: 4 waves x 2 tiles
+constexpr int WD_KC = 64;   // depth of one staged activation chunk
+constexpr int WD_APAD = 8;  // LDS row padding: rows 144 B apart keep a 16-lane read conflict-free
+
+// running argmax: a larger value, or an equal one at a lower index, wins (NaN never does)
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+struct WideOut {
+  float* P;            // partial mode: P[group][M][N]
+  long long ps;        //   group stride (elements)
+  int gsz;             //   splits per group
+  NormIn nrm;          //   NORM: the rows' slice sums of squares
+  float* best_v;       // argmax mode: [M][n_groups]
+  int* best_i;
+  int n_groups, gamma;
+  float* logits;       //   drafted rows' logits [rows][N] or null
+};
+
+template <bool ARGMAX, bool NORM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(
+    const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda, int M,
+    const bf16* __restrict__ W, int N, int K, int gx, int gy, WideOut o) {
+  constexpr int WM = WD_M / 16;
+  constexpr int PPR = WD_KC / 8;                 // 16-byte pieces per row and term
+  constexpr int PT = WD_M * PPR / 256;           // pieces per thread and term
+  __shared__ __attribute__((aligned(16))) bf16 sa[2][2][WD_M][WD_KC + WD_APAD];
+  __shared__ float srs[NORM ? WD_M : 1];
+  __shared__ float sv[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
+  __shared__ int si[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  // workgroup id -> (column group x, row group y, split group z). Workgroups go to the eight
+  // XCDs round robin, so the row groups of one column group get ids 8 apart: one XCD, one
+  // L2, and their weight tiles leave HBM once.
+  const int id = blockIdx.x;
+  int q = id >> 3;
+  const int y = q % gy;
+  q /= gy;
+  const int gx8 = (gx + 7) / 8;
+  const int x = (q % gx8) * 8 + (id & 7), z = q / gx8;
+  if (x >= gx) return;
+  const int m0 = y * WD_M;
+  const int S = K / 256;
+  const int s_lo = ARGMAX ? 0 : z * o.gsz;
+  const int s_hi = ARGMAX ? S : min(S, s_lo + o.gsz);
+  const int kb = s_lo * 256;
+  const int nck = (s_hi - s_lo) * (256 / WD_KC);
+  const int ntiles = (N + 15) / 16;
+  const int tile0 = x * 8 + wave * 2;
+  // tiles past the last one re-read the last tile; their columns are never used
+  const bf16* wp0 = W + (size_t)min(tile0, ntiles - 1) * 16 * K + lane * 8;
+  const bf16* wp1 = W + (size_t)min(tile0 + 1, ntiles - 1) * 16 * K + lane * 8;
+
+  if (NORM) {
+    // the rows' RMSNorm scales, each row's slice sums added as the skinny kernel adds them
+    for (int r = threadIdx.x; r < WD_M; r += 256) {
+      const float* qv = o.nrm.ssq + (size_t)min(m0 + r, M - 1) * SSQ_STRIDE;
+      float s4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int t = 0; t < SSQ_STRIDE / 4; ++t) s += qv[j + 4 * t];
+        s4[j] = s;
+      }
+      srs[NORM ? r : 0] = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / (float)o.nrm.h + o.nrm.eps);
+    }
+  }
+
+  auto load_w = [&](bf16x8 (&w)[2][2], int k) {
+    const size_t off = (size_t)(k >> 8) * T16_BLOCK + ((k & 255) >> 5) * 512;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      w[0][s] = ld8(wp0 + off + s * 512);
+      w[1][s] = ld8(wp1 + off + s * 512);
+    }
+  };
+  auto load_a = [&](u32x4 (&ra)[2][PT], int k) {
+#pragma unroll
+    for (int v = 0; v < PT; ++v) {
+      const int p = threadIdx.x + 256 * v;
+      const size_t src = (size_t)min(m0 + p / PPR, M - 1) * lda + k + (p % PPR) * 8;   // rows >= M repeat the last row
+      ra[0][v] = *reinterpret_cast<const u32x4*>(A + src);
+      ra[1][v] = *reinterpret_cast<const u32x4*>(A_lo + src);
+    }
+  };
+  auto store_a = [&](const u32x4 (&ra)[2][PT], int buf) {
+#pragma unroll
+    for (int v = 0; v < PT; ++v) {
+      const int p = threadIdx.x + 256 * v;
+      *reinterpret_cast<u32x4*>(&sa[buf][0][p / PPR][(p % PPR) * 8]) = ra[0][v];
+      *reinterpret_cast<u32x4*>(&sa[buf][1][p / PPR][(p % PPR) * 8]) = ra[1][v];
+    }
+  };
+  f32x4 acc[WM][2];
+  f32x4 gs[ARGMAX ? 1 : WM][2];
+#pragma unroll
+  for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!ARGMAX) gs[ARGMAX ? 0 : mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  // one staged chunk: per 32-deep step, the hi MFMAs of every (row tile, column tile), then
+  // the lo ones (per element: hi, then lo, step after step)
+  auto mma = [&](int buf, const bf16x8 (&w)[2][2]) {
+#pragma unroll
+    for (int s = 0; s < WD_KC / 32; ++s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 av[WM];
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt)
+          av[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sa[buf][t][mt * 16 + c][s * 32 + g * 8]));
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(av[mt], w[nt][s], acc[mt][nt]);
+      }
+    }
+  };
+  // after chunk j: a 256-deep split ends every 256/WD_KC chunks; add its chain to the group
+  // sum (times the row scale: a separate rounding, as when the skinny kernel stores it)
+  auto fold = [&](int j) {
+    if (ARGMAX || (j + 1) % (256 / WD_KC) != 0) return;
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = NORM ? acc[mt][nt][e] * srs[NORM ? mt * 16 + 4 * g + e : 0] : acc[mt][nt][e];
+          gs[ARGMAX ? 0 : mt][nt][e] += v;
+        }
+        acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  bf16x8 w0[2][2], w1[2][2];
+  u32x4 ra[2][PT];
+  load_a(ra, kb);
+  load_w(w0, kb);
+  store_a(ra, 0);
+  __syncthreads();
+  for (int j = 0; j < nck; j += 2) {
+    // chunk j: LDS buffer 0 and w0; the next chunk is requested before it is computed, and
+    // stored into the other buffer (which every wave finished reading before the last barrier)
+    if (j + 1 < nck) {
+      load_a(ra, kb + (j + 1) * WD_KC);
+      load_w(w1, kb + (j + 1) * WD_KC);
+    }
+    mma(0, w0);
+    fold(j);
+    if (j + 1 < nck) store_a(ra, 1);
+    __syncthreads();
+    if (j + 1 >= nck) break;
+    if (j + 2 < nck) {
+      load_a(ra, kb + (j + 2) * WD_KC);
+      load_w(w0, kb + (j + 2) * WD_KC);
+    }
+    mma(1, w1);
+    fold(j + 1);
+    if (j + 2 < nck) store_a(ra, 0);
+    __syncthreads();
+  }
+
+  if (!ARGMAX) {
+    float* pp = o.P + (long long)z * o.ps;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = (tile0 + nt) * 16 + c;
+      if (n >= N) continue;
+#pragma unroll
+      for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + mt * 16 + 4 * g + e;
+          if (m < M) pp[(size_t)m * N + n] = gs[ARGMAX ? 0 : mt][nt][e];
+        }
+    }
+    return;
+  }
+  // argmax: per row, the best over this lane's two columns, the 16 lanes of its row group,
+  // then the four waves
+#pragma unroll
+  for (int mt = 0; mt < WM; ++mt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + mt * 16 + 4 * g + e;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = (tile0 + nt) * 16 + c;
+        if (n < N) {
+          const float v = acc[mt][nt][e];
+          better(bv, bi, v, n);
+          if (o.logits != nullptr && m < M) {
+            const int b = m / o.gamma, i = m % o.gamma;
+            if (i != 0) o.logits[(size_t)(b * (o.gamma - 1) + i - 1) * N + n] = v;
+          }
+        }
+      }
+#pragma unroll
+      for (int of = 1; of < 16; of <<= 1) {
+        const float ov = __shfl_xor(bv, of, 64);
+        const int oi = __shfl_xor(bi, of, 64);
+        better(bv, bi, ov, oi);
+      }
+      if (c == 0) {
+        sv[ARGMAX ? wave : 0][ARGMAX ? mt * 16 + 4 * g + e : 0] = bv;
+        si[ARGMAX ? wave : 0][ARGMAX ? mt * 16 + 4 * g + e : 0] = bi;
+      }
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < WD_M; r += 256) {
+    float bv = sv[0][ARGMAX ? r : 0];
+    int bi = si[0][ARGMAX ? r : 0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) better(bv, bi, sv[ARGMAX ? w : 0][ARGMAX ? r : 0], si[ARGMAX ? w : 0][ARGMAX ? r : 0]);
+    if (m0 + r < M) {
+      o.best_v[(size_t)(m0 + r) * o.n_groups + x] = bv;
+      o.best_i[(size_t)(m0 + r) * o.n_groups + x] = bi;
+    }
+  }
+}
+
+static unsigned wide_grid(int gx, int gy, int gz) { return (unsigned)((gx + 7) / 8 * 8) * gy * gz; }
+
+int gemm_wide_groups(int K, int gsz) { return (K / 256 + gsz - 1) / gsz; }
+
+hipError_t launch_gemm_wide(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
+                            int gsz, float* P, long long part_stride, hipStream_t st, const NormIn* norm) {
+  if (M < 1 || !A_lo || N < 16 || N % 16 || K < 256 || K % 256 || gsz < 1) return hipErrorInvalidValue;
+  if (norm && (norm->h != K || K > SSQ_STRIDE * SSQ_COLS)) return hipErrorInvalidValue;
+  const int gx = (N + WD_N - 1) / WD_N, gy = (M + WD_M - 1) / WD_M, gz = gemm_wide_groups(K, gsz);
+  WideOut o{};
+  o.P = P; o.ps = part_stride; o.gsz = gsz;
+  if (norm) {
+    o.nrm = *norm;
+    (void)launch(k_gemm_wide<false, true>, wide_grid(gx, gy, gz), 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+  } else {
+    (void)launch(k_gemm_wide<false, false>, wide_grid(gx, gy, gz), 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+  }
+  return hipGetLastError();
+}
+
+int lmhead_wide_groups(int V) { return (V + WD_N - 1) / WD_N; }
+
+hipError_t launch_lmhead_wide(const bf16* Y, const bf16* Y_lo, int ldy, int M, const bf16* W, int V, int K,
+                              float* best_v, int* best_i, int n_groups, int gamma, float* logits, hipStream_t st) {
+  if (M < 1 || !Y_lo || V < 1 || K < 256 || K % 256 || n_groups != lmhead_wide_groups(V) || gamma < 2)
+    return hipErrorInvalidValue;
+  WideOut o{};
+  o.best_v = best_v; o.best_i = best_i; o.n_groups = n_groups; o.gamma = gamma; o.logits = logits;
+  const int gy = (M + WD_M - 1) / WD_M;
+  (void)launch(k_gemm_wide<true, false>, wide_grid(n_groups, gy, 1), 256, 0, st, Y, Y_lo, ldy, M, W, V, K,
+               n_groups, gy, o);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 
 constexpr int TB = 128, TK = 64, TPAD = 8;
 
@@ -410,10 +696,6 @@ hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, co
 constexpr int LM_COLS = 4 * 16;  // vocabulary columns per workgroup (one 16-column tile per wave)
 
 int lmhead_groups(int V) { return (V + LM_COLS - 1) / LM_COLS; }
-
-__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-}
 
 template <int MT>
 __global__ __launch_bounds__(256) void k_lmhead_argmax(const bf16* __restrict__ Y,

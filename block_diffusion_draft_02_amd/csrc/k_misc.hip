@@ -12,19 +12,6 @@
 
 namespace dfl {
 
-// sum of S split-K partials P[s][r][j], s = 0..S-1, in a fixed order (eight running sums
-// over s mod 8, then added pairwise), so the result of a row never depends on the launch
-__device__ __forceinline__ float sum_parts(const float* __restrict__ p, int S, long long ps) {
-  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 8 <= S; s += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] += p[(long long)(s + u) * ps];
-  }
-  for (int u = 0; s < S; ++s, ++u) a[u] += p[(long long)s * ps];
-  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-}
-
 // ---- forward prologue ------------------------------------------------------------------
 // workgroup 0: block-table updates, slots and stamped positions of the block rows, band
 // table; workgroup 1 + r: embedding row of block row r into the residual stream, the sums
@@ -89,7 +76,7 @@ hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long 
 // RoPE pair (l, l + hd/2)
 template <int HD>
 __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, int S,
-                                                 long long ps, int N, int gamma,
+                                                 long long ps, int gsz, int N, int gamma,
                                                  const Band* __restrict__ bands, int nh, int nkv,
                                                  const bf16* __restrict__ qn,
                                                  const bf16* __restrict__ kn, float eps,
@@ -104,8 +91,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, in
   float x1 = 0.f, x2 = 0.f;
   if (act) {
     const float* p = P + (size_t)r * N + col;
-    x1 = sum_parts(p, S, ps);
-    x2 = sum_parts(p + H2, S, ps);
+    x1 = sum_splits<8, float>(p, S, ps, gsz);
+    x2 = sum_splits<8, float>(p + H2, S, ps, gsz);
   }
   const int kind = hh < nh ? 0 : (hh < nh + nkv ? 1 : 2);
   if (kind != 2) {
@@ -143,7 +130,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ P, in
   }
 }
 
-hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
+hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int gsz, int M, int gamma,
                            const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
                            const bf16* k_norm, float eps, const double* inv_freq, float mscale,
                            const long long* slots, KvGeom g, int layer, bf16* Q, bf16* Q_lo,
@@ -151,43 +138,18 @@ hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, 
   const int N = (nh + 2 * nkv) * hd;
   dim3 grid(M, nh + 2 * nkv);
   switch (hd) {
-    case 32: (void)launch(k_qkv_post<32>, grid, 64, 0, st, P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
-    case 64: (void)launch(k_qkv_post<64>, grid, 64, 0, st, P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
-    case 128: (void)launch(k_qkv_post<128>, grid, 64, 0, st, P, S, part_stride, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
+    case 32: (void)launch(k_qkv_post<32>, grid, 64, 0, st, P, S, part_stride, gsz, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
+    case 64: (void)launch(k_qkv_post<64>, grid, 64, 0, st, P, S, part_stride, gsz, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
+    case 128: (void)launch(k_qkv_post<128>, grid, 64, 0, st, P, S, part_stride, gsz, N, gamma, bands_dev, nh, nkv, q_norm, k_norm, eps, inv_freq, mscale, slots, g, layer, Q, Q_lo); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 // ---- residual add + RMSNorm ---------------------------------------------------------------
-// The row-wise consumers of split-K partials: 1024 threads per row = RN_G partial groups x
-// RN_T threads; thread t of group q sums splits q, q + RN_G, ... (ascending) for two 4-float
-// slices of the row, with every load of a pass issued before the first add; the groups are
-// then added in group order through LDS. The order depends only on S.
-constexpr int RN_T = 256;
-constexpr int RN_G = 4;
-constexpr int RN_JM = 8;           // splits per group and pass
+// The row-wise consumers of split-K partials: 1024 threads per row, thread t owns the 4-float
+// slices t, t + 1024, ... of the row and adds their partials in the canonical order.
 constexpr int RN_HMAX = 8192;      // row length the LDS row buffer holds
-
-__device__ __forceinline__ void group_sum2(const float* __restrict__ p, int S, long long ps, int q,
-                                           int j0, int j1, int h, f32x4& a0, f32x4& a1) {
-  a0 = a1 = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sb = q; sb < S; sb += RN_G * RN_JM) {
-    f32x4 v0[RN_JM], v1[RN_JM];
-#pragma unroll
-    for (int u = 0; u < RN_JM; ++u) {
-      const int sp = sb + u * RN_G;
-      const float* b = p + (long long)sp * ps;
-      v0[u] = (sp < S && j0 < h) ? *reinterpret_cast<const f32x4*>(b + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
-      v1[u] = (sp < S && j1 < h) ? *reinterpret_cast<const f32x4*>(b + j1) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int u = 0; u < RN_JM; ++u) {
-      a0 += v0[u];
-      a1 += v1[u];
-    }
-  }
-}
 
 // x (LDS row of h floats, complete) -> out = x * rs * w as hi + lo bf16
 __device__ __forceinline__ void norm_out(const float* xs, int h, float rs, const bf16* __restrict__ w,
@@ -206,43 +168,14 @@ __device__ __forceinline__ void norm_out(const float* xs, int h, float rs, const
 // Sum of the split partials of row r (plus the residual X when given), kept in the LDS row
 // xs and written back to X; returns the row's sum of squares (valid in every thread).
 __device__ __forceinline__ float rows_gather(float* __restrict__ X, const float* __restrict__ p, int S,
-                                             long long ps, int h, float* xs, f32x4 (*red)[RN_T][2],
-                                             float* red_ss) {
-  const int q = threadIdx.x / RN_T, t = threadIdx.x % RN_T;
+                                             long long ps, int gsz, int h, float* xs, float* red_ss) {
   float ss = 0.f;
-  for (int base = 0; base < h; base += RN_T * 8) {
-    const int j0 = base + t * 4, j1 = base + RN_T * 4 + t * 4;
-    f32x4 x0 = f32x4{0.f, 0.f, 0.f, 0.f}, x1 = x0;
-    if (X != nullptr && q == 0) {
-      if (j0 < h) x0 = *reinterpret_cast<const f32x4*>(X + j0);
-      if (j1 < h) x1 = *reinterpret_cast<const f32x4*>(X + j1);
-    }
-    f32x4 a0, a1;
-    group_sum2(p, S, ps, q, j0, j1, h, a0, a1);
-    red[q][t][0] = a0;
-    red[q][t][1] = a1;
-    __syncthreads();
-    if (q == 0) {
-      f32x4 s0 = red[0][t][0], s1 = red[0][t][1];
-#pragma unroll
-      for (int g2 = 1; g2 < RN_G; ++g2) {
-        s0 += red[g2][t][0];
-        s1 += red[g2][t][1];
-      }
-      s0 += x0;
-      s1 += x1;
-      if (j0 < h) {
-        *reinterpret_cast<f32x4*>(xs + j0) = s0;
-        if (X != nullptr) *reinterpret_cast<f32x4*>(X + j0) = s0;
-        ss += s0[0] * s0[0] + s0[1] * s0[1] + s0[2] * s0[2] + s0[3] * s0[3];
-      }
-      if (j1 < h) {
-        *reinterpret_cast<f32x4*>(xs + j1) = s1;
-        if (X != nullptr) *reinterpret_cast<f32x4*>(X + j1) = s1;
-        ss += s1[0] * s1[0] + s1[1] * s1[1] + s1[2] * s1[2] + s1[3] * s1[3];
-      }
-    }
-    __syncthreads();
+  for (int j = threadIdx.x * 4; j < h; j += 1024 * 4) {
+    f32x4 y = sum_splits<16, f32x4>(p + j, S, ps, gsz);
+    if (X != nullptr) y = *reinterpret_cast<const f32x4*>(X + j) + y;
+    *reinterpret_cast<f32x4*>(xs + j) = y;
+    if (X != nullptr) *reinterpret_cast<f32x4*>(X + j) = y;
+    ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red_ss[threadIdx.x >> 6] = ss;
@@ -255,35 +188,32 @@ __device__ __forceinline__ float rows_gather(float* __restrict__ X, const float*
 
 // X[r] += sum_s P[s][r]; Xn[r] = RMSNorm_w(X[r]) as hi + lo bf16; one workgroup per row
 __global__ __launch_bounds__(1024) void k_resid_norm(float* __restrict__ X, const float* __restrict__ P,
-                                                     int S, long long ps, int h,
+                                                     int S, long long ps, int gsz, int h,
                                                      const bf16* __restrict__ w, float eps,
                                                      bf16* __restrict__ Xn, bf16* __restrict__ Xn_lo) {
   __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
-  __shared__ f32x4 red[RN_G][RN_T][2];
   __shared__ float red_ss[16];
   const int r = blockIdx.x;
-  const float tot = rows_gather(X + (size_t)r * h, P + (size_t)r * h, S, ps, h, xs, red, red_ss);
+  const float tot = rows_gather(X + (size_t)r * h, P + (size_t)r * h, S, ps, gsz, h, xs, red_ss);
   const float rs = rsqrtf(tot / (float)h + eps);
   norm_out(xs, h, rs, w, Xn + (size_t)r * h, Xn_lo + (size_t)r * h);
 }
 
-hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
+hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int gsz, int M,
                              int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
                              hipStream_t st) {
-  if (h > RN_HMAX || h % 4) return hipErrorInvalidValue;
-  (void)launch(k_resid_norm, M, 1024, 0, st, X, P, S, part_stride, h, w, eps, Xn, Xn_lo);
+  if (h > RN_HMAX || h % 4 || gsz < 1) return hipErrorInvalidValue;
+  (void)launch(k_resid_norm, M, 1024, 0, st, X, P, S, part_stride, gsz, h, w, eps, Xn, Xn_lo);
   return hipGetLastError();
 }
 
 // ---- residual add, parallel form ----------------------------------------------------------
-// One 64-thread workgroup per (row, 256-column slice): X[r] += sum_s P[s][r] with the splits
-// added in order, every load of a pass issued before the first add; then the slice's sum of
+// One 64-thread workgroup per (row, 256-column slice): X[r] += the canonical sum of the split
+// partials (every load of a pass issued before the first add); then the slice's sum of
 // squares (the next GEMM turns the row's sums into its RMSNorm scale) and X * w as the next
 // GEMM's hi + lo activation.
-constexpr int RS_BATCH = 16;   // splits per load pass
-
 __global__ __launch_bounds__(64) void k_resid_sum(float* __restrict__ X, const float* __restrict__ P,
-                                                  int S, long long ps, int h, const bf16* __restrict__ w,
+                                                  int S, long long ps, int gsz, int h, const bf16* __restrict__ w,
                                                   float* __restrict__ ssq, bf16* __restrict__ Xw,
                                                   bf16* __restrict__ Xw_lo) {
   const int r = blockIdx.x, j = blockIdx.y;
@@ -291,15 +221,7 @@ __global__ __launch_bounds__(64) void k_resid_sum(float* __restrict__ X, const f
   const size_t o = (size_t)r * h + col;
   const f32x4 x = *reinterpret_cast<const f32x4*>(X + o);
   const u32x2 wb = *reinterpret_cast<const u32x2*>(w + col);   // the context's aligned copy
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += RS_BATCH) {
-    f32x4 v[RS_BATCH];
-#pragma unroll
-    for (int u = 0; u < RS_BATCH; ++u)
-      v[u] = s0 + u < S ? *reinterpret_cast<const f32x4*>(P + (long long)(s0 + u) * ps + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < RS_BATCH; ++u) acc += v[u];
-  }
+  const f32x4 acc = sum_splits<16, f32x4>(P + o, S, ps, gsz);
   const f32x4 y = x + acc;
   *reinterpret_cast<f32x4*>(X + o) = y;
   const float wf[4] = {bf2f((bf16)(wb.x & 0xffff)), bf2f((bf16)(wb.x >> 16)), bf2f((bf16)(wb.y & 0xffff)), bf2f((bf16)(wb.y >> 16))};
@@ -312,30 +234,31 @@ __global__ __launch_bounds__(64) void k_resid_sum(float* __restrict__ X, const f
   if (threadIdx.x == 0) ssq[(size_t)r * SSQ_STRIDE + j] = ss;
 }
 
-hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stride, int M, int h,
+hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stride, int gsz, int M, int h,
                             const bf16* w, float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st) {
-  if (h % SSQ_COLS || h > SSQ_STRIDE * SSQ_COLS) return hipErrorInvalidValue;
-  (void)launch(k_resid_sum, dim3(M, h / SSQ_COLS), 64, 0, st, X, P, S, part_stride, h, w, ssq, Xw, Xw_lo);
+  if (h % SSQ_COLS || h > SSQ_STRIDE * SSQ_COLS || gsz < 1) return hipErrorInvalidValue;
+  (void)launch(k_resid_sum, dim3(M, h / SSQ_COLS), 64, 0, st, X, P, S, part_stride, gsz, h, w, ssq, Xw, Xw_lo);
   return hipGetLastError();
 }
 
 // ---- SwiGLU -----------------------------------------------------------------------------
 // the fused gate/up projection's columns are [gate (ff) | up (ff)]
 __global__ __launch_bounds__(256) void k_silu_mul(const float* __restrict__ P, int S, long long ps,
-                                                  int M, int ff, bf16* __restrict__ A,
+                                                  int gsz, int M, int ff, bf16* __restrict__ A,
                                                   bf16* __restrict__ A_lo) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)M * ff) return;
   const size_t r = idx / ff, j = idx % ff;
   const float* p = P + r * 2 * ff + j;
-  const float gs = sum_parts(p, S, ps), us = sum_parts(p + ff, S, ps);
+  const float gs = sum_splits<8, float>(p, S, ps, gsz), us = sum_splits<8, float>(p + ff, S, ps, gsz);
   split_bf16(silu(gs) * us, A[idx], A_lo[idx]);
 }
 
-hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
+hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz, int M, int ff,
                            bf16* A, bf16* A_lo, hipStream_t st) {
+  if (gsz < 1) return hipErrorInvalidValue;
   const size_t n = (size_t)M * ff;
-  (void)launch(k_silu_mul, (unsigned)((n + 255) / 256), 256, 0, st, P, S, part_stride, M, ff, A, A_lo);
+  (void)launch(k_silu_mul, (unsigned)((n + 255) / 256), 256, 0, st, P, S, part_stride, gsz, M, ff, A, A_lo);
   return hipGetLastError();
 }
 
@@ -368,10 +291,9 @@ __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__
                                                        bf16* __restrict__ out,
                                                        bf16* __restrict__ out_lo) {
   __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
-  __shared__ f32x4 red[RN_G][RN_T][2];
   __shared__ float red_ss[16];
   const int r = blockIdx.x;
-  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, h, xs, red, red_ss);
+  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, S, h, xs, red_ss);
   const float rs = rsqrtf(tot / (float)h + eps);
   norm_out(xs, h, rs, w, out + (size_t)r * h, out_lo + (size_t)r * h);
 }
@@ -400,7 +322,8 @@ __global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__
   const bool act = l < H2;
   const size_t ld = (size_t)L * 2 * nkv * HD;
   const float* src = KV + (size_t)r * ld + (size_t)idx * HD;
-  float x1 = act ? sum_parts(src + l, S, ps) : 0.f, x2 = act ? sum_parts(src + l + H2, S, ps) : 0.f;
+  float x1 = act ? sum_splits<8, float>(src + l, S, ps, S) : 0.f;
+  float x2 = act ? sum_splits<8, float>(src + l + H2, S, ps, S) : 0.f;
   if (kv == 0) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float rs = rsqrtf(ss / (float)HD + eps);

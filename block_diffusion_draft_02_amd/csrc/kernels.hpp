@@ -97,6 +97,14 @@ __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (si
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                               int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
                               hipStream_t st, const NormIn* norm = nullptr);
+// Wide form for more than 64 rows (A_lo required, W in the T16 layout, K a multiple of
+// 256, N of 16): partials P[z][M][N] (z < gemm_wide_groups(K, gsz), stride part_stride),
+// each the sum of the 256-deep split chains of group z (splits z*gsz .. z*gsz + gsz - 1)
+// as the consumers' canonical order forms it from the skinny kernel's per-split partials.
+int gemm_wide_groups(int K, int gsz);
+hipError_t launch_gemm_wide(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
+                            int gsz, float* P, long long part_stride, hipStream_t st,
+                            const NormIn* norm = nullptr);
 // Copy a row-major [N, K] bf16 weight into the T16 layout (ceil(N/16)*16 rows, the padding
 // rows zero); K a multiple of 256.
 hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStream_t st);
@@ -113,6 +121,12 @@ int lmhead_persistent_groups(int V, int K, int M, int n_cu);
 hipError_t launch_lmhead_persistent(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W,
                                     int V, int K, float* best_v, int* best_i, int n_groups, int gamma,
                                     float* logits, hipStream_t st);
+// The wide lm_head (any row count, rows 0..M-1 of the forward; W in the T16 layout): one
+// argmax partial per (row, 128-column group); n_groups = lmhead_wide_groups(V).
+int lmhead_wide_groups(int V);
+hipError_t launch_lmhead_wide(const bf16* Y, const bf16* Y_lo, int ldy, int M, const bf16* W, int V, int K,
+                              float* best_v, int* best_i, int n_groups, int gamma, float* logits,
+                              hipStream_t st);
 hipError_t launch_lmhead_argmax(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W, int V,
                                 int K, float* best_v, int* best_i, int n_groups, int gamma,
                                 float* logits, hipStream_t st);
@@ -120,24 +134,27 @@ hipError_t launch_argmax_reduce(const float* best_v, const int* best_i, int n_gr
                                 int n_bands, int gamma, int* tokens, hipStream_t st);
 
 // ---- forward elementwise (k_misc.hip) ------------------------------------------------
+// The consumers of the forward's GEMM partials take (P, S, part_stride, gsz) and add the S
+// partials in the canonical order of sum_splits: groups of gsz splits, each in split order
+// from zero, then the group sums in group order from zero.
 // block tables, slots, band table; X = the block rows' embeddings, their slice sums of
 // squares ssq [rows][h/256], and X * w_in0 as hi + lo bf16 (Xw, Xw_lo)
 hipError_t launch_fwd_prologue(const FwdArgs& a, Band* bands_dev, int* bt, long long* slots,
                                int* kpos, const bf16* embed, const bf16* w_in0, int h, float* X,
                                float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st);
-hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int M, int gamma,
+hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int gsz, int M, int gamma,
                            const Band* bands_dev, int nh, int nkv, int hd, const bf16* q_norm,
                            const bf16* k_norm, float eps, const double* inv_freq, float mscale,
                            const long long* slots, KvGeom g, int layer, bf16* Q, bf16* Q_lo,
                            hipStream_t st);
-hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int M,
+hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_stride, int gsz, int M,
                              int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
                              hipStream_t st);
-// X[r] += sum_s P[s][r] (splits in order); the slice sums of squares of the new rows and
+// X[r] += sum_s P[s][r] (canonical order); the slice sums of squares of the new rows and
 // X * w as hi + lo bf16 (w: the norm weight of the GEMM that consumes them)
-hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stride, int M, int h,
+hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stride, int gsz, int M, int h,
                             const bf16* w, float* ssq, bf16* Xw, bf16* Xw_lo, hipStream_t st);
-hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int M, int ff,
+hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz, int M, int ff,
                            bf16* A, bf16* A_lo, hipStream_t st);
 
 // ---- attention (k_attn.hip) ----------------------------------------------------------

@@ -37,7 +37,8 @@ struct SeqState {
   int kv_len = 0;
 };
 
-struct GemmPlan { int N, K, klen, S; };
+// A forward GEMM: K splits of klen, added by the consumers in groups of gsz splits
+struct GemmPlan { int N, K, klen, S, gsz; };
 
 }  // namespace
 
@@ -146,7 +147,15 @@ GemmPlan plan_gemm(int N, int K) {
   // narrow projections launch several hundred workgroups and the whole matrix is in flight at
   // once. Depends on (N, K) only, never on the number of rows.
   const int klen = 256;
-  return GemmPlan{N, K, klen, (K + klen - 1) / klen};
+  const int S = (K + klen - 1) / klen;
+  // splits per group of the consumers' canonical order: from (N, K) alone, so that the wide
+  // kernel of a 256-row forward (2 row groups x ceil(N/128) column groups per split group)
+  // has at least about a chip's worth (256) of workgroups; a divisor of S, so the groups match
+  const int per_group = 2 * ((N + 127) / 128);
+  const int want = std::max(1, (256 + per_group - 1) / per_group);
+  int gsz = std::max(1, S / want);
+  while (S % gsz) --gsz;
+  return GemmPlan{N, K, klen, S, gsz};
 }
 
 int chunk_pages(int pages) {
@@ -722,9 +731,22 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   }));
   // normed: (A, A_lo) is the residual stream times a norm weight, and the result rows take
   // the rows' RMSNorm scales from the slice sums of squares
+  // More than one row group: the wide kernel, one launch, one partial per split group;
+  // otherwise the skinny kernel, one partial per split. parts(p) = what the consumer adds:
+  // (partials, splits per group).
+  const bool wide = M > ROW_GROUP;
+  auto parts = [&](const GemmPlan& p) {
+    return wide ? std::make_pair(gemm_wide_groups(p.K, p.gsz), 1) : std::make_pair(p.S, p.gsz);
+  };
   auto gemm = [&](const bf16* A, const bf16* A_lo, int lda, const bf16* W, const GemmPlan& p,
                   bool normed) -> hipError_t {
     const long long ps = (long long)M * p.N;
+    if (wide) {
+      const NormIn nn{c->ssq, c->eps, c->h};
+      return timed(c, DFLASH_K_GEMM, st, [&] {
+        return launch_gemm_wide(A, A_lo, lda, M, W, p.N, p.K, p.gsz, c->part, ps, st, normed ? &nn : nullptr);
+      });
+    }
     for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
       const int mg = std::min(ROW_GROUP, M - r0);
       const NormIn nn{c->ssq + (size_t)r0 * SSQ_STRIDE, c->eps, c->h};
@@ -741,7 +763,8 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     const int sw = sliding_layer(c, l) ? 1 : 0;
     HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_qkv, c->g_qkv, true));
     HIPCHK(c, timed(c, DFLASH_K_QKV_POST, st, [&] {
-      return launch_qkv_post(c->part, c->g_qkv.S, (long long)M * c->g_qkv.N, M, gamma, c->bands_dev,
+      return launch_qkv_post(c->part, parts(c->g_qkv).first, (long long)M * c->g_qkv.N, parts(c->g_qkv).second,
+                             M, gamma, c->bands_dev,
                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
                              (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
     }));
@@ -755,32 +778,39 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     }));
     HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, d.o_proj, c->g_o, false));
     HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-      return launch_resid_sum(c->X, c->part, c->g_o.S, (long long)M * c->g_o.N, M, c->h, d.post_norm, c->ssq,
-                              c->Xn, c->Xn_lo, st);
+      return launch_resid_sum(c->X, c->part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
+                              M, c->h, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
     }));
     HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_gu, c->g_gu, true));
     HIPCHK(c, timed(c, DFLASH_K_SILU, st, [&] {
-      return launch_silu_mul(c->part, c->g_gu.S, (long long)M * c->g_gu.N, M, c->ff, c->act, c->act_lo, st);
+      return launch_silu_mul(c->part, parts(c->g_gu).first, (long long)M * c->g_gu.N, parts(c->g_gu).second, M,
+                             c->ff, c->act, c->act_lo, st);
     }));
     HIPCHK(c, gemm(c->act, c->act_lo, c->ff, d.down_proj, c->g_down, false));
     if (l + 1 < c->L) {
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-        return launch_resid_sum(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h,
-                                c->layers[l + 1].in_norm, c->ssq, c->Xn, c->Xn_lo, st);
+        return launch_resid_sum(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
+                                parts(c->g_down).second, M, c->h, c->layers[l + 1].in_norm, c->ssq, c->Xn,
+                                c->Xn_lo, st);
       }));
     } else {
       // the last residual add also applies the final norm: the lm_head's rows (hi + lo)
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-        return launch_resid_norm(c->X, c->part, c->g_down.S, (long long)M * c->g_down.N, M, c->h, c->norm,
-                                 c->eps, c->Xn, c->Xn_lo, st);
+        return launch_resid_norm(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
+                                 parts(c->g_down).second, M, c->h, c->norm, c->eps, c->Xn, c->Xn_lo, st);
       }));
     }
   }
   // one row group of at most 16 rows with the rows in LDS whole: the persistent lm_head;
-  // otherwise one launch per row group of up to 64 rows
+  // more than one row group: the wide lm_head; otherwise one launch per row group
   const int ng_p = lmhead_persistent_groups(c->V, c->h, M, c->n_cu);
-  const int ng = ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
-  if (ng_p > 0) {
+  const int ng = wide ? lmhead_wide_groups(c->V) : ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
+  if (wide) {
+    HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
+      return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, c->lm_head, c->V, c->h, c->best_v, c->best_i, ng, gamma,
+                                logits, st);
+    }));
+  } else if (ng_p > 0) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
       return launch_lmhead_persistent(c->Xn, c->Xn_lo, c->h, M, 0, c->lm_head, c->V, c->h, c->best_v, c->best_i,
                                       ng, gamma, logits, st);

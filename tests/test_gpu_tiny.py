@@ -130,6 +130,27 @@ def test_batch_invariance_bitwise(tiny):
     d.close()
 
 
+def test_wide_rows_parity_yarn_window(tiny):
+    """Seven bands (112 rows: more than one 64-row group, so the wide GEMMs and the wide
+    lm_head run, with a partial 128-row tile) under YaRN and a sliding window, against the
+    oracle."""
+    m, W = tiny
+    my = dict(m, rope_type="yarn", yarn_factor=4.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,
+              yarn_beta_slow=1.0, sliding_window=40, layer_sliding=[True, False])
+    nb = 7
+    pair = Pair(my, W, 200, nb)
+    lens = [3, 150, 47, 16, 90, 1, 121]
+    for s in range(nb):
+        pair.append(s, synth.gen_hidden(m, SEED, lens[s], 60 + s))
+    agree = Agreement()
+    for call in range(4):
+        order = list(range(nb)) if call % 2 == 0 else list(range(nb))[::-1]
+        toks, logits, ref = pair.forward(order, synth.gen_bonus(m, SEED, nb, index=300 + call))
+        agree.add(toks, logits, ref)
+    agree.check(min_positions=300)
+    pair.close()
+
+
 def test_yarn_and_sliding_window(tiny):
     m, W = tiny
     my = dict(m, rope_type="yarn", yarn_factor=4.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,
