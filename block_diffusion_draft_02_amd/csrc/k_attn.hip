@@ -5,10 +5,11 @@
 // Work split: the keys of a band are cut into chunks whose length depends only on the band's
 // own length (a multiple of 256 keys), so a band's result does not depend on which other
 // bands share the call. One workgroup per (chunk, kv head, 32 query rows), with the band
-// table passed by value. The workgroup stages its query rows (hi, lo) and the chunk's page
-// ids in LDS; each of its four wavefronts then takes 32-key slices of the chunk (keys 32w,
-// 32w + 128, ...), loading a slice's K and V^T fragments straight from the pool into MFMA
-// operands, and keeps an online softmax state for its two 16-row query tiles:
+// table passed by value. The workgroup stages its query rows (hi, lo) and all the chunk's
+// page ids in LDS; each of its four wavefronts then takes 32-key slices of the chunk (keys
+// 32w, 32w + 128, ...), loading a slice's K and V^T fragments straight from the pool into MFMA
+// operands, and keeps an online softmax state (exp2 domain, running maximum in raw score
+// units, so a probability is one FMA and one v_exp_f32) for its two 16-row query tiles:
 //   S^T = K Q^T   two 16x16x32 MFMA tiles per slice and query tile; the key order inside
 //                 the tiles is permuted so that every lane ends up holding 8 consecutive
 //                 keys of one row
@@ -27,7 +28,7 @@ constexpr int KP = AW * KW;      // keys of one workgroup pass
 constexpr int RG = 32;           // query rows per workgroup: two 16-row tiles
 constexpr int RPAD = 128;        // query-row slots of one (chunk, kv head) partial
 constexpr int NCH_MAX = 64;      // chunks of one band that k_attn_combine accepts
-constexpr int PG_LDS = 128;      // chunk pages whose ids are staged in LDS (the rest are read from the table)
+// ATTN_CHUNK_PAGES_MAX (kernels.hpp): page ids of a chunk, all staged in LDS
 
 // LDS: the workgroup's query rows (hi, lo) during the key loop, then the four waves'
 // partial states for the merge; plus the chunk's page ids
@@ -44,7 +45,7 @@ struct AttnLds {
       float l[AW][RG];
     } mg;
   };
-  int page[PG_LDS];
+  int page[ATTN_CHUNK_PAGES_MAX];
 };
 
 // one wave's 32-key slice in registers: K fragments of the two S^T tiles, V^T fragments,
@@ -57,15 +58,16 @@ struct Slice {
 };
 
 template <int HD, bool WIN>
-__device__ __forceinline__ void load_slice(Slice<HD, WIN>& sl, const AttnLds<HD>& sm, const int* __restrict__ bt,
+__device__ __forceinline__ void load_slice(Slice<HD, WIN>& sl, const AttnLds<HD>& sm,
                                            const bf16* __restrict__ lpool, const int* __restrict__ kpos,
                                            size_t pl, int kvh, int nkv, int npg, int kt, int c, int grp) {
   constexpr int NS = HD / 32, ND = HD / 16;
   // the slice's 32 keys lie on chunk pages kt/16 and kt/16 + 1 (the zeroed sentinel page 0
-  // past the chunk, so every operand is finite and masked keys add exactly zero)
+  // past the chunk, so every operand is finite and masked keys add exactly zero); the page
+  // ids come from LDS only, so no load of the key loop waits on another
   const int lp = kt >> 4;
-  const int p0 = lp < PG_LDS ? sm.page[lp] : bt[lp];
-  const int p1 = lp + 1 < npg ? (lp + 1 < PG_LDS ? sm.page[lp + 1] : bt[lp + 1]) : 0;
+  const int p0 = sm.page[min(lp, ATTN_CHUNK_PAGES_MAX - 1)];
+  const int p1 = lp + 1 < npg ? sm.page[min(lp + 1, ATTN_CHUNK_PAGES_MAX - 1)] : 0;
   // K fragments: S^T tile t, row c covers slice key (c/4)*8 + t*4 + c%4, so lane (c, grp)
   // of the result holds slice keys grp*8 + 0..7 of query row c (e = t*4 + slot)
 #pragma unroll
@@ -90,7 +92,7 @@ __device__ __forceinline__ void load_slice(Slice<HD, WIN>& sl, const AttnLds<HD>
 }
 
 template <int HD, bool WIN>
-__device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const AttnLds<HD>& sm, int lim,
+__device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const AttnLds<HD>& sm, bool full, int lim,
                                               const int (&qpos)[2], int window, float scale_log2,
                                               float (&m_run)[2], float (&l_run)[2], f32x4 (&o)[2][HD / 16],
                                               int c, int grp) {
@@ -117,36 +119,45 @@ __device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const At
       for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(sl.kf[t][s], ql, sh[rt][t]);
     }
   }
+  // online softmax in the exp2 domain with the running maximum kept in raw score units, so
+  // each probability is one FMA and one v_exp_f32: p = 2^(s * scale - m * scale). Masks are
+  // applied only where a key can be hidden (the chunk's last slice, sliding layers).
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     float sv[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = sh[rt][e >> 2][e & 3] * scale_log2;
-      bool ok = e < lim;
-      if (WIN) ok = ok & (qpos[rt] - sl.kp[e & (WIN ? 7 : 0)] < window);
-      sv[e] = ok ? x : -INFINITY;
-      tmax = fmaxf(tmax, sv[e]);
+      float x = sh[rt][e >> 2][e & 3];
+      if (WIN || !full) {
+        bool ok = e < lim;
+        if (WIN) ok = ok & (qpos[rt] - sl.kp[e & (WIN ? 7 : 0)] < window);
+        x = ok ? x : -INFINITY;
+      }
+      sv[e] = x;
+      tmax = fmaxf(tmax, x);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run[rt], tmax);
     // rescale the running output only when some row's maximum moved
     if (__any(m_new > m_run[rt])) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run[rt] - m_new) * scale_log2);
       l_run[rt] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
     }
     m_run[rt] = m_new;
+    // a row with every key so far hidden keeps m = -inf: its hidden scores still give 2^-inf = 0
+    const float bias = (m_new == -INFINITY) ? 0.f : -m_new * scale_log2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sv[e] = (sv[e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_new);
+      sv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, bias));
       l_run[rt] += sv[e];
     }
-    // O^T += V^T P^T: P^T comes straight from the lane's own registers
-    const bf16x8 pb = pack8(sv);
+    // O^T += V^T P^T: P^T comes straight from the lane's own registers (bf16, round to nearest
+    // even, two per instruction)
+    const bf16x8 pb = __builtin_convertvector((f32x8){sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]}, bf16x8);
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[rt][dt] = mfma16(sl.vf[dt], pb, o[rt][dt]);
   }
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // the chunk's page ids and this workgroup's query rows (row r = rg*32 + rr is block row
   // r % gamma of query head r / gamma of this kv head's group; rows past R are zero)
-  for (int i = threadIdx.x; i < min(npg, PG_LDS); i += AW * 64) sm.page[i] = bt[i];
+  for (int i = threadIdx.x; i < min(npg, ATTN_CHUNK_PAGES_MAX); i += AW * 64) sm.page[i] = bt[i];
   for (int pc = threadIdx.x; pc < RG * HD / 8; pc += AW * 64) {
     const int rr = pc / (HD / 8), d8 = (pc % (HD / 8)) * 8;
     const int r = rg * RG + rr;
@@ -213,12 +224,14 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __syncthreads();
 
   // this wave's slices: keys kt = 32w, 32w + 128, ... (two waves per SIMD, and a second
-  // workgroup per CU, cover the load latency; a register double buffer of the next slice
-  // does not fit next to the 64-register output at head_dim 128)
+  // workgroup per CU, cover the load latency and overlap one wave's softmax with the other's
+  // MFMAs; a register ring of further slices would need one wave per SIMD, which loses that
+  // overlap and measured slower)
   for (int kt = wave * KW; kt < nkeys; kt += KP) {
     Slice<HD, WIN> sl;
-    load_slice<HD, WIN>(sl, sm, bt, lpool, g.kpos, pl, kvh, nkv, npg, kt, c, grp);
-    compute_slice<HD, WIN>(sl, sm, nkeys - kt - grp * 8, qpos, window, scale_log2, m_run, l_run, o, c, grp);
+    load_slice<HD, WIN>(sl, sm, lpool, g.kpos, pl, kvh, nkv, npg, kt, c, grp);
+    compute_slice<HD, WIN>(sl, sm, nkeys - kt >= KW, nkeys - kt - grp * 8, qpos, window, scale_log2, m_run, l_run, o,
+                           c, grp);
   }
 
   // merge the four waves' states in wave order (the LDS now holds the merge area)
@@ -232,7 +245,7 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int dt = 0; dt < ND; ++dt)
       *reinterpret_cast<f32x4*>(&sm.mg.o[wave][rt * 16 + c][dt * 16 + 4 * grp]) = o[rt][dt];
     if (grp == 0) {
-      sm.mg.m[wave][rt * 16 + c] = m_run[rt];
+      sm.mg.m[wave][rt * 16 + c] = m_run[rt] * scale_log2;   // the merge works in the exp2 domain
       sm.mg.l[wave][rt * 16 + c] = lt;
     }
   }

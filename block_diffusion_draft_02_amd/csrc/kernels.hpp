@@ -158,6 +158,9 @@ hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz
                            bf16* A, bf16* A_lo, hipStream_t st);
 
 // ---- attention (k_attn.hip) ----------------------------------------------------------
+// A chunk (one workgroup's keys) spans at most this many pages; the runtime's chunk plan
+// keeps to it (sequences of at most 16 * 16384 keys).
+constexpr int ATTN_CHUNK_PAGES_MAX = 512;
 // total_chunks = sum over bands of nch[sw]; partial buffers sized [total_chunks*nkv][128][hd]
 hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int total_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,

@@ -159,6 +159,7 @@ GemmPlan plan_gemm(int N, int K) {
 }
 
 int chunk_pages(int pages) {
+  // (pages <= 16384 by the config check, so a chunk never exceeds ATTN_CHUNK_PAGES_MAX)
   // 16 pages (256 keys: two passes of the attention workgroup's four 32-key wave slices) per
   // chunk, widened in steps of 16 pages so that a band never has more than 32 chunks: a
   // 4K-key band keeps every workgroup of a layer resident at once, long bands keep the
@@ -256,7 +257,9 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
     return bad("hidden, intermediate, q_dim and num_taps*target_hidden must be multiples of 256");
   if (cfg->mask_token_id < 0 || cfg->mask_token_id >= cfg->vocab) return bad("mask_token_id out of range");
   if (cfg->max_batch < 1 || cfg->max_batch > MAX_BANDS) return bad("max_batch must be in [1, 32]");
-  if (cfg->max_seq_len < 1 || cfg->max_seq_len > (1 << 28)) return bad("max_seq_len out of range");
+  // an attention chunk of the longest sequence must fit the kernel's page-id table
+  if (cfg->max_seq_len < 1 || (long long)cfg->max_seq_len + cfg->gamma_max + 1 > 16LL * 16384)
+    return bad("max_seq_len + gamma_max must be below 262144");
   if (!(cfg->rms_eps >= 0.f)) return bad("rms_eps must be >= 0");
   if (!(cfg->rope_theta > 1.0)) return bad("rope_theta must be > 1");
   if (cfg->rope_type != 0 && cfg->rope_type != 1) return bad("rope_type must be 0 or 1");

@@ -59,7 +59,8 @@ enum {
  * group of at most 8 query heads; gamma_max in [2, 16]; hidden, intermediate,
  * num_q_heads*head_dim and num_taps*target_hidden multiples of 256; hidden <= 8192;
  * max_batch in [1, 32];
- * max_seq_len in [1, 2^28]. Positions (stamped and RoPE) lie in [0, 2^30). */
+ * max_seq_len >= 1 with max_seq_len + gamma_max + 1 <= 262144. Positions (stamped and RoPE)
+ * lie in [0, 2^30). */
 typedef struct {
   int32_t num_layers, hidden, num_q_heads, num_kv_heads, head_dim, intermediate, vocab;
   int32_t num_taps, target_hidden; /* fc in_features = num_taps * target_hidden */

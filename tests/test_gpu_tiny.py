@@ -151,6 +151,34 @@ def test_wide_rows_parity_yarn_window(tiny):
     pair.close()
 
 
+def test_many_bands_many_chunks_window(tiny):
+    """32 bands of 4900-5000 keys (17-20 attention chunks each; the sliding-window layer,
+    window 4200, starts its chunks past the hidden keys and masks inside the first one) under
+    YaRN: checked against the oracle, and bit for bit against single-band calls."""
+    m, W = tiny
+    my = dict(m, rope_type="yarn", yarn_factor=4.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,
+              yarn_beta_slow=1.0, sliding_window=4200, layer_sliding=[True, False])
+    nb = 32
+    pair = Pair(my, W, 5200, nb)
+    lens = [4900 + (37 * s) % 101 for s in range(nb)]
+    for s in range(nb):
+        pair.append(s, synth.gen_hidden(m, SEED, lens[s], 400 + s))
+    agree = Agreement()
+    bonus = synth.gen_bonus(m, SEED, nb, index=500)
+    toks, logits, ref = pair.forward(list(range(nb)), bonus)
+    agree.add(toks, logits, ref)
+    agree.check(min_positions=400)
+    V = m["vocab"]
+    for s in (0, 13, 31):
+        t1 = torch.empty((1, 15), dtype=torch.int32, device=DEV)
+        l1 = torch.empty((15, V), dtype=torch.float32, device=DEV)
+        pair.gpu.dflash_block_forward([s], [bonus[s]], t1, l1)
+        torch.cuda.synchronize()
+        assert np.array_equal(t1[0].cpu().numpy(), toks[s])
+        assert np.array_equal(l1.cpu().numpy().astype(np.float64), logits[s])
+    pair.close()
+
+
 def test_yarn_and_sliding_window(tiny):
     m, W = tiny
     my = dict(m, rope_type="yarn", yarn_factor=4.0, yarn_orig_max_pos=64.0, yarn_beta_fast=32.0,

@@ -64,8 +64,11 @@ def test_create_rejects_unsupported_shapes_before_any_gpu_call(change):
 def test_create_rejects_bad_pool_arguments():
     m = synth.model("tiny-L2-h256")
     w, lay = _null_weights(m)
-    for kw in [dict(max_batch=0), dict(max_batch=33), dict(num_pages=1)]:
-        cfg, keep = B.make_config(m, 128, kw.get("max_batch", 1), num_pages=kw.get("num_pages", 0))
+    # (max_seq_len + gamma_max + 1 must stay within 262144: an attention chunk's page ids
+    # fit the kernel's table)
+    for kw in [dict(max_batch=0), dict(max_batch=33), dict(num_pages=1), dict(max_seq=262144 - 16),
+               dict(max_seq=0)]:
+        cfg, keep = B.make_config(m, kw.get("max_seq", 128), kw.get("max_batch", 1), num_pages=kw.get("num_pages", 0))
         ctx = C.c_void_p()
         assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
     # a page order that is not a permutation of 1..P-1 (P = 11 here)
