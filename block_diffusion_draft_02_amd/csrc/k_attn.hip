@@ -28,6 +28,7 @@ constexpr int KP = AW * KW;      // keys of one workgroup pass
 constexpr int RG = 32;           // query rows per workgroup: two 16-row tiles
 constexpr int RPAD = 128;        // query-row slots of one (chunk, kv head) partial
 constexpr int NCH_MAX = 64;      // chunks of one band that k_attn_combine accepts
+constexpr float RESCALE_LOG2 = 8.f;  // headroom of the lazily moved softmax reference maximum
 // ATTN_CHUNK_PAGES_MAX (kernels.hpp): page ids of a chunk, all staged in LDS
 
 // LDS: the workgroup's query rows (hi, lo) during the key loop, then the four waves'
@@ -139,17 +140,22 @@ __device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const At
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run[rt], tmax);
-    // rescale the running output only when some row's maximum moved
-    if (__any(m_new > m_run[rt])) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run[rt] - m_new) * scale_log2);
+    // m_run is the row's reference maximum, not always the exact one: it moves (and the
+    // running sum and output are rescaled) only when a score would exceed it by more than
+    // 2^RESCALE_LOG2, so probabilities stay below 2^8 (exact in the fp32 sums and in bf16
+    // range) and after the first slices the 64-register rescale almost never runs
+    const bool move = tmax > m_run[rt] && (m_run[rt] == -INFINITY || (tmax - m_run[rt]) * scale_log2 > RESCALE_LOG2);
+    if (__any(move)) {
+      const float m_new = move ? tmax : m_run[rt];
+      const float alpha = (m_new == -INFINITY || m_run[rt] == m_new) ? 1.f
+                                                                     : __builtin_amdgcn_exp2f((m_run[rt] - m_new) * scale_log2);
       l_run[rt] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) o[rt][dt] *= alpha;
+      m_run[rt] = m_new;
     }
-    m_run[rt] = m_new;
     // a row with every key so far hidden keeps m = -inf: its hidden scores still give 2^-inf = 0
-    const float bias = (m_new == -INFINITY) ? 0.f : -m_new * scale_log2;
+    const float bias = (m_run[rt] == -INFINITY) ? 0.f : -m_run[rt] * scale_log2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, bias));
