@@ -181,7 +181,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path would shard data-parallel over sequences, see DESIGN.md)", file=sys.stderr)
+              f"(the path would shard data-parallel over sequences, each GPU serving its own bands)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -312,28 +313,40 @@ def main():
 
 def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     """16 sequences with contexts U[512, 8192] on a shared pool with permuted pages; a step
-    appends `a` rows to every sequence and runs one 16-band forward. Same weights as the
-    batch-1 line (the shapes, not the draws, set the cost)."""
+    appends `a` rows to every sequence in one batched append (the batched context
+    precompute) and runs one 16-band forward. Same weights as the batch-1 line (the shapes,
+    not the draws, set the cost). Also times the batched append alone against the same rows
+    appended sequence by sequence."""
     w = synth.workload(WORKLOAD_B16)
     nb = w["batch"]
     dev = torch.device("cuda:0")
     lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, w["seed"])
     steps = max(5, args.steps // 2)
     total = args.warmup + steps
-    max_seq = int(lens.max()) + total * a + gamma + 16
+    app_reps = 10
+    max_seq = int(lens.max()) + (total + 2 * app_reps) * a + gamma + 16
     per_seq = -(-(max_seq + gamma + 1) // 16)
     order = synth.gen_page_order(per_seq * nb, w["seed"])
     d = B.Drafter(m, Wd, max_seq, nb, page_order=order)
     for s in range(nb):
         d.dflash_ctx_kv_append(s, to_dev(synth.gen_hidden(m, w["seed"], int(lens[s]), s)))
-    Hs = to_dev(synth.gen_hidden(m, w["seed"], total * a, 100))
+    # per step, the rows of all sequences one after another (as the batched call takes them)
+    Hb = to_dev(synth.gen_hidden(m, w["seed"], (total + 2 * app_reps) * nb * a, 100))
     bonus = synth.gen_bonus(m, w["seed"], nb * total)
     toks = torch.empty((nb, gamma - 1), dtype=torch.int32, device=dev)
     seqs = list(range(nb))
+    batched = nb * a <= 256
+
+    def append(i, per_seq_loop=False):
+        rows = Hb[i * nb * a:(i + 1) * nb * a]
+        if batched and not per_seq_loop:
+            d.dflash_ctx_kv_append_batch(seqs, [a] * nb, rows)
+        else:
+            for j, s in enumerate(seqs):
+                d.dflash_ctx_kv_append(s, rows[j * a:(j + 1) * a])
 
     def step(i):
-        for s in seqs:
-            d.dflash_ctx_kv_append(s, Hs[i * a:(i + 1) * a])
+        append(i)
         d.dflash_block_forward(seqs, bonus[i * nb:(i + 1) * nb], toks, gamma=gamma)
 
     for i in range(args.warmup):
@@ -347,9 +360,19 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     el = time.perf_counter() - t0
     br = d.dflash_timing_read()
     d.dflash_timing([])
+    # the append alone: one batched call against the sequence-by-sequence loop, same rows
+    app = {}
+    for mode, first in (("batched", total), ("per_seq", total + app_reps)):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for r in range(app_reps):
+            append(first + r, per_seq_loop=(mode == "per_seq"))
+        torch.cuda.synchronize()
+        app[mode] = (time.perf_counter() - t1) / app_reps * 1e3
     d.close()
     blocks = nb * steps / el
-    log(f"[bench] batch16: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step")
+    log(f"[bench] batch16: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; append of {nb}x{a} rows: "
+        f"batched {app['batched']:.3f} ms, per sequence {app['per_seq']:.3f} ms")
     gemm_ms = br["gemm"][0] / steps
     M = nb * gamma
     gemm_flop = 2 * M * gemm_weight_elems(m)
@@ -360,6 +383,9 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     return dict(workload=WORKLOAD_B16, value=round(blocks, 2), unit="blocks/s", steps=steps,
                 ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
                 ctx_lengths=[int(x) for x in lens], timing="all launch classes bracketed by events",
+                append=dict(rows=nb * a, form="one batched call" if batched else "per sequence",
+                            batched_ms=round(app["batched"], 4), per_seq_loop_ms=round(app["per_seq"], 4),
+                            timing="wall clock, 10 calls, nothing bracketed"),
                 layer_gemms=gemm_stats,
                 kernels_ms_per_step={k: round(v[0] / steps, 4) for k, v in br.items() if v[1]})
 

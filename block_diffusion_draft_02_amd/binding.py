@@ -57,6 +57,7 @@ def lib():
         vp, i32, i64p, i32p = C.c_void_p, C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int32)
         L.dflash_create.argtypes = [C.POINTER(dflash_config), C.POINTER(dflash_weights), vp, C.POINTER(vp)]
         L.dflash_ctx_kv_append.argtypes = [vp, i32, vp, i32p, i32, vp]
+        L.dflash_ctx_kv_append_batch.argtypes = [vp, i32, i32p, i32p, vp, i32p, vp]
         L.dflash_block_forward.argtypes = [vp, i32, i32p, i32p, i32p, i32, vp, vp, vp]
         L.dflash_destroy.argtypes = [vp]
         L.dflash_destroy.restype = None
@@ -70,7 +71,8 @@ def lib():
         L.dflash_timing_read.argtypes = [vp, C.POINTER(C.c_double), i64p, i32]
         L.dflash_strerror.argtypes = [C.c_int]
         L.dflash_strerror.restype = C.c_char_p
-        for f in ("dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_seq_reset",
+        for f in ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch", "dflash_block_forward",
+                  "dflash_seq_reset",
                   "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy", "dflash_timing",
                   "dflash_timing_read"):
             getattr(L, f).restype = C.c_int
@@ -78,7 +80,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_block_forward", "dflash_destroy",
+EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch", "dflash_block_forward",
+            "dflash_destroy",
             "dflash_seq_reset", "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy",
             "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
 
@@ -176,6 +179,15 @@ class Drafter:
         n = int(target_hidden.shape[0])
         pos = _i32_array(positions)
         self._check(self.L.dflash_ctx_kv_append(self.ctx, seq, _ptr(target_hidden), pos, n, _stream(stream)))
+
+    def dflash_ctx_kv_append_batch(self, seqs, counts, target_hidden, positions=None, stream=None):
+        """New rows of several sequences in one pass: target_hidden holds sum(counts) rows,
+        the sequences' rows one after another in the order of seqs."""
+        if int(target_hidden.shape[0]) != int(sum(counts)):
+            raise ValueError("target_hidden must hold sum(counts) rows")
+        s, n, pos = _i32_array(seqs), _i32_array(counts), _i32_array(positions)
+        self._check(self.L.dflash_ctx_kv_append_batch(self.ctx, len(seqs), s, n, _ptr(target_hidden), pos,
+                                                      _stream(stream)))
 
     def dflash_block_forward(self, seqs, bonus, draft_tokens, logits=None, q_rope_pos=None,
                              gamma=None, stream=None):

@@ -358,14 +358,16 @@ struct WideOut {
   float* logits;       //   drafted rows' logits [rows][N] or null
 };
 
-template <bool ARGMAX, bool NORM>
+// SPLIT: the activation carries a lo term (A_lo); without it A is exact bf16 (the context
+// append's target hidden states) and each step is one MFMA.
+template <bool ARGMAX, bool NORM, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(
     const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda, int M,
     const bf16* __restrict__ W, int N, int K, int gx, int gy, WideOut o) {
   constexpr int WM = WD_M / 16;
   constexpr int PPR = WD_KC / 8;                 // 16-byte pieces per row and term
   constexpr int PT = WD_M * PPR / 256;           // pieces per thread and term
-  __shared__ __attribute__((aligned(16))) bf16 sa[2][2][WD_M][WD_KC + WD_APAD];
+  __shared__ __attribute__((aligned(16))) bf16 sa[2][SPLIT ? 2 : 1][WD_M][WD_KC + WD_APAD];
   __shared__ float srs[NORM ? WD_M : 1];
   __shared__ float sv[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
   __shared__ int si[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
@@ -417,21 +419,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       w[1][s] = ld8(wp1 + off + s * 512);
     }
   };
-  auto load_a = [&](u32x4 (&ra)[2][PT], int k) {
+  constexpr int NT = SPLIT ? 2 : 1;   // activation terms
+  auto load_a = [&](u32x4 (&ra)[NT][PT], int k) {
 #pragma unroll
     for (int v = 0; v < PT; ++v) {
       const int p = threadIdx.x + 256 * v;
       const size_t src = (size_t)min(m0 + p / PPR, M - 1) * lda + k + (p % PPR) * 8;   // rows >= M repeat the last row
       ra[0][v] = *reinterpret_cast<const u32x4*>(A + src);
-      ra[1][v] = *reinterpret_cast<const u32x4*>(A_lo + src);
+      if (SPLIT) ra[NT - 1][v] = *reinterpret_cast<const u32x4*>(A_lo + src);
     }
   };
-  auto store_a = [&](const u32x4 (&ra)[2][PT], int buf) {
+  auto store_a = [&](const u32x4 (&ra)[NT][PT], int buf) {
 #pragma unroll
     for (int v = 0; v < PT; ++v) {
       const int p = threadIdx.x + 256 * v;
-      *reinterpret_cast<u32x4*>(&sa[buf][0][p / PPR][(p % PPR) * 8]) = ra[0][v];
-      *reinterpret_cast<u32x4*>(&sa[buf][1][p / PPR][(p % PPR) * 8]) = ra[1][v];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<u32x4*>(&sa[buf][t][p / PPR][(p % PPR) * 8]) = ra[t][v];
     }
   };
   f32x4 acc[WM][2];
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int s = 0; s < WD_KC / 32; ++s) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         bf16x8 av[WM];
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt)
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   };
 
   bf16x8 w0[2][2], w1[2][2];
-  u32x4 ra[2][PT];
+  u32x4 ra[NT][PT];
   load_a(ra, kb);
   load_w(w0, kb);
   store_a(ra, 0);
@@ -577,16 +580,19 @@ int gemm_wide_groups(int K, int gsz) { return (K / 256 + gsz - 1) / gsz; }
 
 hipError_t launch_gemm_wide(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
                             int gsz, float* P, long long part_stride, hipStream_t st, const NormIn* norm) {
-  if (M < 1 || !A_lo || N < 16 || N % 16 || K < 256 || K % 256 || gsz < 1) return hipErrorInvalidValue;
-  if (norm && (norm->h != K || K > SSQ_STRIDE * SSQ_COLS)) return hipErrorInvalidValue;
+  if (M < 1 || N < 16 || N % 16 || K < 256 || K % 256 || gsz < 1) return hipErrorInvalidValue;
+  if (norm && (!A_lo || norm->h != K || K > SSQ_STRIDE * SSQ_COLS)) return hipErrorInvalidValue;
   const int gx = (N + WD_N - 1) / WD_N, gy = (M + WD_M - 1) / WD_M, gz = gemm_wide_groups(K, gsz);
   WideOut o{};
   o.P = P; o.ps = part_stride; o.gsz = gsz;
+  const unsigned grid = wide_grid(gx, gy, gz);
   if (norm) {
     o.nrm = *norm;
-    (void)launch(k_gemm_wide<false, true>, wide_grid(gx, gy, gz), 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+    (void)launch(k_gemm_wide<false, true, true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+  } else if (A_lo) {
+    (void)launch(k_gemm_wide<false, false, true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
   } else {
-    (void)launch(k_gemm_wide<false, false>, wide_grid(gx, gy, gz), 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+    (void)launch(k_gemm_wide<false, false, false>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
   }
   return hipGetLastError();
 }
@@ -600,7 +606,7 @@ hipError_t launch_lmhead_wide(const bf16* Y, const bf16* Y_lo, int ldy, int M, c
   WideOut o{};
   o.best_v = best_v; o.best_i = best_i; o.n_groups = n_groups; o.gamma = gamma; o.logits = logits;
   const int gy = (M + WD_M - 1) / WD_M;
-  (void)launch(k_gemm_wide<true, false>, wide_grid(n_groups, gy, 1), 256, 0, st, Y, Y_lo, ldy, M, W, V, K,
+  (void)launch(k_gemm_wide<true, false, true>, wide_grid(n_groups, gy, 1), 256, 0, st, Y, Y_lo, ldy, M, W, V, K,
                n_groups, gy, o);
   return hipGetLastError();
 }

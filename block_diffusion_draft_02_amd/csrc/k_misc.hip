@@ -285,30 +285,55 @@ hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, i
   return hipGetLastError();
 }
 
+// the batched form: thread r finds its sequence by the row offsets (at most MAX_BANDS)
+__global__ __launch_bounds__(256) void k_append_batch_setup(AppendBatchArgs a, int* __restrict__ bt,
+                                                            long long* __restrict__ slots,
+                                                            int* __restrict__ rowpos,
+                                                            int* __restrict__ kpos) {
+  for (int j = threadIdx.x; j < a.n_upd; j += 256) bt[a.upd_off[j]] = a.upd_page[j];
+  for (int r = threadIdx.x; r < a.n_rows; r += 256) {
+    int b = 0;
+    while (b + 1 < a.n_seqs && r >= a.row0[b + 1]) ++b;
+    const int p = a.kv_len[b] + r - a.row0[b];
+    const long long slot = (long long)a.pages[a.pg0[b] + (p >> 4) - a.lp0[b]] * PAGE + (p & (PAGE - 1));
+    const int pos = a.positions ? a.positions[r] : p;
+    slots[r] = slot;
+    rowpos[r] = pos;
+    kpos[slot] = pos;
+  }
+}
+
+hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long long* slots, int* rowpos,
+                                     int* kpos, hipStream_t st) {
+  if (a.n_seqs < 1 || a.n_seqs > MAX_BANDS || a.n_rows < 1 || a.n_rows > APPEND_BATCH_ROWS) return hipErrorInvalidValue;
+  (void)launch(k_append_batch_setup, 1, 256, 0, st, a, bt, slots, rowpos, kpos);
+  return hipGetLastError();
+}
+
 // one workgroup per row: the sum of the row's S split-K partials, RMSNorm'd
 __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__ X, int S, long long ps,
-                                                       int h, const bf16* __restrict__ w, float eps,
+                                                       int gsz, int h, const bf16* __restrict__ w, float eps,
                                                        bf16* __restrict__ out,
                                                        bf16* __restrict__ out_lo) {
   __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
   __shared__ float red_ss[16];
   const int r = blockIdx.x;
-  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, S, h, xs, red_ss);
+  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, gsz, h, xs, red_ss);
   const float rs = rsqrtf(tot / (float)h + eps);
   norm_out(xs, h, rs, w, out + (size_t)r * h, out_lo + (size_t)r * h);
 }
 
-hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int M, int h,
+hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st) {
-  if (h > RN_HMAX || h % 4) return hipErrorInvalidValue;
-  (void)launch(k_rows_rmsnorm, M, 1024, 0, st, X, S, part_stride, h, w, eps, out, out_lo);
+  if (h > RN_HMAX || h % 4 || gsz < 1) return hipErrorInvalidValue;
+  (void)launch(k_rows_rmsnorm, M, 1024, 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo);
   return hipGetLastError();
 }
 
 // one wavefront per (row, layer, K|V, kv head) of the fused [K0 | V0 | K1 | V1 | ...] output
 template <int HD>
 __global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__ KV, int S,
-                                                       long long ps, int L,
+                                                       long long ps, int gsz, int L,
                                                        const bf16* __restrict__ kn_all, float eps,
                                                        const double* __restrict__ inv_freq,
                                                        float mscale,
@@ -322,8 +347,8 @@ __global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__
   const bool act = l < H2;
   const size_t ld = (size_t)L * 2 * nkv * HD;
   const float* src = KV + (size_t)r * ld + (size_t)idx * HD;
-  float x1 = act ? sum_splits<8, float>(src + l, S, ps, S) : 0.f;
-  float x2 = act ? sum_splits<8, float>(src + l + H2, S, ps, S) : 0.f;
+  float x1 = act ? sum_splits<8, float>(src + l, S, ps, gsz) : 0.f;
+  float x2 = act ? sum_splits<8, float>(src + l + H2, S, ps, gsz) : 0.f;
   if (kv == 0) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float rs = rsqrtf(ss / (float)HD + eps);
@@ -352,16 +377,17 @@ __global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__
   }
 }
 
-hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int n, int L,
+hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int gsz, int n, int L,
                                  const bf16* k_norm_all,
                                  float eps, const double* inv_freq, float mscale,
                                  const long long* slots, const int* rowpos, KvGeom g,
                                  hipStream_t st) {
+  if (gsz < 1) return hipErrorInvalidValue;
   dim3 grid(n, L * 2 * g.nkv);
   switch (g.hd) {
-    case 32: (void)launch(k_kv_append_post<32>, grid, 64, 0, st, KV, S, part_stride, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
-    case 64: (void)launch(k_kv_append_post<64>, grid, 64, 0, st, KV, S, part_stride, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
-    case 128: (void)launch(k_kv_append_post<128>, grid, 64, 0, st, KV, S, part_stride, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 32: (void)launch(k_kv_append_post<32>, grid, 64, 0, st, KV, S, part_stride, gsz, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 64: (void)launch(k_kv_append_post<64>, grid, 64, 0, st, KV, S, part_stride, gsz, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 128: (void)launch(k_kv_append_post<128>, grid, 64, 0, st, KV, S, part_stride, gsz, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

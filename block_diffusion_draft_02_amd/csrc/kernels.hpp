@@ -78,6 +78,22 @@ struct AppendArgs {
   const int* positions;        // device int32 [n] or nullptr (kv_len + r)
 };
 
+// A batched append: new rows of up to MAX_BANDS sequences in one pass, seq-major (rows
+// row0[b] .. row0[b+1]-1 belong to sequence seq[b] and go to its positions kv_len[b] ...).
+constexpr int APPEND_BATCH_ROWS = 256;
+constexpr int APPEND_BATCH_PAGES = APPEND_BATCH_ROWS / PAGE + 2 * MAX_BANDS;
+struct AppendBatchArgs {
+  int n_seqs, n_rows, per_seq;
+  int seq[MAX_BANDS], kv_len[MAX_BANDS], row0[MAX_BANDS + 1];
+  int lp0[MAX_BANDS];            // first logical page the sequence's rows touch
+  int pg0[MAX_BANDS];            // where that page's physical id sits in pages[]
+  int pages[APPEND_BATCH_PAGES];
+  int n_upd;                     // block-table entries to write: bt[upd_off] = upd_page
+  int upd_off[APPEND_BATCH_PAGES];
+  int upd_page[APPEND_BATCH_PAGES];
+  const int* positions;          // device int32 [n_rows] or nullptr (kv_len[b] + i)
+};
+
 // Geometry the attention / writeback kernels need.
 struct KvGeom {
   bf16* pool;        // [L][num_pages][2][nkv] x (K [16][hd] | V [hd][16])
@@ -97,8 +113,8 @@ __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (si
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                               int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
                               hipStream_t st, const NormIn* norm = nullptr);
-// Wide form for more than 64 rows (A_lo required, W in the T16 layout, K a multiple of
-// 256, N of 16): partials P[z][M][N] (z < gemm_wide_groups(K, gsz), stride part_stride),
+// Wide form for more than 64 rows (A_lo optional: without it A is exact bf16; W in the T16
+// layout, K a multiple of 256, N of 16): partials P[z][M][N] (z < gemm_wide_groups(K, gsz), stride part_stride),
 // each the sum of the 256-deep split chains of group z (splits z*gsz .. z*gsz + gsz - 1)
 // as the consumers' canonical order forms it from the skinny kernel's per-split partials.
 int gemm_wide_groups(int K, int gsz);
@@ -172,10 +188,13 @@ hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const 
 // ---- context append (k_misc.hip) -----------------------------------------------------
 hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
                                int* kpos, hipStream_t st);
-// inputs are split-K partials X[s][M][...] (S = 1, part_stride unused for a plain result)
-hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int M, int h,
+hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long long* slots, int* rowpos,
+                                     int* kpos, hipStream_t st);
+// inputs are split-K partials X[s][M][...] added in the canonical order (S = 1, gsz = 1 for a
+// plain result)
+hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st);
-hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int n, int L,
+hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int gsz, int n, int L,
                                  const bf16* k_norm_all,
                                  float eps, const double* inv_freq, float mscale,
                                  const long long* slots, const int* rowpos, KvGeom g,

@@ -326,6 +326,57 @@ void release(dflash_ctx* c) {
 
 }  // namespace
 
+// fc + hidden_norm + the fused K/V GEMM + k_norm/RoPE/writeback for nc context rows whose
+// slots and positions are already on the device (c->slots, c->rowpos)
+int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st) {
+  const KvGeom g = geom(c);
+  const int nkv2 = c->L * 2 * c->kvd;
+  if (nc <= APPEND_BATCH_ROWS) {
+    // up to 64 rows: the weight-streaming skinny GEMMs, one partial per 256-deep split;
+    // up to 256: the wide GEMMs, one partial per split group. Both weights in the T16 layout,
+    // the partials added by the consumers.
+    const bool wide = nc > APPEND_SKINNY;
+    const long long ps_fc = (long long)nc * c->h, ps_kv = (long long)nc * nkv2;
+    const int S_fc = wide ? gemm_wide_groups(c->g_fc.K, c->g_fc.gsz) : c->g_fc.S;
+    const int G_fc = wide ? 1 : c->g_fc.gsz;
+    const int S_kv = wide ? gemm_wide_groups(c->g_kvapp.K, c->g_kvapp.gsz) : c->g_kvapp.S;
+    const int G_kv = wide ? 1 : c->g_kvapp.gsz;
+    HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+      return wide ? launch_gemm_wide(Hc, nullptr, ld, nc, c->fc_t, c->h, ld, c->g_fc.gsz, c->part, ps_fc, st)
+                  : launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc_t, c->h, ld, c->g_fc.klen, c->part, ps_fc, true, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+      return launch_rows_rmsnorm(c->part, S_fc, ps_fc, G_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+      return wide ? launch_gemm_wide(c->Fb, c->Fb_lo, c->h, nc, c->w_kv_t, nkv2, c->h, c->g_kvapp.gsz, c->part, ps_kv,
+                                     st)
+                  : launch_gemm_skinny(c->Fb, c->Fb_lo, c->h, nc, c->w_kv_t, nkv2, c->h, c->g_kvapp.klen, c->part,
+                                       ps_kv, true, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+      return launch_kv_append_post(c->part, S_kv, ps_kv, G_kv, nc, c->L, c->knorm_all, c->eps, c->inv_freq,
+                                   (float)c->mscale, c->slots, c->rowpos, g, st);
+    }));
+    return DFLASH_OK;
+  }
+  // many rows: the LDS-tiled GEMMs over the full K (MFMA-bound), plain fp32 results
+  HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+    return launch_gemm_tiled(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->F32, c->h, st);
+  }));
+  HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+    return launch_rows_rmsnorm(c->F32, 1, 0, 1, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st);
+  }));
+  HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+    return launch_gemm_tiled(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->KV32, nkv2, st);
+  }));
+  HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+    return launch_kv_append_post(c->KV32, 1, 0, 1, nc, c->L, c->knorm_all, c->eps, c->inv_freq, (float)c->mscale,
+                                 c->slots, c->rowpos, g, st);
+  }));
+  return DFLASH_OK;
+}
+
 extern "C" {
 
 const char* dflash_strerror(int code) {
@@ -394,8 +445,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   size_t part = 0;
   for (const GemmPlan* g : {&c->g_qkv, &c->g_o, &c->g_gu, &c->g_down})
     part = std::max(part, (size_t)g->S * c->m_max * g->N);
-  for (const GemmPlan* g : {&c->g_fc, &c->g_kvapp})
+  for (const GemmPlan* g : {&c->g_fc, &c->g_kvapp}) {
     part = std::max(part, (size_t)g->S * APPEND_SKINNY * g->N);
+    part = std::max(part, (size_t)gemm_wide_groups(g->K, g->gsz) * APPEND_BATCH_ROWS * g->N);
+  }
   c->part_elems = part;
   c->lm_groups = lmhead_groups(c->V);
   {
@@ -590,7 +643,6 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
     c->free_pages.pop_front();
   }
   hipStream_t st = (hipStream_t)stream;
-  const KvGeom g = geom(c);
   const int ld = c->T * c->Ht;
   for (int r0 = 0; r0 < n; r0 += APPEND_ROWS) {
     const int nc = std::min(APPEND_ROWS, n - r0);
@@ -622,44 +674,104 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
     }
     HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] { return launch_append_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st); }));
     if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
-    const bf16* Hc = (const bf16*)target_hidden + (size_t)r0 * ld;
-    const int nkv2 = c->L * 2 * c->kvd;
-    if (nc <= APPEND_SKINNY) {
-      // few rows: weight-streaming GEMMs with split-K partials, reduced by the consumers
-      const long long ps_fc = (long long)nc * c->h, ps_kv = (long long)nc * nkv2;
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc_t, c->h, ld, c->g_fc.klen, c->part, ps_fc, true, st);
-      }));
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-        return launch_rows_rmsnorm(c->part, c->g_fc.S, ps_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
-                                   c->Fb_lo, st);
-      }));
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_skinny(c->Fb, c->Fb_lo, c->h, nc, c->w_kv_t, nkv2, c->h, c->g_kvapp.klen, c->part,
-                                  ps_kv, true, st);
-      }));
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-        return launch_kv_append_post(c->part, c->g_kvapp.S, ps_kv, nc, c->L, c->knorm_all, c->eps, c->inv_freq,
-                                     (float)c->mscale, c->slots, c->rowpos, g, st);
-      }));
-    } else {
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_tiled(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->F32, c->h, st);
-      }));
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-        return launch_rows_rmsnorm(c->F32, 1, 0, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st);
-      }));
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-        return launch_gemm_tiled(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->KV32, nkv2, st);
-      }));
-      HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-        return launch_kv_append_post(c->KV32, 1, 0, nc, c->L, c->knorm_all, c->eps, c->inv_freq, (float)c->mscale,
-                                     c->slots, c->rowpos, g, st);
-      }));
-    }
+    const int rc = append_chain(c, (const bf16*)target_hidden + (size_t)r0 * ld, ld, nc, st);
+    if (rc != DFLASH_OK) return rc;
   }
   for (int i = 0; i < n; ++i) s.pos.push_back(positions ? positions[i] : C + i);
   s.kv_len = C + n;
+  return DFLASH_OK;
+}
+
+int dflash_ctx_kv_append_batch(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int32_t* counts,
+                               const void* target_hidden, const int32_t* positions, void* stream) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  if (n_seqs < 1 || n_seqs > c->max_batch) return fail(c, DFLASH_EINVAL, "n_seqs %d not in [1, %d]", n_seqs, c->max_batch);
+  if (!seqs || !counts || !target_hidden) return fail(c, DFLASH_EINVAL, "NULL seqs, counts or target_hidden");
+  std::vector<char> seen(c->max_batch, 0);
+  long long total = 0;
+  int need = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    const int q = seqs[b];
+    if (q < 0 || q >= c->max_batch || seen[q]) return fail(c, DFLASH_ERANGE, "seq %d out of range or repeated", q);
+    seen[q] = 1;
+    if (counts[b] < 0) return fail(c, DFLASH_EINVAL, "counts must be >= 0");
+    const SeqState& s = c->seqs[q];
+    if ((long long)s.kv_len + counts[b] > c->max_seq)
+      return fail(c, DFLASH_ERANGE, "seq %d: kv_len %d + %d exceeds max_seq_len %d", q, s.kv_len, counts[b], c->max_seq);
+    total += counts[b];
+    need += std::max(0, (s.kv_len + counts[b] + PAGE - 1) / PAGE - (int)s.bt.size());
+  }
+  if (total < 1 || total > APPEND_BATCH_ROWS)
+    return fail(c, DFLASH_EINVAL, "total rows %lld not in [1, %d]", total, APPEND_BATCH_ROWS);
+  if (positions) {
+    long long r = 0;
+    for (int b = 0; b < n_seqs; ++b) {
+      const SeqState& s = c->seqs[seqs[b]];
+      long long last = s.pos.empty() ? -1 : s.pos.back();
+      for (int i = 0; i < counts[b]; ++i, ++r) {
+        if (positions[r] <= last || positions[r] >= (1LL << 30))
+          return fail(c, DFLASH_EINVAL, "positions must be strictly increasing per sequence, in [0, 2^30)");
+        last = positions[r];
+      }
+    }
+  }
+  if (need > (int)c->free_pages.size()) return fail(c, DFLASH_EPOOL, "KV pool exhausted (%d pages needed, %zu free)", need, c->free_pages.size());
+  // --- committed from here on: pages are taken in call order, each sequence's in logical order
+  AppendBatchArgs a{};
+  a.per_seq = c->per_seq;
+  a.n_rows = (int)total;
+  int np = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    if (counts[b] == 0) continue;
+    const int q = seqs[b];
+    SeqState& s = c->seqs[q];
+    const int old_pages = (int)s.bt.size();
+    const int want = (s.kv_len + counts[b] + PAGE - 1) / PAGE;
+    while ((int)s.bt.size() < want) {
+      s.bt.push_back(c->free_pages.front());
+      c->free_pages.pop_front();
+    }
+    const int k = a.n_seqs++;
+    a.seq[k] = q;
+    a.kv_len[k] = s.kv_len;
+    a.row0[k + 1] = a.row0[k] + counts[b];
+    a.lp0[k] = s.kv_len / PAGE;
+    a.pg0[k] = np;
+    for (int lp = a.lp0[k]; lp < want; ++lp) {
+      a.pages[np++] = s.bt[lp];
+      if (lp >= old_pages) {
+        a.upd_off[a.n_upd] = q * c->per_seq + lp;
+        a.upd_page[a.n_upd] = s.bt[lp];
+        ++a.n_upd;
+      }
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  a.positions = nullptr;
+  int slot = -1;
+  if (positions) {
+    slot = c->ring_next;
+    c->ring_next = (c->ring_next + 1) % RING;
+    HIPCHK(c, hipEventSynchronize(c->ring_ev[slot]));
+    int* hp = c->ring_host + (size_t)slot * APPEND_ROWS;
+    int* dp = c->ring_dev + (size_t)slot * APPEND_ROWS;
+    memcpy(hp, positions, (size_t)total * sizeof(int));
+    HIPCHK(c, hipMemcpyAsync(dp, hp, (size_t)total * sizeof(int), hipMemcpyHostToDevice, st));
+    a.positions = dp;
+  }
+  HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
+    return launch_append_batch_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st);
+  }));
+  if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
+  const int rc = append_chain(c, (const bf16*)target_hidden, c->T * c->Ht, (int)total, st);
+  if (rc != DFLASH_OK) return rc;
+  long long r = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    SeqState& s = c->seqs[seqs[b]];
+    for (int i = 0; i < counts[b]; ++i, ++r) s.pos.push_back(positions ? positions[r] : s.kv_len + i);
+    s.kv_len += counts[b];
+  }
   return DFLASH_OK;
 }
 

@@ -122,6 +122,27 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *strea
 int dflash_ctx_kv_append(dflash_ctx *ctx, int32_t seq, const void *target_hidden,
                          const int32_t *positions, int32_t n, void *stream);
 
+/* Batched incremental append (metrale_model_arch/dflash_head/from_weights.rs,
+ * DraftProposer::propose_batch with its one batched context precompute, the staging size
+ * PRECOMPUTE_BATCH_ROWS, and the per-sequence watermark DflashProposerState::ctx_committed):
+ * the new rows of several sequences in one pass of fc + hidden_norm and one fused K/V GEMM,
+ * so the append weights are streamed once per call instead of once per sequence. Sequence
+ * seqs[b] receives counts[b] rows (0 allowed) at its watermark kv_len; the result is the
+ * same as dflash_ctx_kv_append called for each sequence in turn (up to the rounding of the
+ * GEMM form chosen by the total row count), and pages are taken in call order, each
+ * sequence's in ascending logical order.
+ *   seqs, counts:  host int32 [n_seqs], seqs distinct;
+ *   target_hidden: device bf16 [sum(counts), num_taps*target_hidden], the sequences' rows
+ *                  one after another in call order;
+ *   positions:     host int32 [sum(counts)] in the same order, strictly increasing within
+ *                  each sequence and above its last stamped position; NULL means kv_len + i.
+ * At most 256 rows per call (sum(counts) in [1, 256]). Errors: ERANGE (seq out of range or
+ * repeated, kv_len + count > max_seq_len), EINVAL (n_seqs, NULL pointers, negative counts,
+ * total rows, positions), EPOOL; all checked before anything is enqueued. */
+int dflash_ctx_kv_append_batch(dflash_ctx *ctx, int32_t n_seqs, const int32_t *seqs,
+                               const int32_t *counts, const void *target_hidden,
+                               const int32_t *positions, void *stream);
+
 /* One gamma-block forward for n_seqs sequences at once (band b = seqs[b] owns rows
  * [b*gamma, (b+1)*gamma)). Row i of band b is token bonus_tokens[b] (i = 0) or
  * mask_token_id, at RoPE position q_rope_pos[b] + i (q_rope_pos NULL: the sequence's

@@ -14,11 +14,13 @@ Sources (page title -- section). Every function below names the one it follows.
             K/V weight layout.
   [atlas-head] spark_model/layers/dflash_head.rs -- DflashBatch (bands of gamma rows per
             sequence) and DraftProposer::propose_batch (drop row 0 of each band).
+  [metrale-fw] metrale_model_arch/dflash_head/from_weights.rs -- DraftProposer::propose_batch
+            (one batched context precompute), PRECOMPUTE_BATCH_ROWS,
+            DflashProposerState::ctx_committed (the per-sequence watermark).
 
 Arithmetic: numpy float64 by default (float32 on request, for timing only). Inputs
 arrive as bf16 bit patterns (uint16) and are widened exactly; no intermediate value is
-rounded. Where the pages leave a step open, the reading taken is marked READING and
-listed in DESIGN.md.
+rounded. Where the pages leave a step open, the reading taken is marked READING.
 
 Parity unpinned (no worked example on the pages fixes them): the sliding-window rule
 inside a non-causal block (READING c1 below) and the placement of the YaRN mscale when
@@ -496,6 +498,50 @@ class Engine:
             s["k"][l] = np.concatenate([s["k"][l], k], axis=0)
             s["v"][l] = np.concatenate([s["v"][l], v], axis=0)
         s["pos"] = np.concatenate([s["pos"], positions])
+
+    # rows one batched context precompute holds ([metrale-fw] PRECOMPUTE_BATCH_ROWS)
+    APPEND_BATCH_ROWS = 256
+
+    def ctx_kv_append_batch(self, seqs, counts, taps_bits: np.ndarray, positions=None):
+        """The batched incremental append ([metrale-fw] DraftProposer::propose_batch, its one
+        context precompute over every sequence's rows past the watermark
+        DflashProposerState::ctx_committed): by definition the per-sequence appends in call
+        order, after every check of the whole call has passed (pages are then taken in call
+        order). taps_bits holds sum(counts) rows, the sequences' rows one after another;
+        positions likewise (None: each sequence's kv_len + i)."""
+        seqs = [int(x) for x in seqs]
+        counts = [int(x) for x in counts]
+        if len(seqs) == 0 or len(seqs) > self.max_batch or len(counts) != len(seqs):
+            raise PoolError("EINVAL", "bad number of sequences")
+        if len(set(seqs)) != len(seqs) or any(not (0 <= x < self.max_batch) for x in seqs):
+            raise PoolError("ERANGE", "seq out of range or repeated")
+        if any(c < 0 for c in counts):
+            raise PoolError("EINVAL", "negative count")
+        for q, c in zip(seqs, counts):
+            if self.kv_len(q) + c > self.max_seq_len:
+                raise PoolError("ERANGE", "kv_len + count exceeds max_seq_len")
+        total = sum(counts)
+        if not (1 <= total <= self.APPEND_BATCH_ROWS) or int(taps_bits.shape[0]) != total:
+            raise PoolError("EINVAL", "total rows out of range")
+        if positions is not None:
+            positions = np.asarray(positions, dtype=np.int64)
+            r = 0
+            for q, c in zip(seqs, counts):
+                p = positions[r:r + c]
+                last = self.seqs[q]["pos"][-1] if self.kv_len(q) else -1
+                if c and (p[0] <= last or np.any(np.diff(p) <= 0) or p[-1] > np.iinfo(np.int32).max):
+                    raise PoolError("EINVAL", "positions must be strictly increasing")
+                r += c
+        need = sum(self.pool.pages_needed(q, self.kv_len(q) + c) for q, c in zip(seqs, counts))
+        if need > len(self.pool.free):
+            raise PoolError("EPOOL", "KV pool exhausted")
+        slots, r = [], 0
+        for q, c in zip(seqs, counts):
+            if c:
+                self.ctx_kv_append(q, taps_bits[r:r + c], None if positions is None else positions[r:r + c])
+                slots.append(self.last_slots)
+            r += c
+        self.last_slots = np.concatenate(slots)
 
     def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False):
         m = self.m

@@ -5,7 +5,7 @@ benchmark. It holds workload shapes and seeded random draws only: no step of the
 drafter's arithmetic lives here. Every tensor is returned as bf16 bit patterns
 (numpy uint16) so that both sides start from the same exact values.
 
-Recipe (also stated in the design doc):
+Recipe:
   * generator: numpy PCG64 seeded with SeedSequence([seed, stream, index]);
     float32 draws rounded to bf16 with round-to-nearest-even;
   * weight matrices ~ N(0, 0.02); norm weights ~ 1 + N(0, 0.02);

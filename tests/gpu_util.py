@@ -42,6 +42,10 @@ class Pair:
         self.gpu.dflash_ctx_kv_append(seq, dev_bf16(H), positions=positions)
         self.ora.ctx_kv_append(seq, H, positions=positions)
 
+    def append_batch(self, seqs, counts, H, positions=None):
+        self.gpu.dflash_ctx_kv_append_batch(seqs, counts, dev_bf16(H), positions=positions)
+        self.ora.ctx_kv_append_batch(seqs, counts, H, positions=positions)
+
     def forward(self, seqs, bonus, q_rope_pos=None, gamma=None):
         gamma = self.m["gamma_max"] if gamma is None else gamma
         n = len(seqs)

@@ -8,7 +8,7 @@ import torch
 import synth
 from block_diffusion_draft_02_amd import binding as B
 from oracle import dflash_oracle as O
-from gpu_util import Agreement, Pair, dev_bf16, pool_view, read_i32, read_i64, DEV
+from gpu_util import Agreement, Pair, dev_bf16, pool_view, read_i32, read_i64, read_slot_kv, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +95,36 @@ def test_batch16_full_contexts_band_invariance(qwen3):
         assert torch.equal(t1[0], tb[s]) and torch.equal(l1, lb[s * 15:(s + 1) * 15])
     assert int(tb.min()) >= 0 and int(tb.max()) < V
     d.close()
+
+
+def test_batched_append_16x16_full_shape(qwen3):
+    """The batched context precompute at the drafter's full shape: 16 sequences x 16 new rows
+    (256 rows: the wide GEMMs over fc's 10240-deep input and the fused K/V weight) in one call,
+    against the oracle's per-sequence appends; then the 16-band forward."""
+    m, W, seed = qwen3
+    nb = 16
+    P = O.pool_pages(512, 16, nb)[1]
+    pair = Pair(m, W, 512, nb, page_order=synth.gen_page_order(P - 1, seed + 3))
+    lens = synth.gen_ctx_lengths(1, 200, nb, seed + 1)
+    for s in range(nb):
+        pair.append(s, synth.gen_hidden(m, seed, int(lens[s]), 200 + s))
+    seqs = list(range(nb))[::-1]
+    pair.append_batch(seqs, [16] * nb, synth.gen_hidden(m, seed, 16 * nb, 300))
+    assert np.array_equal(read_i64(pair.gpu, B.DFLASH_BUF_SLOTS, 16 * nb), pair.ora.last_slots)
+    hd, nkv = m["head_dim"], m["num_kv_heads"]
+    for s in (0, 7, 15):
+        kv, bt = pair.gpu.dflash_seq_info(s)
+        assert kv == pair.ora.kv_len(s) and bt == pair.ora.block_table(s)
+        rows = np.array([kv - 16, kv - 9, kv - 1])
+        slots = pair.ora.pool.slots(s, rows)
+        for l in (0, m["num_layers"] - 1):
+            K, V = read_slot_kv(pair.gpu, l, slots)
+            st = pair.ora.seqs[s]
+            for got, want in ((K, st["k"][l][rows]), (V, st["v"][l][rows])):
+                assert np.abs(O.widen(got) - want).max() <= 2e-2 * np.abs(want).max()
+    agree = Agreement()
+    toks, logits, ref = pair.forward(seqs, synth.gen_bonus(m, seed, nb, index=91))
+    agree.add(toks, logits, ref)
+    rate = agree.check(min_positions=200)
+    print(f"batched append + forward: {agree.n} positions, agreement {rate:.4f}, max rel dlogit {agree.max_rel:.3e}")
+    pair.close()

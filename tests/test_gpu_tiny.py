@@ -219,6 +219,95 @@ def test_long_append_crosses_launch_chunks(tiny):
     pair.close()
 
 
+@pytest.mark.parametrize("counts", [[3, 0, 16, 1, 37], [16, 16, 16, 16, 16, 16, 16, 16], [60, 1, 100, 95]])
+def test_batched_append_matches_oracle(tiny, counts):
+    """One batched append over several sequences (totals of 57, 128 and 256 rows: the skinny
+    and the wide GEMM forms), with caller positions on one sequence and a sequence given no
+    rows: slots, block tables and stamped positions bit for bit, every cached K/V row against
+    the oracle, then forwards over all of them."""
+    m, W = tiny
+    nb = len(counts)
+    P = O.pool_pages(400, 16, nb)[1]
+    pair = Pair(m, W, 400, nb, page_order=synth.gen_page_order(P - 1, SEED + 7))
+    for s in range(nb):
+        if s % 2 == 0:
+            pair.append(s, synth.gen_hidden(m, SEED, 5 + 11 * s, 70 + s))
+    H = synth.gen_hidden(m, SEED, sum(counts), 90)
+    pos = None
+    if nb > 4:
+        # caller positions, gapped, on sequence 1 only (the others continue from kv_len)
+        pos = []
+        for s, c in enumerate(counts):
+            base = pair.ora.kv_len(s)
+            last = int(pair.ora.seqs[s]["pos"][-1]) if base else -1
+            pos += [last + 3 + 2 * i for i in range(c)] if s == 1 else list(range(base, base + c))
+    seqs = list(range(nb))[::-1]
+    order_counts = [counts[s] for s in seqs]
+    Hs = np.concatenate([H[sum(counts[:s]):sum(counts[:s + 1])] for s in seqs]) if nb else H
+    ps = None
+    if pos is not None:
+        ps = np.concatenate([np.asarray(pos[sum(counts[:s]):sum(counts[:s + 1])], dtype=np.int64) for s in seqs])
+    pair.append_batch(seqs, order_counts, Hs, positions=ps)
+    total = sum(counts)
+    assert np.array_equal(read_i64(pair.gpu, B.DFLASH_BUF_SLOTS, total), pair.ora.last_slots)
+    geo = pair.gpu.dflash_pool_geometry()
+    dev_bt = read_i32(pair.gpu, B.DFLASH_BUF_BLOCKTAB, nb * geo["pages_per_seq"]).reshape(nb, -1)
+    for s in range(nb):
+        kv, bt = pair.gpu.dflash_seq_info(s)
+        assert kv == pair.ora.kv_len(s) and bt == pair.ora.block_table(s)
+        assert list(dev_bt[s, :len(bt)]) == bt
+    pool = pool_view(pair.gpu)
+    kpos = read_i32(pair.gpu, B.DFLASH_BUF_KPOS, geo["num_pages"] * 16)
+    for s in range(nb):
+        if pair.ora.kv_len(s):
+            _check_seq_pool(pair, s, pool, kpos)
+    agree = Agreement()
+    live = [s for s in range(nb) if pair.ora.kv_len(s)]
+    for call in range(3):
+        toks, logits, ref = pair.forward(live, synth.gen_bonus(m, SEED, len(live), index=600 + call))
+        agree.add(toks, logits, ref)
+    agree.check()
+    pair.close()
+
+
+def test_batched_append_errors_change_nothing(tiny):
+    """Every refused batched append leaves block tables, kv_len and the pool as they were."""
+    m, W = tiny
+    pair = Pair(m, W, 300, 3, num_pages=9)             # 8 allocatable pages
+    pair.append(0, synth.gen_hidden(m, SEED, 30, 80))   # 2 pages
+    pair.append(1, synth.gen_hidden(m, SEED, 10, 81))   # 1 page: 5 left
+    before = [pair.gpu.dflash_seq_info(s) for s in range(3)]
+    H = dev_bf16(synth.gen_hidden(m, SEED, 257, 82))
+    cases = [
+        (dict(seqs=[0, 0], counts=[1, 1]), "ERANGE"),          # repeated sequence
+        (dict(seqs=[3], counts=[1]), "ERANGE"),                 # out of range
+        (dict(seqs=[1, 0], counts=[1, 271]), "ERANGE"),         # 30 + 271 > max_seq_len 300
+        (dict(seqs=[1, 2], counts=[-1, 2]), "EINVAL"),          # negative count
+        (dict(seqs=[1, 2], counts=[0, 0]), "EINVAL"),           # no rows
+        (dict(seqs=[1, 2], counts=[200, 57]), "EINVAL"),        # 257 rows > 256 per call
+        (dict(seqs=[1, 2], counts=[40, 40]), "EPOOL"),          # 3 + 3 pages, 5 free
+    ]
+    for kw, name in cases:
+        # the C entry directly (the binding would refuse a row-count mismatch itself)
+        rc = pair.gpu.L.dflash_ctx_kv_append_batch(pair.gpu.ctx, len(kw["seqs"]), B._i32_array(kw["seqs"]),
+                                                   B._i32_array(kw["counts"]), B._ptr(H), None, None)
+        assert rc == getattr(B, "DFLASH_" + name), (kw, rc)
+    with pytest.raises(B.DflashError) as ei:           # positions not increasing within sequence 1
+        pair.gpu.dflash_ctx_kv_append_batch([1, 2], [2, 1], H[:3], positions=[40, 39, 0])
+    assert ei.value.name == "EINVAL"
+    with pytest.raises(B.DflashError) as ei:           # at or below sequence 1's last position
+        pair.gpu.dflash_ctx_kv_append_batch([1], [1], H[:1], positions=[9])
+    assert ei.value.name == "EINVAL"
+    assert [pair.gpu.dflash_seq_info(s) for s in range(3)] == before
+    # still exact afterwards
+    pair.append_batch([2, 1], [5, 7], synth.gen_hidden(m, SEED, 12, 84))
+    agree = Agreement()
+    toks, logits, ref = pair.forward([0, 1, 2], synth.gen_bonus(m, SEED, 3, index=700))
+    agree.add(toks, logits, ref)
+    agree.check()
+    pair.close()
+
+
 def test_errors_change_nothing_and_reset_reuses_pages(tiny):
     m, W = tiny
     pair = Pair(m, W, 64, 2, num_pages=6)

@@ -89,6 +89,7 @@ def test_null_arguments():
     lay[1].down_proj = None
     assert L.dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
     assert L.dflash_ctx_kv_append(None, 0, None, None, 1, None) == B.DFLASH_EINVAL
+    assert L.dflash_ctx_kv_append_batch(None, 1, None, None, None, None, None) == B.DFLASH_EINVAL
     assert L.dflash_block_forward(None, 1, None, None, None, 16, None, None, None) == B.DFLASH_EINVAL
     L.dflash_destroy(None)
 

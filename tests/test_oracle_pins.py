@@ -565,3 +565,59 @@ def test_cache_holds_bf16_rounded_kv(tiny):
     b.seqs[0]["v"] = [O.round_bf16(v) for v in b.seqs[0]["v"]]
     bl = b.block_forward([0], [3], gamma=16)["logits"]
     assert 0 < np.abs(a - bl).max() < 0.05 * np.abs(a).max()
+
+
+def test_batched_append_is_one_pass_over_all_rows(tiny):
+    """The batched context precompute: one fc + hidden_norm + K/V pass over the rows of every
+    sequence at once gives, row for row, what each sequence's own pass gives (the step is
+    row-wise), and the engine's batched append equals the per-sequence appends in call order:
+    same cached K/V, same block tables, pages taken in call order."""
+    m, W = tiny
+    order = synth.gen_page_order(O.pool_pages(200, 16, 3)[1] - 1, 9)
+    e1 = O.Engine(m, W, 200, 3, page_order=order)
+    e2 = O.Engine(m, W, 200, 3, page_order=order)
+    for e in (e1, e2):
+        e.ctx_kv_append(0, synth.gen_hidden(m, 5, 21))
+    counts = {2: 17, 0: 9, 1: 0}
+    H = {s: synth.gen_hidden(m, 30 + s, n) for s, n in counts.items()}
+    Hall = np.concatenate([H[s] for s in (2, 0, 1)])
+    pos_all = np.concatenate([np.arange(17), np.arange(21, 30), np.zeros(0, dtype=np.int64)])
+    # the one-pass features and K/V, split back per sequence
+    F_all = e1.d.ctx_features(Hall)
+    kv_all = e1.d.ctx_kv(F_all, pos_all)
+    F2 = e1.d.ctx_features(H[2])
+    kv2 = e1.d.ctx_kv(F2, np.arange(17))
+    assert np.allclose(F_all[:17], F2, rtol=0, atol=1e-12)
+    for (ka, va), (kb, vb) in zip(kv_all, kv2):
+        assert np.allclose(ka[:17], kb, rtol=0, atol=1e-12) and np.allclose(va[:17], vb, rtol=0, atol=1e-12)
+    e1.ctx_kv_append_batch([2, 0, 1], [17, 9, 0], Hall)
+    e2.ctx_kv_append(2, H[2])
+    e2.ctx_kv_append(0, H[0])
+    for s in range(3):
+        assert e1.kv_len(s) == e2.kv_len(s) and e1.block_table(s) == e2.block_table(s)
+        for l in range(m["num_layers"]):
+            assert np.array_equal(e1.seqs[s]["k"][l], e2.seqs[s]["k"][l])
+            assert np.array_equal(e1.seqs[s]["v"][l], e2.seqs[s]["v"][l])
+    assert e1.pool.free == e2.pool.free
+    # slots of the call, in row order
+    assert np.array_equal(e1.last_slots, np.concatenate([e1.pool.slots(2, range(17)), e1.pool.slots(0, range(21, 30))]))
+
+
+def test_batched_append_refusals_change_nothing(tiny):
+    m, W = tiny
+    e = O.Engine(m, W, 300, 3, num_pages=9)              # 8 usable pages
+    e.ctx_kv_append(0, synth.gen_hidden(m, 1, 30))
+    e.ctx_kv_append(1, synth.gen_hidden(m, 2, 10))
+    state = lambda: ([e.block_table(s) for s in range(3)], list(e.pool.free), [e.kv_len(s) for s in range(3)])
+    before = state()
+    H = synth.gen_hidden(m, 3, 257)
+    for seqs, counts, code in [([0, 0], [1, 1], "ERANGE"), ([3], [1], "ERANGE"), ([1, 0], [1, 271], "ERANGE"),
+                               ([1, 2], [-1, 2], "EINVAL"), ([1, 2], [0, 0], "EINVAL"),
+                               ([1, 2], [200, 57], "EINVAL"), ([1, 2], [40, 40], "EPOOL")]:
+        with pytest.raises(O.PoolError) as ei:
+            e.ctx_kv_append_batch(seqs, counts, H[:max(0, sum(counts))])
+        assert ei.value.code == code, (seqs, counts)
+    with pytest.raises(O.PoolError) as ei:
+        e.ctx_kv_append_batch([1, 2], [2, 1], H[:3], positions=[40, 39, 0])
+    assert ei.value.code == "EINVAL"
+    assert state() == before
