@@ -39,13 +39,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemm_bytes(m, M):
+def gemm_bytes(m, M, fp8=False):
     """Algorithmic HBM bytes of the forward's weight-streaming GEMMs for M block rows:
-    each weight byte once, the bf16 activation in, the fp32 result out."""
+    each weight byte once (FP8: one byte a weight and a 4-byte scale a row), the bf16
+    activation in, the fp32 result out."""
     h, hd, nh, nkv, ff = m["hidden"], m["head_dim"], m["num_q_heads"], m["num_kv_heads"], m["intermediate"]
     qd, kvd = nh * hd, nkv * hd
     shapes = [(qd + 2 * kvd, h), (h, qd), (2 * ff, h), (h, ff)]
-    per_layer = sum(N * K * 2 + M * K * 2 + M * N * 4 for N, K in shapes)
+    wb = (lambda N, K: N * K + 4 * N) if fp8 else (lambda N, K: N * K * 2)
+    per_layer = sum(wb(N, K) + M * K * 2 + M * N * 4 for N, K in shapes)
     return per_layer * m["num_layers"]
 
 
@@ -82,8 +84,9 @@ def gemm_weight_elems(m):
     return ((qd + 2 * kvd) * h + h * qd + 2 * ff * h + h * ff) * m["num_layers"]
 
 
-def lmhead_bytes(m, M):
-    return m["vocab"] * m["hidden"] * 2 + M * m["hidden"] * 2
+def lmhead_bytes(m, M, fp8=False):
+    w = m["vocab"] * (m["hidden"] + 4) if fp8 else m["vocab"] * m["hidden"] * 2
+    return w + M * m["hidden"] * 2
 
 
 def attn_bytes(m, kv_lens, gamma):
@@ -165,6 +168,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch16", action="store_true")
     ap.add_argument("--no-longctx", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 E4M3 weight-only lines")
     ap.add_argument("--longctx-only", action="store_true",
                     help="only run the 32-sequence long-context section and print its JSON (for counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -309,11 +313,67 @@ def main():
         out["batch16"] = bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev)
     if not args.no_longctx:
         out["longctx"] = bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev)
+    if not args.no_fp8:
+        out["fp8"] = dict(batch1=bench_fp8_b1(m, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev))
+        if not args.no_batch16:
+            out["fp8"]["batch16"] = bench_batch16(dict(m, weight_format="fp8"), Wd, gamma, a, args, B, torch, np,
+                                                  synth, to_dev)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         out["cpu_baseline"] = run_cpu_baseline(m, W, H_ctx, H_steps, bonus, a, gamma, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def bench_fp8_b1(m, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev):
+    """The batch-1 step with FP8 E4M3 weights (the seven layer GEMMs and the lm_head
+    quantized at create; append, attention, norms and activations stay bf16): the same
+    inputs, plain launches timed, then one pass with every launch bracketed for the
+    per-class times and the weight-stream rates of the GEMM and lm_head classes."""
+    mf = dict(m, weight_format="fp8")
+    steps = args.steps
+    total = args.warmup + 2 * steps + 8
+    ctx = H_ctx.shape[0]
+    d = B.Drafter(mf, Wd, ctx + total * a + gamma + 16, 1)
+    d.dflash_ctx_kv_append(0, to_dev(H_ctx))
+    Hs = to_dev(H_steps)
+    toks = torch.empty((1, gamma - 1), dtype=torch.int32, device="cuda:0")
+    step_i = [0]
+
+    def step():
+        i = step_i[0]
+        d.dflash_ctx_kv_append(0, Hs[i * a:(i + 1) * a])
+        d.dflash_block_forward([0], [int(bonus[i])], toks, gamma=gamma)
+        step_i[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    d.dflash_timing(list(B.K_CLASSES))
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    br = d.dflash_timing_read()
+    d.dflash_timing([])
+    d.close()
+    blocks = steps / el
+    ms = {k: v[0] / steps for k, v in br.items() if v[1]}
+    rates = {}
+    for k, nbytes in (("gemm", gemm_bytes(m, gamma, fp8=True)), ("lmhead", lmhead_bytes(m, gamma, fp8=True))):
+        if k in ms:
+            rates[k] = dict(algorithmic_bytes_per_step=int(nbytes), gbs=round(nbytes / (ms[k] * 1e-3) / 1e9, 1),
+                            frac=round(nbytes / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    log(f"[bench] fp8 batch1: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; "
+        + ", ".join(f"{k} {v['gbs']:.0f} GB/s" for k, v in rates.items()))
+    return dict(workload=WORKLOAD, weight_format="fp8_e4m3", value=round(blocks, 2), unit="blocks/s",
+                steps=steps, ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
+                kernels_ms_per_step={k: round(v, 4) for k, v in ms.items()}, weight_stream=rates,
+                timing="value from plain launches; per-class times from a second, bracketed pass")
 
 
 def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
@@ -376,7 +436,8 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
         app[mode] = (time.perf_counter() - t1) / app_reps * 1e3
     d.close()
     blocks = nb * steps / el
-    log(f"[bench] batch16: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; append of {nb}x{a} rows: "
+    wbytes = 1 if m.get("weight_format") == "fp8" else 2
+    log(f"[bench] batch16 ({'fp8' if wbytes == 1 else 'bf16'}): {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; append of {nb}x{a} rows: "
         f"batched {app['batched']:.3f} ms, per sequence {app['per_seq']:.3f} ms")
     gemm_ms = br["gemm"][0] / steps
     M = nb * gamma
@@ -384,8 +445,8 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     gemm_stats = dict(rows=M, flop_per_step=gemm_flop, ms_per_step=round(gemm_ms, 4),
                       tflops=round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 1),
                       mfma_frac=round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                      weight_gbs=round(gemm_weight_elems(m) * 2 / (gemm_ms * 1e-3) / 1e9, 1))
-    return dict(workload=WORKLOAD_B16, value=round(blocks, 2), unit="blocks/s", steps=steps,
+                      weight_gbs=round(gemm_weight_elems(m) * wbytes / (gemm_ms * 1e-3) / 1e9, 1))
+    return dict(workload=WORKLOAD_B16, weight_format="fp8_e4m3" if wbytes == 1 else "bf16", value=round(blocks, 2), unit="blocks/s", steps=steps,
                 ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
                 ctx_lengths=[int(x) for x in lens], timing="all launch classes bracketed by events",
                 append=dict(rows=nb * a, form="one batched call" if batched else "per sequence",

@@ -11,9 +11,10 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
 
 DFLASH_OK, DFLASH_EINVAL, DFLASH_ENOMEM, DFLASH_EPOOL, DFLASH_ERANGE, DFLASH_EHIP = 0, -1, -2, -3, -4, -5
+DFLASH_WEIGHTS_BF16, DFLASH_WEIGHTS_FP8_E4M3 = 0, 1
 CODE_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EPOOL", -4: "ERANGE", -5: "EHIP"}
 DFLASH_BUF_POOL, DFLASH_BUF_KPOS, DFLASH_BUF_SLOTS, DFLASH_BUF_BLOCKTAB, DFLASH_BUF_HIDDEN = 0, 1, 2, 3, 4
-DFLASH_BUF_HIDDEN_LO = 5
+DFLASH_BUF_HIDDEN_LO, DFLASH_BUF_FP8_LMHEAD, DFLASH_BUF_FP8_LMHEAD_SCALE = 5, 6, 7
 
 
 class dflash_config(C.Structure):
@@ -27,7 +28,7 @@ class dflash_config(C.Structure):
         ("yarn_beta_fast", C.c_double), ("yarn_beta_slow", C.c_double),
         ("sliding_window", C.c_int32), ("layer_sliding", C.POINTER(C.c_uint8)),
         ("max_seq_len", C.c_int32), ("max_batch", C.c_int32), ("num_pages", C.c_int32),
-        ("page_order", C.POINTER(C.c_int32)),
+        ("page_order", C.POINTER(C.c_int32)), ("weight_format", C.c_int32),
     ]
 
 
@@ -119,7 +120,8 @@ def make_config(m: dict, max_seq_len: int, max_batch: int, num_pages: int = 0, p
         sliding_window=int(m.get("sliding_window") or 0),
         layer_sliding=C.cast(ls_arr, C.POINTER(C.c_uint8)) if ls_arr is not None else None,
         max_seq_len=max_seq_len, max_batch=max_batch, num_pages=num_pages,
-        page_order=C.cast(po, C.POINTER(C.c_int32)) if po is not None else None)
+        page_order=C.cast(po, C.POINTER(C.c_int32)) if po is not None else None,
+        weight_format=DFLASH_WEIGHTS_FP8_E4M3 if m.get("weight_format") == "fp8" else DFLASH_WEIGHTS_BF16)
     return cfg, (ls_arr, po)
 
 

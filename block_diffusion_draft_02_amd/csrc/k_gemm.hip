@@ -83,6 +83,88 @@ hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStrea
   return hipGetLastError();
 }
 
+// FP8 weights: OCP E4M3 codes with one fp32 scale per row (weight = code value x scale), in
+// the T16-FP8 layout: the rows go in tiles of 16, a tile's K in 256-deep blocks of 4 KB, and a
+// block holds 4 x 64 16-byte pieces in the order the lanes load them: piece (q, lane) is row
+// lane % 16, the 8 codes of k = 64q + 8g .. (the lane's operand of 32-deep step 2q, g = lane/16)
+// followed by the 8 codes of k = 64q + 32 + 8g .. (step 2q + 1).
+constexpr int T16Q_BLOCK = 16 * 256;   // bytes of one 256-deep block of a tile
+
+// row scale = max |w| / 448 (the largest finite E4M3 value); an all-zero row has scale 1
+__global__ __launch_bounds__(256) void k_row_scale_fp8(const bf16* __restrict__ src, int N, int K, int n_pad,
+                                                       float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= n_pad) return;
+  float amax = 0.f;
+  if (n < N)
+    for (int k = lane * 8; k < K; k += 64 * 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)n * K + k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xffff0000u)));
+      }
+    }
+  amax = wave_max(amax);
+  if (lane == 0) scale[n] = amax > 0.f ? amax / 448.f : 1.f;
+}
+
+// x (finite) to the nearest E4M3 code, ties to even, saturating at +-448
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = __float_as_uint(x) >> 31;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7e;
+  } else if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.f);   // 8 is the smallest normal, 2^-6
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    code = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+    code = code > 0x7eu ? 0x7eu : code;
+  }
+  return code | (sign << 7);
+}
+
+// one thread per 16-byte destination piece; rows past N (padding to whole tiles) are zero
+__global__ __launch_bounds__(256) void k_quant_fp8_t16(const bf16* __restrict__ src, int N, int K, int n_pad,
+                                                       const float* __restrict__ scale,
+                                                       uint8_t* __restrict__ dst) {
+  const size_t p = (size_t)blockIdx.x * 256 + threadIdx.x;   // destination piece
+  if (p >= (size_t)n_pad * K / 16) return;
+  const int lane = (int)(p & 63);
+  const size_t q = p >> 6;
+  const int qq = (int)(q & 3);
+  const size_t blk = q >> 2;
+  const int S = K / 256;
+  const size_t n = (blk / S) * 16 + (lane & 15);
+  const int k0 = (int)(blk % S) * 256 + qq * 64 + (lane >> 4) * 8;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (n < (size_t)N) {
+    const float sc = scale[n];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + n * K + k0 + half * 32);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t bits = (j & 1) ? (v[j >> 1] & 0xffff0000u) : (v[j >> 1] << 16);
+        w[half * 2 + (j >> 2)] |= e4m3_code(__uint_as_float(bits) / sc) << (8 * (j & 3));
+      }
+    }
+  }
+  *reinterpret_cast<u32x4*>(dst + p * 16) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t launch_quant_fp8(const bf16* src, int N, int K, uint8_t* dst, float* scale, hipStream_t st) {
+  if (N < 1 || K < 256 || K % 256) return hipErrorInvalidValue;
+  const int n_pad = (N + 15) / 16 * 16;
+  k_row_scale_fp8<<<(unsigned)((n_pad + 3) / 4), 256, 0, st>>>(src, N, K, n_pad, scale);
+  const size_t pieces = (size_t)n_pad * K / 16;
+  k_quant_fp8_t16<<<(unsigned)((pieces + 255) / 256), 256, 0, st>>>(src, N, K, n_pad, scale, dst);
+  return hipGetLastError();
+}
+
 // One KS-deep (or 256-deep, full = false) weight chunk at depth k for the lane: row-major
 // (wp = row + (lane/16)*8) or T16 (wp = tile + lane*8).
 template <bool TILED>
@@ -163,13 +245,15 @@ __device__ __forceinline__ void stream_tile(AChunk<MT, SPLIT>& sa, const bf16* _
 constexpr int KT = 256;
 
 // NORM: the activation (A, A_lo) is x * w of an RMSNorm (NormIn); the result rows are
-// multiplied by the rows' scales 1/sqrt(mean(x^2) + eps).
-template <int MT, bool SPLIT, bool TILED, bool NORM>
+// multiplied by the rows' scales 1/sqrt(mean(x^2) + eps). FP8: W is in the T16-FP8 layout,
+// its codes become exact bf16 operands in registers, and each result column is multiplied
+// by its row scale wsc[n] (before the RMSNorm scale, each a rounding of its own).
+template <int MT, bool SPLIT, bool TILED, bool NORM, bool FP8>
 __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
                                                     const bf16* __restrict__ A_lo, int lda, int M,
                                                     const bf16* __restrict__ W, int N, int K,
                                                     float* __restrict__ P, long long part_stride,
-                                                    NormIn nrm) {
+                                                    NormIn nrm, const float* __restrict__ wsc) {
   __shared__ __attribute__((aligned(16))) bf16 sa[SPLIT ? 2 : 1][MT * 16][KT + APAD];
   __shared__ float srs[NORM ? MT * 16 : 1];
   constexpr int PT = MT * 16 * KT / 8 / 256;   // 16-byte activation pieces per thread and term
@@ -202,11 +286,21 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
   }
   // out-of-range columns read a valid row (every wave stays for the barrier); their results
   // are never stored
-  const bf16* wp = TILED ? W + ((size_t)min(n0, N - 16) / 16 * (K / KT) + blockIdx.y) * T16_BLOCK + lane * 8
-                         : W + (size_t)(nv ? n : min(n0, N - 1)) * K + kb + g * 8;
   bf16x8 w[KT / 32];
+  u32x4 wq[FP8 ? KT / 64 : 1];
+  float sc = 1.f;
+  if (FP8) {
+    const uint8_t* q8 = reinterpret_cast<const uint8_t*>(W) +
+                        ((size_t)min(n0, N - 16) / 16 * (K / KT) + blockIdx.y) * T16Q_BLOCK + lane * 16;
 #pragma unroll
-  for (int u = 0; u < KT / 32; ++u) w[u] = ld8(wp + u * (TILED ? 512 : 32));
+    for (int u = 0; u < KT / 64; ++u) wq[FP8 ? u : 0] = *reinterpret_cast<const u32x4*>(q8 + u * 1024);
+    sc = wsc[nv ? n : min(n0, N - 1)];
+  } else {
+    const bf16* wp = TILED ? W + ((size_t)min(n0, N - 16) / 16 * (K / KT) + blockIdx.y) * T16_BLOCK + lane * 8
+                           : W + (size_t)(nv ? n : min(n0, N - 1)) * K + kb + g * 8;
+#pragma unroll
+    for (int u = 0; u < KT / 32; ++u) w[u] = ld8(wp + u * (TILED ? 512 : 32));
+  }
   if (NORM) {
     // after the weight loads are issued: waiting on the sums does not wait on the weights
     float ssum = 0.f;
@@ -224,6 +318,13 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
     if (SPLIT) *reinterpret_cast<u32x4*>(&sa[SPLIT ? 1 : 0][r][cc]) = al[SPLIT ? u : 0];
   }
   __syncthreads();
+  if (FP8) {
+#pragma unroll
+    for (int u = 0; u < KT / 64; ++u) {
+      w[2 * u] = fp8x8_bf16(wq[FP8 ? u : 0][0], wq[FP8 ? u : 0][1]);
+      w[2 * u + 1] = fp8x8_bf16(wq[FP8 ? u : 0][2], wq[FP8 ? u : 0][3]);
+    }
+  }
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -246,7 +347,10 @@ __global__ __launch_bounds__(256) void k_gemm_split(const bf16* __restrict__ A,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + 4 * g + i;
-      if (m < M) pp[(size_t)m * N + n] = NORM ? acc[mt][i] * srs[NORM ? m : 0] : acc[mt][i];
+      float v = acc[mt][i];
+      if (FP8) v = v * sc;
+      if (NORM) v = v * srs[NORM ? m : 0];
+      if (m < M) pp[(size_t)m * N + n] = v;
     }
   }
 }
@@ -287,7 +391,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A,
 
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                               int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
-                              hipStream_t st, const NormIn* norm) {
+                              hipStream_t st, const NormIn* norm, const float* wsc) {
   const int S = (K + k_len - 1) / k_len;
   dim3 grid((N + 63) / 64, S);
   const int mt = (M + 15) / 16;
@@ -295,22 +399,25 @@ hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, c
   if (w_tiled && (k_len != KT || K % KT || N % 16)) return hipErrorInvalidValue;
   const NormIn nn = norm ? *norm : NormIn{};
   if (norm && (!w_tiled || !A_lo || nn.h != K || K % SSQ_COLS || K > SSQ_STRIDE * SSQ_COLS)) return hipErrorInvalidValue;
+  if (wsc && (!w_tiled || !A_lo)) return hipErrorInvalidValue;
   if (k_len == KT && K % KT == 0) {
-#define DFL_SPLIT(MTV, SP, TL, NM) (void)launch(k_gemm_split<MTV, SP, TL, NM>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride, nn)
-#define DFL_SPLIT_MT(SP, TL, NM) switch (mt) { case 1: DFL_SPLIT(1, SP, TL, NM); break; case 2: DFL_SPLIT(2, SP, TL, NM); break; \
-                                               case 3: DFL_SPLIT(3, SP, TL, NM); break; default: DFL_SPLIT(4, SP, TL, NM); break; }
-    if (norm) {
-      DFL_SPLIT_MT(true, true, true)
+#define DFL_SPLIT(MTV, SP, TL, NM, F8) (void)launch(k_gemm_split<MTV, SP, TL, NM, F8>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, P, part_stride, nn, wsc)
+#define DFL_SPLIT_MT(SP, TL, NM, F8) switch (mt) { case 1: DFL_SPLIT(1, SP, TL, NM, F8); break; case 2: DFL_SPLIT(2, SP, TL, NM, F8); break; \
+                                                   case 3: DFL_SPLIT(3, SP, TL, NM, F8); break; default: DFL_SPLIT(4, SP, TL, NM, F8); break; }
+    if (wsc) {
+      if (norm) { DFL_SPLIT_MT(true, true, true, true) } else { DFL_SPLIT_MT(true, true, false, true) }
+    } else if (norm) {
+      DFL_SPLIT_MT(true, true, true, false)
     } else if (A_lo) {
-      if (w_tiled) { DFL_SPLIT_MT(true, true, false) } else { DFL_SPLIT_MT(true, false, false) }
+      if (w_tiled) { DFL_SPLIT_MT(true, true, false, false) } else { DFL_SPLIT_MT(true, false, false, false) }
     } else {
-      if (w_tiled) { DFL_SPLIT_MT(false, true, false) } else { DFL_SPLIT_MT(false, false, false) }
+      if (w_tiled) { DFL_SPLIT_MT(false, true, false, false) } else { DFL_SPLIT_MT(false, false, false, false) }
     }
 #undef DFL_SPLIT_MT
 #undef DFL_SPLIT
     return hipGetLastError();
   }
-  if (norm || w_tiled) return hipErrorInvalidValue;
+  if (norm || w_tiled || wsc) return hipErrorInvalidValue;
 #define DFL_SKINNY(MTV, SP) (void)launch(k_gemm_skinny<MTV, SP>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, k_len, P, part_stride)
   if (A_lo) {
     switch (mt) { case 1: DFL_SKINNY(1, true); break; case 2: DFL_SKINNY(2, true); break;
@@ -356,11 +463,14 @@ struct WideOut {
   int* best_i;
   int n_groups, gamma;
   float* logits;       //   drafted rows' logits [rows][N] or null
+  const float* wsc;    // FP8 weights: the per-row scales (padded to whole tiles)
 };
 
 // SPLIT: the activation carries a lo term (A_lo); without it A is exact bf16 (the context
-// append's target hidden states) and each step is one MFMA.
-template <bool ARGMAX, bool NORM, bool SPLIT>
+// append's target hidden states) and each step is one MFMA. FP8: W in the T16-FP8 layout
+// (one 16-byte piece per tile and chunk), codes converted to exact bf16 operands in
+// registers, each column scaled by its row scale as the skinny kernel scales it.
+template <bool ARGMAX, bool NORM, bool SPLIT, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(
     const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda, int M,
     const bf16* __restrict__ W, int N, int K, int gx, int gy, WideOut o) {
@@ -394,6 +504,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // tiles past the last one re-read the last tile; their columns are never used
   const bf16* wp0 = W + (size_t)min(tile0, ntiles - 1) * 16 * K + lane * 8;
   const bf16* wp1 = W + (size_t)min(tile0 + 1, ntiles - 1) * 16 * K + lane * 8;
+  const uint8_t* qp0 = reinterpret_cast<const uint8_t*>(W) + (size_t)min(tile0, ntiles - 1) * 16 * K + lane * 16;
+  const uint8_t* qp1 = reinterpret_cast<const uint8_t*>(W) + (size_t)min(tile0 + 1, ntiles - 1) * 16 * K + lane * 16;
+  float wsc[FP8 ? 2 : 1];
+  if (FP8) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) wsc[FP8 ? nt : 0] = o.wsc[min(tile0 + nt, ntiles - 1) * 16 + c];
+  }
 
   if (NORM) {
     // the rows' RMSNorm scales, each row's slice sums added as the skinny kernel adds them
@@ -411,12 +528,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
 
-  auto load_w = [&](bf16x8 (&w)[2][2], int k) {
-    const size_t off = (size_t)(k >> 8) * T16_BLOCK + ((k & 255) >> 5) * 512;
+  // a chunk's weight operands as raw 16-byte pieces: bf16, one per tile and 32-deep step;
+  // FP8, one per tile (both steps)
+  auto load_w = [&](u32x4 (&w)[2][FP8 ? 1 : 2], int k) {
+    if (FP8) {
+      const size_t off = (size_t)(k >> 8) * T16Q_BLOCK + ((k & 255) >> 6) * 1024;
+      w[0][0] = *reinterpret_cast<const u32x4*>(qp0 + off);
+      w[1][0] = *reinterpret_cast<const u32x4*>(qp1 + off);
+    } else {
+      const size_t off = (size_t)(k >> 8) * T16_BLOCK + ((k & 255) >> 5) * 512;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      w[0][s] = ld8(wp0 + off + s * 512);
-      w[1][s] = ld8(wp1 + off + s * 512);
+      for (int s = 0; s < 2; ++s) {
+        w[0][FP8 ? 0 : s] = *reinterpret_cast<const u32x4*>(wp0 + off + s * 512);
+        w[1][FP8 ? 0 : s] = *reinterpret_cast<const u32x4*>(wp1 + off + s * 512);
+      }
     }
   };
   constexpr int NT = SPLIT ? 2 : 1;   // activation terms
@@ -448,9 +573,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   // one staged chunk: per 32-deep step, the hi MFMAs of every (row tile, column tile), then
   // the lo ones (per element: hi, then lo, step after step)
-  auto mma = [&](int buf, const bf16x8 (&w)[2][2]) {
+  auto mma = [&](int buf, const u32x4 (&w)[2][FP8 ? 1 : 2]) {
 #pragma unroll
     for (int s = 0; s < WD_KC / 32; ++s) {
+      bf16x8 wv[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        wv[nt] = FP8 ? fp8x8_bf16(w[nt][0][2 * s], w[nt][0][2 * s + 1]) : __builtin_bit_cast(bf16x8, w[nt][FP8 ? 0 : s]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         bf16x8 av[WM];
@@ -460,7 +589,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(av[mt], w[nt][s], acc[mt][nt]);
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(av[mt], wv[nt], acc[mt][nt]);
       }
     }
   };
@@ -476,7 +605,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = NORM ? acc[mt][nt][e] * srs[NORM ? mt * 16 + 4 * g + e : 0] : acc[mt][nt][e];
+          float v = acc[mt][nt][e];
+          if (FP8) v = v * wsc[FP8 ? nt : 0];
+          if (NORM) v = v * srs[NORM ? mt * 16 + 4 * g + e : 0];
           gs[ARGMAX ? 0 : mt][nt][e] += v;
         }
         acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -484,7 +615,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   };
 
-  bf16x8 w0[2][2], w1[2][2];
+  u32x4 w0[2][FP8 ? 1 : 2], w1[2][FP8 ? 1 : 2];
   u32x4 ra[NT][PT];
   load_a(ra, kb);
   load_w(w0, kb);
@@ -541,7 +672,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int nt = 0; nt < 2; ++nt) {
         const int n = (tile0 + nt) * 16 + c;
         if (n < N) {
-          const float v = acc[mt][nt][e];
+          const float v = FP8 ? acc[mt][nt][e] * wsc[FP8 ? nt : 0] : acc[mt][nt][e];
           better(bv, bi, v, n);
           if (o.logits != nullptr && m < M) {
             const int b = m / o.gamma, i = m % o.gamma;
@@ -579,20 +710,25 @@ static unsigned wide_grid(int gx, int gy, int gz) { return (unsigned)((gx + 7) /
 int gemm_wide_groups(int K, int gsz) { return (K / 256 + gsz - 1) / gsz; }
 
 hipError_t launch_gemm_wide(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
-                            int gsz, float* P, long long part_stride, hipStream_t st, const NormIn* norm) {
+                            int gsz, float* P, long long part_stride, hipStream_t st, const NormIn* norm,
+                            const float* wsc) {
   if (M < 1 || N < 16 || N % 16 || K < 256 || K % 256 || gsz < 1) return hipErrorInvalidValue;
   if (norm && (!A_lo || norm->h != K || K > SSQ_STRIDE * SSQ_COLS)) return hipErrorInvalidValue;
+  if (wsc && !A_lo) return hipErrorInvalidValue;
   const int gx = (N + WD_N - 1) / WD_N, gy = (M + WD_M - 1) / WD_M, gz = gemm_wide_groups(K, gsz);
   WideOut o{};
-  o.P = P; o.ps = part_stride; o.gsz = gsz;
+  o.P = P; o.ps = part_stride; o.gsz = gsz; o.wsc = wsc;
   const unsigned grid = wide_grid(gx, gy, gz);
-  if (norm) {
-    o.nrm = *norm;
-    (void)launch(k_gemm_wide<false, true, true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+  if (norm) o.nrm = *norm;
+  if (wsc) {
+    if (norm) (void)launch(k_gemm_wide<false, true, true, true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+    else (void)launch(k_gemm_wide<false, false, true, true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+  } else if (norm) {
+    (void)launch(k_gemm_wide<false, true, true, false>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
   } else if (A_lo) {
-    (void)launch(k_gemm_wide<false, false, true>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+    (void)launch(k_gemm_wide<false, false, true, false>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
   } else {
-    (void)launch(k_gemm_wide<false, false, false>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
+    (void)launch(k_gemm_wide<false, false, false, false>, grid, 256, 0, st, A, A_lo, lda, M, W, N, K, gx, gy, o);
   }
   return hipGetLastError();
 }
@@ -600,14 +736,19 @@ hipError_t launch_gemm_wide(const bf16* A, const bf16* A_lo, int lda, int M, con
 int lmhead_wide_groups(int V) { return (V + WD_N - 1) / WD_N; }
 
 hipError_t launch_lmhead_wide(const bf16* Y, const bf16* Y_lo, int ldy, int M, const bf16* W, int V, int K,
-                              float* best_v, int* best_i, int n_groups, int gamma, float* logits, hipStream_t st) {
+                              float* best_v, int* best_i, int n_groups, int gamma, float* logits, hipStream_t st,
+                              const float* wsc) {
   if (M < 1 || !Y_lo || V < 1 || K < 256 || K % 256 || n_groups != lmhead_wide_groups(V) || gamma < 2)
     return hipErrorInvalidValue;
   WideOut o{};
-  o.best_v = best_v; o.best_i = best_i; o.n_groups = n_groups; o.gamma = gamma; o.logits = logits;
+  o.best_v = best_v; o.best_i = best_i; o.n_groups = n_groups; o.gamma = gamma; o.logits = logits; o.wsc = wsc;
   const int gy = (M + WD_M - 1) / WD_M;
-  (void)launch(k_gemm_wide<true, false, true>, wide_grid(n_groups, gy, 1), 256, 0, st, Y, Y_lo, ldy, M, W, V, K,
-               n_groups, gy, o);
+  if (wsc)
+    (void)launch(k_gemm_wide<true, false, true, true>, wide_grid(n_groups, gy, 1), 256, 0, st, Y, Y_lo, ldy, M, W, V,
+                 K, n_groups, gy, o);
+  else
+    (void)launch(k_gemm_wide<true, false, true, false>, wide_grid(n_groups, gy, 1), 256, 0, st, Y, Y_lo, ldy, M, W, V,
+                 K, n_groups, gy, o);
   return hipGetLastError();
 }
 
@@ -817,17 +958,23 @@ constexpr int LMP_WAVES = 8;
 constexpr int LMP_KMAX = 2048;
 
 int lmhead_persistent_groups(int V, int K, int M, int n_cu) {
+  // (K a multiple of the 512-deep chunk: the bf16 and the FP8 weight streams both need it)
   if (M > 16 || K > LMP_KMAX || K % KS) return 0;
   const int tiles = (V + 15) / 16;
   return std::max(1, std::min(n_cu, (tiles + LMP_WAVES - 1) / LMP_WAVES));
 }
 
+// FP8: W in the T16-FP8 layout (a 512-deep chunk is 8 pieces per lane), codes converted to
+// exact bf16 operands, each logit multiplied by its vocabulary row's scale (loaded with the
+// chunk that starts the tile, so it is there when the tile ends).
+template <bool FP8>
 __global__ __launch_bounds__(LMP_WAVES * 64) void k_lmhead_persist(const bf16* __restrict__ Y,
                                                                  const bf16* __restrict__ Y_lo, int ldy,
                                                                  int M, int r0, const bf16* __restrict__ W,
                                                                  int V, int K, float* __restrict__ best_v,
                                                                  int* __restrict__ best_i, int gamma,
-                                                                 float* __restrict__ logits) {
+                                                                 float* __restrict__ logits,
+                                                                 const float* __restrict__ wsc) {
   __shared__ __attribute__((aligned(16))) bf16 sy[2][16][LMP_KMAX + APAD];
   __shared__ float sv[LMP_WAVES][16];
   __shared__ int si[LMP_WAVES][16];
@@ -855,41 +1002,61 @@ __global__ __launch_bounds__(LMP_WAVES * 64) void k_lmhead_persist(const bf16* _
   const int t0 = blockIdx.x * LMP_WAVES + wave;
   const int my_tiles = t0 < n_tiles ? (n_tiles - 1 - t0) / stride + 1 : 0;
   const int items = my_tiles * nch;   // (tile, chunk) pairs this wave streams, in order
-  auto wptr = [&](int q) { return W + (size_t)(t0 + (q / nch) * stride) * 16 * K + lane * 8; };
-  bf16x8 w0[16], w1[16];
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](const bf16x8 (&w)[16], int q) {
+  auto tile_of = [&](int q) { return t0 + (q / nch) * stride; };
+  // one chunk (item q) of the wave's stream: bf16, 16 pieces of 16 bytes; FP8, 8 pieces
+  constexpr int NP = FP8 ? KS / 64 : KS / 32;
+  auto load_chunk = [&](u32x4 (&w)[NP], float& sc, int q) {
     const int j = q % nch;
+    if (FP8) {
+      const uint8_t* b = reinterpret_cast<const uint8_t*>(W) + (size_t)tile_of(q) * 16 * K + (size_t)j * (KS / 256) * T16Q_BLOCK + lane * 16;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+      for (int v = 0; v < NP; ++v) w[v] = *reinterpret_cast<const u32x4*>(b + (v >> 2) * T16Q_BLOCK + (v & 3) * 1024);
+      if (j == 0) sc = wsc[tile_of(q) * 16 + c];
+    } else {
+      const bf16* b = W + (size_t)tile_of(q) * 16 * K + (size_t)j * (KS / 256) * T16_BLOCK + lane * 8;
+#pragma unroll
+      for (int v = 0; v < NP; ++v) w[v] = *reinterpret_cast<const u32x4*>(b + v * 512);
+    }
+  };
+  u32x4 w0[NP], w1[NP];
+  float sc0 = 1.f, sc1 = 1.f, sc = 1.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](const u32x4 (&w)[NP], float scq, int q) {
+    const int j = q % nch;
+    if (FP8 && j == 0) sc = scq;
+#pragma unroll
+    for (int u = 0; u < KS / 32; ++u) {
+      const bf16x8 wv = FP8 ? fp8x8_bf16(w[u >> 1][(u & 1) * 2], w[u >> 1][(u & 1) * 2 + 1])
+                            : __builtin_bit_cast(bf16x8, w[FP8 ? 0 : u]);
       const int k = j * KS + u * 32 + g * 8;
-      acc = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sy[0][c][k])), w[u], acc);
-      acc = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sy[1][c][k])), w[u], acc);
+      acc = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sy[0][c][k])), wv, acc);
+      acc = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sy[1][c][k])), wv, acc);
     }
     if (j == nch - 1) {
       // tile done: lane (c, g) holds rows 4g..4g+3 of column t*16 + c
-      const int n = (t0 + (q / nch) * stride) * 16 + c;
+      const int n = tile_of(q) * 16 + c;
       if (n < V) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          better(bv[e], bi[e], acc[e], n);
+          const float v = FP8 ? acc[e] * sc : acc[e];
+          better(bv[e], bi[e], v, n);
           const int m = 4 * g + e;
           if (logits != nullptr && m < M) {
             const int r = r0 + m, b = r / gamma, i = r % gamma;
-            if (i != 0) logits[(size_t)(b * (gamma - 1) + i - 1) * V + n] = acc[e];
+            if (i != 0) logits[(size_t)(b * (gamma - 1) + i - 1) * V + n] = v;
           }
         }
       }
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  if (items > 0) load_w<true>(w0, wptr(0), 0, true);
+  if (items > 0) load_chunk(w0, sc0, 0);
   for (int q = 0; q < items; q += 2) {
-    if (q + 1 < items) load_w<true>(w1, wptr(q + 1), ((q + 1) % nch) * KS, true);
-    consume(w0, q);
+    if (q + 1 < items) load_chunk(w1, sc1, q + 1);
+    consume(w0, sc0, q);
     if (q + 1 >= items) break;
-    if (q + 2 < items) load_w<true>(w0, wptr(q + 2), ((q + 2) % nch) * KS, true);
-    consume(w1, q + 1);
+    if (q + 2 < items) load_chunk(w0, sc0, q + 2);
+    consume(w1, sc1, q + 1);
   }
   // merge across the 16 lanes of a row group, then across the waves
 #pragma unroll
@@ -921,10 +1088,14 @@ __global__ __launch_bounds__(LMP_WAVES * 64) void k_lmhead_persist(const bf16* _
 
 hipError_t launch_lmhead_persistent(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W,
                                     int V, int K, float* best_v, int* best_i, int n_groups, int gamma,
-                                    float* logits, hipStream_t st) {
+                                    float* logits, hipStream_t st, const float* wsc) {
   if (M < 1 || M > 16 || K > LMP_KMAX || K % KS || n_groups < 1) return hipErrorInvalidValue;
-  (void)launch(k_lmhead_persist, n_groups, LMP_WAVES * 64, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v, best_i,
-               gamma, logits);
+  if (wsc)
+    (void)launch(k_lmhead_persist<true>, n_groups, LMP_WAVES * 64, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v,
+                 best_i, gamma, logits, wsc);
+  else
+    (void)launch(k_lmhead_persist<false>, n_groups, LMP_WAVES * 64, 0, st, Y, Y_lo, ldy, M, r0, W, V, K, best_v,
+                 best_i, gamma, logits, wsc);
   return hipGetLastError();
 }
 

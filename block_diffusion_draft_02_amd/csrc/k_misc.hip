@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64) void k_resid_sum(float* __restrict__ X, const f
   const size_t o = (size_t)r * h + col;
   const f32x4 x = *reinterpret_cast<const f32x4*>(X + o);
   const u32x2 wb = *reinterpret_cast<const u32x2*>(w + col);   // the context's aligned copy
-  const f32x4 acc = sum_splits<16, f32x4>(P + o, S, ps, gsz);
+  const f32x4 acc = sum_splits<32, f32x4>(P + o, S, ps, gsz);   // up to 32 splits in one load pass
   const f32x4 y = x + acc;
   *reinterpret_cast<f32x4*>(X + o) = y;
   const float wf[4] = {bf2f((bf16)(wb.x & 0xffff)), bf2f((bf16)(wb.x >> 16)), bf2f((bf16)(wb.y & 0xffff)), bf2f((bf16)(wb.y >> 16))};

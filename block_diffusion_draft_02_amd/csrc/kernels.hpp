@@ -110,9 +110,10 @@ __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (si
 // terms (each k-step issues two MFMAs). Skinny form: partials P[s][M][N] over K splits of
 // k_len (k_len, K multiples of 256); M <= 64 per launch. W is row-major, or (w_tiled) in the
 // T16 layout, which needs k_len 256 and N a multiple of 16.
+// wsc: W holds FP8 codes in the T16-FP8 layout with these per-row scales (w_tiled, A_lo required)
 hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                               int N, int K, int k_len, float* P, long long part_stride, bool w_tiled,
-                              hipStream_t st, const NormIn* norm = nullptr);
+                              hipStream_t st, const NormIn* norm = nullptr, const float* wsc = nullptr);
 // Wide form for more than 64 rows (A_lo optional: without it A is exact bf16; W in the T16
 // layout, K a multiple of 256, N of 16): partials P[z][M][N] (z < gemm_wide_groups(K, gsz), stride part_stride),
 // each the sum of the 256-deep split chains of group z (splits z*gsz .. z*gsz + gsz - 1)
@@ -120,7 +121,12 @@ hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, c
 int gemm_wide_groups(int K, int gsz);
 hipError_t launch_gemm_wide(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
                             int gsz, float* P, long long part_stride, hipStream_t st,
-                            const NormIn* norm = nullptr);
+                            const NormIn* norm = nullptr, const float* wsc = nullptr);
+// Quantize a row-major [N, K] bf16 weight to OCP FP8 E4M3 codes in the T16-FP8 layout
+// (ceil(N/16)*16 rows of K bytes, padding rows zero) with per-row scales max|w| / 448
+// (1 for an all-zero row; padding rows 1): codes = nearest E4M3 of w / scale, ties to even,
+// saturating at +-448. K a multiple of 256.
+hipError_t launch_quant_fp8(const bf16* src, int N, int K, uint8_t* dst, float* scale, hipStream_t st);
 // Copy a row-major [N, K] bf16 weight into the T16 layout (ceil(N/16)*16 rows, the padding
 // rows zero); K a multiple of 256.
 hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStream_t st);
@@ -136,13 +142,13 @@ int lmhead_groups(int V);
 int lmhead_persistent_groups(int V, int K, int M, int n_cu);
 hipError_t launch_lmhead_persistent(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W,
                                     int V, int K, float* best_v, int* best_i, int n_groups, int gamma,
-                                    float* logits, hipStream_t st);
+                                    float* logits, hipStream_t st, const float* wsc = nullptr);
 // The wide lm_head (any row count, rows 0..M-1 of the forward; W in the T16 layout): one
 // argmax partial per (row, 128-column group); n_groups = lmhead_wide_groups(V).
 int lmhead_wide_groups(int V);
 hipError_t launch_lmhead_wide(const bf16* Y, const bf16* Y_lo, int ldy, int M, const bf16* W, int V, int K,
                               float* best_v, int* best_i, int n_groups, int gamma, float* logits,
-                              hipStream_t st);
+                              hipStream_t st, const float* wsc = nullptr);
 hipError_t launch_lmhead_argmax(const bf16* Y, const bf16* Y_lo, int ldy, int M, int r0, const bf16* W, int V,
                                 int K, float* best_v, int* best_i, int n_groups, int gamma,
                                 float* logits, hipStream_t st);

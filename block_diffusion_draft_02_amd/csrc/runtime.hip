@@ -29,6 +29,9 @@ struct LayerDev {
   bf16 *in_norm, *post_norm;   // owned copies (16-byte aligned: the GEMM staging reads them whole)
   // owned T16 copies of the forward's weights: fused [q;k;v], fused [gate;up], o, down
   bf16 *w_qkv, *w_gu, *o_proj, *down_proj;
+  // FP8 weights instead (weight_format 1): T16-FP8 codes and per-row scales of the same four
+  uint8_t *q_qkv, *q_gu, *q_o, *q_down;
+  float *s_qkv, *s_gu, *s_o, *s_down;
 };
 
 struct SeqState {
@@ -55,6 +58,9 @@ struct dflash_ctx {
   // weights
   const bf16 *fc, *hidden_norm, *norm, *embed;
   bf16* lm_head = nullptr;   // owned T16 copy, vocab padded to whole tiles
+  bool fp8 = false;          // weight_format 1: FP8 E4M3 forward weights and lm_head
+  uint8_t* lm_q = nullptr;   // FP8: T16-FP8 lm_head codes and per-row scales
+  float* lm_s = nullptr;
   std::vector<LayerDev> layers;
   bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;... (row-major, for the tiled GEMM)
   bf16* w_kv_t = nullptr;      // the same in the T16 layout (short appends)
@@ -263,6 +269,8 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
   if (!(cfg->rms_eps >= 0.f)) return bad("rms_eps must be >= 0");
   if (!(cfg->rope_theta > 1.0)) return bad("rope_theta must be > 1");
   if (cfg->rope_type != 0 && cfg->rope_type != 1) return bad("rope_type must be 0 or 1");
+  if (cfg->weight_format != DFLASH_WEIGHTS_BF16 && cfg->weight_format != DFLASH_WEIGHTS_FP8_E4M3)
+    return bad("weight_format must be DFLASH_WEIGHTS_BF16 or DFLASH_WEIGHTS_FP8_E4M3");
   if (cfg->rope_type == 1 && !(cfg->yarn_factor > 0 && cfg->yarn_orig_max_pos > 0 &&
                                cfg->yarn_beta_fast > 0 && cfg->yarn_beta_slow > 0))
     return bad("YaRN parameters must be positive");
@@ -405,6 +413,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->hd = cfg->head_dim; c->qd = c->nh * c->hd; c->kvd = c->nkv * c->hd; c->ff = cfg->intermediate;
   c->V = cfg->vocab; c->T = cfg->num_taps; c->Ht = cfg->target_hidden; c->gmax = cfg->gamma_max;
   c->mask = cfg->mask_token_id; c->max_seq = cfg->max_seq_len; c->max_batch = cfg->max_batch;
+  c->fp8 = cfg->weight_format == DFLASH_WEIGHTS_FP8_E4M3;
   c->eps = cfg->rms_eps; c->rope_type = cfg->rope_type; c->window = cfg->sliding_window;
   c->sliding.assign(c->L, 0);
   if (cfg->layer_sliding)
@@ -489,19 +498,30 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->fc_t, (size_t)hsz * c->T * c->Ht)) ||
       (rc = dalloc(c, &c->knorm_all, (size_t)c->L * c->hd)) ||
       (rc = dalloc(c, &c->inv_freq, (size_t)c->hd / 2)) ||
-      (rc = dalloc(c, &c->lm_head, (size_t)(c->V + 15) / 16 * 16 * hsz)))
+      (c->fp8 ? (rc = dalloc(c, &c->lm_q, (size_t)(c->V + 15) / 16 * 16 * hsz)) ||
+                    (rc = dalloc(c, &c->lm_s, (size_t)(c->V + 15) / 16 * 16))
+              : (rc = dalloc(c, &c->lm_head, (size_t)(c->V + 15) / 16 * 16 * hsz))))
     return fin(rc);
   c->layers.resize(c->L);
   for (int l = 0; l < c->L; ++l) {
     LayerDev& d = c->layers[l];
     const dflash_layer_weights& lw = w->layers[l];
     d.q_norm = (const bf16*)lw.q_norm; d.k_norm = (const bf16*)lw.k_norm;
-    if ((rc = dalloc(c, &d.in_norm, hsz)) || (rc = dalloc(c, &d.post_norm, hsz)) ||
-        (rc = dalloc(c, &d.w_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
-        (rc = dalloc(c, &d.w_gu, (size_t)2 * c->ff * hsz)) ||
-        (rc = dalloc(c, &d.o_proj, (size_t)hsz * c->qd)) ||
-        (rc = dalloc(c, &d.down_proj, (size_t)hsz * c->ff)))
+    if ((rc = dalloc(c, &d.in_norm, hsz)) || (rc = dalloc(c, &d.post_norm, hsz)))
       return fin(rc);
+    if (c->fp8) {
+      if ((rc = dalloc(c, &d.q_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
+          (rc = dalloc(c, &d.s_qkv, (size_t)(c->qd + 2 * c->kvd))) ||
+          (rc = dalloc(c, &d.q_gu, (size_t)2 * c->ff * hsz)) || (rc = dalloc(c, &d.s_gu, (size_t)2 * c->ff)) ||
+          (rc = dalloc(c, &d.q_o, (size_t)hsz * c->qd)) || (rc = dalloc(c, &d.s_o, hsz)) ||
+          (rc = dalloc(c, &d.q_down, (size_t)hsz * c->ff)) || (rc = dalloc(c, &d.s_down, hsz)))
+        return fin(rc);
+    } else if ((rc = dalloc(c, &d.w_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
+               (rc = dalloc(c, &d.w_gu, (size_t)2 * c->ff * hsz)) ||
+               (rc = dalloc(c, &d.o_proj, (size_t)hsz * c->qd)) ||
+               (rc = dalloc(c, &d.down_proj, (size_t)hsz * c->ff))) {
+      return fin(rc);
+    }
   }
   if (hipHostMalloc((void**)&c->ring_host, (size_t)RING * APPEND_ROWS * sizeof(int), hipHostMallocDefault) != hipSuccess) {
     c->ring_host = nullptr;
@@ -521,24 +541,41 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   auto tile = [&](const void* src, int N, int K, bf16* dst) {
     return launch_tile_weight((const bf16*)src, N, K, dst, st);
   };
+  // FP8 weights ([metrale-fw] from_weights, the FP8 weights phase): the same seven per-layer
+  // matrices and the lm_head quantized once, here, with per-row scales; a fused [A;B] is A's
+  // codes and scales followed by B's
+  auto quant = [&](const void* src, int N, int K, uint8_t* dst, float* sc) {
+    return launch_quant_fp8((const bf16*)src, N, K, dst, sc, st);
+  };
   for (int l = 0; l < c->L && e == hipSuccess; ++l) {
     const dflash_layer_weights& lw = w->layers[l];
     LayerDev& d = c->layers[l];
-    if ((e = tile(lw.q_proj, c->qd, c->h, d.w_qkv)) ||
-        (e = tile(lw.k_proj, c->kvd, c->h, d.w_qkv + (size_t)c->qd * hsz)) ||
-        (e = tile(lw.v_proj, c->kvd, c->h, d.w_qkv + (size_t)(c->qd + c->kvd) * hsz)) ||
-        (e = tile(lw.gate_proj, c->ff, c->h, d.w_gu)) ||
-        (e = tile(lw.up_proj, c->ff, c->h, d.w_gu + (size_t)c->ff * hsz)) ||
-        (e = tile(lw.o_proj, c->h, c->qd, d.o_proj)) ||
-        (e = tile(lw.down_proj, c->h, c->ff, d.down_proj)) ||
-        (e = cp(d.in_norm, lw.input_layernorm, hsz * 2)) ||
+    if (c->fp8) {
+      if ((e = quant(lw.q_proj, c->qd, c->h, d.q_qkv, d.s_qkv)) ||
+          (e = quant(lw.k_proj, c->kvd, c->h, d.q_qkv + (size_t)c->qd * hsz, d.s_qkv + c->qd)) ||
+          (e = quant(lw.v_proj, c->kvd, c->h, d.q_qkv + (size_t)(c->qd + c->kvd) * hsz, d.s_qkv + c->qd + c->kvd)) ||
+          (e = quant(lw.gate_proj, c->ff, c->h, d.q_gu, d.s_gu)) ||
+          (e = quant(lw.up_proj, c->ff, c->h, d.q_gu + (size_t)c->ff * hsz, d.s_gu + c->ff)) ||
+          (e = quant(lw.o_proj, c->h, c->qd, d.q_o, d.s_o)) ||
+          (e = quant(lw.down_proj, c->h, c->ff, d.q_down, d.s_down)))
+        break;
+    } else if ((e = tile(lw.q_proj, c->qd, c->h, d.w_qkv)) ||
+               (e = tile(lw.k_proj, c->kvd, c->h, d.w_qkv + (size_t)c->qd * hsz)) ||
+               (e = tile(lw.v_proj, c->kvd, c->h, d.w_qkv + (size_t)(c->qd + c->kvd) * hsz)) ||
+               (e = tile(lw.gate_proj, c->ff, c->h, d.w_gu)) ||
+               (e = tile(lw.up_proj, c->ff, c->h, d.w_gu + (size_t)c->ff * hsz)) ||
+               (e = tile(lw.o_proj, c->h, c->qd, d.o_proj)) ||
+               (e = tile(lw.down_proj, c->h, c->ff, d.down_proj))) {
+      break;
+    }
+    if ((e = cp(d.in_norm, lw.input_layernorm, hsz * 2)) ||
         (e = cp(d.post_norm, lw.post_attention_layernorm, hsz * 2)) ||
         (e = cp((char*)c->w_kv + (size_t)l * 2 * kb, lw.k_proj, kb)) ||
         (e = cp((char*)c->w_kv + (size_t)l * 2 * kb + kb, lw.v_proj, kb)) ||
         (e = cp(c->knorm_all + (size_t)l * c->hd, lw.k_norm, (size_t)c->hd * 2)))
       break;
   }
-  if (e == hipSuccess) e = tile(w->lm_head, c->V, c->h, c->lm_head);
+  if (e == hipSuccess) e = c->fp8 ? quant(w->lm_head, c->V, c->h, c->lm_q, c->lm_s) : tile(w->lm_head, c->V, c->h, c->lm_head);
   if (e == hipSuccess) e = tile(w->fc, c->h, c->T * c->Ht, c->fc_t);
   if (e == hipSuccess) e = tile(c->w_kv, c->L * 2 * c->kvd, c->h, c->w_kv_t);   // after the copies above, same stream
   std::vector<double> f = inv_freq_table(cfg, &c->mscale);
@@ -608,6 +645,12 @@ int dflash_debug_copy(dflash_ctx* c, int32_t buffer, void* dst, size_t offset, s
     case DFLASH_BUF_BLOCKTAB: base = (const char*)c->bt_dev; size = (size_t)c->max_batch * c->per_seq * 4; break;
     case DFLASH_BUF_HIDDEN: base = (const char*)c->Xn; size = (size_t)c->m_max * c->h * 2; break;
     case DFLASH_BUF_HIDDEN_LO: base = (const char*)c->Xn_lo; size = (size_t)c->m_max * c->h * 2; break;
+    case DFLASH_BUF_FP8_LMHEAD:
+      if (!c->fp8) return fail(c, DFLASH_EINVAL, "not an FP8 context");
+      base = (const char*)c->lm_q; size = (size_t)(c->V + 15) / 16 * 16 * c->h; break;
+    case DFLASH_BUF_FP8_LMHEAD_SCALE:
+      if (!c->fp8) return fail(c, DFLASH_EINVAL, "not an FP8 context");
+      base = (const char*)c->lm_s; size = (size_t)(c->V + 15) / 16 * 16 * 4; break;
     default: return fail(c, DFLASH_EINVAL, "unknown buffer %d", buffer);
   }
   if (offset > size || bytes > size - offset) return fail(c, DFLASH_ERANGE, "copy past the end of buffer %d", buffer);
@@ -853,13 +896,14 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   auto parts = [&](const GemmPlan& p) {
     return wide ? std::make_pair(gemm_wide_groups(p.K, p.gsz), 1) : std::make_pair(p.S, p.gsz);
   };
-  auto gemm = [&](const bf16* A, const bf16* A_lo, int lda, const bf16* W, const GemmPlan& p,
+  // wsc: W holds FP8 codes with these row scales
+  auto gemm = [&](const bf16* A, const bf16* A_lo, int lda, const bf16* W, const float* wsc, const GemmPlan& p,
                   bool normed) -> hipError_t {
     const long long ps = (long long)M * p.N;
     if (wide) {
       const NormIn nn{c->ssq, c->eps, c->h};
       return timed(c, DFLASH_K_GEMM, st, [&] {
-        return launch_gemm_wide(A, A_lo, lda, M, W, p.N, p.K, p.gsz, c->part, ps, st, normed ? &nn : nullptr);
+        return launch_gemm_wide(A, A_lo, lda, M, W, p.N, p.K, p.gsz, c->part, ps, st, normed ? &nn : nullptr, wsc);
       });
     }
     for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
@@ -867,7 +911,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       const NormIn nn{c->ssq + (size_t)r0 * SSQ_STRIDE, c->eps, c->h};
       hipError_t e = timed(c, DFLASH_K_GEMM, st, [&] {
         return launch_gemm_skinny(A + (size_t)r0 * lda, A_lo + (size_t)r0 * lda, lda, mg, W, p.N, p.K, p.klen,
-                                  c->part + (size_t)r0 * p.N, ps, true, st, normed ? &nn : nullptr);
+                                  c->part + (size_t)r0 * p.N, ps, true, st, normed ? &nn : nullptr, wsc);
       });
       if (e != hipSuccess) return e;
     }
@@ -876,7 +920,8 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   for (int l = 0; l < c->L; ++l) {
     const LayerDev& d = c->layers[l];
     const int sw = sliding_layer(c, l) ? 1 : 0;
-    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_qkv, c->g_qkv, true));
+    const bool q8 = c->fp8;
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, q8 ? (const bf16*)d.q_qkv : d.w_qkv, q8 ? d.s_qkv : nullptr, c->g_qkv, true));
     HIPCHK(c, timed(c, DFLASH_K_QKV_POST, st, [&] {
       return launch_qkv_post(c->part, parts(c->g_qkv).first, (long long)M * c->g_qkv.N, parts(c->g_qkv).second,
                              M, gamma, c->bands_dev,
@@ -891,17 +936,18 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       return launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
     }));
-    HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, d.o_proj, c->g_o, false));
+    HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, q8 ? (const bf16*)d.q_o : d.o_proj, q8 ? d.s_o : nullptr, c->g_o, false));
     HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
       return launch_resid_sum(c->X, c->part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
                               M, c->h, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
     }));
-    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, d.w_gu, c->g_gu, true));
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, q8 ? (const bf16*)d.q_gu : d.w_gu, q8 ? d.s_gu : nullptr, c->g_gu, true));
     HIPCHK(c, timed(c, DFLASH_K_SILU, st, [&] {
       return launch_silu_mul(c->part, parts(c->g_gu).first, (long long)M * c->g_gu.N, parts(c->g_gu).second, M,
                              c->ff, c->act, c->act_lo, st);
     }));
-    HIPCHK(c, gemm(c->act, c->act_lo, c->ff, d.down_proj, c->g_down, false));
+    HIPCHK(c, gemm(c->act, c->act_lo, c->ff, q8 ? (const bf16*)d.q_down : d.down_proj, q8 ? d.s_down : nullptr,
+                   c->g_down, false));
     if (l + 1 < c->L) {
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
         return launch_resid_sum(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
@@ -917,18 +963,22 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     }
   }
   // one row group of at most 16 rows with the rows in LDS whole: the persistent lm_head;
-  // more than one row group: the wide lm_head; otherwise one launch per row group
+  // more than one row group (or FP8 weights beyond the persistent form): the wide lm_head;
+  // otherwise one launch per row group
   const int ng_p = lmhead_persistent_groups(c->V, c->h, M, c->n_cu);
-  const int ng = wide ? lmhead_wide_groups(c->V) : ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
-  if (wide) {
+  const bool lm_wide = wide || (c->fp8 && ng_p == 0);
+  const int ng = lm_wide ? lmhead_wide_groups(c->V) : ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
+  const bf16* lmw = c->fp8 ? (const bf16*)c->lm_q : c->lm_head;
+  const float* lms = c->fp8 ? c->lm_s : nullptr;
+  if (lm_wide) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
-      return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, c->lm_head, c->V, c->h, c->best_v, c->best_i, ng, gamma,
-                                logits, st);
+      return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, lmw, c->V, c->h, c->best_v, c->best_i, ng, gamma,
+                                logits, st, lms);
     }));
   } else if (ng_p > 0) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
-      return launch_lmhead_persistent(c->Xn, c->Xn_lo, c->h, M, 0, c->lm_head, c->V, c->h, c->best_v, c->best_i,
-                                      ng, gamma, logits, st);
+      return launch_lmhead_persistent(c->Xn, c->Xn_lo, c->h, M, 0, lmw, c->V, c->h, c->best_v, c->best_i,
+                                      ng, gamma, logits, st, lms);
     }));
   } else {
     for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {

@@ -78,7 +78,18 @@ typedef struct {
   const int32_t *page_order;       /* host [num_pages-1]: free-list order, a permutation of
                                       1..num_pages-1; NULL = ascending. Page 0 is a zeroed
                                       sentinel and is never handed out. */
+  int32_t weight_format;           /* DFLASH_WEIGHTS_BF16 or DFLASH_WEIGHTS_FP8_E4M3 */
 } dflash_config;
+
+/* Weight formats (metrale_model_arch/dflash_head/from_weights.rs, DflashQuantization and the
+ * FP8 weights phase of from_weights): with DFLASH_WEIGHTS_FP8_E4M3 the seven per-layer GEMM
+ * weights (q, k, v, o, gate, up, down) and the lm_head are quantized once at create to OCP
+ * FP8 E4M3 codes with one fp32 scale per row: scale = max|row| / 448 (1 for an all-zero row),
+ * code = the nearest E4M3 value of w / scale (fp32 division), ties to even, saturating at
+ * +-448; the GEMMs use code value x scale. Activations, the KV cache, the context-append
+ * weights (fc, the fused K/V weight) and the norms stay bf16. The caller's weights are
+ * still bf16. */
+enum { DFLASH_WEIGHTS_BF16 = 0, DFLASH_WEIGHTS_FP8_E4M3 = 1 };
 
 /* Per-layer weights, device bf16. q/k/v/o/gate/up/down are [out, in]; norms [hidden]
  * or [head_dim] (q_norm, k_norm). Matrices (here and fc, embed_tokens, lm_head below)
@@ -186,9 +197,15 @@ int dflash_pool_geometry(const dflash_ctx *ctx, int64_t *num_pages, int64_t *pag
  *   DFLASH_BUF_BLOCKTAB  int32 [max_batch][pages_per_seq]: the device block tables;
  *   DFLASH_BUF_HIDDEN    bf16 [rows][hidden]: the final-normed hidden rows of the last
  *                        forward (debug seam), high bf16 term;
- *   DFLASH_BUF_HIDDEN_LO the same rows' low bf16 term (hidden = high + low). */
+ *   DFLASH_BUF_HIDDEN_LO the same rows' low bf16 term (hidden = high + low);
+ *   DFLASH_BUF_FP8_LMHEAD (FP8 contexts) the lm_head's E4M3 codes, uint8 in the T16-FP8
+ *                        layout: vocab rows in tiles of 16, a tile's hidden dimension in
+ *                        256-deep blocks of 4096 bytes, byte (q*64 + lane)*16 + b of a block
+ *                        holding row lane%16 at k = 64q + 32*(b/8) + 8*(lane/16) + b%8;
+ *   DFLASH_BUF_FP8_LMHEAD_SCALE (FP8 contexts) float [vocab rounded up to 16]: the row scales. */
 enum { DFLASH_BUF_POOL = 0, DFLASH_BUF_KPOS = 1, DFLASH_BUF_SLOTS = 2,
-       DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4, DFLASH_BUF_HIDDEN_LO = 5 };
+       DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4, DFLASH_BUF_HIDDEN_LO = 5,
+       DFLASH_BUF_FP8_LMHEAD = 6, DFLASH_BUF_FP8_LMHEAD_SCALE = 7 };
 int dflash_debug_copy(dflash_ctx *ctx, int32_t buffer, void *dst, size_t offset, size_t bytes,
                       void *stream);
 

@@ -80,6 +80,71 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------
+# FP8 weights ([metrale-fw] from_weights, the FP8 weights phase; DflashQuantization)
+# ----------------------------------------------------------------------------------
+# OCP FP8 E4M3 ("E4M3FN"): sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+# infinities; codes 0x7F and 0xFF are NaN; the largest finite value is 448 (0x7E);
+# exponent field 0 holds the subnormals m * 2^-9.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each E4M3 code, from the format's definition, in float64."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))   # the 127 non-negative finite values, ascending
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of each (finite) value, ties to the even code, saturating at +-448;
+    the sign of x (also of zero) is kept."""
+    x = np.asarray(x)
+    a = np.minimum(np.abs(x).astype(np.float64), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    dl, dh = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    code = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_encode_f32(x: np.ndarray) -> np.ndarray:
+    """e4m3_encode for float32 input, by rounding the binary32 bits (the test suite checks it
+    against e4m3_encode on dense samples and at every rounding boundary): below 2^-6 the
+    E4M3 values are the multiples of 2^-9 (round-half-even of x * 512); from 2^-6 on, the
+    3 leading mantissa bits rounded half to even, the exponent rebiased from 127 to 7; at
+    448 and above, 448."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x)
+    b = a.view(np.uint32)
+    normal = ((b + np.uint32(0x7FFFF) + ((b >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)).astype(np.int32) - 960
+    code = np.where(a < np.float32(2.0 ** -6), np.rint(a * np.float32(512.0)).astype(np.int32), np.minimum(normal, 0x7E))
+    code = np.where(a >= np.float32(E4M3_MAX), 0x7E, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_fp8(bits: np.ndarray):
+    """Per-row FP8 quantization of a bf16 [N, K] weight, in float32 (the precision the
+    pages keep the row scales in): scale = max|row| / 448 (1 for an all-zero row), codes =
+    nearest E4M3 of w / scale. Returns (codes uint8 [N, K], scale float32 [N])."""
+    w = widen(bits, np.float32)
+    amax = np.abs(w).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    return e4m3_encode_f32(w / scale[:, None]), scale
+
+
+def dequant_fp8(codes: np.ndarray, scale: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """The weight an FP8 GEMM uses: code value x row scale (exact in float64)."""
+    return (e4m3_decode(codes) * scale.astype(np.float64)[:, None]).astype(dtype)
+
+
+# ----------------------------------------------------------------------------------
 # elementary steps
 # ----------------------------------------------------------------------------------
 
@@ -316,6 +381,26 @@ class Drafter:
     def lw(self, l: int, name: str) -> np.ndarray:
         return self.w(f"layers.{l}.{name}")
 
+    # the matrices the FP8 weight format quantizes: the block forward's seven per-layer
+    # GEMMs and the lm_head ([metrale-fw] from_weights); the context append keeps bf16
+    FP8_NAMES = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+    def fw(self, name: str) -> np.ndarray:
+        """A weight of the block forward's GEMMs: bf16, or dequantized FP8 under
+        weight_format "fp8"."""
+        if self.m.get("weight_format") != "fp8" or not (name == "lm_head" or name.split(".")[-1] in self.FP8_NAMES):
+            return self.w(name)
+        key = "fp8:" + name
+        if key in self._cache:
+            return self._cache[key]
+        a = dequant_fp8(*quantize_rows_fp8(self.bits[name]), dtype=self.dtype)
+        if self.cache_weights:
+            self._cache[key] = a
+        return a
+
+    def flw(self, l: int, name: str) -> np.ndarray:
+        return self.fw(f"layers.{l}.{name}")
+
     def cache_store(self, x: np.ndarray) -> np.ndarray:
         return round_bf16(x) if self.kv_bf16 else x
 
@@ -400,9 +485,9 @@ class Drafter:
         scale = 1.0 / math.sqrt(hd)
         for l in range(m["num_layers"]):
             xn = rms_norm(x, self.lw(l, "input_layernorm"), eps)
-            q = (xn @ self.lw(l, "q_proj").T).reshape(gamma, nh, hd)
-            kb = (xn @ self.lw(l, "k_proj").T).reshape(gamma, nkv, hd)
-            vb = (xn @ self.lw(l, "v_proj").T).reshape(gamma, nkv, hd)
+            q = (xn @ self.flw(l, "q_proj").T).reshape(gamma, nh, hd)
+            kb = (xn @ self.flw(l, "k_proj").T).reshape(gamma, nkv, hd)
+            vb = (xn @ self.flw(l, "v_proj").T).reshape(gamma, nkv, hd)
             q = self.rope_rows(rms_norm(q, self.lw(l, "q_norm"), eps), bpos[:, None])
             kb = self.rope_rows(rms_norm(kb, self.lw(l, "k_norm"), eps), bpos[:, None])
             k_all = np.concatenate([ctx_k[l], self.cache_store(kb)], axis=0)
@@ -410,22 +495,25 @@ class Drafter:
             k_pos = np.concatenate([np.asarray(ctx_pos, dtype=np.int64), bpos])
             win = int(m.get("sliding_window", 0) or 0) if self.sliding(l) else 0
             attn = gqa_attention(q, bpos, k_all, v_all, k_pos, scale, win).reshape(gamma, nh * hd)
-            x1 = x + attn @ self.lw(l, "o_proj").T
+            x1 = x + attn @ self.flw(l, "o_proj").T
             x1n = rms_norm(x1, self.lw(l, "post_attention_layernorm"), eps)
-            g = x1n @ self.lw(l, "gate_proj").T
-            u = x1n @ self.lw(l, "up_proj").T
-            x = x1 + (silu(g) * u) @ self.lw(l, "down_proj").T
+            g = x1n @ self.flw(l, "gate_proj").T
+            u = x1n @ self.flw(l, "up_proj").T
+            x = x1 + (silu(g) * u) @ self.flw(l, "down_proj").T
         return rms_norm(x, self.w("norm"), eps)
 
     def lm_head(self, y: np.ndarray, chunk: int = 16384) -> np.ndarray:
         """logits = y @ lm_head^T, the vocabulary taken in chunks (memory only)."""
         if self.cache_weights:
-            return y @ self.w("lm_head").T
+            return y @ self.fw("lm_head").T
         V = self.m["vocab"]
         out = np.empty((y.shape[0], V), dtype=self.dtype)
+        fp8 = self.m.get("weight_format") == "fp8"
         for s in range(0, V, chunk):
             e = min(V, s + chunk)
-            out[:, s:e] = y @ widen(self.bits["lm_head"][s:e], self.dtype).T
+            rows = self.bits["lm_head"][s:e]
+            wt = dequant_fp8(*quantize_rows_fp8(rows), dtype=self.dtype) if fp8 else widen(rows, self.dtype)
+            out[:, s:e] = y @ wt.T
         return out
 
 

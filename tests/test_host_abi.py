@@ -71,6 +71,12 @@ def test_create_rejects_bad_pool_arguments():
         cfg, keep = B.make_config(m, kw.get("max_seq", 128), kw.get("max_batch", 1), num_pages=kw.get("num_pages", 0))
         ctx = C.c_void_p()
         assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    # a weight format other than bf16 (0) and FP8 E4M3 (1)
+    for fmt in (2, 7, -1):
+        cfg, keep = B.make_config(m, 128, 1)
+        cfg.weight_format = fmt
+        ctx = C.c_void_p()
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL and not ctx.value
     # a page order that is not a permutation of 1..P-1 (P = 11 here)
     for order in ([1, 2, 3], list(range(0, 10)), [1] * 10):
         cfg, keep = B.make_config(m, 128, 1, page_order=order)
@@ -115,5 +121,6 @@ def test_config_struct_layout_matches_header():
     assert B.dflash_config.yarn_factor.offset == 64
     assert B.dflash_config.layer_sliding.offset == 104
     assert B.dflash_config.page_order.offset == 128
-    assert C.sizeof(B.dflash_config) == 136
+    assert B.dflash_config.weight_format.offset == 136
+    assert C.sizeof(B.dflash_config) == 144
     assert C.sizeof(B.dflash_layer_weights) == 88 and C.sizeof(B.dflash_weights) == 48

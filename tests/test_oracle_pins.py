@@ -621,3 +621,108 @@ def test_batched_append_refusals_change_nothing(tiny):
         e.ctx_kv_append_batch([1, 2], [2, 1], H[:3], positions=[40, 39, 0])
     assert ei.value.code == "EINVAL"
     assert state() == before
+
+
+# ---- FP8 E4M3 weights ([metrale-fw] from_weights, the FP8 weights phase) -------------------
+
+def test_e4m3_decode_table():
+    """OCP E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, largest finite 448, 0x7F/0xFF
+    NaN, no infinities."""
+    v = O.e4m3_decode(np.arange(256))
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x3C: 1.5,
+            0x40: 2.0, 0x7E: 448.0, 0x81: -(2.0 ** -9), 0xB8: -1.0, 0xFE: -448.0}
+    for c, want in hand.items():
+        assert v[c] == want, hex(c)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.signbit(v[0x80]) and v[0x80] == 0.0
+    # every code from the closed form, written out separately
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        mag = m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        assert v[c] == (-mag if s else mag)
+    fin = v[np.isfinite(v)]
+    assert fin.max() == 448.0 and np.all(np.diff(O.e4m3_decode(np.arange(0x7F))) > 0)
+
+
+def test_e4m3_encode_is_nearest_ties_to_even():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (2.0 ** -9, 0.02, 1.0, 100.0)])
+    pos = O.e4m3_decode(np.arange(0x7F))
+    got = O.e4m3_encode(x)
+    # brute force: the nearest of all 127 magnitudes (ties: the even code), signs kept
+    a = np.minimum(np.abs(x), 448.0)
+    d = np.abs(a[:, None] - pos[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    want = np.where(cand[:, ::2].any(axis=1) & (cand.sum(axis=1) > 1),
+                    np.argmax(cand & (np.arange(0x7F) % 2 == 0), axis=1), np.argmax(cand, axis=1))
+    want = (want | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+    assert np.array_equal(got, want)
+    # midpoints go to the even code; beyond 448 saturates; signed zero
+    mid = (pos[:-1] + pos[1:]) / 2
+    code = O.e4m3_encode(mid)
+    assert np.all(code % 2 == 0)
+    assert list(O.e4m3_encode(np.array([449.0, 1e30, -1e30, 0.0, -0.0]))) == [0x7E, 0x7E, 0xFE, 0x00, 0x80]
+    fin = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(np.array(fin))), np.array(fin, dtype=np.uint8))
+
+
+def test_e4m3_encode_f32_matches_reference():
+    """The engine's float32 encoder equals the nearest-value encoder at every rounding
+    boundary (each midpoint and its float32 neighbours, each value and its neighbours) and on
+    a dense random sample."""
+    pos = O.e4m3_decode(np.arange(0x7F)).astype(np.float32)
+    mid = ((pos[:-1].astype(np.float64) + pos[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([pos, mid, np.array([448.0 * 1.0001], np.float32), np.array([2.0 ** -6, 2.0 ** -10], np.float32)])
+    nb = np.concatenate([pts, np.nextafter(pts, np.float32(0)), np.nextafter(pts, np.float32(1e9))])
+    nb = np.concatenate([nb, -nb])
+    rng = np.random.default_rng(4)
+    dense = np.concatenate([(rng.standard_normal(400000) * s).astype(np.float32) for s in (1e-4, 3e-3, 0.1, 4.0, 200.0)])
+    for x in (nb, dense):
+        assert np.array_equal(O.e4m3_encode_f32(x), O.e4m3_encode(x))
+
+
+def test_fp8_row_quantization_properties():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((40, 512)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    w[7, 11] = -0.5                                  # a row whose maximum is negative
+    bits = synth.f32_to_bf16_bits(w)
+    codes, scale = O.quantize_rows_fp8(bits)
+    wb = O.widen(bits)
+    assert scale.dtype == np.float32 and scale[3] == 1.0 and not codes[3].any()
+    amax_code = codes[np.arange(40), np.abs(wb).argmax(axis=1)]
+    assert np.all((amax_code[np.arange(40) != 3] & 0x7F) == 0x7E) and codes[7, 11] == 0xFE
+    deq = O.dequant_fp8(codes, scale)
+    # error bound: half an E4M3 step: |w| * 2^-4 in the normal range, scale * 2^-10 below it
+    bound = np.maximum(np.abs(wb) * 2.0 ** -4, scale[:, None].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(deq - wb) <= bound)
+
+
+def test_fp8_forward_equals_bf16_on_lossless_weights_and_leaves_the_append(tiny):
+    """FP8 quantizes exactly the forward's seven GEMM weights and the lm_head: on weights that
+    FP8 represents exactly (rows of E4M3 values times a power of two, the row maximum 448
+    times it) the FP8 forward is the bf16 forward; on random weights the forward changes and
+    the context K/V (the append keeps bf16) do not."""
+    m, W = tiny
+    rng = np.random.default_rng(6)
+    Wx = dict(W)
+    for name in list(W):
+        if name == "lm_head" or name.split(".")[-1] in O.Drafter.FP8_NAMES:
+            n, k = W[name].shape
+            codes = rng.integers(0, 0x7E, size=(n, k)) | (rng.integers(0, 2, size=(n, k)) << 7)
+            codes[:, 0] = 0x7E                       # the row maximum: 448
+            vals = O.e4m3_decode(codes) * 2.0 ** -14
+            Wx[name] = synth.f32_to_bf16_bits(vals.astype(np.float32))
+    H = synth.gen_hidden(m, 1001, 40)
+    out = {}
+    for fmt in ("bf16", "fp8"):
+        for tag, weights in (("exact", Wx), ("random", W)):
+            e = O.Engine(dict(m, weight_format=fmt), weights, 64, 1)
+            e.ctx_kv_append(0, H)
+            out[fmt, tag] = (e.block_forward([0], [5], gamma=16)["logits"], e.seqs[0]["k"][1], e.seqs[0]["v"][1])
+    assert np.array_equal(out["fp8", "exact"][0], out["bf16", "exact"][0])
+    assert np.array_equal(out["fp8", "random"][1], out["bf16", "random"][1])
+    assert np.array_equal(out["fp8", "random"][2], out["bf16", "random"][2])
+    assert np.abs(out["fp8", "random"][0] - out["bf16", "random"][0]).max() > 1e-4
