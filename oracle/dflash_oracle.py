@@ -447,7 +447,7 @@ class Drafter:
     # -- one gamma block ------------------------------------------------------------
 
     def block_forward(self, ctx_k, ctx_v, ctx_pos, bonus: int, q_rope_pos: int, gamma: int,
-                      want_hidden: bool = False):
+                      want_hidden: bool = False, markov_prev=None):
         """One band: block [bonus, mask x (gamma-1)] through every layer, final norm,
         lm_head on rows 1..gamma-1, argmax.
 
@@ -462,10 +462,37 @@ class Drafter:
         bpos = q_rope_pos + np.arange(gamma, dtype=np.int64)
         y = self.block_hidden(ctx_k, ctx_v, ctx_pos, toks, bpos)
         logits = self.lm_head(y[1:])
-        res = dict(logits=logits, tokens=argmax_lowest(logits))
+        if self.m.get("markov_rank", 0):
+            logits, drafts = self.markov_chain(logits, bonus, markov_prev)
+        else:
+            drafts = argmax_lowest(logits)
+        res = dict(logits=logits, tokens=drafts)
         if want_hidden:
             res["hidden"] = y
         return res
+
+    def markov_chain(self, logits: np.ndarray, bonus: int, prev=None):
+        """DSpark semi-autoregressive Markov head, greedy ([memra] DflashDraft's `markov` head
+        and the chain in generate_spec_dflash; [atlas-head] the head's markov_w1 / markov_w2
+        fields). W1 [V, R] is a table indexed by the previous token, W2 [V, R] maps the
+        rank-R latent to the vocabulary. Left to right over the drafted rows k = 0..g-1:
+        row k's logits get W2 @ W1[t_k], where t_0 is the bonus token and t_k the token
+        drafted at row k-1, and the draft at row k is the argmax of the biased row. The
+        bias stays in the logits' precision (READING c20).
+
+        prev: optional [g] tokens that replace t_k (teacher forcing, for comparing against
+        a run whose chain took another branch at a near-tie); drafts are still each
+        biased row's argmax. Returns (biased logits [g, V], drafts [g])."""
+        out = np.array(logits, dtype=self.dtype, copy=True)
+        drafts = np.empty(out.shape[0], dtype=np.int32)
+        w2 = self.w("markov_w2")
+        t = int(bonus)
+        for k in range(out.shape[0]):
+            tk = t if prev is None else int(prev[k])
+            out[k] += w2 @ widen(self.bits["markov_w1"][tk], self.dtype)
+            drafts[k] = argmax_lowest(out[k])
+            t = int(drafts[k])
+        return out, drafts
 
     def block_hidden(self, ctx_k, ctx_v, ctx_pos, toks, bpos):
         """Final-normed hidden rows [T, h] of a block with explicit token ids `toks` [T]
@@ -631,7 +658,10 @@ class Engine:
             r += c
         self.last_slots = np.concatenate(slots)
 
-    def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False):
+    def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False, markov_prev=None):
+        """The C ABI's block forward over bands `seqs`. markov_prev (DSpark heads only):
+        optional [n, gamma-1] previous tokens per band for the Markov chain (teacher
+        forcing; see Drafter.markov_chain)."""
         m = self.m
         gamma = m["gamma_max"] if gamma is None else gamma
         seqs = [int(x) for x in seqs]
@@ -659,7 +689,8 @@ class Engine:
             C = self.kv_len(x)
             P = C if q_rope_pos is None else int(q_rope_pos[i])
             outs.append(self.d.block_forward(s["k"], s["v"], s["pos"], int(bonus[i]), P, gamma,
-                                             want_hidden=want_hidden))
+                                             want_hidden=want_hidden,
+                                             markov_prev=None if markov_prev is None else markov_prev[i]))
         res = dict(tokens=np.stack([o["tokens"] for o in outs]),
                    logits=np.stack([o["logits"] for o in outs]))
         if want_hidden:

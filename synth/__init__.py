@@ -8,7 +8,8 @@ drafter's arithmetic lives here. Every tensor is returned as bf16 bit patterns
 Recipe:
   * generator: numpy PCG64 seeded with SeedSequence([seed, stream, index]);
     float32 draws rounded to bf16 with round-to-nearest-even;
-  * weight matrices ~ N(0, 0.02); norm weights ~ 1 + N(0, 0.02);
+  * weight matrices ~ N(0, 0.02); norm weights ~ 1 + N(0, 0.02); a DSpark Markov head's
+    token table ~ N(0, 1) and its projection ~ N(0, 0.03);
   * tapped target hidden states ~ N(0, 1);
   * bonus tokens uniform over the vocabulary; context lengths uniform over the
     workload's range; the pool's page order is a seeded permutation.
@@ -54,6 +55,10 @@ MODELS = {
     "tiny-L2-h256": _TINY,
     "qwen3-L8-h2048": _QWEN3_8L_2048,
     "wide-L5-h5376-yarn-swa2048": _WIDE_5L_5376,
+    # the same drafters with a DSpark Markov head of rank 256 (the rank the pages quote);
+    # their other weights are the same draws as the plain models' under the same seed
+    "tiny-L2-h256-dspark": dict(_TINY, markov_rank=256),
+    "qwen3-L8-h2048-dspark": dict(_QWEN3_8L_2048, markov_rank=256),
 }
 
 # A workload = a model, how many sequences one forward call carries, how their
@@ -175,29 +180,39 @@ def weight_specs(m: dict):
             (p + "up_proj", (ff, h), "mat"),
             (p + "down_proj", (h, ff), "mat"),
         ]
+    if m.get("markov_rank", 0):
+        # DSpark Markov head: a previous-token embedding table and a latent-to-vocabulary
+        # projection, both [vocab, rank]
+        specs += [("markov_w1", (m["vocab"], m["markov_rank"]), "embed"),
+                  ("markov_w2", (m["vocab"], m["markov_rank"]), "proj")]
     return specs
+
+
+# (mean, standard deviation) of each kind of tensor
+_KIND_DIST = {"mat": (0.0, 0.02), "norm": (1.0, 0.02), "embed": (0.0, 1.0), "proj": (0.0, 0.03)}
 
 
 def _weight_args(m: dict, name: str):
     for i, (n, shape, kind) in enumerate(weight_specs(m)):
         if n == name:
-            return i, shape, (0.0 if kind == "mat" else 1.0)
+            return (i, shape) + _KIND_DIST[kind]
     raise KeyError(name)
 
 
 def gen_weight(m: dict, seed: int, name: str) -> np.ndarray:
-    """Weight `name`: matrices N(0, 0.02), norm weights 1 + N(0, 0.02); tensor i of the
-    fixed order draws from stream S_WEIGHTS, index i."""
-    i, shape, mean = _weight_args(m, name)
-    return _normal_bf16(seed, S_WEIGHTS, i, shape, mean, 0.02)
+    """Weight `name`: matrices N(0, 0.02), norm weights 1 + N(0, 0.02), the Markov head's
+    token table N(0, 1) and its projection N(0, 0.03) (a bias of about the logits' spread);
+    tensor i of the fixed order draws from stream S_WEIGHTS, index i."""
+    i, shape, mean, std = _weight_args(m, name)
+    return _normal_bf16(seed, S_WEIGHTS, i, shape, mean, std)
 
 
 def gen_weights(m: dict, seed: int) -> dict:
     """All weights, every block of every tensor drawn in parallel."""
     pending = {}
     for n, _, _ in weight_specs(m):
-        i, shape, mean = _weight_args(m, n)
-        pending[n] = _normal_bf16(seed, S_WEIGHTS, i, shape, mean, 0.02, wait=False)
+        i, shape, mean, std = _weight_args(m, n)
+        pending[n] = _normal_bf16(seed, S_WEIGHTS, i, shape, mean, std, wait=False)
     out = {}
     for n, (arr, futs) in pending.items():
         for f in futs:

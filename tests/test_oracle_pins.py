@@ -726,3 +726,84 @@ def test_fp8_forward_equals_bf16_on_lossless_weights_and_leaves_the_append(tiny)
     assert np.array_equal(out["fp8", "random"][1], out["bf16", "random"][1])
     assert np.array_equal(out["fp8", "random"][2], out["bf16", "random"][2])
     assert np.abs(out["fp8", "random"][0] - out["bf16", "random"][0]).max() > 1e-4
+
+
+# ---- DSpark Markov head ([memra] DflashDraft's markov head and generate_spec_dflash's chain) ----
+
+@pytest.fixture(scope="module")
+def dspark():
+    m = synth.model("tiny-L2-h256-dspark")
+    return m, synth.gen_weights(m, 1201)
+
+
+def _dspark_engine(m, W, n_ctx=24, seed=1201):
+    e = O.Engine(m, W, 64, 2)
+    e.ctx_kv_append(0, synth.gen_hidden(m, seed, n_ctx, 3))
+    e.ctx_kv_append(1, synth.gen_hidden(m, seed, n_ctx + 9, 4))
+    return e
+
+
+def test_markov_chain_by_the_full_bias_table(dspark):
+    """Brute force: Bias[t, v] = <W1[t], W2[v]> for every previous token t at once (one
+    [V, V] product), then the greedy walk t_{k+1} = argmax_v(L_k[v] + Bias[t_k, v]) from
+    the bonus token over the head-less logits L."""
+    m, W = dspark
+    plain = dict(m, markov_rank=0)
+    Wp = {k: v for k, v in W.items() if not k.startswith("markov")}
+    bonus = [17, 900]
+    got = _dspark_engine(m, W).block_forward([0, 1], bonus, gamma=16)
+    base = _dspark_engine(plain, Wp).block_forward([0, 1], bonus, gamma=16)
+    table = O.widen(W["markov_w1"]) @ O.widen(W["markov_w2"]).T        # [V prev, V next]
+    for b in range(2):
+        t = bonus[b]
+        for k in range(15):
+            row = base["logits"][b, k] + table[t]
+            want = int(np.argmax(row))
+            assert got["tokens"][b, k] == want
+            np.testing.assert_allclose(got["logits"][b, k], row, rtol=0, atol=1e-12)
+            t = want
+    # the head changes the drafts (the bias is of the logits' size)
+    assert (got["tokens"] != base["tokens"]).mean() > 0.3
+
+
+def test_markov_planted_walk(dspark):
+    """W1[t] = 64 e_(t mod R) and W2[v, j] = 1 iff v = j + 1: the bias is 64 on token t + 1
+    and 0 elsewhere, far above the logits' spread, so the drafts walk bonus+1, bonus+2, ...
+    This fixes which table the previous token indexes, which one the vocabulary indexes,
+    and that row k takes the token drafted at row k-1."""
+    m, W = dspark
+    V, R = m["vocab"], m["markov_rank"]
+    w1 = np.zeros((V, R), np.float32)
+    w1[np.arange(V), np.arange(V) % R] = 64.0
+    w2 = np.zeros((V, R), np.float32)
+    w2[np.arange(1, R + 1), np.arange(R)] = 1.0
+    Wx = dict(W, markov_w1=synth.f32_to_bf16_bits(w1), markov_w2=synth.f32_to_bf16_bits(w2))
+    e = _dspark_engine(m, Wx)
+    res = e.block_forward([0, 1], [40, 200], gamma=16)
+    assert np.abs(res["logits"]).max() > 60
+    assert res["tokens"].tolist() == [list(range(41, 56)), list(range(201, 216))]
+    # transposed roles (W2 gathered by the previous token) would not walk
+    assert not np.array_equal(O.widen(Wx["markov_w1"]), O.widen(Wx["markov_w2"]))
+
+
+def test_markov_zero_head_is_plain_dflash_and_teacher_forcing_is_consistent(dspark):
+    m, W = dspark
+    V, R = m["vocab"], m["markov_rank"]
+    zero = dict(W, markov_w2=np.zeros((V, R), np.uint16))
+    plain = dict(m, markov_rank=0)
+    Wp = {k: v for k, v in W.items() if not k.startswith("markov")}
+    a = _dspark_engine(m, zero).block_forward([1, 0], [5, 6], gamma=9)
+    b = _dspark_engine(plain, Wp).block_forward([1, 0], [5, 6], gamma=9)
+    assert np.array_equal(a["tokens"], b["tokens"]) and np.array_equal(a["logits"], b["logits"])
+    # forcing the chain onto its own tokens changes nothing; forcing other tokens changes
+    # the rows after the first, and row 0 (the bonus's row) never
+    e = _dspark_engine(m, W)
+    free = e.block_forward([0, 1], [5, 6], gamma=9)
+    prev = np.concatenate([[[5], [6]], free["tokens"][:, :-1]], axis=1)
+    forced = e.block_forward([0, 1], [5, 6], gamma=9, markov_prev=prev)
+    assert np.array_equal(forced["tokens"], free["tokens"]) and np.array_equal(forced["logits"], free["logits"])
+    other = prev.copy()
+    other[:, 1:] = (other[:, 1:] + 1) % V
+    f2 = e.block_forward([0, 1], [5, 6], gamma=9, markov_prev=other)
+    assert np.array_equal(f2["logits"][:, 0], free["logits"][:, 0])
+    assert not np.allclose(f2["logits"][:, 1:], free["logits"][:, 1:])
