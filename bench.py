@@ -84,6 +84,13 @@ def gemm_weight_elems(m):
     return ((qd + 2 * kvd) * h + h * qd + 2 * ff * h + h * ff) * m["num_layers"]
 
 
+def markov_bytes(m, n_bands, gamma):
+    """Algorithmic bytes of a DSpark chain: per drafted row, W2 [V, R] bf16 once for all
+    bands, each band's logits row read and W1 row gathered."""
+    V, R = m["vocab"], m["markov_rank"]
+    return (gamma - 1) * (V * R * 2 + n_bands * (V * 4 + R * 2))
+
+
 def lmhead_bytes(m, M, fp8=False):
     w = m["vocab"] * (m["hidden"] + 4) if fp8 else m["vocab"] * m["hidden"] * 2
     return w + M * m["hidden"] * 2
@@ -169,6 +176,7 @@ def main():
     ap.add_argument("--no-batch16", action="store_true")
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 E4M3 weight-only lines")
+    ap.add_argument("--no-dspark", action="store_true", help="skip the DSpark Markov-head lines")
     ap.add_argument("--longctx-only", action="store_true",
                     help="only run the 32-sequence long-context section and print its JSON (for counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -314,10 +322,20 @@ def main():
     if not args.no_longctx:
         out["longctx"] = bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev)
     if not args.no_fp8:
-        out["fp8"] = dict(batch1=bench_fp8_b1(m, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev))
+        mf = dict(m, weight_format="fp8")
+        out["fp8"] = dict(batch1=bench_variant_b1(mf, "fp8", Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch,
+                                                  to_dev))
         if not args.no_batch16:
-            out["fp8"]["batch16"] = bench_batch16(dict(m, weight_format="fp8"), Wd, gamma, a, args, B, torch, np,
-                                                  synth, to_dev)
+            out["fp8"]["batch16"] = bench_batch16(mf, Wd, gamma, a, args, B, torch, np, synth, to_dev)
+    if not args.no_dspark:
+        # the same trunk with a rank-256 Markov head (its two tables drawn from the same seed)
+        md = synth.model("qwen3-L8-h2048-dspark")
+        Wdd = dict(Wd, **{k: to_dev(synth.gen_weight(md, w["seed"], k)) for k in ("markov_w1", "markov_w2")})
+        out["dspark"] = dict(batch1=bench_variant_b1(md, "dspark", Wdd, H_ctx, H_steps, bonus, a, gamma, args, B,
+                                                     torch, to_dev))
+        if not args.no_batch16:
+            out["dspark"]["batch16"] = bench_batch16(md, Wdd, gamma, a, args, B, torch, np, synth, to_dev)
+        del Wdd
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
@@ -325,16 +343,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_fp8_b1(m, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev):
-    """The batch-1 step with FP8 E4M3 weights (the seven layer GEMMs and the lm_head
-    quantized at create; append, attention, norms and activations stay bf16): the same
-    inputs, plain launches timed, then one pass with every launch bracketed for the
-    per-class times and the weight-stream rates of the GEMM and lm_head classes."""
-    mf = dict(m, weight_format="fp8")
+def bench_variant_b1(mv, label, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev):
+    """The batch-1 step of a variant of the drafter (`mv`: the model with FP8 E4M3 trunk
+    weights, or with a DSpark Markov head): the same inputs, plain launches timed, then one
+    pass with every launch bracketed for the per-class times and the stream rates of the
+    classes the variant changes."""
     steps = args.steps
     total = args.warmup + 2 * steps + 8
     ctx = H_ctx.shape[0]
-    d = B.Drafter(mf, Wd, ctx + total * a + gamma + 16, 1)
+    d = B.Drafter(mv, Wd, ctx + total * a + gamma + 16, 1)
     d.dflash_ctx_kv_append(0, to_dev(H_ctx))
     Hs = to_dev(H_steps)
     toks = torch.empty((1, gamma - 1), dtype=torch.int32, device="cuda:0")
@@ -363,16 +380,24 @@ def bench_fp8_b1(m, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev)
     d.close()
     blocks = steps / el
     ms = {k: v[0] / steps for k, v in br.items() if v[1]}
+    fp8 = mv.get("weight_format") == "fp8"
+    streams = []
+    if fp8:
+        streams += [("gemm", gemm_bytes(mv, gamma, fp8=True)), ("lmhead", lmhead_bytes(mv, gamma, fp8=True))]
+    if mv.get("markov_rank", 0):
+        streams.append(("markov", markov_bytes(mv, 1, gamma)))
     rates = {}
-    for k, nbytes in (("gemm", gemm_bytes(m, gamma, fp8=True)), ("lmhead", lmhead_bytes(m, gamma, fp8=True))):
+    for k, nbytes in streams:
         if k in ms:
             rates[k] = dict(algorithmic_bytes_per_step=int(nbytes), gbs=round(nbytes / (ms[k] * 1e-3) / 1e9, 1),
                             frac=round(nbytes / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
-    log(f"[bench] fp8 batch1: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; "
+    if "markov" in br and br["markov"][1]:
+        rates["markov"]["avg_launch_us"] = round(br["markov"][0] / br["markov"][1] * 1e3, 3)
+    log(f"[bench] {label} batch1: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; "
         + ", ".join(f"{k} {v['gbs']:.0f} GB/s" for k, v in rates.items()))
-    return dict(workload=WORKLOAD, weight_format="fp8_e4m3", value=round(blocks, 2), unit="blocks/s",
+    return dict(workload=WORKLOAD, variant=label, value=round(blocks, 2), unit="blocks/s",
                 steps=steps, ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
-                kernels_ms_per_step={k: round(v, 4) for k, v in ms.items()}, weight_stream=rates,
+                kernels_ms_per_step={k: round(v, 4) for k, v in ms.items()}, streams=rates,
                 timing="value from plain launches; per-class times from a second, bracketed pass")
 
 
@@ -437,7 +462,8 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     d.close()
     blocks = nb * steps / el
     wbytes = 1 if m.get("weight_format") == "fp8" else 2
-    log(f"[bench] batch16 ({'fp8' if wbytes == 1 else 'bf16'}): {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; append of {nb}x{a} rows: "
+    variant = "fp8" if wbytes == 1 else "dspark" if m.get("markov_rank", 0) else "bf16"
+    log(f"[bench] batch16 ({variant}): {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; append of {nb}x{a} rows: "
         f"batched {app['batched']:.3f} ms, per sequence {app['per_seq']:.3f} ms")
     gemm_ms = br["gemm"][0] / steps
     M = nb * gamma
@@ -446,14 +472,21 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
                       tflops=round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 1),
                       mfma_frac=round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                       weight_gbs=round(gemm_weight_elems(m) * wbytes / (gemm_ms * 1e-3) / 1e9, 1))
-    return dict(workload=WORKLOAD_B16, weight_format="fp8_e4m3" if wbytes == 1 else "bf16", value=round(blocks, 2), unit="blocks/s", steps=steps,
+    extra = {}
+    if m.get("markov_rank", 0) and br.get("markov", (0, 0))[1]:
+        mk_ms = br["markov"][0] / steps
+        mk_b = markov_bytes(m, nb, gamma)
+        extra["markov"] = dict(ms_per_step=round(mk_ms, 4), algorithmic_bytes_per_step=int(mk_b),
+                               gbs=round(mk_b / (mk_ms * 1e-3) / 1e9, 1),
+                               avg_launch_us=round(br["markov"][0] / br["markov"][1] * 1e3, 3))
+    return dict(workload=WORKLOAD_B16, variant=variant, value=round(blocks, 2), unit="blocks/s", steps=steps,
                 ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
                 ctx_lengths=[int(x) for x in lens], timing="all launch classes bracketed by events",
                 append=dict(rows=nb * a, form="one batched call" if batched else "per sequence",
                             batched_ms=round(app["batched"], 4), per_seq_loop_ms=round(app["per_seq"], 4),
                             timing="wall clock, 10 calls, nothing bracketed"),
                 layer_gemms=gemm_stats,
-                kernels_ms_per_step={k: round(v[0] / steps, 4) for k, v in br.items() if v[1]})
+                kernels_ms_per_step={k: round(v[0] / steps, 4) for k, v in br.items() if v[1]}, **extra)
 
 
 def bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev):

@@ -29,6 +29,7 @@ class dflash_config(C.Structure):
         ("sliding_window", C.c_int32), ("layer_sliding", C.POINTER(C.c_uint8)),
         ("max_seq_len", C.c_int32), ("max_batch", C.c_int32), ("num_pages", C.c_int32),
         ("page_order", C.POINTER(C.c_int32)), ("weight_format", C.c_int32),
+        ("markov_rank", C.c_int32),
     ]
 
 
@@ -41,7 +42,8 @@ class dflash_layer_weights(C.Structure):
 class dflash_weights(C.Structure):
     _fields_ = [("fc", C.c_void_p), ("hidden_norm", C.c_void_p), ("norm", C.c_void_p),
                 ("embed_tokens", C.c_void_p), ("lm_head", C.c_void_p),
-                ("layers", C.POINTER(dflash_layer_weights))]
+                ("layers", C.POINTER(dflash_layer_weights)),
+                ("markov_w1", C.c_void_p), ("markov_w2", C.c_void_p)]
 
 
 _lib = None
@@ -87,7 +89,7 @@ EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch
             "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
 
 K_CLASSES = ("prologue", "gemm", "qkv_post", "attn", "attn_combine", "resid_norm", "silu",
-             "lmhead", "argmax", "append_gemm", "append_misc")
+             "lmhead", "argmax", "append_gemm", "append_misc", "markov")
 
 
 class DflashError(RuntimeError):
@@ -121,7 +123,8 @@ def make_config(m: dict, max_seq_len: int, max_batch: int, num_pages: int = 0, p
         layer_sliding=C.cast(ls_arr, C.POINTER(C.c_uint8)) if ls_arr is not None else None,
         max_seq_len=max_seq_len, max_batch=max_batch, num_pages=num_pages,
         page_order=C.cast(po, C.POINTER(C.c_int32)) if po is not None else None,
-        weight_format=DFLASH_WEIGHTS_FP8_E4M3 if m.get("weight_format") == "fp8" else DFLASH_WEIGHTS_BF16)
+        weight_format=DFLASH_WEIGHTS_FP8_E4M3 if m.get("weight_format") == "fp8" else DFLASH_WEIGHTS_BF16,
+        markov_rank=int(m.get("markov_rank", 0)))
     return cfg, (ls_arr, po)
 
 
@@ -155,6 +158,9 @@ class Drafter:
         w = dflash_weights(fc=weights["fc"].data_ptr(), hidden_norm=weights["hidden_norm"].data_ptr(),
                            norm=weights["norm"].data_ptr(), embed_tokens=weights["embed_tokens"].data_ptr(),
                            lm_head=weights["lm_head"].data_ptr(), layers=lay)
+        if m.get("markov_rank", 0):
+            w.markov_w1 = weights["markov_w1"].data_ptr()
+            w.markov_w2 = weights["markov_w2"].data_ptr()
         ctx = C.c_void_p()
         rc = self.L.dflash_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(ctx))
         if rc != DFLASH_OK:

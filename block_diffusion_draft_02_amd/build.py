@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
-SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "runtime.hip"]
+SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_markov.hip", "runtime.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

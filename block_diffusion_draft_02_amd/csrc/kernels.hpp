@@ -206,4 +206,23 @@ hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, 
                                  const long long* slots, const int* rowpos, KvGeom g,
                                  hipStream_t st);
 
+// ---- DSpark Markov chain (k_markov.hip) -----------------------------------------------
+// One drafted row k of every band: logits[b*(gamma-1)+k][:] += W2 @ W1[t], t = bonus[b] for
+// k = 0 and row k-1's draft otherwise; the row's argmax goes into key best[k][b] (a 64-bit
+// atomic max). k_markov_finish then writes tokens[b*(gamma-1)+k] for every row and clears
+// the keys (they are zero before the first step of a forward).
+constexpr int MARKOV_MAX_GROUPS = 1024;
+constexpr int MARKOV_MAX_ROWS = 15;   // gamma_max - 1
+struct MarkovStep {
+  const bf16* w1;              // [V, R] previous-token table (the caller's, row-major)
+  const bf16* w2t;             // W2 [V, R] in the T16 layout (rows padded to whole tiles)
+  float* logits;               // [n*(gamma-1), V] the lm_head's logits, biased in place when store
+  unsigned long long* best;    // [MARKOV_MAX_ROWS][MAX_BANDS] argmax keys
+  int V, R, n, gamma, k, store;
+  int bonus[MAX_BANDS];
+};
+int markov_step_groups(int V, int n_cu);
+hipError_t launch_markov_step(const MarkovStep& a, int groups, hipStream_t st);
+hipError_t launch_markov_finish(unsigned long long* best, int n, int gamma, int* tokens, hipStream_t st);
+
 }  // namespace dfl

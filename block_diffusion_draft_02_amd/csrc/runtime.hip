@@ -61,6 +61,13 @@ struct dflash_ctx {
   bool fp8 = false;          // weight_format 1: FP8 E4M3 forward weights and lm_head
   uint8_t* lm_q = nullptr;   // FP8: T16-FP8 lm_head codes and per-row scales
   float* lm_s = nullptr;
+  // DSpark Markov head (markov_rank R > 0)
+  int R = 0;
+  const bf16* mk_w1 = nullptr;   // [V, R] previous-token table (the caller's)
+  bf16* mk_w2t = nullptr;        // owned T16 copy of W2 [V, R]
+  float* mk_logits = nullptr;    // [max_batch*(gamma_max-1), V] logits when the caller wants none
+  unsigned long long* mk_best = nullptr;   // [MARKOV_MAX_ROWS][MAX_BANDS] argmax keys, zero between forwards
+  int mk_groups = 1;
   std::vector<LayerDev> layers;
   bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;... (row-major, for the tiled GEMM)
   bf16* w_kv_t = nullptr;      // the same in the T16 layout (short appends)
@@ -271,6 +278,9 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
   if (cfg->rope_type != 0 && cfg->rope_type != 1) return bad("rope_type must be 0 or 1");
   if (cfg->weight_format != DFLASH_WEIGHTS_BF16 && cfg->weight_format != DFLASH_WEIGHTS_FP8_E4M3)
     return bad("weight_format must be DFLASH_WEIGHTS_BF16 or DFLASH_WEIGHTS_FP8_E4M3");
+  if (cfg->markov_rank != 0 && cfg->markov_rank != 256 && cfg->markov_rank != 512)
+    return bad("markov_rank must be 0, 256 or 512");
+  if (cfg->markov_rank && (!w->markov_w1 || !w->markov_w2)) return bad("a Markov head needs markov_w1 and markov_w2");
   if (cfg->rope_type == 1 && !(cfg->yarn_factor > 0 && cfg->yarn_orig_max_pos > 0 &&
                                cfg->yarn_beta_fast > 0 && cfg->yarn_beta_slow > 0))
     return bad("YaRN parameters must be positive");
@@ -288,6 +298,7 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
   // matrices are streamed with 16-byte loads
   auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   if (!a16(w->fc) || !a16(w->embed_tokens) || !a16(w->lm_head)) return bad("head weight matrices must be 16-byte aligned");
+  if (cfg->markov_rank && (!a16(w->markov_w1) || !a16(w->markov_w2))) return bad("Markov head tables must be 16-byte aligned");
   for (int l = 0; l < cfg->num_layers; ++l) {
     const dflash_layer_weights& lw = w->layers[l];
     if (!a16(lw.q_proj) || !a16(lw.k_proj) || !a16(lw.v_proj) || !a16(lw.o_proj) || !a16(lw.gate_proj) ||
@@ -414,6 +425,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->V = cfg->vocab; c->T = cfg->num_taps; c->Ht = cfg->target_hidden; c->gmax = cfg->gamma_max;
   c->mask = cfg->mask_token_id; c->max_seq = cfg->max_seq_len; c->max_batch = cfg->max_batch;
   c->fp8 = cfg->weight_format == DFLASH_WEIGHTS_FP8_E4M3;
+  c->R = cfg->markov_rank;
+  c->mk_w1 = (const bf16*)w->markov_w1;
   c->eps = cfg->rms_eps; c->rope_type = cfg->rope_type; c->window = cfg->sliding_window;
   c->sliding.assign(c->L, 0);
   if (cfg->layer_sliding)
@@ -502,6 +515,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
                     (rc = dalloc(c, &c->lm_s, (size_t)(c->V + 15) / 16 * 16))
               : (rc = dalloc(c, &c->lm_head, (size_t)(c->V + 15) / 16 * 16 * hsz))))
     return fin(rc);
+  if (c->R) {
+    c->mk_groups = markov_step_groups(c->V, c->n_cu);
+    if ((rc = dalloc(c, &c->mk_w2t, (size_t)(c->V + 15) / 16 * 16 * c->R)) ||
+        (rc = dalloc(c, &c->mk_logits, (size_t)c->max_batch * (c->gmax - 1) * c->V)) ||
+        (rc = dalloc(c, &c->mk_best, (size_t)MARKOV_MAX_ROWS * MAX_BANDS)))
+      return fin(rc);
+  }
   c->layers.resize(c->L);
   for (int l = 0; l < c->L; ++l) {
     LayerDev& d = c->layers[l];
@@ -577,6 +597,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   }
   if (e == hipSuccess) e = c->fp8 ? quant(w->lm_head, c->V, c->h, c->lm_q, c->lm_s) : tile(w->lm_head, c->V, c->h, c->lm_head);
   if (e == hipSuccess) e = tile(w->fc, c->h, c->T * c->Ht, c->fc_t);
+  if (e == hipSuccess && c->R) e = tile(w->markov_w2, c->V, c->R, c->mk_w2t);
+  if (e == hipSuccess && c->R) e = hipMemsetAsync(c->mk_best, 0, (size_t)MARKOV_MAX_ROWS * MAX_BANDS * 8, st);
   if (e == hipSuccess) e = tile(c->w_kv, c->L * 2 * c->kvd, c->h, c->w_kv_t);   // after the copies above, same stream
   std::vector<double> f = inv_freq_table(cfg, &c->mscale);
   if (e == hipSuccess) e = hipMemcpyAsync(c->inv_freq, f.data(), f.size() * sizeof(double), hipMemcpyHostToDevice, st);
@@ -970,6 +992,9 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   const int ng = lm_wide ? lmhead_wide_groups(c->V) : ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
   const bf16* lmw = c->fp8 ? (const bf16*)c->lm_q : c->lm_head;
   const float* lms = c->fp8 ? c->lm_s : nullptr;
+  // a Markov head needs every drafted row's logits: the caller's buffer, else the context's
+  float* const user_logits = logits;
+  if (c->R && !logits) logits = c->mk_logits;
   if (lm_wide) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
       return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, lmw, c->V, c->h, c->best_v, c->best_i, ng, gamma,
@@ -990,9 +1015,23 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       }));
     }
   }
-  HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] {
-    return launch_argmax_reduce(c->best_v, c->best_i, ng, n_seqs, gamma, draft_tokens, st);
-  }));
+  if (!c->R) {
+    HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] {
+      return launch_argmax_reduce(c->best_v, c->best_i, ng, n_seqs, gamma, draft_tokens, st);
+    }));
+    return DFLASH_OK;
+  }
+  // DSpark: the drafted rows one after another, each biased by the previous draft's row of
+  // the Markov head and reduced to its draft (the lm_head's own argmax is not used)
+  MarkovStep ms{};
+  ms.w1 = c->mk_w1; ms.w2t = c->mk_w2t; ms.logits = logits; ms.best = c->mk_best;
+  ms.V = c->V; ms.R = c->R; ms.n = n_seqs; ms.gamma = gamma; ms.store = user_logits != nullptr;
+  for (int b = 0; b < n_seqs; ++b) ms.bonus[b] = bonus[b];
+  for (int k = 0; k < gamma - 1; ++k) {
+    ms.k = k;
+    HIPCHK(c, timed(c, DFLASH_K_MARKOV, st, [&] { return launch_markov_step(ms, c->mk_groups, st); }));
+  }
+  HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] { return launch_markov_finish(c->mk_best, n_seqs, gamma, draft_tokens, st); }));
   return DFLASH_OK;
 }
 

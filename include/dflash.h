@@ -79,6 +79,8 @@ typedef struct {
                                       1..num_pages-1; NULL = ascending. Page 0 is a zeroed
                                       sentinel and is never handed out. */
   int32_t weight_format;           /* DFLASH_WEIGHTS_BF16 or DFLASH_WEIGHTS_FP8_E4M3 */
+  int32_t markov_rank;             /* DSpark Markov head: 0 = none, else its rank R, 256 or 512
+                                      (see dflash_weights and dflash_block_forward) */
 } dflash_config;
 
 /* Weight formats (metrale_model_arch/dflash_head/from_weights.rs, DflashQuantization and the
@@ -102,10 +104,16 @@ typedef struct {
 
 /* fc [hidden, num_taps*target_hidden]; hidden_norm, norm [hidden]; embed_tokens and
  * lm_head [vocab, hidden] are the target's, shared (they may alias). `layers` is a host
- * array [num_layers]. */
+ * array [num_layers]. With markov_rank R > 0, the DSpark Markov head (docs.rs
+ * memra-engine, dflash.rs: DflashDraft's `markov` head; spark_model/layers/dflash_head.rs:
+ * markov_w1, markov_w2): markov_w1 [vocab, R], the table indexed by the previous token, and
+ * markov_w2 [vocab, R], the rank-R latent to vocabulary projection, both device bf16,
+ * borrowed (markov_w1 is read in place; markov_w2 is copied at create); NULL otherwise.
+ * They stay bf16 under DFLASH_WEIGHTS_FP8_E4M3. */
 typedef struct {
   const void *fc, *hidden_norm, *norm, *embed_tokens, *lm_head;
   const dflash_layer_weights *layers;
+  const void *markov_w1, *markov_w2;
 } dflash_weights;
 
 /* Create a drafter: validates the configuration, allocates the KV pool, block tables and
@@ -162,6 +170,12 @@ int dflash_ctx_kv_append_batch(dflash_ctx *ctx, int32_t n_seqs, const int32_t *s
  *   draft_tokens: device int32 [n_seqs, gamma-1]: argmax of rows 1..gamma-1 (lowest
  *                 index on an exact tie);
  *   logits:       device fp32 [n_seqs*(gamma-1), vocab] or NULL.
+ * With a Markov head (markov_rank > 0; docs.rs memra-engine, dflash.rs,
+ * generate_spec_dflash, the semi-autoregressive chain, greedy) the drafted rows are taken
+ * left to right: row k (k = 0..gamma-2, block row k+1) gets the fp32 bias
+ * markov_w2 @ markov_w1[t_k] added to its logits, with t_0 = bonus_tokens[b] and t_k =
+ * draft_tokens[b][k-1], and draft_tokens[b][k] is the argmax of the biased row; `logits`
+ * then holds the biased rows.
  * Errors: EINVAL (n_seqs not in 1..max_batch, NULL pointers, bonus token out of range),
  * ERANGE (seq out of range or repeated, gamma not in [2, gamma_max]), EPOOL. */
 int dflash_block_forward(dflash_ctx *ctx, int32_t n_seqs, const int32_t *seqs,
@@ -228,7 +242,8 @@ enum {
   DFLASH_K_ARGMAX = 8,        /* argmax reduction */
   DFLASH_K_APPEND_GEMM = 9,   /* fc and fused K/V GEMMs of the context append */
   DFLASH_K_APPEND_MISC = 10,  /* append slots, hidden_norm, K/V epilogue + writeback */
-  DFLASH_K_NUM_CLASSES = 11
+  DFLASH_K_MARKOV = 11,       /* the Markov head's chain steps (one per drafted row) */
+  DFLASH_K_NUM_CLASSES = 12
 };
 int dflash_timing(dflash_ctx *ctx, uint32_t class_mask);
 int dflash_timing_read(dflash_ctx *ctx, double *ms, int64_t *launches, int32_t n_classes);

@@ -46,15 +46,25 @@ class Pair:
         self.gpu.dflash_ctx_kv_append_batch(seqs, counts, dev_bf16(H), positions=positions)
         self.ora.ctx_kv_append_batch(seqs, counts, H, positions=positions)
 
-    def forward(self, seqs, bonus, q_rope_pos=None, gamma=None):
+    def forward(self, seqs, bonus, q_rope_pos=None, gamma=None, with_logits=True):
+        """One forward on both sides. With a Markov head the oracle's chain is teacher-forced
+        onto the GPU's drafts (row k's bias uses the GPU's draft of row k-1), so a branch the
+        GPU took at a near-tie is compared on its own terms; the criteria then check each
+        row's draft against the oracle's argmax of the same biased row.
+        with_logits=False passes no logits buffer (the drafts alone; logits are None)."""
         gamma = self.m["gamma_max"] if gamma is None else gamma
         n = len(seqs)
         toks = torch.full((n, gamma - 1), -1, dtype=torch.int32, device=DEV)
-        logits = torch.empty((n * (gamma - 1), self.m["vocab"]), dtype=torch.float32, device=DEV)
+        logits = torch.empty((n * (gamma - 1), self.m["vocab"]), dtype=torch.float32, device=DEV) if with_logits else None
         self.gpu.dflash_block_forward(seqs, bonus, toks, logits, q_rope_pos=q_rope_pos, gamma=gamma)
         torch.cuda.synchronize()
-        ref = self.ora.block_forward(seqs, bonus, q_rope_pos=q_rope_pos, gamma=gamma)
-        return (toks.cpu().numpy(), logits.cpu().numpy().astype(np.float64).reshape(n, gamma - 1, -1), ref)
+        t = toks.cpu().numpy()
+        prev = None
+        if self.m.get("markov_rank", 0):
+            prev = np.concatenate([np.asarray(bonus, dtype=np.int64).reshape(n, 1), t[:, :-1]], axis=1)
+        ref = self.ora.block_forward(seqs, bonus, q_rope_pos=q_rope_pos, gamma=gamma, markov_prev=prev)
+        lg = logits.cpu().numpy().astype(np.float64).reshape(n, gamma - 1, -1) if with_logits else None
+        return (t, lg, ref)
 
     def close(self):
         self.gpu.close()

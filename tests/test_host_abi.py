@@ -122,5 +122,50 @@ def test_config_struct_layout_matches_header():
     assert B.dflash_config.layer_sliding.offset == 104
     assert B.dflash_config.page_order.offset == 128
     assert B.dflash_config.weight_format.offset == 136
+    assert B.dflash_config.markov_rank.offset == 140
     assert C.sizeof(B.dflash_config) == 144
-    assert C.sizeof(B.dflash_layer_weights) == 88 and C.sizeof(B.dflash_weights) == 48
+    assert C.sizeof(B.dflash_layer_weights) == 88 and C.sizeof(B.dflash_weights) == 64
+
+
+def test_struct_layouts_match_the_c_compiler(tmp_path):
+    """Every field offset and struct size of the ctypes mirrors equals what a C compiler
+    makes of include/dflash.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"dflash_config": B.dflash_config, "dflash_layer_weights": B.dflash_layer_weights,
+               "dflash_weights": B.dflash_weights}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dflash.h"', "int main(void) {"]
+    for name, st in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for f, _ in st._fields_:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for name, st in structs.items():
+        assert got[(name, "size")] == C.sizeof(st), name
+        for f, _ in st._fields_:
+            assert got[(name, f)] == getattr(st, f).offset, (name, f)
+
+
+def test_create_rejects_bad_markov_heads():
+    m = synth.model("tiny-L2-h256-dspark")
+    w, lay = _null_weights(m)
+    ctx = C.c_void_p()
+    for rank in (128, 300, 1024, -1):
+        cfg, keep = B.make_config(dict(m, markov_rank=rank), 128, 1)
+        w.markov_w1 = w.markov_w2 = 0x1000
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    cfg, keep = B.make_config(m, 128, 1)
+    for w1, w2 in ((None, 0x1000), (0x1000, None), (0x1008, 0x1000), (0x1000, 0x1004)):
+        w.markov_w1, w.markov_w2 = w1, w2
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    assert not ctx.value
