@@ -23,6 +23,11 @@ namespace {
 
 constexpr int MK_T16_BLOCK = 16 * 256;   // one 256-deep block of a T16 tile (elements)
 constexpr int MK_PAD = 8;                // LDS row padding: rows 16 B off the bank period
+constexpr int MK_DEPTH = 2;              // W2 tiles in flight per wavefront (2 or 3)
+
+// wavefronts a workgroup: 8, except for two band tiles of a rank-512 head, whose registers
+// fit 256 per lane only with 4
+constexpr int mk_waves(int mt, int rb) { return mt == 2 && rb == 2 ? 4 : 8; }
 
 __device__ __forceinline__ void mk_better(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
@@ -51,12 +56,13 @@ __device__ __forceinline__ void mk_reduce16(float& bv, int& bi) {
 
 // MT: 16-band row tiles (bands <= 16 * MT); RB: 256-deep blocks of the rank
 template <int MT, int RB>
-__global__ __launch_bounds__(256) void k_markov_step(const MarkovStep a) {
+__global__ __launch_bounds__(mk_waves(MT, RB) * 64) void k_markov_step(const MarkovStep a) {
+  constexpr int MK_WAVES = mk_waves(MT, RB);
   constexpr int R = RB * 256;
   constexpr int NP = RB * 8;   // 16-byte W2 pieces a lane loads per tile
   __shared__ __attribute__((aligned(16))) bf16 se[MT * 16][R + MK_PAD];
-  __shared__ float rv[4][MT * 16];
-  __shared__ int ri[4][MT * 16];
+  __shared__ float rv[MK_WAVES][MT * 16];
+  __shared__ int ri[MK_WAVES][MT * 16];
   const bf16* __restrict__ w2t = a.w2t;
   float* __restrict__ logits = a.logits;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(256) void k_markov_step(const MarkovStep a) {
   const int g1 = a.gamma - 1, V = a.V, n = a.n;
 
   // W1 rows of the bands' previous tokens; rows past the last band are zero
-  for (int p = threadIdx.x; p < MT * 16 * (R / 8); p += 256) {
+  for (int p = threadIdx.x; p < MT * 16 * (R / 8); p += MK_WAVES * 64) {
     const int b = p / (R / 8), cc = (p % (R / 8)) * 8;
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
     if (b < n) {
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(256) void k_markov_step(const MarkovStep a) {
   // flight while the current one is computed. Lane (c, g) holds bands 16 mt + 4 g + e of
   // vocabulary column t * 16 + c.
   const int n_tiles = (V + 15) / 16;
-  const int stride = gridDim.x * 4;
+  const int stride = gridDim.x * MK_WAVES;
   auto load = [&](u32x4 (&w)[NP], float (&l)[MT][4], int t) {
     const bf16* wp = w2t + (size_t)t * 16 * R + lane * 8;
 #pragma unroll
@@ -128,18 +134,26 @@ __global__ __launch_bounds__(256) void k_markov_step(const MarkovStep a) {
         }
     }
   };
-  u32x4 w0[NP], w1[NP];
-  float l0[MT][4], l1[MT][4];
-  int t = blockIdx.x * 4 + wave;
+  // a ring of MK_DEPTH tiles in flight per wave
+  u32x4 w0[NP], w1[NP], w2[NP];
+  float l0[MT][4], l1[MT][4], l2[MT][4];
+  int t = blockIdx.x * MK_WAVES + wave;
   if (t < n_tiles) load(w0, l0, t);
-  __syncthreads();   // the staged W1 rows (the first tile's loads are already in flight)
-  for (; t < n_tiles; t += 2 * stride) {
-    const int t1 = t + stride;
-    if (t1 < n_tiles) load(w1, l1, t1);
+  if (MK_DEPTH == 3 && t + stride < n_tiles) load(w1, l1, t + stride);
+  __syncthreads();   // the staged W1 rows (the first tiles' loads are already in flight)
+  const int ahead = (MK_DEPTH - 1) * stride;
+  while (t < n_tiles) {
+    if (t + ahead < n_tiles) load(MK_DEPTH == 3 ? w2 : w1, MK_DEPTH == 3 ? l2 : l1, t + ahead);
     consume(w0, l0, t);
-    if (t1 >= n_tiles) break;
-    if (t1 + stride < n_tiles) load(w0, l0, t1 + stride);
-    consume(w1, l1, t1);
+    if ((t += stride) >= n_tiles) break;
+    if (t + ahead < n_tiles) load(w0, l0, t + ahead);
+    consume(w1, l1, t);
+    if ((t += stride) >= n_tiles) break;
+    if (MK_DEPTH == 3) {
+      if (t + ahead < n_tiles) load(w1, l1, t + ahead);
+      consume(w2, l2, t);
+      t += stride;
+    }
   }
 
   // the workgroup's argmax per band, folded into the band's key
@@ -156,7 +170,7 @@ __global__ __launch_bounds__(256) void k_markov_step(const MarkovStep a) {
     float v = rv[0][b];
     int i = ri[0][b];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) mk_better(v, i, rv[w][b], ri[w][b]);
+    for (int w = 1; w < MK_WAVES; ++w) mk_better(v, i, rv[w][b], ri[w][b]);
     __hip_atomic_fetch_max(a.best + a.k * MAX_BANDS + b, mk_key(v, i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -176,17 +190,19 @@ __global__ __launch_bounds__(256) void k_markov_finish(unsigned long long* __res
 
 int markov_step_groups(int V, int n_cu) {
   const int n_tiles = (V + 15) / 16;
-  return std::max(1, std::min((n_tiles + 3) / 4, 2 * n_cu));
+  return std::max(1, std::min((n_tiles + 7) / 8, n_cu));
 }
 
 hipError_t launch_markov_step(const MarkovStep& a, int groups, hipStream_t st) {
   if (a.n < 1 || a.n > MAX_BANDS || a.k < 0 || a.k >= a.gamma - 1 || a.gamma - 1 > MARKOV_MAX_ROWS || groups < 1 ||
       groups > MARKOV_MAX_GROUPS || (a.R != 256 && a.R != 512))
     return hipErrorInvalidValue;
-  const dim3 grid(groups), block(256);
+  const dim3 grid(groups);
   if (a.n <= 16)
-    return a.R == 256 ? launch(k_markov_step<1, 1>, grid, block, 0, st, a) : launch(k_markov_step<1, 2>, grid, block, 0, st, a);
-  return a.R == 256 ? launch(k_markov_step<2, 1>, grid, block, 0, st, a) : launch(k_markov_step<2, 2>, grid, block, 0, st, a);
+    return a.R == 256 ? launch(k_markov_step<1, 1>, grid, dim3(mk_waves(1, 1) * 64), 0, st, a)
+                      : launch(k_markov_step<1, 2>, grid, dim3(mk_waves(1, 2) * 64), 0, st, a);
+  return a.R == 256 ? launch(k_markov_step<2, 1>, grid, dim3(mk_waves(2, 1) * 64), 0, st, a)
+                    : launch(k_markov_step<2, 2>, grid, dim3(mk_waves(2, 2) * 64), 0, st, a);
 }
 
 hipError_t launch_markov_finish(unsigned long long* best, int n, int gamma, int* tokens, hipStream_t st) {
