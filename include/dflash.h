@@ -83,9 +83,10 @@ typedef struct {
                                       (see dflash_weights and dflash_block_forward) */
 } dflash_config;
 
-/* Weight formats (metrale_model_arch/dflash_head/from_weights.rs, DflashQuantization and the
- * FP8 weights phase of from_weights): with DFLASH_WEIGHTS_FP8_E4M3 the seven per-layer GEMM
- * weights (q, k, v, o, gate, up, down) and the lm_head are quantized once at create to OCP
+/* Weight formats (metrale_model_arch/dflash_head/from_weights.rs, the FP8 weights phase of
+ * from_weights; spark_model/layers/dflash_head.rs, DflashQuantization::Fp8Weights): with
+ * DFLASH_WEIGHTS_FP8_E4M3 the seven per-layer GEMM weights (q, k, v, o, gate, up, down) and
+ * the lm_head are quantized once at create to OCP
  * FP8 E4M3 codes with one fp32 scale per row: scale = max|row| / 448 (1 for an all-zero row),
  * code = the nearest E4M3 value of w / scale (fp32 division), ties to even, saturating at
  * +-448; the GEMMs use code value x scale. Activations, the KV cache, the context-append

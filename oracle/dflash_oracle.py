@@ -16,7 +16,12 @@ Sources (page title -- section). Every function below names the one it follows.
             sequence) and DraftProposer::propose_batch (drop row 0 of each band).
   [metrale-fw] metrale_model_arch/dflash_head/from_weights.rs -- DraftProposer::propose_batch
             (one batched context precompute), PRECOMPUTE_BATCH_ROWS,
-            DflashProposerState::ctx_committed (the per-sequence watermark).
+            DflashProposerState::ctx_committed (the per-sequence watermark), the FP8
+            weights phase of from_weights.
+  [atlas-head] also: DflashQuantization (weight-only FP8 with per-row f32 scales) and the
+            DSpark head fields markov_rank / markov_w1 / markov_w2.
+  [memra] also: DflashDraft's `markov` head and the semi-autoregressive chain of
+            generate_spec_dflash (DSpark, greedy).
 
 Arithmetic: numpy float64 by default (float32 on request, for timing only). Inputs
 arrive as bf16 bit patterns (uint16) and are widened exactly; no intermediate value is
@@ -80,7 +85,8 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------
-# FP8 weights ([metrale-fw] from_weights, the FP8 weights phase; DflashQuantization)
+# FP8 weights ([metrale-fw] from_weights, the FP8 weights phase; [atlas-head]
+# DflashQuantization::Fp8Weights). READING c19: the scale and rounding rules below.
 # ----------------------------------------------------------------------------------
 # OCP FP8 E4M3 ("E4M3FN"): sign, 4 exponent bits with bias 7, 3 mantissa bits; no
 # infinities; codes 0x7F and 0xFF are NaN; the largest finite value is 448 (0x7E);
