@@ -59,8 +59,8 @@ def gemm_bytes(m, M, fp8=False):
 # the bytes written). Valid only for the kernel source they were taken on.
 TRAFFIC = {
     "gemm": dict(source="block_diffusion_draft_02_amd/csrc/k_gemm.hip",
-                 sha256="ff5495122e30d73b29933799b1b9d9de07376a46c237b57ae41d509e45f38497",
-                 fetch_bytes=30.18e6, write_bytes=3.540e6),
+                 sha256="16eae5ec64c0f100aaa2b5beff9578a6493c5424bb1e1e045448a6d6b93c5224",
+                 fetch_bytes=30.19e6, write_bytes=3.540e6),
 }
 
 
