@@ -28,8 +28,10 @@ arrive as bf16 bit patterns (uint16) and are widened exactly; no intermediate va
 rounded. Where the pages leave a step open, the reading taken is marked READING.
 
 Parity unpinned (no worked example on the pages fixes them): the sliding-window rule
-inside a non-causal block (READING c1 below) and the placement of the YaRN mscale when
-a trained checkpoint is used (READING c2). Both are pinned only by invariants.
+inside a non-causal block (READING c1 below), the placement of the YaRN mscale when
+a trained checkpoint is used (READING c2), and DFlash2's composition of its dynamic
+convolutions and selector walk (READINGS c21, c23; the pages give shapes and kernel
+names only). They are pinned only by invariants and by their own definitions.
 """
 from __future__ import annotations
 
@@ -468,11 +470,14 @@ class Drafter:
         bpos = q_rope_pos + np.arange(gamma, dtype=np.int64)
         y = self.block_hidden(ctx_k, ctx_v, ctx_pos, toks, bpos)
         logits = self.lm_head(y[1:])
+        extra = {}
         if self.m.get("markov_rank", 0):
             logits, drafts = self.markov_chain(logits, bonus, markov_prev)
+        elif self.dflash2():
+            drafts, extra = self.selector_walk(y[1:], logits, bonus, markov_prev)
         else:
             drafts = argmax_lowest(logits)
-        res = dict(logits=logits, tokens=drafts)
+        res = dict(logits=logits, tokens=drafts, **extra)
         if want_hidden:
             res["hidden"] = y
         return res
@@ -500,6 +505,74 @@ class Drafter:
             t = int(drafts[k])
         return out, drafts
 
+    # ---- DFlash2 ([atlas-head] BlockDiffusionDraftHead's DFlash2 fields and scratch:
+    # attention_conv / mlp_conv base kernels [2 applications, kernel, hidden] and kernel
+    # projections [2*kernel*groups, hidden]; conv_dyn, conv_tmp; the candidate selector's
+    # predecessor / successor codebooks [V, rank] and hidden projection [rank, hidden];
+    # sel_vals / sel_idx top-16 and sel_hproj; the dflash2_conv2, dflash2_topk16 and
+    # dflash2_selector_walk kernels). The pages give shapes and kernel names only: the
+    # composition below is READING c21-c23 and its parity is unpinned.
+
+    def dflash2(self) -> bool:
+        return bool(self.m.get("selector_rank", 0))
+
+    def dconv_prepare(self, l: int, site: str, hn: np.ndarray):
+        """The prepare application of a grouped dynamic causal conv site (READING c21).
+        hn [T, h]: the site's normed input (the block rows of one band, in order). Per row t
+        the dynamic taps D_t = hn_t @ proj^T, viewed as [application 2][tap k][group G]
+        (G = h / group_size), and the kernel of channel c is base[a][j][c] + D_t[a][j][c //
+        group_size]. The prepare output is u_t = sum_j kern_t[0][j] * hn_{t-j} (rows before
+        the band's first contribute zero). Returns (u, kern [T, 2, k, h])."""
+        m = self.m
+        T, h = hn.shape
+        k, gs = m["conv_kernel_size"], m["conv_group_size"]
+        base = self.lw(l, site + "_conv_base").reshape(2, k, h)
+        D = (hn @ self.lw(l, site + "_conv_proj").T).reshape(T, 2, k, h // gs)
+        kern = base[None] + np.repeat(D, gs, axis=3)
+        u = np.zeros_like(hn)
+        for j in range(min(k, T)):
+            u[j:] += kern[j:, 0, j] * hn[:T - j]
+        return u, kern
+
+    @staticmethod
+    def dconv_finish(sub: np.ndarray, kern: np.ndarray) -> np.ndarray:
+        """The finish application (READING c21): v_t = sum_j kern_t[1][j] * sub_{t-j}, on the
+        sublayer's output before the residual add, with the taps computed at prepare."""
+        T = sub.shape[0]
+        v = np.zeros_like(sub)
+        for j in range(min(kern.shape[2], T)):
+            v[j:] += kern[j:, 1, j] * sub[:T - j]
+        return v
+
+    @staticmethod
+    def top_k_candidates(logits: np.ndarray, k: int):
+        """READING c22: each row's k largest logits in descending order, a tie to the lower
+        index (what taking the argmax k times, removing it each time, yields)."""
+        idx = np.argsort(-logits, axis=-1, kind="stable")[..., :k]
+        return idx.astype(np.int32), np.take_along_axis(logits, idx, axis=-1)
+
+    def selector_walk(self, y: np.ndarray, logits: np.ndarray, bonus: int, prev=None):
+        """The candidate selector's chain walk, greedy (READING c23). y [g, h]: the drafted
+        rows' final-normed hidden states (the lm_head's input); logits [g, V]. Per row the
+        top-k candidates with their logits; H_t = hidden_projection @ y_t [rank]; a
+        candidate c scores logit_t(c) + sum_r pred[t_prev][r] * H_t[r] * succ[c][r], with
+        t_prev the bonus token for the first row and the previous row's pick after; the
+        row's draft is the best-scoring candidate (the earlier candidate on a tie).
+        prev: optional [g] previous tokens (teacher forcing). Returns (drafts, extras)."""
+        k = self.m["selector_top_k"]
+        cand, vals = self.top_k_candidates(logits, k)
+        H = y @ self.w("selector_hidden_proj").T
+        drafts = np.empty(logits.shape[0], dtype=np.int32)
+        scores = np.empty((logits.shape[0], k), dtype=self.dtype)
+        t = int(bonus)
+        for r in range(logits.shape[0]):
+            tp = t if prev is None else int(prev[r])
+            gate = widen(self.bits["selector_pred"][tp], self.dtype) * H[r]
+            scores[r] = vals[r] + widen(self.bits["selector_succ"][cand[r]], self.dtype) @ gate
+            drafts[r] = cand[r][int(np.argmax(scores[r]))]
+            t = int(drafts[r])
+        return drafts, dict(cand=cand, cand_logits=vals, sel_h=H, scores=scores)
+
     def block_hidden(self, ctx_k, ctx_v, ctx_pos, toks, bpos):
         """Final-normed hidden rows [T, h] of a block with explicit token ids `toks` [T]
         at explicit positions `bpos` [T]; the gamma-block forward calls it with
@@ -516,8 +589,11 @@ class Drafter:
         bpos = np.asarray(bpos, dtype=np.int64)
         x = widen(self.bits["embed_tokens"][np.asarray(toks)], self.dtype)       # [T, h]
         scale = 1.0 / math.sqrt(hd)
+        d2 = self.dflash2()
         for l in range(m["num_layers"]):
             xn = rms_norm(x, self.lw(l, "input_layernorm"), eps)
+            if d2:
+                xn, kern_a = self.dconv_prepare(l, "attention", xn)
             q = (xn @ self.flw(l, "q_proj").T).reshape(gamma, nh, hd)
             kb = (xn @ self.flw(l, "k_proj").T).reshape(gamma, nkv, hd)
             vb = (xn @ self.flw(l, "v_proj").T).reshape(gamma, nkv, hd)
@@ -528,11 +604,15 @@ class Drafter:
             k_pos = np.concatenate([np.asarray(ctx_pos, dtype=np.int64), bpos])
             win = int(m.get("sliding_window", 0) or 0) if self.sliding(l) else 0
             attn = gqa_attention(q, bpos, k_all, v_all, k_pos, scale, win).reshape(gamma, nh * hd)
-            x1 = x + attn @ self.flw(l, "o_proj").T
+            o = attn @ self.flw(l, "o_proj").T
+            x1 = x + (self.dconv_finish(o, kern_a) if d2 else o)
             x1n = rms_norm(x1, self.lw(l, "post_attention_layernorm"), eps)
+            if d2:
+                x1n, kern_m = self.dconv_prepare(l, "mlp", x1n)
             g = x1n @ self.flw(l, "gate_proj").T
             u = x1n @ self.flw(l, "up_proj").T
-            x = x1 + (silu(g) * u) @ self.flw(l, "down_proj").T
+            mo = (silu(g) * u) @ self.flw(l, "down_proj").T
+            x = x1 + (self.dconv_finish(mo, kern_m) if d2 else mo)
         return rms_norm(x, self.w("norm"), eps)
 
     def lm_head(self, y: np.ndarray, chunk: int = 16384) -> np.ndarray:
@@ -665,9 +745,9 @@ class Engine:
         self.last_slots = np.concatenate(slots)
 
     def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False, markov_prev=None):
-        """The C ABI's block forward over bands `seqs`. markov_prev (DSpark heads only):
-        optional [n, gamma-1] previous tokens per band for the Markov chain (teacher
-        forcing; see Drafter.markov_chain)."""
+        """The C ABI's block forward over bands `seqs`. markov_prev (DSpark and DFlash2
+        heads): optional [n, gamma-1] previous tokens per band for the Markov chain or the
+        selector walk (teacher forcing; see Drafter.markov_chain, Drafter.selector_walk)."""
         m = self.m
         gamma = m["gamma_max"] if gamma is None else gamma
         seqs = [int(x) for x in seqs]
@@ -699,6 +779,9 @@ class Engine:
                                              markov_prev=None if markov_prev is None else markov_prev[i]))
         res = dict(tokens=np.stack([o["tokens"] for o in outs]),
                    logits=np.stack([o["logits"] for o in outs]))
+        for key in ("cand", "cand_logits", "sel_h", "scores"):
+            if key in outs[0]:
+                res[key] = np.stack([o[key] for o in outs])
         if want_hidden:
             res["hidden"] = np.stack([o["hidden"] for o in outs])
         return res

@@ -9,7 +9,8 @@ Recipe:
   * generator: numpy PCG64 seeded with SeedSequence([seed, stream, index]);
     float32 draws rounded to bf16 with round-to-nearest-even;
   * weight matrices ~ N(0, 0.02); norm weights ~ 1 + N(0, 0.02); a DSpark Markov head's
-    token table ~ N(0, 1) and its projection ~ N(0, 0.03);
+    token table ~ N(0, 1) and its projection ~ N(0, 0.03); DFlash2 conv base kernels
+    ~ 0.5 + N(0, 0.02), kernel projections ~ N(0, 0.002), selector codebooks ~ N(0, 0.1);
   * tapped target hidden states ~ N(0, 1);
   * bonus tokens uniform over the vocabulary; context lengths uniform over the
     workload's range; the pool's page order is a seeded permutation.
@@ -59,6 +60,11 @@ MODELS = {
     # their other weights are the same draws as the plain models' under the same seed
     "tiny-L2-h256-dspark": dict(_TINY, markov_rank=256),
     "qwen3-L8-h2048-dspark": dict(_QWEN3_8L_2048, markov_rank=256),
+    # DFlash2: two-tap grouped dynamic convs with 16-channel groups and a rank-256, top-16
+    # candidate selector (the sizes the pages name)
+    "tiny-L2-h256-dflash2": dict(_TINY, conv_kernel_size=2, conv_group_size=16, selector_rank=256, selector_top_k=16),
+    "qwen3-L8-h2048-dflash2": dict(_QWEN3_8L_2048, conv_kernel_size=2, conv_group_size=16, selector_rank=256,
+                                   selector_top_k=16),
 }
 
 # A workload = a model, how many sequences one forward call carries, how their
@@ -185,11 +191,24 @@ def weight_specs(m: dict):
         # projection, both [vocab, rank]
         specs += [("markov_w1", (m["vocab"], m["markov_rank"]), "embed"),
                   ("markov_w2", (m["vocab"], m["markov_rank"]), "proj")]
+    if m.get("selector_rank", 0):
+        # DFlash2: per layer two grouped dynamic convs (base kernel [2, kernel, hidden],
+        # kernel projection [2 * kernel * hidden / group, hidden]); the candidate selector's
+        # codebooks [vocab, rank] and hidden projection [rank, hidden]
+        k, ng, r = m["conv_kernel_size"], 2 * m["conv_kernel_size"] * h // m["conv_group_size"], m["selector_rank"]
+        for l in range(m["num_layers"]):
+            for site in ("attention", "mlp"):
+                specs += [(f"layers.{l}.{site}_conv_base", (2, k, h), "convbase"),
+                          (f"layers.{l}.{site}_conv_proj", (ng, h), "dynproj")]
+        specs += [("selector_pred", (m["vocab"], r), "codebook"),
+                  ("selector_succ", (m["vocab"], r), "codebook"),
+                  ("selector_hidden_proj", (r, h), "mat")]
     return specs
 
 
 # (mean, standard deviation) of each kind of tensor
-_KIND_DIST = {"mat": (0.0, 0.02), "norm": (1.0, 0.02), "embed": (0.0, 1.0), "proj": (0.0, 0.03)}
+_KIND_DIST = {"mat": (0.0, 0.02), "norm": (1.0, 0.02), "embed": (0.0, 1.0), "proj": (0.0, 0.03),
+              "convbase": (0.5, 0.02), "dynproj": (0.0, 0.002), "codebook": (0.0, 0.1)}
 
 
 def _weight_args(m: dict, name: str):
@@ -201,8 +220,11 @@ def _weight_args(m: dict, name: str):
 
 def gen_weight(m: dict, seed: int, name: str) -> np.ndarray:
     """Weight `name`: matrices N(0, 0.02), norm weights 1 + N(0, 0.02), the Markov head's
-    token table N(0, 1) and its projection N(0, 0.03) (a bias of about the logits' spread);
-    tensor i of the fixed order draws from stream S_WEIGHTS, index i."""
+    token table N(0, 1) and its projection N(0, 0.03) (a bias of about the logits' spread),
+    DFlash2's conv base kernels 0.5 + N(0, 0.02) (a two-tap smoothing), kernel projections
+    N(0, 0.002) (dynamic taps a fifth of the base at hidden 2048) and selector codebooks
+    N(0, 0.1) (pair scores of about the top-16 logits' spacing); tensor i of the fixed
+    order draws from stream S_WEIGHTS, index i."""
     i, shape, mean, std = _weight_args(m, name)
     return _normal_bf16(seed, S_WEIGHTS, i, shape, mean, std)
 

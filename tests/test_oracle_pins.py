@@ -807,3 +807,128 @@ def test_markov_zero_head_is_plain_dflash_and_teacher_forcing_is_consistent(dspa
     f2 = e.block_forward([0, 1], [5, 6], gamma=9, markov_prev=other)
     assert np.array_equal(f2["logits"][:, 0], free["logits"][:, 0])
     assert not np.allclose(f2["logits"][:, 1:], free["logits"][:, 1:])
+
+
+# ---- DFlash2 ([atlas-head] the DFlash2 fields, scratch and kernel names; READINGS c21-c23) ----
+
+@pytest.fixture(scope="module")
+def dflash2():
+    m = synth.model("tiny-L2-h256-dflash2")
+    return m, synth.gen_weights(m, 1401)
+
+
+def _plain_weights(W):
+    return {k: v for k, v in W.items() if "_conv_" not in k and not k.startswith("selector")}
+
+
+def test_top_k_is_destructive_argmax(dflash2):
+    """The k candidates equal taking the argmax k times, removing it each time (ties to the
+    lower index), on rows with planted exact ties."""
+    rng = np.random.default_rng(7)
+    x = np.round(rng.standard_normal((12, 300)) * 4) / 4          # many exact ties
+    x[3, [5, 9, 200]] = 10.0
+    idx, val = O.Drafter.top_k_candidates(x, 16)
+    for r in range(x.shape[0]):
+        row = x[r].copy()
+        want = []
+        for _ in range(16):
+            j = int(np.argmax(row))
+            want.append(j)
+            row[j] = -np.inf
+        assert idx[r].tolist() == want and np.array_equal(val[r], x[r, want])
+    assert idx[3, :3].tolist() == [5, 9, 200]
+
+
+def test_dconv_site_by_scalar_loops(dflash2):
+    """The prepare and finish applications written as scalar loops over rows, taps and
+    channels, with the dynamic tap of channel c taken from group c // group_size."""
+    m, W = dflash2
+    d = O.Drafter(m, W)
+    rng = np.random.default_rng(8)
+    T, h, k, gs = 5, m["hidden"], m["conv_kernel_size"], m["conv_group_size"]
+    hn = rng.standard_normal((T, h))
+    u, kern = d.dconv_prepare(1, "mlp", hn)
+    base = O.widen(W["layers.1.mlp_conv_base"])
+    proj = O.widen(W["layers.1.mlp_conv_proj"])
+    sub = rng.standard_normal((T, h))
+    v = d.dconv_finish(sub, kern)
+    for t in range(T):
+        for c in range(0, h, 37):
+            g = c // gs
+            ku = [base[0, j, c] + float(proj[(0 * k + j) * (h // gs) + g] @ hn[t]) for j in range(k)]
+            kf = [base[1, j, c] + float(proj[(1 * k + j) * (h // gs) + g] @ hn[t]) for j in range(k)]
+            want_u = sum(ku[j] * hn[t - j, c] for j in range(k) if t - j >= 0)
+            want_v = sum(kf[j] * sub[t - j, c] for j in range(k) if t - j >= 0)
+            assert abs(u[t, c] - want_u) < 1e-12 and abs(v[t, c] - want_v) < 1e-12
+    # causal: row t depends on rows t and t-1 only
+    hn2 = hn.copy()
+    hn2[3] += 1.0
+    u2, _ = d.dconv_prepare(1, "mlp", hn2)
+    assert np.array_equal(u2[:3], u[:3]) and not np.allclose(u2[3:5], u[3:5])
+
+
+def test_dflash2_with_identity_convs_and_zero_codebooks_is_plain_dflash(dflash2):
+    """Base kernels [1, 0] for both applications, zero kernel projections and zero
+    codebooks: the convs are the identity and the walk picks each row's top candidate, so
+    the DFlash2 forward is the plain forward bit for bit (tokens and logits)."""
+    m, W = dflash2
+    Wx = dict(W)
+    h, L = m["hidden"], m["num_layers"]
+    ident = np.zeros((2, 2, h), np.float32)
+    ident[:, 0, :] = 1.0
+    for l in range(L):
+        for site in ("attention", "mlp"):
+            Wx[f"layers.{l}.{site}_conv_base"] = synth.f32_to_bf16_bits(ident)
+            Wx[f"layers.{l}.{site}_conv_proj"] = np.zeros_like(W[f"layers.{l}.{site}_conv_proj"])
+    for name in ("selector_pred", "selector_succ"):
+        Wx[name] = np.zeros_like(W[name])
+    plain = {k: v for k, v in m.items() if k not in ("conv_kernel_size", "conv_group_size", "selector_rank",
+                                                     "selector_top_k")}
+    outs = []
+    for mm, ww in ((m, Wx), (plain, _plain_weights(W))):
+        e = O.Engine(mm, ww, 64, 2)
+        e.ctx_kv_append(0, synth.gen_hidden(m, 1401, 21, 0))
+        e.ctx_kv_append(1, synth.gen_hidden(m, 1401, 40, 1))
+        outs.append(e.block_forward([1, 0], [33, 600], gamma=16))
+    assert np.array_equal(outs[0]["tokens"], outs[1]["tokens"])
+    assert np.array_equal(outs[0]["logits"], outs[1]["logits"])
+    # and the real DFlash2 weights do change the forward
+    e = O.Engine(m, W, 64, 2)
+    e.ctx_kv_append(0, synth.gen_hidden(m, 1401, 21, 0))
+    e.ctx_kv_append(1, synth.gen_hidden(m, 1401, 40, 1))
+    r = e.block_forward([1, 0], [33, 600], gamma=16)
+    assert np.abs(r["logits"] - outs[1]["logits"]).max() > 1e-2
+
+
+def test_selector_walk_planted_chain(dflash2):
+    """H = ones (rows y = e_0, hidden_projection column 0 = 1), pred[t] = 10 e_(t mod R),
+    succ[c] = e_((c - 1) mod R): a candidate scores +10 iff it is the previous pick + 1.
+    Row r's candidates hold bonus + r + 1 at the lowest logit of the 16: the walk must
+    still draft bonus+1, bonus+2, ... (unary scores alone would pick other tokens)."""
+    m, W = dflash2
+    V, R, h = m["vocab"], m["selector_rank"], m["hidden"]
+    pred = np.zeros((V, R), np.float32)
+    pred[np.arange(V), np.arange(V) % R] = 10.0
+    succ = np.zeros((V, R), np.float32)
+    succ[np.arange(V), (np.arange(V) - 1) % R] = 1.0
+    hp = np.zeros((R, h), np.float32)
+    hp[:, 0] = 1.0
+    Wx = dict(W, selector_pred=synth.f32_to_bf16_bits(pred), selector_succ=synth.f32_to_bf16_bits(succ),
+              selector_hidden_proj=synth.f32_to_bf16_bits(hp))
+    d = O.Drafter(m, Wx)
+    g, bonus = 6, 50
+    y = np.zeros((g, h))
+    y[:, 0] = 1.0
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((g, V))
+    for r in range(g):
+        others = rng.choice(np.setdiff1d(np.arange(300, V), [bonus + r + 1]), 15, replace=False)
+        logits[r, others] = 10.0 + rng.random(15)
+        logits[r, bonus + r + 1] = 9.5
+    drafts, ex = d.selector_walk(y, logits, bonus)
+    assert drafts.tolist() == list(range(bonus + 1, bonus + 1 + g))
+    assert np.allclose(ex["sel_h"], 1.0)
+    assert all(bonus + r + 1 in ex["cand"][r] for r in range(g))
+    # teacher forcing on other previous tokens breaks the chain
+    d2, _ = d.selector_walk(y, logits, bonus, prev=[0] * g)
+    assert not any(d2[r] == bonus + r + 1 for r in range(g))
