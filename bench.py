@@ -177,6 +177,7 @@ def main():
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 E4M3 weight-only lines")
     ap.add_argument("--no-dspark", action="store_true", help="skip the DSpark Markov-head lines")
+    ap.add_argument("--no-dflash2", action="store_true", help="skip the DFlash2 lines")
     ap.add_argument("--longctx-only", action="store_true",
                     help="only run the 32-sequence long-context section and print its JSON (for counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -336,6 +337,17 @@ def main():
         if not args.no_batch16:
             out["dspark"]["batch16"] = bench_batch16(md, Wdd, gamma, a, args, B, torch, np, synth, to_dev)
         del Wdd
+    if not args.no_dflash2:
+        # the same trunk with DFlash2's convs and candidate selector (their tensors drawn from
+        # the same seed)
+        m2 = synth.model("qwen3-L8-h2048-dflash2")
+        extra = [n for n, _, _ in synth.weight_specs(m2) if "_conv_" in n or n.startswith("selector")]
+        Wd2 = dict(Wd, **{k: to_dev(synth.gen_weight(m2, w["seed"], k)) for k in extra})
+        out["dflash2"] = dict(batch1=bench_variant_b1(m2, "dflash2", Wd2, H_ctx, H_steps, bonus, a, gamma, args, B,
+                                                      torch, to_dev))
+        if not args.no_batch16:
+            out["dflash2"]["batch16"] = bench_batch16(m2, Wd2, gamma, a, args, B, torch, np, synth, to_dev)
+        del Wd2
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
@@ -345,7 +357,8 @@ def main():
 
 def bench_variant_b1(mv, label, Wd, H_ctx, H_steps, bonus, a, gamma, args, B, torch, to_dev):
     """The batch-1 step of a variant of the drafter (`mv`: the model with FP8 E4M3 trunk
-    weights, or with a DSpark Markov head): the same inputs, plain launches timed, then one
+    weights, a DSpark Markov head, or DFlash2's convs and selector): the same inputs, plain
+    launches timed, then one
     pass with every launch bracketed for the per-class times and the stream rates of the
     classes the variant changes."""
     steps = args.steps
@@ -462,7 +475,8 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     d.close()
     blocks = nb * steps / el
     wbytes = 1 if m.get("weight_format") == "fp8" else 2
-    variant = "fp8" if wbytes == 1 else "dspark" if m.get("markov_rank", 0) else "bf16"
+    variant = ("fp8" if wbytes == 1 else "dspark" if m.get("markov_rank", 0) else
+               "dflash2" if m.get("selector_rank", 0) else "bf16")
     log(f"[bench] batch16 ({variant}): {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; append of {nb}x{a} rows: "
         f"batched {app['batched']:.3f} ms, per sequence {app['per_seq']:.3f} ms")
     gemm_ms = br["gemm"][0] / steps

@@ -15,6 +15,7 @@ DFLASH_WEIGHTS_BF16, DFLASH_WEIGHTS_FP8_E4M3 = 0, 1
 CODE_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EPOOL", -4: "ERANGE", -5: "EHIP"}
 DFLASH_BUF_POOL, DFLASH_BUF_KPOS, DFLASH_BUF_SLOTS, DFLASH_BUF_BLOCKTAB, DFLASH_BUF_HIDDEN = 0, 1, 2, 3, 4
 DFLASH_BUF_HIDDEN_LO, DFLASH_BUF_FP8_LMHEAD, DFLASH_BUF_FP8_LMHEAD_SCALE = 5, 6, 7
+DFLASH_BUF_SEL_IDX, DFLASH_BUF_SEL_VALS = 8, 9
 
 
 class dflash_config(C.Structure):
@@ -29,21 +30,25 @@ class dflash_config(C.Structure):
         ("sliding_window", C.c_int32), ("layer_sliding", C.POINTER(C.c_uint8)),
         ("max_seq_len", C.c_int32), ("max_batch", C.c_int32), ("num_pages", C.c_int32),
         ("page_order", C.POINTER(C.c_int32)), ("weight_format", C.c_int32),
-        ("markov_rank", C.c_int32),
+        ("markov_rank", C.c_int32), ("conv_kernel_size", C.c_int32), ("conv_group_size", C.c_int32),
+        ("selector_rank", C.c_int32), ("selector_top_k", C.c_int32),
     ]
 
 
 class dflash_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "q_proj", "k_proj", "v_proj", "o_proj", "q_norm", "k_norm", "input_layernorm",
-        "post_attention_layernorm", "gate_proj", "up_proj", "down_proj")]
+        "post_attention_layernorm", "gate_proj", "up_proj", "down_proj",
+        "attention_conv_base", "attention_conv_proj", "mlp_conv_base", "mlp_conv_proj")]
 
 
 class dflash_weights(C.Structure):
     _fields_ = [("fc", C.c_void_p), ("hidden_norm", C.c_void_p), ("norm", C.c_void_p),
                 ("embed_tokens", C.c_void_p), ("lm_head", C.c_void_p),
                 ("layers", C.POINTER(dflash_layer_weights)),
-                ("markov_w1", C.c_void_p), ("markov_w2", C.c_void_p)]
+                ("markov_w1", C.c_void_p), ("markov_w2", C.c_void_p),
+                ("selector_pred", C.c_void_p), ("selector_succ", C.c_void_p),
+                ("selector_hidden_proj", C.c_void_p)]
 
 
 _lib = None
@@ -89,7 +94,7 @@ EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch
             "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
 
 K_CLASSES = ("prologue", "gemm", "qkv_post", "attn", "attn_combine", "resid_norm", "silu",
-             "lmhead", "argmax", "append_gemm", "append_misc", "markov")
+             "lmhead", "argmax", "append_gemm", "append_misc", "markov", "dconv", "selector")
 
 
 class DflashError(RuntimeError):
@@ -124,7 +129,9 @@ def make_config(m: dict, max_seq_len: int, max_batch: int, num_pages: int = 0, p
         max_seq_len=max_seq_len, max_batch=max_batch, num_pages=num_pages,
         page_order=C.cast(po, C.POINTER(C.c_int32)) if po is not None else None,
         weight_format=DFLASH_WEIGHTS_FP8_E4M3 if m.get("weight_format") == "fp8" else DFLASH_WEIGHTS_BF16,
-        markov_rank=int(m.get("markov_rank", 0)))
+        markov_rank=int(m.get("markov_rank", 0)),
+        conv_kernel_size=int(m.get("conv_kernel_size", 0)), conv_group_size=int(m.get("conv_group_size", 0)),
+        selector_rank=int(m.get("selector_rank", 0)), selector_top_k=int(m.get("selector_top_k", 0)))
     return cfg, (ls_arr, po)
 
 
@@ -154,13 +161,18 @@ class Drafter:
         for l in range(nl):
             p = f"layers.{l}."
             for f in dflash_layer_weights._fields_:
-                setattr(lay[l], f[0], weights[p + f[0]].data_ptr())
+                if p + f[0] in weights:
+                    setattr(lay[l], f[0], weights[p + f[0]].data_ptr())
         w = dflash_weights(fc=weights["fc"].data_ptr(), hidden_norm=weights["hidden_norm"].data_ptr(),
                            norm=weights["norm"].data_ptr(), embed_tokens=weights["embed_tokens"].data_ptr(),
                            lm_head=weights["lm_head"].data_ptr(), layers=lay)
         if m.get("markov_rank", 0):
             w.markov_w1 = weights["markov_w1"].data_ptr()
             w.markov_w2 = weights["markov_w2"].data_ptr()
+        if m.get("selector_rank", 0):
+            w.selector_pred = weights["selector_pred"].data_ptr()
+            w.selector_succ = weights["selector_succ"].data_ptr()
+            w.selector_hidden_proj = weights["selector_hidden_proj"].data_ptr()
         ctx = C.c_void_p()
         rc = self.L.dflash_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(ctx))
         if rc != DFLASH_OK:

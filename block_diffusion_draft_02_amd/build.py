@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
-SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_markov.hip", "runtime.hip"]
+SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_markov.hip", "k_dflash2.hip", "runtime.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -58,7 +58,8 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: a symbol no object defines fails the link, not the first load
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{_quiet(r.stdout + r.stderr)}")

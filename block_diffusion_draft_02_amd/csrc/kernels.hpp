@@ -225,4 +225,33 @@ int markov_step_groups(int V, int n_cu);
 hipError_t launch_markov_step(const MarkovStep& a, int groups, hipStream_t st);
 hipError_t launch_markov_finish(unsigned long long* best, int n, int gamma, int* tokens, hipStream_t st);
 
+
+// ---- DFlash2 (k_dflash2.hip) -------------------------------------------------------------
+// grouped dynamic causal convs: two taps, 16-channel groups; the projection's columns are
+// [application 2][tap 2][group h/16]. Rows of a band are consecutive (band b = rows
+// b*gamma .. b*gamma+gamma-1); tap 1 reads the band's previous row.
+hipError_t launch_dconv_prepare(const bf16* Xw, const bf16* Xw_lo, const float* ssq, float eps, int M, int h,
+                                int gamma, const float* P, int S, long long part_stride, int gsz, const bf16* base,
+                                float* dyn, bf16* U, bf16* U_lo, hipStream_t st);
+hipError_t launch_resid_dconv(float* X, const float* P, int S, long long part_stride, int gsz, int M, int h, int gamma,
+                              const float* dyn, const bf16* base, const bf16* w, float* ssq, bf16* Xw, bf16* Xw_lo,
+                              hipStream_t st);
+// top-16 candidates per drafted row: sliced partial lists (cv, ci: [rows][TOPK_MAX_SLICES][16]),
+// then merged into sel_v, sel_i [rows][16] (best first, ties to the lower index)
+constexpr int TOPK_MAX_SLICES = 64;
+int topk_slices(int V);
+hipError_t launch_topk_partial(const float* logits, int rows, int V, float* cv, int* ci, hipStream_t st);
+hipError_t launch_topk_merge(const float* cv, const int* ci, int rows, int V, float* sel_v, int* sel_i,
+                             hipStream_t st);
+// the candidate selector: pair scores [rows][16 prev][16 cand], then the greedy walk per band
+constexpr int SELECTOR_MAX_RANK = 512;
+struct SelectorBonus {
+  int t[MAX_BANDS];
+};
+hipError_t launch_selector_pairs(const int* sel_i, const float* sel_v, const float* Hp, int S, long long part_stride,
+                                 int gsz, int rank, int n_bands, int gamma, const SelectorBonus& bonus,
+                                 const bf16* pred, const bf16* succ, int vocab, float* pair, hipStream_t st);
+hipError_t launch_selector_walk(const int* sel_i, const float* pair, int n_bands, int gamma, int* tokens,
+                                hipStream_t st);
+
 }  // namespace dfl

@@ -32,6 +32,9 @@ struct LayerDev {
   // FP8 weights instead (weight_format 1): T16-FP8 codes and per-row scales of the same four
   uint8_t *q_qkv, *q_gu, *q_o, *q_down;
   float *s_qkv, *s_gu, *s_o, *s_down;
+  // DFlash2: the two conv sites' base kernels (the caller's) and T16 copies of their projections
+  const bf16 *cba = nullptr, *cbm = nullptr;
+  bf16 *w_cpa = nullptr, *w_cpm = nullptr;
 };
 
 struct SeqState {
@@ -68,6 +71,19 @@ struct dflash_ctx {
   float* mk_logits = nullptr;    // [max_batch*(gamma_max-1), V] logits when the caller wants none
   unsigned long long* mk_best = nullptr;   // [MARKOV_MAX_ROWS][MAX_BANDS] argmax keys, zero between forwards
   int mk_groups = 1;
+  // DFlash2 (selector_rank > 0): convs, top-16 candidates and the selector
+  bool d2 = false;
+  int sel_rank = 0;
+  const bf16 *sel_pred = nullptr, *sel_succ = nullptr;
+  bf16* sel_h = nullptr;            // T16 copy of the hidden projection [rank, h]
+  float *dyn_a = nullptr, *dyn_m = nullptr;   // [rows][h/4] dynamic taps of the two sites
+  bf16 *U = nullptr, *U_lo = nullptr;         // convolved sublayer input, hi + lo
+  float* tk_v = nullptr;            // [drafted rows][TOPK_MAX_SLICES][16] partial candidates
+  int* tk_i = nullptr;
+  float* sel_v = nullptr;           // [drafted rows][16] candidates and their logits
+  int* sel_i = nullptr;
+  float* sel_pair = nullptr;        // [drafted rows][16][16] pair scores
+  GemmPlan g_cp{}, g_sh{};
   std::vector<LayerDev> layers;
   bf16* w_kv = nullptr;        // [L*2*kvd, h]: K0;V0;K1;V1;... (row-major, for the tiled GEMM)
   bf16* w_kv_t = nullptr;      // the same in the T16 layout (short appends)
@@ -281,6 +297,23 @@ int check_config(const dflash_config* cfg, const dflash_weights* w, std::string&
   if (cfg->markov_rank != 0 && cfg->markov_rank != 256 && cfg->markov_rank != 512)
     return bad("markov_rank must be 0, 256 or 512");
   if (cfg->markov_rank && (!w->markov_w1 || !w->markov_w2)) return bad("a Markov head needs markov_w1 and markov_w2");
+  if (cfg->conv_kernel_size || cfg->conv_group_size || cfg->selector_rank || cfg->selector_top_k) {
+    if (cfg->conv_kernel_size != 2 || cfg->conv_group_size != 16 || cfg->selector_top_k != 16 ||
+        (cfg->selector_rank != 256 && cfg->selector_rank != 512))
+      return bad("DFlash2 needs conv_kernel_size 2, conv_group_size 16, selector_top_k 16, selector_rank 256 or 512");
+    if (cfg->markov_rank) return bad("a DFlash2 drafter has no Markov head");
+    if (cfg->vocab < 16) return bad("DFlash2 needs a vocabulary of at least 16");
+    if (!w->selector_pred || !w->selector_succ || !w->selector_hidden_proj) return bad("NULL selector weight");
+    auto a16 = [](const void* p) { return p && ((uintptr_t)p & 15) == 0; };
+    if (!a16(w->selector_pred) || !a16(w->selector_succ) || !a16(w->selector_hidden_proj))
+      return bad("selector weights must be non-NULL and 16-byte aligned");
+    for (int l = 0; l < cfg->num_layers; ++l) {
+      const dflash_layer_weights& lw = w->layers[l];
+      if (!a16(lw.attention_conv_base) || !a16(lw.attention_conv_proj) || !a16(lw.mlp_conv_base) ||
+          !a16(lw.mlp_conv_proj))
+        return bad("DFlash2 conv weights must be non-NULL and 16-byte aligned");
+    }
+  }
   if (cfg->rope_type == 1 && !(cfg->yarn_factor > 0 && cfg->yarn_orig_max_pos > 0 &&
                                cfg->yarn_beta_fast > 0 && cfg->yarn_beta_slow > 0))
     return bad("YaRN parameters must be positive");
@@ -427,6 +460,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->fp8 = cfg->weight_format == DFLASH_WEIGHTS_FP8_E4M3;
   c->R = cfg->markov_rank;
   c->mk_w1 = (const bf16*)w->markov_w1;
+  c->d2 = cfg->selector_rank > 0;
+  c->sel_rank = cfg->selector_rank;
+  c->sel_pred = (const bf16*)w->selector_pred;
+  c->sel_succ = (const bf16*)w->selector_succ;
   c->eps = cfg->rms_eps; c->rope_type = cfg->rope_type; c->window = cfg->sliding_window;
   c->sliding.assign(c->L, 0);
   if (cfg->layer_sliding)
@@ -465,7 +502,11 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->g_fc = plan_gemm(c->h, c->T * c->Ht);
   c->g_kvapp = plan_gemm(c->L * 2 * c->kvd, c->h);
   size_t part = 0;
-  for (const GemmPlan* g : {&c->g_qkv, &c->g_o, &c->g_gu, &c->g_down})
+  if (c->d2) {
+    c->g_cp = plan_gemm(c->h / 4, c->h);
+    c->g_sh = plan_gemm(c->sel_rank, c->h);
+  }
+  for (const GemmPlan* g : {&c->g_qkv, &c->g_o, &c->g_gu, &c->g_down, &c->g_cp, &c->g_sh})
     part = std::max(part, (size_t)g->S * c->m_max * g->N);
   for (const GemmPlan* g : {&c->g_fc, &c->g_kvapp}) {
     part = std::max(part, (size_t)g->S * APPEND_SKINNY * g->N);
@@ -518,10 +559,21 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   if (c->R) {
     c->mk_groups = markov_step_groups(c->V, c->n_cu);
     if ((rc = dalloc(c, &c->mk_w2t, (size_t)(c->V + 15) / 16 * 16 * c->R)) ||
-        (rc = dalloc(c, &c->mk_logits, (size_t)c->max_batch * (c->gmax - 1) * c->V)) ||
         (rc = dalloc(c, &c->mk_best, (size_t)MARKOV_MAX_ROWS * MAX_BANDS)))
       return fin(rc);
   }
+  const size_t drafted = (size_t)c->max_batch * (c->gmax - 1);
+  if ((c->R || c->d2) && (rc = dalloc(c, &c->mk_logits, drafted * c->V))) return fin(rc);
+  if (c->d2 &&
+      ((rc = dalloc(c, &c->sel_h, (size_t)c->sel_rank * hsz)) ||
+       (rc = dalloc(c, &c->dyn_a, (size_t)c->m_max * (hsz / 4))) ||
+       (rc = dalloc(c, &c->dyn_m, (size_t)c->m_max * (hsz / 4))) ||
+       (rc = dalloc(c, &c->U, (size_t)c->m_max * hsz)) || (rc = dalloc(c, &c->U_lo, (size_t)c->m_max * hsz)) ||
+       (rc = dalloc(c, &c->tk_v, drafted * TOPK_MAX_SLICES * 16)) ||
+       (rc = dalloc(c, &c->tk_i, drafted * TOPK_MAX_SLICES * 16)) ||
+       (rc = dalloc(c, &c->sel_v, drafted * 16)) || (rc = dalloc(c, &c->sel_i, drafted * 16)) ||
+       (rc = dalloc(c, &c->sel_pair, drafted * 16 * 16))))
+    return fin(rc);
   c->layers.resize(c->L);
   for (int l = 0; l < c->L; ++l) {
     LayerDev& d = c->layers[l];
@@ -529,6 +581,12 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
     d.q_norm = (const bf16*)lw.q_norm; d.k_norm = (const bf16*)lw.k_norm;
     if ((rc = dalloc(c, &d.in_norm, hsz)) || (rc = dalloc(c, &d.post_norm, hsz)))
       return fin(rc);
+    if (c->d2) {
+      d.cba = (const bf16*)lw.attention_conv_base;
+      d.cbm = (const bf16*)lw.mlp_conv_base;
+      if ((rc = dalloc(c, &d.w_cpa, (hsz / 4) * hsz)) || (rc = dalloc(c, &d.w_cpm, (hsz / 4) * hsz)))
+        return fin(rc);
+    }
     if (c->fp8) {
       if ((rc = dalloc(c, &d.q_qkv, (size_t)(c->qd + 2 * c->kvd) * hsz)) ||
           (rc = dalloc(c, &d.s_qkv, (size_t)(c->qd + 2 * c->kvd))) ||
@@ -598,6 +656,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   if (e == hipSuccess) e = c->fp8 ? quant(w->lm_head, c->V, c->h, c->lm_q, c->lm_s) : tile(w->lm_head, c->V, c->h, c->lm_head);
   if (e == hipSuccess) e = tile(w->fc, c->h, c->T * c->Ht, c->fc_t);
   if (e == hipSuccess && c->R) e = tile(w->markov_w2, c->V, c->R, c->mk_w2t);
+  if (e == hipSuccess && c->d2) {
+    e = tile(w->selector_hidden_proj, c->sel_rank, c->h, c->sel_h);
+    for (int l = 0; l < c->L && e == hipSuccess; ++l) {
+      if ((e = tile(w->layers[l].attention_conv_proj, c->h / 4, c->h, c->layers[l].w_cpa)) == hipSuccess)
+        e = tile(w->layers[l].mlp_conv_proj, c->h / 4, c->h, c->layers[l].w_cpm);
+    }
+  }
   if (e == hipSuccess && c->R) e = hipMemsetAsync(c->mk_best, 0, (size_t)MARKOV_MAX_ROWS * MAX_BANDS * 8, st);
   if (e == hipSuccess) e = tile(c->w_kv, c->L * 2 * c->kvd, c->h, c->w_kv_t);   // after the copies above, same stream
   std::vector<double> f = inv_freq_table(cfg, &c->mscale);
@@ -673,6 +738,12 @@ int dflash_debug_copy(dflash_ctx* c, int32_t buffer, void* dst, size_t offset, s
     case DFLASH_BUF_FP8_LMHEAD_SCALE:
       if (!c->fp8) return fail(c, DFLASH_EINVAL, "not an FP8 context");
       base = (const char*)c->lm_s; size = (size_t)(c->V + 15) / 16 * 16 * 4; break;
+    case DFLASH_BUF_SEL_IDX:
+      if (!c->d2) return fail(c, DFLASH_EINVAL, "not a DFlash2 context");
+      base = (const char*)c->sel_i; size = (size_t)c->max_batch * (c->gmax - 1) * 16 * 4; break;
+    case DFLASH_BUF_SEL_VALS:
+      if (!c->d2) return fail(c, DFLASH_EINVAL, "not a DFlash2 context");
+      base = (const char*)c->sel_v; size = (size_t)c->max_batch * (c->gmax - 1) * 16 * 4; break;
     default: return fail(c, DFLASH_EINVAL, "unknown buffer %d", buffer);
   }
   if (offset > size || bytes > size - offset) return fail(c, DFLASH_ERANGE, "copy past the end of buffer %d", buffer);
@@ -939,11 +1010,25 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     }
     return hipSuccess;
   };
+  // DFlash2 conv site: the projection of the normed rows (x * w with the rows' RMSNorm
+  // scales, as the QKV and gate/up GEMMs take them), then the taps and the prepare application
+  auto dconv_site = [&](const bf16* w_proj, const bf16* base, float* dyn) -> hipError_t {
+    hipError_t e = gemm(c->Xn, c->Xn_lo, c->h, w_proj, nullptr, c->g_cp, true);
+    if (e != hipSuccess) return e;
+    return timed(c, DFLASH_K_DCONV, st, [&] {
+      return launch_dconv_prepare(c->Xn, c->Xn_lo, c->ssq, c->eps, M, c->h, gamma, c->part, parts(c->g_cp).first,
+                                  (long long)M * c->g_cp.N, parts(c->g_cp).second, base, dyn, c->U, c->U_lo, st);
+    });
+  };
   for (int l = 0; l < c->L; ++l) {
     const LayerDev& d = c->layers[l];
     const int sw = sliding_layer(c, l) ? 1 : 0;
     const bool q8 = c->fp8;
-    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, q8 ? (const bf16*)d.q_qkv : d.w_qkv, q8 ? d.s_qkv : nullptr, c->g_qkv, true));
+    // DFlash2: the attention input through its dynamic conv (projection of the normed input,
+    // then taps + convolution); the QKV GEMM then reads the convolved rows as they are
+    if (c->d2) HIPCHK(c, dconv_site(d.w_cpa, d.cba, c->dyn_a));
+    HIPCHK(c, gemm(c->d2 ? c->U : c->Xn, c->d2 ? c->U_lo : c->Xn_lo, c->h, q8 ? (const bf16*)d.q_qkv : d.w_qkv,
+                   q8 ? d.s_qkv : nullptr, c->g_qkv, !c->d2));
     HIPCHK(c, timed(c, DFLASH_K_QKV_POST, st, [&] {
       return launch_qkv_post(c->part, parts(c->g_qkv).first, (long long)M * c->g_qkv.N, parts(c->g_qkv).second,
                              M, gamma, c->bands_dev,
@@ -960,17 +1045,35 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     }));
     HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, q8 ? (const bf16*)d.q_o : d.o_proj, q8 ? d.s_o : nullptr, c->g_o, false));
     HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+      if (c->d2)
+        return launch_resid_dconv(c->X, c->part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
+                                  M, c->h, gamma, c->dyn_a, d.cba, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
       return launch_resid_sum(c->X, c->part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
                               M, c->h, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
     }));
-    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, q8 ? (const bf16*)d.q_gu : d.w_gu, q8 ? d.s_gu : nullptr, c->g_gu, true));
+    if (c->d2) HIPCHK(c, dconv_site(d.w_cpm, d.cbm, c->dyn_m));
+    HIPCHK(c, gemm(c->d2 ? c->U : c->Xn, c->d2 ? c->U_lo : c->Xn_lo, c->h, q8 ? (const bf16*)d.q_gu : d.w_gu,
+                   q8 ? d.s_gu : nullptr, c->g_gu, !c->d2));
     HIPCHK(c, timed(c, DFLASH_K_SILU, st, [&] {
       return launch_silu_mul(c->part, parts(c->g_gu).first, (long long)M * c->g_gu.N, parts(c->g_gu).second, M,
                              c->ff, c->act, c->act_lo, st);
     }));
     HIPCHK(c, gemm(c->act, c->act_lo, c->ff, q8 ? (const bf16*)d.q_down : d.down_proj, q8 ? d.s_down : nullptr,
                    c->g_down, false));
-    if (l + 1 < c->L) {
+    if (c->d2) {
+      // the MLP output through the finish application, then (after the last layer) the
+      // final norm of the residual rows
+      const bf16* nw = l + 1 < c->L ? c->layers[l + 1].in_norm : c->norm;
+      HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+        return launch_resid_dconv(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
+                                  parts(c->g_down).second, M, c->h, gamma, c->dyn_m, d.cbm, nw, c->ssq, c->Xn,
+                                  c->Xn_lo, st);
+      }));
+      if (l + 1 == c->L)
+        HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
+          return launch_rows_rmsnorm(c->X, 1, 0, 1, M, c->h, c->norm, c->eps, c->Xn, c->Xn_lo, st);
+        }));
+    } else if (l + 1 < c->L) {
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
         return launch_resid_sum(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
                                 parts(c->g_down).second, M, c->h, c->layers[l + 1].in_norm, c->ssq, c->Xn,
@@ -992,9 +1095,10 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   const int ng = lm_wide ? lmhead_wide_groups(c->V) : ng_p > 0 ? std::min(ng_p, c->lm_groups) : c->lm_groups;
   const bf16* lmw = c->fp8 ? (const bf16*)c->lm_q : c->lm_head;
   const float* lms = c->fp8 ? c->lm_s : nullptr;
-  // a Markov head needs every drafted row's logits: the caller's buffer, else the context's
+  // a Markov head and DFlash2's candidates need every drafted row's logits: the caller's
+  // buffer, else the context's
   float* const user_logits = logits;
-  if (c->R && !logits) logits = c->mk_logits;
+  if ((c->R || c->d2) && !logits) logits = c->mk_logits;
   if (lm_wide) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
       return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, lmw, c->V, c->h, c->best_v, c->best_i, ng, gamma,
@@ -1014,6 +1118,29 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
                                     c->best_v, c->best_i, ng, gamma, logits, st);
       }));
     }
+  }
+  if (c->d2) {
+    // the selector's hidden projection of the final-normed rows, the top-16 candidates of
+    // every drafted row, their pair scores and the walk
+    HIPCHK(c, gemm(c->Xn, c->Xn_lo, c->h, c->sel_h, nullptr, c->g_sh, false));
+    SelectorBonus sb{};
+    for (int b = 0; b < n_seqs; ++b) sb.t[b] = bonus[b];
+    const int drafted = n_seqs * (gamma - 1);
+    HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
+      return launch_topk_partial(logits, drafted, c->V, c->tk_v, c->tk_i, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
+      return launch_topk_merge(c->tk_v, c->tk_i, drafted, c->V, c->sel_v, c->sel_i, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
+      return launch_selector_pairs(c->sel_i, c->sel_v, c->part, parts(c->g_sh).first, (long long)M * c->g_sh.N,
+                                   parts(c->g_sh).second, c->sel_rank, n_seqs, gamma, sb, c->sel_pred, c->sel_succ,
+                                   c->V, c->sel_pair, st);
+    }));
+    HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
+      return launch_selector_walk(c->sel_i, c->sel_pair, n_seqs, gamma, draft_tokens, st);
+    }));
+    return DFLASH_OK;
   }
   if (!c->R) {
     HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] {

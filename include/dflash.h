@@ -81,6 +81,10 @@ typedef struct {
   int32_t weight_format;           /* DFLASH_WEIGHTS_BF16 or DFLASH_WEIGHTS_FP8_E4M3 */
   int32_t markov_rank;             /* DSpark Markov head: 0 = none, else its rank R, 256 or 512
                                       (see dflash_weights and dflash_block_forward) */
+  int32_t conv_kernel_size, conv_group_size, selector_rank, selector_top_k;
+                                   /* DFlash2: all 0 = none; else 2, 16, 256 or 512, 16 (see
+                                      dflash_layer_weights, dflash_weights, dflash_block_forward).
+                                      Not together with a Markov head. */
 } dflash_config;
 
 /* Weight formats (metrale_model_arch/dflash_head/from_weights.rs, the FP8 weights phase of
@@ -101,6 +105,12 @@ typedef struct {
   const void *q_proj, *k_proj, *v_proj, *o_proj, *q_norm, *k_norm;
   const void *input_layernorm, *post_attention_layernorm;
   const void *gate_proj, *up_proj, *down_proj;
+  /* DFlash2 only (NULL otherwise; spark_model/layers/dflash_head.rs, the DFlash2 fields):
+   * the grouped dynamic conv of the attention input and of the MLP input, each a base kernel
+   * [2 applications][conv_kernel_size][hidden] and a kernel projection
+   * [2 * conv_kernel_size * hidden / conv_group_size, hidden] (rows [application][tap][group]);
+   * device bf16, 16-byte aligned; the base kernels are read in place, the projections copied */
+  const void *attention_conv_base, *attention_conv_proj, *mlp_conv_base, *mlp_conv_proj;
 } dflash_layer_weights;
 
 /* fc [hidden, num_taps*target_hidden]; hidden_norm, norm [hidden]; embed_tokens and
@@ -115,6 +125,10 @@ typedef struct {
   const void *fc, *hidden_norm, *norm, *embed_tokens, *lm_head;
   const dflash_layer_weights *layers;
   const void *markov_w1, *markov_w2;
+  /* DFlash2 only (NULL otherwise): the candidate selector's predecessor and successor
+   * codebooks [vocab, selector_rank] (read in place) and hidden projection
+   * [selector_rank, hidden] (copied); device bf16, 16-byte aligned */
+  const void *selector_pred, *selector_succ, *selector_hidden_proj;
 } dflash_weights;
 
 /* Create a drafter: validates the configuration, allocates the KV pool, block tables and
@@ -177,6 +191,19 @@ int dflash_ctx_kv_append_batch(dflash_ctx *ctx, int32_t n_seqs, const int32_t *s
  * markov_w2 @ markov_w1[t_k] added to its logits, with t_0 = bonus_tokens[b] and t_k =
  * draft_tokens[b][k-1], and draft_tokens[b][k] is the argmax of the biased row; `logits`
  * then holds the biased rows.
+ * DFlash2 (conv_kernel_size > 0; spark_model/layers/dflash_head.rs: the dflash2_conv2,
+ * dflash2_topk16 and dflash2_selector_walk kernels and their scratch; the pages give shapes
+ * and names, the composition here is this library's reading):
+ *   - every layer's attention and MLP inputs pass through a grouped dynamic causal conv:
+ *     with h_n the sublayer's normed input, row t's taps are base[a][j][c] +
+ *     (proj @ h_n[t])[(a * conv_kernel_size + j) * (hidden / 16) + c / 16]; the sublayer reads
+ *     u[t] = sum_j tap[0][j] * h_n[t-j] and its output s is added to the residual as
+ *     sum_j tap[1][j] * s[t-j] (rows before the band's first contribute zero);
+ *   - each drafted row's 16 largest logits are its candidates (ties to the lower index);
+ *     H = selector_hidden_proj @ y (y: the row's final-normed hidden state); candidate c
+ *     scores logit(c) + sum_r pred[p][r] * H[r] * succ[c][r], p the previous row's draft
+ *     (bonus_tokens[b] for the first); the best-scoring candidate (the earlier one on a tie)
+ *     is the row's draft. `logits` holds the plain lm_head logits.
  * Errors: EINVAL (n_seqs not in 1..max_batch, NULL pointers, bonus token out of range),
  * ERANGE (seq out of range or repeated, gamma not in [2, gamma_max]), EPOOL. */
 int dflash_block_forward(dflash_ctx *ctx, int32_t n_seqs, const int32_t *seqs,
@@ -217,10 +244,14 @@ int dflash_pool_geometry(const dflash_ctx *ctx, int64_t *num_pages, int64_t *pag
  *                        layout: vocab rows in tiles of 16, a tile's hidden dimension in
  *                        256-deep blocks of 4096 bytes, byte (q*64 + lane)*16 + b of a block
  *                        holding row lane%16 at k = 64q + 32*(b/8) + 8*(lane/16) + b%8;
- *   DFLASH_BUF_FP8_LMHEAD_SCALE (FP8 contexts) float [vocab rounded up to 16]: the row scales. */
+ *   DFLASH_BUF_FP8_LMHEAD_SCALE (FP8 contexts) float [vocab rounded up to 16]: the row scales;
+ *   DFLASH_BUF_SEL_IDX   (DFlash2) int32 [n_seqs*(gamma-1)][16]: the last forward's candidates
+ *                        per drafted row, best first;
+ *   DFLASH_BUF_SEL_VALS  (DFlash2) float [n_seqs*(gamma-1)][16]: their logits. */
 enum { DFLASH_BUF_POOL = 0, DFLASH_BUF_KPOS = 1, DFLASH_BUF_SLOTS = 2,
        DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4, DFLASH_BUF_HIDDEN_LO = 5,
-       DFLASH_BUF_FP8_LMHEAD = 6, DFLASH_BUF_FP8_LMHEAD_SCALE = 7 };
+       DFLASH_BUF_FP8_LMHEAD = 6, DFLASH_BUF_FP8_LMHEAD_SCALE = 7, DFLASH_BUF_SEL_IDX = 8,
+       DFLASH_BUF_SEL_VALS = 9 };
 int dflash_debug_copy(dflash_ctx *ctx, int32_t buffer, void *dst, size_t offset, size_t bytes,
                       void *stream);
 
@@ -244,7 +275,9 @@ enum {
   DFLASH_K_APPEND_GEMM = 9,   /* fc and fused K/V GEMMs of the context append */
   DFLASH_K_APPEND_MISC = 10,  /* append slots, hidden_norm, K/V epilogue + writeback */
   DFLASH_K_MARKOV = 11,       /* the Markov head's chain steps (one per drafted row) */
-  DFLASH_K_NUM_CLASSES = 12
+  DFLASH_K_DCONV = 12,        /* DFlash2 conv prepare (taps + convolved sublayer input) */
+  DFLASH_K_SELECTOR = 13,     /* DFlash2 top-16 candidates, pair scores and walk */
+  DFLASH_K_NUM_CLASSES = 14
 };
 int dflash_timing(dflash_ctx *ctx, uint32_t class_mask);
 int dflash_timing_read(dflash_ctx *ctx, double *ms, int64_t *launches, int32_t n_classes);

@@ -47,10 +47,11 @@ class Pair:
         self.ora.ctx_kv_append_batch(seqs, counts, H, positions=positions)
 
     def forward(self, seqs, bonus, q_rope_pos=None, gamma=None, with_logits=True):
-        """One forward on both sides. With a Markov head the oracle's chain is teacher-forced
-        onto the GPU's drafts (row k's bias uses the GPU's draft of row k-1), so a branch the
-        GPU took at a near-tie is compared on its own terms; the criteria then check each
-        row's draft against the oracle's argmax of the same biased row.
+        """One forward on both sides. With a Markov head (or a DFlash2 selector) the oracle's
+        chain is teacher-forced onto the GPU's drafts (row k's bias, or pair score, uses the
+        GPU's draft of row k-1), so a branch the GPU took at a near-tie is compared on its own
+        terms; the criteria then check each row's draft against the oracle's choice for the
+        same previous token.
         with_logits=False passes no logits buffer (the drafts alone; logits are None)."""
         gamma = self.m["gamma_max"] if gamma is None else gamma
         n = len(seqs)
@@ -60,7 +61,7 @@ class Pair:
         torch.cuda.synchronize()
         t = toks.cpu().numpy()
         prev = None
-        if self.m.get("markov_rank", 0):
+        if self.m.get("markov_rank", 0) or self.m.get("selector_rank", 0):
             prev = np.concatenate([np.asarray(bonus, dtype=np.int64).reshape(n, 1), t[:, :-1]], axis=1)
         ref = self.ora.block_forward(seqs, bonus, q_rope_pos=q_rope_pos, gamma=gamma, markov_prev=prev)
         lg = logits.cpu().numpy().astype(np.float64).reshape(n, gamma - 1, -1) if with_logits else None

@@ -123,8 +123,9 @@ def test_config_struct_layout_matches_header():
     assert B.dflash_config.page_order.offset == 128
     assert B.dflash_config.weight_format.offset == 136
     assert B.dflash_config.markov_rank.offset == 140
-    assert C.sizeof(B.dflash_config) == 144
-    assert C.sizeof(B.dflash_layer_weights) == 88 and C.sizeof(B.dflash_weights) == 64
+    assert B.dflash_config.selector_top_k.offset == 156
+    assert C.sizeof(B.dflash_config) == 160
+    assert C.sizeof(B.dflash_layer_weights) == 120 and C.sizeof(B.dflash_weights) == 88
 
 
 def test_struct_layouts_match_the_c_compiler(tmp_path):
@@ -168,4 +169,25 @@ def test_create_rejects_bad_markov_heads():
     for w1, w2 in ((None, 0x1000), (0x1000, None), (0x1008, 0x1000), (0x1000, 0x1004)):
         w.markov_w1, w.markov_w2 = w1, w2
         assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+    assert not ctx.value
+
+
+def test_create_rejects_bad_dflash2_heads():
+    m = synth.model("tiny-L2-h256-dflash2")
+    w, lay = _null_weights(m)
+    w.selector_pred = w.selector_succ = w.selector_hidden_proj = 0x1000
+    ctx = C.c_void_p()
+    # unsupported sizes, a partial configuration, and a Markov head beside DFlash2
+    for change in (dict(conv_kernel_size=3), dict(conv_group_size=8), dict(selector_top_k=8), dict(selector_rank=128),
+                   dict(selector_rank=0), dict(conv_kernel_size=0), dict(markov_rank=256)):
+        cfg, keep = B.make_config(dict(m, **change), 128, 1)
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL, change
+    # missing or misaligned DFlash2 weights (the layers' conv pointers are 0x1000 from _null_weights)
+    cfg, keep = B.make_config(m, 128, 1)
+    for field, val in (("selector_pred", None), ("selector_hidden_proj", 0x1008)):
+        setattr(w, field, val)
+        assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
+        setattr(w, field, 0x1000)
+    lay[1].mlp_conv_base = None
+    assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
     assert not ctx.value
