@@ -125,8 +125,31 @@ __global__ __launch_bounds__(64) void k_resid_dconv(float* __restrict__ X, const
 }
 
 // ---- top-16 --------------------------------------------------------------------------------
-// a larger value, or an equal one at a lower index, ranks first (NaN never enters)
-__device__ __forceinline__ bool tk_before(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+// a larger value, or an equal one at a lower index, ranks first (NaN never enters). Written
+// without short-circuit evaluation: with the operands in LDS, `||` / `&&` made the compiler
+// branch around (and wait on) each load.
+__device__ __forceinline__ bool tk_before(float v, int i, float bv, int bi) {
+  return (v > bv) | ((v == bv) & (i < bi));
+}
+
+// how many of the N candidates in LDS rank before (v, i); unique indices make the ranks
+// unique. N is fixed (unused slots hold (-inf, distinct indices past the vocabulary), which
+// rank after every real candidate); the loop is unrolled with four counters so the LDS
+// reads are issued back to back.
+template <int N>
+__device__ __forceinline__ int tk_rank(float v, int i, const float* sv, const int* si) {
+  int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+#pragma unroll
+  for (int j = 0; j < N; j += 4) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sv + j);
+    const i32x4 b = *reinterpret_cast<const i32x4*>(si + j);
+    r0 += (int)tk_before(a[0], b[0], v, i);
+    r1 += (int)tk_before(a[1], b[1], v, i);
+    r2 += (int)tk_before(a[2], b[2], v, i);
+    r3 += (int)tk_before(a[3], b[3], v, i);
+  }
+  return (r0 + r1) + (r2 + r3);
+}
 
 // insert (v, i) into a thread's sorted list (best first) if it ranks above its last entry
 __device__ __forceinline__ void tk_insert(float (&lv)[TOPK], int (&li)[TOPK], float v, int i) {
@@ -142,36 +165,24 @@ __device__ __forceinline__ void tk_insert(float (&lv)[TOPK], int (&li)[TOPK], fl
   }
 }
 
-// The workgroup's 16 best over every thread's sorted list: 16 rounds, each taking the best
-// list head (a wave reduction, then the 4 waves) and popping it from its owner's list.
-__device__ void tk_workgroup(float (&lv)[TOPK], int (&li)[TOPK], float* __restrict__ out_v,
-                             int* __restrict__ out_i) {
-  __shared__ float wv[4];
-  __shared__ int wi[4], wt[4];
-  __shared__ int win_t;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// The wavefront's 16 best over its lanes' sorted lists: 16 rounds, each taking the best list
+// head across the lanes (no barrier) and popping it from its owner's list. Lane q gets entry q
+// in (wv, wi) for q < 16.
+__device__ __forceinline__ void tk_wave(float (&lv)[TOPK], int (&li)[TOPK], float& wv, int& wi) {
+  const int lane = threadIdx.x & 63;
+  wv = -INFINITY;
+  wi = 0x7fffffff;
   for (int q = 0; q < TOPK; ++q) {
     float v = lv[0];
-    int i = li[0], t = threadIdx.x;
+    int i = li[0], t = lane;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(v, o, 64);
       const int oi = __shfl_xor(i, o, 64), ot = __shfl_xor(t, o, 64);
       if (tk_before(ov, oi, v, i)) { v = ov; i = oi; t = ot; }
     }
-    if (lane == 0) { wv[wave] = v; wi[wave] = i; wt[wave] = t; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float bv = wv[0];
-      int bi = wi[0], bt = wt[0];
-      for (int w = 1; w < 4; ++w)
-        if (tk_before(wv[w], wi[w], bv, bi)) { bv = wv[w]; bi = wi[w]; bt = wt[w]; }
-      out_v[q] = bv;
-      out_i[q] = bi;
-      win_t = bt;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x == win_t) {
+    if (lane == q) { wv = v; wi = i; }
+    if (lane == t) {
 #pragma unroll
       for (int p = 0; p < TOPK - 1; ++p) { lv[p] = lv[p + 1]; li[p] = li[p + 1]; }
       lv[TOPK - 1] = -INFINITY;
@@ -180,32 +191,114 @@ __device__ void tk_workgroup(float (&lv)[TOPK], int (&li)[TOPK], float* __restri
   }
 }
 
-// One 256-thread workgroup per (drafted row, vocabulary slice): the slice's 16 best logits.
-__global__ __launch_bounds__(256) void k_topk_partial(const float* __restrict__ logits, int V, int slice,
-                                                      float* __restrict__ cv, int* __restrict__ ci) {
-  const int row = blockIdx.x, sl = blockIdx.y;
+// The 16 best of up to 64 candidates, one a lane (-inf where there is none): lane q gets entry q.
+__device__ __forceinline__ void tk_wave64(float v0, int i0, float& wv, int& wi) {
   float lv[TOPK];
   int li[TOPK];
+  lv[0] = v0;
+  li[0] = i0;
 #pragma unroll
-  for (int q = 0; q < TOPK; ++q) { lv[q] = -INFINITY; li[q] = 0x7fffffff; }
-  const int lo = sl * slice, hi = min(V, lo + slice);
-  const float* lr = logits + (size_t)row * V;
-  for (int v = lo + threadIdx.x; v < hi; v += 256) tk_insert(lv, li, lr[v], v);
-  const size_t o = ((size_t)row * gridDim.y + sl) * TOPK;
-  tk_workgroup(lv, li, cv + o, ci + o);
+  for (int q = 1; q < TOPK; ++q) { lv[q] = -INFINITY; li[q] = 0x7fffffff; }
+  tk_wave(lv, li, wv, wi);
 }
 
-// One workgroup per drafted row: the row's 16 best over its slices' lists.
-__global__ __launch_bounds__(256) void k_topk_merge(const float* __restrict__ cv, const int* __restrict__ ci,
-                                                    int n_slices, float* __restrict__ sel_v, int* __restrict__ sel_i) {
-  const int row = blockIdx.x;
+// Visit the elements [lo, hi) of a logits row, thread by thread: f(x, index). With a 16-byte
+// aligned row and 4-aligned bounds the loads are float4, four per lane in flight per round;
+// otherwise one float at a time.
+template <class F>
+__device__ __forceinline__ void tk_scan(const float* __restrict__ lr, int lo, int hi, bool vec, F&& f) {
+  if (vec) {
+    constexpr int U = 4;
+    const f32x4* l4 = reinterpret_cast<const f32x4*>(lr);
+    const int lo4 = lo / 4, hi4 = hi / 4;
+    for (int q = lo4 + (int)threadIdx.x; q < hi4; q += 256 * U) {
+      f32x4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = q + u * 256;
+        x[u] = k < hi4 ? l4[k] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f(x[u][e], (q + u * 256) * 4 + e);
+    }
+  } else {
+    for (int v = lo + (int)threadIdx.x; v < hi; v += 256) f(lr[v], v);
+  }
+}
+
+// One 256-thread workgroup per (drafted row, vocabulary slice): the slice's 16 best logits.
+// Pass 1: every thread's maximum; the 16th largest of those (by rank: each wave's 16 best, then
+// the best 16 of those 64) is a lower bound T of the slice's 16th largest value, since the 16
+// largest maxima are 16 distinct elements. Pass 2: the elements >= T are gathered in LDS (an
+// LDS counter) and ranked. More than 64 of them (mass ties) fall back to every thread's
+// sorted list, so the result is exact either way.
+__global__ __launch_bounds__(256) void k_topk_partial(const float* __restrict__ logits, int V, int slice,
+                                                      float* __restrict__ cv, int* __restrict__ ci) {
+  constexpr int CAP = 64;
+  __shared__ __attribute__((aligned(16))) float mv[256];
+  __shared__ __attribute__((aligned(16))) int mix[256];
+  __shared__ __attribute__((aligned(16))) float tv[4 * TOPK];
+  __shared__ __attribute__((aligned(16))) int ti[4 * TOPK];
+  __shared__ __attribute__((aligned(16))) float gv[CAP];
+  __shared__ __attribute__((aligned(16))) int gi[CAP];
+  __shared__ int cnt;
+  __shared__ float thr;
+  const int row = blockIdx.x, sl = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = sl * slice, hi = min(V, lo + slice);
+  const float* lr = logits + (size_t)row * V;
+  const bool vec = (V & 3) == 0 && (slice & 3) == 0 && ((uintptr_t)logits & 15) == 0;
+  float mx = -INFINITY;
+  int mi = 0x7fffffff - (int)threadIdx.x;   // empty threads stay distinct (and last)
+  tk_scan(lr, lo, hi, vec, [&](float x, int v) {
+    if (tk_before(x, v, mx, mi)) { mx = x; mi = v; }
+  });
+  mv[threadIdx.x] = mx;
+  mix[threadIdx.x] = mi;
+  if (threadIdx.x == 0) cnt = 0;
+  __syncthreads();
+  {
+    const int r = tk_rank<64>(mx, mi, mv + wave * 64, mix + wave * 64);
+    if (r < TOPK) { tv[wave * TOPK + r] = mx; ti[wave * TOPK + r] = mi; }
+  }
+  __syncthreads();
+  if (wave == 0 && tk_rank<4 * TOPK>(tv[lane], ti[lane], tv, ti) == TOPK - 1) thr = tv[lane];
+  if (wave == 1) { gv[lane] = -INFINITY; gi[lane] = 0x7fffffff - lane; }   // unused gather slots
+  __syncthreads();
+  const float t = thr;
+  tk_scan(lr, lo, hi, vec, [&](float x, int v) {
+    if (x >= t) {
+      const int q = atomicAdd(&cnt, 1);
+      if (q < CAP) { gv[q] = x; gi[q] = v; }
+    }
+  });
+  __syncthreads();
+  const int n = cnt;
+  const size_t o = ((size_t)row * gridDim.y + sl) * TOPK;
+  if (n <= CAP) {
+    // n >= 16: the 16 largest maxima are all >= T
+    if (wave == 0 && lane < n) {
+      const int r = tk_rank<CAP>(gv[lane], gi[lane], gv, gi);
+      if (r < TOPK) { cv[o + r] = gv[lane]; ci[o + r] = gi[lane]; }
+    }
+    return;
+  }
+  // mass ties at the threshold: every thread's sorted list, then the waves' 16 best, then wave 0
   float lv[TOPK];
   int li[TOPK];
 #pragma unroll
   for (int q = 0; q < TOPK; ++q) { lv[q] = -INFINITY; li[q] = 0x7fffffff; }
-  const size_t base = (size_t)row * n_slices * TOPK;
-  for (int q = threadIdx.x; q < n_slices * TOPK; q += 256) tk_insert(lv, li, cv[base + q], ci[base + q]);
-  tk_workgroup(lv, li, sel_v + (size_t)row * TOPK, sel_i + (size_t)row * TOPK);
+  tk_scan(lr, lo, hi, vec, [&](float x, int v) { tk_insert(lv, li, x, v); });
+  float wv;
+  int wi;
+  tk_wave(lv, li, wv, wi);
+  if (lane < TOPK) { tv[wave * TOPK + lane] = wv; ti[wave * TOPK + lane] = wi; }
+  __syncthreads();
+  if (wave == 0) {
+    tk_wave64(tv[lane], ti[lane], wv, wi);
+    if (lane < TOPK) { cv[o + lane] = wv; ci[o + lane] = wi; }
+  }
 }
 
 // ---- selector ------------------------------------------------------------------------------
@@ -213,58 +306,149 @@ __global__ __launch_bounds__(256) void k_topk_merge(const float* __restrict__ cv
 // scores T[p][c] = logit(c) + sum_r pred[prev_p][r] * H[r] * succ[c][r] for the row's candidates
 // c and the previous row's candidates p (the band's bonus token alone for its first drafted
 // row). H = the canonical sum of the hidden projection's split partials for block row b*gamma+i.
-__global__ __launch_bounds__(256) void k_selector_pairs(const int* __restrict__ sel_i, const float* __restrict__ sel_v,
-                                                        const float* __restrict__ Hp, int S, long long ps, int gsz,
-                                                        int rank, int gamma, int V, SelectorBonus bonus,
+// The 16 predecessor rows (times H) and the 16 successor rows are staged in LDS with all their
+// loads issued at once; each thread then forms one (p, c) dot product from LDS.
+template <int R>
+__global__ __launch_bounds__(256) void k_selector_pairs(const float* __restrict__ cv, const int* __restrict__ ci,
+                                                        int n_slices, const float* __restrict__ Hp, int S, long long ps,
+                                                        int gsz, int gamma, int V, SelectorBonus bonus,
                                                         const bf16* __restrict__ pred, const bf16* __restrict__ succ,
+                                                        float* __restrict__ sel_v, int* __restrict__ sel_i,
                                                         float* __restrict__ pair) {
-  __shared__ float sH[SELECTOR_MAX_RANK];
+  __shared__ float sH[R];
+  // pred[prev_p] * H and succ[cand_c]; rows 4 floats apart mod 64 banks: 16 lanes reading one
+  // float4 each from 16 rows touch 64 distinct banks
+  __shared__ __attribute__((aligned(16))) float sG[TOPK][R + 4];
+  __shared__ __attribute__((aligned(16))) float sS[TOPK][R + 4];
+  __shared__ float scv[TOPK];
   __shared__ int sprev[TOPK], scand[TOPK];
-  const int d = blockIdx.x, g1 = gamma - 1;
+  __shared__ __attribute__((aligned(16))) float mv2[2][TOPK_MAX_SLICES * TOPK];
+  __shared__ __attribute__((aligned(16))) int mi2[2][TOPK_MAX_SLICES * TOPK];
+  const int d = blockIdx.x, g1 = gamma - 1, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = d / g1, i = d % g1 + 1;
   const int row = b * gamma + i;
-  for (int q = threadIdx.x; q < rank; q += 256) sH[q] = sum_splits<8, float>(Hp + (size_t)row * rank + q, S, ps, gsz);
-  if (threadIdx.x < TOPK) {
-    scand[threadIdx.x] = sel_i[(size_t)d * TOPK + threadIdx.x];
-    sprev[threadIdx.x] = i == 1 ? bonus.t[b] : sel_i[(size_t)(d - 1) * TOPK + threadIdx.x];
+  const int np = i == 1 ? 1 : TOPK;
+  // the row's candidates (wave 0) and the previous row's (wave 1), each the 16 best of the
+  // row's slice lists (at most 64 entries, one a lane); the first drafted row's predecessor is
+  // the band's bonus token
+  // the slices' lists of this row (k = 0) and of the previous drafted row (k = 1): at most
+  // 256 entries each, every one ranked by one thread
+  const int nc = n_slices * TOPK;
+  const int nrows = i > 1 ? 2 : 1;
+  for (int k = 0; k < nrows; ++k) {
+    const size_t base = (size_t)(d - k) * nc;
+    const bool in = (int)threadIdx.x < nc;
+    mv2[k][threadIdx.x] = in ? cv[base + threadIdx.x] : -INFINITY;
+    mi2[k][threadIdx.x] = in ? ci[base + threadIdx.x] : 0x7fffffff - (int)threadIdx.x;
+  }
+  for (int q = threadIdx.x; q < R; q += 256) sH[q] = sum_splits<8, float>(Hp + (size_t)row * R + q, S, ps, gsz);
+  __syncthreads();
+  for (int k = 0; k < nrows; ++k)
+    if ((int)threadIdx.x < nc) {
+      const float v = mv2[k][threadIdx.x];
+      const int id = mi2[k][threadIdx.x];
+      const int r = tk_rank<TOPK_MAX_SLICES * TOPK>(v, id, mv2[k], mi2[k]);
+      if (r < TOPK) {
+        // (ids are clamped: a row with fewer than 16 finite logits leaves placeholder entries)
+        const int cid = min(max(id, 0), V - 1);
+        if (k == 0) {
+          scand[r] = cid;
+          scv[r] = v;
+          sel_v[(size_t)d * TOPK + r] = v;
+          sel_i[(size_t)d * TOPK + r] = id;
+        } else {
+          sprev[r] = cid;
+        }
+      }
+    }
+  if (i == 1 && threadIdx.x < TOPK) sprev[threadIdx.x] = min(max(bonus.t[b], 0), V - 1);
+  __syncthreads();
+  // 8 bf16 per 16-byte piece: R / 8 pieces a row, 2 * TOPK rows
+  constexpr int PPR = R / 8;
+  constexpr int NPIECE = 2 * TOPK * PPR;
+  u32x4 v[(NPIECE + 255) / 256];
+#pragma unroll
+  for (int u = 0; u < (NPIECE + 255) / 256; ++u) {
+    const int q = threadIdx.x + u * 256;
+    const int r2 = q / PPR, k = (q % PPR) * 8;
+    const bool is_pred = r2 < TOPK;
+    const int id = is_pred ? sprev[r2] : scand[r2 - TOPK];
+    v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (q < NPIECE && (!is_pred || r2 < np))
+      v[u] = *reinterpret_cast<const u32x4*>((is_pred ? pred : succ) + (size_t)id * R + k);
+  }
+#pragma unroll
+  for (int u = 0; u < (NPIECE + 255) / 256; ++u) {
+    const int q = threadIdx.x + u * 256;
+    if (q >= NPIECE) continue;
+    const int r2 = q / PPR, k = (q % PPR) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = bf2f((bf16)((v[u][e >> 1] >> (16 * (e & 1))) & 0xffff));
+      if (r2 < TOPK) sG[r2][k + e] = f * sH[k + e];
+      else sS[r2 - TOPK][k + e] = f;
+    }
   }
   __syncthreads();
-  // thread (p, c): one dot product over the rank (p = 0 only for the band's first row)
   const int p = threadIdx.x >> 4, c = threadIdx.x & 15;
-  if (i == 1 && p > 0) return;
-  // (ids are clamped: a row with fewer than 16 finite logits leaves placeholder entries)
-  const int tp = min(max(sprev[p], 0), V - 1), tc = min(max(scand[c], 0), V - 1);
-  const bf16* pr = pred + (size_t)tp * rank;
-  const bf16* sr = succ + (size_t)tc * rank;
+  if (p >= np) return;
   float acc = 0.f;
-  for (int q = 0; q < rank; q += 4) {
-    float pv[4], sv[4];
-    load4(pr + q, pv);
-    load4(sr + q, sv);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc += pv[e] * sH[q + e] * sv[e];
+#pragma unroll 8
+  for (int k = 0; k < R; k += 4) {
+    const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sG[p][k]);
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(&sS[c][k]);
+    acc += g4[0] * s4[0];
+    acc += g4[1] * s4[1];
+    acc += g4[2] * s4[2];
+    acc += g4[3] * s4[3];
   }
-  pair[((size_t)d * TOPK + p) * TOPK + c] = sel_v[(size_t)d * TOPK + c] + acc;
+  pair[((size_t)d * TOPK + p) * TOPK + c] = scv[c] + acc;
 }
 
-// One wavefront per band: the greedy walk over the pair tables, the drafts written per row.
-__global__ __launch_bounds__(64) void k_selector_walk(const int* __restrict__ sel_i, const float* __restrict__ pair,
-                                                      int gamma, int* __restrict__ tokens) {
-  const int b = blockIdx.x, lane = threadIdx.x, g1 = gamma - 1;
+// One wavefront per band: the greedy walk over the pair tables, staged in LDS first (all
+// loads issued at once, so no step waits on memory), the drafts written per row.
+__global__ __launch_bounds__(256) void k_selector_walk(const int* __restrict__ sel_i, const float* __restrict__ pair,
+                                                       int gamma, int* __restrict__ tokens) {
+  constexpr int NP4 = (MAX_GAMMA - 1) * TOPK * TOPK / 4;   // float4 pieces of the largest band
+  __shared__ f32x4 sp4[NP4];
+  __shared__ int sc[MAX_GAMMA - 1][TOPK];
+  const int b = blockIdx.x, lane = threadIdx.x & 63, g1 = gamma - 1;
+  const size_t d0 = (size_t)b * g1;
+  // every load of the staging issued before the first store (a fixed, unrolled count)
+  const f32x4* src = reinterpret_cast<const f32x4*>(pair + d0 * TOPK * TOPK);
+  const int n4 = g1 * TOPK * TOPK / 4;
+  f32x4 v[(NP4 + 255) / 256];
+#pragma unroll
+  for (int u = 0; u < (NP4 + 255) / 256; ++u) {
+    const int q = threadIdx.x + u * 256;
+    v[u] = q < n4 ? src[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int ci_ = threadIdx.x < g1 * TOPK ? sel_i[d0 * TOPK + threadIdx.x] : 0;
+#pragma unroll
+  for (int u = 0; u < (NP4 + 255) / 256; ++u) {
+    const int q = threadIdx.x + u * 256;
+    if (q < n4) sp4[q] = v[u];
+  }
+  if (threadIdx.x < g1 * TOPK) (&sc[0][0])[threadIdx.x] = ci_;
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const float* sp = reinterpret_cast<const float*>(sp4);
   int p = 0;   // position of the previous pick in the previous row's candidates (0 = the bonus row)
   for (int k = 0; k < g1; ++k) {
-    const size_t d = (size_t)b * g1 + k;
-    float v = lane < TOPK ? pair[(d * TOPK + p) * TOPK + lane] : -INFINITY;
-    int c = lane < TOPK ? lane : 0x7fffffff;
+    // the row's best candidate: the lane whose score no other candidate beats
+    const float* rowp = sp + (k * TOPK + p) * TOPK;
+    bool best = false;
+    if (lane < TOPK) {
+      const float v = rowp[lane];
+      int r = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o, 64);
-      const int oc = __shfl_xor(c, o, 64);
-      if (tk_before(ov, oc, v, c)) { v = ov; c = oc; }
+      for (int j = 0; j < TOPK; ++j) r += tk_before(rowp[j], j, v, lane) ? 1 : 0;
+      best = r == 0 && v == v;
     }
-    // (no finite score leaves c past the list: the first candidate is taken)
-    p = c < TOPK ? c : 0;
-    if (lane == 0) tokens[d] = sel_i[d * TOPK + p];
+    const unsigned long long m = __ballot(best);
+    // (no finite score at all: the first candidate is taken)
+    p = m ? __ffsll((long long)m) - 1 : 0;
+    if (lane == 0) tokens[d0 + k] = sc[k][p];
   }
 }
 
@@ -286,34 +470,35 @@ hipError_t launch_resid_dconv(float* X, const float* P, int S, long long part_st
                 base, w, ssq, Xw, Xw_lo);
 }
 
-int topk_slices(int V) { return std::max(1, std::min(TOPK_MAX_SLICES, (V + 2047) / 2048)); }
+int topk_slices(int V) { return std::max(1, std::min(TOPK_MAX_SLICES, (V + 8191) / 8192)); }
 
 hipError_t launch_topk_partial(const float* logits, int rows, int V, float* cv, int* ci, hipStream_t st) {
   if (rows < 1 || V < TOPK) return hipErrorInvalidValue;
   const int ns = topk_slices(V);
-  return launch(k_topk_partial, dim3(rows, ns), dim3(256), 0, st, logits, V, (V + ns - 1) / ns, cv, ci);
+  const int slice = ((V + ns - 1) / ns + 3) / 4 * 4;   // 4-aligned slice bounds
+  return launch(k_topk_partial, dim3(rows, ns), dim3(256), 0, st, logits, V, slice, cv, ci);
 }
 
-hipError_t launch_topk_merge(const float* cv, const int* ci, int rows, int V, float* sel_v, int* sel_i,
-                             hipStream_t st) {
-  if (rows < 1 || V < TOPK) return hipErrorInvalidValue;
-  return launch(k_topk_merge, dim3(rows), dim3(256), 0, st, cv, ci, topk_slices(V), sel_v, sel_i);
-}
-
-hipError_t launch_selector_pairs(const int* sel_i, const float* sel_v, const float* Hp, int S, long long part_stride,
-                                 int gsz, int rank, int n_bands, int gamma, const SelectorBonus& bonus,
-                                 const bf16* pred, const bf16* succ, int vocab, float* pair, hipStream_t st) {
-  if (n_bands < 1 || n_bands > MAX_BANDS || gamma < 2 || rank < 4 || rank % 4 || rank > SELECTOR_MAX_RANK ||
-      vocab < TOPK || gsz < 1)
+hipError_t launch_selector_pairs(const float* cv, const int* ci, const float* Hp, int S, long long part_stride, int gsz,
+                                 int rank, int n_bands, int gamma, const SelectorBonus& bonus, const bf16* pred,
+                                 const bf16* succ, int vocab, float* sel_v, int* sel_i, float* pair, hipStream_t st) {
+  if (n_bands < 1 || n_bands > MAX_BANDS || gamma < 2 || gamma > MAX_GAMMA || vocab < TOPK || gsz < 1)
     return hipErrorInvalidValue;
-  return launch(k_selector_pairs, dim3(n_bands * (gamma - 1)), dim3(256), 0, st, sel_i, sel_v, Hp, S, part_stride,
-                gsz, rank, gamma, vocab, bonus, pred, succ, pair);
+  const dim3 grid(n_bands * (gamma - 1)), block(256);
+  const int ns = topk_slices(vocab);
+  if (rank == 256)
+    return launch(k_selector_pairs<256>, grid, block, 0, st, cv, ci, ns, Hp, S, part_stride, gsz, gamma, vocab, bonus,
+                  pred, succ, sel_v, sel_i, pair);
+  if (rank == 512)
+    return launch(k_selector_pairs<512>, grid, block, 0, st, cv, ci, ns, Hp, S, part_stride, gsz, gamma, vocab, bonus,
+                  pred, succ, sel_v, sel_i, pair);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_selector_walk(const int* sel_i, const float* pair, int n_bands, int gamma, int* tokens,
                                 hipStream_t st) {
-  if (n_bands < 1 || n_bands > MAX_BANDS || gamma < 2) return hipErrorInvalidValue;
-  return launch(k_selector_walk, dim3(n_bands), dim3(64), 0, st, sel_i, pair, gamma, tokens);
+  if (n_bands < 1 || n_bands > MAX_BANDS || gamma < 2 || gamma > MAX_GAMMA) return hipErrorInvalidValue;
+  return launch(k_selector_walk, dim3(n_bands), dim3(256), 0, st, sel_i, pair, gamma, tokens);
 }
 
 }  // namespace dfl

@@ -236,21 +236,21 @@ hipError_t launch_dconv_prepare(const bf16* Xw, const bf16* Xw_lo, const float* 
 hipError_t launch_resid_dconv(float* X, const float* P, int S, long long part_stride, int gsz, int M, int h, int gamma,
                               const float* dyn, const bf16* base, const bf16* w, float* ssq, bf16* Xw, bf16* Xw_lo,
                               hipStream_t st);
-// top-16 candidates per drafted row: sliced partial lists (cv, ci: [rows][TOPK_MAX_SLICES][16]),
-// then merged into sel_v, sel_i [rows][16] (best first, ties to the lower index)
-constexpr int TOPK_MAX_SLICES = 64;
+// top-16 candidates per drafted row: sliced partial lists (cv, ci: [rows][slices][16], at most
+// 16 slices), merged (best first, ties to the lower index) by the selector's pair kernel
+constexpr int TOPK_MAX_SLICES = 16;
+constexpr int MAX_GAMMA = 16;
 int topk_slices(int V);
 hipError_t launch_topk_partial(const float* logits, int rows, int V, float* cv, int* ci, hipStream_t st);
-hipError_t launch_topk_merge(const float* cv, const int* ci, int rows, int V, float* sel_v, int* sel_i,
-                             hipStream_t st);
-// the candidate selector: pair scores [rows][16 prev][16 cand], then the greedy walk per band
+// the candidate selector: each drafted row's 16 candidates into sel_v, sel_i [rows][16], pair
+// scores [rows][16 prev][16 cand], then the greedy walk per band
 constexpr int SELECTOR_MAX_RANK = 512;
 struct SelectorBonus {
   int t[MAX_BANDS];
 };
-hipError_t launch_selector_pairs(const int* sel_i, const float* sel_v, const float* Hp, int S, long long part_stride,
-                                 int gsz, int rank, int n_bands, int gamma, const SelectorBonus& bonus,
-                                 const bf16* pred, const bf16* succ, int vocab, float* pair, hipStream_t st);
+hipError_t launch_selector_pairs(const float* cv, const int* ci, const float* Hp, int S, long long part_stride, int gsz,
+                                 int rank, int n_bands, int gamma, const SelectorBonus& bonus, const bf16* pred,
+                                 const bf16* succ, int vocab, float* sel_v, int* sel_i, float* pair, hipStream_t st);
 hipError_t launch_selector_walk(const int* sel_i, const float* pair, int n_bands, int gamma, int* tokens,
                                 hipStream_t st);
 

@@ -78,7 +78,7 @@ struct dflash_ctx {
   bf16* sel_h = nullptr;            // T16 copy of the hidden projection [rank, h]
   float *dyn_a = nullptr, *dyn_m = nullptr;   // [rows][h/4] dynamic taps of the two sites
   bf16 *U = nullptr, *U_lo = nullptr;         // convolved sublayer input, hi + lo
-  float* tk_v = nullptr;            // [drafted rows][TOPK_MAX_SLICES][16] partial candidates
+  float* tk_v = nullptr;            // [drafted rows][TOPK_MAX_SLICES][16] per-slice candidates
   int* tk_i = nullptr;
   float* sel_v = nullptr;           // [drafted rows][16] candidates and their logits
   int* sel_i = nullptr;
@@ -1130,12 +1130,9 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       return launch_topk_partial(logits, drafted, c->V, c->tk_v, c->tk_i, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
-      return launch_topk_merge(c->tk_v, c->tk_i, drafted, c->V, c->sel_v, c->sel_i, st);
-    }));
-    HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
-      return launch_selector_pairs(c->sel_i, c->sel_v, c->part, parts(c->g_sh).first, (long long)M * c->g_sh.N,
+      return launch_selector_pairs(c->tk_v, c->tk_i, c->part, parts(c->g_sh).first, (long long)M * c->g_sh.N,
                                    parts(c->g_sh).second, c->sel_rank, n_seqs, gamma, sb, c->sel_pred, c->sel_succ,
-                                   c->V, c->sel_pair, st);
+                                   c->V, c->sel_v, c->sel_i, c->sel_pair, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
       return launch_selector_walk(c->sel_i, c->sel_pair, n_seqs, gamma, draft_tokens, st);
