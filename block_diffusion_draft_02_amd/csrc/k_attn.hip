@@ -188,14 +188,16 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int item = (qd / nrg) * 8 + (id & 7);
   if (item >= n_items) return;
   const int nkv = g.nkv;
-  const int cg = item / nkv, kvh = item - cg * nkv;
+  const int cd = item / nkv, kvh = item - cd * nkv;
   const int G = nh / nkv;
-  int b = 0;
-  while (b + 1 < ab.n && cg >= ab.b[b + 1].base[sw]) ++b;
-  const int seq = ab.b[b].seq, C = ab.b[b].kv_len, qpos0 = ab.b[b].q_pos;
-  const int ch = cg - ab.b[b].base[sw];
-  const int k0 = ab.b[b].kstart[sw] + ch * ab.b[b].ck[sw];   // page aligned
-  const int k1 = min(k0 + ab.b[b].ck[sw], C + gamma);
+  int bl = 0;
+  while (bl + 1 < ab.n && cd >= ab.dbase[bl + 1]) ++bl;
+  const int b = ab.bi[bl];
+  const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len, qpos0 = ab.b[bl].q_pos;
+  const int ch = cd - ab.dbase[bl];
+  const size_t pitem = (size_t)(ab.b[bl].base[sw] + ch) * nkv + kvh;   // the call-wide partial slot
+  const int k0 = ab.b[bl].kstart[sw] + ch * ab.b[bl].ck[sw];   // page aligned
+  const int k1 = min(k0 + ab.b[bl].ck[sw], C + gamma);
   const int nkeys = k1 - k0;
   const int npg = (nkeys + PAGE - 1) / PAGE;
   const int R = gamma * G;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     wt[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
     L += wt[w] * sm.mg.l[w][row];
   }
-  float* po = part_o + ((size_t)item * RPAD + r) * HD + slc * DS;
+  float* po = part_o + (pitem * RPAD + r) * HD + slc * DS;
 #pragma unroll
   for (int v = 0; v < DS / 4; ++v) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -279,18 +281,259 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     *reinterpret_cast<f32x4*>(po + v * 4) = acc;
   }
   if (slc == 0) {
-    part_ml[((size_t)item * RPAD + r) * 2 + 0] = M;
-    part_ml[((size_t)item * RPAD + r) * 2 + 1] = L;
+    part_ml[(pitem * RPAD + r) * 2 + 0] = M;
+    part_ml[(pitem * RPAD + r) * 2 + 1] = L;
   }
 }
 
-hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int total_chunks,
+// ---- K/V staged through LDS (head_dim 128, layers without a window, long bands) -----------
+// One 4-wave workgroup per (chunk, kv head) with all of the item's query rows: wave w owns rows
+// 32w .. 32w + 31 (two 16-row tiles, Q hi and lo held in registers) and takes every 32-key
+// slice of the chunk in order, so the chunk's K/V leaves L2 once instead of once per row
+// group. Slices stream through a ring of three LDS slots with the gfx950 global->LDS 16-byte
+// load, which takes no registers: of a slice, wave v brings page v%2 of K (v < 2) or of V
+// (v >= 2), 1 KB an instruction, each lane choosing its source so that the LDS copy is
+// swizzled for the MFMA fragment reads (K: 16-byte unit u of row r of page p sits at unit
+// u ^ (r ^ 4p); V: half h of dim row d sits at half h ^ (d/8 % 2)). Slice j+2 is requested
+// right after the barrier that ends slice j-1, and a wave waits (vmcnt) only for its own
+// loads of slice j: one barrier per slice. A wave's state covers its rows over the whole
+// chunk, so it writes the chunk's partials itself.
+constexpr int DMA_HD = 128;
+constexpr int DMA_RING = 3;
+constexpr int DMA_MIN_CHUNK = 32 * PAGE;   // chunks of at least this many keys (bands past 8192 keys) take this path
+
+struct DmaSlice {
+  bf16 k[2][PAGE * DMA_HD];   // two K pages [16 keys][128], units swizzled within a row
+  bf16 v[2][DMA_HD * PAGE];   // two V pages [128 dims][16 keys], halves swizzled
+};
+
+// s_waitcnt with vmcnt <= N (vmcnt[3:0] | vmcnt[5:4] << 14; expcnt and lgkmcnt left at maximum)
+#define DFL_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+__device__ __forceinline__ void compute_dma(const bf16x8 (&kf)[2][4], const bf16x8 (&vf)[8], const bf16x8 (&qh)[2][4],
+                                            const bf16x8 (&ql)[2][4], bool full, int lim, float scale_log2,
+                                            float (&m_run)[2], float (&l_run)[2], f32x4 (&o)[2][8]) {
+  // S^T = K Q^T, the hi then the lo query term at every k-step (as the register kernel)
+  f32x4 sh[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sh[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(kf[t][s], qh[rt][s], sh[rt][t]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(kf[t][s], ql[rt][s], sh[rt][t]);
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float sv[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = sh[rt][e >> 2][e & 3];
+      if (!full) x = e < lim ? x : -INFINITY;
+      sv[e] = x;
+      tmax = fmaxf(tmax, x);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const bool move = tmax > m_run[rt] && (m_run[rt] == -INFINITY || (tmax - m_run[rt]) * scale_log2 > RESCALE_LOG2);
+    if (__any(move)) {
+      const float m_new = move ? tmax : m_run[rt];
+      const float alpha = (m_new == -INFINITY || m_run[rt] == m_new) ? 1.f
+                                                                     : __builtin_amdgcn_exp2f((m_run[rt] - m_new) * scale_log2);
+      l_run[rt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[rt][dt] *= alpha;
+      m_run[rt] = m_new;
+    }
+    const float bias = (m_run[rt] == -INFINITY) ? 0.f : -m_run[rt] * scale_log2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, bias));
+      l_run[rt] += sv[e];
+    }
+    const bf16x8 pb = __builtin_convertvector((f32x8){sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]}, bf16x8);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[rt][dt] = mfma16(vf[dt], pb, o[rt][dt]);
+  }
+}
+
+struct DmaLds {
+  DmaSlice ring[DMA_RING];
+  int page[ATTN_CHUNK_PAGES_MAX];
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn_dma(const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo,
+                                                        const AttnBands ab, int n_items, int gamma, int nh, KvGeom g,
+                                                        int layer, float scale_log2,
+                                                        float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int HD = DMA_HD, NS = HD / 32, ND = HD / 16, UPR = HD / 8;
+  __shared__ __attribute__((aligned(16))) DmaLds sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, grp = lane >> 4;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int nkv = g.nkv;
+  const int cd = item / nkv, kvh = item - cd * nkv;
+  const int G = nh / nkv;
+  int bl = 0;
+  while (bl + 1 < ab.n && cd >= ab.dbase[bl + 1]) ++bl;
+  const int b = ab.bi[bl];
+  const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len;
+  const int ch = cd - ab.dbase[bl];
+  const size_t pitem = (size_t)(ab.b[bl].base[0] + ch) * nkv + kvh;   // the call-wide partial slot
+  const int k0 = ab.b[bl].kstart[0] + ch * ab.b[bl].ck[0];   // page aligned
+  const int k1 = min(k0 + ab.b[bl].ck[0], C + gamma);
+  const int nkeys = k1 - k0;
+  const int npg = (nkeys + PAGE - 1) / PAGE;
+  const int R = gamma * G;
+  const bool active = wave * 32 < R;   // waves past the query rows only move K/V
+  const size_t pl = page_layer_elems(nkv, HD);
+  const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
+  const int* bt = g.bt + (size_t)seq * g.per_seq + (k0 >> 4);
+  for (int i = threadIdx.x; i < min(npg, ATTN_CHUNK_PAGES_MAX); i += 256) sm.page[i] = bt[i];
+  __syncthreads();   // the page ids
+
+  // this wave's query rows r = 32 wave + 16 rt + c (block row r % gamma of query head
+  // r / gamma of the kv head's group; rows past R are zero) as S^T operands: dims
+  // s*32 + grp*8 .. +7
+  bf16x8 qh[2][NS], ql[2][NS];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][ND];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nsl = (nkeys + 31) / 32;
+  // request slice j into ring slot d: this wave's page (K or V, page wave%2); the zeroed
+  // sentinel page 0 past the chunk; four 1 KB instructions a wave
+  auto issue = [&](DmaSlice& d, int j) {
+    const int p = wave & 1;
+    const int lp = j * 2 + p;
+    const int pgid = lp < npg ? sm.page[min(lp, ATTN_CHUNK_PAGES_MAX - 1)] : 0;
+    if ((wave & 2) == 0) {
+      const bf16* src = lpool + (size_t)pgid * pl + (size_t)kvh * PAGE * HD;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int P = q * 64 + lane;
+        const int rr = P / UPR, u = (P % UPR) ^ ((rr ^ (4 * p)) & (UPR - 1));
+        __builtin_amdgcn_global_load_lds(src + rr * HD + u * 8, &d.k[p][q * 512], 16, 0, 0);
+      }
+    } else {
+      const bf16* src = lpool + (size_t)pgid * pl + (size_t)(nkv + kvh) * HD * PAGE;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int P = q * 64 + lane;
+        const int dd = P >> 1, h = (P & 1) ^ ((dd >> 3) & 1);
+        __builtin_amdgcn_global_load_lds(src + dd * PAGE + h * 8, &d.v[p][q * 512], 16, 0, 0);
+      }
+    }
+  };
+  // one slice: this wave's loads of slice j are done once at most the next slice's four are
+  // in flight; the barrier then makes every wave's share visible and ends every wave's reads
+  // of the slot (nxt) that slice j + 2 now overwrites
+  auto step = [&](int j, const DmaSlice& sl, DmaSlice& nxt) {
+    if (j + 1 < nsl) DFL_WAIT_VM(4); else DFL_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    if (j + 2 < nsl) issue(nxt, j + 2);
+    if (!active) return;
+    bf16x8 kf[2][NS], vf[ND];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kk = (c >> 2) * 8 + t * 4 + (c & 3);
+      const int p = kk >> 4, rr = kk & 15;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int u = (4 * s + grp) ^ ((rr ^ (4 * p)) & (UPR - 1));
+        kf[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sl.k[p][rr * HD + u * 8]));
+      }
+    }
+    {
+      const int p = grp >> 1, h = grp & 1;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const int dd = dt * 16 + c;
+        const int hq = h ^ ((dd >> 3) & 1);
+        vf[dt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sl.v[p][dd * PAGE + hq * 8]));
+      }
+    }
+    const int kt = j * 32;
+    compute_dma(kf, vf, qh, ql, nkeys - kt >= 32, nkeys - kt - grp * 8, scale_log2, m_run, l_run, o);
+  };
+  // the first slice, then the wave's query rows, then the second slice, all in flight
+  // together (the compiler waits for all of them at the loop's entry)
+  issue(sm.ring[0], 0);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = wave * 32 + rt * 16 + c;
+    const size_t qo = ((size_t)(b * gamma + r % gamma) * nh + kvh * G + r / gamma) * HD + grp * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qh[rt][s] = r < R ? ld8(Q + qo + s * 32) : bf16x8{};
+      ql[rt][s] = r < R ? ld8(Q_lo + qo + s * 32) : bf16x8{};
+    }
+  }
+  if (nsl > 1) issue(sm.ring[1], 1);
+  for (int j0 = 0; j0 < nsl; j0 += DMA_RING) {
+    step(j0, sm.ring[0], sm.ring[2]);
+    if (j0 + 1 < nsl) step(j0 + 1, sm.ring[1], sm.ring[0]);
+    if (j0 + 2 < nsl) step(j0 + 2, sm.ring[2], sm.ring[1]);
+  }
+
+  // the wave's state is the chunk's partial of its rows (maximum in the exp2 domain)
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = wave * 32 + rt * 16 + c;
+    float lt = l_run[rt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (r >= R) continue;
+    float* po = part_o + (pitem * RPAD + r) * HD + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[rt][dt];
+    if (grp == 0) {
+      part_ml[(pitem * RPAD + r) * 2 + 0] = m_run[rt] * scale_log2;
+      part_ml[(pitem * RPAD + r) * 2 + 1] = lt;
+    }
+  }
+}
+
+void split_attn_bands(const Band* bands, int n, int sw, int hd, int window, AttnBands (&out)[2], int (&nch)[2]) {
+  const bool lds_ok = hd == DMA_HD && window <= 0 && sw == 0;
+  out[0].n = out[1].n = 0;
+  nch[0] = nch[1] = 0;
+  for (int b = 0; b < n; ++b) {
+    const int k = lds_ok && bands[b].ck[sw] >= DMA_MIN_CHUNK ? 1 : 0;
+    AttnBands& o = out[k];
+    o.bi[o.n] = b;
+    o.dbase[o.n] = nch[k];
+    o.b[o.n] = bands[b];
+    ++o.n;
+    nch[k] += bands[b].nch[sw];
+  }
+}
+
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int chunks, bool lds_path,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st) {
   const int G = nh / g.nkv;
   const int R = gamma * G;
-  if (R > RPAD || R < 1 || total_chunks < 1 || bands.n < 1 || bands.n > MAX_BANDS) return hipErrorInvalidValue;
-  const int n_items = total_chunks * g.nkv;
+  if (R > RPAD || R < 1 || chunks < 1 || bands.n < 1 || bands.n > MAX_BANDS) return hipErrorInvalidValue;
+  const int n_items = chunks * g.nkv;
+  if (lds_path) {
+    if (g.hd != DMA_HD || window > 0 || sw != 0) return hipErrorInvalidValue;
+    (void)launch(k_block_attn_dma, dim3(n_items), 256, 0, st, Q, Q_lo, bands, n_items, gamma, nh, g, layer,
+                 scale_log2, part_o, part_ml);
+    return hipGetLastError();
+  }
   const int nrg = (R + RG - 1) / RG;
   const dim3 grid(((n_items + 7) / 8) * 8 * nrg);
 #define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)

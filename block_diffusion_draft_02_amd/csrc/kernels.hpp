@@ -55,8 +55,11 @@ struct NormIn {
 };
 
 // the band table of one forward, passed by value to the kernels that need it at their start
+// The bands one attention launch works on: a subset of the call's bands, in call order.
 struct AttnBands {
   int n;
+  int bi[MAX_BANDS];      // the band's position in the call (its query rows)
+  int dbase[MAX_BANDS];   // its first chunk among the launch's chunks
   Band b[MAX_BANDS];
 };
 
@@ -183,8 +186,14 @@ hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz
 // A chunk (one workgroup's keys) spans at most this many pages; the runtime's chunk plan
 // keeps to it (sequences of at most 16 * 16384 keys).
 constexpr int ATTN_CHUNK_PAGES_MAX = 512;
-// total_chunks = sum over bands of nch[sw]; partial buffers sized [total_chunks*nkv][128][hd]
-hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int total_chunks,
+// The attention of one layer runs as up to two launches, split by a property of each band
+// alone (so a band's arithmetic never depends on the other bands of the call): bands whose
+// chunks span more than 256 keys (bands of more than 8192 keys) on a head_dim-128 layer
+// without a window stream K/V through LDS (out[1]); the rest load K/V straight into
+// registers (out[0]). nch[k] = the chunks of out[k]. Partials stay indexed by the call-wide
+// chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
+void split_attn_bands(const Band* bands, int n, int sw, int hd, int window, AttnBands (&out)[2], int (&nch)[2]);
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int chunks, bool lds_path,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st);
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,

@@ -972,9 +972,11 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   hipStream_t st = (hipStream_t)stream;
   const KvGeom g = geom(c);
   const int M = n_seqs * gamma;
-  AttnBands ab{};
-  ab.n = n_seqs;
-  for (int b = 0; b < n_seqs; ++b) ab.b[b] = a.bands[b];
+  // the attention launches of full and of sliding-window layers
+  AttnBands ab[2][2];
+  int ab_nch[2][2];
+  for (int sw = 0; sw < 2; ++sw)
+    split_attn_bands(a.bands, n_seqs, sw, c->hd, sw ? c->window : 0, ab[sw], ab_nch[sw]);
   const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
   HIPCHK(c, timed(c, DFLASH_K_PROLOGUE, st, [&] {
     return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed, c->layers[0].in_norm, c->h,
@@ -1035,10 +1037,12 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
                              (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
     }));
-    HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
-      return launch_block_attn(c->Qb, c->Qb_lo, ab, base[sw], gamma, c->nh, g, l, sw,
-                               sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
-    }));
+    for (int k = 0; k < 2; ++k)
+      if (ab_nch[sw][k] > 0)
+        HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
+          return launch_block_attn(c->Qb, c->Qb_lo, ab[sw][k], ab_nch[sw][k], k == 1, gamma, c->nh, g, l, sw,
+                                   sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
+        }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN_COMBINE, st, [&] {
       return launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
