@@ -169,20 +169,29 @@ __device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const At
   }
 }
 
+
+// the band of a path's chunk cd: the last band of that path whose first chunk is <= cd
+__device__ __forceinline__ int attn_band(const AttnBands& ab, int cd, bool lds) {
+  int bl = 0;
+  for (int b = 0; b < ab.n; ++b)
+    if ((((ab.lds_mask >> b) & 1u) != 0) == lds && cd >= ab.dbase[b]) bl = b;
+  return bl;
+}
+
+// the register path's workgroup `id` (ids counted from the first register-path workgroup)
 template <int HD, bool WIN>
-__global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn(
-    const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo, const AttnBands ab, int n_items, int nrg,
-    int gamma, int nh, KvGeom g, int layer, int sw, int window, float scale_log2,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+__device__ __forceinline__ void attn_reg_wg(AttnLds<HD>& sm, int id, const bf16* __restrict__ Q,
+                                            const bf16* __restrict__ Q_lo, const AttnBands& ab, int n_items,
+                                            int nrg, int gamma, int nh, const KvGeom& g, int layer, int sw,
+                                            int window, float scale_log2, float* __restrict__ part_o,
+                                            float* __restrict__ part_ml) {
   constexpr int ND = HD / 16;
-  __shared__ __attribute__((aligned(16))) AttnLds<HD> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, grp = lane >> 4;
   // Workgroups are handed to the eight XCDs round robin, so ids 8 apart share an XCD and its
   // L2: the row groups of one (chunk, kv head) item get ids 8 apart and read its K/V from
   // HBM once.
-  const int id = blockIdx.x;
   const int qd = id >> 3;
   const int rg = qd % nrg;
   const int item = (qd / nrg) * 8 + (id & 7);
@@ -190,9 +199,7 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int nkv = g.nkv;
   const int cd = item / nkv, kvh = item - cd * nkv;
   const int G = nh / nkv;
-  int bl = 0;
-  while (bl + 1 < ab.n && cd >= ab.dbase[bl + 1]) ++bl;
-  const int b = ab.bi[bl];
+  const int bl = attn_band(ab, cd, false), b = bl;
   const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len, qpos0 = ab.b[bl].q_pos;
   const int ch = cd - ab.dbase[bl];
   const size_t pitem = (size_t)(ab.b[bl].base[sw] + ch) * nkv + kvh;   // the call-wide partial slot
@@ -370,23 +377,19 @@ struct DmaLds {
   int page[ATTN_CHUNK_PAGES_MAX];
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn_dma(const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo,
-                                                        const AttnBands ab, int n_items, int gamma, int nh, KvGeom g,
-                                                        int layer, float scale_log2,
-                                                        float* __restrict__ part_o, float* __restrict__ part_ml) {
+// the LDS path's workgroup `item` (one per (chunk, kv head) of the LDS-path bands)
+__device__ __forceinline__ void attn_lds_wg(DmaLds& sm, int item, const bf16* __restrict__ Q,
+                                            const bf16* __restrict__ Q_lo, const AttnBands& ab, int gamma, int nh,
+                                            const KvGeom& g, int layer, float scale_log2,
+                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int HD = DMA_HD, NS = HD / 32, ND = HD / 16, UPR = HD / 8;
-  __shared__ __attribute__((aligned(16))) DmaLds sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, grp = lane >> 4;
-  const int item = blockIdx.x;
-  if (item >= n_items) return;
   const int nkv = g.nkv;
   const int cd = item / nkv, kvh = item - cd * nkv;
   const int G = nh / nkv;
-  int bl = 0;
-  while (bl + 1 < ab.n && cd >= ab.dbase[bl + 1]) ++bl;
-  const int b = ab.bi[bl];
+  const int bl = attn_band(ab, cd, true), b = bl;
   const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len;
   const int ch = cd - ab.dbase[bl];
   const size_t pitem = (size_t)(ab.b[bl].base[0] + ch) * nkv + kvh;   // the call-wide partial slot
@@ -506,37 +509,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
-void split_attn_bands(const Band* bands, int n, int sw, int hd, int window, AttnBands (&out)[2], int (&nch)[2]) {
-  const bool lds_ok = hd == DMA_HD && window <= 0 && sw == 0;
-  out[0].n = out[1].n = 0;
-  nch[0] = nch[1] = 0;
+// One launch per layer: the LDS-path workgroups first (their chunks are the long ones), then
+// the register path's. The LDS holds either path's layout.
+template <int HD, bool WIN>
+struct AttnShm {
+  AttnLds<HD> r;
+};
+template <>
+struct AttnShm<DMA_HD, false> {
+  union {
+    AttnLds<DMA_HD> r;
+    DmaLds d;
+  };
+};
+
+template <int HD, bool WIN>
+__global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_block_attn(
+    const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo, const AttnBands ab, int n_lds_items, int n_items,
+    int nrg, int gamma, int nh, KvGeom g, int layer, int sw, int window, float scale_log2,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) AttnShm<HD, WIN> sm;
+  const int id = blockIdx.x;
+  if constexpr (HD == DMA_HD && !WIN) {
+    if (id < n_lds_items) {
+      attn_lds_wg(sm.d, id, Q, Q_lo, ab, gamma, nh, g, layer, scale_log2, part_o, part_ml);
+      return;
+    }
+  }
+  attn_reg_wg<HD, WIN>(sm.r, id - n_lds_items, Q, Q_lo, ab, n_items, nrg, gamma, nh, g, layer, sw, window,
+                       scale_log2, part_o, part_ml);
+}
+
+
+void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, AttnBands& out,
+               int& reg_chunks, int& lds_chunks) {
+  const bool lds_ok = lds_path && hd == DMA_HD && window <= 0 && sw == 0;
+  out.n = n;
+  out.lds_mask = 0u;
+  reg_chunks = lds_chunks = 0;
   for (int b = 0; b < n; ++b) {
-    const int k = lds_ok && bands[b].ck[sw] >= DMA_MIN_CHUNK ? 1 : 0;
-    AttnBands& o = out[k];
-    o.bi[o.n] = b;
-    o.dbase[o.n] = nch[k];
-    o.b[o.n] = bands[b];
-    ++o.n;
-    nch[k] += bands[b].nch[sw];
+    const bool lds = lds_ok && bands[b].ck[sw] >= DMA_MIN_CHUNK;
+    int& nch = lds ? lds_chunks : reg_chunks;
+    if (lds) out.lds_mask |= 1u << b;
+    out.dbase[b] = nch;
+    out.b[b] = bands[b];
+    nch += bands[b].nch[sw];
   }
 }
 
-hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int chunks, bool lds_path,
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int reg_chunks, int lds_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st) {
   const int G = nh / g.nkv;
   const int R = gamma * G;
-  if (R > RPAD || R < 1 || chunks < 1 || bands.n < 1 || bands.n > MAX_BANDS) return hipErrorInvalidValue;
-  const int n_items = chunks * g.nkv;
-  if (lds_path) {
-    if (g.hd != DMA_HD || window > 0 || sw != 0) return hipErrorInvalidValue;
-    (void)launch(k_block_attn_dma, dim3(n_items), 256, 0, st, Q, Q_lo, bands, n_items, gamma, nh, g, layer,
-                 scale_log2, part_o, part_ml);
-    return hipGetLastError();
-  }
+  if (R > RPAD || R < 1 || reg_chunks < 0 || lds_chunks < 0 || reg_chunks + lds_chunks < 1 || bands.n < 1 ||
+      bands.n > MAX_BANDS)
+    return hipErrorInvalidValue;
+  if (lds_chunks > 0 && (g.hd != DMA_HD || window > 0 || sw != 0)) return hipErrorInvalidValue;
+  const int n_items = reg_chunks * g.nkv, n_lds = lds_chunks * g.nkv;
   const int nrg = (R + RG - 1) / RG;
-  const dim3 grid(((n_items + 7) / 8) * 8 * nrg);
-#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
+  const dim3 grid(n_lds + ((n_items + 7) / 8) * 8 * nrg);
+#define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands, n_lds, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
   const bool win = window > 0;
   switch (g.hd) {
     case 128: if (win) DFL_ATTN(128, true); else DFL_ATTN(128, false); break;

@@ -55,11 +55,11 @@ struct NormIn {
 };
 
 // the band table of one forward, passed by value to the kernels that need it at their start
-// The bands one attention launch works on: a subset of the call's bands, in call order.
+// The bands of an attention launch (the call's bands, in call order) and the path each takes.
 struct AttnBands {
   int n;
-  int bi[MAX_BANDS];      // the band's position in the call (its query rows)
-  int dbase[MAX_BANDS];   // its first chunk among the launch's chunks
+  unsigned lds_mask;      // bit b: band b stages its K/V through LDS
+  int dbase[MAX_BANDS];   // the band's first chunk among its path's chunks
   Band b[MAX_BANDS];
 };
 
@@ -186,14 +186,16 @@ hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz
 // A chunk (one workgroup's keys) spans at most this many pages; the runtime's chunk plan
 // keeps to it (sequences of at most 16 * 16384 keys).
 constexpr int ATTN_CHUNK_PAGES_MAX = 512;
-// The attention of one layer runs as up to two launches, split by a property of each band
-// alone (so a band's arithmetic never depends on the other bands of the call): bands whose
-// chunks span more than 256 keys (bands of more than 8192 keys) on a head_dim-128 layer
-// without a window stream K/V through LDS (out[1]); the rest load K/V straight into
-// registers (out[0]). nch[k] = the chunks of out[k]. Partials stay indexed by the call-wide
-// chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
-void split_attn_bands(const Band* bands, int n, int sw, int hd, int window, AttnBands (&out)[2], int (&nch)[2]);
-hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int chunks, bool lds_path,
+// The attention of one layer is one launch whose bands take one of two paths, chosen by a
+// property of each band alone (so a band's arithmetic never depends on the other bands of
+// the call): with the LDS path enabled (a property of the drafter, fixed at create), bands
+// whose chunks span more than 256 keys (bands of more than 8192 keys) on a head_dim-128
+// layer without a window stream K/V through LDS; the rest load K/V straight into registers.
+// plan_attn fills the table and counts each path's chunks; partials stay indexed by the
+// call-wide chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
+void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, AttnBands& out,
+               int& reg_chunks, int& lds_chunks);
+hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int reg_chunks, int lds_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st);
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,

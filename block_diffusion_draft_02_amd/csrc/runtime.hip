@@ -72,6 +72,10 @@ struct dflash_ctx {
   unsigned long long* mk_best = nullptr;   // [MARKOV_MAX_ROWS][MAX_BANDS] argmax keys, zero between forwards
   int mk_groups = 1;
   // DFlash2 (selector_rank > 0): convs, top-16 candidates and the selector
+  // long bands stream attention K/V through LDS (drafters made for 8 or more sequences: one
+  // long band alone fills the chip better with the register path, a crowd of them reads
+  // less from L2 with this one; fixed at create, so no call's bands change another's bits)
+  bool attn_lds = false;
   bool d2 = false;
   int sel_rank = 0;
   const bf16 *sel_pred = nullptr, *sel_succ = nullptr;
@@ -457,6 +461,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->hd = cfg->head_dim; c->qd = c->nh * c->hd; c->kvd = c->nkv * c->hd; c->ff = cfg->intermediate;
   c->V = cfg->vocab; c->T = cfg->num_taps; c->Ht = cfg->target_hidden; c->gmax = cfg->gamma_max;
   c->mask = cfg->mask_token_id; c->max_seq = cfg->max_seq_len; c->max_batch = cfg->max_batch;
+  c->attn_lds = cfg->max_batch >= 8;
   c->fp8 = cfg->weight_format == DFLASH_WEIGHTS_FP8_E4M3;
   c->R = cfg->markov_rank;
   c->mk_w1 = (const bf16*)w->markov_w1;
@@ -973,10 +978,10 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   const KvGeom g = geom(c);
   const int M = n_seqs * gamma;
   // the attention launches of full and of sliding-window layers
-  AttnBands ab[2][2];
-  int ab_nch[2][2];
+  AttnBands ab[2];
+  int ab_reg[2], ab_lds[2];
   for (int sw = 0; sw < 2; ++sw)
-    split_attn_bands(a.bands, n_seqs, sw, c->hd, sw ? c->window : 0, ab[sw], ab_nch[sw]);
+    plan_attn(a.bands, n_seqs, sw, c->hd, sw ? c->window : 0, c->attn_lds, ab[sw], ab_reg[sw], ab_lds[sw]);
   const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
   HIPCHK(c, timed(c, DFLASH_K_PROLOGUE, st, [&] {
     return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed, c->layers[0].in_norm, c->h,
@@ -1037,12 +1042,10 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
                              (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
     }));
-    for (int k = 0; k < 2; ++k)
-      if (ab_nch[sw][k] > 0)
-        HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
-          return launch_block_attn(c->Qb, c->Qb_lo, ab[sw][k], ab_nch[sw][k], k == 1, gamma, c->nh, g, l, sw,
-                                   sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
-        }));
+    HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
+      return launch_block_attn(c->Qb, c->Qb_lo, ab[sw], ab_reg[sw], ab_lds[sw], gamma, c->nh, g, l, sw,
+                               sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
+    }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN_COMBINE, st, [&] {
       return launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);

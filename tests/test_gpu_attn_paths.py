@@ -1,11 +1,11 @@
-"""GPU parity of the two attention paths in one call: on a head_dim-128 layer without a window,
-a band whose chunks span 32 pages or more (a band of more than 8192 keys) streams its K/V
-through LDS, every other band loads K/V straight into registers; windowed layers always take
-the register path. A small head_dim-128 drafter (2 layers, hidden 512, 16:2 heads) with bands
-on both sides of 8192 keys, last chunks of 1 and of 30 keys, a windowed layer next to a full
-one, and block widths that leave query-row waves idle (gamma 2, 9, 16): logits against the
-oracle to the bf16 parity bar, and every band of the mixed call bit for bit equal to the
-same band alone."""
+"""GPU parity of the two attention paths in one call: in a drafter made for 8 or more
+sequences, on a head_dim-128 layer without a window, a band whose chunks span 32 pages or
+more (a band of more than 8192 keys) streams its K/V through LDS, every other band loads K/V
+straight into registers; windowed layers always take the register path. A small
+head_dim-128 drafter (2 layers, hidden 512, 16:2 heads) with bands on both sides of 8192
+keys, last chunks of 1 and of 30 keys, a windowed layer next to a full one, and block widths
+that leave query-row waves idle (gamma 2, 9, 16): logits against the oracle to the bf16
+parity bar, and every band of the mixed call bit for bit equal to the same band alone."""
 import numpy as np
 import pytest
 import torch
@@ -36,8 +36,9 @@ def test_mixed_paths_parity_and_band_invariance(window):
     m = _model(window)
     W = synth.gen_weights(m, SEED)
     nb = len(LENS)
-    pair = Pair(m, W, max(LENS) + 64, nb,
-                page_order=synth.gen_page_order(O.pool_pages(max(LENS) + 64, 16, nb)[1] - 1, SEED))
+    # made for 8 sequences: the LDS path is on
+    pair = Pair(m, W, max(LENS) + 64, 8,
+                page_order=synth.gen_page_order(O.pool_pages(max(LENS) + 64, 16, 8)[1] - 1, SEED))
     for s, n in enumerate(LENS):
         pair.append(s, synth.gen_hidden(m, SEED, n, 70 + s))
     agree = Agreement()
