@@ -17,6 +17,8 @@
 //                 registers and V^T is one 16-byte load because V pages are stored [d][16]
 // The four states are merged in wave order through LDS into one (max, sum, unnormalised O)
 // partial per row and chunk; k_attn_combine merges the chunks of a band.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -170,11 +172,11 @@ __device__ __forceinline__ void compute_slice(const Slice<HD, WIN>& sl, const At
 }
 
 
-// the band of a path's chunk cd: the last band of that path whose first chunk is <= cd
-__device__ __forceinline__ int attn_band(const AttnBands& ab, int cd, bool lds) {
+// the band of a path's chunk cd: the band of that path whose chunks cover cd
+__device__ __forceinline__ int attn_band(const AttnBands& ab, int cd, bool lds, int sw) {
   int bl = 0;
   for (int b = 0; b < ab.n; ++b)
-    if ((((ab.lds_mask >> b) & 1u) != 0) == lds && cd >= ab.dbase[b]) bl = b;
+    if ((((ab.lds_mask >> b) & 1u) != 0) == lds && cd >= ab.dbase[b] && cd < ab.dbase[b] + ab.b[b].nch[sw]) bl = b;
   return bl;
 }
 
@@ -199,7 +201,7 @@ __device__ __forceinline__ void attn_reg_wg(AttnLds<HD>& sm, int id, const bf16*
   const int nkv = g.nkv;
   const int cd = item / nkv, kvh = item - cd * nkv;
   const int G = nh / nkv;
-  const int bl = attn_band(ab, cd, false), b = bl;
+  const int bl = attn_band(ab, cd, false, sw), b = bl;
   const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len, qpos0 = ab.b[bl].q_pos;
   const int ch = cd - ab.dbase[bl];
   const size_t pitem = (size_t)(ab.b[bl].base[sw] + ch) * nkv + kvh;   // the call-wide partial slot
@@ -389,7 +391,7 @@ __device__ __forceinline__ void attn_lds_wg(DmaLds& sm, int item, const bf16* __
   const int nkv = g.nkv;
   const int cd = item / nkv, kvh = item - cd * nkv;
   const int G = nh / nkv;
-  const int bl = attn_band(ab, cd, true), b = bl;
+  const int bl = attn_band(ab, cd, true, 0), b = bl;
   const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len;
   const int ch = cd - ab.dbase[bl];
   const size_t pitem = (size_t)(ab.b[bl].base[0] + ch) * nkv + kvh;   // the call-wide partial slot
@@ -547,12 +549,19 @@ void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_pa
   out.n = n;
   out.lds_mask = 0u;
   reg_chunks = lds_chunks = 0;
+  int order[MAX_BANDS];
   for (int b = 0; b < n; ++b) {
-    const bool lds = lds_ok && bands[b].ck[sw] >= DMA_MIN_CHUNK;
-    int& nch = lds ? lds_chunks : reg_chunks;
-    if (lds) out.lds_mask |= 1u << b;
-    out.dbase[b] = nch;
     out.b[b] = bands[b];
+    if (lds_ok && bands[b].ck[sw] >= DMA_MIN_CHUNK) out.lds_mask |= 1u << b;
+    order[b] = b;
+  }
+  // each path's chunks are numbered band by band, the bands with the longest chunks first, so
+  // the longest workgroups start first (the dispatch order only; no band's sums change)
+  std::stable_sort(order, order + n, [&](int x, int y) { return bands[x].ck[sw] > bands[y].ck[sw]; });
+  for (int i = 0; i < n; ++i) {
+    const int b = order[i];
+    int& nch = (out.lds_mask >> b) & 1u ? lds_chunks : reg_chunks;
+    out.dbase[b] = nch;
     nch += bands[b].nch[sw];
   }
 }

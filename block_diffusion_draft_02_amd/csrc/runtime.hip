@@ -191,25 +191,29 @@ GemmPlan plan_gemm(int N, int K) {
   return GemmPlan{N, K, klen, S, gsz};
 }
 
-int chunk_pages(int pages) {
+int chunk_pages(int pages, bool lds) {
   // (pages <= 16384 by the config check, so a chunk never exceeds ATTN_CHUNK_PAGES_MAX)
   // 16 pages (256 keys: two passes of the attention workgroup's four 32-key wave slices) per
   // chunk, widened in steps of 16 pages so that a band never has more than 32 chunks: a
   // 4K-key band keeps every workgroup of a layer resident at once, long bands keep the
-  // partial traffic and the merge bounded
+  // partial traffic and the merge bounded. Bands past 512 pages on the attention's LDS path
+  // (one workgroup per chunk and kv head, not four) take at most 16 chunks, as long as a
+  // chunk's page ids fit the workgroup's table: half the partials and merge work
+  if (lds && pages > 512) return std::min(ATTN_CHUNK_PAGES_MAX, 16 * ((pages + 255) / 256));
   return 16 * std::max(1, (pages + 511) / 512);
 }
 
-void plan_chunks(int kstart, int kend, int& ck, int& nch) {
+void plan_chunks(int kstart, int kend, bool lds, int& ck, int& nch) {
   const int pages = (kend - kstart + PAGE - 1) / PAGE;
-  const int ckp = chunk_pages(pages);
+  const int ckp = chunk_pages(pages, lds);
   nch = (pages + ckp - 1) / ckp;
   ck = ckp * PAGE;
 }
 
 int max_chunks(int pages_max) {
   int m = 1;
-  for (int p = 1; p <= pages_max; ++p) m = std::max(m, (p + chunk_pages(p) - 1) / chunk_pages(p));
+  // (the LDS path's plan never has more chunks than the register path's)
+  for (int p = 1; p <= pages_max; ++p) m = std::max(m, (p + chunk_pages(p, false) - 1) / chunk_pages(p, false));
   return m;
 }
 
@@ -969,7 +973,9 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     }
     for (int sw = 0; sw < 2; ++sw) {
       B.kstart[sw] = sw == 0 ? 0 : (klo / PAGE) * PAGE;
-      plan_chunks(B.kstart[sw], kend, B.ck[sw], B.nch[sw]);
+      // full layers of a drafter with the LDS path may plan for it (the path itself is chosen
+      // from the plan: chunks of 32 pages or more)
+      plan_chunks(B.kstart[sw], kend, c->attn_lds && c->hd == 128 && sw == 0, B.ck[sw], B.nch[sw]);
       B.base[sw] = base[sw];
       base[sw] += B.nch[sw];
     }

@@ -1,9 +1,10 @@
 """GPU parity of the two attention paths in one call: in a drafter made for 8 or more
 sequences, on a head_dim-128 layer without a window, a band whose chunks span 32 pages or
-more (a band of more than 8192 keys) streams its K/V through LDS, every other band loads K/V
-straight into registers; windowed layers always take the register path. A small
-head_dim-128 drafter (2 layers, hidden 512, 16:2 heads) with bands on both sides of 8192
-keys, last chunks of 1 and of 30 keys, a windowed layer next to a full one, and block widths
+more (a band of more than 8192 keys, planned in at most 16 chunks) streams its K/V through
+LDS, every other band loads K/V straight into registers; windowed layers always take the
+register path. A small head_dim-128 drafter (2 layers, hidden 512, 16:2 heads) with bands on
+both sides of 8192 keys, two LDS chunk widths, last chunks of 1 and of 30 keys, a windowed
+layer next to a full one, and block widths
 that leave query-row waves idle (gamma 2, 9, 16): logits against the oracle to the bf16
 parity bar, and every band of the mixed call bit for bit equal to the same band alone."""
 import numpy as np
@@ -17,9 +18,10 @@ from gpu_util import Agreement, Pair, DEV
 pytestmark = pytest.mark.gpu
 
 SEED = 1501
-# C + 16 keys: 8193 (17 chunks of 512, the last holding 1 key), 8192 (the register path's
-# largest band: 32 chunks of 256), 9246 (the last chunk 30 keys), 316, 12016
-LENS = [8177, 8176, 9230, 300, 12000]
+# C + 16 keys: 8449 (LDS path, 12 chunks of 768 keys, the last holding 1 key), 8192 (the
+# register path's largest band: 32 chunks of 256), 9246 (LDS path, 13 chunks of 768, the last
+# 30 keys), 316, 14016 (LDS path, 14 chunks of 1024: the longest chunks, dispatched first)
+LENS = [8433, 8176, 9230, 300, 14000]
 
 
 def _model(window):
