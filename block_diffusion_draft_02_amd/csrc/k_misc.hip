@@ -330,66 +330,105 @@ hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int
   return hipGetLastError();
 }
 
-// one wavefront per (row, layer, K|V, kv head) of the fused [K0 | V0 | K1 | V1 | ...] output
-template <int HD>
-__global__ __launch_bounds__(64) void k_kv_append_post(const float* __restrict__ KV, int S,
-                                                       long long ps, int gsz, int L,
-                                                       const bf16* __restrict__ kn_all, float eps,
-                                                       const double* __restrict__ inv_freq,
-                                                       float mscale,
-                                                       const long long* __restrict__ slots,
-                                                       const int* __restrict__ rowpos, KvGeom g) {
+// one workgroup per (16 rows, layer, K|V, KH kv heads) of the fused [K0 | V0 | K1 | V1 | ...]
+// output (16 waves), every load of the workgroup issued before any is used (KH = 4 for long
+// appends; 1 for short ones, which need the workgroups more). K: a wave per row (sum of the
+// split partials, k-norm over the head, RoPE with the row's angles taken once for its KH
+// heads), written along the page's [key][d] rows. V: the rows staged in LDS, then written
+// along the page's [d][key] rows, consecutive threads on consecutive keys of one dim.
+template <int HD, int KH>
+__global__ __launch_bounds__(1024) void k_kv_append_post(const float* __restrict__ KV, int S,
+                                                         long long ps, int gsz, int n, int L,
+                                                         const bf16* __restrict__ kn_all, float eps,
+                                                         const double* __restrict__ inv_freq, float mscale,
+                                                         const long long* __restrict__ slots,
+                                                         const int* __restrict__ rowpos, KvGeom g) {
   constexpr int H2 = HD / 2;
-  const int r = blockIdx.x, idx = blockIdx.y, l = threadIdx.x;
-  const int nkv = g.nkv;
-  const int layer = idx / (2 * nkv), rem = idx % (2 * nkv);
-  const int kv = rem / nkv, kvh = rem % nkv;
-  const bool act = l < H2;
+  __shared__ float vt[KH][16][HD + 1];
+  const int r0 = blockIdx.x * 16;
+  const int nkv = g.nkv, nq = (nkv + KH - 1) / KH;
+  const int layer = blockIdx.y / (2 * nq), rem = blockIdx.y % (2 * nq);
+  const int kv = rem / nq, h0 = (rem % nq) * KH;
+  const int nhh = min(KH, nkv - h0);
+  const int nr = min(16, n - r0);
   const size_t ld = (size_t)L * 2 * nkv * HD;
-  const float* src = KV + (size_t)r * ld + (size_t)idx * HD;
-  float x1 = act ? sum_splits<8, float>(src + l, S, ps, gsz) : 0.f;
-  float x2 = act ? sum_splits<8, float>(src + l + H2, S, ps, gsz) : 0.f;
+  const size_t col0 = ((size_t)(layer * 2 + kv) * nkv + h0) * HD;   // head h0's first column
+  const size_t pl = page_layer_elems(nkv, HD);
   if (kv == 0) {
-    const float ss = wave_sum(x1 * x1 + x2 * x2);
-    const float rs = rsqrtf(ss / (float)HD + eps);
-    if (act) {
-      const bf16* w = kn_all + (size_t)layer * HD;
-      x1 *= rs * bf2f(w[l]);
-      x2 *= rs * bf2f(w[l + H2]);
-      rope_pair(x1, x2, rowpos[r], inv_freq[l]);
-      x1 *= mscale;
-      x2 *= mscale;
+    const int i = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const bool act = l < H2;
+    if (i >= nr) return;
+    const int r = r0 + i;
+    const float* src = KV + (size_t)r * ld + col0;
+    float x1[KH], x2[KH];
+#pragma unroll
+    for (int h = 0; h < KH; ++h) {
+      const bool on = act && h < nhh;
+      x1[h] = on ? sum_splits<8, float>(src + h * HD + l, S, ps, gsz) : 0.f;
+      x2[h] = on ? sum_splits<8, float>(src + h * HD + l + H2, S, ps, gsz) : 0.f;
     }
+    // the pair's angle in double precision (positions reach tens of thousands)
+    float cf = 0.f, sf = 0.f;
+    if (act) {
+      double sn, cn;
+      sincos((double)rowpos[r] * inv_freq[l], &sn, &cn);
+      cf = (float)cn;
+      sf = (float)sn;
+    }
+    const long long slot = slots[r];
+    bf16* kpg = g.pool + ((size_t)layer * g.num_pages + (slot >> 4)) * pl + (int)(slot & (PAGE - 1)) * HD;
+    const bf16* wn = kn_all + (size_t)layer * HD;
+    const float w1 = act ? bf2f(wn[l]) : 0.f, w2 = act ? bf2f(wn[l + H2]) : 0.f;
+#pragma unroll
+    for (int h = 0; h < KH; ++h) {
+      if (h >= nhh) break;
+      const float ss = wave_sum(x1[h] * x1[h] + x2[h] * x2[h]);
+      const float rs = rsqrtf(ss / (float)HD + eps);
+      if (!act) continue;
+      const float a = x1[h] * (rs * w1), b = x2[h] * (rs * w2);
+      const float y1 = a * cf - b * sf;
+      const float y2 = b * cf + a * sf;
+      bf16* k = kpg + (size_t)(h0 + h) * PAGE * HD;
+      k[l] = f2bf(y1 * mscale);
+      k[l + H2] = f2bf(y2 * mscale);
+    }
+    return;
   }
-  if (!act) return;
-  const long long slot = slots[r];
-  const long long page = slot >> 4;
-  const int off = (int)(slot & (PAGE - 1));
-  bf16* pg = g.pool + ((size_t)layer * g.num_pages + page) * page_layer_elems(nkv, HD);
-  if (kv == 0) {
-    bf16* k = pg + ((size_t)kvh * PAGE + off) * HD;
-    k[l] = f2bf(x1);
-    k[l + H2] = f2bf(x2);
-  } else {
-    bf16* v = pg + (size_t)(nkv + kvh) * HD * PAGE + off;
-    v[(size_t)l * PAGE] = f2bf(x1);
-    v[(size_t)(l + H2) * PAGE] = f2bf(x2);
+  constexpr int NE = KH * 16 * HD;
+  for (int e = threadIdx.x; e < NE; e += 1024) {
+    const int h = e / (16 * HD), i = (e / HD) % 16, d = e % HD;
+    vt[h][i][d] = h < nhh && i < nr
+                      ? sum_splits<8, float>(KV + (size_t)(r0 + i) * ld + col0 + (size_t)h * HD + d, S, ps, gsz)
+                      : 0.f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < NE; e += 1024) {
+    const int h = e / (16 * HD), d = (e / 16) % HD, i = e % 16;
+    if (h >= nhh || i >= nr) continue;
+    const long long slot = slots[r0 + i];
+    bf16* v = g.pool + ((size_t)layer * g.num_pages + (slot >> 4)) * pl + (size_t)(nkv + h0 + h) * HD * PAGE +
+              (size_t)d * PAGE + (int)(slot & (PAGE - 1));
+    *v = f2bf(vt[h][i][d]);
   }
 }
 
 hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int gsz, int n, int L,
-                                 const bf16* k_norm_all,
-                                 float eps, const double* inv_freq, float mscale,
-                                 const long long* slots, const int* rowpos, KvGeom g,
-                                 hipStream_t st) {
+                                 const bf16* k_norm_all, float eps, const double* inv_freq, float mscale,
+                                 const long long* slots, const int* rowpos, KvGeom g, hipStream_t st) {
   if (gsz < 1) return hipErrorInvalidValue;
-  dim3 grid(n, L * 2 * g.nkv);
+  if (n < 1) return hipErrorInvalidValue;
+  // four kv heads a workgroup once a launch has enough rows to fill the chip without them
+  const bool wide = n >= 256;
+  const int kh = wide ? 4 : 1;
+  dim3 grid((n + 15) / 16, L * 2 * ((g.nkv + kh - 1) / kh));
+#define DFL_POST(HDV, KHV) (void)launch(k_kv_append_post<HDV, KHV>, grid, 1024, 0, st, KV, S, part_stride, gsz, n, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g)
   switch (g.hd) {
-    case 32: (void)launch(k_kv_append_post<32>, grid, 64, 0, st, KV, S, part_stride, gsz, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
-    case 64: (void)launch(k_kv_append_post<64>, grid, 64, 0, st, KV, S, part_stride, gsz, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
-    case 128: (void)launch(k_kv_append_post<128>, grid, 64, 0, st, KV, S, part_stride, gsz, L, k_norm_all, eps, inv_freq, mscale, slots, rowpos, g); break;
+    case 32: if (wide) DFL_POST(32, 4); else DFL_POST(32, 1); break;
+    case 64: if (wide) DFL_POST(64, 4); else DFL_POST(64, 1); break;
+    case 128: if (wide) DFL_POST(128, 4); else DFL_POST(128, 1); break;
     default: return hipErrorInvalidValue;
   }
+#undef DFL_POST
   return hipGetLastError();
 }
 

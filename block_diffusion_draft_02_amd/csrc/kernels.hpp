@@ -212,10 +212,8 @@ hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long lon
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st);
 hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int gsz, int n, int L,
-                                 const bf16* k_norm_all,
-                                 float eps, const double* inv_freq, float mscale,
-                                 const long long* slots, const int* rowpos, KvGeom g,
-                                 hipStream_t st);
+                                 const bf16* k_norm_all, float eps, const double* inv_freq, float mscale,
+                                 const long long* slots, const int* rowpos, KvGeom g, hipStream_t st);
 
 // ---- DSpark Markov chain (k_markov.hip) -----------------------------------------------
 // One drafted row k of every band: logits[b*(gamma-1)+k][:] += W2 @ W1[t], t = bonus[b] for
