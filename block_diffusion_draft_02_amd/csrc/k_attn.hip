@@ -309,7 +309,6 @@ __device__ __forceinline__ void attn_reg_wg(AttnLds<HD>& sm, int id, const bf16*
 // chunk, so it writes the chunk's partials itself.
 constexpr int DMA_HD = 128;
 constexpr int DMA_RING = 3;
-constexpr int DMA_MIN_CHUNK = 32 * PAGE;   // chunks of at least this many keys (bands past 8192 keys) take this path
 
 struct DmaSlice {
   bf16 k[2][PAGE * DMA_HD];   // two K pages [16 keys][128], units swizzled within a row
@@ -543,7 +542,7 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 
-void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, AttnBands& out,
+void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, int gamma, AttnBands& out,
                int& reg_chunks, int& lds_chunks) {
   const bool lds_ok = lds_path && hd == DMA_HD && window <= 0 && sw == 0;
   out.n = n;
@@ -552,7 +551,8 @@ void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_pa
   int order[MAX_BANDS];
   for (int b = 0; b < n; ++b) {
     out.b[b] = bands[b];
-    if (lds_ok && bands[b].ck[sw] >= DMA_MIN_CHUNK) out.lds_mask |= 1u << b;
+    const int pages = (bands[b].kv_len + gamma - bands[b].kstart[sw] + PAGE - 1) / PAGE;
+    if (lds_ok && pages > ATTN_LDS_MIN_PAGES) out.lds_mask |= 1u << b;
     order[b] = b;
   }
   // each path's chunks are numbered band by band, the bands with the longest chunks first, so

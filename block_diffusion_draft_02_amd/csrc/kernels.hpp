@@ -189,11 +189,12 @@ constexpr int ATTN_CHUNK_PAGES_MAX = 512;
 // The attention of one layer is one launch whose bands take one of two paths, chosen by a
 // property of each band alone (so a band's arithmetic never depends on the other bands of
 // the call): with the LDS path enabled (a property of the drafter, fixed at create), bands
-// whose chunks span more than 256 keys (bands of more than 8192 keys) on a head_dim-128
-// layer without a window stream K/V through LDS; the rest load K/V straight into registers.
-// plan_attn fills the table and counts each path's chunks; partials stay indexed by the
-// call-wide chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
-void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, AttnBands& out,
+// of more than ATTN_LDS_MIN_PAGES pages (2048 keys) on a head_dim-128 layer without a window
+// stream K/V through LDS, planned in at most 16 chunks; the rest load K/V straight into
+// registers. plan_attn fills the table and counts each path's chunks; partials stay indexed
+// by the call-wide chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
+constexpr int ATTN_LDS_MIN_PAGES = 128;
+void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, int gamma, AttnBands& out,
                int& reg_chunks, int& lds_chunks);
 hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int reg_chunks, int lds_chunks,
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,

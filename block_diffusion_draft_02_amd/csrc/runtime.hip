@@ -72,9 +72,10 @@ struct dflash_ctx {
   unsigned long long* mk_best = nullptr;   // [MARKOV_MAX_ROWS][MAX_BANDS] argmax keys, zero between forwards
   int mk_groups = 1;
   // DFlash2 (selector_rank > 0): convs, top-16 candidates and the selector
-  // long bands stream attention K/V through LDS (drafters made for 8 or more sequences: one
-  // long band alone fills the chip better with the register path, a crowd of them reads
-  // less from L2 with this one; fixed at create, so no call's bands change another's bits)
+  // bands past 2048 keys stream attention K/V through LDS (drafters made for 8 or more
+  // sequences: one band alone fills the chip better with the register path, a crowd of them
+  // reads less from L2 with this one; fixed at create, so no call's bands change another's
+  // bits)
   bool attn_lds = false;
   bool d2 = false;
   int sel_rank = 0;
@@ -196,10 +197,10 @@ int chunk_pages(int pages, bool lds) {
   // 16 pages (256 keys: two passes of the attention workgroup's four 32-key wave slices) per
   // chunk, widened in steps of 16 pages so that a band never has more than 32 chunks: a
   // 4K-key band keeps every workgroup of a layer resident at once, long bands keep the
-  // partial traffic and the merge bounded. Bands past 512 pages on the attention's LDS path
-  // (one workgroup per chunk and kv head, not four) take at most 16 chunks, as long as a
-  // chunk's page ids fit the workgroup's table: half the partials and merge work
-  if (lds && pages > 512) return std::min(ATTN_CHUNK_PAGES_MAX, 16 * ((pages + 255) / 256));
+  // partial traffic and the merge bounded. Bands on the attention's LDS path (one workgroup
+  // per chunk and kv head, not four) take at most 16 chunks, as long as a chunk's page ids
+  // fit the workgroup's table: fewer partials and less merge work
+  if (lds && pages > ATTN_LDS_MIN_PAGES) return std::min(ATTN_CHUNK_PAGES_MAX, 16 * ((pages + 255) / 256));
   return 16 * std::max(1, (pages + 511) / 512);
 }
 
@@ -973,8 +974,8 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     }
     for (int sw = 0; sw < 2; ++sw) {
       B.kstart[sw] = sw == 0 ? 0 : (klo / PAGE) * PAGE;
-      // full layers of a drafter with the LDS path may plan for it (the path itself is chosen
-      // from the plan: chunks of 32 pages or more)
+      // full layers of a drafter with the LDS path plan its bands for it (the same page rule
+      // picks the path)
       plan_chunks(B.kstart[sw], kend, c->attn_lds && c->hd == 128 && sw == 0, B.ck[sw], B.nch[sw]);
       B.base[sw] = base[sw];
       base[sw] += B.nch[sw];
@@ -987,7 +988,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   AttnBands ab[2];
   int ab_reg[2], ab_lds[2];
   for (int sw = 0; sw < 2; ++sw)
-    plan_attn(a.bands, n_seqs, sw, c->hd, sw ? c->window : 0, c->attn_lds, ab[sw], ab_reg[sw], ab_lds[sw]);
+    plan_attn(a.bands, n_seqs, sw, c->hd, sw ? c->window : 0, c->attn_lds, gamma, ab[sw], ab_reg[sw], ab_lds[sw]);
   const float scale_log2 = (float)(1.0 / std::sqrt((double)c->hd) * 1.4426950408889634);
   HIPCHK(c, timed(c, DFLASH_K_PROLOGUE, st, [&] {
     return launch_fwd_prologue(a, c->bands_dev, c->bt_dev, c->slots, c->kpos, c->embed, c->layers[0].in_norm, c->h,

@@ -74,9 +74,9 @@ typedef struct {
   const uint8_t *layer_sliding;    /* host [num_layers], 1 = sliding layer; NULL = none */
   int32_t max_seq_len;             /* context rows a sequence may hold */
   int32_t max_batch;               /* sequence slots 0..max_batch-1; with 8 or more, bands of
-                                      more than 8192 keys on head_dim-128 layers without a
+                                      more than 2048 keys on head_dim-128 layers without a
                                       window take the attention path that stages K/V in LDS
-                                      (faster in a crowd of long bands, slower for one alone);
+                                      (faster in a crowd of bands, slower for one alone);
                                       fixed at create, so it never ties one band's results to
                                       the others of a call */
   int32_t num_pages;               /* 0 = the formula above; >= 2 = explicit pool size */

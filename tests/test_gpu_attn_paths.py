@@ -1,9 +1,9 @@
 """GPU parity of the two attention paths in one call: in a drafter made for 8 or more
 sequences, on a head_dim-128 layer without a window, a band whose chunks span 32 pages or
-more (a band of more than 8192 keys, planned in at most 16 chunks) streams its K/V through
+more (a band of more than 2048 keys, planned in at most 16 chunks) streams its K/V through
 LDS, every other band loads K/V straight into registers; windowed layers always take the
 register path. A small head_dim-128 drafter (2 layers, hidden 512, 16:2 heads) with bands on
-both sides of 8192 keys, two LDS chunk widths, last chunks of 1 and of 30 keys, a windowed
+both sides of 2048 keys, three LDS chunk widths, last chunks of 1 and of 30 keys, a windowed
 layer next to a full one, and block widths
 that leave query-row waves idle (gamma 2, 9, 16): logits against the oracle to the bf16
 parity bar, and every band of the mixed call bit for bit equal to the same band alone."""
@@ -18,10 +18,11 @@ from gpu_util import Agreement, Pair, DEV
 pytestmark = pytest.mark.gpu
 
 SEED = 1501
-# C + 16 keys: 8449 (LDS path, 12 chunks of 768 keys, the last holding 1 key), 8192 (the
-# register path's largest band: 32 chunks of 256), 9246 (LDS path, 13 chunks of 768, the last
-# 30 keys), 316, 14016 (LDS path, 14 chunks of 1024: the longest chunks, dispatched first)
-LENS = [8433, 8176, 9230, 300, 14000]
+# C + 16 keys: 2049 (LDS path, 9 chunks of 256 keys, the last holding 1 key), 2048 (the
+# register path's largest band: 8 chunks of 256), 9246 (LDS path, 13 chunks of 768, the last
+# 30 keys), 316 (register path), 14016 (LDS path, 14 chunks of 1024: the longest chunks,
+# dispatched first)
+LENS = [2033, 2032, 9230, 300, 14000]
 
 
 def _model(window):
