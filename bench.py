@@ -54,12 +54,13 @@ def gemm_bytes(m, M, fp8=False):
 # HBM bytes per launch of the forward's layer GEMMs (k_gemm_split, mean over
 # the QKV, O, gate/up and down shapes), from `rocprofv3 --pmc FETCH_SIZE` and
 # `--pmc WRITE_SIZE` runs of `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-batch16
-# --no-longctx`, scaled by what the same counters read for 20 plain 256 MiB device copies
-# (`bench.py --calibrate-copy 256`: FETCH_SIZE 0.500 of the bytes read, WRITE_SIZE 1.000 of
-# the bytes written). Valid only for the kernel source they were taken on.
+# --no-longctx --no-fp8 --no-dspark --no-dflash2`, scaled by what the same counters read for
+# 20 plain 256 MiB device copies (`bench.py --calibrate-copy 256`: FETCH_SIZE 0.500 of the
+# bytes read, WRITE_SIZE 1.000 of the bytes written). Valid only for the kernel source they
+# were taken on.
 TRAFFIC = {
     "gemm": dict(source="block_diffusion_draft_02_amd/csrc/k_gemm.hip",
-                 sha256="16eae5ec64c0f100aaa2b5beff9578a6493c5424bb1e1e045448a6d6b93c5224",
+                 sha256="04b83fc65f4e529ebb539016f316553d4aa4eaba1fa99707446eb4f0f7395dd1",
                  fetch_bytes=30.19e6, write_bytes=3.540e6),
 }
 
