@@ -591,10 +591,12 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& b
 }
 
 // Merge a band's chunk partials into the attention output (hi + lo bf16 terms). One
-// workgroup per (band, kv head, 8 query rows); thread (row, 4-float slice, chunk group q)
+// workgroup per (band, kv head, CMB_ROWS query rows; four, so that even one band spreads
+// over 128 workgroups); thread (row, 4-float slice, chunk group q)
 // folds chunks q, q + CQ, q + 2CQ, ... with a running maximum, all of its loads issued at
 // once; the CQ groups are then merged in group order. The order depends only on the band's
 // own chunk count.
+constexpr int CMB_ROWS = 4;
 template <int HD>
 __global__ __launch_bounds__(1024) void k_attn_combine(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml,
@@ -603,14 +605,15 @@ __global__ __launch_bounds__(1024) void k_attn_combine(const float* __restrict__
                                                        bf16* __restrict__ out,
                                                        bf16* __restrict__ out_lo) {
   constexpr int NSL = HD / 4;             // 4-float slices per row
-  constexpr int CQ = 1024 / (8 * NSL);    // chunk groups
+  constexpr int CR = CMB_ROWS;
+  constexpr int CQ = 1024 / (CR * NSL);   // chunk groups
   constexpr int JM = NCH_MAX / CQ;        // chunks per group at most
-  __shared__ f32x4 red_o[CQ][8][NSL];
-  __shared__ float red_m[CQ][8], red_l[CQ][8];
+  __shared__ f32x4 red_o[CQ][CR][NSL];
+  __shared__ float red_m[CQ][CR], red_l[CQ][CR];
   const int b = blockIdx.x, kvh = blockIdx.y;
-  const int q = threadIdx.x / (8 * NSL);
-  const int row = (threadIdx.x / NSL) % 8, slc = threadIdx.x % NSL;
-  const int r = blockIdx.z * 8 + row;
+  const int q = threadIdx.x / (CR * NSL);
+  const int row = (threadIdx.x / NSL) % CR, slc = threadIdx.x % NSL;
+  const int r = blockIdx.z * CR + row;
   const int G = nh / nkv;
   const bool rv = r < gamma * G;
   const int nch = bands[b].nch[sw], base = bands[b].base[sw];
@@ -671,7 +674,7 @@ hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const 
                                int n_bands, int gamma, int nh, int nkv, int hd, int sw,
                                bf16* out, bf16* out_lo, hipStream_t st) {
   const int G = nh / nkv;
-  dim3 grid(n_bands, nkv, (gamma * G + 7) / 8);
+  dim3 grid(n_bands, nkv, (gamma * G + CMB_ROWS - 1) / CMB_ROWS);
   switch (hd) {
     case 32: (void)launch(k_attn_combine<32>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
     case 64: (void)launch(k_attn_combine<64>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
