@@ -3,13 +3,16 @@
 // sliding layers additionally hide keys with q_pos - k_pos >= window).
 //
 // Work split: the keys of a band are cut into chunks whose length depends only on the band's
-// own length (a multiple of 256 keys), so a band's result does not depend on which other
-// bands share the call. One workgroup per (chunk, kv head, 32 query rows), with the band
-// table passed by value. The workgroup stages its query rows (hi, lo) and all the chunk's
-// page ids in LDS; each of its four wavefronts then takes 32-key slices of the chunk (keys
-// 32w, 32w + 128, ...), loading a slice's K and V^T fragments straight from the pool into MFMA
-// operands, and keeps an online softmax state (exp2 domain, running maximum in raw score
-// units, so a probability is one FMA and one v_exp_f32) for its two 16-row query tiles:
+// own length (a multiple of 256 keys) and the drafter's create-time path switch, so a band's
+// result does not depend on which other bands share the call. Two paths share one launch
+// per layer, each band taking one by its own length (the LDS path, further below, streams a
+// long band's K/V through LDS for all its query rows at once). The register path: one
+// workgroup per (chunk, kv head, 32 query rows), with the band table passed by value. The
+// workgroup stages its query rows (hi, lo) and all the chunk's page ids in LDS; each of its
+// four wavefronts then takes 32-key slices of the chunk (keys 32w, 32w + 128, ...), loading a
+// slice's K and V^T fragments straight from the pool into MFMA operands, and keeps an online
+// softmax state (exp2 domain, running maximum in raw score units, so a probability is one FMA
+// and one v_exp_f32) for its two 16-row query tiles:
 //   S^T = K Q^T   two 16x16x32 MFMA tiles per slice and query tile; the key order inside
 //                 the tiles is permuted so that every lane ends up holding 8 consecutive
 //                 keys of one row
@@ -295,7 +298,7 @@ __device__ __forceinline__ void attn_reg_wg(AttnLds<HD>& sm, int id, const bf16*
   }
 }
 
-// ---- K/V staged through LDS (head_dim 128, layers without a window, long bands) -----------
+// ---- K/V staged through LDS (head_dim 128, layers without a window, bands past 2048 keys) --
 // One 4-wave workgroup per (chunk, kv head) with all of the item's query rows: wave w owns rows
 // 32w .. 32w + 31 (two 16-row tiles, Q hi and lo held in registers) and takes every 32-key
 // slice of the chunk in order, so the chunk's K/V leaves L2 once instead of once per row
