@@ -104,6 +104,8 @@ __device__ __forceinline__ T ld_part(const float* p) { return *reinterpret_cast<
 
 template <int B, typename T>
 __device__ __forceinline__ T sum_splits(const float* __restrict__ p, int S, long long ps, int gsz) {
+  // one split (a plain result): one load, and the same 0 + v the general path forms
+  if (S == 1) return T{} + ld_part<T>(p);
   T t = T{}, grp = T{};
   int in_grp = 0;
   for (int s0 = 0; s0 < S; s0 += B) {

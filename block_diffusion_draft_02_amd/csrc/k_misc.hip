@@ -395,11 +395,21 @@ __global__ __launch_bounds__(1024) void k_kv_append_post(const float* __restrict
     return;
   }
   constexpr int NE = KH * 16 * HD;
-  for (int e = threadIdx.x; e < NE; e += 1024) {
+  constexpr int NU = (NE + 1023) / 1024;   // elements per thread
+  // every load first (one round trip), then the LDS stores
+  float tv[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int e = threadIdx.x + u * 1024;
     const int h = e / (16 * HD), i = (e / HD) % 16, d = e % HD;
-    vt[h][i][d] = h < nhh && i < nr
-                      ? sum_splits<8, float>(KV + (size_t)(r0 + i) * ld + col0 + (size_t)h * HD + d, S, ps, gsz)
-                      : 0.f;
+    tv[u] = e < NE && h < nhh && i < nr
+                ? sum_splits<8, float>(KV + (size_t)(r0 + i) * ld + col0 + (size_t)h * HD + d, S, ps, gsz)
+                : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int e = threadIdx.x + u * 1024;
+    if (e < NE) vt[e / (16 * HD)][(e / HD) % 16][e % HD] = tv[u];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < NE; e += 1024) {
