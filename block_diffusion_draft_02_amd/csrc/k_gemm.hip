@@ -444,7 +444,7 @@ hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, c
 //    per-split partials (sum_splits), so one partial per group is handed over.
 //  * argmax mode (lm_head): one chain over the full K, then per row the best (value, lowest
 //    index) over the workgroup's columns, and optionally the drafted rows' fp32 logits.
-constexpr int WD_M = 64;    // rows per workgroup (four 16-row tiles)
+constexpr int WD_M = 64;    // rows per workgroup (four 16-row tiles: three workgroups a CU)
 constexpr int WD_N = 128;   // columns per workgroup: 4 waves x 2 tiles
 constexpr int WD_KC = 64;   // depth of one staged activation chunk
 constexpr int WD_APAD = 8;  // LDS row padding: rows 144 B apart keep a 16-lane read conflict-free
