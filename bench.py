@@ -60,7 +60,7 @@ def gemm_bytes(m, M, fp8=False):
 # were taken on.
 TRAFFIC = {
     "gemm": dict(source="block_diffusion_draft_02_amd/csrc/k_gemm.hip",
-                 sha256="04b83fc65f4e529ebb539016f316553d4aa4eaba1fa99707446eb4f0f7395dd1",
+                 sha256="06d2d180beb322cc28cd2c6e9944cd4a3b990c00a1bc8e2ac35d191410d4013e",
                  fetch_bytes=30.19e6, write_bytes=3.540e6),
 }
 
