@@ -67,6 +67,7 @@ def lib():
         L.dflash_ctx_kv_append.argtypes = [vp, i32, vp, i32p, i32, vp]
         L.dflash_ctx_kv_append_batch.argtypes = [vp, i32, i32p, i32p, vp, i32p, vp]
         L.dflash_block_forward.argtypes = [vp, i32, i32p, i32p, i32p, i32, vp, vp, vp]
+        L.dflash_block_forward_noalloc.argtypes = [vp, i32, i32p, i32p, i32p, i32, vp, vp, vp]
         L.dflash_destroy.argtypes = [vp]
         L.dflash_destroy.restype = None
         L.dflash_seq_reset.argtypes = [vp, i32]
@@ -80,7 +81,7 @@ def lib():
         L.dflash_strerror.argtypes = [C.c_int]
         L.dflash_strerror.restype = C.c_char_p
         for f in ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch", "dflash_block_forward",
-                  "dflash_seq_reset",
+                  "dflash_block_forward_noalloc", "dflash_seq_reset",
                   "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy", "dflash_timing",
                   "dflash_timing_read"):
             getattr(L, f).restype = C.c_int
@@ -89,7 +90,7 @@ def lib():
 
 
 EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch", "dflash_block_forward",
-            "dflash_destroy",
+            "dflash_block_forward_noalloc", "dflash_destroy",
             "dflash_seq_reset", "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy",
             "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
 
@@ -214,6 +215,15 @@ class Drafter:
         gamma = self.m["gamma_max"] if gamma is None else gamma
         s, b, q = _i32_array(seqs), _i32_array(bonus), _i32_array(q_rope_pos)
         self._check(self.L.dflash_block_forward(
+            self.ctx, len(seqs), s, b, q, gamma, _ptr(draft_tokens),
+            _ptr(logits) if logits is not None else None, _stream(stream)))
+
+    def dflash_block_forward_noalloc(self, seqs, bonus, draft_tokens, logits=None, q_rope_pos=None,
+                                     gamma=None, stream=None):
+        """dflash_block_forward with its partials in the library's static per-device scratch."""
+        gamma = self.m["gamma_max"] if gamma is None else gamma
+        s, b, q = _i32_array(seqs), _i32_array(bonus), _i32_array(q_rope_pos)
+        self._check(self.L.dflash_block_forward_noalloc(
             self.ctx, len(seqs), s, b, q, gamma, _ptr(draft_tokens),
             _ptr(logits) if logits is not None else None, _stream(stream)))
 

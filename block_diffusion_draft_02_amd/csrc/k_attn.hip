@@ -31,7 +31,7 @@ constexpr int KW = 32;           // keys of one wavefront's slice per pass
 constexpr int AW = 4;            // wavefronts per workgroup
 constexpr int KP = AW * KW;      // keys of one workgroup pass
 constexpr int RG = 32;           // query rows per workgroup: two 16-row tiles
-constexpr int RPAD = 128;        // query-row slots of one (chunk, kv head) partial
+constexpr int RPAD = ATTN_PART_ROWS;   // query-row slots of one (chunk, kv head) partial
 constexpr int NCH_MAX = 64;      // chunks of one band that k_attn_combine accepts
 constexpr float RESCALE_LOG2 = 8.f;  // headroom of the lazily moved softmax reference maximum
 // ATTN_CHUNK_PAGES_MAX (kernels.hpp): page ids of a chunk, all staged in LDS
@@ -560,7 +560,13 @@ void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_pa
   }
   // each path's chunks are numbered band by band, the bands with the longest chunks first, so
   // the longest workgroups start first (the dispatch order only; no band's sums change)
-  std::stable_sort(order, order + n, [&](int x, int y) { return bands[x].ck[sw] > bands[y].ck[sw]; });
+  // (a stable insertion sort: at most 32 bands, and no temporary buffer is allocated)
+  for (int i = 1; i < n; ++i) {
+    const int b = order[i];
+    int j = i;
+    for (; j > 0 && bands[order[j - 1]].ck[sw] < bands[b].ck[sw]; --j) order[j] = order[j - 1];
+    order[j] = b;
+  }
   for (int i = 0; i < n; ++i) {
     const int b = order[i];
     int& nch = (out.lds_mask >> b) & 1u ? lds_chunks : reg_chunks;

@@ -194,6 +194,9 @@ constexpr int ATTN_CHUNK_PAGES_MAX = 512;
 // registers. plan_attn fills the table and counts each path's chunks; partials stay indexed
 // by the call-wide chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
 constexpr int ATTN_LDS_MIN_PAGES = 128;
+// query-row slots of one (chunk, kv head) partial: part_o [items][ATTN_PART_ROWS][hd] and
+// part_ml [items][ATTN_PART_ROWS][2] for items = (chunks of the call) * nkv
+constexpr int ATTN_PART_ROWS = 128;
 void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, int gamma, AttnBands& out,
                int& reg_chunks, int& lds_chunks);
 hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int reg_chunks, int lds_chunks,

@@ -9,7 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <deque>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -17,6 +17,12 @@
 #include "kernels.hpp"
 
 using namespace dfl;
+
+// Scratch of dflash_block_forward_noalloc: the forward's partials when the caller cannot
+// allocate. In host code `scratch` is only a stand-in for the symbol: its device address on
+// each device comes from hipGetSymbolAddress (scratch_setup), and only that address is used.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)DFLASH_NOALLOC_SCRATCH_MB << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -35,6 +41,18 @@ struct LayerDev {
   // DFlash2: the two conv sites' base kernels (the caller's) and T16 copies of their projections
   const bf16 *cba = nullptr, *cbm = nullptr;
   bf16 *w_cpa = nullptr, *w_cpm = nullptr;
+};
+
+// The pool's free list: a ring of page ids sized once at create, so that taking and returning
+// pages never allocates
+struct FreeList {
+  std::vector<int> ring;
+  size_t head = 0, count = 0;
+  void init(size_t cap) { ring.assign(std::max<size_t>(cap, 1), 0); head = count = 0; }
+  size_t size() const { return count; }
+  int front() const { return ring[head]; }
+  void pop_front() { head = (head + 1) % ring.size(); --count; }
+  void push_back(int p) { ring[(head + count) % ring.size()] = p; ++count; }
 };
 
 struct SeqState {
@@ -117,6 +135,7 @@ struct dflash_ctx {
   int* best_i = nullptr;
   int lm_groups = 0;
   int n_cu = 1;               // compute units of the device the context was created on
+  int dev = 0;                // that device
   GemmPlan g_qkv, g_o, g_gu, g_down, g_fc, g_kvapp;
   // append scratch
   float* F32 = nullptr;
@@ -134,9 +153,9 @@ struct dflash_ctx {
   long long tcnt[DFLASH_K_NUM_CLASSES] = {};
   // host state
   std::vector<SeqState> seqs;
-  std::deque<int> free_pages;
+  FreeList free_pages;
   std::vector<void*> owned;
-  std::string err;
+  char err[512] = {0};
   bool poisoned = false;
 };
 
@@ -144,12 +163,10 @@ namespace {
 
 int fail(dflash_ctx* c, int code, const char* fmt, ...) {
   if (c) {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(c->err, sizeof c->err, fmt, ap);
     va_end(ap);
-    c->err = buf;
     if (code == DFLASH_EHIP) c->poisoned = true;
   }
   return code;
@@ -375,6 +392,25 @@ std::vector<double> inv_freq_table(const dflash_config* cfg, double* mscale) {
   return f;
 }
 
+// The no-allocation forward's scratch on each device: every device the library runs on holds
+// its own copy of `scratch` until the process ends; dflash_create looks its address up once
+// per device, with that device current, and kernels get that address (g_scratch_ptr).
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_setup(dflash_ctx* c) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (c->dev < 0 || c->dev >= MAX_DEVICES) return fail(c, DFLASH_EINVAL, "device %d beyond the library's %d", c->dev, MAX_DEVICES);
+  if (g_scratch_ptr[c->dev]) return DFLASH_OK;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p)
+    return fail(c, DFLASH_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+  g_scratch_ptr[c->dev] = p;
+  return DFLASH_OK;
+}
+
 void release(dflash_ctx* c) {
   if (!c) return;
   for (int i = 0; i < RING; ++i)
@@ -452,7 +488,7 @@ const char* dflash_strerror(int code) {
   }
 }
 
-const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err.c_str() : ""; }
+const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err : ""; }
 
 int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* stream, dflash_ctx** out) {
   if (!out) return DFLASH_EINVAL;
@@ -483,6 +519,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   // a zeroed sentinel that is never handed out
   c->per_seq = (c->max_seq + c->gmax + 1 + PAGE - 1) / PAGE;
   c->num_pages = cfg->num_pages ? cfg->num_pages : (long long)c->per_seq * c->max_batch + 1;
+  c->free_pages.init((size_t)c->num_pages);
   if (cfg->page_order) {
     std::vector<char> seen(c->num_pages, 0);
     for (long long i = 0; i + 1 < c->num_pages; ++i) {
@@ -498,11 +535,16 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
     for (long long p = 1; p < c->num_pages; ++p) c->free_pages.push_back((int)p);
   }
   c->seqs.resize(c->max_batch);
+  // a sequence's tables never outgrow these, so appends and forwards never reallocate them
+  for (SeqState& q : c->seqs) {
+    q.bt.reserve(c->per_seq);
+    q.pos.reserve(c->max_seq);
+  }
   c->m_max = c->max_batch * c->gmax;
   c->fc = (const bf16*)w->fc; c->hidden_norm = (const bf16*)w->hidden_norm; c->norm = (const bf16*)w->norm;
   c->embed = (const bf16*)w->embed_tokens;
 
-  auto fin = [&](int r) { if (r != DFLASH_OK) { std::string e = c->err; release(c); (void)e; } return r; };
+  auto fin = [&](int r) { if (r != DFLASH_OK) release(c); return r; };
   const size_t hsz = (size_t)c->h;
   const size_t pl = page_layer_elems(c->nkv, c->hd);
   c->g_qkv = plan_gemm(c->qd + 2 * c->kvd, c->h);
@@ -526,9 +568,13 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
   c->lm_groups = lmhead_groups(c->V);
   {
     int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+    if (hipGetDevice(&dev) != hipSuccess) return fin(fail(c, DFLASH_EHIP, "hipGetDevice failed"));
+    c->dev = dev;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
       c->n_cu = ncu;
   }
+  // the no-allocation forward's scratch: its device address, looked up once per device
+  if ((rc = scratch_setup(c)) != DFLASH_OK) return fin(rc);
   // split-KV partial slots: chunks per band are bounded by the chunk plan
   const size_t items = (size_t)c->max_batch * max_chunks(c->per_seq) * c->nkv;
   if ((rc = dalloc(c, &c->pool, (size_t)c->L * c->num_pages * pl)) ||
@@ -834,7 +880,7 @@ int dflash_ctx_kv_append_batch(dflash_ctx* c, int32_t n_seqs, const int32_t* seq
   if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
   if (n_seqs < 1 || n_seqs > c->max_batch) return fail(c, DFLASH_EINVAL, "n_seqs %d not in [1, %d]", n_seqs, c->max_batch);
   if (!seqs || !counts || !target_hidden) return fail(c, DFLASH_EINVAL, "NULL seqs, counts or target_hidden");
-  std::vector<char> seen(c->max_batch, 0);
+  bool seen[MAX_BANDS] = {};   // max_batch <= MAX_BANDS
   long long total = 0;
   int need = 0;
   for (int b = 0; b < n_seqs; ++b) {
@@ -921,16 +967,91 @@ int dflash_ctx_kv_append_batch(dflash_ctx* c, int32_t n_seqs, const int32_t* seq
   return DFLASH_OK;
 }
 
-int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int32_t* bonus,
-                         const int32_t* q_rope_pos, int32_t gamma, int32_t* draft_tokens,
-                         float* logits, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The device scratch one forward writes and reads back: split-K partials, attention
+// partials and lm_head argmax partials (all fully written before they are read)
+struct FwdScratch {
+  float* part;
+  float* aparts_o;
+  float* aparts_ml;
+  float* best_v;
+  int* best_i;
+};
+
+// what a forward of n_seqs bands of `gamma` rows needs of each scratch buffer (elements),
+// given the call's total attention chunks of full-attention layers
+struct FwdNeed {
+  size_t part, aparts_o, aparts_ml, best;
+};
+
+FwdNeed fwd_need(const dflash_ctx* c, int n_seqs, int gamma, int chunks_full) {
+  const int M = n_seqs * gamma;
+  const bool wide = M > ROW_GROUP;
+  FwdNeed n{};
+  for (const GemmPlan* g : {&c->g_qkv, &c->g_o, &c->g_gu, &c->g_down, &c->g_cp, &c->g_sh}) {
+    if (g->N == 0) continue;   // (the DFlash2 plans of a plain drafter)
+    const int cnt = wide ? gemm_wide_groups(g->K, g->gsz) : g->S;
+    n.part = std::max(n.part, (size_t)cnt * M * g->N);
+  }
+  // a sliding layer's keys start at or after a full layer's, so its chunks are never more
+  const size_t items = (size_t)chunks_full * c->nkv;
+  n.aparts_o = items * ATTN_PART_ROWS * c->hd;
+  n.aparts_ml = items * ATTN_PART_ROWS * 2;
+  n.best = (size_t)M * std::max(c->lm_groups, lmhead_wide_groups(c->V));
+  return n;
+}
+
+size_t align256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+// the forward's scratch carved out of the device's static array; false if it does not fit
+bool carve_static(const dflash_ctx* c, const FwdNeed& n, FwdScratch& sc, size_t& total) {
+  const size_t b_part = align256(n.part * 4), b_o = align256(n.aparts_o * 4), b_ml = align256(n.aparts_ml * 4),
+               b_bv = align256(n.best * 4), b_bi = align256(n.best * 4);
+  total = b_part + b_o + b_ml + b_bv + b_bi;
+  if (total > NOALLOC_SCRATCH_BYTES) return false;
+  char* base = (char*)g_scratch_ptr[c->dev];
+  sc.part = (float*)base;
+  sc.aparts_o = (float*)(base + b_part);
+  sc.aparts_ml = (float*)(base + b_part + b_o);
+  sc.best_v = (float*)(base + b_part + b_o + b_ml);
+  sc.best_i = (int*)(base + b_part + b_o + b_ml + b_bv);
+  return true;
+}
+
+// a band's split-KV plan for full (sw 0) and sliding (sw 1) layers: keys from kstart (page
+// aligned) to kv_len + gamma in nch chunks of ck keys
+void band_plan(const dflash_ctx* c, const SeqState& s, int q_pos, int gamma, Band& B) {
+  const int C = s.kv_len;
+  const int kend = C + gamma;
+  // full layers: every key; sliding layers: from the first context row whose stamped
+  // position is within the window of block row 0 (rows further down see a subset)
+  int klo = 0;
+  if (c->window > 0) {
+    const long long lim = (long long)q_pos - c->window;  // visible iff pos > lim
+    klo = (int)(std::upper_bound(s.pos.begin(), s.pos.end(), lim) - s.pos.begin());
+  }
+  for (int sw = 0; sw < 2; ++sw) {
+    B.kstart[sw] = sw == 0 ? 0 : (klo / PAGE) * PAGE;
+    // full layers of a drafter with the LDS path plan its bands for it (the same page rule
+    // picks the path)
+    plan_chunks(B.kstart[sw], kend, c->attn_lds && c->hd == 128 && sw == 0, B.ck[sw], B.nch[sw]);
+  }
+}
+
+int block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int32_t* bonus,
+                  const int32_t* q_rope_pos, int32_t gamma, int32_t* draft_tokens, float* logits, void* stream,
+                  bool noalloc) {
   if (!c) return DFLASH_EINVAL;
   if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
   if (n_seqs < 1 || n_seqs > c->max_batch) return fail(c, DFLASH_EINVAL, "n_seqs %d not in [1, %d]", n_seqs, c->max_batch);
   if (!seqs || !bonus || !draft_tokens) return fail(c, DFLASH_EINVAL, "NULL seqs, bonus_tokens or draft_tokens");
   if (gamma < 2 || gamma > c->gmax) return fail(c, DFLASH_ERANGE, "gamma %d not in [2, %d]", gamma, c->gmax);
-  std::vector<char> seen(c->max_batch, 0);
-  int need = 0;
+  bool seen[MAX_BANDS] = {};   // max_batch <= MAX_BANDS
+  FwdArgs a{};
+  int need = 0, chunks_full = 0;
   for (int b = 0; b < n_seqs; ++b) {
     const int q = seqs[b];
     if (q < 0 || q >= c->max_batch || seen[q]) return fail(c, DFLASH_ERANGE, "seq %d out of range or repeated", q);
@@ -940,10 +1061,20 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       return fail(c, DFLASH_EINVAL, "q_rope_pos must be in [0, 2^30)");
     const SeqState& s = c->seqs[q];
     need += std::max(0, (s.kv_len + gamma + PAGE - 1) / PAGE - (int)s.bt.size());
+    Band& B = a.bands[b];
+    B.seq = q; B.kv_len = s.kv_len; B.q_pos = q_rope_pos ? q_rope_pos[b] : s.kv_len; B.bonus = bonus[b];
+    band_plan(c, s, B.q_pos, gamma, B);
+    chunks_full += B.nch[0];
   }
   if (need > (int)c->free_pages.size()) return fail(c, DFLASH_EPOOL, "KV pool exhausted (%d pages needed, %zu free)", need, c->free_pages.size());
+  FwdScratch sc{c->part, c->aparts_o, c->aparts_ml, c->best_v, c->best_i};
+  if (noalloc) {
+    size_t total = 0;
+    if (!carve_static(c, fwd_need(c, n_seqs, gamma, chunks_full), sc, total))
+      return fail(c, DFLASH_ERANGE, "this forward needs %zu bytes of scratch, above the no-allocation limit of %zu",
+                  total, NOALLOC_SCRATCH_BYTES);
+  }
   // --- committed from here on
-  FwdArgs a{};
   a.n_bands = n_seqs; a.gamma = gamma; a.mask_token = c->mask; a.per_seq = c->per_seq; a.n_upd = 0;
   int base[2] = {0, 0};
   for (int b = 0; b < n_seqs; ++b) {
@@ -960,23 +1091,10 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       s.bt.push_back(p);
     }
     Band& B = a.bands[b];
-    B.seq = q; B.kv_len = C; B.q_pos = q_rope_pos ? q_rope_pos[b] : C; B.bonus = bonus[b];
     const int lp0 = C / PAGE;
     B.pg[0] = s.bt[lp0];
     B.pg[1] = lp0 + 1 < (int)s.bt.size() ? s.bt[lp0 + 1] : 0;
-    const int kend = C + gamma;
-    // full layers: every key; sliding layers: from the first context row whose stamped
-    // position is within the window of block row 0 (rows further down see a subset)
-    int klo = 0;
-    if (c->window > 0) {
-      const long long lim = (long long)B.q_pos - c->window;  // visible iff pos > lim
-      klo = (int)(std::upper_bound(s.pos.begin(), s.pos.end(), lim) - s.pos.begin());
-    }
     for (int sw = 0; sw < 2; ++sw) {
-      B.kstart[sw] = sw == 0 ? 0 : (klo / PAGE) * PAGE;
-      // full layers of a drafter with the LDS path plan its bands for it (the same page rule
-      // picks the path)
-      plan_chunks(B.kstart[sw], kend, c->attn_lds && c->hd == 128 && sw == 0, B.ck[sw], B.nch[sw]);
       B.base[sw] = base[sw];
       base[sw] += B.nch[sw];
     }
@@ -1010,7 +1128,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     if (wide) {
       const NormIn nn{c->ssq, c->eps, c->h};
       return timed(c, DFLASH_K_GEMM, st, [&] {
-        return launch_gemm_wide(A, A_lo, lda, M, W, p.N, p.K, p.gsz, c->part, ps, st, normed ? &nn : nullptr, wsc);
+        return launch_gemm_wide(A, A_lo, lda, M, W, p.N, p.K, p.gsz, sc.part, ps, st, normed ? &nn : nullptr, wsc);
       });
     }
     for (int r0 = 0; r0 < M; r0 += ROW_GROUP) {
@@ -1018,7 +1136,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       const NormIn nn{c->ssq + (size_t)r0 * SSQ_STRIDE, c->eps, c->h};
       hipError_t e = timed(c, DFLASH_K_GEMM, st, [&] {
         return launch_gemm_skinny(A + (size_t)r0 * lda, A_lo + (size_t)r0 * lda, lda, mg, W, p.N, p.K, p.klen,
-                                  c->part + (size_t)r0 * p.N, ps, true, st, normed ? &nn : nullptr, wsc);
+                                  sc.part + (size_t)r0 * p.N, ps, true, st, normed ? &nn : nullptr, wsc);
       });
       if (e != hipSuccess) return e;
     }
@@ -1030,7 +1148,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     hipError_t e = gemm(c->Xn, c->Xn_lo, c->h, w_proj, nullptr, c->g_cp, true);
     if (e != hipSuccess) return e;
     return timed(c, DFLASH_K_DCONV, st, [&] {
-      return launch_dconv_prepare(c->Xn, c->Xn_lo, c->ssq, c->eps, M, c->h, gamma, c->part, parts(c->g_cp).first,
+      return launch_dconv_prepare(c->Xn, c->Xn_lo, c->ssq, c->eps, M, c->h, gamma, sc.part, parts(c->g_cp).first,
                                   (long long)M * c->g_cp.N, parts(c->g_cp).second, base, dyn, c->U, c->U_lo, st);
     });
   };
@@ -1044,32 +1162,32 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
     HIPCHK(c, gemm(c->d2 ? c->U : c->Xn, c->d2 ? c->U_lo : c->Xn_lo, c->h, q8 ? (const bf16*)d.q_qkv : d.w_qkv,
                    q8 ? d.s_qkv : nullptr, c->g_qkv, !c->d2));
     HIPCHK(c, timed(c, DFLASH_K_QKV_POST, st, [&] {
-      return launch_qkv_post(c->part, parts(c->g_qkv).first, (long long)M * c->g_qkv.N, parts(c->g_qkv).second,
+      return launch_qkv_post(sc.part, parts(c->g_qkv).first, (long long)M * c->g_qkv.N, parts(c->g_qkv).second,
                              M, gamma, c->bands_dev,
                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
                              (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
       return launch_block_attn(c->Qb, c->Qb_lo, ab[sw], ab_reg[sw], ab_lds[sw], gamma, c->nh, g, l, sw,
-                               sw ? c->window : 0, scale_log2, c->aparts_o, c->aparts_ml, st);
+                               sw ? c->window : 0, scale_log2, sc.aparts_o, sc.aparts_ml, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN_COMBINE, st, [&] {
-      return launch_attn_combine(c->aparts_o, c->aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
+      return launch_attn_combine(sc.aparts_o, sc.aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
     }));
     HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, q8 ? (const bf16*)d.q_o : d.o_proj, q8 ? d.s_o : nullptr, c->g_o, false));
     HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
       if (c->d2)
-        return launch_resid_dconv(c->X, c->part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
+        return launch_resid_dconv(c->X, sc.part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
                                   M, c->h, gamma, c->dyn_a, d.cba, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
-      return launch_resid_sum(c->X, c->part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
+      return launch_resid_sum(c->X, sc.part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
                               M, c->h, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
     }));
     if (c->d2) HIPCHK(c, dconv_site(d.w_cpm, d.cbm, c->dyn_m));
     HIPCHK(c, gemm(c->d2 ? c->U : c->Xn, c->d2 ? c->U_lo : c->Xn_lo, c->h, q8 ? (const bf16*)d.q_gu : d.w_gu,
                    q8 ? d.s_gu : nullptr, c->g_gu, !c->d2));
     HIPCHK(c, timed(c, DFLASH_K_SILU, st, [&] {
-      return launch_silu_mul(c->part, parts(c->g_gu).first, (long long)M * c->g_gu.N, parts(c->g_gu).second, M,
+      return launch_silu_mul(sc.part, parts(c->g_gu).first, (long long)M * c->g_gu.N, parts(c->g_gu).second, M,
                              c->ff, c->act, c->act_lo, st);
     }));
     HIPCHK(c, gemm(c->act, c->act_lo, c->ff, q8 ? (const bf16*)d.q_down : d.down_proj, q8 ? d.s_down : nullptr,
@@ -1079,7 +1197,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       // final norm of the residual rows
       const bf16* nw = l + 1 < c->L ? c->layers[l + 1].in_norm : c->norm;
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-        return launch_resid_dconv(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
+        return launch_resid_dconv(c->X, sc.part, parts(c->g_down).first, (long long)M * c->g_down.N,
                                   parts(c->g_down).second, M, c->h, gamma, c->dyn_m, d.cbm, nw, c->ssq, c->Xn,
                                   c->Xn_lo, st);
       }));
@@ -1089,14 +1207,14 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
         }));
     } else if (l + 1 < c->L) {
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-        return launch_resid_sum(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
+        return launch_resid_sum(c->X, sc.part, parts(c->g_down).first, (long long)M * c->g_down.N,
                                 parts(c->g_down).second, M, c->h, c->layers[l + 1].in_norm, c->ssq, c->Xn,
                                 c->Xn_lo, st);
       }));
     } else {
       // the last residual add also applies the final norm: the lm_head's rows (hi + lo)
       HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
-        return launch_resid_norm(c->X, c->part, parts(c->g_down).first, (long long)M * c->g_down.N,
+        return launch_resid_norm(c->X, sc.part, parts(c->g_down).first, (long long)M * c->g_down.N,
                                  parts(c->g_down).second, M, c->h, c->norm, c->eps, c->Xn, c->Xn_lo, st);
       }));
     }
@@ -1115,12 +1233,12 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   if ((c->R || c->d2) && !logits) logits = c->mk_logits;
   if (lm_wide) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
-      return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, lmw, c->V, c->h, c->best_v, c->best_i, ng, gamma,
+      return launch_lmhead_wide(c->Xn, c->Xn_lo, c->h, M, lmw, c->V, c->h, sc.best_v, sc.best_i, ng, gamma,
                                 logits, st, lms);
     }));
   } else if (ng_p > 0) {
     HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
-      return launch_lmhead_persistent(c->Xn, c->Xn_lo, c->h, M, 0, lmw, c->V, c->h, c->best_v, c->best_i,
+      return launch_lmhead_persistent(c->Xn, c->Xn_lo, c->h, M, 0, lmw, c->V, c->h, sc.best_v, sc.best_i,
                                       ng, gamma, logits, st, lms);
     }));
   } else {
@@ -1129,7 +1247,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       HIPCHK(c, timed(c, DFLASH_K_LMHEAD, st, [&] {
         return launch_lmhead_argmax(c->Xn + (size_t)r0 * c->h, c->Xn_lo + (size_t)r0 * c->h, c->h, mg, r0,
                                     c->lm_head, c->V, c->h,
-                                    c->best_v, c->best_i, ng, gamma, logits, st);
+                                    sc.best_v, sc.best_i, ng, gamma, logits, st);
       }));
     }
   }
@@ -1144,7 +1262,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
       return launch_topk_partial(logits, drafted, c->V, c->tk_v, c->tk_i, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_SELECTOR, st, [&] {
-      return launch_selector_pairs(c->tk_v, c->tk_i, c->part, parts(c->g_sh).first, (long long)M * c->g_sh.N,
+      return launch_selector_pairs(c->tk_v, c->tk_i, sc.part, parts(c->g_sh).first, (long long)M * c->g_sh.N,
                                    parts(c->g_sh).second, c->sel_rank, n_seqs, gamma, sb, c->sel_pred, c->sel_succ,
                                    c->V, c->sel_v, c->sel_i, c->sel_pair, st);
     }));
@@ -1155,7 +1273,7 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   }
   if (!c->R) {
     HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] {
-      return launch_argmax_reduce(c->best_v, c->best_i, ng, n_seqs, gamma, draft_tokens, st);
+      return launch_argmax_reduce(sc.best_v, sc.best_i, ng, n_seqs, gamma, draft_tokens, st);
     }));
     return DFLASH_OK;
   }
@@ -1171,6 +1289,28 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
   }
   HIPCHK(c, timed(c, DFLASH_K_ARGMAX, st, [&] { return launch_markov_finish(c->mk_best, n_seqs, gamma, draft_tokens, st); }));
   return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int32_t* bonus,
+                         const int32_t* q_rope_pos, int32_t gamma, int32_t* draft_tokens,
+                         float* logits, void* stream) {
+  return block_forward(c, n_seqs, seqs, bonus, q_rope_pos, gamma, draft_tokens, logits, stream, false);
+}
+
+int dflash_block_forward_noalloc(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int32_t* bonus,
+                                 const int32_t* q_rope_pos, int32_t gamma, int32_t* draft_tokens,
+                                 float* logits, void* stream) {
+  if (!c) return DFLASH_EINVAL;
+  // launch timing would create events: it is off for this call
+  const uint32_t tmask = c->tmask;
+  c->tmask = 0;
+  const int rc = block_forward(c, n_seqs, seqs, bonus, q_rope_pos, gamma, draft_tokens, logits, stream, true);
+  c->tmask = tmask;
+  return rc;
 }
 
 int dflash_timing(dflash_ctx* c, uint32_t class_mask) {

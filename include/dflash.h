@@ -26,7 +26,10 @@
  *  - Everything named "host" is host memory read during the call only.
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on it and
  *    the call returns; outputs are valid once the stream has reached that point. A
- *    context is used by one host thread at a time.
+ *    context is used by one host thread at a time, and the work of its calls must be
+ *    ordered: every call reuses the context's scratch and writes its KV pool, so calls
+ *    enqueued on different streams must be ordered by the caller (events or syncs), or they
+ *    race.
  *  - Every condition the host can check is checked before anything is enqueued, and a
  *    failing call changes no state (no pages taken, kv_len unchanged). A HIP runtime
  *    failure returns DFLASH_EHIP and leaves the context unusable (every later call
@@ -214,6 +217,25 @@ int dflash_ctx_kv_append_batch(dflash_ctx *ctx, int32_t n_seqs, const int32_t *s
 int dflash_block_forward(dflash_ctx *ctx, int32_t n_seqs, const int32_t *seqs,
                          const int32_t *bonus_tokens, const int32_t *q_rope_pos,
                          int32_t gamma, int32_t *draft_tokens, float *logits, void *stream);
+
+/* dflash_block_forward without any allocation, for callers that cannot allocate device
+ * memory during the call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it): the same arguments, checks, kernels and results (bit for bit), but the
+ * forward's split-K, attention and argmax partials live in one static device array of
+ * DFLASH_NOALLOC_SCRATCH_MB MiB per device instead of the context's scratch. The call makes
+ * no hipMalloc / hipFree or host heap allocation and never times its launches (dflash_timing
+ * is ignored for it).
+ *   - A forward whose partials do not fit the array is refused with DFLASH_ERANGE before
+ *     anything is enqueued (batch 1 of a 2048-hidden, 8-layer drafter at a 4096-row context
+ *     needs about 11 MiB; many long bands can need more than the limit).
+ *   - Every call on one device shares that device's array, whatever the context: calls that
+ *     overlap on the GPU (on different streams, or from different contexts without ordering)
+ *     race on it. The array keeps the last call's contents; every partial is written before
+ *     it is read, so nothing needs clearing. */
+#define DFLASH_NOALLOC_SCRATCH_MB 64
+int dflash_block_forward_noalloc(dflash_ctx *ctx, int32_t n_seqs, const int32_t *seqs,
+                                 const int32_t *bonus_tokens, const int32_t *q_rope_pos,
+                                 int32_t gamma, int32_t *draft_tokens, float *logits, void *stream);
 
 /* Release everything the context owns (waits for its outstanding work). NULL is a no-op. */
 void dflash_destroy(dflash_ctx *ctx);
