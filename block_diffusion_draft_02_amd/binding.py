@@ -140,6 +140,54 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr())
 
 
+def _check_tensor(t, name, dtype, numel=None, device=True, shape=None):
+    """Raise ValueError unless `t` is a contiguous torch tensor of `dtype` with at least `numel`
+    elements (or exactly `shape`), on a GPU when `device`: the library reads and writes through
+    the raw pointer, so anything else would read or write outside the tensor."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+
+
+def _check_len(vals, name, n):
+    if vals is not None and len(vals) != n:
+        raise ValueError(f"{name} must have {n} entries, got {len(vals)}")
+
+
+def weight_shapes(m: dict) -> dict:
+    """Shape of every weight the drafter reads, by the names Drafter takes."""
+    h, hd = m["hidden"], m["head_dim"]
+    qd, kvd, ff, V = m["num_q_heads"] * hd, m["num_kv_heads"] * hd, m["intermediate"], m["vocab"]
+    out = {"fc": (h, m["num_taps"] * m["target_hidden"]), "hidden_norm": (h,), "norm": (h,),
+           "embed_tokens": (V, h), "lm_head": (V, h)}
+    for l in range(m["num_layers"]):
+        p = f"layers.{l}."
+        out.update({p + "q_proj": (qd, h), p + "k_proj": (kvd, h), p + "v_proj": (kvd, h), p + "o_proj": (h, qd),
+                    p + "q_norm": (hd,), p + "k_norm": (hd,), p + "input_layernorm": (h,),
+                    p + "post_attention_layernorm": (h,), p + "gate_proj": (ff, h), p + "up_proj": (ff, h),
+                    p + "down_proj": (h, ff)})
+        if m.get("selector_rank", 0):
+            k, ng = m["conv_kernel_size"], 2 * m["conv_kernel_size"] * h // m["conv_group_size"]
+            for site in ("attention", "mlp"):
+                out.update({f"{p}{site}_conv_base": (2, k, h), f"{p}{site}_conv_proj": (ng, h)})
+    if m.get("markov_rank", 0):
+        out.update({"markov_w1": (V, m["markov_rank"]), "markov_w2": (V, m["markov_rank"])})
+    if m.get("selector_rank", 0):
+        r = m["selector_rank"]
+        out.update({"selector_pred": (V, r), "selector_succ": (V, r), "selector_hidden_proj": (r, h)})
+    return out
+
+
 def _stream(stream):
     if stream is not None:
         return C.c_void_p(stream)
@@ -153,7 +201,15 @@ class Drafter:
 
     def __init__(self, m: dict, weights: dict, max_seq_len: int, max_batch: int,
                  num_pages: int = 0, page_order=None, stream=None):
+        import torch
+        self.ctx = None
         self.m = m
+        shapes = weight_shapes(m)
+        for dev in (False, True):   # every property but the device first, then the devices
+            for name, shape in shapes.items():
+                if name not in weights:
+                    raise ValueError(f"weight {name} is missing")
+                _check_tensor(weights[name], name, torch.bfloat16, shape=shape, device=dev)
         self.L = lib()
         self.weights = weights
         cfg, self._keep = make_config(m, max_seq_len, max_batch, num_pages, page_order)
@@ -196,16 +252,45 @@ class Drafter:
             pass
 
     # -- the calls -------------------------------------------------------------------------
+    def _check_hidden(self, target_hidden, rows=None):
+        import torch
+        width = self.m["num_taps"] * self.m["target_hidden"]
+        if getattr(target_hidden, "ndim", 0) != 2 or int(target_hidden.shape[1]) != width:
+            raise ValueError(f"target_hidden must be [rows, {width}] (num_taps * target_hidden)")
+        if rows is not None and int(target_hidden.shape[0]) != rows:
+            raise ValueError(f"target_hidden must hold {rows} rows, got {int(target_hidden.shape[0])}")
+        _check_tensor(target_hidden, "target_hidden", torch.bfloat16)
+
+    def _check_forward(self, seqs, bonus, q_rope_pos, gamma, draft_tokens, logits):
+        import torch
+        n = len(seqs)
+        if n < 1:
+            raise ValueError("seqs must name at least one sequence")
+        _check_len(bonus, "bonus", n)
+        _check_len(q_rope_pos, "q_rope_pos", n)
+        if not isinstance(gamma, int) or gamma < 2:
+            raise ValueError("gamma must be an int >= 2")
+        # every property but the device first, then the devices
+        for dev in (False, True):
+            _check_tensor(draft_tokens, "draft_tokens", torch.int32, numel=n * (gamma - 1), device=dev)
+            if logits is not None:
+                _check_tensor(logits, "logits", torch.float32, numel=n * (gamma - 1) * self.m["vocab"], device=dev)
+
     def dflash_ctx_kv_append(self, seq, target_hidden, positions=None, stream=None):
+        if getattr(target_hidden, "ndim", 0) != 2:
+            raise ValueError("target_hidden must be [rows, num_taps * target_hidden]")
         n = int(target_hidden.shape[0])
+        _check_len(positions, "positions", n)
+        self._check_hidden(target_hidden)
         pos = _i32_array(positions)
         self._check(self.L.dflash_ctx_kv_append(self.ctx, seq, _ptr(target_hidden), pos, n, _stream(stream)))
 
     def dflash_ctx_kv_append_batch(self, seqs, counts, target_hidden, positions=None, stream=None):
         """New rows of several sequences in one pass: target_hidden holds sum(counts) rows,
         the sequences' rows one after another in the order of seqs."""
-        if int(target_hidden.shape[0]) != int(sum(counts)):
-            raise ValueError("target_hidden must hold sum(counts) rows")
+        _check_len(counts, "counts", len(seqs))
+        _check_len(positions, "positions", int(sum(counts)))
+        self._check_hidden(target_hidden, rows=int(sum(counts)))
         s, n, pos = _i32_array(seqs), _i32_array(counts), _i32_array(positions)
         self._check(self.L.dflash_ctx_kv_append_batch(self.ctx, len(seqs), s, n, _ptr(target_hidden), pos,
                                                       _stream(stream)))
@@ -213,6 +298,7 @@ class Drafter:
     def dflash_block_forward(self, seqs, bonus, draft_tokens, logits=None, q_rope_pos=None,
                              gamma=None, stream=None):
         gamma = self.m["gamma_max"] if gamma is None else gamma
+        self._check_forward(seqs, bonus, q_rope_pos, gamma, draft_tokens, logits)
         s, b, q = _i32_array(seqs), _i32_array(bonus), _i32_array(q_rope_pos)
         self._check(self.L.dflash_block_forward(
             self.ctx, len(seqs), s, b, q, gamma, _ptr(draft_tokens),
@@ -222,6 +308,7 @@ class Drafter:
                                      gamma=None, stream=None):
         """dflash_block_forward with its partials in the library's static per-device scratch."""
         gamma = self.m["gamma_max"] if gamma is None else gamma
+        self._check_forward(seqs, bonus, q_rope_pos, gamma, draft_tokens, logits)
         s, b, q = _i32_array(seqs), _i32_array(bonus), _i32_array(q_rope_pos)
         self._check(self.L.dflash_block_forward_noalloc(
             self.ctx, len(seqs), s, b, q, gamma, _ptr(draft_tokens),
@@ -258,6 +345,11 @@ class Drafter:
 
     def dflash_debug_copy(self, buffer, dst, offset=0, nbytes=None, stream=None):
         """Copy into a torch tensor (host or device) `dst`; nbytes defaults to dst's size."""
-        nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+        if not dst.is_contiguous():
+            raise ValueError("dst must be contiguous")
+        cap = dst.numel() * dst.element_size()
+        nbytes = cap if nbytes is None else nbytes
+        if nbytes > cap:
+            raise ValueError(f"dst holds {cap} bytes, {nbytes} requested")
         self._check(self.L.dflash_debug_copy(self.ctx, buffer, C.c_void_p(dst.data_ptr()), offset, nbytes,
                                              _stream(stream)))

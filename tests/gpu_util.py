@@ -135,3 +135,34 @@ def read_slot_kv(gpu, layer: int, slots: np.ndarray):
         K[i] = pg[0].reshape(nkv, 16, hd)[:, off, :]
         V[i] = pg[1].reshape(nkv, hd, 16)[:, :, off]
     return K, V
+
+
+# The pool holds bf16 K/V and the oracle rounds every cached row to bf16 once, from float64.
+# The GPU rounds its fp32 result once too, so an element either matches the oracle's or sits
+# one bf16 step away (when the two unrounded values straddle a rounding boundary). Elements
+# near zero get an absolute floor: there the GPU's fp32 sums may differ from the exact ones by
+# more than the element's own (tiny) step.
+KV_FLOOR = 2.0 ** -16
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """The bf16 step at each value's magnitude: 2^(e-8) for |x| in [2^(e-1), 2^e); 0 at 0."""
+    _, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.where(x != 0, np.ldexp(1.0, e - 8), 0.0)
+
+
+def assert_kv_close(got_bits: np.ndarray, want: np.ndarray, what: str, slots=None):
+    """Cached K or V rows [n, nkv, hd] (bf16 bits) against the oracle's, element by element:
+    |got - want| <= ulp(want) + KV_FLOOR * max|want|. The message names the layer / tensor
+    (`what`), the slot, the kv head and the element of the worst miss."""
+    g = O.widen(got_bits)
+    w = np.asarray(want, dtype=np.float64)
+    tol = bf16_ulp(w) + KV_FLOOR * np.abs(w).max()
+    excess = np.abs(g - w) - tol
+    if (excess > 0).any():
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        row = i[0] if slots is None else f"slot {int(np.asarray(slots)[i[0]])}"
+        n_bad = int((excess > 0).sum())
+        raise AssertionError(f"{what}: {n_bad} elements beyond one bf16 step; worst at row {row}, kv head {i[1]}, "
+                             f"element {i[2]}: got {g[i]!r}, want {w[i]!r} (tolerance {tol[i]:.3g})")
+

@@ -191,3 +191,85 @@ def test_create_rejects_bad_dflash2_heads():
     lay[1].mlp_conv_base = None
     assert B.lib().dflash_create(C.byref(cfg), C.byref(w), None, C.byref(ctx)) == B.DFLASH_EINVAL
     assert not ctx.value
+
+
+# ---- the binding checks every argument before it reaches the library ------------------
+
+
+class _NoLib:
+    """Stands in for the loaded library: any call into it fails the test."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"the binding called {name} with a bad argument")
+
+
+def _unbound_drafter(m):
+    d = B.Drafter.__new__(B.Drafter)
+    d.m, d.L, d.ctx = m, _NoLib(), None
+    return d
+
+
+def test_binding_rejects_bad_tensors_and_lists_before_calling_the_library():
+    import torch
+    m = synth.model("tiny-L2-h256")
+    d = _unbound_drafter(m)
+    width = m["num_taps"] * m["target_hidden"]
+    H = torch.zeros((8, width), dtype=torch.bfloat16)
+    bad_hidden = [
+        (torch.zeros((8, width), dtype=torch.float32), "bfloat16"),
+        (torch.zeros((8, width + 1), dtype=torch.bfloat16), "num_taps"),
+        (torch.zeros((width, 8), dtype=torch.bfloat16).t(), "contiguous"),
+        (torch.zeros((8 * width,), dtype=torch.bfloat16), "num_taps"),
+        (H, "GPU tensor"),   # every check passes but the device (this host has no GPU tensors)
+    ]
+    for t, why in bad_hidden:
+        with pytest.raises(ValueError, match=why):
+            d.dflash_ctx_kv_append(0, t)
+    with pytest.raises(ValueError, match="positions must have 8"):
+        d.dflash_ctx_kv_append(0, H, positions=[1, 2, 3])
+    with pytest.raises(ValueError, match="counts must have 2"):
+        d.dflash_ctx_kv_append_batch([0, 1], [8], H)
+    with pytest.raises(ValueError, match="hold 9 rows"):
+        d.dflash_ctx_kv_append_batch([0, 1], [4, 5], H)
+    with pytest.raises(ValueError, match="positions must have 8"):
+        d.dflash_ctx_kv_append_batch([0, 1], [4, 4], H, positions=list(range(7)))
+    V = m["vocab"]
+    toks = torch.zeros((2, 15), dtype=torch.int32)
+    lg = torch.zeros((30, V), dtype=torch.float32)
+    bad_forward = [
+        (dict(seqs=[], bonus=[], draft_tokens=toks), "at least one"),
+        (dict(seqs=[0, 1], bonus=[3], draft_tokens=toks), "bonus must have 2"),
+        (dict(seqs=[0, 1], bonus=[3, 4], q_rope_pos=[9], draft_tokens=toks), "q_rope_pos must have 2"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks.to(torch.int64)), "int32"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks[:, :14].contiguous()), "28 elements, 30 needed"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks[:, ::2]), "contiguous"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks, logits=lg[:29]), "elements"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks, logits=lg.to(torch.float64)), "float32"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks, gamma=1), "gamma"),
+        (dict(seqs=[0, 1], bonus=[3, 4], draft_tokens=toks, logits=lg), "GPU tensor"),
+    ]
+    for kw, why in bad_forward:
+        for f in (d.dflash_block_forward, d.dflash_block_forward_noalloc):
+            with pytest.raises(ValueError, match=why):
+                f(**kw)
+    with pytest.raises(ValueError, match="bytes"):
+        d.dflash_debug_copy(B.DFLASH_BUF_POOL, torch.zeros(4, dtype=torch.int32), nbytes=17)
+
+
+def test_binding_rejects_bad_weights_before_calling_the_library():
+    import torch
+    m = synth.model("tiny-L2-h256")
+    shapes = B.weight_shapes(m)
+    W = {k: torch.zeros(v, dtype=torch.bfloat16) for k, v in shapes.items()}
+    for name, change, why in [("fc", lambda t: t[:, :-1].contiguous(), "shape"),
+                              ("layers.1.k_norm", lambda t: t.float(), "bfloat16"),
+                              ("lm_head", lambda t: t.t(), "contiguous|shape"),
+                              ("norm", None, "missing"),
+                              ("embed_tokens", lambda t: t, "GPU tensor")]:
+        bad = dict(W)
+        if change is None:
+            del bad[name]
+        else:
+            bad[name] = change(W[name])
+        with pytest.raises(ValueError, match=why):
+            B.Drafter(m, bad, 128, 1)

@@ -465,6 +465,34 @@ def test_lm_head_planted_argmax(tiny):
         assert r2["tokens"][0][row - 1] == tok   # drafts come from rows 1..gamma-1
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_chunked_lm_head_equals_cached_and_scalar_dots(tiny, fmt):
+    """The lm_head without cached weights takes the vocabulary in chunks (the branch the
+    large-vocabulary parity tests run): equal to the cached product, chunk edges and a ragged
+    last chunk included, and (bf16) to scalar dot products on sampled entries; the whole
+    forward without cached weights equals the cached one."""
+    m, W = tiny
+    if fmt == "fp8":
+        m = dict(m, weight_format="fp8")
+    g = np.random.default_rng(7)
+    y = g.standard_normal((15, m["hidden"]))
+    a = O.Drafter(m, W).lm_head(y)
+    b = O.Drafter(m, W, cache_weights=False).lm_head(y, chunk=100)   # 10 chunks of 100 and one of 24
+    assert a.shape == b.shape == (15, m["vocab"])
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13 * np.abs(a).max())
+    if fmt == "bf16":
+        lm = W["lm_head"]
+        for r, v in [(0, 0), (3, 99), (3, 100), (14, 1023), (7, 1000), (9, 512)]:
+            w = [float(x) for x in O.widen(lm[v])]
+            assert math.isclose(b[r, v], math.fsum(yi * wi for yi, wi in zip(y[r], w)), rel_tol=1e-12, abs_tol=1e-12)
+    e1 = _engine_with_ctx(m, W)
+    e2 = _engine_with_ctx(m, W, cache_weights=False)
+    r1 = e1.block_forward([0], [11], gamma=16)
+    r2 = e2.block_forward([0], [11], gamma=16)
+    assert np.allclose(r1["logits"], r2["logits"], rtol=1e-12, atol=1e-12 * np.abs(r1["logits"]).max())
+    assert np.array_equal(r1["tokens"], r2["tokens"])
+
+
 def test_engine_errors_leave_state_unchanged(tiny):
     m, W = tiny
     e = O.Engine(m, W, 40, 2)
