@@ -16,6 +16,9 @@ CODE_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "EPOOL", -4: "ERANGE", -5
 DFLASH_BUF_POOL, DFLASH_BUF_KPOS, DFLASH_BUF_SLOTS, DFLASH_BUF_BLOCKTAB, DFLASH_BUF_HIDDEN = 0, 1, 2, 3, 4
 DFLASH_BUF_HIDDEN_LO, DFLASH_BUF_FP8_LMHEAD, DFLASH_BUF_FP8_LMHEAD_SCALE = 5, 6, 7
 DFLASH_BUF_SEL_IDX, DFLASH_BUF_SEL_VALS = 8, 9
+DFLASH_BUF_CTX_FEAT, DFLASH_BUF_CTX_FEAT_LO = 10, 11
+DFLASH_BUF_LAYER_Q, DFLASH_BUF_LAYER_Q_LO, DFLASH_BUF_LAYER_ATTN, DFLASH_BUF_LAYER_ATTN_LO = 12, 13, 14, 15
+DFLASH_BUF_LAYER_X1, DFLASH_BUF_LAYER_X = 16, 17
 
 
 class dflash_config(C.Structure):
@@ -74,6 +77,7 @@ def lib():
         L.dflash_seq_info.argtypes = [vp, i32, i32p, i32p, i32p, i32]
         L.dflash_pool_geometry.argtypes = [vp, i64p, i64p, i64p, i64p, i64p]
         L.dflash_debug_copy.argtypes = [vp, i32, vp, C.c_size_t, C.c_size_t, vp]
+        L.dflash_debug_capture.argtypes = [vp, i32]
         L.dflash_last_error.argtypes = [vp]
         L.dflash_last_error.restype = C.c_char_p
         L.dflash_timing.argtypes = [vp, C.c_uint32]
@@ -82,8 +86,8 @@ def lib():
         L.dflash_strerror.restype = C.c_char_p
         for f in ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch", "dflash_block_forward",
                   "dflash_block_forward_noalloc", "dflash_seq_reset",
-                  "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy", "dflash_timing",
-                  "dflash_timing_read"):
+                  "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy", "dflash_debug_capture",
+                  "dflash_timing", "dflash_timing_read"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -92,7 +96,7 @@ def lib():
 EXPORTED = ("dflash_create", "dflash_ctx_kv_append", "dflash_ctx_kv_append_batch", "dflash_block_forward",
             "dflash_block_forward_noalloc", "dflash_destroy",
             "dflash_seq_reset", "dflash_seq_info", "dflash_pool_geometry", "dflash_debug_copy",
-            "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
+            "dflash_debug_capture", "dflash_last_error", "dflash_strerror", "dflash_timing", "dflash_timing_read")
 
 K_CLASSES = ("prologue", "gemm", "qkv_post", "attn", "attn_combine", "resid_norm", "silu",
              "lmhead", "argmax", "append_gemm", "append_misc", "markov", "dconv", "selector")
@@ -342,6 +346,10 @@ class Drafter:
         ms, cnt = (C.c_double * n)(), (C.c_int64 * n)()
         self._check(self.L.dflash_timing_read(self.ctx, ms, cnt, n))
         return {K_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
+
+    def dflash_debug_capture(self, on=True):
+        """Capture each layer's intermediates of the following forwards (see dflash.h)."""
+        self._check(self.L.dflash_debug_capture(self.ctx, 1 if on else 0))
 
     def dflash_debug_copy(self, buffer, dst, offset=0, nbytes=None, stream=None):
         """Copy into a torch tensor (host or device) `dst`; nbytes defaults to dst's size."""

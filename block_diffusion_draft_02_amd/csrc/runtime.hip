@@ -145,6 +145,10 @@ struct dflash_ctx {
   int* ring_dev = nullptr;
   hipEvent_t ring_ev[RING] = {};
   int ring_next = 0;
+  // per-layer intermediates of the last forward (dflash_debug_capture): [L][m_max][width]
+  bool cap_on = false;
+  bf16 *cap_q = nullptr, *cap_q_lo = nullptr, *cap_a = nullptr, *cap_a_lo = nullptr;
+  float *cap_x1 = nullptr, *cap_x = nullptr;
   // launch timing (opt-in per class)
   uint32_t tmask = 0;
   std::vector<hipEvent_t> tev;   // pairs (start, end)
@@ -800,6 +804,21 @@ int dflash_debug_copy(dflash_ctx* c, int32_t buffer, void* dst, size_t offset, s
     case DFLASH_BUF_SEL_VALS:
       if (!c->d2) return fail(c, DFLASH_EINVAL, "not a DFlash2 context");
       base = (const char*)c->sel_v; size = (size_t)c->max_batch * (c->gmax - 1) * 16 * 4; break;
+    case DFLASH_BUF_CTX_FEAT: base = (const char*)c->Fb; size = (size_t)APPEND_ROWS * c->h * 2; break;
+    case DFLASH_BUF_CTX_FEAT_LO: base = (const char*)c->Fb_lo; size = (size_t)APPEND_ROWS * c->h * 2; break;
+    case DFLASH_BUF_LAYER_Q:
+    case DFLASH_BUF_LAYER_Q_LO:
+    case DFLASH_BUF_LAYER_ATTN:
+    case DFLASH_BUF_LAYER_ATTN_LO:
+    case DFLASH_BUF_LAYER_X1:
+    case DFLASH_BUF_LAYER_X: {
+      if (!c->cap_q) return fail(c, DFLASH_EINVAL, "no capture: call dflash_debug_capture first");
+      const size_t rows = (size_t)c->L * c->m_max;
+      const void* bufs[] = {c->cap_q, c->cap_q_lo, c->cap_a, c->cap_a_lo, c->cap_x1, c->cap_x};
+      base = (const char*)bufs[buffer - DFLASH_BUF_LAYER_Q];
+      size = buffer >= DFLASH_BUF_LAYER_X1 ? rows * c->h * 4 : rows * c->qd * 2;
+      break;
+    }
     default: return fail(c, DFLASH_EINVAL, "unknown buffer %d", buffer);
   }
   if (offset > size || bytes > size - offset) return fail(c, DFLASH_ERANGE, "copy past the end of buffer %d", buffer);
@@ -1167,6 +1186,14 @@ int block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int3
                              c->nh, c->nkv, c->hd, d.q_norm, d.k_norm, c->eps, c->inv_freq,
                              (float)c->mscale, c->slots, g, l, c->Qb, c->Qb_lo, st);
     }));
+    // the debug seam's copies (dflash_debug_capture): device-to-device, stream-ordered
+    auto capture = [&](void* dst, const void* src, size_t row_bytes) -> hipError_t {
+      if (!c->cap_on || noalloc) return hipSuccess;
+      return hipMemcpyAsync((char*)dst + (size_t)l * c->m_max * row_bytes, src, (size_t)M * row_bytes,
+                            hipMemcpyDeviceToDevice, st);
+    };
+    HIPCHK(c, capture(c->cap_q, c->Qb, (size_t)c->qd * 2));
+    HIPCHK(c, capture(c->cap_q_lo, c->Qb_lo, (size_t)c->qd * 2));
     HIPCHK(c, timed(c, DFLASH_K_ATTN, st, [&] {
       return launch_block_attn(c->Qb, c->Qb_lo, ab[sw], ab_reg[sw], ab_lds[sw], gamma, c->nh, g, l, sw,
                                sw ? c->window : 0, scale_log2, sc.aparts_o, sc.aparts_ml, st);
@@ -1175,6 +1202,8 @@ int block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int3
       return launch_attn_combine(sc.aparts_o, sc.aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
     }));
+    HIPCHK(c, capture(c->cap_a, c->attn, (size_t)c->qd * 2));
+    HIPCHK(c, capture(c->cap_a_lo, c->attn_lo, (size_t)c->qd * 2));
     HIPCHK(c, gemm(c->attn, c->attn_lo, c->qd, q8 ? (const bf16*)d.q_o : d.o_proj, q8 ? d.s_o : nullptr, c->g_o, false));
     HIPCHK(c, timed(c, DFLASH_K_RESID_NORM, st, [&] {
       if (c->d2)
@@ -1183,6 +1212,7 @@ int block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int3
       return launch_resid_sum(c->X, sc.part, parts(c->g_o).first, (long long)M * c->g_o.N, parts(c->g_o).second,
                               M, c->h, d.post_norm, c->ssq, c->Xn, c->Xn_lo, st);
     }));
+    HIPCHK(c, capture(c->cap_x1, c->X, (size_t)c->h * 4));
     if (c->d2) HIPCHK(c, dconv_site(d.w_cpm, d.cbm, c->dyn_m));
     HIPCHK(c, gemm(c->d2 ? c->U : c->Xn, c->d2 ? c->U_lo : c->Xn_lo, c->h, q8 ? (const bf16*)d.q_gu : d.w_gu,
                    q8 ? d.s_gu : nullptr, c->g_gu, !c->d2));
@@ -1218,6 +1248,7 @@ int block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int3
                                  parts(c->g_down).second, M, c->h, c->norm, c->eps, c->Xn, c->Xn_lo, st);
       }));
     }
+    HIPCHK(c, capture(c->cap_x, c->X, (size_t)c->h * 4));
   }
   // one row group of at most 16 rows with the rows in LDS whole: the persistent lm_head;
   // more than one row group (or FP8 weights beyond the persistent form): the wide lm_head;
@@ -1311,6 +1342,21 @@ int dflash_block_forward_noalloc(dflash_ctx* c, int32_t n_seqs, const int32_t* s
   const int rc = block_forward(c, n_seqs, seqs, bonus, q_rope_pos, gamma, draft_tokens, logits, stream, true);
   c->tmask = tmask;
   return rc;
+}
+
+int dflash_debug_capture(dflash_ctx* c, int32_t on) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->poisoned) return fail(c, DFLASH_EHIP, "context unusable after an earlier HIP error");
+  if (on && !c->cap_q) {
+    const size_t rows = (size_t)c->L * c->m_max;
+    int rc;
+    if ((rc = dalloc(c, &c->cap_q, rows * c->qd)) || (rc = dalloc(c, &c->cap_q_lo, rows * c->qd)) ||
+        (rc = dalloc(c, &c->cap_a, rows * c->qd)) || (rc = dalloc(c, &c->cap_a_lo, rows * c->qd)) ||
+        (rc = dalloc(c, &c->cap_x1, rows * c->h)) || (rc = dalloc(c, &c->cap_x, rows * c->h)))
+      return rc;
+  }
+  c->cap_on = on != 0;
+  return DFLASH_OK;
 }
 
 int dflash_timing(dflash_ctx* c, uint32_t class_mask) {

@@ -274,13 +274,35 @@ int dflash_pool_geometry(const dflash_ctx *ctx, int64_t *num_pages, int64_t *pag
  *   DFLASH_BUF_FP8_LMHEAD_SCALE (FP8 contexts) float [vocab rounded up to 16]: the row scales;
  *   DFLASH_BUF_SEL_IDX   (DFlash2) int32 [n_seqs*(gamma-1)][16]: the last forward's candidates
  *                        per drafted row, best first;
- *   DFLASH_BUF_SEL_VALS  (DFlash2) float [n_seqs*(gamma-1)][16]: their logits. */
+ *   DFLASH_BUF_SEL_VALS  (DFlash2) float [n_seqs*(gamma-1)][16]: their logits;
+ *   DFLASH_BUF_CTX_FEAT, DFLASH_BUF_CTX_FEAT_LO  bf16 [2048][hidden]: the context features
+ *                        F = hidden_norm(H fc^T) of the last append's last (at most
+ *                        2048-row) launch chunk, rows in order, as high + low bf16 terms;
+ * and, once dflash_debug_capture has turned capture on, the per-layer intermediates of the
+ * last forward, each [num_layers][max_batch * gamma_max][width], rows of layer l at
+ * l * max_batch * gamma_max, the call's rows first (band b's row i at b * gamma + i):
+ *   DFLASH_BUF_LAYER_Q, _Q_LO       bf16, width num_q_heads*head_dim: Q after q_norm and RoPE
+ *                                   (times the YaRN mscale), high and low terms;
+ *   DFLASH_BUF_LAYER_ATTN, _ATTN_LO bf16, width num_q_heads*head_dim: the attention output
+ *                                   (before o_proj), high and low terms;
+ *   DFLASH_BUF_LAYER_X1  float, width hidden: the residual after the attention block;
+ *   DFLASH_BUF_LAYER_X   float, width hidden: the layer's output (residual after the MLP). */
 enum { DFLASH_BUF_POOL = 0, DFLASH_BUF_KPOS = 1, DFLASH_BUF_SLOTS = 2,
        DFLASH_BUF_BLOCKTAB = 3, DFLASH_BUF_HIDDEN = 4, DFLASH_BUF_HIDDEN_LO = 5,
        DFLASH_BUF_FP8_LMHEAD = 6, DFLASH_BUF_FP8_LMHEAD_SCALE = 7, DFLASH_BUF_SEL_IDX = 8,
-       DFLASH_BUF_SEL_VALS = 9 };
+       DFLASH_BUF_SEL_VALS = 9, DFLASH_BUF_CTX_FEAT = 10, DFLASH_BUF_CTX_FEAT_LO = 11,
+       DFLASH_BUF_LAYER_Q = 12, DFLASH_BUF_LAYER_Q_LO = 13, DFLASH_BUF_LAYER_ATTN = 14,
+       DFLASH_BUF_LAYER_ATTN_LO = 15, DFLASH_BUF_LAYER_X1 = 16, DFLASH_BUF_LAYER_X = 17 };
 int dflash_debug_copy(dflash_ctx *ctx, int32_t buffer, void *dst, size_t offset, size_t bytes,
                       void *stream);
+
+/* Test seam (memra_engine/dflash.rs, DflashDraft::forward_block: its per-layer dumps of q,
+ * attn, x1 and every layer's output for parity against a reference): on != 0 makes every
+ * later dflash_block_forward also copy each layer's Q, attention output and residuals into
+ * capture buffers (allocated here on first use, ENOMEM if that fails) that dflash_debug_copy
+ * reads; 0 stops the copies. The copies are stream-ordered device-to-device copies and change
+ * no result. dflash_block_forward_noalloc never captures. */
+int dflash_debug_capture(dflash_ctx *ctx, int32_t on);
 
 /* ---- kernel timing ------------------------------------------------------------------
  * Launch classes of the append and forward sequences. With timing on, every launch of a

@@ -455,7 +455,7 @@ class Drafter:
     # -- one gamma block ------------------------------------------------------------
 
     def block_forward(self, ctx_k, ctx_v, ctx_pos, bonus: int, q_rope_pos: int, gamma: int,
-                      want_hidden: bool = False, markov_prev=None):
+                      want_hidden: bool = False, markov_prev=None, capture=None):
         """One band: block [bonus, mask x (gamma-1)] through every layer, final norm,
         lm_head on rows 1..gamma-1, argmax.
 
@@ -468,7 +468,7 @@ class Drafter:
         toks = np.full(gamma, self.m["mask_token_id"], dtype=np.int64)
         toks[0] = bonus
         bpos = q_rope_pos + np.arange(gamma, dtype=np.int64)
-        y = self.block_hidden(ctx_k, ctx_v, ctx_pos, toks, bpos)
+        y = self.block_hidden(ctx_k, ctx_v, ctx_pos, toks, bpos, capture=capture)
         logits = self.lm_head(y[1:])
         extra = {}
         if self.m.get("markov_rank", 0):
@@ -573,7 +573,7 @@ class Drafter:
             t = int(drafts[r])
         return drafts, dict(cand=cand, cand_logits=vals, sel_h=H, scores=scores)
 
-    def block_hidden(self, ctx_k, ctx_v, ctx_pos, toks, bpos):
+    def block_hidden(self, ctx_k, ctx_v, ctx_pos, toks, bpos, capture=None):
         """Final-normed hidden rows [T, h] of a block with explicit token ids `toks` [T]
         at explicit positions `bpos` [T]; the gamma-block forward calls it with
         [bonus, mask x (gamma-1)] at q_rope_pos + i. Keys are the context keys followed by
@@ -581,6 +581,11 @@ class Drafter:
         [memra] DflashDraft::forward_round: per layer input_layernorm on block rows,
         q/k/v projections, per-head q_norm / k_norm, RoPE, attention over context + block,
         o_proj + residual, post_attention_layernorm, SwiGLU MLP + residual; final norm.
+
+        capture: an optional list that receives, per layer, the intermediates [memra]
+        DflashDraft::forward_block dumps for parity runs: q (after q_norm, RoPE and mscale,
+        [T, nh, hd]), the block's k and v as cached, the attention output [T, nh*hd], x1 (the
+        residual after attention) and x (the layer output). Recording them changes nothing.
         """
         m = self.m
         h, nh, nkv, hd = m["hidden"], m["num_q_heads"], m["num_kv_heads"], m["head_dim"]
@@ -613,6 +618,8 @@ class Drafter:
             u = x1n @ self.flw(l, "up_proj").T
             mo = (silu(g) * u) @ self.flw(l, "down_proj").T
             x = x1 + (self.dconv_finish(mo, kern_m) if d2 else mo)
+            if capture is not None:
+                capture.append(dict(q=q, k=k_all[-gamma:], v=v_all[-gamma:], attn=attn, x1=x1, x=x))
         return rms_norm(x, self.w("norm"), eps)
 
     def lm_head(self, y: np.ndarray, chunk: int = 16384) -> np.ndarray:
@@ -744,7 +751,8 @@ class Engine:
             r += c
         self.last_slots = np.concatenate(slots)
 
-    def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False, markov_prev=None):
+    def block_forward(self, seqs, bonus, q_rope_pos=None, gamma=None, want_hidden=False, markov_prev=None,
+                      capture=False):
         """The C ABI's block forward over bands `seqs`. markov_prev (DSpark and DFlash2
         heads): optional [n, gamma-1] previous tokens per band for the Markov chain or the
         selector walk (teacher forcing; see Drafter.markov_chain, Drafter.selector_walk)."""
@@ -769,14 +777,17 @@ class Engine:
             self.pool.ensure(x, C + gamma)
             slots.append(self.pool.slots(x, range(C, C + gamma)))
         self.last_slots = np.concatenate(slots)
-        outs = []
+        outs, caps = [], []
         for i, x in enumerate(seqs):
             s = self.seqs[x]
             C = self.kv_len(x)
             P = C if q_rope_pos is None else int(q_rope_pos[i])
+            cap = [] if capture else None
             outs.append(self.d.block_forward(s["k"], s["v"], s["pos"], int(bonus[i]), P, gamma,
                                              want_hidden=want_hidden,
-                                             markov_prev=None if markov_prev is None else markov_prev[i]))
+                                             markov_prev=None if markov_prev is None else markov_prev[i],
+                                             capture=cap))
+            caps.append(cap)
         res = dict(tokens=np.stack([o["tokens"] for o in outs]),
                    logits=np.stack([o["logits"] for o in outs]))
         for key in ("cand", "cand_logits", "sel_h", "scores"):
@@ -784,4 +795,6 @@ class Engine:
                 res[key] = np.stack([o[key] for o in outs])
         if want_hidden:
             res["hidden"] = np.stack([o["hidden"] for o in outs])
+        if capture:
+            res["layers"] = caps   # [band][layer] dicts of Drafter.block_hidden's capture
         return res

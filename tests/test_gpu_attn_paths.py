@@ -62,3 +62,42 @@ def test_mixed_paths_parity_and_band_invariance(window):
     print(f"attention paths (window {window}): {agree.n} positions, agreement {rate:.4f}, "
           f"max rel dlogit {agree.max_rel:.3e}")
     pair.close()
+
+
+# A drafter made for fewer than 8 sequences keeps every band on the register path, whose chunk
+# plan widens chunks in 16-page steps so a band never has more than 32: 9000 keys take 32-page
+# chunks (18 of them), 16400 keys (the wide drafter's full-attention layer) 48-page chunks (22),
+# 24000 keys 48-page chunks (32, the cap; the last one partial).
+WIDE_LENS = [8984, 16384, 23984]
+
+
+@pytest.mark.parametrize("window", [0, 5000])
+def test_widened_register_chunks_parity_and_band_invariance(window):
+    m = _model(window)
+    W = synth.gen_weights(m, SEED + 1)
+    nb = len(WIDE_LENS)
+    max_seq = max(WIDE_LENS) + 64
+    pair = Pair(m, W, max_seq, 4,
+                page_order=synth.gen_page_order(O.pool_pages(max_seq, 16, 4)[1] - 1, SEED + 1))
+    for s, n in enumerate(WIDE_LENS):
+        pair.append(s, synth.gen_hidden(m, SEED + 1, n, 90 + s))
+    agree = Agreement()
+    V = m["vocab"]
+    for call, gamma in enumerate([16, 9, 16]):
+        bonus = synth.gen_bonus(m, SEED + 1, nb, index=20 * call + (window > 0))
+        seqs = list(range(nb))[::-1] if call == 1 else list(range(nb))
+        qpos = [WIDE_LENS[s] + 40 * call for s in seqs] if call == 2 else None
+        toks, logits, ref = pair.forward(seqs, bonus, q_rope_pos=qpos, gamma=gamma)
+        agree.add(toks, logits, ref)
+        for i, s in enumerate(seqs):
+            t1 = torch.empty((1, gamma - 1), dtype=torch.int32, device=DEV)
+            l1 = torch.empty((gamma - 1, V), dtype=torch.float32, device=DEV)
+            pair.gpu.dflash_block_forward([s], [bonus[i]], t1, l1, q_rope_pos=None if qpos is None else [qpos[i]],
+                                          gamma=gamma)
+            torch.cuda.synchronize()
+            assert np.array_equal(t1[0].cpu().numpy(), toks[i]), f"band {s} (C={WIDE_LENS[s]}) drafts"
+            assert np.array_equal(l1.cpu().numpy().astype(np.float64), logits[i]), f"band {s} logits"
+    rate = agree.check(min_positions=80)
+    print(f"widened register chunks (window {window}): {agree.n} positions, agreement {rate:.4f}, "
+          f"max rel dlogit {agree.max_rel:.3e}")
+    pair.close()

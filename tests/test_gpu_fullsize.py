@@ -51,8 +51,8 @@ def test_ctx4096_batch1_parity(qwen3):
 
 
 def test_batch16_forward_parity_short_contexts(qwen3):
-    """The 16-band forward (256 rows: several skinny-GEMM row groups, 16 attention bands) on
-    non-contiguous pages, against the oracle, at contexts it computes in seconds."""
+    """The 16-band forward (256 rows: the wide GEMMs and the wide lm_head, 16 attention bands)
+    on non-contiguous pages, against the oracle, at short contexts."""
     m, W, seed = qwen3
     nb = 16
     max_seq = 512
@@ -66,6 +66,32 @@ def test_batch16_forward_parity_short_contexts(qwen3):
     agree.add(toks, logits, ref)
     rate = agree.check(min_positions=200)
     print(f"batch16 parity: {agree.n} positions, agreement {rate:.4f}, max rel dlogit {agree.max_rel:.3e}")
+    pair.close()
+
+
+def test_batch16_workload_contexts_parity_64_blocks(qwen3):
+    """The batched workload itself: 16 sequences with contexts U{512..8192} from its seed on a
+    permuted pool (bands of more than 2048 keys take the attention's LDS path), four 16-band
+    forwards (64 blocks) against the oracle, pooled; the calls vary bonus tokens, band order,
+    block width and RoPE positions past kv_len."""
+    m, W, _ = qwen3
+    w = synth.workload("qwen3-L8-h2048-b16-ctx512to8192")
+    nb, seed = w["batch"], w["seed"]
+    lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, seed)
+    max_seq = w["max_seq_len"]
+    pair = Pair(m, W, max_seq, nb, page_order=synth.gen_page_order(O.pool_pages(max_seq, 16, nb)[1] - 1, seed))
+    for s in range(nb):
+        pair.append(s, synth.gen_hidden(m, seed, int(lens[s]), s))
+    print(f"appended {int(lens.sum())} rows over {nb} sequences on both sides", flush=True)
+    agree = Agreement()
+    for call in range(4):
+        seqs = list(range(nb))[::-1] if call % 2 else list(range(nb))
+        qpos = [int(lens[s]) + 9 * call for s in seqs] if call == 3 else None
+        toks, logits, ref = pair.forward(seqs, synth.gen_bonus(m, seed, nb, index=600 + call), q_rope_pos=qpos)
+        agree.add(toks, logits, ref)
+        print(f"call {call}: {agree.n} positions, max rel dlogit {agree.max_rel:.3e}", flush=True)
+    rate = agree.check(min_positions=900)
+    print(f"batch16 workload parity: {agree.n} positions, agreement {rate:.4f}, max rel dlogit {agree.max_rel:.3e}")
     pair.close()
 
 

@@ -493,6 +493,31 @@ def test_chunked_lm_head_equals_cached_and_scalar_dots(tiny, fmt):
     assert np.array_equal(r1["tokens"], r2["tokens"])
 
 
+def test_layer_capture_records_the_forward_and_changes_nothing(tiny):
+    """The opt-in per-layer capture (the parity seam's dumps) leaves the forward unchanged,
+    and what it records fits together: x1 = previous layer output + attn o_proj^T, the last
+    layer's output through the final norm and lm_head gives the logits, and the captured
+    block K/V are what the forward left as the block's keys."""
+    m, W = tiny
+    e = _engine_with_ctx(m, W)
+    plain = e.block_forward([0], [11], gamma=16)
+    r = e.block_forward([0], [11], gamma=16, capture=True, want_hidden=True)
+    assert np.array_equal(plain["logits"], r["logits"]) and np.array_equal(plain["tokens"], r["tokens"])
+    layers = r["layers"][0]
+    assert len(layers) == m["num_layers"]
+    x_prev = O.widen(W["embed_tokens"][[11] + [m["mask_token_id"]] * 15])
+    for l, c in enumerate(layers):
+        assert c["q"].shape == (16, m["num_q_heads"], m["head_dim"])
+        assert c["k"].shape == c["v"].shape == (16, m["num_kv_heads"], m["head_dim"])
+        o = c["attn"] @ O.widen(W[f"layers.{l}.o_proj"]).T
+        assert np.allclose(c["x1"], x_prev + o, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(c["k"], O.round_bf16(c["k"]))     # cached K/V are bf16 values
+        x_prev = c["x"]
+    y = O.rms_norm(layers[-1]["x"], O.widen(W["norm"]), m["rms_eps"])
+    assert np.allclose(y, r["hidden"][0], rtol=1e-12, atol=1e-12)
+    assert np.allclose(y[1:] @ O.widen(W["lm_head"]).T, r["logits"][0], rtol=1e-10, atol=1e-10)
+
+
 def test_engine_errors_leave_state_unchanged(tiny):
     m, W = tiny
     e = O.Engine(m, W, 40, 2)
