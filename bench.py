@@ -32,6 +32,8 @@ METRIC = "drafted γ=16 blocks/sec at batch 1 and 16; achieved HBM GB/s vs peak"
 WORKLOAD = "qwen3-L8-h2048-ctx4096-b1"
 WORKLOAD_B16 = "qwen3-L8-h2048-b16-ctx512to8192"
 WORKLOAD_LONG = "qwen3-L8-h2048-b32-ctx8192to32768-append2048"
+WORKLOAD_WIDE = "wide-L5-h5376-yarn-swa2048-ctx16384-b1"
+WORKLOAD_TINY = "tiny-L2-h256-ctx64-b1"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -98,9 +100,18 @@ def lmhead_bytes(m, M, fp8=False):
 
 
 def attn_bytes(m, kv_lens, gamma):
-    """K and V bytes every layer reads: (C + gamma) keys per band, both halves, all kv heads."""
+    """K and V bytes the layers read: per band, the keys visible to the block (every key, C +
+    gamma, in full-attention layers; in sliding layers the keys within the window of block
+    row 0, min(C, W - 1) context keys + gamma, with default positions), both halves, all kv
+    heads."""
     kvd = m["num_kv_heads"] * m["head_dim"]
-    return sum((c + gamma) for c in kv_lens) * kvd * 2 * 2 * m["num_layers"]
+    win = int(m.get("sliding_window") or 0)
+    sl = m.get("layer_sliding") or [False] * m["num_layers"]
+    keys = 0
+    for l in range(m["num_layers"]):
+        for c in kv_lens:
+            keys += (min(c, win - 1) if (win and sl[l]) else c) + gamma
+    return keys * kvd * 2 * 2
 
 
 def forward_bytes(m, kv_lens, gamma):
@@ -140,30 +151,89 @@ def cpu_model():
     return "unknown"
 
 
-def run_cpu_baseline(m, W, H_ctx, H_steps, bonus, a, gamma, budget_s):
-    """The oracle as it stands, on this host: untimed prefill + fp64 weight widening, then
-    steps (append a rows + one block forward) until `budget_s` of timed work."""
-    from oracle import dflash_oracle as O
-    eng = O.Engine(m, W, H_ctx.shape[0] + 64 * a + gamma + 16, 1)
-    eng.ctx_kv_append(0, H_ctx)
-    for n, _, _ in __import__("synth").weight_specs(m):
-        eng.d.w(n)
+def _oracle_steps(step, budget_s, n_max):
+    """Run step(i) until budget_s seconds of it have run (at least once, at most n_max)."""
     t0 = time.perf_counter()
     n = 0
-    n_max = min(64, H_steps.shape[0] // a, len(bonus))
     while True:
-        eng.ctx_kv_append(0, H_steps[n * a:(n + 1) * a])
-        eng.block_forward([0], [int(bonus[n])], gamma=gamma)
+        step(n)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= n_max:
-            break
+            return n, el
+
+
+def cpu_baseline_config(name, m, W, dtype, budget_s, a, gamma, H_app=None):
+    """The oracle as it stands on this host for one workload and precision: an untimed prefill
+    of the workload's contexts (seeded draws) and weight widening, then timed steps. A step is
+    what the GPU line times: an `a`-row context append per sequence (the batched append for
+    the 16-band workload) and one gamma-block forward over every sequence; for the long-context
+    workload, one sequence's 2048-row append and its block forward."""
+    import numpy as np
+
+    import synth
+    from oracle import dflash_oracle as O
+    w = synth.workload(name)
+    seed, nb = w["seed"], w["batch"]
+    lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, seed)
+    t_setup = time.perf_counter()
+    if name == WORKLOAD_LONG:
+        nb = 1   # one sequence of the workload, labelled per sequence
+    max_seq = int(lens[:nb].max()) + 64 * a + 2048 + gamma + 16
+    eng = O.Engine(m, W, max_seq, nb, dtype=dtype)
+    for s in range(nb):
+        for c, r0 in enumerate(range(0, int(lens[s]), 2048)):
+            eng.ctx_kv_append(s, synth.gen_hidden(m, seed, min(2048, int(lens[s]) - r0), 1000 * s + c))
+    for n_, _, _ in synth.weight_specs(m):
+        if n_ != "embed_tokens":
+            eng.d.w(n_)
+    setup_s = time.perf_counter() - t_setup
+    seqs = list(range(nb))
+    bonus = synth.gen_bonus(m, seed, 64 * nb, index=5)
+    if name == WORKLOAD_LONG:
+        Hl = synth.gen_hidden(m, seed, w["append"], 999)
+
+        def step(i):
+            eng.ctx_kv_append(0, Hl)
+            eng.block_forward([0], [int(bonus[i])], gamma=gamma)
+        n, el = _oracle_steps(step, budget_s, 1)
+        unit, value = "sequences/s", n / el
+        what = (f"one sequence of the workload (context {int(lens[0])}): its 2048-row append and one block "
+                f"forward per step")
+    else:
+        Hs = synth.gen_hidden(m, seed, 64 * nb * a, 7)
+
+        def step(i):
+            rows = Hs[i * nb * a:(i + 1) * nb * a]
+            if nb > 1:
+                eng.ctx_kv_append_batch(seqs, [a] * nb, rows)
+            else:
+                eng.ctx_kv_append(0, rows)
+            eng.block_forward(seqs, [int(b) for b in bonus[i * nb:(i + 1) * nb]], gamma=gamma)
+        n, el = _oracle_steps(step, budget_s, 64)
+        unit, value = "blocks/s", n * nb / el
+        what = f"{n} steps ({a}-row append per sequence + one {nb}-band gamma={gamma} forward)"
+    return dict(workload=name, dtype=np.dtype(dtype).name, value=round(value, 4), unit=unit, steps=n,
+                seconds=round(el, 3), setup_seconds=round(setup_s, 1), sample=what)
+
+
+def run_cpu_baseline(configs, budget_s, a, gamma):
+    """The oracle on every workload in float64 (its parity mode) and float32; `configs` maps a
+    workload name to (model, weights). The headline entry is the batch-1 workload in float64."""
+    import numpy as np
     thr, api = blas_threads()
-    return dict(value=n / el, unit="blocks/s", cores=thr, kind="oracle",
-                sample=f"{n} steps ({a}-row context append + one gamma={gamma} block forward) of the "
-                       f"same workload after an untimed {H_ctx.shape[0]}-row prefill and fp64 weight "
-                       f"widening; numpy float64, BLAS={api}; host CPU: {cpu_model()}",
-                seconds=el)
+    entries = []
+    for name, (m, W) in configs.items():
+        for dt in (np.float64, np.float32):
+            e = cpu_baseline_config(name, m, W, dt, budget_s, a, gamma)
+            log(f"[bench] cpu oracle {name} {e['dtype']}: {e['value']} {e['unit']} "
+                f"({e['seconds']} s timed, {e['setup_seconds']} s setup)")
+            entries.append(e)
+    head = next(e for e in entries if e["workload"] == WORKLOAD and e["dtype"] == "float64")
+    return dict(value=head["value"], unit="blocks/s", cores=thr, kind="oracle",
+                sample=f"{head['sample']} of {WORKLOAD} after an untimed prefill of its context and weight "
+                       f"widening; numpy float64, BLAS={api} on {thr} threads; host CPU: {cpu_model()}",
+                seconds=head["seconds"], by_config=entries)
 
 
 def main():
@@ -172,8 +242,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--append-rows", type=int, default=16)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="timed budget of the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="timed budget of the oracle baseline, per workload and precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-quick", action="store_true", help="oracle baseline on the batch-1 workload only")
+    ap.add_argument("--no-wide", action="store_true", help="skip the wide-drafter line")
     ap.add_argument("--no-batch16", action="store_true")
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 E4M3 weight-only lines")
@@ -350,9 +423,20 @@ def main():
             out["dflash2"]["batch16"] = bench_batch16(m2, Wd2, gamma, a, args, B, torch, np, synth, to_dev)
         del Wd2
 
+    W_wide = None
+    if not args.no_wide:
+        del Wd
+        out["wide"], W_wide = bench_wide(a, args, B, torch, np, synth, to_dev)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        out["cpu_baseline"] = run_cpu_baseline(m, W, H_ctx, H_steps, bonus, a, gamma, args.cpu_seconds)
+        configs = {WORKLOAD_TINY: None, WORKLOAD: (m, W), WORKLOAD_B16: (m, W), WORKLOAD_LONG: (m, W)}
+        mt = synth.model("tiny-L2-h256")
+        configs[WORKLOAD_TINY] = (mt, synth.gen_weights(mt, synth.workload(WORKLOAD_TINY)["seed"]))
+        if W_wide is not None:
+            configs[WORKLOAD_WIDE] = (synth.model("wide-L5-h5376-yarn-swa2048"), W_wide)
+        if args.cpu_quick:
+            configs = {WORKLOAD: configs[WORKLOAD]}
+        out["cpu_baseline"] = run_cpu_baseline(configs, args.cpu_seconds, a, gamma)
     print(json.dumps(out), flush=True)
 
 
@@ -564,6 +648,76 @@ def bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev):
                 attention=dict(bound="hbm", kv_bytes_per_forward=int(kv_bytes), ms_per_forward=round(attn_ms, 4),
                                launches_per_forward=attn[1] / reps, achieved=round(attn_gbs, 1),
                                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(attn_gbs / HBM_PEAK_GBS, 4)))
+
+
+def bench_wide(a, args, B, torch, np, synth, to_dev):
+    """The wide drafter (5 layers, hidden 5376, GQA 64:8, ff 10752, vocab 262144, YaRN, window
+    2048 on layers 0-3) at batch 1 on a 16384-row context (prefilled untimed): a step is an
+    `a`-row append and one block forward. Plain launches give blocks/s; a second pass with every
+    launch bracketed by events gives the per-class times and the weight-stream rates of the
+    layer GEMMs and the 2.8 GB lm_head, and the attention's K/V bytes per second."""
+    w = synth.workload(WORKLOAD_WIDE)
+    m, seed = w["model_cfg"], w["seed"]
+    gamma = m["gamma_max"]
+    t = time.perf_counter()
+    W = synth.gen_weights(m, seed)
+    Wd = {k: to_dev(v) for k, v in W.items()}
+    ctx = w["ctx"][0]
+    steps = max(5, args.steps // 2)
+    total = args.warmup + 2 * steps
+    d = B.Drafter(m, Wd, ctx + total * a + gamma + 16, 1)
+    for c, r0 in enumerate(range(0, ctx, 2048)):
+        d.dflash_ctx_kv_append(0, to_dev(synth.gen_hidden(m, seed, min(2048, ctx - r0), c)))
+    Hs = to_dev(synth.gen_hidden(m, seed, total * a, 100))
+    bonus = synth.gen_bonus(m, seed, total)
+    toks = torch.empty((1, gamma - 1), dtype=torch.int32, device="cuda:0")
+    torch.cuda.synchronize()
+    log(f"[bench] wide: weights and {ctx}-row prefill in {time.perf_counter() - t:.1f}s")
+    step_i = [0]
+
+    def step():
+        i = step_i[0]
+        d.dflash_ctx_kv_append(0, Hs[i * a:(i + 1) * a])
+        d.dflash_block_forward([0], [int(bonus[i])], toks, gamma=gamma)
+        step_i[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kv0 = d.dflash_seq_info(0)[0]
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kv1 = d.dflash_seq_info(0)[0]
+    d.dflash_timing(list(B.K_CLASSES))
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    br = d.dflash_timing_read()
+    d.dflash_timing([])
+    d.close()
+    ms = {k: v[0] / steps for k, v in br.items() if v[1]}
+    blocks = steps / el
+    mean_kv = (kv0 + kv1) / 2 + a / 2
+    rates = {}
+    for k, nbytes in (("gemm", gemm_bytes(m, gamma)), ("lmhead", lmhead_bytes(m, gamma)),
+                      ("attn", attn_bytes(m, [mean_kv], gamma))):
+        if k in ms:
+            g = nbytes / (ms[k] * 1e-3) / 1e9
+            rates[k] = dict(algorithmic_bytes_per_step=int(nbytes), ms_per_step=round(ms[k], 4), gbs=round(g, 1),
+                            frac=round(g / HBM_PEAK_GBS, 4),
+                            avg_launch_us=round(br[k][0] / br[k][1] * 1e3, 3), launches_per_step=br[k][1] / steps)
+    step_bytes = forward_bytes(m, [mean_kv], gamma) + append_bytes(m, a)
+    log(f"[bench] wide batch1: {blocks:.1f} blocks/s, {el / steps * 1e3:.3f} ms/step; "
+        + ", ".join(f"{k} {v['gbs']:.0f} GB/s" for k, v in rates.items()))
+    return dict(workload=WORKLOAD_WIDE, value=round(blocks, 2), unit="blocks/s", steps=steps,
+                ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
+                step_algorithmic_bytes=int(step_bytes),
+                step_gbs=round(step_bytes / (el / steps) / 1e9, 1), streams=rates,
+                kernels_ms_per_step={k: round(v, 4) for k, v in ms.items()},
+                timing="value from plain launches; per-class times from a second, bracketed pass"), W
 
 
 if __name__ == "__main__":
