@@ -254,6 +254,8 @@ def main():
     ap.add_argument("--no-dflash2", action="store_true", help="skip the DFlash2 lines")
     ap.add_argument("--longctx-only", action="store_true",
                     help="only run the 32-sequence long-context section and print its JSON (for counter runs)")
+    ap.add_argument("--batch16-only", action="store_true",
+                    help="only run the 16-sequence batched section and print its JSON (for counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 20 plain device-to-device copies of MIB MiB (the reference for "
                          "scaling the HBM traffic counters) and exit")
@@ -300,6 +302,9 @@ def main():
     Wd = {k: to_dev(v) for k, v in W.items()}
     if args.longctx_only:
         print(json.dumps(bench_longctx(m, Wd, gamma, B, torch, np, synth, to_dev)), flush=True)
+        return
+    if args.batch16_only:
+        print(json.dumps(bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev)), flush=True)
         return
     max_seq = ctx + total * a + gamma + 16
     d = B.Drafter(m, Wd, max_seq, 1)

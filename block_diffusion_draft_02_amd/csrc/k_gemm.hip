@@ -432,22 +432,28 @@ hipError_t launch_gemm_skinny(const bf16* A, const bf16* A_lo, int lda, int M, c
 
 // ---------------------------------------------------------------------------------------
 // Wide form for many rows (the batched forward): one workgroup computes WD_M rows x WD_N
-// columns. Activation chunks (hi and lo, WD_KC deep) are staged through LDS, double
-// buffered and shared by the four waves; wave w owns columns [32w, 32w + 32) as two T16
-// tiles and loads their weight operands straight into registers (every load one contiguous
-// 1 KB run), one chunk ahead. Per output element the MFMA sequence is the skinny kernels':
-// 256-deep chains from zero, each 32-deep step one MFMA on the hi term, then one on the lo
-// term.
+// columns; wave w owns columns [32w, 32w + 32) as two T16 tiles. Per output element the MFMA
+// sequence is the skinny kernels': 256-deep chains from zero, each 32-deep step one MFMA on
+// the hi term, then one on the lo term.
 //  * partial mode (layer GEMMs): the workgroup takes one group of gsz consecutive 256-deep
 //    splits and adds their chains in split order from zero (each times the row's RMSNorm
 //    scale under NORM). That is the group sum the consumers form from the skinny kernel's
 //    per-split partials (sum_splits), so one partial per group is handed over.
 //  * argmax mode (lm_head): one chain over the full K, then per row the best (value, lowest
 //    index) over the workgroup's columns, and optionally the drafted rows' fp32 logits.
-constexpr int WD_M = 64;    // rows per workgroup (four 16-row tiles: three workgroups a CU)
+// Data movement: the k range streams in WD_KC-deep chunks. A chunk's activation rows (hi and
+// lo) go through a ring of WD_NS LDS stages by the gfx950 global->LDS 16-byte load (no
+// registers; each lane picks its source so that unit u of row r lands at unit u ^ ((r >> 1)
+// & 7), which keeps the 16 rows one LDS cycle serves on distinct banks); its weight operands
+// go straight into registers (every load one contiguous 1 KB run), as many chunks ahead.
+// Chunk j + WD_NS - 1 is requested right after the barrier that ends chunk j - 1, and a wave
+// waits only for its own loads of chunk j, so WD_NS - 1 chunks are in flight while one is
+// multiplied.
+constexpr int WD_M = 64;    // rows per workgroup (four 16-row tiles)
 constexpr int WD_N = 128;   // columns per workgroup: 4 waves x 2 tiles
-constexpr int WD_KC = 64;   // depth of one staged activation chunk
-constexpr int WD_APAD = 8;  // LDS row padding: rows 144 B apart keep a 16-lane read conflict-free
+constexpr int WD_KC = 64;   // depth of one chunk
+constexpr int WD_NS = 3;    // chunks in the ring (activation stages in LDS, weight sets in registers)
+static_assert(WD_NS == 3, "the wide kernel's waits and stage rotation are written for three chunks");
 
 // running argmax: a larger value, or an equal one at a lower index, wins (NaN never does)
 __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
@@ -466,22 +472,42 @@ struct WideOut {
   const float* wsc;    // FP8 weights: the per-row scales (padded to whole tiles)
 };
 
+// one ring stage: the activation chunk of WD_M rows, hi and (SPLIT) lo, each row WD_KC deep
+// (8 units of 16 bytes, swizzled)
+template <bool SPLIT>
+struct WideStage {
+  bf16 a[SPLIT ? 2 : 1][WD_M * WD_KC];
+};
+
+// s_waitcnt with vmcnt <= N (vmcnt[3:0] | vmcnt[5:4] << 14; expcnt and lgkmcnt left at maximum)
+#define DFL_WIDE_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+
 // SPLIT: the activation carries a lo term (A_lo); without it A is exact bf16 (the context
 // append's target hidden states) and each step is one MFMA. FP8: W in the T16-FP8 layout
 // (one 16-byte piece per tile and chunk), codes converted to exact bf16 operands in
 // registers, each column scaled by its row scale as the skinny kernel scales it.
+template <bool ARGMAX, bool NORM>
+struct WideLds {
+  float srs[NORM ? WD_M : 1];
+  float sv[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
+  int si[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
+};
+
 template <bool ARGMAX, bool NORM, bool SPLIT, bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(
-    const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda, int M,
-    const bf16* __restrict__ W, int N, int K, int gx, int gy, WideOut o) {
+__device__ __forceinline__ void gemm_wide_wg(WideStage<SPLIT>& st0, WideStage<SPLIT>& st1, WideStage<SPLIT>& st2,
+                                             WideLds<ARGMAX, NORM>& sm,
+                                             const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda,
+                                             int M, const bf16* __restrict__ W, int N, int K, int gx, int gy,
+                                             const WideOut& o) {
   constexpr int WM = WD_M / 16;
-  constexpr int PPR = WD_KC / 8;                 // 16-byte pieces per row and term
-  constexpr int PT = WD_M * PPR / 256;           // pieces per thread and term
-  __shared__ __attribute__((aligned(16))) bf16 sa[2][SPLIT ? 2 : 1][WD_M][WD_KC + WD_APAD];
-  __shared__ float srs[NORM ? WD_M : 1];
-  __shared__ float sv[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
-  __shared__ int si[ARGMAX ? 4 : 1][ARGMAX ? WD_M : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NT = SPLIT ? 2 : 1;          // activation terms
+  constexpr int NWL = FP8 ? 1 : 2;           // weight loads per tile and chunk
+  constexpr int OPS = NT * 2 + 2 * NWL;      // memory instructions a wave issues per chunk
+  auto& srs = sm.srs;
+  auto& sv = sm.sv;
+  auto& si = sm.si;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   // workgroup id -> (column group x, row group y, split group z). Workgroups go to the eight
   // XCDs round robin, so the row groups of one column group get ids 8 apart: one XCD, one
@@ -511,6 +537,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) wsc[FP8 ? nt : 0] = o.wsc[min(tile0 + nt, ntiles - 1) * 16 + c];
   }
+  // this wave's two 1 KB pieces of each activation term of a stage: LDS units
+  // P = (2 wave + h) * 64 + lane, row P / 8 (rows past M repeat the last row; their results
+  // are never stored), source unit (P % 8) ^ ((row >> 1) & 7)
+  // (the lane's part of the address is a loop-invariant element offset: the chunk is chosen by
+  // a uniform base, so no address register is rewritten while a load that read it may be in
+  // flight, which made the compiler wait for every load before reusing it)
+  uint32_t voff[2];   // bytes
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int P = (2 * wave + h) * 64 + lane;
+    const int r = P >> 3, u = (P & 7) ^ ((r >> 1) & 7);
+    voff[h] = (uint32_t)(min(m0 + r, M - 1) * lda + u * 8) * 2u;
+  }
+  const bf16* srcA[NT] = {A + kb};
+  if (SPLIT) srcA[NT - 1] = A_lo + kb;
 
   if (NORM) {
     // the rows' RMSNorm scales, each row's slice sums added as the skinny kernel adds them
@@ -526,40 +567,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
       srs[NORM ? r : 0] = rsqrtf(((s4[0] + s4[1]) + (s4[2] + s4[3])) / (float)o.nrm.h + o.nrm.eps);
     }
+    __syncthreads();   // the scales, before any wave folds a split (and before any DMA is in flight)
   }
 
-  // a chunk's weight operands as raw 16-byte pieces: bf16, one per tile and 32-deep step;
-  // FP8, one per tile (both steps)
-  auto load_w = [&](u32x4 (&w)[2][FP8 ? 1 : 2], int k) {
+  // chunk j's loads: the activation stage (DMA into LDS), then the weight operands as raw
+  // 16-byte pieces (bf16: one per tile and 32-deep step; FP8: one per tile). Every step issues
+  // the same loads: past the last chunk it re-reads the last one (from L2) into a stage and a
+  // weight set nothing reads again, so that the compiler sees one fixed count of loads in
+  // flight (with a conditional issue it waited for every load before each chunk's MFMAs)
+  auto issue = [&](WideStage<SPLIT>& st, u32x4 (&w)[2][NWL], int j) {
+    // (a scalar: kept out of the per-lane address arithmetic)
+    const int k = __builtin_amdgcn_readfirstlane(min(j, nck - 1) * WD_KC);   // relative to kb
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // (the empty asm keeps the 32-bit offset a value of this block, so the load takes the
+        // scalar-base + 32-bit vector-offset form instead of a 64-bit address register)
+        uint32_t vo = voff[h];
+        asm volatile("" : "+v"(vo));
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(srcA[t] + k) + vo,
+                                         st.a[t] + (2 * wave + h) * 512, 16, 0, 0);
+      }
+    const int kk = kb + k;
     if (FP8) {
-      const size_t off = (size_t)(k >> 8) * T16Q_BLOCK + ((k & 255) >> 6) * 1024;
+      const size_t off = (size_t)(kk >> 8) * T16Q_BLOCK + ((kk & 255) >> 6) * 1024;
       w[0][0] = *reinterpret_cast<const u32x4*>(qp0 + off);
       w[1][0] = *reinterpret_cast<const u32x4*>(qp1 + off);
     } else {
-      const size_t off = (size_t)(k >> 8) * T16_BLOCK + ((k & 255) >> 5) * 512;
+      const size_t off = (size_t)(kk >> 8) * T16_BLOCK + ((kk & 255) >> 5) * 512;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        w[0][FP8 ? 0 : s] = *reinterpret_cast<const u32x4*>(wp0 + off + s * 512);
-        w[1][FP8 ? 0 : s] = *reinterpret_cast<const u32x4*>(wp1 + off + s * 512);
+      for (int s = 0; s < NWL; ++s) {
+        w[0][s] = *reinterpret_cast<const u32x4*>(wp0 + off + s * 512);
+        w[1][s] = *reinterpret_cast<const u32x4*>(wp1 + off + s * 512);
       }
-    }
-  };
-  constexpr int NT = SPLIT ? 2 : 1;   // activation terms
-  auto load_a = [&](u32x4 (&ra)[NT][PT], int k) {
-#pragma unroll
-    for (int v = 0; v < PT; ++v) {
-      const int p = threadIdx.x + 256 * v;
-      const size_t src = (size_t)min(m0 + p / PPR, M - 1) * lda + k + (p % PPR) * 8;   // rows >= M repeat the last row
-      ra[0][v] = *reinterpret_cast<const u32x4*>(A + src);
-      if (SPLIT) ra[NT - 1][v] = *reinterpret_cast<const u32x4*>(A_lo + src);
-    }
-  };
-  auto store_a = [&](const u32x4 (&ra)[NT][PT], int buf) {
-#pragma unroll
-    for (int v = 0; v < PT; ++v) {
-      const int p = threadIdx.x + 256 * v;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) *reinterpret_cast<u32x4*>(&sa[buf][t][p / PPR][(p % PPR) * 8]) = ra[t][v];
     }
   };
   f32x4 acc[WM][2];
@@ -571,9 +612,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (!ARGMAX) gs[ARGMAX ? 0 : mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  // one staged chunk: per 32-deep step, the hi MFMAs of every (row tile, column tile), then
-  // the lo ones (per element: hi, then lo, step after step)
-  auto mma = [&](int buf, const u32x4 (&w)[2][FP8 ? 1 : 2]) {
+  // one chunk: per 32-deep step, the hi MFMAs of every (row tile, column tile), then the lo
+  // ones (per element: hi, then lo, step after step)
+  auto mma = [&](const WideStage<SPLIT>& st, const u32x4 (&w)[2][NWL]) {
 #pragma unroll
     for (int s = 0; s < WD_KC / 32; ++s) {
       bf16x8 wv[2];
@@ -583,9 +624,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         bf16x8 av[WM];
+        const bf16* base = st.a[t];
 #pragma unroll
-        for (int mt = 0; mt < WM; ++mt)
-          av[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sa[buf][t][mt * 16 + c][s * 32 + g * 8]));
+        for (int mt = 0; mt < WM; ++mt) {
+          const int r = mt * 16 + c, u = s * 4 + g;
+          av[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + r * WD_KC + ((u ^ ((r >> 1) & 7)) * 8)));
+        }
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
@@ -614,33 +658,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   };
-
-  u32x4 w0[2][FP8 ? 1 : 2], w1[2][FP8 ? 1 : 2];
-  u32x4 ra[NT][PT];
-  load_a(ra, kb);
-  load_w(w0, kb);
-  store_a(ra, 0);
-  __syncthreads();
-  for (int j = 0; j < nck; j += 2) {
-    // chunk j: LDS buffer 0 and w0; the next chunk is requested before it is computed, and
-    // stored into the other buffer (which every wave finished reading before the last barrier)
-    if (j + 1 < nck) {
-      load_a(ra, kb + (j + 1) * WD_KC);
-      load_w(w1, kb + (j + 1) * WD_KC);
-    }
-    mma(0, w0);
+  // chunk j sits in ring stage j % WD_NS and weight set j % WD_NS; on entry to its step the
+  // chunks j .. j + WD_NS - 2 are requested. The wave waits for its own loads of chunk j; the
+  // barrier makes every wave's share of the stage visible and ends every wave's reads of stage
+  // (j - 1) % WD_NS, which chunk j + WD_NS - 1 refills once chunk j's MFMAs are issued (its
+  // weight set was last read by chunk j - 1's MFMAs)
+  u32x4 wr[WD_NS][2][NWL];
+  auto step = [&](int j, WideStage<SPLIT>& cur, const u32x4 (&wc)[2][NWL], WideStage<SPLIT>& nxt,
+                  u32x4 (&wn)[2][NWL]) {
+    DFL_WIDE_WAIT_VM(OPS);   // chunk j + 1's loads may still be in flight
+    __builtin_amdgcn_s_barrier();
+    mma(cur, wc);
+    issue(nxt, wn, j + WD_NS - 1);
     fold(j);
-    if (j + 1 < nck) store_a(ra, 1);
-    __syncthreads();
-    if (j + 1 >= nck) break;
-    if (j + 2 < nck) {
-      load_a(ra, kb + (j + 2) * WD_KC);
-      load_w(w0, kb + (j + 2) * WD_KC);
-    }
-    mma(1, w1);
-    fold(j + 1);
-    if (j + 2 < nck) store_a(ra, 0);
-    __syncthreads();
+  };
+  issue(st0, wr[0], 0);
+  issue(st1, wr[1], 1);
+  for (int j = 0; j < nck; j += WD_NS) {
+    step(j, st0, wr[0], st2, wr[2]);
+    if (j + 1 < nck) step(j + 1, st1, wr[1], st0, wr[0]);
+    if (j + 2 < nck) step(j + 2, st2, wr[2], st1, wr[1]);
   }
 
   if (!ARGMAX) {
@@ -703,6 +740,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       o.best_i[(size_t)(m0 + r) * o.n_groups + x] = bi;
     }
   }
+}
+
+template <bool ARGMAX, bool NORM, bool SPLIT, bool FP8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_wide(
+    const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda, int M,
+    const bf16* __restrict__ W, int N, int K, int gx, int gy, WideOut o) {
+  // the ring's stages are separate LDS objects: the compiler then knows that a stage's reads
+  // do not alias the loads in flight into the others (one array made it wait for every load
+  // before the first read of each chunk)
+  __shared__ __attribute__((aligned(16))) WideStage<SPLIT> st0, st1, st2;
+  __shared__ WideLds<ARGMAX, NORM> sm;
+  gemm_wide_wg<ARGMAX, NORM, SPLIT, FP8>(st0, st1, st2, sm, A, A_lo, lda, M, W, N, K, gx, gy, o);
 }
 
 static unsigned wide_grid(int gx, int gy, int gz) { return (unsigned)((gx + 7) / 8 * 8) * gy * gz; }
