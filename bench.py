@@ -56,13 +56,13 @@ def gemm_bytes(m, M, fp8=False):
 # HBM bytes per launch of the forward's layer GEMMs (k_gemm_split, mean over
 # the QKV, O, gate/up and down shapes), from `rocprofv3 --pmc FETCH_SIZE` and
 # `--pmc WRITE_SIZE` runs of `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-batch16
-# --no-longctx --no-fp8 --no-dspark --no-dflash2`, scaled by what the same counters read for
+# --no-longctx --no-fp8 --no-dspark --no-dflash2 --no-wide`, scaled by what the same counters read for
 # 20 plain 256 MiB device copies (`bench.py --calibrate-copy 256`: FETCH_SIZE 0.500 of the
 # bytes read, WRITE_SIZE 1.000 of the bytes written). Valid only for the kernel source they
 # were taken on.
 TRAFFIC = {
     "gemm": dict(source="block_diffusion_draft_02_amd/csrc/k_gemm.hip",
-                 sha256="06d2d180beb322cc28cd2c6e9944cd4a3b990c00a1bc8e2ac35d191410d4013e",
+                 sha256="44617ab29dc69c5bc9f5e49c4970ef7a25b300b0908646e0415cdde03a2ab183",
                  fetch_bytes=30.19e6, write_bytes=3.540e6),
 }
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
-SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_markov.hip", "k_dflash2.hip", "runtime.hip"]
+SOURCES = ["k_gemm.hip", "k_gemm_wide.hip", "k_gemm_tiled.hip", "k_attn.hip", "k_misc.hip", "k_markov.hip", "k_dflash2.hip", "runtime.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -55,7 +55,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     # -z defs: a symbol no object defines fails the link, not the first load

@@ -29,6 +29,20 @@ constexpr int MAX_BANDS = 32;     // sequences in one forward call
 constexpr int APPEND_ROWS = 2048; // context rows per append launch sequence
 constexpr int APPEND_PAGES = APPEND_ROWS / PAGE + 1;
 
+// T16 weight layout (the forward's GEMMs and the lm_head): the rows of a [N, K] weight go
+// in tiles of 16; a tile's K is a run of 256-deep blocks, and a block holds its 16 x 256
+// values as 8 x 64 16-byte pieces in exactly the order the 64 lanes of a wavefront load them
+// (piece (u, lane) = row lane%16, k = u*32 + (lane/16)*8 .. +7). A tile is then 16*K
+// contiguous values, and every load instruction of a wavefront reads 1 KB in one run.
+constexpr int T16_BLOCK = 16 * 256;
+
+// FP8 weights: OCP E4M3 codes with one fp32 scale per row (weight = code value x scale), in
+// the T16-FP8 layout: the rows go in tiles of 16, a tile's K in 256-deep blocks of 4 KB, and a
+// block holds 4 x 64 16-byte pieces in the order the lanes load them: piece (q, lane) is row
+// lane % 16, the 8 codes of k = 64q + 8g .. (the lane's operand of 32-deep step 2q, g = lane/16)
+// followed by the 8 codes of k = 64q + 32 + 8g .. (step 2q + 1).
+constexpr int T16Q_BLOCK = 16 * 256;   // bytes of one 256-deep block of a tile
+
 // One band (sequence) of a forward call, as the kernels see it.
 struct Band {
   int seq;       // sequence slot
@@ -108,7 +122,7 @@ struct KvGeom {
 
 __host__ __device__ inline size_t page_layer_elems(int nkv, int hd) { return (size_t)2 * nkv * PAGE * hd; }
 
-// ---- GEMMs (k_gemm.hip) --------------------------------------------------------------
+// ---- GEMMs (k_gemm.hip, k_gemm_wide.hip, k_gemm_tiled.hip) ----------------------------
 // Y[M,N] = A[M,K] W[N,K]^T where the activation A = A_hi + A_lo is carried as two bf16
 // terms (each k-step issues two MFMAs). Skinny form: partials P[s][M][N] over K splits of
 // k_len (k_len, K multiples of 256); M <= 64 per launch. W is row-major, or (w_tiled) in the
