@@ -3,6 +3,9 @@
     python -m block_diffusion_draft_02_amd.build        # or build() from Python
 
 Objects go to _build/ at the repository root; the shared library lands next to this file.
+build_host_check() also links tests/host/abi_check: the runtime's host code compiled with
+AddressSanitizer and UndefinedBehaviorSanitizer (the host pass only), the library's kernel
+objects as they are, and a driver that calls every entry point.
 """
 from __future__ import annotations
 
@@ -69,5 +72,51 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+HOST_CHECK_DIR = os.path.join(ROOT, "tests", "host")
+HOST_CHECK = os.path.join(HOST_CHECK_DIR, "abi_check")
+# sanitizers for the host compilation pass only (device code is built as in the library)
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+LINK_SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def clangxx() -> str:
+    for c in ("/opt/rocm/llvm/bin/clang++", shutil.which("amdclang++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("clang++ of the ROCm toolchain not found")
+
+
+def _run(cmd, what):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{what} failed: {' '.join(cmd)}\n{_quiet(r.stdout + r.stderr)}")
+
+
+def build_host_check(verbose: bool = True) -> str:
+    os.makedirs(os.path.join(BUILD, "san"), exist_ok=True)
+    kernels = [s for s in SOURCES if s != "runtime.hip"]
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in kernels]
+    if not all(os.path.exists(o) for o in objs):
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(kernels))) as ex:
+            objs = list(ex.map(_compile, kernels))
+    rt = os.path.join(BUILD, "san", "runtime.o")
+    _run([hipcc(), *FLAGS, "-O1", "-g", *HOST_SAN, "-c", os.path.join(CSRC, "runtime.hip"), "-o", rt],
+         "sanitized runtime compile")
+    drv = os.path.join(BUILD, "san", "abi_check.o")
+    _run([clangxx(), "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer", *LINK_SAN, "-D__HIP_PLATFORM_AMD__",
+          "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-c",
+          os.path.join(HOST_CHECK_DIR, "abi_check.cpp"), "-o", drv], "host check compile")
+    tmp = HOST_CHECK + ".tmp"
+    _run([clangxx(), *LINK_SAN, "-o", tmp, drv, rt, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+          "-Wl,-rpath,/opt/rocm/lib"], "host check link")
+    os.replace(tmp, HOST_CHECK)
+    if verbose:
+        print(f"built {HOST_CHECK}")
+    return HOST_CHECK
+
+
 if __name__ == "__main__":
     build()
+    if "--host-check" in sys.argv:
+        build_host_check()

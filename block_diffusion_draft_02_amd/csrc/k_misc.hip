@@ -242,22 +242,29 @@ hipError_t launch_resid_sum(float* X, const float* P, int S, long long part_stri
 }
 
 // ---- SwiGLU -----------------------------------------------------------------------------
-// the fused gate/up projection's columns are [gate (ff) | up (ff)]
+// the fused gate/up projection's columns are [gate (ff) | up (ff)]; one thread per four
+// consecutive columns of a row (16-byte partial loads), each column's arithmetic on its own
 __global__ __launch_bounds__(256) void k_silu_mul(const float* __restrict__ P, int S, long long ps,
                                                   int gsz, int M, int ff, bf16* __restrict__ A,
                                                   bf16* __restrict__ A_lo) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)M * ff) return;
-  const size_t r = idx / ff, j = idx % ff;
+  const int fq = ff / 4;
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (size_t)M * fq) return;
+  const size_t r = q / fq, j = (q % fq) * 4;
   const float* p = P + r * 2 * ff + j;
-  const float gs = sum_splits<8, float>(p, S, ps, gsz), us = sum_splits<8, float>(p + ff, S, ps, gsz);
-  split_bf16(silu(gs) * us, A[idx], A_lo[idx]);
+  const f32x4 gs = sum_splits<8, f32x4>(p, S, ps, gsz), us = sum_splits<8, f32x4>(p + ff, S, ps, gsz);
+  bf16 hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_bf16(silu(gs[e]) * us[e], hi[e], lo[e]);
+  *reinterpret_cast<uint2*>(A + r * ff + j) = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+  *reinterpret_cast<uint2*>(A_lo + r * ff + j) = uint2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
 }
 
 hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz, int M, int ff,
                            bf16* A, bf16* A_lo, hipStream_t st) {
-  if (gsz < 1) return hipErrorInvalidValue;
-  const size_t n = (size_t)M * ff;
+  // 16-byte partial loads: ff and the split stride in whole quads
+  if (gsz < 1 || ff % 4 != 0 || part_stride % 4 != 0) return hipErrorInvalidValue;
+  const size_t n = (size_t)M * (ff / 4);
   (void)launch(k_silu_mul, (unsigned)((n + 255) / 256), 256, 0, st, P, S, part_stride, gsz, M, ff, A, A_lo);
   return hipGetLastError();
 }
