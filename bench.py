@@ -515,7 +515,8 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
     dev = torch.device("cuda:0")
     lens = synth.gen_ctx_lengths(w["ctx"][0], w["ctx"][1], nb, w["seed"])
     steps = max(5, args.steps // 2)
-    total = args.warmup + steps
+    # warmup, the plain timed steps, then as many bracketed by events for the breakdown
+    total = args.warmup + 2 * steps
     app_reps = 10
     max_seq = int(lens.max()) + (total + 2 * app_reps) * a + gamma + 16
     per_seq = -(-(max_seq + gamma + 1) // 16)
@@ -544,13 +545,20 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
 
     for i in range(args.warmup):
         step(i)
+    # the rate from plain launches (events attached to launches slow them down), the per-class
+    # breakdown from a second pass of as many steps with every launch class bracketed
     torch.cuda.synchronize()
-    d.dflash_timing(list(B.K_CLASSES))
     t0 = time.perf_counter()
     for i in range(steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    d.dflash_timing(list(B.K_CLASSES))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + steps + i)
+    torch.cuda.synchronize()
+    el_br = time.perf_counter() - t0
     br = d.dflash_timing_read()
     d.dflash_timing([])
     # the append alone: one batched call against the sequence-by-sequence loop, same rows
@@ -585,7 +593,9 @@ def bench_batch16(m, Wd, gamma, a, args, B, torch, np, synth, to_dev):
                                avg_launch_us=round(br["markov"][0] / br["markov"][1] * 1e3, 3))
     return dict(workload=WORKLOAD_B16, variant=variant, value=round(blocks, 2), unit="blocks/s", steps=steps,
                 ms_per_step=round(el / steps * 1e3, 4), tokens_per_s=round(blocks * (gamma - 1), 1),
-                ctx_lengths=[int(x) for x in lens], timing="all launch classes bracketed by events",
+                bracketed_ms_per_step=round(el_br / steps * 1e3, 4), ctx_lengths=[int(x) for x in lens],
+                timing="value from plain launches; per-class times from a second pass with every launch class "
+                       "bracketed by events",
                 append=dict(rows=nb * a, form="one batched call" if batched else "per sequence",
                             batched_ms=round(app["batched"], 4), per_seq_loop_ms=round(app["per_seq"], 4),
                             timing="wall clock, 10 calls, nothing bracketed"),
