@@ -147,9 +147,11 @@ hipError_t launch_quant_fp8(const bf16* src, int N, int K, uint8_t* dst, float* 
 // Copy a row-major [N, K] bf16 weight into the T16 layout (ceil(N/16)*16 rows, the padding
 // rows zero); K a multiple of 256.
 hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStream_t st);
-// Tiled form for large M: C[M,N] fp32 (ldc), K multiple of 64; A_lo may be null (A exact).
+// Tiled form for large M: ks k splits (gemm_tiled_splits(N, K)), split z's fp32 result in
+// C + z*M*ldc ([M, N], row stride ldc); K a multiple of 32*ks; A_lo may be null (A exact).
+int gemm_tiled_splits(int N, int K);
 hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
-                             int N, int K, float* C, int ldc, hipStream_t st);
+                             int N, int K, int ks, float* C, int ldc, hipStream_t st);
 // lm_head (W in the T16 layout) + argmax partials: for rows r0..r0+M-1 of the forward (M <= 64), best (value,
 // index) per row over each workgroup's vocabulary range; optionally the fp32 logits of
 // drafted rows (row % gamma != 0) into logits[(r/gamma)*(gamma-1) + r%gamma - 1][V].

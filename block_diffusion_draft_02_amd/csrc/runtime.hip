@@ -461,19 +461,22 @@ int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st) 
     }));
     return DFLASH_OK;
   }
-  // many rows: the LDS-tiled GEMMs over the full K (MFMA-bound), plain fp32 results
+  // many rows: the LDS-tiled GEMMs (MFMA-bound), plain fp32 results of each k split, added
+  // in split order by the consumers
+  const int ks_fc = gemm_tiled_splits(c->h, ld), ks_kv = gemm_tiled_splits(nkv2, c->h);
   HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-    return launch_gemm_tiled(Hc, nullptr, ld, nc, c->fc, c->h, ld, c->F32, c->h, st);
+    return launch_gemm_tiled(Hc, nullptr, ld, nc, c->fc, c->h, ld, ks_fc, c->F32, c->h, st);
   }));
   HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-    return launch_rows_rmsnorm(c->F32, 1, 0, 1, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st);
+    return launch_rows_rmsnorm(c->F32, ks_fc, (long long)nc * c->h, ks_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
+                               c->Fb_lo, st);
   }));
   HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
-    return launch_gemm_tiled(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->KV32, nkv2, st);
+    return launch_gemm_tiled(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, ks_kv, c->KV32, nkv2, st);
   }));
   HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-    return launch_kv_append_post(c->KV32, 1, 0, 1, nc, c->L, c->knorm_all, c->eps, c->inv_freq, (float)c->mscale,
-                                 c->slots, c->rowpos, g, st);
+    return launch_kv_append_post(c->KV32, ks_kv, (long long)nc * nkv2, ks_kv, nc, c->L, c->knorm_all, c->eps,
+                                 c->inv_freq, (float)c->mscale, c->slots, c->rowpos, g, st);
   }));
   return DFLASH_OK;
 }
@@ -602,10 +605,10 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->aparts_ml, items * 128 * 2)) ||
       (rc = dalloc(c, &c->best_v, (size_t)c->m_max * c->lm_groups)) ||
       (rc = dalloc(c, &c->best_i, (size_t)c->m_max * c->lm_groups)) ||
-      (rc = dalloc(c, &c->F32, (size_t)APPEND_ROWS * hsz)) ||
+      (rc = dalloc(c, &c->F32, (size_t)gemm_tiled_splits(c->h, c->T * c->Ht) * APPEND_ROWS * hsz)) ||
       (rc = dalloc(c, &c->Fb, (size_t)APPEND_ROWS * hsz)) ||
       (rc = dalloc(c, &c->Fb_lo, (size_t)APPEND_ROWS * hsz)) ||
-      (rc = dalloc(c, &c->KV32, (size_t)APPEND_ROWS * c->L * 2 * c->kvd)) ||
+      (rc = dalloc(c, &c->KV32, (size_t)gemm_tiled_splits(c->L * 2 * c->kvd, c->h) * APPEND_ROWS * c->L * 2 * c->kvd)) ||
       (rc = dalloc(c, &c->ring_dev, (size_t)RING * APPEND_ROWS)) ||
       (rc = dalloc(c, &c->w_kv, (size_t)c->L * 2 * c->kvd * hsz)) ||
       (rc = dalloc(c, &c->w_kv_t, (size_t)c->L * 2 * c->kvd * hsz)) ||
