@@ -102,8 +102,8 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // splits are each added in split order starting from zero, then the group sums in group
 // order starting from zero. Every consumer of the forward's GEMM partials adds them this
 // way, so a GEMM that forms the group sums itself (handing over one partial per group, then
-// gsz = 1) gives the same bits. Loads go out B at a time before their adds, unconditionally
-// (a pass past S re-reads the last split and drops it), so none waits for another.
+// gsz = 1) gives the same bits. Loads go out up to B at a time before their adds, so none
+// waits for another.
 template <typename T>
 __device__ __forceinline__ T ld_part(const float* p) { return *reinterpret_cast<const T*>(p); }
 
@@ -114,9 +114,12 @@ __device__ __forceinline__ T sum_splits(const float* __restrict__ p, int S, long
   T t = T{}, grp = T{};
   int in_grp = 0;
   for (int s0 = 0; s0 < S; s0 += B) {
+    // every load of the pass issued before the first add; none past the last split (S is
+    // uniform, so the skips are scalar branches; re-reading the last split instead cost the
+    // consumers up to four times their loads)
     T v[B];
 #pragma unroll
-    for (int u = 0; u < B; ++u) v[u] = ld_part<T>(p + (long long)min(s0 + u, S - 1) * ps);
+    for (int u = 0; u < B; ++u) v[u] = s0 + u < S ? ld_part<T>(p + (long long)(s0 + u) * ps) : T{};
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       if (s0 + u < S) {
