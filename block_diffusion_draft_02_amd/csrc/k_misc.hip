@@ -147,14 +147,15 @@ hipError_t launch_qkv_post(const float* P, int S, long long part_stride, int gsz
 }
 
 // ---- residual add + RMSNorm ---------------------------------------------------------------
-// The row-wise consumers of split-K partials: 1024 threads per row, thread t owns the 4-float
-// slices t, t + 1024, ... of the row and adds their partials in the canonical order.
+// The row-wise consumers of split-K partials: one workgroup per row (rn_threads(h) threads),
+// thread t owns the 4-float slices t, t + T, ... of the row and adds their partials in the
+// canonical order.
 constexpr int RN_HMAX = 8192;      // row length the LDS row buffer holds
 
 // x (LDS row of h floats, complete) -> out = x * rs * w as hi + lo bf16
 __device__ __forceinline__ void norm_out(const float* xs, int h, float rs, const bf16* __restrict__ w,
                                          bf16* __restrict__ o, bf16* __restrict__ ol) {
-  for (int j = threadIdx.x * 4; j < h; j += 1024 * 4) {
+  for (int j = threadIdx.x * 4; j < h; j += blockDim.x * 4) {
     // the norm weight is a caller's pointer with only bf16 alignment guaranteed
     const float wf[4] = {bf2f(w[j]), bf2f(w[j + 1]), bf2f(w[j + 2]), bf2f(w[j + 3])};
     bf16 hi[4], lo[4];
@@ -165,12 +166,16 @@ __device__ __forceinline__ void norm_out(const float* xs, int h, float rs, const
   }
 }
 
+// threads of a row workgroup: one per 4-float slice up to 1024 (whole waves; a row of 2048 took
+// 1024 threads with half of them idle, and twice the rounds of workgroups)
+static unsigned rn_threads(int h) { return (unsigned)std::min(1024, std::max(64, (h / 4 + 63) / 64 * 64)); }
+
 // Sum of the split partials of row r (plus the residual X when given), kept in the LDS row
 // xs and written back to X; returns the row's sum of squares (valid in every thread).
 __device__ __forceinline__ float rows_gather(float* __restrict__ X, const float* __restrict__ p, int S,
                                              long long ps, int gsz, int h, float* xs, float* red_ss) {
   float ss = 0.f;
-  for (int j = threadIdx.x * 4; j < h; j += 1024 * 4) {
+  for (int j = threadIdx.x * 4; j < h; j += blockDim.x * 4) {
     f32x4 y = sum_splits<16, f32x4>(p + j, S, ps, gsz);
     if (X != nullptr) y = *reinterpret_cast<const f32x4*>(X + j) + y;
     *reinterpret_cast<f32x4*>(xs + j) = y;
@@ -181,8 +186,7 @@ __device__ __forceinline__ float rows_gather(float* __restrict__ X, const float*
   if ((threadIdx.x & 63) == 0) red_ss[threadIdx.x >> 6] = ss;
   __syncthreads();
   float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) tot += red_ss[i];
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red_ss[i];
   return tot;
 }
 
@@ -203,7 +207,7 @@ hipError_t launch_resid_norm(float* X, const float* P, int S, long long part_str
                              int h, const bf16* w, float eps, bf16* Xn, bf16* Xn_lo,
                              hipStream_t st) {
   if (h > RN_HMAX || h % 4 || gsz < 1) return hipErrorInvalidValue;
-  (void)launch(k_resid_norm, M, 1024, 0, st, X, P, S, part_stride, gsz, h, w, eps, Xn, Xn_lo);
+  (void)launch(k_resid_norm, M, rn_threads(h), 0, st, X, P, S, part_stride, gsz, h, w, eps, Xn, Xn_lo);
   return hipGetLastError();
 }
 
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st) {
   if (h > RN_HMAX || h % 4 || gsz < 1) return hipErrorInvalidValue;
-  (void)launch(k_rows_rmsnorm, M, 1024, 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo);
+  (void)launch(k_rows_rmsnorm, M, rn_threads(h), 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo);
   return hipGetLastError();
 }
 
