@@ -321,23 +321,35 @@ hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long lon
   return hipGetLastError();
 }
 
-// one workgroup per row: the sum of the row's S split-K partials, RMSNorm'd
+// one workgroup per row: the sum of the row's S split-K partials, RMSNorm'd; optionally the
+// row's RoPE (cos, sin) pairs for the fused K/V epilogue (one thread per pair)
 __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__ X, int S, long long ps,
                                                        int gsz, int h, const bf16* __restrict__ w, float eps,
                                                        bf16* __restrict__ out,
-                                                       bf16* __restrict__ out_lo) {
+                                                       bf16* __restrict__ out_lo,
+                                                       const int* __restrict__ rowpos,
+                                                       const double* __restrict__ inv_freq, int half,
+                                                       float2* __restrict__ cs) {
   __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
   __shared__ float red_ss[16];
   const int r = blockIdx.x;
+  if (cs && (int)threadIdx.x < half) {
+    double sn, cn;
+    sincos((double)rowpos[r] * inv_freq[threadIdx.x], &sn, &cn);
+    cs[(size_t)r * half + threadIdx.x] = make_float2((float)cn, (float)sn);
+  }
   const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, gsz, h, xs, red_ss);
   const float rs = rsqrtf(tot / (float)h + eps);
   norm_out(xs, h, rs, w, out + (size_t)r * h, out_lo + (size_t)r * h);
 }
 
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
-                               const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st) {
+                               const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st,
+                               const int* rowpos, const double* inv_freq, int half, float2* cs) {
   if (h > RN_HMAX || h % 4 || gsz < 1) return hipErrorInvalidValue;
-  (void)launch(k_rows_rmsnorm, M, rn_threads(h), 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo);
+  if (cs && (!rowpos || !inv_freq || half < 1 || half > (int)rn_threads(h))) return hipErrorInvalidValue;
+  (void)launch(k_rows_rmsnorm, M, rn_threads(h), 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo, rowpos,
+               inv_freq, half, cs);
   return hipGetLastError();
 }
 

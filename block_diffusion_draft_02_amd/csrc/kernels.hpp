@@ -152,6 +152,16 @@ hipError_t launch_tile_weight(const bf16* src, int N, int K, bf16* dst, hipStrea
 int gemm_tiled_splits(int N, int K);
 hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W,
                              int N, int K, int ks, float* C, int ldc, hipStream_t st);
+// The append's fused K/V GEMM with k_norm, RoPE and the page writes in its epilogue (one k
+// split, whatever gemm_tiled_splits says): N = L * 2 * nkv * hd ([K0 | V0 | K1 | V1 | ...]),
+// nkv * hd a multiple of 256, hd 32, 64 or 128. Row r of A goes to pool slot slots[r]; cs holds
+// the rows' RoPE (cos, sin) pairs, float2 [M][hd / 2]. Per element the arithmetic of
+// launch_kv_append_post on a one-split launch_gemm_tiled result, except the order in which a
+// head's squares are summed for the k_norm.
+bool gemm_tiled_kv_fusable(int N, int nkv, int hd);
+hipError_t launch_gemm_tiled_kv(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
+                                const bf16* k_norm_all, float eps, float mscale, const long long* slots,
+                                const float2* cs, KvGeom g, hipStream_t st);
 // lm_head (W in the T16 layout) + argmax partials: for rows r0..r0+M-1 of the forward (M <= 64), best (value,
 // index) per row over each workgroup's vocabulary range; optionally the fp32 logits of
 // drafted rows (row % gamma != 0) into logits[(r/gamma)*(gamma-1) + r%gamma - 1][V].
@@ -228,9 +238,12 @@ hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, i
 hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long long* slots, int* rowpos,
                                      int* kpos, hipStream_t st);
 // inputs are split-K partials X[s][M][...] added in the canonical order (S = 1, gsz = 1 for a
-// plain result)
+// plain result). With cs non-null, row r also writes its RoPE (cos, sin) pairs at position
+// rowpos[r] into cs[r][0..half) (angles in double precision, then rounded to float).
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
-                               const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st);
+                               const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st,
+                               const int* rowpos = nullptr, const double* inv_freq = nullptr, int half = 0,
+                               float2* cs = nullptr);
 hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int gsz, int n, int L,
                                  const bf16* k_norm_all, float eps, const double* inv_freq, float mscale,
                                  const long long* slots, const int* rowpos, KvGeom g, hipStream_t st);

@@ -140,7 +140,9 @@ struct dflash_ctx {
   // append scratch
   float* F32 = nullptr;
   bf16 *Fb = nullptr, *Fb_lo = nullptr;
-  float* KV32 = nullptr;
+  float* KV32 = nullptr;       // the K/V GEMM's fp32 result where its epilogue cannot be fused
+  float2* rope_cs = nullptr;   // [APPEND_ROWS][hd / 2] the appended rows' RoPE (cos, sin)
+  bool kv_fused = false;       // long appends: the K/V GEMM writes the pages itself
   int* ring_host = nullptr;
   int* ring_dev = nullptr;
   hipEvent_t ring_ev[RING] = {};
@@ -462,15 +464,23 @@ int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st) 
     return DFLASH_OK;
   }
   // many rows: the LDS-tiled GEMMs (MFMA-bound), plain fp32 results of each k split, added
-  // in split order by the consumers
+  // in split order by the consumers; the K/V GEMM writes the pages from its epilogue where the
+  // shape allows (the row kernel then also takes the rows' RoPE angles)
   const int ks_fc = gemm_tiled_splits(c->h, ld), ks_kv = gemm_tiled_splits(nkv2, c->h);
   HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
     return launch_gemm_tiled(Hc, nullptr, ld, nc, c->fc, c->h, ld, ks_fc, c->F32, c->h, st);
   }));
   HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
     return launch_rows_rmsnorm(c->F32, ks_fc, (long long)nc * c->h, ks_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
-                               c->Fb_lo, st);
+                               c->Fb_lo, st, c->rowpos, c->inv_freq, c->hd / 2, c->kv_fused ? c->rope_cs : nullptr);
   }));
+  if (c->kv_fused) {
+    HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
+      return launch_gemm_tiled_kv(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, c->knorm_all, c->eps,
+                                  (float)c->mscale, c->slots, c->rope_cs, g, st);
+    }));
+    return DFLASH_OK;
+  }
   HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
     return launch_gemm_tiled(c->Fb, c->Fb_lo, c->h, nc, c->w_kv, nkv2, c->h, ks_kv, c->KV32, nkv2, st);
   }));
@@ -548,6 +558,7 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
     q.pos.reserve(c->max_seq);
   }
   c->m_max = c->max_batch * c->gmax;
+  c->kv_fused = gemm_tiled_kv_fusable(c->L * 2 * c->kvd, c->nkv, c->hd);
   c->fc = (const bf16*)w->fc; c->hidden_norm = (const bf16*)w->hidden_norm; c->norm = (const bf16*)w->norm;
   c->embed = (const bf16*)w->embed_tokens;
 
@@ -608,7 +619,8 @@ int dflash_create(const dflash_config* cfg, const dflash_weights* w, void* strea
       (rc = dalloc(c, &c->F32, (size_t)gemm_tiled_splits(c->h, c->T * c->Ht) * APPEND_ROWS * hsz)) ||
       (rc = dalloc(c, &c->Fb, (size_t)APPEND_ROWS * hsz)) ||
       (rc = dalloc(c, &c->Fb_lo, (size_t)APPEND_ROWS * hsz)) ||
-      (rc = dalloc(c, &c->KV32, (size_t)gemm_tiled_splits(c->L * 2 * c->kvd, c->h) * APPEND_ROWS * c->L * 2 * c->kvd)) ||
+      (rc = dalloc(c, &c->KV32, c->kv_fused ? 0 : (size_t)gemm_tiled_splits(c->L * 2 * c->kvd, c->h) * APPEND_ROWS * c->L * 2 * c->kvd)) ||
+      (rc = dalloc(c, &c->rope_cs, (size_t)APPEND_ROWS * (c->hd / 2))) ||
       (rc = dalloc(c, &c->ring_dev, (size_t)RING * APPEND_ROWS)) ||
       (rc = dalloc(c, &c->w_kv, (size_t)c->L * 2 * c->kvd * hsz)) ||
       (rc = dalloc(c, &c->w_kv_t, (size_t)c->L * 2 * c->kvd * hsz)) ||
