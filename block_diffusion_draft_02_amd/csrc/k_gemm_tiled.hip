@@ -8,18 +8,29 @@
 namespace dfl {
 
 constexpr int TB_M = 256, TB_N = 256;  // output tile of a workgroup
-constexpr int TK = 32;                 // depth of one stage (one MFMA step)
+constexpr int TK = 32;                 // depth of one MFMA step
 constexpr int T_WAVES = 8;             // 4 row quarters x 2 column halves: a wave owns 64 x 128
 constexpr int T_KS_MAX = 4;            // k splits at most
 
-// one stage: the A rows (hi and, with SPLIT, lo) and the W rows of a 32-deep k step, 64 bytes
-// a row; row r's 16-byte unit u sits at unit u ^ ((r >> 1) & 3), so the 8 lanes an LDS cycle
-// serves (rows 0-7 of a 16-row fragment, one unit) hit distinct 16-byte bank groups
+// The ring: with the lo term (SPLIT) a stage is one 32-deep step (48 KB) and the ring three
+// stages; an exact activation's stage is two steps deep (64 KB) and the ring two stages, so
+// its barrier and waits come once per 64 MFMAs a wave, as with the lo term.
+template <bool SPLIT>
+struct TiledShape {
+  static constexpr int TKS = SPLIT ? 32 : 64;   // k depth of a stage
+  static constexpr int NST = SPLIT ? 3 : 2;     // stages in the ring
+  static constexpr int UPR = TKS / 8;           // 16-byte units of a stage row
+  static constexpr int NP = UPR / 2;            // 1 KB DMA pieces of one operand a wave brings per stage
+};
+
+// one stage: the A rows (hi and, with SPLIT, lo) and the W rows of its k range, TKS * 2 bytes
+// a row; row r's 16-byte unit u sits at unit u ^ ((r >> 1) & (UPR - 1)), so the 16 lanes an
+// LDS cycle serves (rows of a 16-row fragment, one unit) hit distinct 16-byte bank groups
 template <bool SPLIT>
 struct TiledStage {
-  bf16 a[TB_M * TK];
-  bf16 al[SPLIT ? TB_M * TK : 8];
-  bf16 w[TB_N * TK];
+  bf16 a[TB_M * TiledShape<SPLIT>::TKS];
+  bf16 al[SPLIT ? TB_M * TiledShape<SPLIT>::TKS : 8];
+  bf16 w[TB_N * TiledShape<SPLIT>::TKS];
 };
 
 // s_waitcnt with vmcnt <= N (vmcnt[3:0] | vmcnt[5:4] << 14; expcnt and lgkmcnt left at maximum)
@@ -28,10 +39,11 @@ struct TiledStage {
 // k splits: from (N, K) alone, never from the row count, so that a row's result does not
 // depend on how rows are grouped into launches. A narrow output (few 256-column tiles) splits
 // its K in two or four so that a 2048-row launch still has about a chip's worth of workgroups.
+// Each split is a whole number of the deeper (64) stages.
 int gemm_tiled_splits(int N, int K) {
   const int tiles = (APPEND_ROWS / TB_M) * ((N + TB_N - 1) / TB_N);
   int ks = 1;
-  while (ks < T_KS_MAX && tiles * ks * 2 <= 256 && K % (TK * ks * 2) == 0) ks *= 2;
+  while (ks < T_KS_MAX && tiles * ks * 2 <= 256 && K % (TiledShape<false>::TKS * ks * 2) == 0) ks *= 2;
   return ks;
 }
 
@@ -204,36 +216,38 @@ __device__ __forceinline__ void kv_epilogue(f32x4 (&acc)[4][8], char* reg, int m
 // C[z] = A W^T over k split z (plain fp32 results; within a split the sum over k runs in
 // order, step by step, the hi then the lo term at every 32-deep step). One 8-wave workgroup
 // per 256 x 256 tile and split, each wave 64 x 128 (four 16-row by eight 16-column MFMA
-// tiles): per step a wave reads 8 (hi, lo) activation fragments and 8 weight fragments for
-// 64 MFMAs, and the workgroup brings 48 KB into LDS for 256 x 256 x 32 products (a 128 x 128
-// tile brings 24 KB for a quarter of them). The steps stream through a ring of three LDS
-// stages with the gfx950 global->LDS 16-byte load: wave v brings an eighth of every operand
-// of a stage, 1 KB an instruction, each lane choosing its source so that the LDS copy is
-// swizzled. Step j+2 is requested right after the barrier that ends step j-1; a wave waits
-// only for its own loads of step j (one barrier per step). Every step issues the same loads
-// (past the last step it re-reads the last one into a stage nobody reads again), so the
-// compiler sees one fixed count in flight, and the three stages are separate LDS objects.
+// tiles): per 32-deep step a wave reads 8 activation fragments (each hi and lo with SPLIT)
+// and 8 weight fragments, and the workgroup brings 48 KB (32 KB without the lo term) into LDS
+// for 256 x 256 x 32 products. The stages stream through the ring with the gfx950
+// global->LDS 16-byte load: wave v brings an eighth of every operand of a stage, 1 KB an
+// instruction, each lane choosing its source so that the LDS copy is swizzled. Stage j+NST-1
+// is requested right after the barrier that ends stage j-1; a wave waits only for its own
+// loads of stage j (one barrier per stage). Every stage issues the same loads (past the last
+// one it re-reads the last into a stage nobody reads again), so the compiler sees one fixed
+// count in flight, and the stages are separate LDS objects.
 template <bool SPLIT, int EPI_HD>
 __device__ __forceinline__ void gemm_tiled_wg(TiledStage<SPLIT>& st0, TiledStage<SPLIT>& st1, TiledStage<SPLIT>& st2,
                                               const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda,
                                               int M, const bf16* __restrict__ W, int N, int K, int kps,
                                               float* __restrict__ C, int ldc, const KvEpi& ep) {
-  constexpr int NI = SPLIT ? 6 : 4;   // DMA instructions per wave and stage
+  using SH = TiledShape<SPLIT>;
+  constexpr int TKS = SH::TKS, NST = SH::NST, UPR = SH::UPR, NP = SH::NP;
+  constexpr int NI = NP * (SPLIT ? 3 : 2);   // DMA instructions per wave and stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * TB_M, n0 = blockIdx.x * TB_N;
   const int kb = blockIdx.z * kps;
-  const int nk = kps / TK;
+  const int nk = kps / TKS;
   const int c = lane & 15, g = lane >> 4;
-  // this wave's two 1 KB pieces of each operand of a stage: LDS units P = (2 wave + h) * 64 +
-  // lane, row P / 4, source unit (P % 4) ^ ((row >> 1) & 3); byte offsets (rows past M or N
-  // repeat the last one; their results are never stored), loop-invariant
-  uint32_t offA[2], offW[2];
+  // this wave's NP 1 KB pieces of each operand of a stage: LDS units P = (NP wave + h) * 64 +
+  // lane, row P / UPR, source unit (P % UPR) ^ ((row >> 1) & (UPR - 1)); byte offsets (rows past
+  // M or N repeat the last one; their results are never stored), loop-invariant
+  uint32_t offA[NP], offW[NP];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int P = (2 * wave + h) * 64 + lane;
-    const int r = P >> 2, u = (P & 3) ^ ((r >> 1) & 3);
+  for (int h = 0; h < NP; ++h) {
+    const int P = (NP * wave + h) * 64 + lane;
+    const int r = P / UPR, u = (P % UPR) ^ ((r >> 1) & (UPR - 1));
     offA[h] = (uint32_t)((size_t)min(m0 + r, M - 1) * lda + u * 8) * 2u;
     offW[h] = (uint32_t)((size_t)min(n0 + r, N - 1) * K + u * 8) * 2u;
   }
@@ -241,10 +255,10 @@ __device__ __forceinline__ void gemm_tiled_wg(TiledStage<SPLIT>& st0, TiledStage
   const bf16* srcAl = SPLIT ? A_lo + kb : A;
   const bf16* srcW = W + kb;
   auto issue = [&](TiledStage<SPLIT>& st, int j) {
-    const int k = __builtin_amdgcn_readfirstlane(min(j, nk - 1) * TK);
+    const int k = __builtin_amdgcn_readfirstlane(min(j, nk - 1) * TKS);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int o = (2 * wave + h) * 512;
+    for (int h = 0; h < NP; ++h) {
+      const int o = (NP * wave + h) * 512;
       uint32_t va = offA[h], vw = offW[h];
       asm volatile("" : "+v"(va), "+v"(vw));
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(srcA + k) + va, &st.a[o], 16, 0, 0);
@@ -257,36 +271,47 @@ __device__ __forceinline__ void gemm_tiled_wg(TiledStage<SPLIT>& st0, TiledStage
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto frag = [&](const bf16* base, int r) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + r * TK + ((g ^ ((r >> 1) & 3)) * 8)));
+  // the fragment of 32-deep step s of the stage
+  auto frag = [&](const bf16* base, int r, int s) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + r * TKS + (((s * 4 + g) ^ ((r >> 1) & (UPR - 1))) * 8)));
   };
   auto mma = [&](const TiledStage<SPLIT>& st) {
-    bf16x8 b[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = frag(st.w, wn * 128 + j * 16 + c);
+    for (int s = 0; s < TKS / TK; ++s) {
+      bf16x8 b[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 a = frag(st.a, wm * 64 + i * 16 + c);
-      const bf16x8 al = SPLIT ? frag(st.al, wm * 64 + i * 16 + c) : a;
+      for (int j = 0; j < 8; ++j) b[j] = frag(st.w, wn * 128 + j * 16 + c, s);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc[i][j] = mfma16(a, b[j], acc[i][j]);
-        if (SPLIT) acc[i][j] = mfma16(al, b[j], acc[i][j]);
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a = frag(st.a, wm * 64 + i * 16 + c, s);
+        const bf16x8 al = SPLIT ? frag(st.al, wm * 64 + i * 16 + c, s) : a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[i][j] = mfma16(a, b[j], acc[i][j]);
+          if (SPLIT) acc[i][j] = mfma16(al, b[j], acc[i][j]);
+        }
       }
     }
   };
   auto step = [&](int j, const TiledStage<SPLIT>& cur, TiledStage<SPLIT>& nxt) {
-    DFL_GEMM_WAIT_VM(NI);   // step j + 1's loads may still be in flight
+    DFL_GEMM_WAIT_VM(NI * (NST - 2));   // the next stages' loads may still be in flight
     __builtin_amdgcn_s_barrier();
-    issue(nxt, j + 2);
+    issue(nxt, j + NST - 1);
     if (j < nk) mma(cur);
   };
   issue(st0, 0);
-  issue(st1, 1);
-  for (int j = 0; j < nk; j += 3) {
-    step(j, st0, st2);
-    step(j + 1, st1, st0);
-    step(j + 2, st2, st1);
+  if constexpr (NST == 3) {
+    issue(st1, 1);
+    for (int j = 0; j < nk; j += 3) {
+      step(j, st0, st2);
+      step(j + 1, st1, st0);
+      step(j + 2, st2, st1);
+    }
+  } else {
+    for (int j = 0; j < nk; j += 2) {
+      step(j, st0, st1);
+      step(j + 1, st1, st0);
+    }
   }
   DFL_GEMM_WAIT_VM(0);   // the loads past the last step land before the workgroup ends
   if constexpr (EPI_HD > 0) {
@@ -317,13 +342,19 @@ template <bool SPLIT, int EPI_HD>
 __global__ __launch_bounds__(T_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tiled(
     const bf16* __restrict__ A, const bf16* __restrict__ A_lo, int lda, int M, const bf16* __restrict__ W, int N,
     int K, int kps, float* __restrict__ C, int ldc, KvEpi ep) {
-  __shared__ __attribute__((aligned(16))) TiledStage<SPLIT> st0, st1, st2;
-  gemm_tiled_wg<SPLIT, EPI_HD>(st0, st1, st2, A, A_lo, lda, M, W, N, K, kps, C, ldc, ep);
+  __shared__ __attribute__((aligned(16))) TiledStage<SPLIT> st0, st1;
+  if constexpr (TiledShape<SPLIT>::NST == 3) {
+    __shared__ __attribute__((aligned(16))) TiledStage<SPLIT> st2;
+    gemm_tiled_wg<SPLIT, EPI_HD>(st0, st1, st2, A, A_lo, lda, M, W, N, K, kps, C, ldc, ep);
+  } else {
+    gemm_tiled_wg<SPLIT, EPI_HD>(st0, st1, st1, A, A_lo, lda, M, W, N, K, kps, C, ldc, ep);
+  }
 }
 
 hipError_t launch_gemm_tiled(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K, int ks,
                              float* C, int ldc, hipStream_t st) {
-  if (M <= 0 || N <= 0 || ks < 1 || ks > T_KS_MAX || K % (TK * ks) != 0 || (lda % 8) != 0 || ldc < N)
+  const int tks = A_lo ? TiledShape<true>::TKS : TiledShape<false>::TKS;
+  if (M <= 0 || N <= 0 || ks < 1 || ks > T_KS_MAX || K % (tks * ks) != 0 || (lda % 8) != 0 || ldc < N)
     return hipErrorInvalidValue;
   // the DMA offsets are 32-bit byte offsets from the operands' bases
   if ((size_t)M * lda * 2 >= (1ull << 32) || (size_t)N * K * 2 >= (1ull << 32)) return hipErrorInvalidValue;
@@ -346,7 +377,7 @@ bool gemm_tiled_kv_fusable(int N, int nkv, int hd) {
 hipError_t launch_gemm_tiled_kv(const bf16* A, const bf16* A_lo, int lda, int M, const bf16* W, int N, int K,
                                 const bf16* k_norm_all, float eps, float mscale, const long long* slots,
                                 const float2* cs, KvGeom g, hipStream_t st) {
-  if (M <= 0 || !A_lo || !gemm_tiled_kv_fusable(N, g.nkv, g.hd) || K % TK != 0 || (lda % 8) != 0)
+  if (M <= 0 || !A_lo || !gemm_tiled_kv_fusable(N, g.nkv, g.hd) || K % TiledShape<true>::TKS != 0 || (lda % 8) != 0)
     return hipErrorInvalidValue;
   if ((size_t)M * lda * 2 >= (1ull << 32) || (size_t)N * K * 2 >= (1ull << 32)) return hipErrorInvalidValue;
   const KvEpi ep{slots, cs, k_norm_all, eps, mscale, g};
