@@ -67,16 +67,17 @@ __device__ __forceinline__ long long shfl64(long long v, int src) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-// The K/V epilogue of one wave's 64 x 128 piece of a tile: rows R0 .. R0+63 (R0 = m0 + 64 wm), columns
-// = HW = 128 / HD whole heads of one layer's K or V block. The wave's region is 16 KB of LDS
-// no other wave touches; it carries the values to the pool (V in two passes of 64 columns).
+// The K/V epilogue of one wave's 64 x 128 piece of a tile: rows R0 .. R0+63 (R0 = m0 + 64 wm),
+// columns = HW = 128 / HD whole heads of one layer's K or V block. The wave's region is 16 KB
+// of LDS no other wave touches; it carries the values to the pool (V in two passes of 64
+// columns).
 // K: x = 0 + the GEMM's result; the head's sum of squares (over j in this lane, then over the
 // 16 lanes of the row, which all end with the same sum); k_norm; RoPE on the pairs (d, d +
 // HD/2), which sit in this lane's j-blocks jj and jj + JH/2; times mscale; staged in LDS as
-// each is made, then 16-byte stores along the page's [key][d] rows (16 lanes a 256-byte row). V: bf16(0 + result), staged
-// [d][key] with the keys shifted by the first row's page offset, so that a 16-key group is one
-// page row: 16-byte stores where the group's 16 rows have consecutive slots starting a page,
-// element stores elsewhere.
+// each is made, then 16-byte stores along the page's [key][d] rows (16 lanes a 256-byte row).
+// V: bf16(0 + result), staged [d][key] with the keys shifted by the first row's page offset,
+// so that a 16-key group is one page row: 16-byte stores where the group's 16 rows have
+// consecutive slots starting a page, element stores elsewhere.
 template <int HD>
 __device__ __forceinline__ void kv_epilogue(f32x4 (&acc)[4][8], char* reg, int m0, int n0, int M, int wm, int wn,
                                             int lane, const KvEpi& ep) {
@@ -94,10 +95,10 @@ __device__ __forceinline__ void kv_epilogue(f32x4 (&acc)[4][8], char* reg, int m
   bf16* const lay = g.pool + (size_t)layer * g.num_pages * pl;
   const long long sl = lane < nv ? ep.slots[R0 + lane] : -1;
   if ((blk & 1) == 0) {
-    // [64 rows][128 columns], 256-byte rows; 16-byte unit u of row r at u ^ 2 ((r >> 2) & 3), so the
-    // four rows a 2-byte store instruction touches (4 apart) fall on distinct banks. This lane's
-    // rows are 16 i + 4 gq + e, so its swizzle is 2 gq throughout: one address per j-block, the
-    // row a constant offset.
+    // [64 rows][128 columns], 256-byte rows; 16-byte unit u of row r at u ^ 2 ((r >> 2) & 3), so
+    // the four rows a 2-byte store instruction touches (4 apart) fall on distinct banks. This
+    // lane's rows are 16 i + 4 gq + e, so its swizzle is 2 gq throughout: one address per
+    // j-block, the row a constant offset.
     char* kb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) kb[j] = reg + gq * 1024 + (2 * (j ^ gq) + (c >> 3)) * 16 + (c & 7) * 2;
