@@ -216,7 +216,7 @@ constexpr int ATTN_CHUNK_PAGES_MAX = 512;
 // property of each band alone (so a band's arithmetic never depends on the other bands of
 // the call): with the LDS path enabled (a property of the drafter, fixed at create), bands
 // of more than ATTN_LDS_MIN_PAGES pages (2048 keys) on a head_dim-128 layer without a window
-// stream K/V through LDS, planned in at most 16 chunks; the rest load K/V straight into
+// stream K/V through LDS, planned in at most 12 chunks; the rest load K/V straight into
 // registers. plan_attn fills the table and counts each path's chunks; partials stay indexed
 // by the call-wide chunk numbering (Band::base), sized [sum of nch * nkv][128][hd].
 constexpr int ATTN_LDS_MIN_PAGES = 128;

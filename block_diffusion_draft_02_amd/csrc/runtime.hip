@@ -221,9 +221,10 @@ int chunk_pages(int pages, bool lds) {
   // chunk, widened in steps of 16 pages so that a band never has more than 32 chunks: a
   // 4K-key band keeps every workgroup of a layer resident at once, long bands keep the
   // partial traffic and the merge bounded. Bands on the attention's LDS path (one workgroup
-  // per chunk and kv head, not four) take at most 16 chunks, as long as a chunk's page ids
-  // fit the workgroup's table: fewer partials and less merge work
-  if (lds && pages > ATTN_LDS_MIN_PAGES) return std::min(ATTN_CHUNK_PAGES_MAX, 16 * ((pages + 255) / 256));
+  // per chunk and kv head, not four) take at most 12 chunks, as long as a chunk's page ids
+  // fit the workgroup's table: fewer partials and less merge work (12 ran the 16-band and the
+  // long-context forwards faster than 16, 10 or 8)
+  if (lds && pages > ATTN_LDS_MIN_PAGES) return std::min(ATTN_CHUNK_PAGES_MAX, 16 * ((pages + 191) / 192));
   return 16 * std::max(1, (pages + 511) / 512);
 }
 

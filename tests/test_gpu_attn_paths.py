@@ -1,6 +1,6 @@
 """GPU parity of the two attention paths in one call: in a drafter made for 8 or more
-sequences, on a head_dim-128 layer without a window, a band whose chunks span 32 pages or
-more (a band of more than 2048 keys, planned in at most 16 chunks) streams its K/V through
+sequences, on a head_dim-128 layer without a window, a band of more than 2048 keys (planned
+in at most 12 chunks) streams its K/V through
 LDS, every other band loads K/V straight into registers; windowed layers always take the
 register path. A small head_dim-128 drafter (2 layers, hidden 512, 16:2 heads) with bands on
 both sides of 2048 keys, three LDS chunk widths, last chunks of 1 and of 30 keys, a windowed
@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 
 SEED = 1501
 # C + 16 keys: 2049 (LDS path, 9 chunks of 256 keys, the last holding 1 key), 2048 (the
-# register path's largest band: 8 chunks of 256), 9246 (LDS path, 13 chunks of 768, the last
-# 30 keys), 316 (register path), 14016 (LDS path, 14 chunks of 1024: the longest chunks,
+# register path's largest band: 8 chunks of 256), 9246 (LDS path, 10 chunks of 1024, the last
+# 30 keys), 316 (register path), 14016 (LDS path, 11 chunks of 1280: the longest chunks,
 # dispatched first)
 LENS = [2033, 2032, 9230, 300, 14000]
 

@@ -31,7 +31,7 @@ def _both(d, seqs, bonus, gamma, qpos=None):
 
 def _hd128_model():
     m = synth.model("qwen3-L8-h2048")
-    m.update(num_layers=2, hidden=512, num_q_heads=16, num_kv_heads=2, head_dim=128, intermediate=1024,
+    m.update(num_layers=2, hidden=512, num_q_heads=16, num_kv_heads=4, head_dim=128, intermediate=1024,
              vocab=2048, num_taps=2, target_hidden=512)
     return m
 
@@ -54,9 +54,10 @@ def test_noalloc_matches_forward_tiny_two_calls_shrinking():
 
 
 def test_noalloc_matches_forward_both_attention_paths_then_refuses_oversize():
-    """A head_dim-128 drafter made for 32 sequences (bands past 2048 keys take the LDS path):
-    16 bands of 24000 keys need ~37 MiB of partials (fits), then 4 mixed bands (smaller); 32
-    such bands need more than the 64 MiB array and are refused with ERANGE, changing nothing."""
+    """A head_dim-128 drafter (4 kv heads) made for 32 sequences (bands past 2048 keys take the
+    LDS path, 12 chunks at 24000 keys): 16 bands of 24000 keys need ~49 MiB of attention
+    partials (fits), then 2 bands (smaller); 32 such bands need ~97 MiB, more than the 64 MiB
+    array, and are refused with ERANGE, changing nothing."""
     m = _hd128_model()
     W = dev_weights(synth.gen_weights(m, SEED))
     n_long, C = 32, 24000
