@@ -10,6 +10,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace dfl {
 
 // ---- forward prologue ------------------------------------------------------------------
@@ -274,29 +276,8 @@ hipError_t launch_silu_mul(const float* P, int S, long long part_stride, int gsz
 }
 
 // ---- context append ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_append_setup(AppendArgs a, int* __restrict__ bt,
-                                                      long long* __restrict__ slots,
-                                                      int* __restrict__ rowpos,
-                                                      int* __restrict__ kpos) {
-  for (int j = threadIdx.x; j < a.n_upd; j += 256) bt[a.upd_off[j]] = a.upd_page[j];
-  for (int r = threadIdx.x; r < a.n; r += 256) {
-    const int p = a.kv_len + r;
-    const int lp = (p >> 4) - a.first_lpage;
-    const long long slot = (long long)a.pages[lp] * PAGE + (p & (PAGE - 1));
-    const int pos = a.positions ? a.positions[r] : p;
-    slots[r] = slot;
-    rowpos[r] = pos;
-    kpos[slot] = pos;
-  }
-}
-
-hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
-                               int* kpos, hipStream_t st) {
-  (void)launch(k_append_setup, 1, 256, 0, st, a, bt, slots, rowpos, kpos);
-  return hipGetLastError();
-}
-
-// the batched form: thread r finds its sequence by the row offsets (at most MAX_BANDS)
+// the batched append's setup: thread r finds its sequence by the row offsets (at most
+// MAX_BANDS); the single-sequence append's setup is done by its row kernel (below)
 __global__ __launch_bounds__(256) void k_append_batch_setup(AppendBatchArgs a, int* __restrict__ bt,
                                                             long long* __restrict__ slots,
                                                             int* __restrict__ rowpos,
@@ -321,21 +302,52 @@ hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long lon
   return hipGetLastError();
 }
 
+// The single-sequence append's setup, done by the row kernel (SETUP): row r's slot
+// (pages[logical page] * 16 + position % 16, positions kv_len + r onwards in the cache) and
+// stamped position (the caller's, else kv_len + r), written into slots, rowpos and the pool's
+// kpos; workgroup 0 also writes the new block-table entries.
+struct RowsSetup {
+  AppendArgs a;
+  int* bt;
+  long long* slots;
+  int* rowpos;
+  int* kpos;
+};
+
 // one workgroup per row: the sum of the row's S split-K partials, RMSNorm'd; optionally the
-// row's RoPE (cos, sin) pairs for the fused K/V epilogue (one thread per pair)
+// row's RoPE (cos, sin) pairs for the fused K/V epilogue (one thread per pair), and (SETUP)
+// the append's slots, positions and block tables
+template <bool SETUP>
 __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__ X, int S, long long ps,
                                                        int gsz, int h, const bf16* __restrict__ w, float eps,
                                                        bf16* __restrict__ out,
                                                        bf16* __restrict__ out_lo,
                                                        const int* __restrict__ rowpos,
                                                        const double* __restrict__ inv_freq, int half,
-                                                       float2* __restrict__ cs) {
+                                                       float2* __restrict__ cs,
+                                                       std::conditional_t<SETUP, RowsSetup, int> su) {
   __shared__ __attribute__((aligned(16))) float xs[RN_HMAX];
   __shared__ float red_ss[16];
   const int r = blockIdx.x;
+  int pos = 0;
+  if constexpr (SETUP) {
+    const AppendArgs& a = su.a;
+    if (r == 0)
+      for (int j = threadIdx.x; j < a.n_upd; j += blockDim.x) su.bt[a.upd_off[j]] = a.upd_page[j];
+    const int p = a.kv_len + r;
+    const long long slot = (long long)a.pages[(p >> 4) - a.first_lpage] * PAGE + (p & (PAGE - 1));
+    pos = a.positions ? a.positions[r] : p;
+    if (threadIdx.x == 0) {
+      su.slots[r] = slot;
+      su.rowpos[r] = pos;
+      su.kpos[slot] = pos;
+    }
+  } else {
+    if (cs) pos = rowpos[r];
+  }
   if (cs && (int)threadIdx.x < half) {
     double sn, cn;
-    sincos((double)rowpos[r] * inv_freq[threadIdx.x], &sn, &cn);
+    sincos((double)pos * inv_freq[threadIdx.x], &sn, &cn);
     cs[(size_t)r * half + threadIdx.x] = make_float2((float)cn, (float)sn);
   }
   const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, gsz, h, xs, red_ss);
@@ -345,11 +357,19 @@ __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__
 
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st,
-                               const int* rowpos, const double* inv_freq, int half, float2* cs) {
+                               const int* rowpos, const double* inv_freq, int half, float2* cs,
+                               const AppendArgs* setup, int* bt, long long* slots, int* rowpos_out, int* kpos) {
   if (h > RN_HMAX || h % 4 || gsz < 1) return hipErrorInvalidValue;
-  if (cs && (!rowpos || !inv_freq || half < 1 || half > (int)rn_threads(h))) return hipErrorInvalidValue;
-  (void)launch(k_rows_rmsnorm, M, rn_threads(h), 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo, rowpos,
-               inv_freq, half, cs);
+  if (cs && (!inv_freq || half < 1 || half > (int)rn_threads(h) || (!setup && !rowpos))) return hipErrorInvalidValue;
+  if (setup) {
+    if (setup->n != M || !bt || !slots || !rowpos_out || !kpos) return hipErrorInvalidValue;
+    const RowsSetup su{*setup, bt, slots, rowpos_out, kpos};
+    (void)launch(k_rows_rmsnorm<true>, M, rn_threads(h), 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo,
+                 rowpos, inv_freq, half, cs, su);
+  } else {
+    (void)launch(k_rows_rmsnorm<false>, M, rn_threads(h), 0, st, X, S, part_stride, gsz, h, w, eps, out, out_lo,
+                 rowpos, inv_freq, half, cs, 0);
+  }
   return hipGetLastError();
 }
 

@@ -233,17 +233,19 @@ hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const 
                                bf16* out, bf16* out_lo, hipStream_t st);
 
 // ---- context append (k_misc.hip) -----------------------------------------------------
-hipError_t launch_append_setup(const AppendArgs& a, int* bt, long long* slots, int* rowpos,
-                               int* kpos, hipStream_t st);
 hipError_t launch_append_batch_setup(const AppendBatchArgs& a, int* bt, long long* slots, int* rowpos,
                                      int* kpos, hipStream_t st);
 // inputs are split-K partials X[s][M][...] added in the canonical order (S = 1, gsz = 1 for a
 // plain result). With cs non-null, row r also writes its RoPE (cos, sin) pairs at position
-// rowpos[r] into cs[r][0..half) (angles in double precision, then rounded to float).
+// rowpos[r] into cs[r][0..half) (angles in double precision, then rounded to float). With
+// setup non-null (M = setup->n), the launch also does the single-sequence append's setup for
+// those rows (their slots, stamped positions and the new block-table entries into slots,
+// rowpos_out, kpos and bt), and the angles use the positions it stamps.
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
                                const bf16* w, float eps, bf16* out, bf16* out_lo, hipStream_t st,
                                const int* rowpos = nullptr, const double* inv_freq = nullptr, int half = 0,
-                               float2* cs = nullptr);
+                               float2* cs = nullptr, const AppendArgs* setup = nullptr, int* bt = nullptr,
+                               long long* slots = nullptr, int* rowpos_out = nullptr, int* kpos = nullptr);
 hipError_t launch_kv_append_post(const float* KV, int S, long long part_stride, int gsz, int n, int L,
                                  const bf16* k_norm_all, float eps, const double* inv_freq, float mscale,
                                  const long long* slots, const int* rowpos, KvGeom g, hipStream_t st);

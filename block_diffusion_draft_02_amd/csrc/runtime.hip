@@ -430,9 +430,11 @@ void release(dflash_ctx* c) {
 
 }  // namespace
 
-// fc + hidden_norm + the fused K/V GEMM + k_norm/RoPE/writeback for nc context rows whose
-// slots and positions are already on the device (c->slots, c->rowpos)
-int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st) {
+// fc + hidden_norm + the fused K/V GEMM + k_norm/RoPE/writeback for nc context rows. With
+// setup, the row kernel after the fc GEMM first writes the rows' slots, positions and block
+// tables (the fc GEMM needs none of them); otherwise they are already on the device
+// (c->slots, c->rowpos)
+int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st, const AppendArgs* setup) {
   const KvGeom g = geom(c);
   const int nkv2 = c->L * 2 * c->kvd;
   if (nc <= APPEND_BATCH_ROWS) {
@@ -450,7 +452,8 @@ int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st) 
                   : launch_gemm_skinny(Hc, nullptr, ld, nc, c->fc_t, c->h, ld, c->g_fc.klen, c->part, ps_fc, true, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
-      return launch_rows_rmsnorm(c->part, S_fc, ps_fc, G_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st);
+      return launch_rows_rmsnorm(c->part, S_fc, ps_fc, G_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb, c->Fb_lo, st,
+                                 nullptr, nullptr, 0, nullptr, setup, c->bt_dev, c->slots, c->rowpos, c->kpos);
     }));
     HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
       return wide ? launch_gemm_wide(c->Fb, c->Fb_lo, c->h, nc, c->w_kv_t, nkv2, c->h, c->g_kvapp.gsz, c->part, ps_kv,
@@ -473,7 +476,8 @@ int append_chain(dflash_ctx* c, const bf16* Hc, int ld, int nc, hipStream_t st) 
   }));
   HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] {
     return launch_rows_rmsnorm(c->F32, ks_fc, (long long)nc * c->h, ks_fc, nc, c->h, c->hidden_norm, c->eps, c->Fb,
-                               c->Fb_lo, st, c->rowpos, c->inv_freq, c->hd / 2, c->kv_fused ? c->rope_cs : nullptr);
+                               c->Fb_lo, st, c->rowpos, c->inv_freq, c->hd / 2, c->kv_fused ? c->rope_cs : nullptr,
+                               setup, c->bt_dev, c->slots, c->rowpos, c->kpos);
   }));
   if (c->kv_fused) {
     HIPCHK(c, timed(c, DFLASH_K_APPEND_GEMM, st, [&] {
@@ -899,10 +903,11 @@ int dflash_ctx_kv_append(dflash_ctx* c, int32_t seq, const void* target_hidden,
       HIPCHK(c, hipMemcpyAsync(dp, hp, (size_t)nc * sizeof(int), hipMemcpyHostToDevice, st));
       a.positions = dp;
     }
-    HIPCHK(c, timed(c, DFLASH_K_APPEND_MISC, st, [&] { return launch_append_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st); }));
-    if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
-    const int rc = append_chain(c, (const bf16*)target_hidden + (size_t)r0 * ld, ld, nc, st);
+    // (the row kernel of the chain does this chunk's setup, reading the positions the ring
+    // slot holds; the slot is free again once the chain has run)
+    const int rc = append_chain(c, (const bf16*)target_hidden + (size_t)r0 * ld, ld, nc, st, &a);
     if (rc != DFLASH_OK) return rc;
+    if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
   }
   for (int i = 0; i < n; ++i) s.pos.push_back(positions ? positions[i] : C + i);
   s.kv_len = C + n;
@@ -991,7 +996,7 @@ int dflash_ctx_kv_append_batch(dflash_ctx* c, int32_t n_seqs, const int32_t* seq
     return launch_append_batch_setup(a, c->bt_dev, c->slots, c->rowpos, c->kpos, st);
   }));
   if (slot >= 0) HIPCHK(c, hipEventRecord(c->ring_ev[slot], st));
-  const int rc = append_chain(c, (const bf16*)target_hidden, c->T * c->Ht, (int)total, st);
+  const int rc = append_chain(c, (const bf16*)target_hidden, c->T * c->Ht, (int)total, st, nullptr);
   if (rc != DFLASH_OK) return rc;
   long long r = 0;
   for (int b = 0; b < n_seqs; ++b) {
