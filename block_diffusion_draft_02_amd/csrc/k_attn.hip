@@ -311,7 +311,10 @@ __device__ __forceinline__ void attn_reg_wg(AttnLds<HD>& sm, int id, const bf16*
 // loads of slice j: one barrier per slice. A wave's state covers its rows over the whole
 // chunk, so it writes the chunk's partials itself.
 constexpr int DMA_HD = 128;
-constexpr int DMA_RING = 3;
+constexpr int DMA_RING = 3;        // ring slots of the LDS path in the launch shared with the register path
+#ifndef ATTN_LDS_RING
+#define ATTN_LDS_RING 3            // ring slots of the LDS path's own launch
+#endif
 
 struct DmaSlice {
   bf16 k[2][PAGE * DMA_HD];   // two K pages [16 keys][128], units swizzled within a row
@@ -321,28 +324,34 @@ struct DmaSlice {
 // s_waitcnt with vmcnt <= N (vmcnt[3:0] | vmcnt[5:4] << 14; expcnt and lgkmcnt left at maximum)
 #define DFL_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-__device__ __forceinline__ void compute_dma(const bf16x8 (&kf)[2][4], const bf16x8 (&vf)[8], const bf16x8 (&qh)[2][4],
-                                            const bf16x8 (&ql)[2][4], bool full, int lim, float scale_log2,
-                                            float (&m_run)[2], float (&l_run)[2], f32x4 (&o)[2][8]) {
+// One slice for a wave's RT row tiles. `loadv` reads the slice's V fragments from LDS: with two
+// tiles before the scores (both tiles' products use them), with one only after the softmax,
+// when the K fragments are dead, so that a wave fits in 128 registers.
+template <int RT, class LoadV>
+__device__ __forceinline__ void compute_dma(const bf16x8 (&kf)[2][4], LoadV&& loadv, const bf16x8 (&qh)[RT][4],
+                                            const bf16x8 (&ql)[RT][4], bool full, int lim, float scale_log2,
+                                            float (&m_run)[RT], float (&l_run)[RT], f32x4 (&o)[RT][8]) {
+  bf16x8 vf[8];
+  if constexpr (RT > 1) loadv(vf);
   // S^T = K Q^T, the hi then the lo query term at every k-step (as the register kernel)
-  f32x4 sh[2][2];
+  f32x4 sh[RT][2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int t = 0; t < 2; ++t) sh[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(kf[t][s], qh[rt][s], sh[rt][t]);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int t = 0; t < 2; ++t) sh[rt][t] = mfma16(kf[t][s], ql[rt][s], sh[rt][t]);
   }
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     float sv[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -371,22 +380,38 @@ __device__ __forceinline__ void compute_dma(const bf16x8 (&kf)[2][4], const bf16
       l_run[rt] += sv[e];
     }
     const bf16x8 pb = __builtin_convertvector((f32x8){sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]}, bf16x8);
+    if constexpr (RT == 1) loadv(vf);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[rt][dt] = mfma16(vf[dt], pb, o[rt][dt]);
   }
 }
 
-struct DmaLds {
-  DmaSlice ring[DMA_RING];
+template <int NR>
+struct DmaLdsT {
+  DmaSlice ring[NR];
   int page[ATTN_CHUNK_PAGES_MAX];
 };
+using DmaLds = DmaLdsT<DMA_RING>;
 
-// the LDS path's workgroup `item` (one per (chunk, kv head) of the LDS-path bands)
-__device__ __forceinline__ void attn_lds_wg(DmaLds& sm, int item, const bf16* __restrict__ Q,
+// wait until at most `ahead` slices' loads (IPW instructions each) of this wave are in flight
+template <int IPW>
+__device__ __forceinline__ void wait_slices(int ahead) {
+  if (ahead >= 3) DFL_WAIT_VM(3 * IPW);
+  else if (ahead == 2) DFL_WAIT_VM(2 * IPW);
+  else if (ahead == 1) DFL_WAIT_VM(IPW);
+  else DFL_WAIT_VM(0);
+}
+
+// the LDS path's workgroup `item` (one per (chunk, kv head) of the LDS-path bands): 8 / RT
+// waves, each with RT 16-row tiles of the item's query rows, slices through a ring of NR slots
+// (NR - 1 requested ahead)
+template <int RT, int NR>
+__device__ __forceinline__ void attn_lds_wg(DmaLdsT<NR>& sm, int item, const bf16* __restrict__ Q,
                                             const bf16* __restrict__ Q_lo, const AttnBands& ab, int gamma, int nh,
                                             const KvGeom& g, int layer, float scale_log2,
                                             float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int HD = DMA_HD, NS = HD / 32, ND = HD / 16, UPR = HD / 8;
+  constexpr int NW = 8 / RT, IPW = 16 / NW;   // waves; 1 KB load instructions a wave and slice
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, grp = lane >> 4;
@@ -402,57 +427,79 @@ __device__ __forceinline__ void attn_lds_wg(DmaLds& sm, int item, const bf16* __
   const int nkeys = k1 - k0;
   const int npg = (nkeys + PAGE - 1) / PAGE;
   const int R = gamma * G;
-  const bool active = wave * 32 < R;   // waves past the query rows only move K/V
+  const bool active = wave * 16 * RT < R;   // waves past the query rows only move K/V
   const size_t pl = page_layer_elems(nkv, HD);
   const bf16* lpool = g.pool + (size_t)layer * g.num_pages * pl;
   const int* bt = g.bt + (size_t)seq * g.per_seq + (k0 >> 4);
-  for (int i = threadIdx.x; i < min(npg, ATTN_CHUNK_PAGES_MAX); i += 256) sm.page[i] = bt[i];
-  __syncthreads();   // the page ids
-
-  // this wave's query rows r = 32 wave + 16 rt + c (block row r % gamma of query head
+  // this wave's query rows r = 16 (RT wave + rt) + c (block row r % gamma of query head
   // r / gamma of the kv head's group; rows past R are zero) as S^T operands: dims
   // s*32 + grp*8 .. +7
-  bf16x8 qh[2][NS], ql[2][NS];
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x4 o[2][ND];
+  bf16x8 qh[RT][NS], ql[RT][NS];
+  float m_run[RT], l_run[RT];
+  f32x4 o[RT][ND];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt) m_run[rt] = -INFINITY, l_run[rt] = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the query rows first, so that their loads overlap the page ids'
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = (wave * RT + rt) * 16 + c;
+    const size_t qo = ((size_t)(b * gamma + r % gamma) * nh + kvh * G + r / gamma) * HD + grp * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qh[rt][s] = r < R ? ld8(Q + qo + s * 32) : bf16x8{};
+      ql[rt][s] = r < R ? ld8(Q_lo + qo + s * 32) : bf16x8{};
+    }
+  }
+  for (int i = threadIdx.x; i < min(npg, ATTN_CHUNK_PAGES_MAX); i += NW * 64) sm.page[i] = bt[i];
+  __syncthreads();   // the page ids
+  DFL_WAIT_VM(0);    // and the query rows, in every wave, before the first slice is requested
+
   const int nsl = (nkeys + 31) / 32;
-  // request slice j into ring slot d: this wave's page (K or V, page wave%2); the zeroed
-  // sentinel page 0 past the chunk; four 1 KB instructions a wave
+  // request slice j into ring slot d: the slice's four pages (K0, K1, V0, V1; the zeroed
+  // sentinel page 0 past the chunk) are 16 1 KB instructions, IPW of them this wave's:
+  // instruction q of page (wave IPW + i) / 4, q = (wave IPW + i) % 4
   auto issue = [&](DmaSlice& d, int j) {
-    const int p = wave & 1;
-    const int lp = j * 2 + p;
-    const int pgid = lp < npg ? sm.page[min(lp, ATTN_CHUNK_PAGES_MAX - 1)] : 0;
-    if ((wave & 2) == 0) {
-      const bf16* src = lpool + (size_t)pgid * pl + (size_t)kvh * PAGE * HD;
+    constexpr int PPW = IPW >= 4 ? IPW / 4 : 1;   // pages a wave touches
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int P = q * 64 + lane;
-        const int rr = P / UPR, u = (P % UPR) ^ ((rr ^ (4 * p)) & (UPR - 1));
-        __builtin_amdgcn_global_load_lds(src + rr * HD + u * 8, &d.k[p][q * 512], 16, 0, 0);
-      }
-    } else {
-      const bf16* src = lpool + (size_t)pgid * pl + (size_t)(nkv + kvh) * HD * PAGE;
+    for (int pi = 0; pi < PPW; ++pi) {
+      const int pg = (wave * IPW) / 4 + pi;
+      const int p = pg & 1;
+      const int lp = j * 2 + p;
+      const int pgid = lp < npg ? sm.page[min(lp, ATTN_CHUNK_PAGES_MAX - 1)] : 0;
+      constexpr int QN = IPW >= 4 ? 4 : IPW;
+      const int q0 = IPW >= 4 ? 0 : (wave * IPW) % 4;
+      if (pg < 2) {
+        const bf16* src = lpool + (size_t)pgid * pl + (size_t)kvh * PAGE * HD;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int P = q * 64 + lane;
-        const int dd = P >> 1, h = (P & 1) ^ ((dd >> 3) & 1);
-        __builtin_amdgcn_global_load_lds(src + dd * PAGE + h * 8, &d.v[p][q * 512], 16, 0, 0);
+        for (int qi = 0; qi < QN; ++qi) {
+          const int P = (q0 + qi) * 64 + lane;
+          const int rr = P / UPR, u = (P % UPR) ^ ((rr ^ (4 * p)) & (UPR - 1));
+          __builtin_amdgcn_global_load_lds(src + rr * HD + u * 8, &d.k[p][(q0 + qi) * 512], 16, 0, 0);
+        }
+      } else {
+        const bf16* src = lpool + (size_t)pgid * pl + (size_t)(nkv + kvh) * HD * PAGE;
+#pragma unroll
+        for (int qi = 0; qi < QN; ++qi) {
+          const int P = (q0 + qi) * 64 + lane;
+          const int dd = P >> 1, h = (P & 1) ^ ((dd >> 3) & 1);
+          __builtin_amdgcn_global_load_lds(src + dd * PAGE + h * 8, &d.v[p][(q0 + qi) * 512], 16, 0, 0);
+        }
       }
     }
   };
-  // one slice: this wave's loads of slice j are done once at most the next slice's four are
-  // in flight; the barrier then makes every wave's share visible and ends every wave's reads
-  // of the slot (nxt) that slice j + 2 now overwrites
+  // one slice: this wave's loads of slice j are done once at most those of slices j + 1 ..
+  // j + NR - 2 are in flight; the barrier then makes every wave's share visible and ends every
+  // wave's reads of the slot (nxt, slice j - 1's) that slice j + NR - 1 now overwrites
   auto step = [&](int j, const DmaSlice& sl, DmaSlice& nxt) {
-    if (j + 1 < nsl) DFL_WAIT_VM(4); else DFL_WAIT_VM(0);
+    wait_slices<IPW>(min(NR - 2, nsl - 1 - j));
     __builtin_amdgcn_s_barrier();
-    if (j + 2 < nsl) issue(nxt, j + 2);
+    if (j + NR - 1 < nsl) issue(nxt, j + NR - 1);
     if (!active) return;
-    bf16x8 kf[2][NS], vf[ND];
+    bf16x8 kf[2][NS];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int kk = (c >> 2) * 8 + t * 4 + (c & 3);
@@ -463,7 +510,7 @@ __device__ __forceinline__ void attn_lds_wg(DmaLds& sm, int item, const bf16* __
         kf[t][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sl.k[p][rr * HD + u * 8]));
       }
     }
-    {
+    auto loadv = [&](bf16x8 (&vf)[ND]) {
       const int p = grp >> 1, h = grp & 1;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
@@ -471,34 +518,25 @@ __device__ __forceinline__ void attn_lds_wg(DmaLds& sm, int item, const bf16* __
         const int hq = h ^ ((dd >> 3) & 1);
         vf[dt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sl.v[p][dd * PAGE + hq * 8]));
       }
-    }
+    };
     const int kt = j * 32;
-    compute_dma(kf, vf, qh, ql, nkeys - kt >= 32, nkeys - kt - grp * 8, scale_log2, m_run, l_run, o);
+    compute_dma<RT>(kf, loadv, qh, ql, nkeys - kt >= 32, nkeys - kt - grp * 8, scale_log2, m_run, l_run, o);
   };
-  // the first slice, then the wave's query rows, then the second slice, all in flight
-  // together (the compiler waits for all of them at the loop's entry)
-  issue(sm.ring[0], 0);
+  // slices 0 .. NR - 2 in flight before the loop (the query rows are already in registers, so
+  // no load but the ring's is pending inside it)
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = wave * 32 + rt * 16 + c;
-    const size_t qo = ((size_t)(b * gamma + r % gamma) * nh + kvh * G + r / gamma) * HD + grp * 8;
+  for (int i = 0; i < NR - 1; ++i)
+    if (i < nsl) issue(sm.ring[i], i);
+  for (int j0 = 0; j0 < nsl; j0 += NR) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qh[rt][s] = r < R ? ld8(Q + qo + s * 32) : bf16x8{};
-      ql[rt][s] = r < R ? ld8(Q_lo + qo + s * 32) : bf16x8{};
-    }
-  }
-  if (nsl > 1) issue(sm.ring[1], 1);
-  for (int j0 = 0; j0 < nsl; j0 += DMA_RING) {
-    step(j0, sm.ring[0], sm.ring[2]);
-    if (j0 + 1 < nsl) step(j0 + 1, sm.ring[1], sm.ring[0]);
-    if (j0 + 2 < nsl) step(j0 + 2, sm.ring[2], sm.ring[1]);
+    for (int r = 0; r < NR; ++r)
+      if (j0 + r < nsl) step(j0 + r, sm.ring[r], sm.ring[(r + NR - 1) % NR]);
   }
 
   // the wave's state is the chunk's partial of its rows (maximum in the exp2 domain)
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = wave * 32 + rt * 16 + c;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = (wave * RT + rt) * 16 + c;
     float lt = l_run[rt];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
@@ -536,7 +574,7 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int id = blockIdx.x;
   if constexpr (HD == DMA_HD && !WIN) {
     if (id < n_lds_items) {
-      attn_lds_wg(sm.d, id, Q, Q_lo, ab, gamma, nh, g, layer, scale_log2, part_o, part_ml);
+      attn_lds_wg<2, DMA_RING>(sm.d, id, Q, Q_lo, ab, gamma, nh, g, layer, scale_log2, part_o, part_ml);
       return;
     }
   }
@@ -544,6 +582,16 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                        scale_log2, part_o, part_ml);
 }
 
+
+// The LDS path alone (a plan with no register-path chunk): eight waves of one 16-row tile
+// each, held to 128 registers, so that with the ring and page ids alone in LDS (50 KB) two
+// workgroups share a CU at four waves a SIMD.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_block_attn_lds(
+    const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo, const AttnBands ab, int gamma, int nh, KvGeom g,
+    int layer, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) DmaLdsT<ATTN_LDS_RING> sm;
+  attn_lds_wg<1, ATTN_LDS_RING>(sm, blockIdx.x, Q, Q_lo, ab, gamma, nh, g, layer, scale_log2, part_o, part_ml);
+}
 
 void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, int gamma, AttnBands& out,
                int& reg_chunks, int& lds_chunks) {
@@ -585,6 +633,11 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& b
     return hipErrorInvalidValue;
   if (lds_chunks > 0 && (g.hd != DMA_HD || window > 0 || sw != 0)) return hipErrorInvalidValue;
   const int n_items = reg_chunks * g.nkv, n_lds = lds_chunks * g.nkv;
+  if (n_items == 0) {
+    (void)launch(k_block_attn_lds, dim3(n_lds), 512, 0, st, Q, Q_lo, bands, gamma, nh, g, layer, scale_log2, part_o,
+                 part_ml);
+    return hipGetLastError();
+  }
   const int nrg = (R + RG - 1) / RG;
   const dim3 grid(n_lds + ((n_items + 7) / 8) * 8 * nrg);
 #define DFL_ATTN(HDV, W) (void)launch(k_block_attn<HDV, W>, grid, AW * 64, 0, st, Q, Q_lo, bands, n_lds, n_items, nrg, gamma, nh, g, layer, sw, window, scale_log2, part_o, part_ml)
@@ -600,13 +653,14 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& b
 }
 
 // Merge a band's chunk partials into the attention output (hi + lo bf16 terms). One
-// workgroup per (band, kv head, CMB_ROWS query rows; four, so that even one band spreads
-// over 128 workgroups); thread (row, 4-float slice, chunk group q)
-// folds chunks q, q + CQ, q + 2CQ, ... with a running maximum, all of its loads issued at
-// once; the CQ groups are then merged in group order. The order depends only on the band's
-// own chunk count.
+// workgroup per (band, kv head, RB blocks of CMB_ROWS query rows; blocks of four rows, so
+// that even one band spreads over 128 workgroups); thread (row, 4-float slice, chunk group q)
+// folds chunks q, q + CQ, q + 2CQ, ... (JM slots, at least the band's chunk count over CQ)
+// with a running maximum, all of its loads issued at once; the CQ groups are then merged in
+// group order. The order depends only on the band's own chunk count: JM and RB change how
+// many loads a thread has in flight, not what any output element adds in which order.
 constexpr int CMB_ROWS = 4;
-template <int HD>
+template <int HD, int JM, int RB>
 __global__ __launch_bounds__(1024) void k_attn_combine(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml,
                                                        const Band* __restrict__ bands, int gamma,
@@ -616,81 +670,113 @@ __global__ __launch_bounds__(1024) void k_attn_combine(const float* __restrict__
   constexpr int NSL = HD / 4;             // 4-float slices per row
   constexpr int CR = CMB_ROWS;
   constexpr int CQ = 1024 / (CR * NSL);   // chunk groups
-  constexpr int JM = NCH_MAX / CQ;        // chunks per group at most
-  __shared__ f32x4 red_o[CQ][CR][NSL];
-  __shared__ float red_m[CQ][CR], red_l[CQ][CR];
+  __shared__ f32x4 red_o[RB][CQ][CR][NSL];
+  __shared__ float red_m[RB][CQ][CR], red_l[RB][CQ][CR];
   const int b = blockIdx.x, kvh = blockIdx.y;
   const int q = threadIdx.x / (CR * NSL);
   const int row = (threadIdx.x / NSL) % CR, slc = threadIdx.x % NSL;
-  const int r = blockIdx.z * CR + row;
   const int G = nh / nkv;
-  const bool rv = r < gamma * G;
+  const int R = gamma * G;
   const int nch = bands[b].nch[sw], base = bands[b].base[sw];
-  float mc[JM], lc[JM];
-  f32x4 oc[JM];
+  float mc[RB][JM], lc[RB][JM];
+  f32x4 oc[RB][JM];
 #pragma unroll
-  for (int j = 0; j < JM; ++j) {
-    const int cc = q + j * CQ;
-    if (rv && cc < nch) {
-      const size_t it = ((size_t)(base + cc) * nkv + kvh) * RPAD + r;
-      mc[j] = part_ml[it * 2];
-      lc[j] = part_ml[it * 2 + 1];
-      oc[j] = *reinterpret_cast<const f32x4*>(part_o + it * HD + slc * 4);
-    } else {
-      mc[j] = -INFINITY;
-      lc[j] = 0.f;
-      oc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = (blockIdx.z * RB + rb) * CR + row;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+      const int cc = q + j * CQ;
+      if (r < R && cc < nch) {
+        const size_t it = ((size_t)(base + cc) * nkv + kvh) * RPAD + r;
+        mc[rb][j] = part_ml[it * 2];
+        lc[rb][j] = part_ml[it * 2 + 1];
+        oc[rb][j] = *reinterpret_cast<const f32x4*>(part_o + it * HD + slc * 4);
+      } else {
+        mc[rb][j] = -INFINITY;
+        lc[rb][j] = 0.f;
+        oc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   }
-  float M = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < JM; ++j) M = fmaxf(M, mc[j]);
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < JM; ++j) {
-    const float w = (mc[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc[j] - M);
-    acc += w * oc[j];
-    L += w * lc[j];
-  }
-  red_o[q][row][slc] = acc;
-  if (slc == 0) {
-    red_m[q][row] = M;
-    red_l[q][row] = L;
+    for (int j = 0; j < JM; ++j) M = fmaxf(M, mc[rb][j]);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+      const float w = (mc[rb][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc[rb][j] - M);
+      acc += w * oc[rb][j];
+      L += w * lc[rb][j];
+    }
+    red_o[rb][q][row][slc] = acc;
+    if (slc == 0) {
+      red_m[rb][q][row] = M;
+      red_l[rb][q][row] = L;
+    }
   }
   __syncthreads();
-  if (q != 0 || !rv) return;
-  float Mt = -INFINITY;
+  if (q != 0) return;
 #pragma unroll
-  for (int g2 = 0; g2 < CQ; ++g2) Mt = fmaxf(Mt, red_m[g2][row]);
-  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-  float Lt = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = (blockIdx.z * RB + rb) * CR + row;
+    if (r >= R) continue;
+    float Mt = -INFINITY;
 #pragma unroll
-  for (int g2 = 0; g2 < CQ; ++g2) {
-    const float mg = red_m[g2][row];
-    const float w = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mg - Mt);
-    tot += w * red_o[g2][row][slc];
-    Lt += w * red_l[g2][row];
+    for (int g2 = 0; g2 < CQ; ++g2) Mt = fmaxf(Mt, red_m[rb][g2][row]);
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+    float Lt = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < CQ; ++g2) {
+      const float mg = red_m[rb][g2][row];
+      const float w = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mg - Mt);
+      tot += w * red_o[rb][g2][row][slc];
+      Lt += w * red_l[rb][g2][row];
+    }
+    const float inv = 1.f / Lt;
+    const int i = r % gamma, hq = r / gamma;
+    const size_t o = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + slc * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(tot[e] * inv, out[o + e], out_lo[o + e]);
   }
-  const float inv = 1.f / Lt;
-  const int i = r % gamma, hq = r / gamma;
-  const size_t o = ((size_t)(b * gamma + i) * nh + kvh * G + hq) * HD + slc * 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) split_bf16(tot[e] * inv, out[o + e], out_lo[o + e]);
+}
+
+template <int HD>
+hipError_t launch_combine_hd(const float* part_o, const float* part_ml, const Band* bands_dev, int n_bands,
+                             int max_nch, int gamma, int nh, int nkv, int sw, bf16* out, bf16* out_lo,
+                             hipStream_t st) {
+  constexpr int CQ = 1024 / (CMB_ROWS * (HD / 4));
+  constexpr int JS = (16 + CQ - 1) / CQ;   // slots for bands of up to 16 chunks
+  constexpr int JX = NCH_MAX / CQ;         // slots for any band
+  const int groups = (gamma * (nh / nkv) + CMB_ROWS - 1) / CMB_ROWS;
+  // four row blocks a workgroup once the call has rows for more than 2048 single blocks (then
+  // every thread keeps 4 JS loads in flight and the launch fills the chip in about two rounds)
+  const bool wide = max_nch <= JS * CQ && (long long)n_bands * nkv * groups > 2048;
+  if (wide) {
+    const dim3 grid(n_bands, nkv, (groups + 3) / 4);
+    (void)launch(k_attn_combine<HD, JS, 4>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo);
+  } else if (max_nch <= JS * CQ) {
+    (void)launch(k_attn_combine<HD, JS, 1>, dim3(n_bands, nkv, groups), 1024, 0, st, part_o, part_ml, bands_dev,
+                 gamma, nh, nkv, sw, out, out_lo);
+  } else {
+    (void)launch(k_attn_combine<HD, JX, 1>, dim3(n_bands, nkv, groups), 1024, 0, st, part_o, part_ml, bands_dev,
+                 gamma, nh, nkv, sw, out, out_lo);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,
-                               int n_bands, int gamma, int nh, int nkv, int hd, int sw,
+                               int n_bands, int max_nch, int gamma, int nh, int nkv, int hd, int sw,
                                bf16* out, bf16* out_lo, hipStream_t st) {
-  const int G = nh / nkv;
-  dim3 grid(n_bands, nkv, (gamma * G + CMB_ROWS - 1) / CMB_ROWS);
+  if (max_nch < 1 || max_nch > NCH_MAX) return hipErrorInvalidValue;
   switch (hd) {
-    case 32: (void)launch(k_attn_combine<32>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
-    case 64: (void)launch(k_attn_combine<64>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
-    case 128: (void)launch(k_attn_combine<128>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo); break;
+    case 32: return launch_combine_hd<32>(part_o, part_ml, bands_dev, n_bands, max_nch, gamma, nh, nkv, sw, out, out_lo, st);
+    case 64: return launch_combine_hd<64>(part_o, part_ml, bands_dev, n_bands, max_nch, gamma, nh, nkv, sw, out, out_lo, st);
+    case 128: return launch_combine_hd<128>(part_o, part_ml, bands_dev, n_bands, max_nch, gamma, nh, nkv, sw, out, out_lo, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace dfl

@@ -229,7 +229,7 @@ hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& b
                              int gamma, int nh, KvGeom g, int layer, int sw, int window,
                              float scale_log2, float* part_o, float* part_ml, hipStream_t st);
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, const Band* bands_dev,
-                               int n_bands, int gamma, int nh, int nkv, int hd, int sw,
+                               int n_bands, int max_nch, int gamma, int nh, int nkv, int hd, int sw,
                                bf16* out, bf16* out_lo, hipStream_t st);
 
 // ---- context append (k_misc.hip) -----------------------------------------------------

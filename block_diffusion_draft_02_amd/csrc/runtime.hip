@@ -1220,7 +1220,9 @@ int block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int3
                                sw ? c->window : 0, scale_log2, sc.aparts_o, sc.aparts_ml, st);
     }));
     HIPCHK(c, timed(c, DFLASH_K_ATTN_COMBINE, st, [&] {
-      return launch_attn_combine(sc.aparts_o, sc.aparts_ml, c->bands_dev, n_seqs, gamma, c->nh,
+      int max_nch = 1;
+      for (int b = 0; b < n_seqs; ++b) max_nch = std::max(max_nch, a.bands[b].nch[sw]);
+      return launch_attn_combine(sc.aparts_o, sc.aparts_ml, c->bands_dev, n_seqs, max_nch, gamma, c->nh,
                                  c->nkv, c->hd, sw, c->attn, c->attn_lo, st);
     }));
     HIPCHK(c, capture(c->cap_a, c->attn, (size_t)c->qd * 2));
