@@ -418,9 +418,11 @@ __device__ __forceinline__ void attn_lds_wg(DmaLdsT<NR>& sm, int item, const bf1
   const int nkv = g.nkv;
   const int cd = item / nkv, kvh = item - cd * nkv;
   const int G = nh / nkv;
-  const int bl = attn_band(ab, cd, true, 0), b = bl;
+  int run = 0;   // the dispatch run holding cd
+  while (run + 1 < ab.n_lg && cd >= ab.lg_start[run + 1]) ++run;
+  const int bl = ab.lg_band[run], b = bl;
   const int seq = ab.b[bl].seq, C = ab.b[bl].kv_len;
-  const int ch = cd - ab.dbase[bl];
+  const int ch = ab.lg_chunk[run] + (cd - ab.lg_start[run]);
   const size_t pitem = (size_t)(ab.b[bl].base[0] + ch) * nkv + kvh;   // the call-wide partial slot
   const int k0 = ab.b[bl].kstart[0] + ch * ab.b[bl].ck[0];   // page aligned
   const int k1 = min(k0 + ab.b[bl].ck[0], C + gamma);
@@ -621,6 +623,40 @@ void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_pa
     out.dbase[b] = nch;
     nch += bands[b].nch[sw];
   }
+  // the LDS path's dispatch order: every chunk longest first. A band's full chunks form one
+  // run (in the order above, whose chunk widths fall), its last chunk another; the last chunks
+  // are sorted by their own length and merged in (full runs first on ties). Only the order in
+  // which workgroups start changes: a chunk's partial slot stays base + chunk.
+  out.n_lg = 0;
+  if (lds_chunks == 0) return;
+  int last[MAX_BANDS], nl = 0;
+  auto last_len = [&](int b) {
+    const Band& B = bands[b];
+    return B.kv_len + gamma - B.kstart[sw] - (B.nch[sw] - 1) * B.ck[sw];
+  };
+  for (int i = 0; i < n; ++i) {
+    const int b = order[i];
+    if (!((out.lds_mask >> b) & 1u)) continue;
+    int j = nl++;
+    for (; j > 0 && last_len(last[j - 1]) < last_len(b); --j) last[j] = last[j - 1];
+    last[j] = b;
+  }
+  int pos = 0, il = 0;
+  auto run = [&](int b, int c0, int cnt) {
+    out.lg_start[out.n_lg] = (unsigned short)pos;
+    out.lg_band[out.n_lg] = (unsigned char)b;
+    out.lg_chunk[out.n_lg] = (unsigned char)c0;
+    ++out.n_lg;
+    pos += cnt;
+  };
+  for (int i = 0; i < n; ++i) {
+    const int b = order[i];
+    if (!((out.lds_mask >> b) & 1u) || bands[b].nch[sw] < 2) continue;
+    while (il < nl && last_len(last[il]) > bands[b].ck[sw]) run(last[il], bands[last[il]].nch[sw] - 1, 1), ++il;
+    run(b, 0, bands[b].nch[sw] - 1);
+  }
+  while (il < nl) run(last[il], bands[last[il]].nch[sw] - 1, 1), ++il;
+  out.lg_start[out.n_lg] = (unsigned short)pos;
 }
 
 hipError_t launch_block_attn(const bf16* Q, const bf16* Q_lo, const AttnBands& bands, int reg_chunks, int lds_chunks,

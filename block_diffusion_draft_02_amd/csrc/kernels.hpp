@@ -74,6 +74,12 @@ struct AttnBands {
   int n;
   unsigned lds_mask;      // bit b: band b stages its K/V through LDS
   int dbase[MAX_BANDS];   // the band's first chunk among its path's chunks
+  // the LDS path's chunks in dispatch order, longest first, as runs of equal-length chunks
+  // (a band's full chunks, then its last one): run g holds dispatch positions
+  // lg_start[g] .. lg_start[g + 1] - 1, chunks lg_chunk[g], lg_chunk[g] + 1, ... of band lg_band[g]
+  int n_lg;
+  unsigned short lg_start[2 * MAX_BANDS + 1];
+  unsigned char lg_band[2 * MAX_BANDS], lg_chunk[2 * MAX_BANDS];
   Band b[MAX_BANDS];
 };
 
