@@ -787,9 +787,9 @@ hipError_t launch_combine_hd(const float* part_o, const float* part_ml, const Ba
   constexpr int JS = (16 + CQ - 1) / CQ;   // slots for bands of up to 16 chunks
   constexpr int JX = NCH_MAX / CQ;         // slots for any band
   const int groups = (gamma * (nh / nkv) + CMB_ROWS - 1) / CMB_ROWS;
-  // four row blocks a workgroup once the call has rows for more than 2048 single blocks (then
+  // four row blocks a workgroup once the call has rows for 2048 or more single blocks (then
   // every thread keeps 4 JS loads in flight and the launch fills the chip in about two rounds)
-  const bool wide = max_nch <= JS * CQ && (long long)n_bands * nkv * groups > 2048;
+  const bool wide = max_nch <= JS * CQ && (long long)n_bands * nkv * groups >= 2048;
   if (wide) {
     const dim3 grid(n_bands, nkv, (groups + 3) / 4);
     (void)launch(k_attn_combine<HD, JS, 4>, grid, 1024, 0, st, part_o, part_ml, bands_dev, gamma, nh, nkv, sw, out, out_lo);

@@ -345,14 +345,16 @@ __global__ __launch_bounds__(1024) void k_rows_rmsnorm(const float* __restrict__
   } else {
     if (cs) pos = rowpos[r];
   }
+  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, gsz, h, xs, red_ss);
+  const float rs = rsqrtf(tot / (float)h + eps);
+  norm_out(xs, h, rs, w, out + (size_t)r * h, out_lo + (size_t)r * h);
+  // the angles last: their double-precision sincos would otherwise hold the row's loads
+  // (and every other wave, at the gather's barrier) behind it
   if (cs && (int)threadIdx.x < half) {
     double sn, cn;
     sincos((double)pos * inv_freq[threadIdx.x], &sn, &cn);
     cs[(size_t)r * half + threadIdx.x] = make_float2((float)cn, (float)sn);
   }
-  const float tot = rows_gather(nullptr, X + (size_t)r * h, S, ps, gsz, h, xs, red_ss);
-  const float rs = rsqrtf(tot / (float)h + eps);
-  norm_out(xs, h, rs, w, out + (size_t)r * h, out_lo + (size_t)r * h);
 }
 
 hipError_t launch_rows_rmsnorm(const float* X, int S, long long part_stride, int gsz, int M, int h,
