@@ -105,7 +105,7 @@ def build_host_check(verbose: bool = True) -> str:
          "sanitized runtime compile")
     drv = os.path.join(BUILD, "san", "abi_check.o")
     _run([clangxx(), "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer", *LINK_SAN, "-D__HIP_PLATFORM_AMD__",
-          "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-c",
+          "-Wno-c++20-extensions", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
           os.path.join(HOST_CHECK_DIR, "abi_check.cpp"), "-o", drv], "host check compile")
     tmp = HOST_CHECK + ".tmp"
     _run([clangxx(), *LINK_SAN, "-o", tmp, drv, rt, *objs, "-L/opt/rocm/lib", "-lamdhip64",

@@ -8,9 +8,10 @@
 // the chunk planner, the configuration checks or the argument checks ends the run with a
 // sanitizer report.
 //
-//   abi_check cpu   no device needed: error names, every configuration refusal, the NULL
-//                   handle paths, and (only where no device is present) create's unwind
-//                   when the device cannot be used; nothing is enqueued
+//   abi_check cpu   no device needed: the attention planner's band tables over random band
+//                   sets, error names, every configuration refusal, the NULL handle paths,
+//                   and (only where no device is present) create's unwind when the device
+//                   cannot be used; nothing is enqueued
 //   abi_check gpu   on a GPU: bf16, FP8, Markov-head and DFlash2 drafters; single and
 //                   batched appends; forwards of several widths and band sets (results
 //                   bit for bit equal band by band and between the two forward entry
@@ -30,6 +31,7 @@
 #include <vector>
 
 #include "dflash.h"
+#include "kernels.hpp"   // the attention planner's band table (dfl::plan_attn)
 
 namespace {
 
@@ -151,7 +153,71 @@ dflash_config base_config(const Model& m, int max_seq, int max_batch) {
 
 // ---- no device ------------------------------------------------------------------------------
 
+// dfl::plan_attn, the attention launch's band table: over seeded random band sets, the register
+// path's chunk bases must tile its chunks, and the LDS path's dispatch runs must hold each of
+// its chunks exactly once, in order of non-increasing length (any order computes the same
+// bits; a chunk missed or taken twice would not)
+void check_attn_plan() {
+  uint64_t s = 12345;
+  auto rnd = [&](int n) {
+    s = s * 6364136223846793005ULL + 1442695040888963407ULL;
+    return (int)((s >> 33) % (uint64_t)n);
+  };
+  int bad = 0;
+  for (int it = 0; it < 4000; ++it) {
+    const int n = 1 + rnd(dfl::MAX_BANDS), gamma = 1 + rnd(16);
+    dfl::Band bands[dfl::MAX_BANDS] = {};
+    for (int b = 0; b < n; ++b) {
+      dfl::Band& B = bands[b];
+      B.seq = b;
+      B.kv_len = rnd(it % 3 == 0 ? 40000 : 9000);
+      const int pages = (B.kv_len + gamma + dfl::PAGE - 1) / dfl::PAGE;
+      const int ckp = 16 * std::max(1 + rnd(12), (pages + 16 * 32 - 1) / (16 * 32));   // at most 32 chunks
+      B.ck[0] = ckp * dfl::PAGE;
+      B.nch[0] = (pages + ckp - 1) / ckp;
+    }
+    dfl::AttnBands ab;
+    int reg = 0, lds = 0;
+    dfl::plan_attn(bands, n, 0, 128, 0, true, gamma, ab, reg, lds);
+    std::vector<int> seen_reg, seen_lds;
+    int want_reg = 0, want_lds = 0;
+    for (int b = 0; b < n; ++b) {
+      const bool on_lds = (ab.lds_mask >> b) & 1u;
+      const int pages = (bands[b].kv_len + gamma + dfl::PAGE - 1) / dfl::PAGE;
+      bool ok = on_lds == (pages > dfl::ATTN_LDS_MIN_PAGES);
+      if (on_lds) want_lds += bands[b].nch[0];
+      else {
+        want_reg += bands[b].nch[0];
+        for (int c = 0; c < bands[b].nch[0]; ++c) seen_reg.push_back(ab.dbase[b] + c);
+      }
+      if (!ok) ++bad;
+    }
+    int prev = 1 << 30;
+    bool ok = ab.n_lg <= 2 * dfl::MAX_BANDS && (lds == 0 || (ab.n_lg > 0 && ab.lg_start[0] == 0 && ab.lg_start[ab.n_lg] == lds));
+    for (int g = 0; ok && g < ab.n_lg; ++g) {
+      const int b = ab.lg_band[g];
+      ok = b < n && ((ab.lds_mask >> b) & 1u) && ab.lg_start[g + 1] > ab.lg_start[g];
+      for (int d = ab.lg_start[g]; ok && d < ab.lg_start[g + 1]; ++d) {
+        const int c = ab.lg_chunk[g] + (d - ab.lg_start[g]);
+        const dfl::Band& B = bands[b];
+        const int len = std::min(B.ck[0], B.kv_len + gamma - B.kstart[0] - c * B.ck[0]);
+        ok = c < B.nch[0] && len > 0 && len <= prev;
+        prev = len;
+        seen_lds.push_back(b * 256 + c);
+      }
+    }
+    std::sort(seen_reg.begin(), seen_reg.end());
+    std::sort(seen_lds.begin(), seen_lds.end());
+    for (int i = 0; ok && i < (int)seen_reg.size(); ++i) ok = seen_reg[i] == i;
+    ok = ok && reg == want_reg && lds == want_lds && (int)seen_lds.size() == want_lds &&
+         std::adjacent_find(seen_lds.begin(), seen_lds.end()) == seen_lds.end();
+    if (!ok) ++bad;
+  }
+  CHECK(bad == 0, "attention planner: %d of 4000 random band sets planned wrongly", bad);
+}
+
 int run_cpu() {
+  check_attn_plan();
   for (int code : {(int)DFLASH_OK, (int)DFLASH_EINVAL, (int)DFLASH_ENOMEM, (int)DFLASH_EPOOL, (int)DFLASH_ERANGE,
                    (int)DFLASH_EHIP, 7, -99})
     CHECK(dflash_strerror(code) != nullptr && std::strlen(dflash_strerror(code)) > 0, "strerror %d", code);
