@@ -6,7 +6,8 @@
 // own length (a multiple of 256 keys) and the drafter's create-time path switch, so a band's
 // result does not depend on which other bands share the call. Two paths share one launch
 // per layer, each band taking one by its own length (the LDS path, further below, streams a
-// long band's K/V through LDS for all its query rows at once). The register path: one
+// long band's K/V through LDS for all its query rows at once; a call whose bands all take it
+// runs that path's own launch). The register path: one
 // workgroup per (chunk, kv head, 32 query rows), with the band table passed by value. The
 // workgroup stages its query rows (hi, lo) and all the chunk's page ids in LDS; each of its
 // four wavefronts then takes 32-key slices of the chunk (keys 32w, 32w + 128, ...), loading a
@@ -299,22 +300,20 @@ __device__ __forceinline__ void attn_reg_wg(AttnLds<HD>& sm, int id, const bf16*
 }
 
 // ---- K/V staged through LDS (head_dim 128, layers without a window, bands past 2048 keys) --
-// One 4-wave workgroup per (chunk, kv head) with all of the item's query rows: wave w owns rows
-// 32w .. 32w + 31 (two 16-row tiles, Q hi and lo held in registers) and takes every 32-key
+// One workgroup per (chunk, kv head) with all of the item's query rows, in waves of RT 16-row
+// tiles (Q hi and lo held in registers): in the launch shared with the register path 4 waves
+// of two tiles, in the LDS path's own launch 8 waves of one. Every wave takes every 32-key
 // slice of the chunk in order, so the chunk's K/V leaves L2 once instead of once per row
-// group. Slices stream through a ring of three LDS slots with the gfx950 global->LDS 16-byte
-// load, which takes no registers: of a slice, wave v brings page v%2 of K (v < 2) or of V
-// (v >= 2), 1 KB an instruction, each lane choosing its source so that the LDS copy is
-// swizzled for the MFMA fragment reads (K: 16-byte unit u of row r of page p sits at unit
-// u ^ (r ^ 4p); V: half h of dim row d sits at half h ^ (d/8 % 2)). Slice j+2 is requested
-// right after the barrier that ends slice j-1, and a wave waits (vmcnt) only for its own
-// loads of slice j: one barrier per slice. A wave's state covers its rows over the whole
-// chunk, so it writes the chunk's partials itself.
+// group. Slices stream through a ring of LDS slots with the gfx950 global->LDS 16-byte load,
+// which takes no registers: a slice's four 4 KB pages (K of keys 0-15 and 16-31, then V) are
+// sixteen 1 KB instructions shared out over the waves, each lane choosing its source so that
+// the LDS copy is swizzled for the MFMA fragment reads (K: 16-byte unit u of row r of page p
+// sits at unit u ^ (r ^ 4p); V: half h of dim row d sits at half h ^ (d/8 % 2)). Slice j + 2
+// is requested right after the barrier that ends slice j - 1, and a wave waits (vmcnt) only
+// for its own loads of slice j: one barrier per slice. A wave's state covers its rows over the
+// whole chunk, so it writes the chunk's partials itself. Chunks start longest first.
 constexpr int DMA_HD = 128;
-constexpr int DMA_RING = 3;        // ring slots of the LDS path in the launch shared with the register path
-#ifndef ATTN_LDS_RING
-#define ATTN_LDS_RING 3            // ring slots of the LDS path's own launch
-#endif
+constexpr int DMA_RING = 3;   // ring slots (a fourth measured no faster in either launch)
 
 struct DmaSlice {
   bf16 k[2][PAGE * DMA_HD];   // two K pages [16 keys][128], units swizzled within a row
@@ -591,8 +590,8 @@ __global__ __launch_bounds__(AW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_block_attn_lds(
     const bf16* __restrict__ Q, const bf16* __restrict__ Q_lo, const AttnBands ab, int gamma, int nh, KvGeom g,
     int layer, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) DmaLdsT<ATTN_LDS_RING> sm;
-  attn_lds_wg<1, ATTN_LDS_RING>(sm, blockIdx.x, Q, Q_lo, ab, gamma, nh, g, layer, scale_log2, part_o, part_ml);
+  __shared__ __attribute__((aligned(16))) DmaLds sm;
+  attn_lds_wg<1, DMA_RING>(sm, blockIdx.x, Q, Q_lo, ab, gamma, nh, g, layer, scale_log2, part_o, part_ml);
 }
 
 void plan_attn(const Band* bands, int n, int sw, int hd, int window, bool lds_path, int gamma, AttnBands& out,
